@@ -1,0 +1,183 @@
+"""fp64 CPU oracle for KDA prefill -- TEST INFRASTRUCTURE.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  It shares no code with the GPU library (gated_delta_rule_46_amd)
+and never imports it.
+
+* ``prefill``  -- token-by-token recurrence (kda_oracle.c), outputs, final
+  states and checkpoints.
+* ``package``  -- the affine map S_out = M S_in + D of a token range and the
+  range's outputs from a zero state (kda_oracle.c).
+* ``compose`` / ``scan_sequential`` / ``scan_blelloch`` -- package algebra
+  written from its definition with numpy matmuls (pegainfer PR #970,
+  whale-lane commit text: (M,D) packages combined all-prefix, with a Blelloch
+  prefix-scan fallback).
+* ``mirror`` -- the fp64 chunkwise form (used only to pin chunk-size
+  independence and the chunk algebra; never as the oracle).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+__all__ = ["build", "prefill", "package", "compose", "identity_package", "scan_sequential",
+           "scan_blelloch", "rel_l2", "threads"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        d, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        lib.kda_oracle_prefill.argtypes = [i64, i32, i32, i32, d, d, d, d, d, d, i32, d,
+                                           ctypes.c_double, i32, i32, d, d, d, d, i32]
+        lib.kda_oracle_prefill.restype = ctypes.c_int
+        lib.kda_oracle_package.argtypes = [i64, i32, i32, i32, d, d, d, d, d, i64, i64,
+                                           ctypes.c_double, i32, d, d, d, i32]
+        lib.kda_oracle_package.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def threads() -> int:
+    return max(1, os.cpu_count() or 1)
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c64(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+def prefill(q, k, v, g, beta, cu_seqlens, S0=None, scale=1.0, qk_l2norm=1,
+            ckpt_interval=0, ckpt_offsets=None, nthreads=None):
+    """Token-by-token KDA prefill in fp64.
+
+    q, k, g: [T,H,dk]; v: [T,H,dv]; beta: [T,H]; cu_seqlens: [N+1]; S0: [N,H,dk,dv].
+    Returns (o [T,H,dv], S_final [N,H,dk,dv], ckpt [rows,H,dk,dv] or None).
+    """
+    q, k, v, g, beta = (_c64(x) for x in (q, k, v, g, beta))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    S0 = _c64(S0)
+    o = np.zeros((T, H, dv))
+    Sf = np.zeros((N, H, dk, dv))
+    ck = None
+    off = None
+    if ckpt_interval:
+        off = np.ascontiguousarray(ckpt_offsets, dtype=np.int64)
+        ck = np.zeros((int(off[-1]), H, dk, dv))
+    rc = _load().kda_oracle_prefill(T, H, dk, dv, _p(q), _p(k), _p(v), _p(g), _p(beta),
+                                    _p(cu), N, _p(S0), float(scale), int(qk_l2norm),
+                                    int(ckpt_interval), _p(off), _p(ck), _p(o), _p(Sf),
+                                    int(nthreads or threads()))
+    if rc != 0:
+        raise ValueError("kda_oracle_prefill rejected its arguments")
+    return o, Sf, ck
+
+
+def package(q, k, v, g, beta, a, b, scale=1.0, qk_l2norm=1, nthreads=None):
+    """Package (M [H,dk,dk], D [H,dk,dv]) of rows [a, b) plus o_local [T,H,dv]
+    (rows a..b-1 filled: outputs of the range started from a zero state)."""
+    q, k, v, g, beta = (_c64(x) for x in (q, k, v, g, beta))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    M = np.zeros((H, dk, dk))
+    D = np.zeros((H, dk, dv))
+    o = np.zeros((T, H, dv))
+    rc = _load().kda_oracle_package(T, H, dk, dv, _p(q), _p(k), _p(v), _p(g), _p(beta),
+                                    int(a), int(b), float(scale), int(qk_l2norm),
+                                    _p(M), _p(D), _p(o), int(nthreads or threads()))
+    if rc != 0:
+        raise ValueError("kda_oracle_package rejected its arguments")
+    return M, D, o
+
+
+# ---------------------------------------------------------------------------
+# Package algebra, from its definition: S -> M S + D, composition "later after
+# earlier": (Mb, Db) o (Ma, Da) = (Mb Ma, Mb Da + Db), identity (I, 0).
+# ---------------------------------------------------------------------------
+def compose(later, earlier):
+    Mb, Db = later
+    Ma, Da = earlier
+    return Mb @ Ma, Mb @ Da + Db
+
+
+def identity_package(H, dk, dv):
+    return np.broadcast_to(np.eye(dk), (H, dk, dk)).copy(), np.zeros((H, dk, dv))
+
+
+def scan_sequential(Ms, Ds, S0):
+    """S_in[0] = S0; S_in[j+1] = M_j S_in[j] + D_j.  Returns (S_in [nseg,...], S_final)."""
+    S = np.array(S0, dtype=np.float64)
+    S_in = []
+    for M, D in zip(Ms, Ds):
+        S_in.append(S)
+        S = M @ S + D
+    return np.stack(S_in), S
+
+
+def scan_blelloch(Ms, Ds, S0):
+    """Exclusive prefix of the packages by a Blelloch up-sweep / down-sweep
+    (padded with identity packages to a power of two), then S_in[j] = Pre_j(S0)."""
+    n = len(Ms)
+    H, dk, _ = Ms[0].shape
+    dv = Ds[0].shape[2]
+    size = 1
+    while size < n:
+        size *= 2
+    P = [(np.array(Ms[j]), np.array(Ds[j])) for j in range(n)]
+    P += [identity_package(H, dk, dv) for _ in range(size - n)]
+    step = 1
+    while step < size:                       # up-sweep
+        for i in range(2 * step - 1, size, 2 * step):
+            P[i] = compose(P[i], P[i - step])
+        step *= 2
+    total = P[size - 1]
+    P[size - 1] = identity_package(H, dk, dv)
+    step = size // 2
+    while step >= 1:                         # down-sweep
+        for i in range(2 * step - 1, size, 2 * step):
+            left = P[i - step]
+            P[i - step] = P[i]
+            P[i] = compose(left, P[i])
+        step //= 2
+    S0 = np.asarray(S0, dtype=np.float64)
+    S_in = np.stack([P[j][0] @ S0 + P[j][1] for j in range(n)])
+    S_final = total[0] @ S0 + total[1]
+    return S_in, S_final
+
+
+def rel_l2(x, ref) -> float:
+    """||x - ref||_2 / ||ref||_2 over the whole tensor, in fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref.ravel())
+    num = np.linalg.norm((x - ref).ravel())
+    if den == 0.0:
+        return float(num)
+    return float(num / den)

@@ -1,0 +1,330 @@
+"""Pins of the fp64 oracle against facts fixed by the mathematics (CPU only).
+
+Each test checks the oracle against something other than itself: a closed
+form, an invariant, a hand computation, or a brute-force dense product.  The
+mistakes each one catches are listed in its docstring.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import mirror
+from workloads import make_workload, ckpt_offsets, leveled_segments
+
+TIGHT = 1e-11
+
+
+def rnd_inputs(seed, T, H, dk, dv, gate_shift=0.0, beta_shift=0.0, N=None):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((T, H, dk))
+    k = rng.standard_normal((T, H, dk))
+    v = rng.standard_normal((T, H, dv))
+    g = -np.logaddexp(0.0, rng.standard_normal((T, H, dk)) + gate_shift)
+    beta = 1.0 / (1.0 + np.exp(-(rng.standard_normal((T, H)) + beta_shift)))
+    return q, k, v, g, beta
+
+
+def unit_rows(x):
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+# ---------------------------------------------------------------------------
+def test_hand_computed_two_tokens():
+    """Two tokens, dk = dv = 2, worked by hand from the recurrence.
+
+    Token 1: S0 = 0, k = (1,0), v = (2,3), beta = 1/2, g = (0,0)
+        S1 = 1/2 k v^T = [[1, 1.5], [0, 0]];  q = (1,0) -> o1 = S1^T q = (1, 1.5)
+    Token 2: alpha = (1/2, 1): decayed S = [[0.5, 0.75], [0, 0]]
+        k = (0.6, 0.8), r = S^T k = (0.3, 0.45), v = (1, -1), beta = 1
+        S2 = S + k (v - r)^T = [[0.92, -0.12], [0.56, -1.16]]
+        q = (0, 1) -> o2 = S2^T q = (0.56, -1.16)
+    Catches: decay after the erase, o from the pre-update state, S vs S^T,
+    beta applied to the erase only.
+    """
+    q = np.array([[[1.0, 0.0]], [[0.0, 1.0]]])
+    k = np.array([[[1.0, 0.0]], [[0.6, 0.8]]])
+    v = np.array([[[2.0, 3.0]], [[1.0, -1.0]]])
+    g = np.array([[[0.0, 0.0]], [[np.log(0.5), 0.0]]])
+    beta = np.array([[0.5], [1.0]])
+    o, Sf, _ = oracle.prefill(q, k, v, g, beta, [0, 2], qk_l2norm=0)
+    np.testing.assert_allclose(o[0, 0], [1.0, 1.5], atol=1e-14)
+    np.testing.assert_allclose(o[1, 0], [0.56, -1.16], atol=1e-14)
+    np.testing.assert_allclose(Sf[0, 0], [[0.92, -0.12], [0.56, -1.16]], atol=1e-14)
+
+
+def test_beta_zero_is_pure_decay():
+    """beta = 0: S_t = Diag(prod alpha) S0 and o_t = S0^T (exp(G_t) * q_t).
+    Catches: wrong gate map (g vs exp(g)), decay on the wrong axis, missing S0."""
+    T, H, dk, dv = 40, 2, 8, 6
+    q, k, v, g, _ = rnd_inputs(1, T, H, dk, dv)
+    q = unit_rows(q)
+    beta = np.zeros((T, H))
+    S0 = np.random.default_rng(2).standard_normal((1, H, dk, dv))
+    o, Sf, _ = oracle.prefill(q, k, v, g, beta, [0, T], S0=S0, qk_l2norm=0)
+    G = np.cumsum(g, axis=0)                                   # [T,H,dk]
+    exp_o = np.einsum("hij,thi->thj", S0[0], np.exp(G) * q)
+    np.testing.assert_allclose(o, exp_o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(Sf[0], np.exp(G[-1])[:, :, None] * S0[0], rtol=1e-12, atol=1e-14)
+
+
+def test_alpha_one_beta_zero_constant_state():
+    """alpha = 1, beta = 0: the state never changes; o_t = S0^T q_t."""
+    T, H, dk, dv = 17, 1, 5, 7
+    q, k, v, _, _ = rnd_inputs(3, T, H, dk, dv)
+    S0 = np.random.default_rng(4).standard_normal((1, H, dk, dv))
+    o, Sf, _ = oracle.prefill(q, k, v, np.zeros((T, H, dk)), np.zeros((T, H)), [0, T],
+                              S0=S0, qk_l2norm=0)
+    np.testing.assert_allclose(Sf[0], S0[0], atol=0)
+    np.testing.assert_allclose(o, np.einsum("hij,thi->thj", S0[0], q), rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("dk,dv,n", [(8, 8, 8), (16, 5, 11), (6, 12, 6)])
+def test_orthonormal_keys_recall_values(dk, dv, n):
+    """alpha = 1, beta = 1, orthonormal keys k_1..k_n (n <= dk), any S0:
+    S_n^T k_i = v_i for every i, and a query equal to the key just written
+    reads back its value.  Catches: S vs S^T, a missing erase, o taken before
+    the write."""
+    rng = np.random.default_rng(5 + dk + dv)
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    keys = Qm[:n]                                            # orthonormal rows
+    k = keys[:, None, :]
+    v = rng.standard_normal((n, 1, dv))
+    q = k.copy()
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    o, Sf, _ = oracle.prefill(q, k, v, np.zeros((n, 1, dk)), np.ones((n, 1)), [0, n],
+                              S0=S0, qk_l2norm=0)
+    np.testing.assert_allclose(Sf[0, 0].T @ keys.T, v[:, 0].T, atol=1e-12)
+    np.testing.assert_allclose(o[:, 0], v[:, 0], atol=1e-12)
+
+
+def test_l2norm_definition():
+    """With beta = 0, alpha = 1 and S0 = I the output is the normalised query,
+    q / sqrt(|q|^2 + 1e-6): for |q| = 1e-3 that is q / sqrt(2e-6).  Large
+    queries are scale-invariant.  Catches: a missing or misplaced eps, the norm
+    taken over the wrong axis, the query scale dropped."""
+    dk = 4
+    u = unit_rows(np.array([[1.0, 2.0, -2.0, 0.5]]))
+    q = np.stack([1e-3 * u, 30.0 * u, 1.0 * u])[:, :, :]      # [3,1,dk]
+    T = q.shape[0]
+    S0 = np.eye(dk)[None, None]
+    o, _, _ = oracle.prefill(q, q, q, np.zeros((T, 1, dk)), np.zeros((T, 1)), [0, T],
+                             S0=S0, qk_l2norm=1, scale=0.5)
+    np.testing.assert_allclose(o[0, 0], 0.5 * 1e-3 / np.sqrt(2e-6) * u[0], rtol=1e-12)
+    np.testing.assert_allclose(o[1, 0], 0.5 * u[0], rtol=1e-8)
+    np.testing.assert_allclose(o[2, 0], 0.5 * u[0] / np.sqrt(1.0 + 1e-6), rtol=1e-13)
+
+
+def brute_force(q, k, v, g, beta, S0):
+    """Explicit dense products: A_t = (I - b k k^T) Diag(alpha_t), S_t from the
+    closed form S_t = (prod_{s<=t} A_s) S0 + sum_{s<=t} (prod_{s<u<=t} A_u) b_s k_s v_s^T."""
+    T, dk = k.shape
+    A = [(np.eye(dk) - beta[t] * np.outer(k[t], k[t])) @ np.diag(np.exp(g[t])) for t in range(T)]
+    outs, states = [], []
+    for t in range(T):
+        prod = np.eye(dk)
+        for s in range(t + 1):
+            prod = A[s] @ prod
+        S = prod @ S0
+        for s in range(t + 1):
+            tail = np.eye(dk)
+            for u in range(s + 1, t + 1):
+                tail = A[u] @ tail
+            S = S + tail @ (beta[s] * np.outer(k[s], v[s]))
+        states.append(S)
+        outs.append(S.T @ q[t])
+    return np.array(outs), states
+
+
+def test_brute_force_dense_product():
+    """The token loop equals the explicit product of the per-token maps.
+    Catches: any dropped term, sign, or index in the recurrence."""
+    T, dk, dv = 24, 6, 4
+    q, k, v, g, beta = rnd_inputs(7, T, 1, dk, dv)
+    q, k = unit_rows(q), unit_rows(k)
+    S0 = np.random.default_rng(8).standard_normal((1, 1, dk, dv))
+    o, Sf, _ = oracle.prefill(q, k, v, g, beta, [0, T], S0=S0, qk_l2norm=0)
+    ob, states = brute_force(q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0], S0[0, 0])
+    np.testing.assert_allclose(o[:, 0], ob, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(Sf[0, 0], states[-1], rtol=1e-11, atol=1e-12)
+
+
+def test_package_equals_dense_product():
+    """M is the product of the per-token maps, D the zero-start state, and
+    o_local the zero-start outputs; S_out = M S_in + D for any S_in."""
+    T, dk, dv = 20, 5, 3
+    q, k, v, g, beta = rnd_inputs(9, T, 1, dk, dv)
+    q, k = unit_rows(q), unit_rows(k)
+    a, b = 4, 17
+    M, D, ol = oracle.package(q, k, v, g, beta, a, b, qk_l2norm=0)
+    Mb = np.eye(dk)
+    for t in range(a, b):
+        At = (np.eye(dk) - beta[t, 0] * np.outer(k[t, 0], k[t, 0])) @ np.diag(np.exp(g[t, 0]))
+        Mb = At @ Mb
+    np.testing.assert_allclose(M[0], Mb, rtol=1e-12, atol=1e-14)
+    ob, states = brute_force(q[a:b, 0], k[a:b, 0], v[a:b, 0], g[a:b, 0], beta[a:b, 0],
+                             np.zeros((dk, dv)))
+    np.testing.assert_allclose(D[0], states[-1], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(ol[a:b, 0], ob, rtol=1e-11, atol=1e-13)
+    S_in = np.random.default_rng(10).standard_normal((1, 1, dk, dv))
+    _, Sf, _ = oracle.prefill(q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b], [0, b - a],
+                              S0=S_in, qk_l2norm=0)
+    np.testing.assert_allclose(Sf[0, 0], M[0] @ S_in[0, 0] + D[0], rtol=1e-11, atol=1e-13)
+
+
+def test_superposition():
+    """The state map is jointly linear in (S0, V): run(S0, V) = run(S0, 0) + run(0, V)."""
+    T, H, dk, dv = 50, 2, 8, 8
+    q, k, v, g, beta = rnd_inputs(11, T, H, dk, dv)
+    S0 = np.random.default_rng(12).standard_normal((1, H, dk, dv))
+    o, Sf, _ = oracle.prefill(q, k, v, g, beta, [0, T], S0=S0)
+    o1, S1, _ = oracle.prefill(q, k, np.zeros_like(v), g, beta, [0, T], S0=S0)
+    o2, S2, _ = oracle.prefill(q, k, v, g, beta, [0, T], S0=None)
+    np.testing.assert_allclose(o, o1 + o2, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(Sf, S1 + S2, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("C", [1, 2, 8, 16, 32, 64, 128])
+def test_chunk_size_independence(C):
+    """The chunkwise fp64 form equals the token loop for every chunk size,
+    with a ragged last chunk (T = 150).  C = 1 is the recurrence itself."""
+    T, H, dk, dv = 150, 2, 16, 8
+    q, k, v, g, beta = rnd_inputs(13, T, H, dk, dv)
+    S0 = 0.1 * np.random.default_rng(14).standard_normal((1, H, dk, dv))
+    o, Sf, _ = oracle.prefill(q, k, v, g, beta, [0, T], S0=S0)
+    om, Sm = mirror.chunked_prefill(q, k, v, g, beta, [0, T], S0, C)
+    assert oracle.rel_l2(om, o) < 1e-12
+    assert oracle.rel_l2(Sm, Sf) < 1e-12
+
+
+def test_composition_over_random_cuts():
+    """Packages of random chunk-aligned cuts, composed in order, reproduce the
+    sequential state; sequential and Blelloch scans agree; each segment's
+    outputs are its zero-start outputs plus the contribution of its incoming
+    state.  Long-memory gates keep M far from zero."""
+    T, H, dk, dv = 384, 2, 8, 8
+    q, k, v, g, beta = rnd_inputs(15, T, H, dk, dv, gate_shift=-6.0, beta_shift=-3.0)
+    S0 = np.random.default_rng(16).standard_normal((1, H, dk, dv))
+    o, Sf, _ = oracle.prefill(q, k, v, g, beta, [0, T], S0=S0)
+    rng = np.random.default_rng(17)
+    for nseg in (1, 2, 3, 5, 6):
+        cuts = np.sort(rng.choice(np.arange(1, T // 64), nseg - 1, replace=False)) * 64
+        starts = np.concatenate([[0], cuts, [T]])
+        Ms, Ds, oloc = [], [], np.zeros_like(o)
+        for j in range(nseg):
+            M, D, ol = oracle.package(q, k, v, g, beta, starts[j], starts[j + 1])
+            assert np.abs(M).max() > 1e-3          # long memory: M is not negligible
+            Ms.append(M)
+            Ds.append(D)
+            oloc[starts[j]:starts[j + 1]] = ol[starts[j]:starts[j + 1]]
+        S_in, S_fin = oracle.scan_sequential(Ms, Ds, S0[0])
+        np.testing.assert_allclose(S_fin, Sf[0], rtol=1e-10, atol=1e-12)
+        S_in_b, S_fin_b = oracle.scan_blelloch(Ms, Ds, S0[0])
+        np.testing.assert_allclose(S_in_b, S_in, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(S_fin_b, S_fin, rtol=1e-11, atol=1e-12)
+        # outputs: o = o_local + correction from S_in (linearity in S_in)
+        for j in range(nseg):
+            a, b = starts[j], starts[j + 1]
+            oc, _, _ = oracle.prefill(q[a:b], k[a:b], np.zeros_like(v[a:b]), g[a:b],
+                                      beta[a:b], [0, b - a], S0=S_in[j][None])
+            np.testing.assert_allclose(oloc[a:b] + oc, o[a:b], rtol=1e-9, atol=1e-11)
+
+
+def test_resume_from_checkpoint():
+    """Checkpoint at p = m * interval, then resume with it as S0: equals the
+    continuous run (outputs and final state)."""
+    T, H, dk, dv = 320, 2, 8, 8
+    q, k, v, g, beta = rnd_inputs(18, T, H, dk, dv, gate_shift=-4.0)
+    S0 = np.random.default_rng(19).standard_normal((1, H, dk, dv))
+    off = ckpt_offsets([T], 64)
+    o, Sf, ck = oracle.prefill(q, k, v, g, beta, [0, T], S0=S0, ckpt_interval=64,
+                               ckpt_offsets=off)
+    assert ck.shape[0] == 5
+    np.testing.assert_allclose(ck[4], Sf[0], atol=0)     # rung at the prompt end
+    for m in (1, 3):
+        p = 64 * m
+        o2, Sf2, _ = oracle.prefill(q[p:], k[p:], v[p:], g[p:], beta[p:], [0, T - p],
+                                    S0=ck[m - 1][None])
+        np.testing.assert_allclose(o2, o[p:], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(Sf2, Sf, rtol=1e-11, atol=1e-12)
+
+
+def test_state_norm_bound():
+    """||S_t||_F <= max_d alpha_{t,d} ||S_{t-1}||_F + beta_t ||v_t||, since
+    ||I - b k k^T||_2 <= 1 for unit k and 0 <= b <= 1."""
+    T, dk, dv = 64, 8, 8
+    q, k, v, g, beta = rnd_inputs(20, T, 1, dk, dv)
+    S0 = np.random.default_rng(21).standard_normal((1, 1, dk, dv))
+    off = ckpt_offsets([T], 1)
+    _, _, ck = oracle.prefill(q, k, v, g, beta, [0, T], S0=S0, ckpt_interval=1,
+                              ckpt_offsets=off)
+    prev = S0[0, 0]
+    for t in range(T):
+        lhs = np.linalg.norm(ck[t, 0])
+        rhs = np.exp(g[t, 0]).max() * np.linalg.norm(prev) + beta[t, 0] * np.linalg.norm(v[t, 0])
+        assert lhs <= rhs * (1 + 1e-12)
+        prev = ck[t, 0]
+
+
+def test_varlen_packing_and_permutation():
+    """Packing sequences equals running each alone; permuting the sequences
+    permutes outputs and states; checkpoint rows follow the offsets."""
+    lens = [70, 1, 128, 200, 64]
+    T, H, dk, dv = sum(lens), 2, 8, 4
+    q, k, v, g, beta = rnd_inputs(22, T, H, dk, dv)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    S0 = np.random.default_rng(23).standard_normal((len(lens), H, dk, dv))
+    off = ckpt_offsets(lens, 64)
+    o, Sf, ck = oracle.prefill(q, k, v, g, beta, cu, S0=S0, ckpt_interval=64, ckpt_offsets=off)
+    for n, L in enumerate(lens):
+        a, b = cu[n], cu[n + 1]
+        o1, S1, c1 = oracle.prefill(q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b], [0, L],
+                                    S0=S0[n:n + 1], ckpt_interval=64,
+                                    ckpt_offsets=ckpt_offsets([L], 64))
+        np.testing.assert_allclose(o1, o[a:b], atol=0)
+        np.testing.assert_allclose(S1[0], Sf[n], atol=0)
+        if L >= 64:
+            np.testing.assert_allclose(c1, ck[off[n]:off[n + 1]], atol=0)
+    perm = [3, 0, 4, 2, 1]
+    idx = np.concatenate([np.arange(cu[p], cu[p + 1]) for p in perm])
+    cu2 = np.concatenate([[0], np.cumsum([lens[p] for p in perm])])
+    o2, S2, _ = oracle.prefill(q[idx], k[idx], v[idx], g[idx], beta[idx], cu2, S0=S0[perm])
+    np.testing.assert_allclose(o2, o[idx], atol=0)
+    np.testing.assert_allclose(S2, Sf[perm], atol=0)
+
+
+def test_empty_sequences_and_zero_length():
+    """A zero-length sequence keeps its S0 and writes nothing; T = 0 works."""
+    H, dk, dv = 1, 4, 4
+    S0 = np.random.default_rng(24).standard_normal((2, H, dk, dv))
+    z = np.zeros((0, H, dk))
+    o, Sf, _ = oracle.prefill(z, z, np.zeros((0, H, dv)), z, np.zeros((0, H)), [0, 0, 0], S0=S0)
+    assert o.shape == (0, H, dv)
+    np.testing.assert_allclose(Sf, S0, atol=0)
+
+
+def test_standard_workload_recipes():
+    """The generator reproduces the documented workload shapes: config 3's
+    leveled segments and config 4's length draw (sum 447,540; 82 rungs)."""
+    b = leveled_segments(131072, 16)
+    assert list(np.diff(b))[:3] == [9536, 9344, 9088] and b[-1] == 131072
+    from workloads import varlen_lengths
+    L = varlen_lengths(46004, 64)
+    assert int(L.sum()) == 447540 and int(L.min()) == 513 and int(L.max()) == 29856
+    assert int((L // 4096).sum()) == 82
+    w = make_workload("t", [100, 28], 2, 8, 8, "bf16", 1)
+    assert w.q.dtype == np.uint16 and w.T == 128 and w.S0.shape == (2, 2, 8, 8)
+
+
+def test_bf16_rounding_matches_torch():
+    """The generator's round-to-nearest-even to bf16 agrees bit for bit with
+    torch's CPU conversion, ties and NaN included."""
+    import torch
+    from workloads import bf16_round_bits, bf16_bits_to_f32
+    rng = np.random.default_rng(25)
+    x = np.concatenate([rng.standard_normal(10000).astype(np.float32),
+                        np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -0.0, 3e38, 1e-40,
+                                  np.inf, -np.inf], dtype=np.float32)])
+    ours = bf16_round_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    assert np.isnan(bf16_bits_to_f32(bf16_round_bits(np.array([np.nan], np.float32))))[0]
