@@ -1,0 +1,273 @@
+// kda_api.hip -- the C ABI declared in include/kda.h: argument validation,
+// workspace sizing and launch planning.  Every check runs on the host before
+// the first launch, so a call either enqueues all of its work or none of it.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return KDA_OK;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Shared checks of the problem description.
+int check_config(const kda_config *cfg) {
+    if (!cfg) return fail(KDA_ERR_ARG, "cfg is NULL");
+    if (cfg->num_heads <= 0) return fail(KDA_ERR_ARG, "num_heads must be positive (got %d)", cfg->num_heads);
+    if (cfg->io_dtype != KDA_DTYPE_F32 && cfg->io_dtype != KDA_DTYPE_BF16)
+        return fail(KDA_ERR_ARG, "io_dtype must be KDA_DTYPE_F32 or KDA_DTYPE_BF16 (got %d)", cfg->io_dtype);
+    if (cfg->qk_l2norm != 0 && cfg->qk_l2norm != 1)
+        return fail(KDA_ERR_ARG, "qk_l2norm must be 0 or 1 (got %d)", cfg->qk_l2norm);
+    if (!std::isfinite(cfg->scale)) return fail(KDA_ERR_ARG, "scale must be finite");
+    if (cfg->chunk != kda::kChunk)
+        return fail(KDA_ERR_UNSUPPORTED, "chunk must be %d (got %d)", kda::kChunk, cfg->chunk);
+    const bool bf = cfg->io_dtype == KDA_DTYPE_BF16;
+    if (!kda::engine_supported(bf, cfg->dk, cfg->dv, 64))
+        return fail(KDA_ERR_UNSUPPORTED, "unsupported head dims dk=%d dv=%d for %s I/O", cfg->dk,
+                    cfg->dv, bf ? "bf16" : "fp32");
+    return KDA_OK;
+}
+
+int check_tensor(const void *p, const char *name, bool required, size_t align = 16) {
+    if (!p) return required ? fail(KDA_ERR_ARG, "%s is NULL", name) : KDA_OK;
+    if (!aligned(p, align)) return fail(KDA_ERR_ALIGN, "%s is not %zu-byte aligned", name, align);
+    return KDA_OK;
+}
+
+int check_ckpt_interval(int32_t interval) {
+    if (interval <= 0 || interval % kda::kChunk != 0)
+        return fail(KDA_ERR_ARG, "checkpoint interval must be a positive multiple of %d (got %d)",
+                    kda::kChunk, interval);
+    return KDA_OK;
+}
+
+int launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+#define KDA_TRY(x)                 \
+    do {                           \
+        const int _st = (x);       \
+        if (_st != KDA_OK) return _st; \
+    } while (0)
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_string(int status) {
+    switch (status) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_ARG: return "KDA_ERR_ARG: invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: shape or dtype not built";
+        case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: misaligned device pointer";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+        case KDA_ERR_DEVICE: return "KDA_ERR_DEVICE: kernel launch failed";
+    }
+    return "unknown KDA status";
+}
+
+const char *kda_last_error(void) { return g_last_error.c_str(); }
+
+const char *kda_version(void) { return "0.1.0"; }
+
+size_t kda_prefill_workspace(const kda_config *cfg, int64_t T, int32_t N) {
+    (void)cfg;
+    (void)T;
+    return round256((size_t)(N > 0 ? N : 1) * sizeof(int32_t));
+}
+
+int kda_prefill(const kda_config *cfg, const void *q, const void *k, const void *v,
+                const float *g, const float *beta, const int64_t *cu_seqlens, int32_t N,
+                int64_t T, const float *S0, float *S_final, void *o, const kda_ckpt *ckpt,
+                void *ws, size_t ws_bytes, void *stream) {
+    KDA_TRY(check_config(cfg));
+    if (T < 0) return fail(KDA_ERR_ARG, "T must be >= 0 (got %lld)", (long long)T);
+    if (N < 0) return fail(KDA_ERR_ARG, "N must be >= 0 (got %d)", N);
+    if (T > 0 && N == 0) return fail(KDA_ERR_ARG, "T > 0 needs at least one sequence");
+    if (N == 0) return ok();
+    const bool need_rows = T > 0;
+    KDA_TRY(check_tensor(q, "q", need_rows));
+    KDA_TRY(check_tensor(k, "k", need_rows));
+    KDA_TRY(check_tensor(v, "v", need_rows));
+    KDA_TRY(check_tensor(g, "g", need_rows));
+    KDA_TRY(check_tensor(beta, "beta", need_rows, 4));
+    KDA_TRY(check_tensor(o, "o", need_rows));
+    KDA_TRY(check_tensor(cu_seqlens, "cu_seqlens", true, 8));
+    KDA_TRY(check_tensor(S0, "S0", false, 16));
+    KDA_TRY(check_tensor(S_final, "S_final", false, 16));
+    if (ckpt) {
+        KDA_TRY(check_ckpt_interval(ckpt->interval));
+        KDA_TRY(check_tensor(ckpt->states, "ckpt->states", true, 16));
+        KDA_TRY(check_tensor(ckpt->offsets, "ckpt->offsets", N > 1, 8));
+    }
+    const size_t need = kda_prefill_workspace(cfg, T, N);
+    if (!ws || ws_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, ws_bytes);
+    KDA_TRY(check_tensor(ws, "ws", true, 16));
+
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf = cfg->io_dtype == KDA_DTYPE_BF16;
+    const int nb = kda::engine_pick_nb(bf, cfg->dk, cfg->dv, (int64_t)N * cfg->num_heads,
+                                       kda::kModePrefill);
+    int32_t *order = nullptr;
+    if (N > 1 && N <= 8192) {
+        order = (int32_t *)ws;
+        hipError_t e = kda::launch_plan(cu_seqlens, N, order, s);
+        if (e != hipSuccess) return launched(e, "plan");
+    }
+    kda::EngineArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
+    a.bounds = cu_seqlens; a.order = order; a.n_units = N; a.H = cfg->num_heads;
+    a.ncb_s = cfg->dv / nb; a.ncb_m = 0;
+    a.S_init = S0; a.S_out = S_final; a.M_out = nullptr;
+    a.interval = ckpt ? ckpt->interval : 0;
+    a.ckpt_off = ckpt ? ckpt->offsets : nullptr;
+    a.ckpt_S = ckpt ? ckpt->states : nullptr;
+    a.ckpt_M = nullptr;
+    a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;
+    return launched(kda::launch_engine(kda::kModePrefill, bf, cfg->dk, cfg->dv, nb, a, s), "prefill");
+}
+
+int kda_segment_package(const kda_config *cfg, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta, int64_t T, const int64_t *seg_start,
+                        int32_t nseg, void *o_local, float *M, float *D, const kda_ckpt *ckpt,
+                        float *sub_M, float *sub_D, void *ws, size_t ws_bytes, void *stream) {
+    (void)ws;
+    (void)ws_bytes;
+    KDA_TRY(check_config(cfg));
+    if (T <= 0) return fail(KDA_ERR_ARG, "T must be positive (got %lld)", (long long)T);
+    if (nseg <= 0) return fail(KDA_ERR_ARG, "nseg must be positive (got %d)", nseg);
+    KDA_TRY(check_tensor(q, "q", true));
+    KDA_TRY(check_tensor(k, "k", true));
+    KDA_TRY(check_tensor(v, "v", true));
+    KDA_TRY(check_tensor(g, "g", true));
+    KDA_TRY(check_tensor(beta, "beta", true, 4));
+    KDA_TRY(check_tensor(o_local, "o_local", true));
+    KDA_TRY(check_tensor(seg_start, "seg_start", true, 8));
+    KDA_TRY(check_tensor(M, "M", true));
+    KDA_TRY(check_tensor(D, "D", true));
+    const bool subs = ckpt && (sub_M || sub_D);
+    if (subs) {
+        KDA_TRY(check_ckpt_interval(ckpt->interval));
+        KDA_TRY(check_tensor(sub_M, "sub_M", true));
+        KDA_TRY(check_tensor(sub_D, "sub_D", true));
+    }
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf = cfg->io_dtype == KDA_DTYPE_BF16;
+    const int nb = kda::engine_pick_nb(bf, cfg->dk, cfg->dv, (int64_t)nseg * cfg->num_heads,
+                                       kda::kModePackage);
+    kda::EngineArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o_local;
+    a.bounds = seg_start; a.order = nullptr; a.n_units = nseg; a.H = cfg->num_heads;
+    a.ncb_s = cfg->dv / nb; a.ncb_m = cfg->dk / nb;
+    a.S_init = nullptr; a.S_out = D; a.M_out = M;
+    a.interval = subs ? ckpt->interval : 0;
+    a.ckpt_off = nullptr; a.ckpt_S = subs ? sub_D : nullptr; a.ckpt_M = subs ? sub_M : nullptr;
+    a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;
+    return launched(kda::launch_engine(kda::kModePackage, bf, cfg->dk, cfg->dv, nb, a, s), "package");
+}
+
+size_t kda_segment_scan_workspace(const kda_config *cfg, int32_t nseg, int32_t algo) {
+    if (!cfg || nseg <= 0 || algo != KDA_SCAN_BLELLOCH) return 0;
+    return round256(kda::blelloch_workspace(cfg->dk, cfg->dv, cfg->num_heads, nseg));
+}
+
+int kda_segment_scan(const kda_config *cfg, int32_t nseg, const float *M, const float *D,
+                     const float *S0, float *S_in, float *S_final, int32_t algo, void *ws,
+                     size_t ws_bytes, void *stream) {
+    KDA_TRY(check_config(cfg));
+    if (nseg <= 0) return fail(KDA_ERR_ARG, "nseg must be positive (got %d)", nseg);
+    if (algo != KDA_SCAN_SEQUENTIAL && algo != KDA_SCAN_BLELLOCH)
+        return fail(KDA_ERR_ARG, "algo must be KDA_SCAN_SEQUENTIAL or KDA_SCAN_BLELLOCH (got %d)", algo);
+    KDA_TRY(check_tensor(M, "M", true));
+    KDA_TRY(check_tensor(D, "D", true));
+    KDA_TRY(check_tensor(S0, "S0", false));
+    KDA_TRY(check_tensor(S_in, "S_in", true));
+    KDA_TRY(check_tensor(S_final, "S_final", true));
+    hipStream_t s = (hipStream_t)stream;
+    if (algo == KDA_SCAN_SEQUENTIAL)
+        return launched(kda::launch_scan_sequential(cfg->dk, cfg->dv, cfg->num_heads, nseg, M, D,
+                                                    S0, S_in, S_final, s), "sequential scan");
+    const size_t need = kda_segment_scan_workspace(cfg, nseg, algo);
+    if (!ws || ws_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, ws_bytes);
+    KDA_TRY(check_tensor(ws, "ws", true));
+    return launched(kda::launch_scan_blelloch(cfg->dk, cfg->dv, cfg->num_heads, nseg, M, D, S0,
+                                              S_in, S_final, ws, s), "Blelloch scan");
+}
+
+int kda_output_fixup(const kda_config *cfg, const void *q, const void *k, const float *g,
+                     const float *beta, int64_t T, const int64_t *seg_start, int32_t nseg,
+                     const float *S_in, void *o, void *ws, size_t ws_bytes, void *stream) {
+    (void)ws;
+    (void)ws_bytes;
+    KDA_TRY(check_config(cfg));
+    if (T <= 0) return fail(KDA_ERR_ARG, "T must be positive (got %lld)", (long long)T);
+    if (nseg <= 0) return fail(KDA_ERR_ARG, "nseg must be positive (got %d)", nseg);
+    KDA_TRY(check_tensor(q, "q", true));
+    KDA_TRY(check_tensor(k, "k", true));
+    KDA_TRY(check_tensor(g, "g", true));
+    KDA_TRY(check_tensor(beta, "beta", true, 4));
+    KDA_TRY(check_tensor(seg_start, "seg_start", true, 8));
+    KDA_TRY(check_tensor(S_in, "S_in", true));
+    KDA_TRY(check_tensor(o, "o", true));
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf = cfg->io_dtype == KDA_DTYPE_BF16;
+    const int nb = kda::engine_pick_nb(bf, cfg->dk, cfg->dv, (int64_t)nseg * cfg->num_heads,
+                                       kda::kModeFixup);
+    kda::EngineArgs a{};
+    a.q = q; a.k = k; a.v = nullptr; a.g = g; a.beta = beta; a.o = o;
+    a.bounds = seg_start; a.order = nullptr; a.n_units = nseg; a.H = cfg->num_heads;
+    a.ncb_s = cfg->dv / nb; a.ncb_m = 0;
+    a.S_init = S_in; a.S_out = nullptr; a.M_out = nullptr;
+    a.interval = 0; a.ckpt_off = nullptr; a.ckpt_S = nullptr; a.ckpt_M = nullptr;
+    a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;
+    return launched(kda::launch_engine(kda::kModeFixup, bf, cfg->dk, cfg->dv, nb, a, s), "fixup");
+}
+
+int kda_checkpoint_write(const kda_config *cfg, const kda_ckpt *ckpt, int64_t T,
+                         const int64_t *seg_start, int32_t nseg, const float *S_in,
+                         const float *sub_M, const float *sub_D, void *stream) {
+    KDA_TRY(check_config(cfg));
+    if (!ckpt) return fail(KDA_ERR_ARG, "ckpt is NULL");
+    KDA_TRY(check_ckpt_interval(ckpt->interval));
+    if (T <= 0) return fail(KDA_ERR_ARG, "T must be positive (got %lld)", (long long)T);
+    if (nseg <= 0) return fail(KDA_ERR_ARG, "nseg must be positive (got %d)", nseg);
+    KDA_TRY(check_tensor(ckpt->states, "ckpt->states", true));
+    KDA_TRY(check_tensor(seg_start, "seg_start", true, 8));
+    KDA_TRY(check_tensor(S_in, "S_in", true));
+    KDA_TRY(check_tensor(sub_M, "sub_M", true));
+    KDA_TRY(check_tensor(sub_D, "sub_D", true));
+    return launched(kda::launch_ckpt_write(cfg->dk, cfg->dv, cfg->num_heads, T, seg_start, nseg,
+                                           ckpt->interval, S_in, sub_M, sub_D, ckpt->states,
+                                           (hipStream_t)stream), "checkpoint write");
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// Internal interfaces between the C ABI (kda_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kChunk = 64;
+
+enum EngineMode : int { kModePrefill = 0, kModePackage = 1, kModeFixup = 2 };
+
+// Arguments of the fused chunk engine (one workgroup per (unit, head,
+// column block); a unit is a sequence for prefill and a segment otherwise).
+struct EngineArgs {
+    const void *q, *k, *v;       // [T,H,dk] / [T,H,dv], io dtype
+    const float *g, *beta;       // [T,H,dk], [T,H]
+    void *o;                     // [T,H,dv]: written (prefill/package) or updated (fixup)
+    const int64_t *bounds;       // [n_units+1] token offsets (cu_seqlens or seg_start)
+    const int32_t *order;        // [n_units] longest-first unit order, NULL = identity
+    int32_t n_units;
+    int32_t H;
+    int32_t ncb_s;               // column blocks over the value state (dv / NB)
+    int32_t ncb_m;               // column blocks over the M state (dk / NB), package only
+    const float *S_init;         // prefill: S0 (nullable); fixup: S_in
+    float *S_out;                // prefill: S_final (nullable); package: D
+    float *M_out;                // package: M
+    int32_t interval;            // checkpoint interval in tokens, 0 = none
+    const int64_t *ckpt_off;     // prefill: first rung row per sequence (nullable)
+    float *ckpt_S;               // prefill: checkpoint states; package: sub_D (nullable)
+    float *ckpt_M;               // package: sub_M (nullable)
+    float scale;
+    int32_t l2norm;
+};
+
+// Launches the engine.  bf16 selects bf16 I/O (bf16 MFMA operands) versus
+// fp32 I/O (fp32 MFMA).  nb is the value-column block width.  Returns a HIP
+// error code.  `grid_units` is n_units (the launch covers every unit).
+hipError_t launch_engine(int mode, bool bf16, int dk, int dv, int nb, const EngineArgs &a,
+                         hipStream_t stream);
+bool engine_supported(bool bf16, int dk, int dv, int nb);
+int engine_pick_nb(bool bf16, int dk, int dv, int64_t units, int mode);
+
+// Longest-first schedule of n sequences from cu_seqlens (device), into order[n].
+hipError_t launch_plan(const int64_t *cu_seqlens, int32_t n, int32_t *order, hipStream_t s);
+
+// Package scans (fp32).
+hipError_t launch_scan_sequential(int dk, int dv, int H, int nseg, const float *M,
+                                  const float *D, const float *S0, float *S_in,
+                                  float *S_final, hipStream_t s);
+hipError_t launch_scan_blelloch(int dk, int dv, int H, int nseg, const float *M,
+                                const float *D, const float *S0, float *S_in,
+                                float *S_final, void *ws, hipStream_t s);
+size_t blelloch_workspace(int dk, int dv, int H, int nseg);
+
+// Segment-path checkpoints: states[row] = sub_M[row] S_in[j] + sub_D[row].
+hipError_t launch_ckpt_write(int dk, int dv, int H, int64_t T, const int64_t *seg_start,
+                             int nseg, int interval, const float *S_in, const float *sub_M,
+                             const float *sub_D, float *states, hipStream_t s);
+
+}  // namespace kda

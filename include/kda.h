@@ -1,0 +1,204 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) KDA prefill library, libkda.so.
+ *
+ * Kimi Delta Attention (KDA) is a gated delta-rule linear-attention
+ * recurrence with one decay per key channel.  For each sequence and head,
+ * with a dk x dv state S,
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t,          alpha_t = exp(g_t)   (g_t <= 0, per key channel)
+ *
+ * where q_t, k_t are L2-normalised inside the library (x / sqrt(|x|^2 + 1e-6),
+ * q then multiplied by `scale`) when cfg->qk_l2norm is 1.  The pages this
+ * library follows name KDA and its serving machinery but do not write the
+ * recurrence out; the statement above is the standard KDA definition.
+ *
+ * Two paths compute it:
+ *
+ *  - Chunked prefill (kda_prefill): sequences packed by cu_seqlens, one
+ *    state block per sequence (kern PR #44 "Prefill-only pipeline
+ *    parallelism", commit "k3: flash-kda builds a varlen variant": cu_seqlens
+ *    splits the rows into sequences, each with its own state block, and a
+ *    tile-prefix step lays out the tiles), with optional state checkpoints
+ *    (ROCm/ATOM PR #2709 "PP8 prefill for P/D serving", Changes: KDA state
+ *    checkpoints on the chunk grid).
+ *
+ *  - Segment path for one long sequence (pegainfer PR #970 "cross-process CP
+ *    whale gang", whale-lane commit text: each segment exports a KDA (M,D)
+ *    package, packages are combined all-prefix or by a Blelloch prefix scan):
+ *        kda_segment_package -> kda_segment_scan -> kda_output_fixup
+ *        -> kda_checkpoint_write
+ *    Segment j maps its incoming state to S_out = M_j S_in + D_j.  Its outputs
+ *    are first computed from a zero state (o_local) and then corrected from
+ *    its incoming state S_in^j.  All segments run as parallel work on one GPU.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Layouts (row-major, contiguous): q, k, g [T,H,dk]; v, o [T,H,dv];
+ *    beta [T,H]; states [., H, dk, dv] (key-major); M [., H, dk, dk].
+ *  - q, k, v, o are float32 (io_dtype KDA_DTYPE_F32) or bfloat16
+ *    (KDA_DTYPE_BF16, raw 16-bit storage).  g, beta and all states are
+ *    float32.  Arithmetic: fp32 accumulation; matrix products on MFMA with
+ *    bf16 operands for bf16 I/O and fp32 operands for fp32 I/O.
+ *  - Supported shapes: dk == dv in {64, 128} for bf16, dk == dv == 64 for
+ *    fp32; chunk == 64.  Other shapes return KDA_ERR_UNSUPPORTED.
+ *  - Every pointer is a device pointer unless stated; every device pointer
+ *    must be 16-byte aligned (KDA_ERR_ALIGN otherwise).
+ *  - Ownership: the caller owns every buffer.  The library allocates no
+ *    device memory and keeps none between calls; scratch comes from the
+ *    caller's workspace, sized by the matching *_workspace query.
+ *  - Asynchrony: all work is enqueued on `stream` (a hipStream_t; NULL = the
+ *    null stream) without synchronising.  Argument errors are detected on
+ *    the host and returned before anything is launched.  A failed launch
+ *    returns KDA_ERR_DEVICE.  Device-side data (cu_seqlens monotone, segment
+ *    starts chunk-aligned, g <= 0) is not validated: that would need a sync.
+ *  - Numerical domain: the per-channel log-decay summed over any aligned
+ *    16-token block must stay above about -80 (a mean alpha above ~0.007
+ *    per token); beyond it intermediate exponentials leave fp32 range.
+ *  - Threading: reentrant; the only process state is a per-thread error
+ *    string and a cached device-attribute query.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define KDA_OK              0
+#define KDA_ERR_ARG         1  /* null pointer, negative size, bad enum          */
+#define KDA_ERR_UNSUPPORTED 2  /* shape / dtype / chunk the library does not build */
+#define KDA_ERR_ALIGN       3  /* a device pointer is not 16-byte aligned        */
+#define KDA_ERR_WORKSPACE   4  /* workspace missing or smaller than the query    */
+#define KDA_ERR_DEVICE      5  /* a kernel launch failed                          */
+
+#define KDA_DTYPE_F32  0
+#define KDA_DTYPE_BF16 1
+
+#define KDA_SCAN_SEQUENTIAL 0
+#define KDA_SCAN_BLELLOCH   1
+
+/* Problem description, read on the host during the call only. */
+typedef struct {
+    int32_t num_heads;   /* H                                              */
+    int32_t dk, dv;      /* key / value head dims                          */
+    int32_t chunk;       /* must be 64                                     */
+    int32_t io_dtype;    /* KDA_DTYPE_F32 or KDA_DTYPE_BF16 (q, k, v, o)   */
+    float scale;         /* query scale applied after normalisation        */
+    int32_t qk_l2norm;   /* 1: L2-normalise q and k in-kernel; 0: use as is */
+} kda_config;
+
+/*
+ * State checkpoints.  Rungs sit at sequence-relative positions p = m*interval
+ * (m >= 1, p <= sequence length): the state after the first p tokens.
+ * interval is a positive multiple of the chunk (0 = no checkpoints).  The
+ * rung of sequence n at p is row offsets[n] + p/interval - 1 of `states`
+ * [rows, H, dk, dv].  offsets (device int64 [N+1]) may be NULL for a single
+ * sequence (rows then start at 0).
+ */
+typedef struct {
+    int32_t interval;
+    const int64_t *offsets;
+    float *states;
+} kda_ckpt;
+
+/* ------------------------------------------------------------------------ */
+/* Chunked prefill                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes kda_prefill needs for N packed sequences (never 0). */
+size_t kda_prefill_workspace(const kda_config *cfg, int64_t T, int32_t N);
+
+/*
+ * Chunked KDA prefill of N sequences packed along T.
+ *   q, k [T,H,dk], v [T,H,dv] (io_dtype); g [T,H,dk], beta [T,H] (fp32);
+ *   cu_seqlens: device int64 [N+1], cu_seqlens[0] = 0, cu_seqlens[N] = T,
+ *       non-decreasing; a zero-length sequence keeps its S0;
+ *   S0 [N,H,dk,dv] initial states, NULL = zeros;
+ *   S_final [N,H,dk,dv] final states, NULL = not written;
+ *   o [T,H,dv] outputs (io_dtype);
+ *   ckpt: NULL or checkpoints as described at kda_ckpt;
+ *   ws / ws_bytes: scratch of at least kda_prefill_workspace() bytes.
+ * Work is scheduled longest sequence first.  N = 0 or T = 0 is a no-op.
+ */
+int kda_prefill(const kda_config *cfg, const void *q, const void *k, const void *v,
+                const float *g, const float *beta, const int64_t *cu_seqlens, int32_t N,
+                int64_t T, const float *S0, float *S_final, void *o, const kda_ckpt *ckpt,
+                void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Segment path (one sequence of T tokens split into nseg segments)         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Per-segment packages.  seg_start: device int64 [nseg+1], seg_start[0] = 0,
+ * seg_start[nseg] = T, every interior start a multiple of the chunk.
+ * Writes, for every segment j and head h:
+ *   o_local [T,H,dv]  outputs of the segment computed from a zero state;
+ *   M [nseg,H,dk,dk]  the segment's linear part (product of its token maps);
+ *   D [nseg,H,dk,dv]  the segment's state when started from zero;
+ *   with ckpt != NULL (states unused here) and sub_M / sub_D non-NULL, the
+ *   sub-package (Pi_p, S0_p) of every rung p inside (seg_start[j],
+ *   seg_start[j+1]]: the map from S_in^j to the state at p, at rung row
+ *   p/interval - 1 of sub_M [rows,H,dk,dk] and sub_D [rows,H,dk,dv].
+ * No workspace is needed (ws may be NULL).
+ */
+int kda_segment_package(const kda_config *cfg, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta, int64_t T, const int64_t *seg_start,
+                        int32_t nseg, void *o_local, float *M, float *D, const kda_ckpt *ckpt,
+                        float *sub_M, float *sub_D, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes kda_segment_scan needs (0 for the sequential scan). */
+size_t kda_segment_scan_workspace(const kda_config *cfg, int32_t nseg, int32_t algo);
+
+/*
+ * Prefix scan of the packages: S_in^0 = S0 (NULL = zeros),
+ * S_in^{j+1} = M_j S_in^j + D_j.  Writes S_in [nseg,H,dk,dv] and
+ * S_final [H,dk,dv].  algo KDA_SCAN_SEQUENTIAL walks the segments in order;
+ * KDA_SCAN_BLELLOCH runs a work-efficient up-sweep / down-sweep exclusive
+ * scan over the composition (Mb,Db) o (Ma,Da) = (Mb Ma, Mb Da + Db), padded
+ * with identity packages to a power of two, in the workspace.
+ * M and D are not modified.
+ */
+int kda_segment_scan(const kda_config *cfg, int32_t nseg, const float *M, const float *D,
+                     const float *S0, float *S_in, float *S_final, int32_t algo,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Output fix-up: o holds o_local on entry and the final outputs on return,
+ * o_t += contribution of S_in^j propagated through segment j.  The
+ * correction stops exactly once the propagated state is all zeros in fp32.
+ * No workspace is needed.
+ */
+int kda_output_fixup(const kda_config *cfg, const void *q, const void *k, const float *g,
+                     const float *beta, int64_t T, const int64_t *seg_start, int32_t nseg,
+                     const float *S_in, void *o, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Checkpoint states of the segment path: for every rung p (see kda_ckpt;
+ * one sequence, so rows start at 0) inside segment j,
+ *     states[p/interval - 1] = sub_M[row] S_in^j + sub_D[row]
+ * from the sub-packages written by kda_segment_package.
+ */
+int kda_checkpoint_write(const kda_config *cfg, const kda_ckpt *ckpt, int64_t T,
+                         const int64_t *seg_start, int32_t nseg, const float *S_in,
+                         const float *sub_M, const float *sub_D, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Diagnostics                                                               */
+/* ------------------------------------------------------------------------ */
+const char *kda_status_string(int status);
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char *kda_last_error(void);
+/* Library version, "major.minor.patch". */
+const char *kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

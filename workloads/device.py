@@ -1,0 +1,32 @@
+"""Moves a generated Workload to torch tensors on a device (plumbing only)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+
+def _io_tensor(a: np.ndarray, dtype: str, device) -> torch.Tensor:
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(device)
+
+
+def to_torch(w, device="cuda") -> dict:
+    out = {
+        "q": _io_tensor(w.q, w.dtype, device),
+        "k": _io_tensor(w.k, w.dtype, device),
+        "v": _io_tensor(w.v, w.dtype, device),
+        "g": torch.from_numpy(w.g).to(device),
+        "beta": torch.from_numpy(w.beta).to(device),
+        "cu_seqlens": torch.from_numpy(w.cu_seqlens.astype(np.int64)).to(device),
+        "S0": None if w.S0 is None else torch.from_numpy(w.S0).to(device),
+    }
+    if w.seg_start is not None:
+        out["seg_start"] = torch.from_numpy(w.seg_start.astype(np.int64)).to(device)
+    return out
+
+
+def to_numpy_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
