@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""KDA prefill benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
+
+One step is one full KDA layer over the workload: for the segment-path
+workloads (default: 131,072 tokens, H=32, d=128, bf16, 16 leveled segments,
+Blelloch scan, checkpoints every 4096 tokens) package -> scan -> fix-up ->
+checkpoint write; for the chunked workloads one kda_prefill call.  Inputs are
+seeded synthetic tensors already resident in HBM when timing starts.
+
+Prints one JSON line with tokens/s per layer, the dominant kernel's roofline
+(algorithmic bytes over its HIP-event-timed duration against 8 TB/s HBM), the
+chunked form's algorithmic MFMA fraction, and the fp64 oracle timed on a
+bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def chunk_flops_per_token_head(C: int, dk: int, dv: int) -> float:
+    """Algorithmic flops of the chunkwise form per token and head (triangles
+    exploited): Gram A and P, UT inverse, W and U~, and the three state
+    products U = U~ - W S, O = Qbar S + P U, S <- gamma S + Kbar^T U."""
+    gram = dk * (C - 1) + dk * (C + 1)
+    wy = (C + 1) * dk + (C + 1) * dv
+    inv = C * C / 3.0
+    state = 2 * dk * dv * 3 + (C + 1) * dv
+    return gram + wy + inv + state
+
+
+def bytes_per_token_head(dk: int, dv: int, io_bytes: int) -> int:
+    """q, k, v, o in the I/O dtype, g and beta in fp32."""
+    return io_bytes * (2 * dk + 2 * dv) + 4 * dk + 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, target_s: float) -> dict:
+    """The fp64 oracle as it stands, on the first tokens of sequence 0, all heads."""
+    import oracle
+    oracle.build(force=False)
+    threads = oracle.threads()
+    L0 = int(w.lengths[0])
+
+    def run(ntok):
+        a = int(w.cu_seqlens[0])
+        sl = slice(a, a + ntok)
+        q, k, v, g, b = (np.ascontiguousarray(getattr(w, n)[sl]) for n in ("q", "k", "v", "g", "beta"))
+        from workloads import to_f64
+        args = [to_f64(q, w.dtype), to_f64(k, w.dtype), to_f64(v, w.dtype),
+                g.astype(np.float64), b.astype(np.float64)]
+        S0 = None if w.S0 is None else w.S0[0:1]
+        t = time.perf_counter()
+        oracle.prefill(*args, [0, ntok], S0=S0, nthreads=threads)
+        return time.perf_counter() - t
+
+    probe = min(L0, 512)
+    dt = run(probe)
+    ntok = int(min(L0, max(probe, probe * target_s / max(dt, 1e-6))))
+    ntok = max(64, (ntok // 64) * 64) if L0 >= 64 else L0
+    dt = run(ntok)
+    return {"value": round(ntok / dt, 2), "unit": "tokens/s", "cores": int(min(threads, w.H)),
+            "kind": "oracle",
+            "sample": f"first {ntok} tokens of sequence 0, all {w.H} heads, fp64 token loop, "
+                      f"{threads} threads over heads ({dt:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        sys.exit(2)
+    import torch
+    from workloads import standard_workload, ckpt_offsets
+    from workloads.device import to_torch
+    import gated_delta_rule_46_amd.kda as K
+
+    w = standard_workload(args.config)
+    t = to_torch(w)
+    dev = t["q"].device
+    T, H, dk, dv = w.T, w.H, w.dk, w.dv
+    segmented = w.seg_start is not None
+    io_bytes = 2 if w.dtype == "bf16" else 4
+    stream = torch.cuda.current_stream()
+
+    ev = {}
+
+    def mark(name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        ev.setdefault(name, []).append(e)
+
+    if segmented:
+        S0 = None if t["S0"] is None else t["S0"][0].contiguous()
+        interval = w.ckpt_interval
+
+        def step(timed):
+            if timed:
+                mark("pkg0")
+            o, M, D, sM, sD = K.kda_segment_package(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                                    t["seg_start"], ckpt_interval=interval)
+            if timed:
+                mark("pkg1")
+            S_in, S_fin = K.kda_segment_scan(M, D, S0, algo=w.scan_algo)
+            if timed:
+                mark("scan1")
+            K.kda_output_fixup(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o)
+            if timed:
+                mark("fix1")
+            if interval:
+                K.kda_checkpoint_write(t["seg_start"], S_in, sM, sD, T=T, interval=interval)
+            if timed:
+                mark("ck1")
+            return o
+        main_kernel = "chunk_engine<package>"
+        rows = T // interval if interval else 0
+        nseg = len(w.seg_start) - 1
+        extra_bytes = 4 * H * (dk * dk + dk * dv) * (nseg + rows)   # M, D and rung sub-packages
+    else:
+        off = None
+        if w.ckpt_interval:
+            off = torch.from_numpy(ckpt_offsets(w.lengths, w.ckpt_interval)).to(dev)
+
+        def step(timed):
+            if timed:
+                mark("pkg0")
+            o, Sf, ck = K.kda_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"],
+                                      t["S0"], ckpt_interval=w.ckpt_interval, ckpt_offsets=off)
+            if timed:
+                mark("pkg1")
+            return o
+        main_kernel = "chunk_engine<prefill>"
+        rows = int(ckpt_offsets(w.lengths, w.ckpt_interval)[-1]) if w.ckpt_interval else 0
+        extra_bytes = 4 * H * dk * dv * (2 * w.N + rows)             # S0, S_final, checkpoints
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1000.0 * elapsed / args.steps
+
+    def avg_ms(a, b):
+        return float(np.mean([x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]))
+
+    kernel_ms = avg_ms("pkg0", "pkg1")
+    breakdown = {"main": round(kernel_ms, 4)}
+    if segmented:
+        breakdown.update(scan=round(avg_ms("pkg1", "scan1"), 4), fixup=round(avg_ms("scan1", "fix1"), 4),
+                         ckpt=round(avg_ms("fix1", "ck1"), 4))
+    alg_bytes = T * H * bytes_per_token_head(dk, dv, io_bytes) + extra_bytes
+    achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
+    flops = T * H * chunk_flops_per_token_head(64, dk, dv)
+    tok_s = T / (ms_per_step * 1e-3)
+    result = {
+        "metric": "KDA prefill tokens/s per layer (H=32, d=128) + % MI355X bf16 MFMA peak",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": T, "H": H, "dk": dk, "dv": dv, "chunk": 64,
+                   "path": "segment" if segmented else "chunked",
+                   "segments": (len(w.seg_start) - 1) if segmented else None,
+                   "scan": ("blelloch" if w.scan_algo == 1 else "sequential") if segmented else None,
+                   "sequences": w.N, "ckpt_interval": w.ckpt_interval},
+        "mfma_frac": round(flops / (ms_per_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+        "mfma_tflops_alg": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "hbm", "kernel": main_kernel, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "alg_bytes_per_launch": int(alg_bytes),
+                     "launch_ms": round(kernel_ms, 4)},
+        "breakdown_ms": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
