@@ -186,11 +186,17 @@ int kda_segment_package(const kda_config *cfg, const void *q, const void *k, con
     kda::EngineArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o_local;
     a.bounds = seg_start; a.order = nullptr; a.n_units = nseg; a.H = cfg->num_heads;
-    a.ncb_s = cfg->dv / nb; a.ncb_m = cfg->dk / nb;
     a.S_init = nullptr; a.S_out = D; a.M_out = M;
     a.interval = subs ? ckpt->interval : 0;
     a.ckpt_off = nullptr; a.ckpt_S = subs ? sub_D : nullptr; a.ckpt_M = subs ? sub_M : nullptr;
     a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;
+    // Two launches: the M blocks (which stop as soon as M is exactly zero)
+    // and the value blocks.  Mixing short and long workgroups in one grid
+    // leaves the long ones unevenly spread over the CUs.
+    a.ncb_s = 0; a.ncb_m = cfg->dk / nb;
+    hipError_t e = kda::launch_engine(kda::kModePackage, bf, cfg->dk, cfg->dv, nb, a, s);
+    if (e != hipSuccess) return launched(e, "package (M blocks)");
+    a.ncb_s = cfg->dv / nb; a.ncb_m = 0;
     return launched(kda::launch_engine(kda::kModePackage, bf, cfg->dk, cfg->dv, nb, a, s), "package");
 }
 
