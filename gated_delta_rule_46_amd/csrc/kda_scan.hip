@@ -6,27 +6,34 @@
 // Blelloch prefix scan) map a segment's incoming state to S_out = M S_in + D.
 // Composition, later after earlier: (Mb,Db) o (Ma,Da) = (Mb Ma, Mb Da + Db).
 //
-// Every product here is "out[DK x 32] = L[DK x DK] R[DK x 32] + Add" in fp32
-// on one workgroup: L staged whole in LDS, the 32-column tile of R in LDS.
-// When L is exactly zero (the usual case once a segment has forgotten its
-// incoming state) the multiply is skipped and out = Add, which is exact.
+// Every product here is "out[DK x cols] = L[DK x DK] R[DK x cols] + Add" in
+// fp32 on one workgroup: L is staged whole in LDS (and tested for being all
+// zeros on the way in), R 32 columns at a time.  A zero L -- the usual case
+// once a segment has forgotten its incoming state -- turns the product into a
+// copy of Add, which is exact.  Copies use 16-byte accesses.
 
 #include "kda_internal.h"
 
 namespace kda {
 namespace {
 
-constexpr int TC = 32;     // columns per tile
+constexpr int TC = 32;     // columns per GEMM tile
 constexpr int NTH = 256;   // threads per workgroup
 
 template <int DK> struct AffineLds {
-    static constexpr int LDL = DK + 1;
+    static constexpr int LDL = DK + 4;     // keeps 16-byte alignment of rows
     static constexpr int LDRT = TC + 1;
     static constexpr int bytes = (DK * LDL + DK * LDRT) * 4 + 64;
 };
 
-// Loads L (row-major DK x DK, leading dim DK) into LDS; returns whether any
-// element is nonzero (block-uniform).
+__device__ __forceinline__ bool nonzero4(float4 x) {
+    const uint32_t m = 0x7fffffffu;
+    return ((__builtin_bit_cast(uint32_t, x.x) & m) | (__builtin_bit_cast(uint32_t, x.y) & m) |
+            (__builtin_bit_cast(uint32_t, x.z) & m) | (__builtin_bit_cast(uint32_t, x.w) & m)) != 0u;
+}
+
+// Stages L (row-major DK x DK) into LDS; returns whether any element is nonzero
+// (block-uniform).
 template <int DK>
 __device__ bool stage_left(const float *L, float *sL, int *s_nz) {
     constexpr int LDL = AffineLds<DK>::LDL;
@@ -34,54 +41,84 @@ __device__ bool stage_left(const float *L, float *sL, int *s_nz) {
     if (t == 0) *s_nz = 0;
     __syncthreads();
     bool nz = false;
-    if (L) {
-        for (int e = t; e < DK * DK; e += NTH) {
-            const float x = L[e];
-            sL[(e / DK) * LDL + (e % DK)] = x;
-            nz |= (__builtin_bit_cast(uint32_t, x) & 0x7fffffffu) != 0u;
-        }
+    for (int e = t; e < DK * DK / 4; e += NTH) {
+        const float4 x = ((const float4 *)L)[e];
+        const int r = (e * 4) / DK, c = (e * 4) % DK;
+        *(float4 *)(sL + r * LDL + c) = x;
+        nz |= nonzero4(x);
     }
     if (nz) atomicOr(s_nz, 1);
     __syncthreads();
-    return *s_nz != 0;
+    const bool res = *s_nz != 0;
+    __syncthreads();
+    return res;
 }
 
-// out[:, 0:TC] = sL * R[:, 0:TC] + Add[:, 0:TC]   (R, Add, out row-major with
-// their own leading dims; Add may be null; R may alias out only if the caller
-// has already staged it -- R is staged into LDS before any store).
+// Block-uniform test of a DK x DK matrix for a nonzero element.
 template <int DK>
-__device__ void affine_tile(const float *sL, bool nz, const float *R, int ldr, const float *Add,
-                            int lda, float *out, int ldo, float *sR) {
+__device__ bool any_nonzero(const float *L, int *s_nz) {
+    const int t = threadIdx.x;
+    if (t == 0) *s_nz = 0;
+    __syncthreads();
+    bool nz = false;
+    for (int e = t; e < DK * DK / 4; e += NTH) nz |= nonzero4(((const float4 *)L)[e]);
+    if (nz) atomicOr(s_nz, 1);
+    __syncthreads();
+    const bool res = *s_nz != 0;
+    __syncthreads();
+    return res;
+}
+
+// out[:, 0:TC] = sL * R[:, 0:TC] + Add[:, 0:TC].  R is staged in LDS before any
+// store, so out may alias R; Add may alias out (each element is read by the
+// thread that writes it, before it writes).  Add may be null.
+template <int DK>
+__device__ void gemm_tile(const float *sL, const float *R, int ldr, const float *Add, int lda,
+                          float *out, int ldo, float *sR) {
     constexpr int LDL = AffineLds<DK>::LDL;
     constexpr int LDRT = AffineLds<DK>::LDRT;
     constexpr int TPR = NTH / DK;        // threads per row
     constexpr int CPT = TC / TPR;        // columns per thread
     const int t = threadIdx.x;
     const int r = t / TPR, c0 = (t % TPR) * CPT;
-    if (nz) {
-        for (int e = t; e < DK * TC; e += NTH) {
-            const int rr = e / TC, cc = e % TC;
-            sR[rr * LDRT + cc] = R[(int64_t)rr * ldr + cc];
-        }
+    for (int e = t; e < DK * TC; e += NTH) {
+        const int rr = e / TC, cc = e % TC;
+        sR[rr * LDRT + cc] = R[(int64_t)rr * ldr + cc];
     }
     float acc[CPT];
 #pragma unroll
     for (int j = 0; j < CPT; ++j) acc[j] = Add ? Add[(int64_t)r * lda + c0 + j] : 0.f;
     __syncthreads();
-    if (nz) {
-        for (int k = 0; k < DK; ++k) {
-            const float lv = sL[r * LDL + k];
+    for (int k = 0; k < DK; ++k) {
+        const float lv = sL[r * LDL + k];
 #pragma unroll
-            for (int j = 0; j < CPT; ++j) acc[j] = fmaf(lv, sR[k * LDRT + c0 + j], acc[j]);
-        }
+        for (int j = 0; j < CPT; ++j) acc[j] = fmaf(lv, sR[k * LDRT + c0 + j], acc[j]);
     }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < CPT; ++j) out[(int64_t)r * ldo + c0 + j] = acc[j];
 }
 
+// dst = src for a contiguous block of n floats (n % 4 == 0), or zeros if src is null.
+__device__ __forceinline__ void copy_block(float *dst, const float *src, int64_t n) {
+    for (int64_t e = threadIdx.x; e < n / 4; e += NTH)
+        ((float4 *)dst)[e] = src ? ((const float4 *)src)[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// out = L * R + Add over all `ncol` columns (row-major DK x ncol), L in sL.
+template <int DK>
+__device__ void affine_full(const float *sL, bool nz, const float *R, const float *Add, float *out,
+                            int ncol, float *sR) {
+    if (!nz) {
+        copy_block(out, Add, (int64_t)DK * ncol);
+        return;
+    }
+    for (int col = 0; col < ncol; col += TC)
+        gemm_tile<DK>(sL, R + col, ncol, Add ? Add + col : nullptr, ncol, out + col, ncol, sR);
+}
+
 // ---------------------------------------------------------------------------
-// Sequential scan: grid (H, DV/TC).  S_in[0] = S0, S_in[j+1] = M_j S_in[j] + D_j.
+// Sequential scan: one workgroup per head.  S_in[0] = S0, S_in[j+1] = M_j S_in[j] + D_j.
 // ---------------------------------------------------------------------------
 template <int DK, int DV>
 __global__ __launch_bounds__(NTH) void scan_seq_kernel(int H, int nseg, const float *M,
@@ -91,163 +128,164 @@ __global__ __launch_bounds__(NTH) void scan_seq_kernel(int H, int nseg, const fl
     float *sL = (float *)smem;
     float *sR = sL + DK * AffineLds<DK>::LDL;
     int *s_nz = (int *)(sR + DK * AffineLds<DK>::LDRT);
-    const int h = blockIdx.x, col = blockIdx.y * TC;
-    const int64_t sstride = (int64_t)DK * DV;
-    // S_in[0] = S0 (or zeros)
-    for (int e = threadIdx.x; e < DK * TC; e += NTH) {
-        const int rr = e / TC, cc = e % TC;
-        S_in[(int64_t)h * sstride + rr * DV + col + cc] = S0 ? S0[(int64_t)h * sstride + rr * DV + col + cc] : 0.f;
-    }
+    const int h = blockIdx.x;
+    const int64_t ss = (int64_t)DK * DV;
+    copy_block(S_in + (int64_t)h * ss, S0 ? S0 + (int64_t)h * ss : nullptr, ss);
     __syncthreads();
     for (int j = 0; j < nseg; ++j) {
-        const float *Mj = M + ((int64_t)j * H + h) * DK * DK;
-        const float *Dj = D + ((int64_t)j * H + h) * sstride + col;
-        const float *Sj = S_in + ((int64_t)j * H + h) * sstride + col;
-        float *dst = (j + 1 < nseg) ? S_in + ((int64_t)(j + 1) * H + h) * sstride + col
-                                    : S_final + (int64_t)h * sstride + col;
-        const bool nz = stage_left<DK>(Mj, sL, s_nz);
-        affine_tile<DK>(sL, nz, Sj, DV, Dj, DV, dst, DV, sR);
-        __threadfence_block();
+        const float *Sj = S_in + ((int64_t)j * H + h) * ss;
+        float *dst = (j + 1 < nseg) ? S_in + ((int64_t)(j + 1) * H + h) * ss : S_final + (int64_t)h * ss;
+        const bool nz = stage_left<DK>(M + ((int64_t)j * H + h) * DK * DK, sL, s_nz);
+        affine_full<DK>(sL, nz, Sj, D + ((int64_t)j * H + h) * ss, dst, DV, sR);
         __syncthreads();
     }
 }
 
 // ---------------------------------------------------------------------------
-// Blelloch scan over packages stored in the workspace:
-//   Pm [size+1][H][DK][DK], Pd [size+1][H][DK][DV]; slot `size` keeps the total.
+// Blelloch scan over packages in the workspace:
+//   Pm [size+1][H][DK][DK], Pd [size+1][H][DK][DV], Fz [size+1][H] (1 = M may
+//   be nonzero); slot `size` keeps the total.  One workgroup per (pair, head),
+//   so each pair's slots are touched by one workgroup only.
 // ---------------------------------------------------------------------------
 template <int DK, int DV>
-__global__ void blel_init_kernel(int H, int nseg, int size, const float *M, const float *D,
-                                 float *Pm, float *Pd) {
+__global__ __launch_bounds__(NTH) void blel_init_kernel(int H, int nseg, const float *M,
+                                                        const float *D, float *Pm, float *Pd,
+                                                        int *Fz) {
+    __shared__ int s_nz;
+    const int slot = blockIdx.x, h = blockIdx.y;
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
-    const int64_t totalM = (int64_t)size * H * mm, totalD = (int64_t)size * H * dd;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < totalM + totalD;
-         e += (int64_t)gridDim.x * blockDim.x) {
-        if (e < totalM) {
-            const int64_t slot = e / (H * mm);
-            const int64_t within = e % mm;
-            Pm[e] = slot < nseg ? M[e] : ((within / DK) == (within % DK) ? 1.f : 0.f);
-        } else {
-            const int64_t f = e - totalM;
-            const int64_t slot = f / (H * dd);
-            Pd[f] = slot < nseg ? D[f] : 0.f;
-        }
+    float *pm = Pm + ((int64_t)slot * H + h) * mm;
+    float *pd = Pd + ((int64_t)slot * H + h) * dd;
+    if (slot < nseg) {
+        const float *m = M + ((int64_t)slot * H + h) * mm;
+        copy_block(pm, m, mm);
+        copy_block(pd, D + ((int64_t)slot * H + h) * dd, dd);
+        const bool nz = any_nonzero<DK>(m, &s_nz);
+        if (threadIdx.x == 0) Fz[slot * H + h] = nz ? 1 : 0;
+    } else {
+        for (int e = threadIdx.x; e < mm; e += NTH) pm[e] = (e / DK == e % DK) ? 1.f : 0.f;
+        copy_block(pd, nullptr, dd);
+        if (threadIdx.x == 0) Fz[slot * H + h] = 1;
     }
 }
 
-// One level: grid (npairs, H).  Pair p touches i = (p+1)*2*step - 1 and
-// j = i - step.  Up-sweep: P[i] = P[i] o P[j].  Down-sweep: (P[j], P[i]) =
-// (P[i], P[j] o P[i]).  In both, out = Lpkg o Rpkg is written to slot i.
 template <int DK, int DV>
 __global__ __launch_bounds__(NTH) void blel_level_kernel(int H, int step, int down, float *Pm,
-                                                         float *Pd) {
+                                                         float *Pd, int *Fz) {
     extern __shared__ __align__(16) unsigned char smem[];
     float *sL = (float *)smem;
     float *sR = sL + DK * AffineLds<DK>::LDL;
     int *s_nz = (int *)(sR + DK * AffineLds<DK>::LDRT);
     const int h = blockIdx.y;
     const int64_t i = (int64_t)(blockIdx.x + 1) * 2 * step - 1, j = i - step;
-    const int64_t li = down ? j : i, ri = down ? i : j;
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
-    float *Lm = Pm + (li * H + h) * mm, *Ld = Pd + (li * H + h) * dd;
-    float *Rm = Pm + (ri * H + h) * mm, *Rd = Pd + (ri * H + h) * dd;
-    float *Om = Pm + (i * H + h) * mm, *Od = Pd + (i * H + h) * dd;
-    float *Jm = Pm + (j * H + h) * mm, *Jd = Pd + (j * H + h) * dd;
-    const bool nz = stage_left<DK>(Lm, sL, s_nz);
-    // Column tiles of the M part (no addend) and of the D part (addend L.D).
-    // Each tile's inputs are read before its outputs are written, tiles are
-    // disjoint, and L.M is already in LDS, so the in-place update is safe.
-    constexpr int LDRT = AffineLds<DK>::LDRT;
+    float *Mi = Pm + (i * H + h) * mm, *Di = Pd + (i * H + h) * dd;
+    float *Mj = Pm + (j * H + h) * mm, *Dj = Pd + (j * H + h) * dd;
+    const int fi = Fz[i * H + h], fj = Fz[j * H + h];
+    if (!down) {
+        // P[i] = P[i] o P[j] = (Mi Mj, Mi Dj + Di); unchanged when Mi == 0
+        if (!fi) return;
+        const bool nz = stage_left<DK>(Mi, sL, s_nz);
+        if (nz) {
+            for (int col = 0; col < DK; col += TC) gemm_tile<DK>(sL, Mj + col, DK, nullptr, 0, Mi + col, DK, sR);
+            for (int col = 0; col < DV; col += TC) gemm_tile<DK>(sL, Dj + col, DV, Di + col, DV, Di + col, DV, sR);
+        }
+        if (threadIdx.x == 0) Fz[i * H + h] = (nz && fj) ? 1 : 0;
+        return;
+    }
+    // down-sweep: (P[j], P[i]) = (P[i], P[j] o P[i]) with P[j] o P[i] = (Mj Mi, Mj Di + Dj)
+    const bool nz = fj ? stage_left<DK>(Mj, sL, s_nz) : false;
+    if (!nz) {
+        // Mj == 0: P[j] <- P[i]; P[i] <- (0, Dj), element by element
+        for (int64_t e = threadIdx.x; e < mm / 4; e += NTH) {
+            ((float4 *)Mj)[e] = ((const float4 *)Mi)[e];
+            ((float4 *)Mi)[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        for (int64_t e = threadIdx.x; e < dd / 4; e += NTH) {
+            const float4 a = ((const float4 *)Di)[e], b = ((const float4 *)Dj)[e];
+            ((float4 *)Dj)[e] = a;
+            ((float4 *)Di)[e] = b;
+        }
+        if (threadIdx.x == 0) { Fz[j * H + h] = fi; Fz[i * H + h] = 0; }
+        return;
+    }
+    // general case, column tile by column tile: the tile of P[i] is staged
+    // before it is overwritten, Mj is in LDS
     for (int part = 0; part < 2; ++part) {
         const int ncol = part == 0 ? DK : DV;
-        const int ld = ncol;
-        float *Rp = part == 0 ? Rm : Rd;
-        float *Op = part == 0 ? Om : Od;
-        float *Jp = part == 0 ? Jm : Jd;
-        const float *Add = part == 0 ? nullptr : Ld;
+        float *Rp = part == 0 ? Mi : Di;
+        float *Jp = part == 0 ? Mj : Dj;
         for (int col = 0; col < ncol; col += TC) {
-            // keep the old R tile (down-sweep copies it to slot j)
+            // old P[i] tile -> registers (for P[j]) and the product into P[i]
             float keep[DK * TC / NTH];
-            int kidx = 0;
-            for (int e = threadIdx.x; e < DK * TC; e += NTH) {
-                const int rr = e / TC, cc = e % TC;
-                keep[kidx++] = Rp[(int64_t)rr * ld + col + cc];
-            }
-            // stage R tile and the addend, compute, then write
-            for (int e = threadIdx.x; e < DK * TC; e += NTH) {
-                const int rr = e / TC, cc = e % TC;
-                sR[rr * LDRT + cc] = Rp[(int64_t)rr * ld + col + cc];
-            }
-            constexpr int TPR = NTH / DK, CPT = TC / TPR;
-            const int r = threadIdx.x / TPR, c0 = (threadIdx.x % TPR) * CPT;
-            float acc[CPT];
-#pragma unroll
-            for (int q = 0; q < CPT; ++q) acc[q] = Add ? Add[(int64_t)r * ld + col + c0 + q] : 0.f;
+            int kq = 0;
+            for (int e = threadIdx.x; e < DK * TC; e += NTH) keep[kq++] = Rp[(int64_t)(e / TC) * ncol + col + e % TC];
+            float addv[DK * TC / NTH];
+            kq = 0;
+            if (part == 1)
+                for (int e = threadIdx.x; e < DK * TC; e += NTH) addv[kq++] = Dj[(int64_t)(e / TC) * ncol + col + e % TC];
             __syncthreads();
-            if (nz) {
-                for (int k = 0; k < DK; ++k) {
-                    const float lv = sL[r * AffineLds<DK>::LDL + k];
-#pragma unroll
-                    for (int q = 0; q < CPT; ++q) acc[q] = fmaf(lv, sR[k * LDRT + c0 + q], acc[q]);
-                }
-            }
-            __syncthreads();
-#pragma unroll
-            for (int q = 0; q < CPT; ++q) Op[(int64_t)r * ld + col + c0 + q] = acc[q];
-            if (down) {
-                kidx = 0;
-                for (int e = threadIdx.x; e < DK * TC; e += NTH) {
-                    const int rr = e / TC, cc = e % TC;
-                    Jp[(int64_t)rr * ld + col + cc] = keep[kidx++];
-                }
+            gemm_tile<DK>(sL, Rp + col, ncol, nullptr, 0, Rp + col, ncol, sR);
+            __syncthreads();   // the product tile was written with a different thread mapping
+            // add Dj (old) to the D part, then move the old P[i] tile to P[j]
+            kq = 0;
+            for (int e = threadIdx.x; e < DK * TC; e += NTH) {
+                const int64_t idx = (int64_t)(e / TC) * ncol + col + e % TC;
+                if (part == 1) Rp[idx] += addv[kq];
+                Jp[idx] = keep[kq];
+                ++kq;
             }
             __syncthreads();
         }
     }
+    if (threadIdx.x == 0) { Fz[j * H + h] = fi; Fz[i * H + h] = fi ? 1 : 0; }
 }
 
 // After the up-sweep: slot `size` = total, slot size-1 = identity.
 template <int DK, int DV>
-__global__ void blel_root_kernel(int H, int size, float *Pm, float *Pd) {
+__global__ __launch_bounds__(NTH) void blel_root_kernel(int H, int size, float *Pm, float *Pd,
+                                                        int *Fz) {
+    const int h = blockIdx.x;
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < H * (mm + dd);
-         e += (int64_t)gridDim.x * blockDim.x) {
-        if (e < H * mm) {
-            float *src = Pm + (int64_t)(size - 1) * H * mm + e;
-            Pm[(int64_t)size * H * mm + e] = *src;
-            const int64_t within = e % mm;
-            *src = (within / DK) == (within % DK) ? 1.f : 0.f;
-        } else {
-            const int64_t f = e - H * mm;
-            float *src = Pd + (int64_t)(size - 1) * H * dd + f;
-            Pd[(int64_t)size * H * dd + f] = *src;
-            *src = 0.f;
-        }
+    float *lm = Pm + ((int64_t)(size - 1) * H + h) * mm, *ld = Pd + ((int64_t)(size - 1) * H + h) * dd;
+    float *tm = Pm + ((int64_t)size * H + h) * mm, *td = Pd + ((int64_t)size * H + h) * dd;
+    for (int64_t e = threadIdx.x; e < mm / 4; e += NTH) {
+        const float4 x = ((const float4 *)lm)[e];
+        ((float4 *)tm)[e] = x;
+        const int r = (int)((4 * e) / DK), c = (int)((4 * e) % DK);
+        ((float4 *)lm)[e] = make_float4(r == c ? 1.f : 0.f, r == c + 1 ? 1.f : 0.f,
+                                        r == c + 2 ? 1.f : 0.f, r == c + 3 ? 1.f : 0.f);
     }
+    for (int64_t e = threadIdx.x; e < dd / 4; e += NTH) {
+        ((float4 *)td)[e] = ((const float4 *)ld)[e];
+        ((float4 *)ld)[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (threadIdx.x == 0) { Fz[size * H + h] = Fz[(size - 1) * H + h]; Fz[(size - 1) * H + h] = 1; }
 }
 
 // S_in[j] = P[j].M S0 + P[j].D (j < nseg);  S_final = P[size].M S0 + P[size].D.
-// grid (nseg+1, H, DV/TC).
+// grid (nseg+1, H).
 template <int DK, int DV>
 __global__ __launch_bounds__(NTH) void blel_apply_kernel(int H, int nseg, int size, const float *Pm,
-                                                         const float *Pd, const float *S0,
-                                                         float *S_in, float *S_final) {
+                                                         const float *Pd, const int *Fz,
+                                                         const float *S0, float *S_in, float *S_final) {
     extern __shared__ __align__(16) unsigned char smem[];
     float *sL = (float *)smem;
     float *sR = sL + DK * AffineLds<DK>::LDL;
     int *s_nz = (int *)(sR + DK * AffineLds<DK>::LDRT);
-    const int jj = blockIdx.x, h = blockIdx.y, col = blockIdx.z * TC;
+    const int jj = blockIdx.x, h = blockIdx.y;
     const int slot = jj < nseg ? jj : size;
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
     const float *Lm = Pm + ((int64_t)slot * H + h) * mm;
-    const float *Ad = Pd + ((int64_t)slot * H + h) * dd + col;
-    float *out = (jj < nseg ? S_in + ((int64_t)jj * H + h) * dd : S_final + (int64_t)h * dd) + col;
-    const bool nz = S0 ? stage_left<DK>(Lm, sL, s_nz) : false;
-    affine_tile<DK>(sL, nz, S0 ? S0 + (int64_t)h * dd + col : nullptr, DV, Ad, DV, out, DV, sR);
+    const float *Ad = Pd + ((int64_t)slot * H + h) * dd;
+    float *out = jj < nseg ? S_in + ((int64_t)jj * H + h) * dd : S_final + (int64_t)h * dd;
+    const bool nz = (S0 && Fz[slot * H + h]) ? stage_left<DK>(Lm, sL, s_nz) : false;
+    affine_full<DK>(sL, nz, S0 ? S0 + (int64_t)h * dd : nullptr, Ad, out, DV, sR);
 }
 
-// Segment-path checkpoints: grid (rows, H, DV/TC).  Rung row r sits at
-// p = (r+1)*interval inside segment j (seg_start[j] < p <= seg_start[j+1]).
+// Segment-path checkpoints: grid (rows, H).  Rung row r sits at
+// p = (r+1)*interval inside segment j (seg_start[j] < p <= seg_start[j+1]):
+// states[r] = sub_M[r] S_in[j] + sub_D[r].
 template <int DK, int DV>
 __global__ __launch_bounds__(NTH) void ckpt_kernel(int H, int nseg, const int64_t *seg_start,
                                                    int interval, const float *S_in,
@@ -258,14 +296,14 @@ __global__ __launch_bounds__(NTH) void ckpt_kernel(int H, int nseg, const int64_
     float *sR = sL + DK * AffineLds<DK>::LDL;
     int *s_nz = (int *)(sR + DK * AffineLds<DK>::LDRT);
     const int64_t r = blockIdx.x;
-    const int h = blockIdx.y, col = blockIdx.z * TC;
+    const int h = blockIdx.y;
     const int64_t p = (r + 1) * interval;
     int j = 0;
     while (j + 1 < nseg && seg_start[j + 1] < p) ++j;
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
     const bool nz = stage_left<DK>(sub_M + (r * H + h) * mm, sL, s_nz);
-    affine_tile<DK>(sL, nz, S_in + ((int64_t)j * H + h) * dd + col, DV,
-                    sub_D + (r * H + h) * dd + col, DV, states + (r * H + h) * dd + col, DV, sR);
+    affine_full<DK>(sL, nz, S_in + ((int64_t)j * H + h) * dd, sub_D + (r * H + h) * dd,
+                    states + (r * H + h) * dd, DV, sR);
 }
 
 // Longest-first order of up to kPlanMax sequences (rank sort on chunk counts,
@@ -292,45 +330,51 @@ hipError_t set_lds(K kern, int bytes) {
     return hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
+int pow2_at_least(int n) {
+    int size = 1;
+    while (size < n) size *= 2;
+    return size;
+}
+
 template <int DK, int DV>
 hipError_t scan_seq_t(int H, int nseg, const float *M, const float *D, const float *S0,
                       float *S_in, float *S_final, hipStream_t s) {
     const int lds = AffineLds<DK>::bytes;
     hipError_t e = set_lds(scan_seq_kernel<DK, DV>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_seq_kernel<DK, DV>), dim3(H, DV / TC), dim3(NTH), lds, s, H, nseg,
-                       M, D, S0, S_in, S_final);
+    hipLaunchKernelGGL((scan_seq_kernel<DK, DV>), dim3(H), dim3(NTH), lds, s, H, nseg, M, D, S0,
+                       S_in, S_final);
     return hipGetLastError();
 }
 
 template <int DK, int DV>
 hipError_t scan_blel_t(int H, int nseg, const float *M, const float *D, const float *S0,
                        float *S_in, float *S_final, void *ws, hipStream_t s) {
-    int size = 1;
-    while (size < nseg) size *= 2;
+    const int size = pow2_at_least(nseg);
     float *Pm = (float *)ws;
     float *Pd = Pm + (int64_t)(size + 1) * H * DK * DK;
+    int *Fz = (int *)(Pd + (int64_t)(size + 1) * H * DK * DV);
     const int lds = AffineLds<DK>::bytes;
     hipError_t e;
-    hipLaunchKernelGGL((blel_init_kernel<DK, DV>), dim3(1024), dim3(256), 0, s, H, nseg, size, M,
-                       D, Pm, Pd);
+    hipLaunchKernelGGL((blel_init_kernel<DK, DV>), dim3(size, H), dim3(NTH), 0, s, H, nseg, M, D, Pm,
+                       Pd, Fz);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = set_lds(blel_level_kernel<DK, DV>, lds)) != hipSuccess) return e;
     for (int step = 1; step < size; step *= 2) {
         hipLaunchKernelGGL((blel_level_kernel<DK, DV>), dim3(size / (2 * step), H), dim3(NTH), lds,
-                           s, H, step, 0, Pm, Pd);
+                           s, H, step, 0, Pm, Pd, Fz);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((blel_root_kernel<DK, DV>), dim3(256), dim3(256), 0, s, H, size, Pm, Pd);
+    hipLaunchKernelGGL((blel_root_kernel<DK, DV>), dim3(H), dim3(NTH), 0, s, H, size, Pm, Pd, Fz);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     for (int step = size / 2; step >= 1; step /= 2) {
         hipLaunchKernelGGL((blel_level_kernel<DK, DV>), dim3(size / (2 * step), H), dim3(NTH), lds,
-                           s, H, step, 1, Pm, Pd);
+                           s, H, step, 1, Pm, Pd, Fz);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if ((e = set_lds(blel_apply_kernel<DK, DV>, lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL((blel_apply_kernel<DK, DV>), dim3(nseg + 1, H, DV / TC), dim3(NTH), lds, s,
-                       H, nseg, size, Pm, Pd, S0, S_in, S_final);
+    hipLaunchKernelGGL((blel_apply_kernel<DK, DV>), dim3(nseg + 1, H), dim3(NTH), lds, s, H, nseg,
+                       size, Pm, Pd, Fz, S0, S_in, S_final);
     return hipGetLastError();
 }
 
@@ -343,17 +387,17 @@ hipError_t ckpt_t(int H, int64_t T, const int64_t *seg_start, int nseg, int inte
     const int lds = AffineLds<DK>::bytes;
     hipError_t e = set_lds(ckpt_kernel<DK, DV>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((ckpt_kernel<DK, DV>), dim3((unsigned)rows, H, DV / TC), dim3(NTH), lds, s, H,
-                       nseg, seg_start, interval, S_in, sub_M, sub_D, states);
+    hipLaunchKernelGGL((ckpt_kernel<DK, DV>), dim3((unsigned)rows, H), dim3(NTH), lds, s, H, nseg,
+                       seg_start, interval, S_in, sub_M, sub_D, states);
     return hipGetLastError();
 }
 
 }  // namespace
 
 size_t blelloch_workspace(int dk, int dv, int H, int nseg) {
-    int size = 1;
-    while (size < nseg) size *= 2;
-    return (size_t)(size + 1) * H * ((size_t)dk * dk + (size_t)dk * dv) * sizeof(float);
+    const int size = pow2_at_least(nseg);
+    return (size_t)(size + 1) * H * ((size_t)dk * dk + (size_t)dk * dv) * sizeof(float) +
+           (size_t)(size + 1) * H * sizeof(int);
 }
 
 hipError_t launch_scan_sequential(int dk, int dv, int H, int nseg, const float *M, const float *D,

@@ -42,8 +42,9 @@
  *    bf16 operands for bf16 I/O and fp32 operands for fp32 I/O.
  *  - Supported shapes: dk == dv in {64, 128} for bf16, dk == dv == 64 for
  *    fp32; chunk == 64.  Other shapes return KDA_ERR_UNSUPPORTED.
- *  - Every pointer is a device pointer unless stated; every device pointer
- *    must be 16-byte aligned (KDA_ERR_ALIGN otherwise).
+ *  - Every pointer is a device pointer unless stated.  Tensors (q, k, v, g,
+ *    o, states, M, D, workspace) must be 16-byte aligned, beta 4-byte and the
+ *    int64 index arrays 8-byte aligned (KDA_ERR_ALIGN otherwise).
  *  - Ownership: the caller owns every buffer.  The library allocates no
  *    device memory and keeps none between calls; scratch comes from the
  *    caller's workspace, sized by the matching *_workspace query.
@@ -56,7 +57,7 @@
  *    16-token block must stay above about -80 (a mean alpha above ~0.007
  *    per token); beyond it intermediate exponentials leave fp32 range.
  *  - Threading: reentrant; the only process state is a per-thread error
- *    string and a cached device-attribute query.
+ *    string.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -152,7 +153,8 @@ int kda_segment_package(const kda_config *cfg, const void *q, const void *k, con
                         int32_t nseg, void *o_local, float *M, float *D, const kda_ckpt *ckpt,
                         float *sub_M, float *sub_D, void *ws, size_t ws_bytes, void *stream);
 
-/* Workspace bytes kda_segment_scan needs (0 for the sequential scan). */
+/* Workspace bytes kda_segment_scan needs (0 for the sequential scan; for the
+ * Blelloch scan the padded packages plus one flag per package). */
 size_t kda_segment_scan_workspace(const kda_config *cfg, int32_t nseg, int32_t algo);
 
 /*
