@@ -5,6 +5,10 @@
 Every .hip file under csrc/ is compiled with hipcc for gfx950 and linked into
 gated_delta_rule_46_amd/libkda.so.  Packed fp32 VALU instructions are turned
 off (-packed-fp32-ops): the kernels rely on plain fp32 arithmetic only.
+
+The device assembly of every source is emitted alongside (_build/*.s) and
+checked by isa_check: the build fails if any MFMA accumulates onto the fresh
+result of an MFMA of another shape (see isa_check for why).
 """
 from __future__ import annotations
 
@@ -37,11 +41,35 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _assemble_listing(src: str) -> str:
+    out = os.path.join(BUILD, os.path.basename(src) + ".s")
+    cmd = [HIPCC, *COMMON, "--cuda-device-only", "-S", src, "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stdout}\n{r.stderr}")
+    return out
+
+
+def check_listings(paths) -> None:
+    from .isa_check import check_file
+    bad = []
+    for p in paths:
+        bad += [(os.path.basename(p),) + h for h in check_file(p)]
+    if bad:
+        lines = "\n".join(f"  {f}:{ln} ({fn[:60]}): {a}  ->  {b}  [{d} wait states]"
+                           for (f, fn, ln, a, b, d) in bad[:20])
+        raise RuntimeError(f"{len(bad)} MFMA accumulator chain(s) switch MFMA shape:\n{lines}")
+
+
 def build_library(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with ThreadPoolExecutor(max(1, min(8, len(srcs)))) as ex:
-        objs = list(ex.map(_compile, srcs))
+    with ThreadPoolExecutor(max(1, min(8, 2 * len(srcs)))) as ex:
+        objs_f = [ex.submit(_compile, s_) for s_ in srcs]
+        lst_f = [ex.submit(_assemble_listing, s_) for s_ in srcs]
+        objs = [f.result() for f in objs_f]
+        listings = [f.result() for f in lst_f]
+    check_listings(listings)
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

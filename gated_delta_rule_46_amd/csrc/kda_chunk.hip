@@ -4,31 +4,24 @@
 // chunks of 64 tokens in order.  A unit is a sequence (prefill) or a segment
 // (package / fix-up).  The waves split into two roles that run concurrently:
 //
-//   producers (waves 0-3) prepare chunk c+1: loads (prefetched one chunk
-//     ahead), L2 norms, in-chunk cumulative log2-decay, exponentials, the
-//     Gram matrices A and P on MFMA, the diagonal 16x16 inverses of (I + A)
-//     and the block forward substitution for W;
+//   producers (waves 0-3, one per 16-row block b of the chunk) prepare chunk
+//     c+1: loads (prefetched one chunk ahead), L2 norms, in-block cumulative
+//     log2-decay, exponentials, the Gram matrices A and P on MFMA and the
+//     diagonal 16x16 inverses T_bb = (I + A_bb)^-1;
 //   consumers (waves 4-7) own a quarter of the state's columns each (fp32 MFMA
-//     accumulators) and apply chunk c: the substitution for U~, then
-//         U = U~ - W S,   O = (Q*Gam) S + P U,   S <- Diag(gamma_C) S + Kbar^T U.
+//     accumulators) and apply chunk c:
+//         U = (I + A)^-1 (beta V - R_k S)       R_k = beta K*Gam
+//         O = (Q*Gam) S + P U,   S <- Diag(gamma_C) S + Kbar^T U.
 //
-// Every wave executes the same four workgroup barriers per iteration; the
-// producer's and the consumer's phases sit between the same barriers:
-//
-//        producer (chunk c+1)                     consumer (chunk c)
-//   [B4->B1] norms, decay scan, block totals     U~ by substitution, U = U~ - W S,
-//                                                O = Qbar S + P U (stored to HBM),
-//                                                S <- gamma S + Kbar^T U
-//   [B1->B2] factors, exponentials; writes Qbar, rungs, zero test
-//            Kbar^T, beta*V, R_k; diagonal Gram
-//   [B2->B3] off-diagonal Gram, T_bb; writes     -
-//            P, -A blocks, T_bb
-//   [B3->B4] substitution; writes -W             -
-//
-// The consumers read every hand-off tile before B1 and the producers rewrite
-// them only after B1, so one copy of each tile suffices (gamma_C is
-// double-buffered by chunk parity).  Loads are prefetched one chunk ahead into
-// registers: g, k and beta at the start of [B2->B3], q and v at its end.
+// Two workgroup barriers per chunk.  Between the second barrier and the first
+// the consumers apply chunk c (reading every hand-off tile) while the
+// producers do all the work of chunk c+1 that only needs their own block:
+// norms, decay scan, exponentials, diagonal Gram blocks and T_bb.  Between the
+// first barrier and the second the producers combine the block totals into
+// the per-channel factors, write the hand-off tiles and the off-diagonal Gram
+// blocks, while the consumers store checkpoint rungs and run the zero test.
+// T_bb is written during the consumers' phase, so it is double-buffered by
+// chunk parity; every other hand-off tile has a single copy.
 //
 // Numerical scheme: one reference point per 16-row block.  The diagonal block
 // uses the block start (lhs factor <= 1, rhs factor <= e^{span of 16 tokens}),
@@ -49,8 +42,6 @@ namespace {
 
 using namespace mf;
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kEps = 1e-6f;
 constexpr int kThreads = 512;
 
 // Returns x unchanged, but hides its value from the optimiser.  Lane indices
@@ -76,23 +67,22 @@ template <int DK, int NB, bool BF> struct Lds {
     static constexpr int LDT = 16 + PAD;        // 16x16 blocks
     static constexpr int LDAD = 20;             // fp32 16x16 blocks
     static constexpr int o_flag = 0;                                  // int[16]
-    static constexpr int o_gam = 64;                                  // f32 [2][DK]
-    static constexpr int o_tot = o_gam + 2 * DK * 4;                  // f32 [4][DK]
+    static constexpr int o_gam = 64;                                  // f32 [DK]
+    static constexpr int o_tot = o_gam + DK * 4;                      // f32 [4][DK]
     static constexpr int o_fac = o_tot + 4 * DK * 4;                  // f32 [4][4][DK]
-    static constexpr int o_qbar = o_fac + 16 * DK * 4;                // hand-off
-    static constexpr int o_wneg = o_qbar + 64 * LDQ * ES;             // hand-off
-    static constexpr int o_kbt = o_wneg + 64 * LDQ * ES;              // hand-off
-    static constexpr int o_p = o_kbt + DK * LDK * ES;                 // hand-off
-    static constexpr int o_bv = o_p + 64 * LDP * ES;                  // consumer-read scratch
-    static constexpr int o_aoff = o_bv + 64 * LDV * ES;               // consumer-read scratch
-    static constexpr int o_td = o_aoff + 6 * 16 * LDT * ES;           // consumer-read scratch
-    static constexpr int o_ad = o_td + 4 * 16 * LDT * ES;             // producer scratch
+    static constexpr int o_qbar = o_fac + 16 * DK * 4;                // hand-off: Q Gam
+    static constexpr int o_rk = o_qbar + 64 * LDQ * ES;               // hand-off: -R_k
+    static constexpr int o_kbt = o_rk + 64 * LDQ * ES;                // hand-off: Kbar^T
+    static constexpr int o_p = o_kbt + DK * LDK * ES;                 // hand-off: P
+    static constexpr int o_bv = o_p + 64 * LDP * ES;                  // hand-off: beta V
+    static constexpr int o_aoff = o_bv + 64 * LDV * ES;               // hand-off: -A blocks
+    static constexpr int o_td = o_aoff + 6 * 16 * LDT * ES;           // hand-off: T_bb [2][4]
+    static constexpr int o_ad = o_td + 2 * 4 * 16 * LDT * ES;         // producer scratch
     static constexpr int o_ro = o_ad + 4 * 16 * LDAD * 4;             // producer scratch
-    static constexpr int o_rk = o_ro + 48 * LDQ * ES;                 // producer scratch
-    static constexpr int size = o_rk + 64 * LDQ * ES;
-    static_assert(o_qbar % 16 == 0 && o_wneg % 16 == 0 && o_kbt % 16 == 0 && o_p % 16 == 0 &&
+    static constexpr int size = o_ro + 48 * LDQ * ES;
+    static_assert(o_qbar % 16 == 0 && o_rk % 16 == 0 && o_kbt % 16 == 0 && o_p % 16 == 0 &&
                   o_bv % 16 == 0 && o_aoff % 16 == 0 && o_td % 16 == 0 && o_ad % 16 == 0 &&
-                  o_ro % 16 == 0 && o_rk % 16 == 0, "LDS alignment");
+                  o_ro % 16 == 0, "LDS alignment");
     static_assert(size <= 160 * 1024, "LDS budget");
 };
 
@@ -142,56 +132,34 @@ __device__ __forceinline__ void store_state(float *dst, int ld, int col0, int gq
                 dst[(int64_t)(16 * r + 4 * gq + i) * ld + col0 + 16 * n + m] = zero ? 0.f : S[r][n][i];
 }
 
-// Block forward substitution (I + A) X = R for one 16-column tile: R rows come
-// from `rhs` (row-major, leading dim ld, column col); -A off-diagonal blocks
-// and the diagonal inverses T_bb come from LDS.  X in MFMA C layout.
-template <bool BF, typename L>
-__device__ __forceinline__ void substitute(const typename Ops<BF>::T *rhs, int ld, int col,
-                                           f32x4 (&X)[4], const typename Ops<BF>::T *s_aoff,
-                                           const typename Ops<BF>::T *s_td, int m, int gq) {
-    using O = Ops<BF>;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        f32x4 Y;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Y[i] = (float)rhs[(16 * b + 4 * gq + i) * ld + col];
-#pragma unroll
-        for (int a2 = 0; a2 < b; ++a2)
-            Y = O::mma16(Y, O::ld4(s_aoff + (aoff_idx(b, a2) * 16 + m) * L::LDT + 4 * gq),
-                         O::cvt4(X[a2]));
-        X[b] = O::mma16(f32x4{0.f, 0.f, 0.f, 0.f},
-                        O::ld4(s_td + (16 * b + m) * L::LDT + 4 * gq), O::cvt4(Y));
-    }
-}
+template <int MODE, bool MB> struct Roles {
+    static constexpr bool HAS_V = (MODE != kModeFixup) && !MB;   // beta V enters U
+    static constexpr bool HAS_O = !MB;                           // outputs are produced
+    static constexpr bool CHECK0 = (MODE == kModeFixup) || MB;   // stop once S is exactly 0
+};
 
-template <int DK, int DV, int NB, bool BF, int MODE, bool MB>
-__device__ __forceinline__ void engine_body(const EngineArgs &a, unsigned char *smem, const int u,
-                                            const int h, const int cbase, const int64_t t0,
-                                            const int64_t t1) {
+// ===========================================================================
+// Producer wave for row block B of every chunk.
+// ===========================================================================
+template <int DK, int DV, int NB, bool BF, int MODE, bool MB, int B>
+__device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *smem, const int h,
+                                         const int cbase, const int64_t t0, const int64_t t1,
+                                         const int nchunks) {
     using O = Ops<BF>;
     using T = typename O::T;
     using F8 = typename O::F8;
     using L = Lds<DK, NB, BF>;
+    using R = Roles<MODE, MB>;
     constexpr int KS = DK / 32;      // 32-channel steps of a row
     constexpr int VS = NB / 32;      // 32-column steps of the value block
-    constexpr int NBW = NB / 4;      // state columns per consumer wave
-    constexpr int NTW = NBW / 16;    // state column tiles per consumer wave
-    constexpr int DKT = DK / 16;     // state row tiles
-    constexpr int WCW = DK / 4;      // W columns per producer wave
-    constexpr int WTW = WCW / 16;    // W column tiles per producer wave
     constexpr int W8 = BF ? 4 : 8;
-    constexpr bool HAS_V = (MODE != kModeFixup) && !MB;
-    constexpr bool HAS_O = !MB;
-    constexpr bool CHECK0 = (MODE == kModeFixup) || MB;
-    constexpr int LDST = MB ? DK : DV;     // leading dim of this block's global state
-    static_assert(NTW >= 1 && WTW >= 1, "tile shape");
 
     int *s_flag = (int *)(smem + L::o_flag);
     float *s_gam = (float *)(smem + L::o_gam);
     float *s_tot = (float *)(smem + L::o_tot);
     float *s_fac = (float *)(smem + L::o_fac);
     T *s_qbar = (T *)(smem + L::o_qbar);
-    T *s_wneg = (T *)(smem + L::o_wneg);
+    T *s_rk = (T *)(smem + L::o_rk);
     T *s_kbt = (T *)(smem + L::o_kbt);
     T *s_p = (T *)(smem + L::o_p);
     T *s_bv = (T *)(smem + L::o_bv);
@@ -199,348 +167,368 @@ __device__ __forceinline__ void engine_body(const EngineArgs &a, unsigned char *
     T *s_td = (T *)(smem + L::o_td);
     float *s_ad = (float *)(smem + L::o_ad);
     T *s_ro = (T *)(smem + L::o_ro);
-    T *s_rk = (T *)(smem + L::o_rk);
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, m = lane & 15, gq = lane >> 4;
-    // wave index as a scalar: the role branch below is wave-uniform
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool producer = wv < 4;
-    const int pw = wv & 3;                  // producer block / consumer column quarter
+    const int lane = threadIdx.x & 63;
     const int H = a.H;
-    const int64_t len = t1 - t0;
-    const int nchunks = (int)((len + kChunk - 1) / kChunk);
 
-    if (producer) {
-        // =====================================================================
-        // Producers: prepare chunk c+1 while the consumers apply chunk c.
-        // =====================================================================
-        const int prow = 16 * pw + m;       // this lane's row in the chunk
-        if (MODE == kModeFixup) {           // mirror the consumers' zero test
-            __syncthreads();
-            const bool any = s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3];
-            __syncthreads();
-            if (!any) return;
+    // Blocks of P right of the diagonal are zero in every chunk.
+    if (R::HAS_O) {
+        const int m = lane & 15, gq = lane >> 4;
+#pragma unroll
+        for (int a2 = B + 1; a2 < 4; ++a2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s_p[(16 * B + 4 * gq + i) * L::LDP + 16 * a2 + m] = (T)0.f;
+    }
+    // Identity selectors: an MFMA of a row-layout fragment with isel[hh]
+    // returns channels 16hh..16hh+15 of the 32-channel step transposed.
+    F8 isel[2];
+    {
+        const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            float e[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) e[j] = (8 * g + j == 16 * hh + n) ? 1.f : 0.f;
+            isel[hh] = O::cvt8(e);
         }
-        Raw<BF, KS, VS> raw;
-        bool raw_valid = false;
-        // Loads the rows of chunk c.  A row past the end of the unit is read
-        // from the unit's first row (always in bounds) and masked to zero when
-        // unpacked, so the loads need no branches and no zero-fill.
-        auto row_of = [&](int c, int prow_) -> int64_t {
-            const int64_t r0 = t0 + (int64_t)c * kChunk;
-            return (r0 + prow_) < t1 ? r0 + prow_ : t0;
-        };
-        // g, k and beta of chunk c (issued once the previous rows are consumed).
-        auto issue_loads_gk = [&](int c) {
-            const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
-            const int prow = 16 * pw + m;
-            raw_valid = (t0 + (int64_t)c * kChunk + prow) < t1;
-            const int64_t tok = row_of(c, prow);
-            const int64_t base = (tok * H + h) * DK;
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                ld_words<BF>(a.k, base + 32 * kk + 8 * gq, &raw.k[W8 * kk]);
-                ld_words<false>(a.g, base + 32 * kk + 8 * gq, &raw.g[8 * kk]);
-            }
-            raw.b = a.beta[tok * H + h];
-        };
-        // q and v of chunk c (needed from phase 2 on, so issued one phase later).
-        auto issue_loads_qv = [&](int c) {
-            const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
-            const int prow = 16 * pw + m;
-            const int64_t tok = row_of(c, prow);
-            const int64_t base = (tok * H + h) * DK;
-            if (HAS_O) {
-#pragma unroll
-                for (int kk = 0; kk < KS; ++kk) ld_words<BF>(a.q, base + 32 * kk + 8 * gq, &raw.q[W8 * kk]);
-            }
-            if (HAS_V) {
-                const int64_t vb = (tok * H + h) * DV + cbase;
-#pragma unroll
-                for (int kk = 0; kk < VS; ++kk) ld_words<BF>(a.v, vb + 32 * kk + 8 * gq, &raw.v[W8 * kk]);
-            }
-        };
+    }
 
-        float gl[KS * 8];                   // in-block cumulative log2-decay
-        float fq = 0.f, fk = 0.f, bt = 0.f;
-        F8 lhsK[KS], lhsQ[KS], rhsD[KS];   // rhsD[kk] is dead after its diagonal Gram step
-        f32x4 Ad, Pd;
+    Raw<BF, KS, VS> raw;
+    bool raw_valid = false;
+    int64_t ld_tok = t0;
+    // Rows of chunk c.  A row past the end of the unit is read from the unit's
+    // first row (always in bounds) and masked to zero when used, so the loads
+    // need no branches.
+    auto set_rows = [&](int c) {
+        const int m = opaque(lane) & 15;
+        const int64_t r = t0 + (int64_t)c * kChunk + 16 * B + m;
+        raw_valid = r < t1;
+        ld_tok = raw_valid ? r : t0;
+    };
+    auto issue_g = [&]() {
+        const int gq = opaque(lane) >> 4;
+        const int64_t base = (ld_tok * H + h) * DK;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) ld_words<false>(a.g, base + 32 * kk + 8 * gq, &raw.g[8 * kk]);
+        raw.b = a.beta[ld_tok * H + h];
+    };
+    auto issue_kq = [&]() {
+        const int gq = opaque(lane) >> 4;
+        const int64_t base = (ld_tok * H + h) * DK;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) ld_words<BF>(a.k, base + 32 * kk + 8 * gq, &raw.k[W8 * kk]);
+        if (R::HAS_O) {
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) ld_words<BF>(a.q, base + 32 * kk + 8 * gq, &raw.q[W8 * kk]);
+        }
+    };
+    auto issue_v = [&]() {
+        const int gq = opaque(lane) >> 4;
+        const int64_t vb = (ld_tok * H + h) * DV + cbase;
+#pragma unroll
+        for (int kk = 0; kk < VS; ++kk) ld_words<BF>(a.v, vb + 32 * kk + 8 * gq, &raw.v[W8 * kk]);
+    };
 
-        // [5->1]: norms and the in-block cumulative log2-decay of the rows in
-        // `raw` (kept packed), block totals to LDS.
-        auto phase1 = [&]() {
-            const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
-            const int prow = 16 * pw + m;
-            (void)prow; (void)gq;
-            // padded rows act as identity: k = q = v = 0, g = 0, beta = 0
-            const float vmask = raw_valid ? 1.f : 0.f;
-            float sq = 0.f, sk = 0.f;
+    float bt = 0.f;
+    F8 lhsK[KS], rhsD[KS], lhsQ[KS], bvp[VS];
+    f32x4 Pd;
+
+    // Own-block work of chunk c (runs while the consumers apply chunk c-1):
+    // decay scan and block totals, norms, two exponentials per element, the
+    // Gram fragments, the rhs tile R_o of later blocks, the diagonal Gram
+    // blocks and T_bb.  Issues the loads of chunk c+1 as registers free up.
+    auto phase_own = [&](int c) {
+        const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
+        const int prow = 16 * B + m;
+        const bool more = c + 1 < nchunks;
+        const bool partial = t0 + (int64_t)(c + 1) * kChunk > t1;
+        const float vm = raw_valid ? 1.f : 0.f;
+        float gl[KS * 8];
+#pragma unroll
+        for (int e = 0; e < KS * 8; ++e) gl[e] = __builtin_bit_cast(float, raw.g[e]);
+        if (partial) {   // padded rows act as identity: g = 0, k = q = v = 0, beta = 0
+#pragma unroll
+            for (int e = 0; e < KS * 8; ++e) gl[e] *= vm;
+        }
+        bt = raw.b * vm;
+#pragma unroll
+        for (int e = 0; e < KS * 8; ++e) gl[e] = scan16(gl[e] * kLog2e);
+        float fk, fq = 0.f;
+        {
+            float sk = 0.f, sq = 0.f;
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
                 float x[8];
                 unpack_words<BF>(&raw.k[W8 * kk], x);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) sk += x[j] * x[j];
-                unpack_words<false>(&raw.g[8 * kk], &gl[8 * kk]);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) gl[8 * kk + j] *= vmask;
-            }
-            bt = raw.b * vmask;
-            sk += __shfl_xor(sk, 16); sk += __shfl_xor(sk, 32);
-            fk = (a.l2norm ? rsqrtf(sk + kEps) : 1.f) * vmask;
-            (void)sq;
-#pragma unroll
-            for (int e = 0; e < KS * 8; ++e) gl[e] = scan16(gl[e] * kLog2e);
-            if (m == 15) {
-#pragma unroll
-                for (int kk = 0; kk < KS; ++kk) {
-                    float *d = s_tot + pw * DK + 32 * kk + 8 * gq;
-                    *(f32x4 *)d = f32x4{gl[8 * kk], gl[8 * kk + 1], gl[8 * kk + 2], gl[8 * kk + 3]};
-                    *(f32x4 *)(d + 4) = f32x4{gl[8 * kk + 4], gl[8 * kk + 5], gl[8 * kk + 6], gl[8 * kk + 7]};
-                }
-            }
-        };
-
-        // [1->2]: per-channel factors (once per channel), two exponentials per
-        // element, operand tiles, diagonal Gram blocks.
-        auto phase2 = [&](int cp) {
-            const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
-            const int prow = 16 * pw + m;
-            (void)prow; (void)gq;
-            // Per-channel factors of block b = pw (log2 domain, all <= 1):
-            //   f0 = e^{rho_{b-1}}            (Qbar, R_k from the block-relative factor)
-            //   f1 = e^{G_C - rho_{b-1}}      (Kbar)
-            //   f2 = e^{tot_b}                (rhs of later blocks; block 3 keeps e^{tot_2})
-            //   f3 = e^{rho_{b-1} - rho_0}    (block 2: e^{tot_1}; block 3: e^{tot_1 + tot_2})
-            // where rho_a is the cumulative decay at the end of block a.
-            float *fac = s_fac + pw * 4 * DK;
-            for (int ch = lane; ch < DK; ch += 64) {
-                const float t0_ = s_tot[ch], t1_ = s_tot[DK + ch], t2_ = s_tot[2 * DK + ch], t3_ = s_tot[3 * DK + ch];
-                const float off = (pw >= 1 ? t0_ : 0.f) + (pw >= 2 ? t1_ : 0.f) + (pw >= 3 ? t2_ : 0.f);
-                const float gc = t0_ + t1_ + t2_ + t3_;
-                const float tw = pw == 0 ? t0_ : pw == 1 ? t1_ : t2_;
-                fac[ch] = ex2(off);
-                fac[DK + ch] = ex2(gc - off);
-                fac[2 * DK + ch] = ex2(tw);
-                fac[3 * DK + ch] = ex2(pw == 2 ? t1_ : t1_ + t2_);
-                if (pw == 0) s_gam[(cp & 1) * DK + ch] = ex2(gc);
-            }
-            if (HAS_O) {
-                float sq = 0.f;
-#pragma unroll
-                for (int kk = 0; kk < KS; ++kk) {
-                    float x[8];
+                if (R::HAS_O) {
                     unpack_words<BF>(&raw.q[W8 * kk], x);
 #pragma unroll
                     for (int j = 0; j < 8; ++j) sq += x[j] * x[j];
                 }
-                sq += __shfl_xor(sq, 16); sq += __shfl_xor(sq, 32);
-                fq = (a.l2norm ? a.scale * rsqrtf(sq + kEps) : a.scale) * (raw_valid ? 1.f : 0.f);
             }
-            if (HAS_V) {
+            sk += __shfl_xor(sk, 16); sk += __shfl_xor(sk, 32);
+            fk = (a.l2norm ? rsqrtf(sk + kEps) : 1.f) * vm;
+            if (R::HAS_O) {
+                sq += __shfl_xor(sq, 16); sq += __shfl_xor(sq, 32);
+                fq = (a.l2norm ? a.scale * rsqrtf(sq + kEps) : a.scale) * vm;
+            }
+        }
+        if (R::HAS_V) {
 #pragma unroll
-                for (int kk = 0; kk < VS; ++kk) {
-                    float bv[8];
-                    unpack_words<BF>(&raw.v[W8 * kk], bv);
+            for (int kk = 0; kk < VS; ++kk) {
+                float x[8];
+                unpack_words<BF>(&raw.v[W8 * kk], x);
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) bv[j] *= bt;
-                    O::st8(s_bv + prow * L::LDV + 32 * kk + 8 * gq, bv);
+                for (int j = 0; j < 8; ++j) x[j] *= bt;
+                bvp[kk] = O::cvt8(x);
+            }
+        }
+        if (more) {
+            set_rows(c + 1);
+            issue_g();
+            if (R::HAS_V) issue_v();
+        }
+        if (m == 15) {
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                float *d = s_tot + B * DK + 32 * kk + 8 * gq;
+                *(f32x4 *)d = f32x4{gl[8 * kk], gl[8 * kk + 1], gl[8 * kk + 2], gl[8 * kk + 3]};
+                *(f32x4 *)(d + 4) = f32x4{gl[8 * kk + 4], gl[8 * kk + 5], gl[8 * kk + 6], gl[8 * kk + 7]};
+            }
+        }
+        float *fown = s_fac + B * 4 * DK;   // e^{tot_B}: rhs of later blocks
+        if (B < 3) {
+            wave_sync_lds();
+            for (int ch = opaque(lane); ch < DK; ch += 64) fown[ch] = ex2(s_tot[B * DK + ch]);
+            wave_sync_lds();
+        }
+        const float fkb = fk * bt;
+        f32x4 Ad = {0.f, 0.f, 0.f, 0.f};
+        Pd = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            const int c0 = 32 * kk + 8 * gq;
+            float e1[8], e2[8], kx[8], lk[8], rd[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) { e1[j] = ex2(gl[8 * kk + j]); e2[j] = ex2(-gl[8 * kk + j]); }
+            unpack_words<BF>(&raw.k[W8 * kk], kx);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                lk[j] = kx[j] * fkb * e1[j];
+                rd[j] = kx[j] * fk * e2[j];
+            }
+            lhsK[kk] = O::cvt8(lk);
+            rhsD[kk] = O::cvt8(rd);
+            if (B < 3) {
+                const f32x4 f0 = *(const f32x4 *)(fown + c0), f1 = *(const f32x4 *)(fown + c0 + 4);
+                float t8[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) { t8[j] = rd[j] * f0[j]; t8[j + 4] = rd[j + 4] * f1[j]; }
+                O::st8(s_ro + prow * L::LDQ + c0, t8);
+            }
+            if (R::HAS_O) {
+                float qx[8], lq[8];
+                unpack_words<BF>(&raw.q[W8 * kk], qx);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) lq[j] = qx[j] * fq * e1[j];
+                lhsQ[kk] = O::cvt8(lq);
+                Pd = O::mma32(Pd, lhsQ[kk], rhsD[kk]);
+            }
+            Ad = O::mma32(Ad, lhsK[kk], rhsD[kk]);
+            // one 32-channel step at a time keeps the fp32 temporaries short-lived
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (more) issue_kq();
+
+        // T_bb = (I + A_bb)^-1: column m by forward substitution on the lanes of
+        // group 0; row r+1 of A_bb is read while row r is being reduced.
+        float *ad = s_ad + B * 16 * L::LDAD;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ad[(4 * gq + i) * L::LDAD + m] = Ad[i];
+        wave_sync_lds();
+        if (gq == 0) {
+            float tc[16];
+            f32x4 nxt[4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) nxt[q4] = *(const f32x4 *)(ad + 4 * q4);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                f32x4 cur[4];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nxt[q4];
+                if (r < 15) {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) nxt[q4] = *(const f32x4 *)(ad + (r + 1) * L::LDAD + 4 * q4);
+                }
+                float s = (r == m) ? 1.f : 0.f;
+#pragma unroll
+                for (int i = 0; i < r; ++i) s = fmaf(-cur[i >> 2][i & 3], tc[i], s);
+                tc[r] = s;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            T *td = s_td + ((c & 1) * 4 + B) * 16 * L::LDT;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) td[r * L::LDT + m] = (T)tc[r];
+        }
+    };
+
+    // Cross-block work of chunk c (runs while the consumers store rungs):
+    // per-channel factors from the four block totals, the hand-off tiles and
+    // the off-diagonal Gram blocks (B, a2), a2 < B.
+    auto phase_cross = [&]() {
+        const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
+        const int prow = 16 * B + m;
+        // Factors of block B (log2 domain, all <= 1), rho_a = decay at the end
+        // of block a:  [0] e^{rho_{B-1}}   (Qbar, R_k)
+        //              [1] e^{G_C - rho_{B-1}}   (Kbar)
+        //              [2] e^{rho_{B-1} - rho_0}  (rhs of block 0, B >= 2)
+        //              [3] e^{rho_2 - rho_1}      (rhs of block 1, B = 3)
+        float *fac = s_fac + B * 4 * DK;
+        for (int ch = opaque(lane); ch < DK; ch += 64) {
+            const float u0 = s_tot[ch], u1 = s_tot[DK + ch], u2 = s_tot[2 * DK + ch], u3 = s_tot[3 * DK + ch];
+            const float rho = (B >= 1 ? u0 : 0.f) + (B >= 2 ? u1 : 0.f) + (B >= 3 ? u2 : 0.f);
+            const float gc = u0 + u1 + u2 + u3;
+            if (B > 0) fac[ch] = ex2(rho);
+            fac[DK + ch] = ex2(gc - rho);
+            if (B == 2) fac[2 * DK + ch] = ex2(u1);
+            if (B == 3) { fac[2 * DK + ch] = ex2(u1 + u2); fac[3 * DK + ch] = ex2(u2); }
+            if (B == 0) s_gam[ch] = ex2(gc);
+        }
+        wave_sync_lds();
+        if (R::HAS_V) {
+#pragma unroll
+            for (int kk = 0; kk < VS; ++kk) O::stf(s_bv + prow * L::LDV + 32 * kk + 8 * gq, bvp[kk]);
+        }
+        if (R::HAS_O) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                s_p[(16 * B + 4 * gq + i) * L::LDP + 16 * B + m] = (T)((m <= 4 * gq + i) ? Pd[i] : 0.f);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            const int c0 = 32 * kk + 8 * gq;
+            {   // Kbar = rd * e^{G_C - rho_{B-1}}, stored transposed via two MFMAs
+                float rd[8], kb[8];
+                O::unpack8(rhsD[kk], rd);
+                const f32x4 f0 = *(const f32x4 *)(fac + DK + c0), f1 = *(const f32x4 *)(fac + DK + c0 + 4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) { kb[j] = rd[j] * f0[j]; kb[j + 4] = rd[j + 4] * f1[j]; }
+                const F8 kbf = O::cvt8(kb);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const f32x4 tr = O::mma32(f32x4{0.f, 0.f, 0.f, 0.f}, kbf, isel[hh]);
+                    O::st4(s_kbt + (32 * kk + 16 * hh + m) * L::LDK + 16 * B + 4 * gq, tr);
                 }
             }
-            Ad = f32x4{0.f, 0.f, 0.f, 0.f};
-            Pd = f32x4{0.f, 0.f, 0.f, 0.f};
-            wave_sync_lds();
+            if (B == 0) {   // block 0 is referenced to the chunk start already
+                O::stf(s_rk + prow * L::LDQ + c0, O::neg(lhsK[kk]));
+                if (R::HAS_O) O::stf(s_qbar + prow * L::LDQ + c0, lhsQ[kk]);
+            } else {
+                const f32x4 f0 = *(const f32x4 *)(fac + c0), f1 = *(const f32x4 *)(fac + c0 + 4);
+                float x[8], t8[8];
+                O::unpack8(lhsK[kk], x);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) { t8[j] = -(x[j] * f0[j]); t8[j + 4] = -(x[j + 4] * f1[j]); }
+                O::st8(s_rk + prow * L::LDQ + c0, t8);
+                if (R::HAS_O) {
+                    O::unpack8(lhsQ[kk], x);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) { t8[j] = x[j] * f0[j]; t8[j + 4] = x[j + 4] * f1[j]; }
+                    O::st8(s_qbar + prow * L::LDQ + c0, t8);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // Off-diagonal blocks: rhs rows of block a2 are referenced to the end of
+        // a2; blocks further back are rescaled by e^{rho_{B-1} - rho_{a2}} <= 1.
+#pragma unroll
+        for (int a2 = 0; a2 < B; ++a2) {
+            f32x4 Ao = {0.f, 0.f, 0.f, 0.f}, P_ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
                 const int c0 = 32 * kk + 8 * gq;
-                float F0[8], F1[8], F2[8];
-                {
-                    const f32x4 a0 = *(const f32x4 *)(fac + c0), a1 = *(const f32x4 *)(fac + c0 + 4);
-                    const f32x4 b0 = *(const f32x4 *)(fac + DK + c0), b1 = *(const f32x4 *)(fac + DK + c0 + 4);
-                    const f32x4 d0 = *(const f32x4 *)(fac + 2 * DK + c0), d1 = *(const f32x4 *)(fac + 2 * DK + c0 + 4);
+                F8 Bf = O::ld8(s_ro + (16 * a2 + m) * L::LDQ + c0);
+                if (a2 < B - 1) {
+                    const float *fs = fac + ((B == 3 && a2 == 1) ? 3 : 2) * DK + c0;
+                    const f32x4 f0 = *(const f32x4 *)fs, f1 = *(const f32x4 *)(fs + 4);
+                    float x[8];
+                    O::unpack8(Bf, x);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        F0[j] = a0[j]; F0[j + 4] = a1[j];
-                        F1[j] = b0[j]; F1[j + 4] = b1[j];
-                        F2[j] = d0[j]; F2[j + 4] = d1[j];
-                    }
+                    for (int j = 0; j < 4; ++j) { x[j] *= f0[j]; x[j + 4] *= f1[j]; }
+                    Bf = O::cvt8(x);
                 }
-                float e1[8], e2[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) { e1[j] = ex2(gl[8 * kk + j]); e2[j] = ex2(-gl[8 * kk + j]); }
-                {   // key side: lhs (x beta) and R_k = beta K Gam; rhs, rhs of later blocks, Kbar
-                    float kx[8], lk[8], rd[8], t8[8];
-                    unpack_words<BF>(&raw.k[W8 * kk], kx);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float kq = kx[j] * fk;
-                        lk[j] = bt * kq * e1[j];
-                        rd[j] = kq * e2[j];
-                    }
-                    lhsK[kk] = O::cvt8(lk);
-                    rhsD[kk] = O::cvt8(rd);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) t8[j] = lk[j] * F0[j];
-                    O::st8(s_rk + prow * L::LDQ + c0, t8);
-                    if (pw < 3) {
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) t8[j] = rd[j] * F2[j];
-                        O::st8(s_ro + prow * L::LDQ + c0, t8);
-                    }
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) s_kbt[(c0 + j) * L::LDK + prow] = (T)(rd[j] * F1[j]);
-                }
-                if (HAS_O) {   // query side: lhs and Qbar = Q Gam
-                    float qx[8], lq[8], t8[8];
-                    unpack_words<BF>(&raw.q[W8 * kk], qx);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) lq[j] = qx[j] * fq * e1[j];
-                    lhsQ[kk] = O::cvt8(lq);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) t8[j] = lq[j] * F0[j];
-                    O::st8(s_qbar + prow * L::LDQ + c0, t8);
-                    Pd = O::mma32(Pd, lhsQ[kk], rhsD[kk]);
-                }
-                Ad = O::mma32(Ad, lhsK[kk], rhsD[kk]);
-                // one 32-channel step at a time keeps the fp32 temporaries short-lived
-                __builtin_amdgcn_sched_barrier(0);
+                Ao = O::mma32(Ao, lhsK[kk], Bf);
+                if (R::HAS_O) P_ = O::mma32(P_, lhsQ[kk], Bf);
             }
-        };
-
-        // [2->3]: off-diagonal Gram blocks and T_bb = (I + A_bb)^-1.
-        auto phase3 = [&](int cp) {
-            const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
-            const int prow = 16 * pw + m;
-            (void)prow; (void)gq;
-            // g, k and beta of this chunk are consumed: prefetch the next chunk's
-            if (cp + 1 < nchunks) issue_loads_gk(cp + 1);
-            const float *fac = s_fac + pw * 4 * DK;
+            T *dst = s_aoff + aoff_idx(B, a2) * 16 * L::LDT;
 #pragma unroll
-            for (int a2 = 0; a2 < 3; ++a2) {
-                if (a2 >= pw) break;
-                // blocks pw >= 2, a2 <= pw - 2: lhs referenced to rho_a2, i.e. the
-                // block-relative lhs times e^{rho_{pw-1} - rho_a2} <= 1 (f3, or
-                // f2 = e^{tot_2} for block 3 against block 1)
-                const bool scaled = a2 < pw - 1;
-                const float *fs = (pw == 3 && a2 == 1) ? fac + 2 * DK : fac + 3 * DK;
-                f32x4 Ao = {0.f, 0.f, 0.f, 0.f}, P_ = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < KS; ++kk) {
-                    F8 lk2 = lhsK[kk], lq2 = lhsQ[kk];
-                    if (scaled) {
-                        const int c0 = 32 * kk + 8 * gq;
-                        float x[8], y[8];
-                        O::unpack8(lhsK[kk], x);
-                        if (HAS_O) O::unpack8(lhsQ[kk], y);
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const float f = fs[c0 + j];
-                            x[j] *= f;
-                            if (HAS_O) y[j] *= f;
-                        }
-                        lk2 = O::cvt8(x);
-                        if (HAS_O) lq2 = O::cvt8(y);
-                    }
-                    const F8 B = O::ld8(s_ro + (16 * a2 + m) * L::LDQ + 32 * kk + 8 * gq);
-                    Ao = O::mma32(Ao, lk2, B);
-                    if (HAS_O) P_ = O::mma32(P_, lq2, B);
-                }
-                T *dst = s_aoff + aoff_idx(pw, a2) * 16 * L::LDT;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    dst[(4 * gq + i) * L::LDT + m] = (T)(-Ao[i]);
-                    if (HAS_O) s_p[(16 * pw + 4 * gq + i) * L::LDP + 16 * a2 + m] = (T)P_[i];
-                }
-                __builtin_amdgcn_sched_barrier(0);
+            for (int i = 0; i < 4; ++i) {
+                dst[(4 * gq + i) * L::LDT + m] = (T)(-Ao[i]);
+                if (R::HAS_O) s_p[(16 * B + 4 * gq + i) * L::LDP + 16 * a2 + m] = (T)P_[i];
             }
-            if (HAS_O) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rr = 16 * pw + 4 * gq + i;
-                    s_p[rr * L::LDP + 16 * pw + m] = (T)((m <= 4 * gq + i) ? Pd[i] : 0.f);
-                    for (int a2 = pw + 1; a2 < 4; ++a2) s_p[rr * L::LDP + 16 * a2 + m] = (T)0.f;
-                }
-            }
-
-            float *ad = s_ad + pw * 16 * L::LDAD;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ad[(4 * gq + i) * L::LDAD + m] = Ad[i];
-            wave_sync_lds();
-            if (gq == 0) {
-                // column m of T_bb by forward substitution; row r+1 of A_bb is
-                // read while row r is being reduced
-                float tc[16];
-                f32x4 nxt[4];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) nxt[q4] = *(const f32x4 *)(ad + 4 * q4);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    f32x4 cur[4];
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nxt[q4];
-                    if (r < 15) {
-#pragma unroll
-                        for (int q4 = 0; q4 < 4; ++q4) nxt[q4] = *(const f32x4 *)(ad + (r + 1) * L::LDAD + 4 * q4);
-                    }
-                    float s = (r == m) ? 1.f : 0.f;
-#pragma unroll
-                    for (int i = 0; i < r; ++i) s = fmaf(-cur[i >> 2][i & 3], tc[i], s);
-                    tc[r] = s;
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                T *td = s_td + pw * 16 * L::LDT;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) td[r * L::LDT + m] = (T)tc[r];
-            }
-            if (cp + 1 < nchunks) issue_loads_qv(cp + 1);
-        };
-
-        // [3->4]: substitution for this wave's W columns, written as -W.
-        auto phase4 = [&]() {
-            const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
-            const int prow = 16 * pw + m;
-            (void)prow; (void)gq;
-#pragma unroll
-            for (int ct = 0; ct < WTW; ++ct) {
-                f32x4 X[4];
-                substitute<BF, L>(s_rk, L::LDQ, pw * WCW + 16 * ct + m, X, s_aoff, s_td, m, gq);
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        s_wneg[(16 * b + 4 * gq + i) * L::LDQ + pw * WCW + 16 * ct + m] = (T)(-X[b][i]);
-            }
-        };
-
-        // prologue: chunk 0
-        if (nchunks > 0) { issue_loads_gk(0); issue_loads_qv(0); phase1(); }
-        __syncthreads();                                                      // B1
-        if (nchunks > 0) phase2(0);
-        __syncthreads();                                                      // B2
-        if (nchunks > 0) phase3(0);
-        __syncthreads();                                                      // B3
-        if (nchunks > 0) phase4();
-        __syncthreads();                                                      // B4
-        for (int c = 0; c < nchunks; ++c) {
-            const bool next = c + 1 < nchunks;
-            if (next) phase1();
-            __syncthreads();                                                  // B1
-            if (next) phase2(c + 1);
-            __syncthreads();                                                  // B2
-            if (CHECK0 && !(s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3])) return;
-            if (next) phase3(c + 1);
-            __syncthreads();                                                  // B3
-            if (next) phase4();
-            __syncthreads();                                                  // B4
+            __builtin_amdgcn_sched_barrier(0);
         }
-        return;
-    }
+    };
 
-    // =========================================================================
-    // Consumers: wave pw owns state columns wcol .. wcol + NBW - 1.
-    // =========================================================================
+    // prologue: chunk 0
+    if (nchunks > 0) {
+        set_rows(0);
+        issue_g();
+        issue_kq();
+        if (R::HAS_V) issue_v();
+        phase_own(0);
+    }
+    __syncthreads();                                                          // BA
+    if (nchunks > 0) phase_cross();
+    __syncthreads();                                                          // BB
+    for (int c = 0; c < nchunks; ++c) {
+        if (R::CHECK0 && c > 0 && !(s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3])) return;
+        const bool next = c + 1 < nchunks;
+        if (next) phase_own(c + 1);
+        __syncthreads();                                                      // BA
+        if (next) phase_cross();
+        __syncthreads();                                                      // BB
+    }
+}
+
+// ===========================================================================
+// Consumer wave pw: state columns cbase + pw*NB/4 .. + NB/4 - 1.
+// ===========================================================================
+template <int DK, int DV, int NB, bool BF, int MODE, bool MB>
+__device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *smem, const int u,
+                                         const int h, const int cbase, const int64_t t0,
+                                         const int64_t t1, const int nchunks, const int pw) {
+    using O = Ops<BF>;
+    using T = typename O::T;
+    using F8 = typename O::F8;
+    using F4 = typename O::F4;
+    using L = Lds<DK, NB, BF>;
+    using R = Roles<MODE, MB>;
+    constexpr int KS = DK / 32;
+    constexpr int NBW = NB / 4;      // state columns per consumer wave
+    constexpr int NTW = NBW / 16;    // state column tiles per consumer wave
+    constexpr int DKT = DK / 16;     // state row tiles
+    constexpr int LDST = MB ? DK : DV;
+    static_assert(NTW >= 1, "tile shape");
+
+    int *s_flag = (int *)(smem + L::o_flag);
+    const float *s_gam = (const float *)(smem + L::o_gam);
+    const T *s_qbar = (const T *)(smem + L::o_qbar);
+    const T *s_rk = (const T *)(smem + L::o_rk);
+    const T *s_kbt = (const T *)(smem + L::o_kbt);
+    const T *s_p = (const T *)(smem + L::o_p);
+    const T *s_bv = (const T *)(smem + L::o_bv);
+    const T *s_aoff = (const T *)(smem + L::o_aoff);
+    const T *s_td = (const T *)(smem + L::o_td);
+
+    const int lane = threadIdx.x & 63;
+    const int m = lane & 15, gq = lane >> 4;
+    const int H = a.H;
+    const int64_t len = t1 - t0;
     const int wcol = cbase + pw * NBW;
+
     f32x4 S[DKT][NTW];
     {
         const float *src = nullptr;
@@ -579,118 +567,142 @@ __device__ __forceinline__ void engine_body(const EngineArgs &a, unsigned char *
         if (!any) return;
     }
 
-    f32x4 U[4][NTW];
-    F8 Ub[2][NTW];
+    // beta V enters U through an MFMA with an identity selector: the A operand
+    // is a 32-column window of the beta V tile, isel[n] picks this wave's
+    // column tile n out of it in the MFMA output layout.
+    const int win = (pw * NBW) & ~31;
+    F8 isel[NTW];
+#pragma unroll
+    for (int n = 0; n < NTW; ++n) {
+        const int off = pw * NBW + 16 * n - win;
+        float e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = (4 * gq + (j & 3) + 16 * (j >> 2) == off + m) ? 1.f : 0.f;
+        isel[n] = O::cvt8(e);
+    }
 
-    // [5->1]: U~ = substitution on beta*V, then U = U~ - W S.
-    auto phase1 = [&]() {
+    // Applies chunk c: U, outputs, state update.
+    auto apply = [&](int c) {
         const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
-        const int wcol = cbase + pw * NBW + 0 * m;
-        (void)wcol; (void)gq;
-        f32x4 Ut[4][NTW];
-#pragma unroll
-        for (int n = 0; n < NTW; ++n) {
-            f32x4 X[4];
-            if (HAS_V) {
-                substitute<BF, L>(s_bv, L::LDV, pw * NBW + 16 * n + m, X, s_aoff, s_td, m, gq);
-            } else {
-#pragma unroll
-                for (int b = 0; b < 4; ++b) X[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-            for (int b = 0; b < 4; ++b) Ut[b][n] = X[b];
-        }
         F8 Sb[KS][NTW];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
             for (int n = 0; n < NTW; ++n) Sb[kk][n] = O::cvt44(S[2 * kk][n], S[2 * kk + 1][n]);
+        // U = beta V - R_k S
+        f32x4 U[4][NTW];
 #pragma unroll
         for (int mu = 0; mu < 4; ++mu)
 #pragma unroll
-            for (int n = 0; n < NTW; ++n) U[mu][n] = Ut[mu][n];
+            for (int n = 0; n < NTW; ++n) U[mu][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mu = 0; mu < 4; ++mu)
+        for (int mu = 0; mu < 4; ++mu) {
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
-                const T *p = s_wneg + (16 * mu + m) * L::LDQ + 32 * kk + 4 * gq;
+                const T *p = s_rk + (16 * mu + m) * L::LDQ + 32 * kk + 4 * gq;
                 const F8 Af = O::ld44(p, p + 16);
 #pragma unroll
                 for (int n = 0; n < NTW; ++n) U[mu][n] = O::mma32(U[mu][n], Af, Sb[kk][n]);
             }
+            if (R::HAS_V) {
+                const T *p = s_bv + (16 * mu + m) * L::LDV + win + 4 * gq;
+                const F8 Af = O::ld44(p, p + 16);
+#pragma unroll
+                for (int n = 0; n < NTW; ++n) U[mu][n] = O::mma32(U[mu][n], Af, isel[n]);
+            }
+        }
+        // (I + A) X = U by block forward substitution; X overwrites U.  The
+        // off-diagonal terms accumulate onto U with the same 32-deep MFMA that
+        // produced U, two 16-blocks per instruction (a zero half where a block
+        // row has an odd count): an accumulator chain must not switch MFMA
+        // opcodes, gfx950 does not order a srcC read after a different-shape
+        // MFMA that has just written it.  T_bb starts from a zero accumulator.
+        const T *td = s_td + (c & 1) * 4 * 16 * L::LDT;
+        const F4 z4 = O::cvt4(f32x4{0.f, 0.f, 0.f, 0.f});
+        auto negA = [&](int b, int a2) { return O::ld4(s_aoff + (aoff_idx(b, a2) * 16 + m) * L::LDT + 4 * gq); };
+        F4 Xb[4][NTW];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            F8 A01, A2;
+            if (b == 1) A01 = O::cat(negA(1, 0), z4);
+            if (b >= 2) A01 = O::cat(negA(b, 0), negA(b, 1));
+            if (b == 3) A2 = O::cat(negA(3, 2), z4);
+            const typename O::F4 Tf = O::ld4(td + (16 * b + m) * L::LDT + 4 * gq);
+#pragma unroll
+            for (int n = 0; n < NTW; ++n) {
+                f32x4 Y = U[b][n];
+                if (b == 1) Y = O::mma32(Y, A01, O::cat(Xb[0][n], z4));
+                if (b >= 2) Y = O::mma32(Y, A01, O::cat(Xb[0][n], Xb[1][n]));
+                if (b == 3) Y = O::mma32(Y, A2, O::cat(Xb[2][n], z4));
+                U[b][n] = O::mma16(f32x4{0.f, 0.f, 0.f, 0.f}, Tf, O::cvt4(Y));
+                Xb[b][n] = O::cvt4(U[b][n]);
+            }
+        }
+        F8 Ub[2][NTW];
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-            for (int n = 0; n < NTW; ++n) Ub[k2][n] = O::cvt44(U[2 * k2][n], U[2 * k2 + 1][n]);
-    };
+            for (int n = 0; n < NTW; ++n) Ub[k2][n] = O::cat(Xb[2 * k2][n], Xb[2 * k2 + 1][n]);
 
-    // [1->2]: O = Qbar S + P U, stored (fix-up: added) to HBM.
-    auto phase2 = [&](int c) {
-        const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
-        const int wcol = cbase + pw * NBW + 0 * m;
-        (void)wcol; (void)gq;
-        F8 Sb[KS][NTW];
+        if (R::HAS_O) {
+            // O^T = S^T Qbar^T + U^T P^T: the MFMA output then holds four
+            // consecutive columns of one token per lane (row-contiguous stores).
+            f32x4 Ot[4][NTW];
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
+            for (int mu = 0; mu < 4; ++mu)
 #pragma unroll
-            for (int n = 0; n < NTW; ++n) Sb[kk][n] = O::cvt44(S[2 * kk][n], S[2 * kk + 1][n]);
-        f32x4 Oc[4][NTW];
+                for (int n = 0; n < NTW; ++n) Ot[mu][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mu = 0; mu < 4; ++mu)
+            for (int mu = 0; mu < 4; ++mu) {
 #pragma unroll
-            for (int n = 0; n < NTW; ++n) Oc[mu][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int kk = 0; kk < KS; ++kk) {
+                    const T *p = s_qbar + (16 * mu + m) * L::LDQ + 32 * kk + 4 * gq;
+                    const F8 Bq = O::ld44(p, p + 16);
 #pragma unroll
-        for (int mu = 0; mu < 4; ++mu)
+                    for (int n = 0; n < NTW; ++n) Ot[mu][n] = O::mma32(Ot[mu][n], Sb[kk][n], Bq);
+                }
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const T *p = s_qbar + (16 * mu + m) * L::LDQ + 32 * kk + 4 * gq;
-                const F8 Af = O::ld44(p, p + 16);
+                for (int k2 = 0; k2 <= (mu >> 1); ++k2) {
+                    const T *p = s_p + (16 * mu + m) * L::LDP + 32 * k2 + 4 * gq;
+                    const F8 Bp = O::ld44(p, p + 16);
 #pragma unroll
-                for (int n = 0; n < NTW; ++n) Oc[mu][n] = O::mma32(Oc[mu][n], Af, Sb[kk][n]);
+                    for (int n = 0; n < NTW; ++n) Ot[mu][n] = O::mma32(Ot[mu][n], Ub[k2][n], Bp);
+                }
             }
+            const int64_t r0 = t0 + (int64_t)c * kChunk;
 #pragma unroll
-        for (int mu = 0; mu < 4; ++mu)
-#pragma unroll
-            for (int k2 = 0; k2 <= (mu >> 1); ++k2) {
-                const T *p = s_p + (16 * mu + m) * L::LDP + 32 * k2 + 4 * gq;
-                const F8 Af = O::ld44(p, p + 16);
-#pragma unroll
-                for (int n = 0; n < NTW; ++n) Oc[mu][n] = O::mma32(Oc[mu][n], Af, Ub[k2][n]);
-            }
-        const int64_t r0 = t0 + (int64_t)c * kChunk;
-#pragma unroll
-        for (int mu = 0; mu < 4; ++mu)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t tok = r0 + 16 * mu + 4 * gq + i;
+            for (int mu = 0; mu < 4; ++mu) {
+                const int64_t tok = r0 + 16 * mu + m;
                 if (tok < t1) {
 #pragma unroll
                     for (int n = 0; n < NTW; ++n) {
-                        const int64_t idx = (tok * H + h) * DV + wcol + 16 * n + m;
-                        float val = Oc[mu][n][i];
+                        const int64_t idx = (tok * H + h) * DV + wcol + 16 * n + 4 * gq;
+                        f32x4 val = Ot[mu][n];
                         if (BF) {
-                            bf16_t *o = (bf16_t *)a.o;
-                            if (MODE == kModeFixup) val += (float)o[idx];
-                            o[idx] = (bf16_t)val;
+                            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                            u32x2 *o = (u32x2 *)((bf16_t *)a.o + idx);
+                            if (MODE == kModeFixup) {
+                                const u32x2 w = *o;
+                                val[0] += __builtin_bit_cast(float, w[0] << 16);
+                                val[1] += __builtin_bit_cast(float, w[0] & 0xffff0000u);
+                                val[2] += __builtin_bit_cast(float, w[1] << 16);
+                                val[3] += __builtin_bit_cast(float, w[1] & 0xffff0000u);
+                            }
+                            *(bf16x4 *)o = Ops<true>::cvt4(val);
                         } else {
-                            float *o = (float *)a.o;
-                            if (MODE == kModeFixup) val += o[idx];
-                            o[idx] = val;
+                            f32x4 *o = (f32x4 *)((float *)a.o + idx);
+                            if (MODE == kModeFixup) val += *o;
+                            *o = val;
                         }
                     }
                 }
             }
-    };
+        }
 
-    // [2->3]: S <- Diag(gamma_C) S + Kbar^T U.
-    auto phase3 = [&](int c) {
-        const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
-        const int wcol = cbase + pw * NBW + 0 * m;
-        (void)wcol; (void)gq;
-        const float *gam = s_gam + (c & 1) * DK;
+        // S <- Diag(gamma_C) S + Kbar^T U
 #pragma unroll
         for (int r = 0; r < DKT; ++r) {
-            const f32x4 gm = *(const f32x4 *)(gam + 16 * r + 4 * gq);
+            const f32x4 gm = *(const f32x4 *)(s_gam + 16 * r + 4 * gq);
 #pragma unroll
             for (int n = 0; n < NTW; ++n) S[r][n] *= gm;
 #pragma unroll
@@ -703,11 +715,9 @@ __device__ __forceinline__ void engine_body(const EngineArgs &a, unsigned char *
         }
     };
 
-    // [3->4]: rung stores and the zero test after chunk c.
-    auto phase4 = [&](int c) {
+    // Rung stores and the zero test after chunk c.
+    auto rungs = [&](int c) {
         const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
-        const int wcol = cbase + pw * NBW + 0 * m;
-        (void)wcol; (void)gq;
         if (a.interval > 0) {
             if (MODE == kModePrefill && a.ckpt_S) {
                 const int64_t p = (int64_t)(c + 1) * kChunk;
@@ -725,31 +735,21 @@ __device__ __forceinline__ void engine_body(const EngineArgs &a, unsigned char *
                 }
             }
         }
-        if (CHECK0) {
+        if (R::CHECK0) {
             const bool nz = state_nonzero();
             if (lane == 0) s_flag[pw] = nz ? 1 : 0;
         }
     };
 
     // prologue: the producers prepare chunk 0
-    __syncthreads();                                                          // B1
-    __syncthreads();                                                          // B2
-    __syncthreads();                                                          // B3
-    __syncthreads();                                                          // B4
+    __syncthreads();                                                          // BA
+    __syncthreads();                                                          // BB
     for (int c = 0; c < nchunks; ++c) {
-        // [B4 -> B1]: every read of the hand-off tiles
-        phase1();
-        if (HAS_O) phase2(c);
-        phase3(c);
-        __syncthreads();                                                      // B1
-        // [B1 -> B2]: rung stores, zero test
-        phase4(c);
-        __syncthreads();                                                      // B2
-        if (CHECK0 && !(s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3])) {
-            // The state is exactly zero and stays zero.
+        if (R::CHECK0 && c > 0 && !(s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3])) {
+            // The state after chunk c-1 is exactly zero and stays zero.
             if (MB) {
                 if (a.interval > 0 && a.ckpt_M) {
-                    const int64_t first = (t0 + (int64_t)(c + 1) * kChunk) / a.interval + 1;
+                    const int64_t first = (t0 + (int64_t)c * kChunk) / a.interval + 1;
                     for (int64_t mm = first; mm * a.interval <= t1; ++mm)
                         store_state<DKT, NTW>(a.ckpt_M + ((mm - 1) * H + h) * DK * DK, DK, wcol, gq, m, S, true);
                 }
@@ -757,8 +757,10 @@ __device__ __forceinline__ void engine_body(const EngineArgs &a, unsigned char *
             }
             return;
         }
-        __syncthreads();                                                      // B3
-        __syncthreads();                                                      // B4
+        apply(c);
+        __syncthreads();                                                      // BA
+        rungs(c);
+        __syncthreads();                                                      // BB
     }
 
     if (MODE == kModePrefill && a.S_out)
@@ -766,6 +768,32 @@ __device__ __forceinline__ void engine_body(const EngineArgs &a, unsigned char *
     if (MODE == kModePackage) {
         if (MB) store_state<DKT, NTW>(a.M_out + (int64_t)(u * H + h) * DK * DK, DK, wcol, gq, m, S, false);
         else store_state<DKT, NTW>(a.S_out + (int64_t)(u * H + h) * DK * DV, DV, wcol, gq, m, S, false);
+    }
+}
+
+template <int DK, int DV, int NB, bool BF, int MODE, bool MB>
+__device__ __forceinline__ void engine_body(const EngineArgs &a, unsigned char *smem, const int u,
+                                            const int h, const int cbase, const int64_t t0,
+                                            const int64_t t1) {
+    const int nchunks = (int)((t1 - t0 + kChunk - 1) / kChunk);
+    // wave index as a scalar: the role branches below are wave-uniform
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (wv >= 4) {
+        consumer<DK, DV, NB, BF, MODE, MB>(a, smem, u, h, cbase, t0, t1, nchunks, wv - 4);
+        return;
+    }
+    if (MODE == kModeFixup) {   // mirror the consumers' test of the incoming state
+        const int *s_flag = (const int *)smem;
+        __syncthreads();
+        const bool any = s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3];
+        __syncthreads();
+        if (!any) return;
+    }
+    switch (wv) {
+        case 0: producer<DK, DV, NB, BF, MODE, MB, 0>(a, smem, h, cbase, t0, t1, nchunks); break;
+        case 1: producer<DK, DV, NB, BF, MODE, MB, 1>(a, smem, h, cbase, t0, t1, nchunks); break;
+        case 2: producer<DK, DV, NB, BF, MODE, MB, 2>(a, smem, h, cbase, t0, t1, nchunks); break;
+        default: producer<DK, DV, NB, BF, MODE, MB, 3>(a, smem, h, cbase, t0, t1, nchunks); break;
     }
 }
 

@@ -72,9 +72,24 @@ template <> struct Ops<true> {
     }
     __device__ static F4 ld4(const T *p) { return *(const F4 *)p; }
     __device__ static void st8(T *p, const float *v) { *(F8 *)p = cvt8(v); }
+    __device__ static void stf(T *p, F8 f) { *(F8 *)p = f; }
+    __device__ static void st4(T *p, f32x4 v) { *(F4 *)p = cvt4(v); }
+    // sign flip of every element (bit operation, exact)
+    __device__ static F8 neg(F8 f) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        return __builtin_bit_cast(F8, __builtin_bit_cast(u32x4, f) ^ 0x80008000u);
+    }
+    __device__ static F8 cat(F4 a, F4 b) {
+        return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
     __device__ static void unpack8(F8 f, float *out) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 w = __builtin_bit_cast(u32x4, f);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) out[j] = (float)f[j];
+        for (int j = 0; j < 4; ++j) {
+            out[2 * j] = __builtin_bit_cast(float, w[j] << 16);
+            out[2 * j + 1] = __builtin_bit_cast(float, w[j] & 0xffff0000u);
+        }
     }
     __device__ static f32x4 mma32(f32x4 c, F8 a, F8 b) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -111,6 +126,10 @@ template <> struct Ops<false> {
         *(f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
         *(f32x4 *)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
     }
+    __device__ static void stf(T *p, F8 f) { *(f32x4 *)p = f.lo; *(f32x4 *)(p + 4) = f.hi; }
+    __device__ static void st4(T *p, f32x4 v) { *(f32x4 *)p = v; }
+    __device__ static F8 neg(F8 f) { return F8{-f.lo, -f.hi}; }
+    __device__ static F8 cat(F4 a, F4 b) { return F8{a, b}; }
     __device__ static f32x4 mma32(f32x4 c, F8 a, F8 b) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[s], b.lo[s], c, 0, 0, 0);
