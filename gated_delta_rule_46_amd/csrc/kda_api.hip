@@ -145,7 +145,7 @@ int kda_prefill(const kda_config *cfg, const void *q, const void *k, const void 
     kda::EngineArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
     a.bounds = cu_seqlens; a.order = order; a.n_units = N; a.H = cfg->num_heads;
-    a.ncb_s = cfg->dv / nb; a.ncb_m = 0;
+    a.ncb = cfg->dv / nb;
     a.S_init = S0; a.S_out = S_final; a.M_out = nullptr;
     a.interval = ckpt ? ckpt->interval : 0;
     a.ckpt_off = ckpt ? ckpt->offsets : nullptr;
@@ -171,13 +171,14 @@ int kda_segment_package(const kda_config *cfg, const void *q, const void *k, con
     KDA_TRY(check_tensor(beta, "beta", true, 4));
     KDA_TRY(check_tensor(o_local, "o_local", true));
     KDA_TRY(check_tensor(seg_start, "seg_start", true, 8));
-    KDA_TRY(check_tensor(M, "M", true));
+    KDA_TRY(check_tensor(M, "M", false));
     KDA_TRY(check_tensor(D, "D", true));
     const bool subs = ckpt && (sub_M || sub_D);
     if (subs) {
         KDA_TRY(check_ckpt_interval(ckpt->interval));
-        KDA_TRY(check_tensor(sub_M, "sub_M", true));
+        KDA_TRY(check_tensor(sub_M, "sub_M", M != nullptr));
         KDA_TRY(check_tensor(sub_D, "sub_D", true));
+        if (sub_M && !M) return fail(KDA_ERR_ARG, "sub_M needs M (M is NULL)");
     }
     hipStream_t s = (hipStream_t)stream;
     const bool bf = cfg->io_dtype == KDA_DTYPE_BF16;
@@ -190,14 +191,15 @@ int kda_segment_package(const kda_config *cfg, const void *q, const void *k, con
     a.interval = subs ? ckpt->interval : 0;
     a.ckpt_off = nullptr; a.ckpt_S = subs ? sub_D : nullptr; a.ckpt_M = subs ? sub_M : nullptr;
     a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;
-    // Two launches: the M blocks (which stop as soon as M is exactly zero)
-    // and the value blocks.  Mixing short and long workgroups in one grid
-    // leaves the long ones unevenly spread over the CUs.
-    a.ncb_s = 0; a.ncb_m = cfg->dk / nb;
+    // Two launches, value blocks then M blocks (which stop as soon as M is
+    // exactly zero).  Mixing short and long workgroups in one grid leaves the
+    // long ones unevenly spread over the CUs.
+    a.ncb = cfg->dv / nb;
     hipError_t e = kda::launch_engine(kda::kModePackage, bf, cfg->dk, cfg->dv, nb, a, s);
-    if (e != hipSuccess) return launched(e, "package (M blocks)");
-    a.ncb_s = cfg->dv / nb; a.ncb_m = 0;
-    return launched(kda::launch_engine(kda::kModePackage, bf, cfg->dk, cfg->dv, nb, a, s), "package");
+    if (e != hipSuccess || !M) return launched(e, "package");
+    a.ncb = cfg->dk / nb;
+    return launched(kda::launch_engine(kda::kModePackageM, bf, cfg->dk, cfg->dv, nb, a, s),
+                    "package (M blocks)");
 }
 
 size_t kda_segment_scan_workspace(const kda_config *cfg, int32_t nseg, int32_t algo) {
@@ -251,7 +253,7 @@ int kda_output_fixup(const kda_config *cfg, const void *q, const void *k, const 
     kda::EngineArgs a{};
     a.q = q; a.k = k; a.v = nullptr; a.g = g; a.beta = beta; a.o = o;
     a.bounds = seg_start; a.order = nullptr; a.n_units = nseg; a.H = cfg->num_heads;
-    a.ncb_s = cfg->dv / nb; a.ncb_m = 0;
+    a.ncb = cfg->dv / nb;
     a.S_init = S_in; a.S_out = nullptr; a.M_out = nullptr;
     a.interval = 0; a.ckpt_off = nullptr; a.ckpt_S = nullptr; a.ckpt_M = nullptr;
     a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;

@@ -726,7 +726,7 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
                     store_state<DKT, NTW>(a.ckpt_S + (rowc * H + h) * DK * DV, DV, wcol, gq, m, S, false);
                 }
             }
-            if (MODE == kModePackage) {
+            if (MODE == kModePackage || MODE == kModePackageM) {
                 const int64_t p = t0 + (int64_t)(c + 1) * kChunk;   // sequence-relative (one sequence)
                 float *dst = MB ? a.ckpt_M : a.ckpt_S;
                 if (dst && p <= t1 && p % a.interval == 0) {
@@ -765,7 +765,7 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
 
     if (MODE == kModePrefill && a.S_out)
         store_state<DKT, NTW>(a.S_out + (int64_t)(u * H + h) * DK * DV, DV, wcol, gq, m, S, false);
-    if (MODE == kModePackage) {
+    if (MODE == kModePackage || MODE == kModePackageM) {
         if (MB) store_state<DKT, NTW>(a.M_out + (int64_t)(u * H + h) * DK * DK, DK, wcol, gq, m, S, false);
         else store_state<DKT, NTW>(a.S_out + (int64_t)(u * H + h) * DK * DV, DV, wcol, gq, m, S, false);
     }
@@ -803,7 +803,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_engine(EngineArgs a) {
     const int H = a.H;
     // Block -> (item, column block).  The column blocks of one item share
     // blockIdx mod 8, so they run on the same XCD and share its L2.
-    const int ncb = a.ncb_s + a.ncb_m;
+    const int ncb = a.ncb;
     const int bx = blockIdx.x;
     const int cb = (bx >> 3) % ncb;
     const int item = ((bx >> 3) / ncb) * 8 + (bx & 7);
@@ -812,10 +812,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_engine(EngineArgs a) {
     const int h = item - pos * H;
     const int u = a.order ? a.order[pos] : pos;
     const int64_t t0 = a.bounds[u], t1 = a.bounds[u + 1];
-    if (MODE == kModePackage && cb >= a.ncb_s)
-        engine_body<DK, DV, NB, BF, MODE, true>(a, smem, u, h, (cb - a.ncb_s) * NB, t0, t1);
-    else
-        engine_body<DK, DV, NB, BF, MODE, false>(a, smem, u, h, cb * NB, t0, t1);
+    engine_body<DK, DV, NB, BF, MODE, MODE == kModePackageM>(a, smem, u, h, cb * NB, t0, t1);
 }
 
 template <int DK, int DV, int NB, bool BF, int MODE>
@@ -825,7 +822,7 @@ hipError_t launch_one(const EngineArgs &a, hipStream_t stream) {
     hipError_t e = hipFuncSetAttribute((const void *)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, L::size);
     if (e != hipSuccess) return e;
-    const int ncb = a.ncb_s + a.ncb_m;
+    const int ncb = a.ncb;
     const int64_t items = (int64_t)a.n_units * a.H;
     const int64_t grid = ((items + 7) / 8) * 8 * ncb;
     if (grid == 0) return hipSuccess;
@@ -839,6 +836,7 @@ hipError_t launch_modes(int mode, const EngineArgs &a, hipStream_t s) {
         case kModePrefill: return launch_one<DK, DV, NB, BF, kModePrefill>(a, s);
         case kModePackage: return launch_one<DK, DV, NB, BF, kModePackage>(a, s);
         case kModeFixup: return launch_one<DK, DV, NB, BF, kModeFixup>(a, s);
+        case kModePackageM: return launch_one<DK, DV, NB, BF, kModePackageM>(a, s);
     }
     return hipErrorInvalidValue;
 }

@@ -8,7 +8,10 @@ namespace kda {
 
 constexpr int kChunk = 64;
 
-enum EngineMode : int { kModePrefill = 0, kModePackage = 1, kModeFixup = 2 };
+// Prefill: sequences from S0.  Package: value blocks of every segment from a
+// zero state (o_local, D, sub_D).  PackageM: the segment's linear part M (and
+// sub_M) from the identity.  Fixup: outputs corrected from S_in.
+enum EngineMode : int { kModePrefill = 0, kModePackage = 1, kModeFixup = 2, kModePackageM = 3 };
 
 // Arguments of the fused chunk engine (one workgroup per (unit, head,
 // column block); a unit is a sequence for prefill and a segment otherwise).
@@ -20,8 +23,7 @@ struct EngineArgs {
     const int32_t *order;        // [n_units] longest-first unit order, NULL = identity
     int32_t n_units;
     int32_t H;
-    int32_t ncb_s;               // column blocks over the value state (dv / NB)
-    int32_t ncb_m;               // column blocks over the M state (dk / NB), package only
+    int32_t ncb;                 // column blocks of the launch (dv / NB, or dk / NB for M)
     const float *S_init;         // prefill: S0 (nullable); fixup: S_in
     float *S_out;                // prefill: S_final (nullable); package: D
     float *M_out;                // package: M

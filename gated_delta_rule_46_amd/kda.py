@@ -168,26 +168,29 @@ def kda_prefill(q, k, v, g, beta, cu_seqlens, S0=None, *, want_final=True, ckpt_
 
 
 def kda_segment_package(q, k, v, g, beta, seg_start, *, ckpt_interval=0, scale=1.0,
-                        qk_l2norm=True, stream=None):
-    """Per-segment packages.  Returns (o_local, M, D, sub_M, sub_D)."""
+                        qk_l2norm=True, want_M=True, stream=None):
+    """Per-segment packages.  Returns (o_local, M, D, sub_M, sub_D); M and
+    sub_M are None when want_M is False (the M launch is then skipped)."""
     T, H, dk, dv, dev = _inputs(q, k, v, g, beta)
     nseg = seg_start.numel() - 1
     _need(seg_start, "seg_start", (nseg + 1,), torch.int64, dev)
     cfg = make_config(H, dk, dv, q.dtype, scale, qk_l2norm)
     o_local = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
-    M = torch.empty((nseg, H, dk, dk), dtype=torch.float32, device=dev)
+    M = torch.empty((nseg, H, dk, dk), dtype=torch.float32, device=dev) if want_M else None
     D = torch.empty((nseg, H, dk, dv), dtype=torch.float32, device=dev)
     sub_M = sub_D = None
     ckp = None
     if ckpt_interval:
         rows = T // ckpt_interval
-        sub_M = torch.empty((rows, H, dk, dk), dtype=torch.float32, device=dev)
+        if want_M:
+            sub_M = torch.empty((rows, H, dk, dk), dtype=torch.float32, device=dev)
         sub_D = torch.empty((rows, H, dk, dv), dtype=torch.float32, device=dev)
         if rows:
             ckp = ctypes.pointer(kda_ckpt(int(ckpt_interval), None, None))
     st = LIB.kda_segment_package(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(g), _p(beta), T,
                                  _p(seg_start), nseg, _p(o_local), _p(M), _p(D), ckp,
-                                 _p(sub_M) if ckp else None, _p(sub_D) if ckp else None,
+                                 _p(sub_M) if (ckp and want_M) else None,
+                                 _p(sub_D) if ckp else None,
                                  None, 0, _stream(stream))
     _check(st, "kda_segment_package")
     return o_local, M, D, sub_M, sub_D

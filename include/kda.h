@@ -141,11 +141,15 @@ int kda_prefill(const kda_config *cfg, const void *q, const void *k, const void 
  * Writes, for every segment j and head h:
  *   o_local [T,H,dv]  outputs of the segment computed from a zero state;
  *   M [nseg,H,dk,dk]  the segment's linear part (product of its token maps);
+ *                     M = NULL skips it (a caller whose incoming states are
+ *                     all zero, or that only needs o_local and D);
  *   D [nseg,H,dk,dv]  the segment's state when started from zero;
  *   with ckpt != NULL (states unused here) and sub_M / sub_D non-NULL, the
  *   sub-package (Pi_p, S0_p) of every rung p inside (seg_start[j],
  *   seg_start[j+1]]: the map from S_in^j to the state at p, at rung row
- *   p/interval - 1 of sub_M [rows,H,dk,dk] and sub_D [rows,H,dk,dv].
+ *   p/interval - 1 of sub_M [rows,H,dk,dk] and sub_D [rows,H,dk,dv]
+ *   (sub_M may be NULL only when M is NULL).
+ * Two kernel launches: the value blocks (o_local, D, sub_D), then the M blocks.
  * No workspace is needed (ws may be NULL).
  */
 int kda_segment_package(const kda_config *cfg, const void *q, const void *k, const void *v,

@@ -153,6 +153,9 @@ def test_segment_entry_points_validate():
     assert pk(ckpt=ctypes.byref(ck), subM=FAKE, subD=None) == K.KDA_ERR_ARG
     ck_bad = K.kda_ckpt(0, None, None)
     assert pk(ckpt=ctypes.byref(ck_bad), subM=FAKE, subD=FAKE) == K.KDA_ERR_ARG
+    ck_ok = K.kda_ckpt(64, None, None)
+    assert pk(M=None, ckpt=ctypes.byref(ck_ok), subM=FAKE, subD=FAKE) == K.KDA_ERR_ARG   # sub_M needs M
+    assert "sub_M" in last_error()
 
     sc = lambda algo, ws=None, nb=0: P.kda_segment_scan(ctypes.byref(c), 4, FAKE, FAKE, None, FAKE,
                                                         FAKE, algo, ws, nb, None)

@@ -268,6 +268,23 @@ def test_segment_single_segment_equals_prefill(K):
     assert_close("S_final vs prefill", r["S_final"], Sf[0], 1e-5)
 
 
+def test_segment_package_without_M(K):
+    say("package without M: o_local, D, sub_D identical to the full call (bf16 d=128)")
+    import torch
+    w = make_workload("t", [1024], 2, 128, 128, "bf16", 23, s0_std=None,
+                      seg_start=[0, 320, 640, 1024])
+    t = to_torch(w)
+    full = K.kda_segment_package(t["q"], t["k"], t["v"], t["g"], t["beta"], t["seg_start"],
+                                 ckpt_interval=128)
+    part = K.kda_segment_package(t["q"], t["k"], t["v"], t["g"], t["beta"], t["seg_start"],
+                                 ckpt_interval=128, want_M=False)
+    sync()
+    assert part[1] is None and part[3] is None
+    assert torch.equal(full[0], part[0])
+    assert torch.equal(full[2], part[2])
+    assert torch.equal(full[4], part[4])
+
+
 # ---------------------------------------------------------------------------
 # full-size standard workloads, sampled units
 # ---------------------------------------------------------------------------
