@@ -6,25 +6,25 @@
 // Blelloch prefix scan) map a segment's incoming state to S_out = M S_in + D.
 // Composition, later after earlier: (Mb,Db) o (Ma,Da) = (Mb Ma, Mb Da + Db).
 //
-// Every product here is "out[DK x cols] = L[DK x DK] R[DK x cols] + Add" in
-// fp32 on one workgroup: L is staged whole in LDS (and tested for being all
-// zeros on the way in), R 32 columns at a time.  A zero L -- the usual case
-// once a segment has forgotten its incoming state -- turns the product into a
-// copy of Add, which is exact.  Copies use 16-byte accesses.
+// Every product here is "out[DK x NC] = L[DK x DK] R[DK x NC] + Add" in fp32
+// by one workgroup of four waves.  A zero L -- the usual case once a segment
+// has forgotten its incoming state -- turns the product into a copy of Add,
+// which is exact; the zero test reads L once with all loads in flight.  A
+// nonzero L is multiplied on the fp32 matrix cores (v_mfma_f32_16x16x4_f32)
+// with both operands read straight from L2; wave w owns output rows
+// [w*DK/4, (w+1)*DK/4) and the whole product stays in accumulators until it
+// is stored, so the output may overwrite an operand after a barrier.  No
+// kernel here uses LDS beyond the barrier's own, so many workgroups share a
+// CU and the copies run at streaming bandwidth.
 
 #include "kda_internal.h"
 
 namespace kda {
 namespace {
 
-constexpr int TC = 32;     // columns per GEMM tile
-constexpr int NTH = 256;   // threads per workgroup
+constexpr int NTH = 256;   // threads per workgroup (four waves)
 
-template <int DK> struct AffineLds {
-    static constexpr int LDL = DK + 4;     // keeps 16-byte alignment of rows
-    static constexpr int LDRT = TC + 1;
-    static constexpr int bytes = (DK * LDL + DK * LDRT) * 4 + 64;
-};
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bool nonzero4(float4 x) {
     const uint32_t m = 0x7fffffffu;
@@ -32,89 +32,117 @@ __device__ __forceinline__ bool nonzero4(float4 x) {
             (__builtin_bit_cast(uint32_t, x.z) & m) | (__builtin_bit_cast(uint32_t, x.w) & m)) != 0u;
 }
 
-// Stages L (row-major DK x DK) into LDS; returns whether any element is nonzero
-// (block-uniform).
-template <int DK>
-__device__ bool stage_left(const float *L, float *sL, int *s_nz) {
-    constexpr int LDL = AffineLds<DK>::LDL;
-    const int t = threadIdx.x;
-    if (t == 0) *s_nz = 0;
-    __syncthreads();
+// Workgroup-uniform test of N floats (N a multiple of 4 * NTH) for a nonzero
+// element; every load is issued before the first is used.
+template <int N>
+__device__ __forceinline__ bool block_nonzero(const float *p) {
+    constexpr int PER = N / 4 / NTH;
+    static_assert(PER * 4 * NTH == N, "block size");
+    float4 x[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) x[i] = ((const float4 *)p)[threadIdx.x + i * NTH];
     bool nz = false;
-    for (int e = t; e < DK * DK / 4; e += NTH) {
-        const float4 x = ((const float4 *)L)[e];
-        const int r = (e * 4) / DK, c = (e * 4) % DK;
-        *(float4 *)(sL + r * LDL + c) = x;
-        nz |= nonzero4(x);
-    }
-    if (nz) atomicOr(s_nz, 1);
-    __syncthreads();
-    const bool res = *s_nz != 0;
-    __syncthreads();
-    return res;
-}
-
-// Block-uniform test of a DK x DK matrix for a nonzero element.
-template <int DK>
-__device__ bool any_nonzero(const float *L, int *s_nz) {
-    const int t = threadIdx.x;
-    if (t == 0) *s_nz = 0;
-    __syncthreads();
-    bool nz = false;
-    for (int e = t; e < DK * DK / 4; e += NTH) nz |= nonzero4(((const float4 *)L)[e]);
-    if (nz) atomicOr(s_nz, 1);
-    __syncthreads();
-    const bool res = *s_nz != 0;
-    __syncthreads();
-    return res;
-}
-
-// out[:, 0:TC] = sL * R[:, 0:TC] + Add[:, 0:TC].  R is staged in LDS before any
-// store, so out may alias R; Add may alias out (each element is read by the
-// thread that writes it, before it writes).  Add may be null.
-template <int DK>
-__device__ void gemm_tile(const float *sL, const float *R, int ldr, const float *Add, int lda,
-                          float *out, int ldo, float *sR) {
-    constexpr int LDL = AffineLds<DK>::LDL;
-    constexpr int LDRT = AffineLds<DK>::LDRT;
-    constexpr int TPR = NTH / DK;        // threads per row
-    constexpr int CPT = TC / TPR;        // columns per thread
-    const int t = threadIdx.x;
-    const int r = t / TPR, c0 = (t % TPR) * CPT;
-    for (int e = t; e < DK * TC; e += NTH) {
-        const int rr = e / TC, cc = e % TC;
-        sR[rr * LDRT + cc] = R[(int64_t)rr * ldr + cc];
-    }
-    float acc[CPT];
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) acc[j] = Add ? Add[(int64_t)r * lda + c0 + j] : 0.f;
-    __syncthreads();
-    for (int k = 0; k < DK; ++k) {
-        const float lv = sL[r * LDL + k];
+    for (int i = 0; i < PER; ++i) nz |= nonzero4(x[i]);
+    return __syncthreads_or(nz) != 0;
+}
+
+// dst = src over N floats (zeros when src is null), 16-byte accesses.
+template <int N>
+__device__ __forceinline__ void copy_n(float *dst, const float *src) {
+    constexpr int PER = N / 4 / NTH;
+    static_assert(PER * 4 * NTH == N, "block size");
+    float4 x[PER];
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) acc[j] = fmaf(lv, sR[k * LDRT + c0 + j], acc[j]);
+    for (int i = 0; i < PER; ++i)
+        x[i] = src ? ((const float4 *)src)[threadIdx.x + i * NTH] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) ((float4 *)dst)[threadIdx.x + i * NTH] = x[i];
+}
+
+// Accumulators of one wave's rows of a DK x NC product.
+template <int DK, int NC> struct Acc {
+    static constexpr int RT = DK / 64;     // 16-row tiles per wave
+    static constexpr int CT = NC / 16;     // 16-column tiles
+    f32x4 v[RT][CT];
+};
+
+// acc = L R (L row-major DK x DK, R row-major DK x NC), fp32 MFMA.  Lane
+// (n, g) of wave w holds rows w*DK/4 + 16 rt + 4 g + i of column 16 ct + n.
+template <int DK, int NC>
+__device__ __forceinline__ void mm_acc(const float *L, const float *R, Acc<DK, NC> &acc) {
+    constexpr int RT = Acc<DK, NC>::RT, CT = Acc<DK, NC>::CT;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int r0 = w * (DK / 4);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc.v[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // fully unrolled: the loads of later k-steps are issued while earlier
+    // MFMAs run, which hides the L2 latency of the operand reads
+#pragma unroll
+    for (int k0 = 0; k0 < DK; k0 += 4) {
+        float a[RT], b[CT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) a[rt] = L[(int64_t)(r0 + 16 * rt + n) * DK + k0 + g];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) b[ct] = R[(int64_t)(k0 + g) * NC + 16 * ct + n];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+                acc.v[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rt], b[ct], acc.v[rt][ct], 0, 0, 0);
     }
-    __syncthreads();
+}
+
+// out = acc + Add (Add may be null); each element is read and written by the
+// lane that owns it.
+template <int DK, int NC>
+__device__ __forceinline__ void store_acc(const Acc<DK, NC> &acc, const float *Add, float *out) {
+    constexpr int RT = Acc<DK, NC>::RT, CT = Acc<DK, NC>::CT;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int r0 = w * (DK / 4);
+    if (Add) {
+        float add[RT][CT][4];
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) out[(int64_t)r * ldo + c0 + j] = acc[j];
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    add[rt][ct][i] = Add[(int64_t)(r0 + 16 * rt + 4 * g + i) * NC + 16 * ct + n];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    out[(int64_t)(r0 + 16 * rt + 4 * g + i) * NC + 16 * ct + n] = acc.v[rt][ct][i] + add[rt][ct][i];
+    } else {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    out[(int64_t)(r0 + 16 * rt + 4 * g + i) * NC + 16 * ct + n] = acc.v[rt][ct][i];
+    }
 }
 
-// dst = src for a contiguous block of n floats (n % 4 == 0), or zeros if src is null.
-__device__ __forceinline__ void copy_block(float *dst, const float *src, int64_t n) {
-    for (int64_t e = threadIdx.x; e < n / 4; e += NTH)
-        ((float4 *)dst)[e] = src ? ((const float4 *)src)[e] : make_float4(0.f, 0.f, 0.f, 0.f);
-}
-
-// out = L * R + Add over all `ncol` columns (row-major DK x ncol), L in sL.
-template <int DK>
-__device__ void affine_full(const float *sL, bool nz, const float *R, const float *Add, float *out,
-                            int ncol, float *sR) {
+// out = L R + Add, or a copy of Add when L is zero (nz false).  out must not
+// alias L, R or Add.
+template <int DK, int NC>
+__device__ __forceinline__ void affine(const float *L, bool nz, const float *R, const float *Add,
+                                       float *out) {
     if (!nz) {
-        copy_block(out, Add, (int64_t)DK * ncol);
+        copy_n<DK * NC>(out, Add);
         return;
     }
-    for (int col = 0; col < ncol; col += TC)
-        gemm_tile<DK>(sL, R + col, ncol, Add ? Add + col : nullptr, ncol, out + col, ncol, sR);
+    Acc<DK, NC> acc;
+    mm_acc<DK, NC>(L, R, acc);
+    store_acc<DK, NC>(acc, Add, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -124,19 +152,16 @@ template <int DK, int DV>
 __global__ __launch_bounds__(NTH) void scan_seq_kernel(int H, int nseg, const float *M,
                                                        const float *D, const float *S0,
                                                        float *S_in, float *S_final) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    float *sL = (float *)smem;
-    float *sR = sL + DK * AffineLds<DK>::LDL;
-    int *s_nz = (int *)(sR + DK * AffineLds<DK>::LDRT);
     const int h = blockIdx.x;
-    const int64_t ss = (int64_t)DK * DV;
-    copy_block(S_in + (int64_t)h * ss, S0 ? S0 + (int64_t)h * ss : nullptr, ss);
+    const int64_t ss = (int64_t)DK * DV, mm = (int64_t)DK * DK;
+    copy_n<DK * DV>(S_in + (int64_t)h * ss, S0 ? S0 + (int64_t)h * ss : nullptr);
     __syncthreads();
     for (int j = 0; j < nseg; ++j) {
         const float *Sj = S_in + ((int64_t)j * H + h) * ss;
         float *dst = (j + 1 < nseg) ? S_in + ((int64_t)(j + 1) * H + h) * ss : S_final + (int64_t)h * ss;
-        const bool nz = stage_left<DK>(M + ((int64_t)j * H + h) * DK * DK, sL, s_nz);
-        affine_full<DK>(sL, nz, Sj, D + ((int64_t)j * H + h) * ss, dst, DV, sR);
+        const float *Mj = M + ((int64_t)j * H + h) * mm;
+        const bool nz = block_nonzero<DK * DK>(Mj);
+        affine<DK, DV>(Mj, nz, Sj, D + ((int64_t)j * H + h) * ss, dst);
         __syncthreads();
     }
 }
@@ -151,20 +176,19 @@ template <int DK, int DV>
 __global__ __launch_bounds__(NTH) void blel_init_kernel(int H, int nseg, const float *M,
                                                         const float *D, float *Pm, float *Pd,
                                                         int *Fz) {
-    __shared__ int s_nz;
     const int slot = blockIdx.x, h = blockIdx.y;
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
     float *pm = Pm + ((int64_t)slot * H + h) * mm;
     float *pd = Pd + ((int64_t)slot * H + h) * dd;
     if (slot < nseg) {
         const float *m = M + ((int64_t)slot * H + h) * mm;
-        copy_block(pm, m, mm);
-        copy_block(pd, D + ((int64_t)slot * H + h) * dd, dd);
-        const bool nz = any_nonzero<DK>(m, &s_nz);
+        const bool nz = block_nonzero<DK * DK>(m);
+        copy_n<DK * DK>(pm, m);
+        copy_n<DK * DV>(pd, D + ((int64_t)slot * H + h) * dd);
         if (threadIdx.x == 0) Fz[slot * H + h] = nz ? 1 : 0;
     } else {
-        for (int e = threadIdx.x; e < mm; e += NTH) pm[e] = (e / DK == e % DK) ? 1.f : 0.f;
-        copy_block(pd, nullptr, dd);
+        for (int e = threadIdx.x; e < DK * DK; e += NTH) pm[e] = (e / DK == e % DK) ? 1.f : 0.f;
+        copy_n<DK * DV>(pd, nullptr);
         if (threadIdx.x == 0) Fz[slot * H + h] = 1;
     }
 }
@@ -172,10 +196,6 @@ __global__ __launch_bounds__(NTH) void blel_init_kernel(int H, int nseg, const f
 template <int DK, int DV>
 __global__ __launch_bounds__(NTH) void blel_level_kernel(int H, int step, int down, float *Pm,
                                                          float *Pd, int *Fz) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    float *sL = (float *)smem;
-    float *sR = sL + DK * AffineLds<DK>::LDL;
-    int *s_nz = (int *)(sR + DK * AffineLds<DK>::LDRT);
     const int h = blockIdx.y;
     const int64_t i = (int64_t)(blockIdx.x + 1) * 2 * step - 1, j = i - step;
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
@@ -185,16 +205,21 @@ __global__ __launch_bounds__(NTH) void blel_level_kernel(int H, int step, int do
     if (!down) {
         // P[i] = P[i] o P[j] = (Mi Mj, Mi Dj + Di); unchanged when Mi == 0
         if (!fi) return;
-        const bool nz = stage_left<DK>(Mi, sL, s_nz);
+        const bool nz = block_nonzero<DK * DK>(Mi);
         if (nz) {
-            for (int col = 0; col < DK; col += TC) gemm_tile<DK>(sL, Mj + col, DK, nullptr, 0, Mi + col, DK, sR);
-            for (int col = 0; col < DV; col += TC) gemm_tile<DK>(sL, Dj + col, DV, Di + col, DV, Di + col, DV, sR);
+            Acc<DK, DK> am;
+            Acc<DK, DV> ad;
+            mm_acc<DK, DK>(Mi, Mj, am);
+            mm_acc<DK, DV>(Mi, Dj, ad);
+            __syncthreads();                       // every read of Mi precedes its overwrite
+            store_acc<DK, DK>(am, nullptr, Mi);
+            store_acc<DK, DV>(ad, Di, Di);
         }
         if (threadIdx.x == 0) Fz[i * H + h] = (nz && fj) ? 1 : 0;
         return;
     }
     // down-sweep: (P[j], P[i]) = (P[i], P[j] o P[i]) with P[j] o P[i] = (Mj Mi, Mj Di + Dj)
-    const bool nz = fj ? stage_left<DK>(Mj, sL, s_nz) : false;
+    const bool nz = fj ? block_nonzero<DK * DK>(Mj) : false;
     if (!nz) {
         // Mj == 0: P[j] <- P[i]; P[i] <- (0, Dj), element by element
         for (int64_t e = threadIdx.x; e < mm / 4; e += NTH) {
@@ -209,34 +234,38 @@ __global__ __launch_bounds__(NTH) void blel_level_kernel(int H, int step, int do
         if (threadIdx.x == 0) { Fz[j * H + h] = fi; Fz[i * H + h] = 0; }
         return;
     }
-    // general case, column tile by column tile: the tile of P[i] is staged
-    // before it is overwritten, Mj is in LDS
-    for (int part = 0; part < 2; ++part) {
-        const int ncol = part == 0 ? DK : DV;
-        float *Rp = part == 0 ? Mi : Di;
-        float *Jp = part == 0 ? Mj : Dj;
-        for (int col = 0; col < ncol; col += TC) {
-            // old P[i] tile -> registers (for P[j]) and the product into P[i]
-            float keep[DK * TC / NTH];
-            int kq = 0;
-            for (int e = threadIdx.x; e < DK * TC; e += NTH) keep[kq++] = Rp[(int64_t)(e / TC) * ncol + col + e % TC];
-            float addv[DK * TC / NTH];
-            kq = 0;
-            if (part == 1)
-                for (int e = threadIdx.x; e < DK * TC; e += NTH) addv[kq++] = Dj[(int64_t)(e / TC) * ncol + col + e % TC];
-            __syncthreads();
-            gemm_tile<DK>(sL, Rp + col, ncol, nullptr, 0, Rp + col, ncol, sR);
-            __syncthreads();   // the product tile was written with a different thread mapping
-            // add Dj (old) to the D part, then move the old P[i] tile to P[j]
-            kq = 0;
-            for (int e = threadIdx.x; e < DK * TC; e += NTH) {
-                const int64_t idx = (int64_t)(e / TC) * ncol + col + e % TC;
-                if (part == 1) Rp[idx] += addv[kq];
-                Jp[idx] = keep[kq];
-                ++kq;
-            }
-            __syncthreads();
-        }
+    // general case: both products into accumulators, then each lane moves its
+    // own elements: P[j] <- old P[i], P[i] <- (Mj Mi, Mj Di + old Dj)
+    Acc<DK, DK> am;
+    Acc<DK, DV> ad;
+    mm_acc<DK, DK>(Mj, Mi, am);
+    mm_acc<DK, DV>(Mj, Di, ad);
+    __syncthreads();
+    {
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+        const int n = lane & 15, g = lane >> 4;
+        const int r0 = w * (DK / 4);
+#pragma unroll
+        for (int rt = 0; rt < Acc<DK, DK>::RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < Acc<DK, DK>::CT; ++ct)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t e = (int64_t)(r0 + 16 * rt + 4 * g + q) * DK + 16 * ct + n;
+                    Mj[e] = Mi[e];
+                    Mi[e] = am.v[rt][ct][q];
+                }
+#pragma unroll
+        for (int rt = 0; rt < Acc<DK, DV>::RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < Acc<DK, DV>::CT; ++ct)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t e = (int64_t)(r0 + 16 * rt + 4 * g + q) * DV + 16 * ct + n;
+                    const float oj = Dj[e];
+                    Dj[e] = Di[e];
+                    Di[e] = ad.v[rt][ct][q] + oj;
+                }
     }
     if (threadIdx.x == 0) { Fz[j * H + h] = fi; Fz[i * H + h] = fi ? 1 : 0; }
 }
@@ -269,18 +298,14 @@ template <int DK, int DV>
 __global__ __launch_bounds__(NTH) void blel_apply_kernel(int H, int nseg, int size, const float *Pm,
                                                          const float *Pd, const int *Fz,
                                                          const float *S0, float *S_in, float *S_final) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    float *sL = (float *)smem;
-    float *sR = sL + DK * AffineLds<DK>::LDL;
-    int *s_nz = (int *)(sR + DK * AffineLds<DK>::LDRT);
     const int jj = blockIdx.x, h = blockIdx.y;
     const int slot = jj < nseg ? jj : size;
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
     const float *Lm = Pm + ((int64_t)slot * H + h) * mm;
     const float *Ad = Pd + ((int64_t)slot * H + h) * dd;
     float *out = jj < nseg ? S_in + ((int64_t)jj * H + h) * dd : S_final + (int64_t)h * dd;
-    const bool nz = (S0 && Fz[slot * H + h]) ? stage_left<DK>(Lm, sL, s_nz) : false;
-    affine_full<DK>(sL, nz, S0 ? S0 + (int64_t)h * dd : nullptr, Ad, out, DV, sR);
+    const bool nz = (S0 && Fz[slot * H + h]) ? block_nonzero<DK * DK>(Lm) : false;
+    affine<DK, DV>(Lm, nz, S0 ? S0 + (int64_t)h * dd : nullptr, Ad, out);
 }
 
 // Segment-path checkpoints: grid (rows, H).  Rung row r sits at
@@ -291,19 +316,16 @@ __global__ __launch_bounds__(NTH) void ckpt_kernel(int H, int nseg, const int64_
                                                    int interval, const float *S_in,
                                                    const float *sub_M, const float *sub_D,
                                                    float *states) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    float *sL = (float *)smem;
-    float *sR = sL + DK * AffineLds<DK>::LDL;
-    int *s_nz = (int *)(sR + DK * AffineLds<DK>::LDRT);
     const int64_t r = blockIdx.x;
     const int h = blockIdx.y;
     const int64_t p = (r + 1) * interval;
     int j = 0;
     while (j + 1 < nseg && seg_start[j + 1] < p) ++j;
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
-    const bool nz = stage_left<DK>(sub_M + (r * H + h) * mm, sL, s_nz);
-    affine_full<DK>(sL, nz, S_in + ((int64_t)j * H + h) * dd, sub_D + (r * H + h) * dd,
-                    states + (r * H + h) * dd, DV, sR);
+    const float *Lm = sub_M + (r * H + h) * mm;
+    const bool nz = block_nonzero<DK * DK>(Lm);
+    affine<DK, DV>(Lm, nz, S_in + ((int64_t)j * H + h) * dd, sub_D + (r * H + h) * dd,
+                   states + (r * H + h) * dd);
 }
 
 // Longest-first order of up to kPlanMax sequences (rank sort on chunk counts,
@@ -325,11 +347,6 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int64_t *cu, int n, in
     }
 }
 
-template <typename K>
-hipError_t set_lds(K kern, int bytes) {
-    return hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-}
-
 int pow2_at_least(int n) {
     int size = 1;
     while (size < n) size *= 2;
@@ -339,10 +356,7 @@ int pow2_at_least(int n) {
 template <int DK, int DV>
 hipError_t scan_seq_t(int H, int nseg, const float *M, const float *D, const float *S0,
                       float *S_in, float *S_final, hipStream_t s) {
-    const int lds = AffineLds<DK>::bytes;
-    hipError_t e = set_lds(scan_seq_kernel<DK, DV>, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_seq_kernel<DK, DV>), dim3(H), dim3(NTH), lds, s, H, nseg, M, D, S0,
+    hipLaunchKernelGGL((scan_seq_kernel<DK, DV>), dim3(H), dim3(NTH), 0, s, H, nseg, M, D, S0,
                        S_in, S_final);
     return hipGetLastError();
 }
@@ -354,26 +368,23 @@ hipError_t scan_blel_t(int H, int nseg, const float *M, const float *D, const fl
     float *Pm = (float *)ws;
     float *Pd = Pm + (int64_t)(size + 1) * H * DK * DK;
     int *Fz = (int *)(Pd + (int64_t)(size + 1) * H * DK * DV);
-    const int lds = AffineLds<DK>::bytes;
     hipError_t e;
     hipLaunchKernelGGL((blel_init_kernel<DK, DV>), dim3(size, H), dim3(NTH), 0, s, H, nseg, M, D, Pm,
                        Pd, Fz);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = set_lds(blel_level_kernel<DK, DV>, lds)) != hipSuccess) return e;
     for (int step = 1; step < size; step *= 2) {
-        hipLaunchKernelGGL((blel_level_kernel<DK, DV>), dim3(size / (2 * step), H), dim3(NTH), lds,
+        hipLaunchKernelGGL((blel_level_kernel<DK, DV>), dim3(size / (2 * step), H), dim3(NTH), 0,
                            s, H, step, 0, Pm, Pd, Fz);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipLaunchKernelGGL((blel_root_kernel<DK, DV>), dim3(H), dim3(NTH), 0, s, H, size, Pm, Pd, Fz);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     for (int step = size / 2; step >= 1; step /= 2) {
-        hipLaunchKernelGGL((blel_level_kernel<DK, DV>), dim3(size / (2 * step), H), dim3(NTH), lds,
+        hipLaunchKernelGGL((blel_level_kernel<DK, DV>), dim3(size / (2 * step), H), dim3(NTH), 0,
                            s, H, step, 1, Pm, Pd, Fz);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    if ((e = set_lds(blel_apply_kernel<DK, DV>, lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL((blel_apply_kernel<DK, DV>), dim3(nseg + 1, H), dim3(NTH), lds, s, H, nseg,
+    hipLaunchKernelGGL((blel_apply_kernel<DK, DV>), dim3(nseg + 1, H), dim3(NTH), 0, s, H, nseg,
                        size, Pm, Pd, Fz, S0, S_in, S_final);
     return hipGetLastError();
 }
@@ -384,10 +395,7 @@ hipError_t ckpt_t(int H, int64_t T, const int64_t *seg_start, int nseg, int inte
                   hipStream_t s) {
     const int64_t rows = T / interval;
     if (rows == 0) return hipSuccess;
-    const int lds = AffineLds<DK>::bytes;
-    hipError_t e = set_lds(ckpt_kernel<DK, DV>, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((ckpt_kernel<DK, DV>), dim3((unsigned)rows, H), dim3(NTH), lds, s, H, nseg,
+    hipLaunchKernelGGL((ckpt_kernel<DK, DV>), dim3((unsigned)rows, H), dim3(NTH), 0, s, H, nseg,
                        seg_start, interval, S_in, sub_M, sub_D, states);
     return hipGetLastError();
 }
