@@ -11,8 +11,9 @@ seeded synthetic tensors already resident in HBM when timing starts.
 
 Prints one JSON line with tokens/s per layer, the dominant kernel's roofline
 (algorithmic bytes over its HIP-event-timed duration against 8 TB/s HBM), the
-chunked form's algorithmic MFMA fraction, and the fp64 oracle timed on a
-bounded sample on the host cores.
+chunked form's algorithmic MFMA fraction, the fp64 oracle timed on a bounded
+sample on the host cores, and (under "decode") the one-token decode kernel on
+a 64-sequence batch against its own HBM roofline.
 """
 from __future__ import annotations
 
@@ -73,6 +74,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--decode-launches", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--roofline-launches", type=int, default=5,
@@ -122,6 +125,54 @@ def cpu_baseline(w, target_s: float) -> dict:
             "kind": "oracle",
             "sample": f"first {ntok} tokens of sequence 0, all {w.H} heads, fp64 token loop, "
                       f"{threads} threads over heads ({dt:.1f} s)"}
+
+
+def decode_measure(K, launches: int) -> dict:
+    """kda_decode on 64 sequences x 32 heads (d=128, bf16, gate logits,
+    128-slot pool with in-place rows, forks, fresh and discarded states).
+    The states touched by one call (~230 MiB) would fit in the 256 MiB
+    last-level cache, so a 1 GiB buffer is read through before every timed
+    call (a read leaves clean lines, whose eviction costs the timed call
+    nothing, and pushes the previous call's dirty states back to HBM) and
+    each call is bracketed by its own HIP events: the figure is a cold-HBM
+    one.  Algorithmic bytes: each state read and written once
+    (fp32), q, k, v, o in bf16, g and beta in fp32."""
+    import torch
+    from workloads import standard_decode_batch
+    from workloads.device import decode_to_torch
+    b = standard_decode_batch()
+    t = decode_to_torch(b)
+    n_slots = b.pool.shape[0]
+    state = 4 * b.H * b.dk * b.dv
+    nread = int(np.sum((b.read_idx >= 0) & (b.read_idx < n_slots)))
+    nwrite = int(np.sum((b.write_idx >= 0) & (b.write_idx < n_slots)))
+    alg = state * (nread + nwrite) + b.N * b.H * (2 * (2 * b.dk + 2 * b.dv) + 4 * b.dk + 4)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        K.kda_decode(t["q"], t["k"], t["v"], t["g"], t["beta"], t["pool"], t["read_idx"],
+                     t["write_idx"], gate_logits=True)
+    for _ in range(5):
+        call()
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device=t["q"].device)
+    pairs = []
+    for _ in range(launches):
+        flush.sum()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+    gbs = alg / (ms * 1e-3) / 1e9
+    return {"workload": b.name, "kernel": "decode_kernel<128,128,bf16>",
+            "tokens_per_s": round(b.N / (ms * 1e-3), 1), "launch_us": round(ms * 1e3, 2),
+            "launches_timed": launches, "cache": "1 GiB read before each timed call",
+            "alg_bytes_per_launch": int(alg),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
 def main():
@@ -259,6 +310,9 @@ def main():
                      "launch_ms": round(kernel_ms, 4), "launches_timed": args.roofline_launches},
         "breakdown_ms": breakdown,
     }
+    if not args.no_decode:
+        del t
+        result["decode"] = decode_measure(K, args.decode_launches)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -33,8 +33,9 @@ int ok() {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Shared checks of the problem description.
-int check_config(const kda_config *cfg) {
+// Shared checks of the problem description; `decode` selects the decode
+// kernel's shape set instead of the chunk engine's.
+int check_config(const kda_config *cfg, bool decode = false) {
     if (!cfg) return fail(KDA_ERR_ARG, "cfg is NULL");
     if (cfg->num_heads <= 0) return fail(KDA_ERR_ARG, "num_heads must be positive (got %d)", cfg->num_heads);
     if (cfg->io_dtype != KDA_DTYPE_F32 && cfg->io_dtype != KDA_DTYPE_BF16)
@@ -45,6 +46,12 @@ int check_config(const kda_config *cfg) {
     if (cfg->chunk != kda::kChunk)
         return fail(KDA_ERR_UNSUPPORTED, "chunk must be %d (got %d)", kda::kChunk, cfg->chunk);
     const bool bf = cfg->io_dtype == KDA_DTYPE_BF16;
+    if (decode) {
+        if (!kda::decode_supported(cfg->dk, cfg->dv))
+            return fail(KDA_ERR_UNSUPPORTED, "unsupported head dims dk=%d dv=%d for decode",
+                        cfg->dk, cfg->dv);
+        return KDA_OK;
+    }
     if (!kda::engine_supported(bf, cfg->dk, cfg->dv, 64))
         return fail(KDA_ERR_UNSUPPORTED, "unsupported head dims dk=%d dv=%d for %s I/O", cfg->dk,
                     cfg->dv, bf ? "bf16" : "fp32");
@@ -276,6 +283,38 @@ int kda_checkpoint_write(const kda_config *cfg, const kda_ckpt *ckpt, int64_t T,
     return launched(kda::launch_ckpt_write(cfg->dk, cfg->dv, cfg->num_heads, T, seg_start, nseg,
                                            ckpt->interval, S_in, sub_M, sub_D, ckpt->states,
                                            (hipStream_t)stream), "checkpoint write");
+}
+
+int kda_decode(const kda_config *cfg, int32_t N, const void *q, const void *k, const void *v,
+               const float *g, const float *beta, int32_t gate_logits,
+               const kda_state_pool *pool, void *o, void *stream) {
+    KDA_TRY(check_config(cfg, true));
+    if (N < 0) return fail(KDA_ERR_ARG, "N must be non-negative (got %d)", N);
+    if (gate_logits != 0 && gate_logits != 1)
+        return fail(KDA_ERR_ARG, "gate_logits must be 0 or 1 (got %d)", gate_logits);
+    if (!pool) return fail(KDA_ERR_ARG, "pool is NULL");
+    if (pool->n_slots <= 0)
+        return fail(KDA_ERR_ARG, "pool->n_slots must be positive (got %lld)", (long long)pool->n_slots);
+    if (N == 0) return ok();
+    if ((int64_t)N * cfg->num_heads * (cfg->dv / 64) > INT32_MAX)
+        return fail(KDA_ERR_UNSUPPORTED, "N * num_heads is too large for one launch");
+    KDA_TRY(check_tensor(q, "q", true));
+    KDA_TRY(check_tensor(k, "k", true));
+    KDA_TRY(check_tensor(v, "v", true));
+    KDA_TRY(check_tensor(g, "g", true));
+    KDA_TRY(check_tensor(beta, "beta", true, 4));
+    KDA_TRY(check_tensor(o, "o", true));
+    KDA_TRY(check_tensor(pool->states, "pool->states", true, 16));
+    KDA_TRY(check_tensor(pool->read_idx, "pool->read_idx", true, 4));
+    KDA_TRY(check_tensor(pool->write_idx, "pool->write_idx", true, 4));
+    kda::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
+    a.pool = pool->states; a.n_slots = pool->n_slots;
+    a.read_idx = pool->read_idx; a.write_idx = pool->write_idx;
+    a.N = N; a.H = cfg->num_heads; a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;
+    a.gate_logits = gate_logits;
+    return launched(kda::launch_decode(cfg->io_dtype == KDA_DTYPE_BF16, cfg->dk, cfg->dv, a,
+                                       (hipStream_t)stream), "decode");
 }
 
 }  // extern "C"

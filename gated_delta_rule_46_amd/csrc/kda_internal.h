@@ -60,4 +60,20 @@ hipError_t launch_ckpt_write(int dk, int dv, int H, int64_t T, const int64_t *se
                              int nseg, int interval, const float *S_in, const float *sub_M,
                              const float *sub_D, float *states, hipStream_t s);
 
+// One-token step against a state pool (kda_decode.hip).
+struct DecodeArgs {
+    const void *q, *k, *v;       // [N,H,dk] / [N,H,dv], io dtype
+    const float *g, *beta;       // [N,H,dk], [N,H]: gates or, with gate_logits, logits
+    void *o;                     // [N,H,dv]
+    float *pool;                 // [n_slots,H,dk,dv]
+    int64_t n_slots;
+    const int32_t *read_idx, *write_idx;   // [N]
+    int32_t N, H;
+    float scale;
+    int32_t l2norm;
+    int32_t gate_logits;
+};
+bool decode_supported(int dk, int dv);
+hipError_t launch_decode(bool bf16, int dk, int dv, const DecodeArgs &a, hipStream_t s);
+
 }  // namespace kda

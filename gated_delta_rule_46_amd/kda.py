@@ -21,7 +21,8 @@ CHUNK = 64
 
 EXPORTS = ("kda_prefill_workspace", "kda_prefill", "kda_segment_package",
            "kda_segment_scan_workspace", "kda_segment_scan", "kda_output_fixup",
-           "kda_checkpoint_write", "kda_status_string", "kda_last_error", "kda_version")
+           "kda_checkpoint_write", "kda_decode", "kda_status_string", "kda_last_error",
+           "kda_version")
 
 
 class KdaError(RuntimeError):
@@ -41,6 +42,11 @@ class kda_ckpt(ctypes.Structure):
                 ("states", ctypes.c_void_p)]
 
 
+class kda_state_pool(ctypes.Structure):
+    _fields_ = [("states", ctypes.c_void_p), ("n_slots", ctypes.c_int64),
+                ("read_idx", ctypes.c_void_p), ("write_idx", ctypes.c_void_p)]
+
+
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is missing: build it with "
@@ -48,6 +54,7 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     P, S, I32, I64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
     cfgp, ckp = ctypes.POINTER(kda_config), ctypes.POINTER(kda_ckpt)
+    poolp = ctypes.POINTER(kda_state_pool)
     sig = {
         "kda_prefill_workspace": (S, [cfgp, I64, I32]),
         "kda_prefill": (ctypes.c_int, [cfgp, P, P, P, P, P, P, I32, I64, P, P, P, ckp, P, S, P]),
@@ -57,6 +64,7 @@ def _load():
         "kda_segment_scan": (ctypes.c_int, [cfgp, I32, P, P, P, P, P, I32, P, S, P]),
         "kda_output_fixup": (ctypes.c_int, [cfgp, P, P, P, P, I64, P, I32, P, P, P, S, P]),
         "kda_checkpoint_write": (ctypes.c_int, [cfgp, ckp, I64, P, I32, P, P, P, P]),
+        "kda_decode": (ctypes.c_int, [cfgp, I32, P, P, P, P, P, I32, poolp, P, P]),
         "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "kda_last_error": (ctypes.c_char_p, []),
         "kda_version": (ctypes.c_char_p, []),
@@ -271,3 +279,28 @@ def kda_segment_prefill(q, k, v, g, beta, seg_start, S0=None, *, algo=KDA_SCAN_B
         ck = kda_checkpoint_write(seg_start, S_in, sub_M, sub_D, T=q.shape[0],
                                   interval=ckpt_interval, dtype=q.dtype, stream=stream)
     return o, S_final, ck
+
+
+def kda_decode(q, k, v, g, beta, pool, read_idx, write_idx, *, gate_logits=False, scale=1.0,
+               qk_l2norm=True, out=None, stream=None):
+    """One decode step for N sequences (row n of q, k, v, g, beta).
+
+    pool: fp32 [n_slots,H,dk,dv] states, updated in place at write_idx;
+    read_idx / write_idx: int32 [N] device tensors (negative = zero state /
+    not written).  gate_logits: g and beta are logits activated in the kernel.
+    Returns o [N,H,dv].
+    """
+    N, H, dk, dv, dev = _inputs(q, k, v, g, beta)
+    n_slots = pool.shape[0]
+    _need(pool, "pool", (n_slots, H, dk, dv), torch.float32, dev)
+    _need(read_idx, "read_idx", (N,), torch.int32, dev)
+    _need(write_idx, "write_idx", (N,), torch.int32, dev)
+    cfg = make_config(H, dk, dv, q.dtype, scale, qk_l2norm)
+    o = out if out is not None else torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    _need(o, "out", (N, H, dv), q.dtype, dev)
+    pl = kda_state_pool(ctypes.c_void_p(pool.data_ptr()), n_slots, ctypes.c_void_p(read_idx.data_ptr()),
+                        ctypes.c_void_p(write_idx.data_ptr()))
+    st = LIB.kda_decode(ctypes.byref(cfg), N, _p(q), _p(k), _p(v), _p(g), _p(beta),
+                        int(bool(gate_logits)), ctypes.byref(pl), _p(o), _stream(stream))
+    _check(st, "kda_decode")
+    return o

@@ -32,6 +32,12 @@
  *    are first computed from a zero state (o_local) and then corrected from
  *    its incoming state S_in^j.  All segments run as parallel work on one GPU.
  *
+ *  - Decode (kda_decode): one new token per sequence against a pool of
+ *    states addressed by read and write slots (ROCm/ATOM PR #2709, review
+ *    notes: the fused sigmoid-gated delta-rule update takes a read-side state
+ *    index beside the write table, so a forked request resumes a shared
+ *    prefix state), with the gate activations optionally fused.
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Layouts (row-major, contiguous): q, k, g [T,H,dk]; v, o [T,H,dv];
@@ -106,6 +112,24 @@ typedef struct {
     const int64_t *offsets;
     float *states;
 } kda_ckpt;
+
+/*
+ * A pool of fp32 states [n_slots, H, dk, dv] addressed per sequence by slot.
+ * read_idx[n] is the slot holding sequence n's state before its new tokens
+ * (an index < 0 or >= n_slots means a zero state); write_idx[n] is the slot
+ * that receives its state after them (< 0 or >= n_slots: not written).
+ * read_idx[n] == write_idx[n] updates the slot in place; two different slots
+ * fork the state and leave the read slot as it was.  A call's write slots must
+ * differ from one another and from every other sequence's read slot, and
+ * calls that overlap on one pool race.  Both index arrays are device int32
+ * [N]; out-of-range indices are treated as above, never dereferenced.
+ */
+typedef struct {
+    float *states;
+    int64_t n_slots;
+    const int32_t *read_idx;
+    const int32_t *write_idx;
+} kda_state_pool;
 
 /* ------------------------------------------------------------------------ */
 /* Chunked prefill                                                           */
@@ -193,6 +217,25 @@ int kda_output_fixup(const kda_config *cfg, const void *q, const void *k, const 
 int kda_checkpoint_write(const kda_config *cfg, const kda_ckpt *ckpt, int64_t T,
                          const int64_t *seg_start, int32_t nseg, const float *S_in,
                          const float *sub_M, const float *sub_D, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Decode                                                                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * One decode step: sequence n takes one new token, row n of
+ *   q, k [N,H,dk], v [N,H,dv] (io_dtype); g [N,H,dk], beta [N,H] (fp32);
+ * gate_logits 0: g is log alpha and beta is beta, as in prefill;
+ *             1: both are logits, activated in the kernel as
+ *                log alpha = -softplus(g) and beta = sigmoid(beta);
+ * pool: the states read and written as described at kda_state_pool;
+ * o [N,H,dv] (io_dtype): o_n = S_n^T q_n with the updated state.
+ * Shapes: dk, dv in {64, 128}, for either io_dtype.  N = 0 is a no-op.
+ * No workspace.  One kernel launch.
+ */
+int kda_decode(const kda_config *cfg, int32_t N, const void *q, const void *k, const void *v,
+               const float *g, const float *beta, int32_t gate_logits,
+               const kda_state_pool *pool, void *o, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Diagnostics                                                               */

@@ -12,6 +12,12 @@ and never imports it.
   written from its definition with numpy matmuls (pegainfer PR #970,
   whale-lane commit text: (M,D) packages combined all-prefix, with a Blelloch
   prefix-scan fallback).
+* ``decode`` -- one new token per sequence against a pool of states read and
+  written through slot indices (ROCm/ATOM PR #2709, review notes: the fused
+  sigmoid-gated delta-rule update takes a read-side state index beside the
+  write table).  It is the token recurrence above on sequences of length 1;
+  gate logits are activated first with ``softplus`` / ``sigmoid`` written
+  from their definitions.
 * ``mirror`` -- the fp64 chunkwise form (used only to pin chunk-size
   independence and the chunk algebra; never as the oracle).
 """
@@ -29,7 +35,7 @@ _LIB = os.path.join(_HERE, "libkda_oracle.so")
 _lib = None
 
 __all__ = ["build", "prefill", "package", "compose", "identity_package", "scan_sequential",
-           "scan_blelloch", "rel_l2", "threads"]
+           "scan_blelloch", "rel_l2", "threads", "softplus", "sigmoid", "decode"]
 
 
 def build(force: bool = True) -> str:
@@ -115,6 +121,52 @@ def package(q, k, v, g, beta, a, b, scale=1.0, qk_l2norm=1, nthreads=None):
     if rc != 0:
         raise ValueError("kda_oracle_package rejected its arguments")
     return M, D, o
+
+
+# ---------------------------------------------------------------------------
+# Decode against a state pool
+# ---------------------------------------------------------------------------
+def softplus(x):
+    """log(1 + e^x) in fp64, as log(e^0 + e^x) without overflow."""
+    return np.logaddexp(0.0, np.asarray(x, dtype=np.float64))
+
+
+def sigmoid(x):
+    """1 / (1 + e^-x) in fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-x))
+
+
+def decode(q, k, v, g, beta, pool, read_idx, write_idx, gate_logits=False, scale=1.0,
+           qk_l2norm=1):
+    """One decode step: sequence n takes row n of q, k, v [N,H,d], g [N,H,dk],
+    beta [N,H].  With gate_logits, log alpha = -softplus(g) and
+    beta = sigmoid(beta).  Sequence n starts from pool[read_idx[n]] (zeros
+    when the index is outside [0, n_slots)) and its new state goes to
+    pool[write_idx[n]] (nowhere when outside).  All reads happen before any
+    write.  Returns (o [N,H,dv], new pool), both fp64."""
+    q, k, v, g, beta = (_c64(x) for x in (q, k, v, g, beta))
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    pool = np.asarray(pool, dtype=np.float64)
+    n_slots = pool.shape[0]
+    if gate_logits:
+        g = -softplus(g)
+        beta = sigmoid(beta)
+    S0 = np.zeros((N, H, dk, dv))
+    for n in range(N):
+        r = int(read_idx[n])
+        if 0 <= r < n_slots:
+            S0[n] = pool[r]
+    o, Sf, _ = prefill(q, k, v, g, beta, np.arange(N + 1), S0=S0, scale=scale,
+                       qk_l2norm=qk_l2norm)
+    out = pool.copy()
+    for n in range(N):
+        w = int(write_idx[n])
+        if 0 <= w < n_slots:
+            out[w] = Sf[n]
+    return o, out
 
 
 # ---------------------------------------------------------------------------

@@ -73,6 +73,9 @@ def test_struct_layouts():
     # kda_config: seven 4-byte fields; kda_ckpt: int32 + two pointers
     assert ctypes.sizeof(K.kda_config) == 28
     assert K.kda_ckpt.offsets.offset == 8 and ctypes.sizeof(K.kda_ckpt) == 24
+    # kda_state_pool: pointer, int64, two pointers
+    assert ctypes.sizeof(K.kda_state_pool) == 32
+    assert K.kda_state_pool.n_slots.offset == 8 and K.kda_state_pool.write_idx.offset == 24
 
 
 def test_status_strings_and_version():
@@ -180,6 +183,32 @@ def test_segment_entry_points_validate():
     assert cw(ctypes.byref(K.kda_ckpt(4000, None, FAKE))) == K.KDA_ERR_ARG
     assert cw(ctypes.byref(ck), subD=None) == K.KDA_ERR_ARG
     assert cw(ctypes.byref(ck), subD=MISALIGNED) == K.KDA_ERR_ALIGN
+
+
+def decode(c, N=4, gate_logits=1, pool=None, q=FAKE, o=FAKE, beta=FAKE):
+    if pool is None:
+        pool = K.kda_state_pool(FAKE, 8, FAKE, FAKE)
+    return K.LIB.kda_decode(ctypes.byref(c) if c is not None else None, N, q, FAKE, FAKE, FAKE,
+                            beta, gate_logits, ctypes.byref(pool) if pool else None, o, None)
+
+
+def test_decode_validates():
+    assert decode(None) == K.KDA_ERR_ARG
+    assert decode(cfg(dk=96)) == K.KDA_ERR_UNSUPPORTED and "decode" in last_error()
+    # decode builds every dk, dv in {64, 128} for both dtypes
+    assert decode(cfg(dk=128, dv=64, dtype=0), q=None) == K.KDA_ERR_ARG
+    assert "q is NULL" in last_error()
+    assert decode(cfg(), N=-1) == K.KDA_ERR_ARG
+    assert decode(cfg(), gate_logits=2) == K.KDA_ERR_ARG and "gate_logits" in last_error()
+    assert decode(cfg(), pool=False) == K.KDA_ERR_ARG and "pool is NULL" in last_error()
+    assert decode(cfg(), pool=K.kda_state_pool(FAKE, 0, FAKE, FAKE)) == K.KDA_ERR_ARG
+    assert decode(cfg(), pool=K.kda_state_pool(FAKE, 4, None, FAKE)) == K.KDA_ERR_ARG
+    assert "read_idx" in last_error()
+    assert decode(cfg(), pool=K.kda_state_pool(MISALIGNED, 4, FAKE, FAKE)) == K.KDA_ERR_ALIGN
+    assert decode(cfg(), o=MISALIGNED) == K.KDA_ERR_ALIGN
+    assert decode(cfg(), beta=FAKE + 2) == K.KDA_ERR_ALIGN
+    # N = 0 is a no-op that touches no pointer
+    assert decode(cfg(), N=0, q=None, o=None) == K.KDA_OK
 
 
 def test_errors_are_per_thread():

@@ -288,6 +288,91 @@ def test_segment_package_without_M(K):
 # ---------------------------------------------------------------------------
 # full-size standard workloads, sampled units
 # ---------------------------------------------------------------------------
+# ---------------------------------------------------------------------------
+# Decode against a state pool
+# ---------------------------------------------------------------------------
+def _decode_case(K, b, name):
+    import torch
+    from workloads.device import decode_to_torch
+    say(f"decode {name}: N={b.N} H={b.H} dk={b.dk} dv={b.dv} {b.dtype} logits={b.gate_logits}")
+    t = decode_to_torch(b)
+    pool_in = t["pool"].clone()
+    o = K.kda_decode(t["q"], t["k"], t["v"], t["g"], t["beta"], t["pool"], t["read_idx"],
+                     t["write_idx"], gate_logits=b.gate_logits, scale=b.scale,
+                     qk_l2norm=bool(b.qk_l2norm))
+    sync()
+    o_ref, pool_ref = oracle.decode(b.f64("q"), b.f64("k"), b.f64("v"), b.f64("g"),
+                                    b.f64("beta"), b.pool, b.read_idx, b.write_idx,
+                                    gate_logits=b.gate_logits, scale=b.scale,
+                                    qk_l2norm=b.qk_l2norm)
+    assert_close(f"decode {name} o", to_numpy_f64(o), o_ref, OUT_TOL[b.dtype])
+    n_slots = b.pool.shape[0]
+    written = sorted({int(w) for w in b.write_idx if 0 <= w < n_slots})
+    if written:
+        assert_close(f"decode {name} written states", to_numpy_f64(t["pool"][written]),
+                     pool_ref[written], STATE_TOL[b.dtype])
+    kept = [i for i in range(n_slots) if i not in written]
+    assert torch.equal(t["pool"][kept], pool_in[kept]), "a slot that is not written changed"
+
+
+@pytest.mark.parametrize("dtype,dk,dv,logits", [("bf16", 128, 128, True), ("bf16", 64, 64, False),
+                                                ("f32", 64, 64, True), ("f32", 128, 64, False),
+                                                ("bf16", 64, 128, True)])
+def test_decode_parity(K, dtype, dk, dv, logits):
+    from workloads import make_decode_batch
+    b = make_decode_batch("decode-small", 20, 3, dk, dv, dtype, 4601, gate_logits=logits)
+    _decode_case(K, b, f"{dtype} {dk}x{dv}")
+
+
+def test_decode_standard_batch(K):
+    """64 sequences, H=32, d=128, bf16, 128-slot pool, gate logits: the
+    decode workload the benchmark times, compared in full."""
+    from workloads import standard_decode_batch
+    _decode_case(K, standard_decode_batch(), "n64")
+
+
+def test_decode_out_of_range_slots(K):
+    """Indices outside [0, n_slots) read a zero state and write nothing."""
+    from workloads import make_decode_batch
+    b = make_decode_batch("decode-oob", 6, 2, 64, 64, "f32", 4602, n_slots=12,
+                          read_idx=[0, 12, -3, 1, 99, 2], write_idx=[6, 7, 8, 12, 9, -1])
+    _decode_case(K, b, "out of range")
+
+
+def test_decode_chain_equals_prefill(K):
+    """Sixteen decode steps in place on one slot against the oracle's
+    prefill of the same sixteen tokens from that slot's state."""
+    import torch
+    w = make_workload("decode-chain", [16], 2, 128, 128, "bf16", 4603, s0_std=0.1)
+    t = to_torch(w)
+    pool = torch.zeros((3, 2, 128, 128), dtype=torch.float32, device="cuda")
+    pool[2] = t["S0"][0]
+    idx = torch.tensor([2], dtype=torch.int32, device="cuda")
+    say("decode chain: 16 steps, H=2, d=128, bf16")
+    outs = []
+    for s_ in range(16):
+        outs.append(K.kda_decode(t["q"][s_:s_ + 1], t["k"][s_:s_ + 1], t["v"][s_:s_ + 1],
+                                 t["g"][s_:s_ + 1], t["beta"][s_:s_ + 1], pool, idx, idx))
+    sync()
+    o_ref, Sf_ref, _ = oracle_full(w)
+    assert_close("decode chain o", to_numpy_f64(torch.cat(outs)), o_ref, OUT_TOL["bf16"])
+    assert_close("decode chain state", to_numpy_f64(pool[2]), Sf_ref[0], STATE_TOL["bf16"])
+    assert float(pool[:2].abs().max()) == 0.0
+
+
+def test_decode_empty_batch(K):
+    import torch
+    pool = torch.randn((2, 1, 64, 64), device="cuda")
+    before = pool.clone()
+    e = torch.empty((0, 1, 64), dtype=torch.bfloat16, device="cuda")
+    o = K.kda_decode(e, e, e, torch.empty((0, 1, 64), device="cuda"),
+                     torch.empty((0, 1), device="cuda"), pool,
+                     torch.empty(0, dtype=torch.int32, device="cuda"),
+                     torch.empty(0, dtype=torch.int32, device="cuda"))
+    sync()
+    assert o.shape == (0, 1, 64) and torch.equal(pool, before)
+
+
 def test_config1_full(K):
     say("config1: T=8192 H=32 d=128 bf16 chunked prefill (sampled heads 0, 17, 31)")
     import torch

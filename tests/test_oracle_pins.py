@@ -328,3 +328,127 @@ def test_bf16_rounding_matches_torch():
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     np.testing.assert_array_equal(ours, ref)
     assert np.isnan(bf16_bits_to_f32(bf16_round_bits(np.array([np.nan], np.float32))))[0]
+
+
+# ---------------------------------------------------------------------------
+# Decode against a state pool
+# ---------------------------------------------------------------------------
+def test_gate_activations_closed_forms():
+    """softplus and sigmoid against values and identities fixed by their
+    definitions, and against scipy's independent routines.
+    Catches: softplus(-x) for softplus(x), a sign flip in sigmoid, overflow at
+    large |x|."""
+    from scipy.special import expit, log_expit
+    assert oracle.softplus(0.0) == pytest.approx(np.log(2.0), abs=1e-16)
+    assert oracle.sigmoid(0.0) == 0.5
+    x = np.linspace(-60.0, 60.0, 241)
+    np.testing.assert_allclose(oracle.softplus(x) - oracle.softplus(-x), x, atol=1e-12)
+    np.testing.assert_allclose(oracle.sigmoid(x) + oracle.sigmoid(-x), 1.0, atol=1e-15)
+    np.testing.assert_allclose(oracle.sigmoid(x), np.exp(-oracle.softplus(-x)), rtol=1e-13)
+    np.testing.assert_allclose(oracle.sigmoid(x), expit(x), rtol=1e-14)
+    np.testing.assert_allclose(-oracle.softplus(-x), log_expit(x), rtol=1e-13, atol=1e-300)
+    assert oracle.softplus(-40.0) == pytest.approx(np.exp(-40.0), rel=1e-12)
+    assert np.isfinite(oracle.softplus(1e4)) and oracle.softplus(1e4) == 1e4
+
+
+def l2n(x):
+    """x / sqrt(|x|^2 + 1e-6), the normalisation the recurrence applies."""
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + 1e-6)
+
+
+def _decode_inputs(seed, N, H, dk, dv, n_slots):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((N, H, dk))
+    k = rng.standard_normal((N, H, dk))
+    v = rng.standard_normal((N, H, dv))
+    ga = rng.standard_normal((N, H, dk))
+    ba = rng.standard_normal((N, H))
+    pool = 0.1 * rng.standard_normal((n_slots, H, dk, dv))
+    return q, k, v, ga, ba, pool
+
+
+def test_decode_from_zero_state_closed_form():
+    """Read index -1: S = beta k^ v^T and o = beta (k^ . q^) v, whatever the
+    decay.  Catches: a missing normalisation, S^T for S, the decay applied
+    to the write, a read of slot 0 for a negative index."""
+    N, H, dk, dv = 3, 2, 8, 5
+    q, k, v, ga, ba, pool = _decode_inputs(7, N, H, dk, dv, 4)
+    read = np.array([-1, -1, -1])
+    write = np.array([0, 1, -1])
+    o, out = oracle.decode(q, k, v, ga, ba, pool, read, write, gate_logits=True)
+    beta = 1.0 / (1.0 + np.exp(-ba))
+    qn, kn = l2n(q), l2n(k)
+    for n in range(N):
+        for h in range(H):
+            S = beta[n, h] * np.outer(kn[n, h], v[n, h])
+            np.testing.assert_allclose(o[n, h], beta[n, h] * (kn[n, h] @ qn[n, h]) * v[n, h],
+                                       rtol=1e-12, atol=1e-14)
+            if write[n] >= 0:
+                np.testing.assert_allclose(out[write[n], h], S, rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(out[2:], pool[2:])
+
+
+def test_decode_pure_decay_and_recall():
+    """beta = 0 gives S' = Diag(alpha) S and o = S'^T q^; alpha = 1, beta = 1
+    and q = k give o = v (the written key recalls its value).  Catches:
+    decay on the value axis, exp(g) vs g, the erase sign."""
+    N, H, dk, dv = 2, 2, 6, 4
+    q, k, v, ga, _, pool = _decode_inputs(8, N, H, dk, dv, 2)
+    g = -oracle.softplus(ga)
+    read = np.array([1, 0])
+    write = np.array([1, 0])
+    o, out = oracle.decode(q, k, v, g, np.zeros((N, H)), pool, read, write)
+    for n in range(N):
+        for h in range(H):
+            S = np.exp(g[n, h])[:, None] * pool[read[n], h]
+            np.testing.assert_allclose(out[write[n], h], S, rtol=1e-13)
+            np.testing.assert_allclose(o[n, h], S.T @ l2n(q)[n, h], rtol=1e-12, atol=1e-15)
+    ku = unit_rows(k)
+    o, out = oracle.decode(ku, ku, v, np.zeros((N, H, dk)), np.ones((N, H)), pool, read, write,
+                           qk_l2norm=0)
+    np.testing.assert_allclose(o, v, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_slot_semantics():
+    """Forks leave the read slot as it was, in-place rows replace it, rows
+    with a negative write index keep nothing, untouched slots are copied
+    through, and the logits path equals the activated gates computed with
+    scipy.  Catches: writes into the read slot of a fork, a write for index
+    -1, gates activated twice or not at all."""
+    from scipy.special import expit, log_expit
+    N, H, dk, dv = 4, 1, 4, 3
+    q, k, v, ga, ba, pool = _decode_inputs(9, N, H, dk, dv, 8)
+    read = np.array([2, 5, 0, 3])
+    write = np.array([2, 6, -1, 7])
+    o, out = oracle.decode(q, k, v, ga, ba, pool, read, write, gate_logits=True)
+    o2, out2 = oracle.decode(q, k, v, log_expit(-ga), expit(ba), pool, read, write)
+    np.testing.assert_allclose(o, o2, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(out, out2, rtol=1e-13, atol=1e-15)
+    for s in (0, 1, 3, 4, 5):
+        np.testing.assert_array_equal(out[s], pool[s])
+    assert not np.allclose(out[2], pool[2])
+    # the forked and in-place states are one-token updates of their read slots
+    for n, (r, w) in enumerate(zip(read, write)):
+        if w < 0:
+            continue
+        o1, S1, _ = oracle.prefill(q[n:n + 1], k[n:n + 1], v[n:n + 1], log_expit(-ga[n:n + 1]),
+                                   expit(ba[n:n + 1]), [0, 1], S0=pool[r][None])
+        np.testing.assert_allclose(out[w], S1[0], rtol=1e-13, atol=1e-15)
+
+
+def test_decode_chain_equals_prefill():
+    """T decode steps in place on one slot equal a T-token prefill from that
+    slot's state: the pool plumbing adds nothing to the recurrence."""
+    T, H, dk, dv = 12, 2, 8, 8
+    q, k, v, g, beta = rnd_inputs(10, T, H, dk, dv)
+    pool = 0.1 * np.random.default_rng(11).standard_normal((3, H, dk, dv))
+    o_ref, Sf, _ = oracle.prefill(q, k, v, g, beta, [0, T], S0=pool[1][None])
+    cur = pool.copy()
+    outs = []
+    for t in range(T):
+        o, cur = oracle.decode(q[t:t + 1], k[t:t + 1], v[t:t + 1], g[t:t + 1], beta[t:t + 1],
+                               cur, [1], [1])
+        outs.append(o[0])
+    np.testing.assert_allclose(np.stack(outs), o_ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(cur[1], Sf[0], rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(cur[0], pool[0])

@@ -30,3 +30,16 @@ def to_torch(w, device="cuda") -> dict:
 
 def to_numpy_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def decode_to_torch(b, device="cuda") -> dict:
+    return {
+        "q": _io_tensor(b.q, b.dtype, device),
+        "k": _io_tensor(b.k, b.dtype, device),
+        "v": _io_tensor(b.v, b.dtype, device),
+        "g": torch.from_numpy(b.g).to(device),
+        "beta": torch.from_numpy(b.beta).to(device),
+        "pool": torch.from_numpy(b.pool).to(device),
+        "read_idx": torch.from_numpy(b.read_idx).to(device),
+        "write_idx": torch.from_numpy(b.write_idx).to(device),
+    }

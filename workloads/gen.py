@@ -31,9 +31,10 @@ __all__ = [
     "Workload", "make_workload", "standard_workload", "STANDARD",
     "bf16_round_bits", "bf16_bits_to_f32", "to_f64", "leveled_segments",
     "varlen_lengths", "ckpt_offsets", "GATE_COST_Q", "SEGMENT_FLOOR",
+    "DecodeBatch", "make_decode_batch", "decode_slots", "standard_decode_batch",
 ]
 
-T_Q, T_K, T_V, T_BETA, T_G, T_S0 = 0, 1, 2, 3, 4, 5
+T_Q, T_K, T_V, T_BETA, T_G, T_S0, T_POOL = 0, 1, 2, 3, 4, 5, 6
 
 # Segment cost model coefficient and the per-segment token floor quoted by the
 # pegainfer "cross-process CP whale gang" PR (commit "whale rendezvous":
@@ -274,3 +275,90 @@ def standard_workload(idx: int, s0_std: float | None = None, **over) -> Workload
                              s0_std=0.1 if s0_std is None else s0_std, ckpt_interval=4096,
                              **over)
     raise ValueError(idx)
+
+
+# ----------------------------------------------------------------------------
+# Decode batches: one new token per sequence, states in a slot pool
+# ----------------------------------------------------------------------------
+@dataclass
+class DecodeBatch:
+    name: str
+    N: int
+    H: int
+    dk: int
+    dv: int
+    dtype: str
+    q: np.ndarray                   # [N,H,dk] uint16 bf16 bits or float32
+    k: np.ndarray
+    v: np.ndarray                   # [N,H,dv]
+    g: np.ndarray                   # [N,H,dk] float32: logits when gate_logits, else log-decay
+    beta: np.ndarray                # [N,H] float32: logits when gate_logits, else beta
+    gate_logits: bool
+    pool: np.ndarray                # [n_slots,H,dk,dv] float32
+    read_idx: np.ndarray            # int32 [N]
+    write_idx: np.ndarray           # int32 [N]
+    scale: float = 1.0
+    qk_l2norm: int = 1
+
+    def f64(self, name: str) -> np.ndarray:
+        a = getattr(self, name)
+        if name in ("q", "k", "v"):
+            return to_f64(a, self.dtype)
+        return np.asarray(a, dtype=np.float64)
+
+
+def decode_slots(N: int, n_slots: int):
+    """Slot pattern of a decode batch with N <= n_slots // 2.
+
+    Sequence n reads slot perm[n] (a fixed permutation of 0..N-1).  Even n
+    update in place; odd n fork into slot N + n, which nothing reads.  Every
+    8th sequence (n % 8 == 3) starts from a zero state (read index -1) and
+    every 16th (n % 16 == 5) keeps no state (write index -1).  Write slots are
+    then distinct and never another sequence's read slot.
+    """
+    if 2 * N > n_slots:
+        raise ValueError("the pattern needs n_slots >= 2N")
+    perm = np.random.default_rng([N, n_slots]).permutation(N).astype(np.int32)
+    read = perm.copy()
+    write = np.where(np.arange(N) % 2 == 0, perm, N + np.arange(N)).astype(np.int32)
+    read[np.arange(N) % 8 == 3] = -1
+    write[np.arange(N) % 16 == 5] = -1
+    return read, write
+
+
+def make_decode_batch(name: str, N: int, H: int, dk: int, dv: int, dtype: str, seed: int,
+                      n_slots: int | None = None, gate_logits: bool = True,
+                      s_std: float = 0.1, read_idx=None, write_idx=None) -> DecodeBatch:
+    n_slots = 2 * N if n_slots is None else n_slots
+    io = np.uint16 if dtype == "bf16" else np.float32
+    q = np.empty((N, H, dk), dtype=io)
+    k = np.empty((N, H, dk), dtype=io)
+    v = np.empty((N, H, dv), dtype=io)
+    g = np.empty((N, H, dk), dtype=np.float32)
+    beta = np.empty((N, H), dtype=np.float32)
+    _fill(q, seed, T_Q, "normal", 0.0, dtype, N, H, dk)
+    _fill(k, seed, T_K, "normal", 0.0, dtype, N, H, dk)
+    _fill(v, seed, T_V, "normal", 0.0, dtype, N, H, dv)
+    _fill(beta, seed, T_BETA, "normal" if gate_logits else "sigmoid", 0.0, "f32", N, H, 0)
+    _fill(g, seed, T_G, "normal" if gate_logits else "neg_softplus", 0.0, "f32", N, H, dk)
+    pool = np.empty((n_slots, H, dk, dv), dtype=np.float32)
+
+    def slot(i):
+        rng = np.random.default_rng([seed, T_POOL, i])
+        pool[i] = rng.standard_normal((H, dk, dv), dtype=np.float32) * np.float32(s_std)
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(slot, range(n_slots)))
+    if read_idx is None or write_idx is None:
+        r, w = decode_slots(N, n_slots)
+        read_idx = r if read_idx is None else read_idx
+        write_idx = w if write_idx is None else write_idx
+    return DecodeBatch(name=name, N=N, H=H, dk=dk, dv=dv, dtype=dtype, q=q, k=k, v=v, g=g,
+                       beta=beta, gate_logits=gate_logits, pool=pool,
+                       read_idx=np.asarray(read_idx, dtype=np.int32),
+                       write_idx=np.asarray(write_idx, dtype=np.int32))
+
+
+def standard_decode_batch(**over) -> DecodeBatch:
+    """64 sequences (the varlen batch's count), H=32, d=128, bf16, 128-slot pool."""
+    return make_decode_batch("kda-decode-n64-h32-d128-bf16", 64, 32, 128, 128, "bf16",
+                             46005, **over)
