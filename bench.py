@@ -48,16 +48,19 @@ def bytes_per_token_head(dk: int, dv: int, io_bytes: int) -> int:
     return io_bytes * (2 * dk + 2 * dv) + 4 * dk + 4
 
 
-def recorded_traffic(workload: str, kernel_mode: str):
-    """HBM bytes per launch of the dominant kernel from profiles/hbm_traffic.json
-    (two rocprofv3 --pmc runs, FETCH_SIZE and WRITE_SIZE, each scaled by what
-    the same counter reads for a plain copy of known size), or None when that
-    record is for another workload or the kernel sources changed since."""
+def recorded_traffic(workload: str, kernel_mode: str, entry: str | None = None):
+    """HBM bytes per launch of a kernel from profiles/hbm_traffic.json (two
+    rocprofv3 --pmc runs, FETCH_SIZE and WRITE_SIZE, each scaled by what the
+    same counter reads for a plain copy of known size), or None when that
+    record is for another workload or the kernel's sources changed since.
+    `entry` selects a nested record (e.g. "decode")."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
+    if entry is not None:
+        rec = rec.get(entry, {})
     if rec.get("workload") != workload or kernel_mode not in rec.get("kernel", ""):
         return None
     h = hashlib.sha256()
@@ -75,6 +78,7 @@ def parse():
     ap.add_argument("--config", type=int, default=3, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--no-resume", action="store_true", help="skip the resume measurement")
     ap.add_argument("--decode-launches", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -127,6 +131,51 @@ def cpu_baseline(w, target_s: float) -> dict:
                       f"{threads} threads over heads ({dt:.1f} s)"}
 
 
+def resume_measure(K, w, t, launches: int) -> dict:
+    """kda_prefill_resume over the segment workload's tokens read as one
+    sequence per segment, each continuing in place from a pool slot at its
+    absolute start position, rungs every `ckpt_interval` tokens on the
+    absolute grid.  HIP events around each call; algorithmic bytes as for
+    prefill (1540 B per token-head) plus the states read, written and rung."""
+    import torch
+    from workloads import ckpt_offsets
+    nseg = len(w.seg_start) - 1
+    lengths = np.diff(w.seg_start)
+    pos0 = torch.from_numpy(w.seg_start[:-1].astype(np.int64)).cuda()
+    iv = w.ckpt_interval or 4096
+    off_np = ckpt_offsets(lengths, iv, pos0=w.seg_start[:-1])
+    off = torch.from_numpy(off_np).cuda()
+    gen = torch.Generator(device="cuda").manual_seed(46003)
+    pool = 0.1 * torch.randn((nseg, w.H, w.dk, w.dv), generator=gen, device="cuda")
+    idx = torch.arange(nseg, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        K.kda_prefill_resume(t["q"], t["k"], t["v"], t["g"], t["beta"], t["seg_start"], pool, idx,
+                             idx, pos0=pos0, ckpt_interval=iv, ckpt_offsets=off)
+    call()
+    pairs = []
+    for _ in range(launches):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+    io_bytes = 2 if w.dtype == "bf16" else 4
+    alg = (w.T * w.H * bytes_per_token_head(w.dk, w.dv, io_bytes)
+           + 4 * w.H * w.dk * w.dv * (2 * nseg + int(off_np[-1])))
+    gbs = alg / (ms * 1e-3) / 1e9
+    return {"workload": f"{w.name} as {nseg} sequences resumed in place at their absolute starts",
+            "kernel": "chunk_engine<prefill> from a state pool", "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+            "launch_ms": round(ms, 4), "launches_timed": launches, "rungs": int(off_np[-1]),
+            "alg_bytes_per_launch": int(alg),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
 def decode_measure(K, launches: int) -> dict:
     """kda_decode on 64 sequences x 32 heads (d=128, bf16, gate logits,
     128-slot pool with in-place rows, forks, fresh and discarded states).
@@ -172,7 +221,8 @@ def decode_measure(K, launches: int) -> dict:
             "launches_timed": launches, "cache": "1 GiB read before each timed call",
             "alg_bytes_per_launch": int(alg),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": recorded_traffic(b.name, "decode_kernel", "decode")}}
 
 
 def main():
@@ -310,6 +360,8 @@ def main():
                      "launch_ms": round(kernel_ms, 4), "launches_timed": args.roofline_launches},
         "breakdown_ms": breakdown,
     }
+    if segmented and not args.no_resume:
+        result["resume"] = resume_measure(K, w, t, args.roofline_launches)
     if not args.no_decode:
         del t
         result["decode"] = decode_measure(K, args.decode_launches)

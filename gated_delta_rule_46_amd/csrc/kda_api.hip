@@ -84,6 +84,78 @@ int launched(hipError_t e, const char *what) {
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
+size_t prefill_ws_bytes(int32_t N) { return round256((size_t)(N > 0 ? N : 1) * sizeof(int32_t)); }
+
+// Chunked prefill with initial / final states either dense (S0, S_final) or
+// in a slot pool; pos0 (nullable) shifts the checkpoint grid.
+int prefill_impl(const char *what, const kda_config *cfg, const void *q, const void *k,
+                 const void *v, const float *g, const float *beta, const int64_t *cu_seqlens,
+                 int32_t N, int64_t T, const float *S0, float *S_final,
+                 const kda_state_pool *pool, const int64_t *pos0, void *o, const kda_ckpt *ckpt,
+                 void *ws, size_t ws_bytes, void *stream) {
+    KDA_TRY(check_config(cfg));
+    if (T < 0) return fail(KDA_ERR_ARG, "T must be >= 0 (got %lld)", (long long)T);
+    if (N < 0) return fail(KDA_ERR_ARG, "N must be >= 0 (got %d)", N);
+    if (T > 0 && N == 0) return fail(KDA_ERR_ARG, "T > 0 needs at least one sequence");
+    if (pool) {
+        if (pool->n_slots <= 0)
+            return fail(KDA_ERR_ARG, "pool->n_slots must be positive (got %lld)",
+                        (long long)pool->n_slots);
+        KDA_TRY(check_tensor(pool->states, "pool->states", true, 16));
+        KDA_TRY(check_tensor(pool->read_idx, "pool->read_idx", N > 0, 4));
+        KDA_TRY(check_tensor(pool->write_idx, "pool->write_idx", N > 0, 4));
+    }
+    KDA_TRY(check_tensor(pos0, "pos0", false, 8));
+    if (N == 0) return ok();
+    const bool need_rows = T > 0;
+    KDA_TRY(check_tensor(q, "q", need_rows));
+    KDA_TRY(check_tensor(k, "k", need_rows));
+    KDA_TRY(check_tensor(v, "v", need_rows));
+    KDA_TRY(check_tensor(g, "g", need_rows));
+    KDA_TRY(check_tensor(beta, "beta", need_rows, 4));
+    KDA_TRY(check_tensor(o, "o", need_rows));
+    KDA_TRY(check_tensor(cu_seqlens, "cu_seqlens", true, 8));
+    KDA_TRY(check_tensor(S0, "S0", false, 16));
+    KDA_TRY(check_tensor(S_final, "S_final", false, 16));
+    if (ckpt) {
+        KDA_TRY(check_ckpt_interval(ckpt->interval));
+        KDA_TRY(check_tensor(ckpt->states, "ckpt->states", true, 16));
+        KDA_TRY(check_tensor(ckpt->offsets, "ckpt->offsets", N > 1, 8));
+    }
+    const size_t need = prefill_ws_bytes(N);
+    if (!ws || ws_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, ws_bytes);
+    KDA_TRY(check_tensor(ws, "ws", true, 16));
+
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf = cfg->io_dtype == KDA_DTYPE_BF16;
+    const int nb = kda::engine_pick_nb(bf, cfg->dk, cfg->dv, (int64_t)N * cfg->num_heads,
+                                       kda::kModePrefill);
+    int32_t *order = nullptr;
+    if (N > 1 && N <= 8192) {
+        order = (int32_t *)ws;
+        hipError_t e = kda::launch_plan(cu_seqlens, N, order, s);
+        if (e != hipSuccess) return launched(e, "plan");
+    }
+    kda::EngineArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
+    a.bounds = cu_seqlens; a.order = order; a.n_units = N; a.H = cfg->num_heads;
+    a.ncb = cfg->dv / nb;
+    a.S_init = pool ? pool->states : S0;
+    a.S_out = pool ? pool->states : S_final;
+    a.M_out = nullptr;
+    a.interval = ckpt ? ckpt->interval : 0;
+    a.ckpt_off = ckpt ? ckpt->offsets : nullptr;
+    a.ckpt_S = ckpt ? ckpt->states : nullptr;
+    a.ckpt_M = nullptr;
+    a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;
+    a.s_in_idx = pool ? pool->read_idx : nullptr;
+    a.s_out_idx = pool ? pool->write_idx : nullptr;
+    a.n_slots = pool ? pool->n_slots : 0;
+    a.pos0 = pos0;
+    return launched(kda::launch_engine(kda::kModePrefill, bf, cfg->dk, cfg->dv, nb, a, s), what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -107,59 +179,24 @@ const char *kda_version(void) { return "0.1.0"; }
 size_t kda_prefill_workspace(const kda_config *cfg, int64_t T, int32_t N) {
     (void)cfg;
     (void)T;
-    return round256((size_t)(N > 0 ? N : 1) * sizeof(int32_t));
+    return prefill_ws_bytes(N);
 }
 
 int kda_prefill(const kda_config *cfg, const void *q, const void *k, const void *v,
                 const float *g, const float *beta, const int64_t *cu_seqlens, int32_t N,
                 int64_t T, const float *S0, float *S_final, void *o, const kda_ckpt *ckpt,
                 void *ws, size_t ws_bytes, void *stream) {
-    KDA_TRY(check_config(cfg));
-    if (T < 0) return fail(KDA_ERR_ARG, "T must be >= 0 (got %lld)", (long long)T);
-    if (N < 0) return fail(KDA_ERR_ARG, "N must be >= 0 (got %d)", N);
-    if (T > 0 && N == 0) return fail(KDA_ERR_ARG, "T > 0 needs at least one sequence");
-    if (N == 0) return ok();
-    const bool need_rows = T > 0;
-    KDA_TRY(check_tensor(q, "q", need_rows));
-    KDA_TRY(check_tensor(k, "k", need_rows));
-    KDA_TRY(check_tensor(v, "v", need_rows));
-    KDA_TRY(check_tensor(g, "g", need_rows));
-    KDA_TRY(check_tensor(beta, "beta", need_rows, 4));
-    KDA_TRY(check_tensor(o, "o", need_rows));
-    KDA_TRY(check_tensor(cu_seqlens, "cu_seqlens", true, 8));
-    KDA_TRY(check_tensor(S0, "S0", false, 16));
-    KDA_TRY(check_tensor(S_final, "S_final", false, 16));
-    if (ckpt) {
-        KDA_TRY(check_ckpt_interval(ckpt->interval));
-        KDA_TRY(check_tensor(ckpt->states, "ckpt->states", true, 16));
-        KDA_TRY(check_tensor(ckpt->offsets, "ckpt->offsets", N > 1, 8));
-    }
-    const size_t need = kda_prefill_workspace(cfg, T, N);
-    if (!ws || ws_bytes < need)
-        return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, ws_bytes);
-    KDA_TRY(check_tensor(ws, "ws", true, 16));
+    return prefill_impl("prefill", cfg, q, k, v, g, beta, cu_seqlens, N, T, S0, S_final, nullptr,
+                        nullptr, o, ckpt, ws, ws_bytes, stream);
+}
 
-    hipStream_t s = (hipStream_t)stream;
-    const bool bf = cfg->io_dtype == KDA_DTYPE_BF16;
-    const int nb = kda::engine_pick_nb(bf, cfg->dk, cfg->dv, (int64_t)N * cfg->num_heads,
-                                       kda::kModePrefill);
-    int32_t *order = nullptr;
-    if (N > 1 && N <= 8192) {
-        order = (int32_t *)ws;
-        hipError_t e = kda::launch_plan(cu_seqlens, N, order, s);
-        if (e != hipSuccess) return launched(e, "plan");
-    }
-    kda::EngineArgs a{};
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
-    a.bounds = cu_seqlens; a.order = order; a.n_units = N; a.H = cfg->num_heads;
-    a.ncb = cfg->dv / nb;
-    a.S_init = S0; a.S_out = S_final; a.M_out = nullptr;
-    a.interval = ckpt ? ckpt->interval : 0;
-    a.ckpt_off = ckpt ? ckpt->offsets : nullptr;
-    a.ckpt_S = ckpt ? ckpt->states : nullptr;
-    a.ckpt_M = nullptr;
-    a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;
-    return launched(kda::launch_engine(kda::kModePrefill, bf, cfg->dk, cfg->dv, nb, a, s), "prefill");
+int kda_prefill_resume(const kda_config *cfg, const void *q, const void *k, const void *v,
+                       const float *g, const float *beta, const int64_t *cu_seqlens, int32_t N,
+                       int64_t T, const int64_t *pos0, const kda_state_pool *pool, void *o,
+                       const kda_ckpt *ckpt, void *ws, size_t ws_bytes, void *stream) {
+    if (!pool) return fail(KDA_ERR_ARG, "pool is NULL");
+    return prefill_impl("prefill resume", cfg, q, k, v, g, beta, cu_seqlens, N, T, nullptr,
+                        nullptr, pool, pos0, o, ckpt, ws, ws_bytes, stream);
 }
 
 int kda_segment_package(const kda_config *cfg, const void *q, const void *k, const void *v,

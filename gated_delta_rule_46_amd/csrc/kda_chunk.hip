@@ -530,9 +530,16 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
     const int wcol = cbase + pw * NBW;
 
     f32x4 S[DKT][NTW];
+    // rungs sit at absolute positions pbase + p (p sequence-relative)
+    const int64_t pbase = (MODE == kModePrefill && a.pos0) ? a.pos0[u] : 0;
     {
         const float *src = nullptr;
-        if (MODE == kModePrefill && a.S_init) src = a.S_init + (int64_t)(u * H + h) * DK * DV;
+        if (MODE == kModePrefill && a.s_in_idx) {
+            const int32_t slot = a.s_in_idx[u];
+            if (slot >= 0 && slot < a.n_slots) src = a.S_init + ((int64_t)slot * H + h) * DK * DV;
+        } else if (MODE == kModePrefill && a.S_init) {
+            src = a.S_init + (int64_t)(u * H + h) * DK * DV;
+        }
         if (MODE == kModeFixup) src = a.S_init + (int64_t)(u * H + h) * DK * DV;
 #pragma unroll
         for (int r = 0; r < DKT; ++r)
@@ -721,8 +728,9 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
         if (a.interval > 0) {
             if (MODE == kModePrefill && a.ckpt_S) {
                 const int64_t p = (int64_t)(c + 1) * kChunk;
-                if (p <= len && p % a.interval == 0) {
-                    const int64_t rowc = (a.ckpt_off ? a.ckpt_off[u] : 0) + p / a.interval - 1;
+                if (p <= len && (pbase + p) % a.interval == 0) {
+                    const int64_t rowc = (a.ckpt_off ? a.ckpt_off[u] : 0) +
+                                         (pbase + p) / a.interval - pbase / a.interval - 1;
                     store_state<DKT, NTW>(a.ckpt_S + (rowc * H + h) * DK * DV, DV, wcol, gq, m, S, false);
                 }
             }
@@ -763,8 +771,16 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
         __syncthreads();                                                      // BB
     }
 
-    if (MODE == kModePrefill && a.S_out)
-        store_state<DKT, NTW>(a.S_out + (int64_t)(u * H + h) * DK * DV, DV, wcol, gq, m, S, false);
+    if (MODE == kModePrefill) {
+        float *dst = nullptr;
+        if (a.s_out_idx) {
+            const int32_t slot = a.s_out_idx[u];
+            if (slot >= 0 && slot < a.n_slots) dst = a.S_out + ((int64_t)slot * H + h) * DK * DV;
+        } else if (a.S_out) {
+            dst = a.S_out + (int64_t)(u * H + h) * DK * DV;
+        }
+        if (dst) store_state<DKT, NTW>(dst, DV, wcol, gq, m, S, false);
+    }
     if (MODE == kModePackage || MODE == kModePackageM) {
         if (MB) store_state<DKT, NTW>(a.M_out + (int64_t)(u * H + h) * DK * DK, DK, wcol, gq, m, S, false);
         else store_state<DKT, NTW>(a.S_out + (int64_t)(u * H + h) * DK * DV, DV, wcol, gq, m, S, false);

@@ -33,6 +33,14 @@ struct EngineArgs {
     float *ckpt_M;               // package: sub_M (nullable)
     float scale;
     int32_t l2norm;
+    // Prefill from a state pool (all nullable): the initial state of unit u is
+    // slot s_in_idx[u] of S_init and its final state goes to slot s_out_idx[u]
+    // of S_out (slots outside [0, n_slots): zero state / not stored); pos0[u]
+    // is the absolute position of the unit's first token, which places the
+    // checkpoint rungs on the original sequence's grid.
+    const int32_t *s_in_idx, *s_out_idx;
+    int64_t n_slots;
+    const int64_t *pos0;
 };
 
 // Launches the engine.  bf16 selects bf16 I/O (bf16 MFMA operands) versus

@@ -19,7 +19,7 @@ KDA_DTYPE_F32, KDA_DTYPE_BF16 = 0, 1
 KDA_SCAN_SEQUENTIAL, KDA_SCAN_BLELLOCH = 0, 1
 CHUNK = 64
 
-EXPORTS = ("kda_prefill_workspace", "kda_prefill", "kda_segment_package",
+EXPORTS = ("kda_prefill_workspace", "kda_prefill", "kda_prefill_resume", "kda_segment_package",
            "kda_segment_scan_workspace", "kda_segment_scan", "kda_output_fixup",
            "kda_checkpoint_write", "kda_decode", "kda_status_string", "kda_last_error",
            "kda_version")
@@ -58,6 +58,8 @@ def _load():
     sig = {
         "kda_prefill_workspace": (S, [cfgp, I64, I32]),
         "kda_prefill": (ctypes.c_int, [cfgp, P, P, P, P, P, P, I32, I64, P, P, P, ckp, P, S, P]),
+        "kda_prefill_resume": (ctypes.c_int, [cfgp, P, P, P, P, P, P, I32, I64, P, poolp, P, ckp,
+                                              P, S, P]),
         "kda_segment_package": (ctypes.c_int, [cfgp, P, P, P, P, P, I64, P, I32, P, P, P, ckp,
                                                P, P, P, S, P]),
         "kda_segment_scan_workspace": (S, [cfgp, I32, I32]),
@@ -173,6 +175,47 @@ def kda_prefill(q, k, v, g, beta, cu_seqlens, S0=None, *, want_final=True, ckpt_
                          N, T, _p(S0), _p(Sf), _p(o), ckp, _p(ws), wsb, _stream(stream))
     _check(st, "kda_prefill")
     return o, Sf, ck
+
+
+def kda_prefill_resume(q, k, v, g, beta, cu_seqlens, pool, read_idx, write_idx, *, pos0=None,
+                       ckpt_interval=0, ckpt_offsets=None, scale=1.0, qk_l2norm=True, out=None,
+                       stream=None):
+    """Chunked prefill continuing each sequence from pool[read_idx[n]]; the
+    final state goes to pool[write_idx[n]] (pool updated in place).  pos0:
+    int64 [N] absolute start positions (multiples of 64) that place the
+    checkpoint rungs; ckpt_offsets: int64 [N+1] first rung rows (required
+    with ckpt_interval for N > 1).  Returns (o, checkpoint states or None)."""
+    T, H, dk, dv, dev = _inputs(q, k, v, g, beta)
+    N = cu_seqlens.numel() - 1
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int64, dev)
+    n_slots = pool.shape[0]
+    _need(pool, "pool", (n_slots, H, dk, dv), torch.float32, dev)
+    _need(read_idx, "read_idx", (N,), torch.int32, dev)
+    _need(write_idx, "write_idx", (N,), torch.int32, dev)
+    if pos0 is not None:
+        _need(pos0, "pos0", (N,), torch.int64, dev)
+    cfg = make_config(H, dk, dv, q.dtype, scale, qk_l2norm)
+    o = out if out is not None else torch.empty((T, H, dv), dtype=q.dtype, device=dev)
+    _need(o, "out", (T, H, dv), q.dtype, dev)
+    ck = None
+    ckp = None
+    if ckpt_interval:
+        if ckpt_offsets is None:
+            raise ValueError("ckpt_offsets is required with ckpt_interval")
+        _need(ckpt_offsets, "ckpt_offsets", (N + 1,), torch.int64, dev)
+        rows = int(ckpt_offsets[-1].item())
+        ck = torch.empty((max(rows, 0), H, dk, dv), dtype=torch.float32, device=dev)
+        ckp = ctypes.pointer(kda_ckpt(int(ckpt_interval), _p(ckpt_offsets), _p(ck) if rows else
+                                      ctypes.c_void_p(torch.empty(1, device=dev).data_ptr())))
+    pl = kda_state_pool(ctypes.c_void_p(pool.data_ptr()), n_slots,
+                        ctypes.c_void_p(read_idx.data_ptr()), ctypes.c_void_p(write_idx.data_ptr()))
+    wsb = LIB.kda_prefill_workspace(ctypes.byref(cfg), T, N)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    st = LIB.kda_prefill_resume(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(g), _p(beta),
+                                _p(cu_seqlens), N, T, _p(pos0), ctypes.byref(pl), _p(o), ckp,
+                                _p(ws), wsb, _stream(stream))
+    _check(st, "kda_prefill_resume")
+    return o, ck
 
 
 def kda_segment_package(q, k, v, g, beta, seg_start, *, ckpt_interval=0, scale=1.0,

@@ -32,6 +32,12 @@
  *    are first computed from a zero state (o_local) and then corrected from
  *    its incoming state S_in^j.  All segments run as parallel work on one GPU.
  *
+ *  - Resume (kda_prefill_resume): chunked prefill that continues sequences
+ *    from states held in a slot pool, e.g. a checkpoint rung restored from a
+ *    prefix cache, with rungs kept on the original sequence's grid (ROCm/ATOM
+ *    PR #2709, Changes: prefix caching of KDA state; demand checkpoints and
+ *    the prompt-end anchor floored onto the chunk grid).
+ *
  *  - Decode (kda_decode): one new token per sequence against a pool of
  *    states addressed by read and write slots (ROCm/ATOM PR #2709, review
  *    notes: the fused sigmoid-gated delta-rule update takes a read-side state
@@ -154,6 +160,28 @@ int kda_prefill(const kda_config *cfg, const void *q, const void *k, const void 
                 const float *g, const float *beta, const int64_t *cu_seqlens, int32_t N,
                 int64_t T, const float *S0, float *S_final, void *o, const kda_ckpt *ckpt,
                 void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Chunked prefill that continues N sequences from states in a pool.
+ * Arguments as kda_prefill, except:
+ *   pool: sequence n starts from slot pool->read_idx[n] and its final state
+ *       is stored in slot pool->write_idx[n] (see kda_state_pool; a slot may
+ *       be read and written by the same sequence: it is then updated in
+ *       place);
+ *   pos0: device int64 [N], the absolute position in its original sequence
+ *       of each sequence's first token, a multiple of the chunk (NULL = all
+ *       0).  The tokens are positions pos0[n] .. pos0[n] + len - 1;
+ *   ckpt: rungs at absolute positions P = m*interval with
+ *       pos0[n] < P <= pos0[n] + len, at row
+ *       offsets[n] + P/interval - pos0[n]/interval - 1.
+ * Resuming from the rung at P with pos0 = P reproduces the continuous run's
+ * outputs, later rungs and final state (up to rounding).  Workspace as
+ * kda_prefill_workspace(cfg, T, N).
+ */
+int kda_prefill_resume(const kda_config *cfg, const void *q, const void *k, const void *v,
+                       const float *g, const float *beta, const int64_t *cu_seqlens, int32_t N,
+                       int64_t T, const int64_t *pos0, const kda_state_pool *pool, void *o,
+                       const kda_ckpt *ckpt, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Segment path (one sequence of T tokens split into nseg segments)         */

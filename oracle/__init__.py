@@ -18,6 +18,11 @@ and never imports it.
   write table).  It is the token recurrence above on sequences of length 1;
   gate logits are activated first with ``softplus`` / ``sigmoid`` written
   from their definitions.
+* ``prefill_resume`` -- prefill that continues sequences from pool slots, with
+  rungs at absolute positions of the original sequence (ROCm/ATOM PR #2709,
+  Changes: prefix caching of KDA state, checkpoints on the chunk grid): the
+  token recurrence run piece by piece between rung positions, each piece's
+  final state being the rung.
 * ``mirror`` -- the fp64 chunkwise form (used only to pin chunk-size
   independence and the chunk algebra; never as the oracle).
 """
@@ -35,7 +40,8 @@ _LIB = os.path.join(_HERE, "libkda_oracle.so")
 _lib = None
 
 __all__ = ["build", "prefill", "package", "compose", "identity_package", "scan_sequential",
-           "scan_blelloch", "rel_l2", "threads", "softplus", "sigmoid", "decode"]
+           "scan_blelloch", "rel_l2", "threads", "softplus", "sigmoid", "decode",
+           "prefill_resume"]
 
 
 def build(force: bool = True) -> str:
@@ -167,6 +173,54 @@ def decode(q, k, v, g, beta, pool, read_idx, write_idx, gate_logits=False, scale
         if 0 <= w < n_slots:
             out[w] = Sf[n]
     return o, out
+
+
+def prefill_resume(q, k, v, g, beta, cu_seqlens, pool, read_idx, write_idx, pos0=None,
+                   ckpt_interval=0, scale=1.0, qk_l2norm=1):
+    """Sequence n (rows cu[n]..cu[n+1]) starts from pool[read_idx[n]] (zeros
+    outside [0, n_slots)) at absolute position pos0[n]; its final state goes
+    to pool[write_idx[n]].  Rungs at absolute P = m*interval with
+    pos0 < P <= pos0 + len, in sequence order then position order.
+    Returns (o [T,H,dv], new pool, rungs [rows,H,dk,dv] or None), fp64."""
+    q, k, v, g, beta = (_c64(x) for x in (q, k, v, g, beta))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    pool = np.asarray(pool, dtype=np.float64)
+    n_slots = pool.shape[0]
+    p0 = np.zeros(N, dtype=np.int64) if pos0 is None else np.asarray(pos0, dtype=np.int64)
+    o = np.zeros((T, H, dv))
+    out = pool.copy()
+    finals = {}
+    rungs = []
+    for n in range(N):
+        a, b = int(cu[n]), int(cu[n + 1])
+        r = int(read_idx[n])
+        S = pool[r].copy() if 0 <= r < n_slots else np.zeros((H, dk, dv))
+        cuts = [a]
+        if ckpt_interval:
+            P = (int(p0[n]) // ckpt_interval + 1) * ckpt_interval
+            while P <= int(p0[n]) + (b - a):
+                cuts.append(a + P - int(p0[n]))
+                P += ckpt_interval
+        if cuts[-1] != b:
+            cuts.append(b)
+        for i in range(len(cuts) - 1):
+            x, y = cuts[i], cuts[i + 1]
+            on, Sn, _ = prefill(q[x:y], k[x:y], v[x:y], g[x:y], beta[x:y], [0, y - x], S0=S[None],
+                                scale=scale, qk_l2norm=qk_l2norm)
+            o[x:y] = on
+            S = Sn[0]
+            if ckpt_interval and (int(p0[n]) + y - a) % ckpt_interval == 0:
+                rungs.append(S.copy())
+        finals[n] = S
+    for n in range(N):
+        w = int(write_idx[n])
+        if 0 <= w < n_slots:
+            out[w] = finals[n]
+    ck = np.stack(rungs) if rungs else (np.zeros((0, H, dk, dv)) if ckpt_interval else None)
+    return o, out, ck
 
 
 # ---------------------------------------------------------------------------

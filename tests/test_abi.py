@@ -211,6 +211,22 @@ def test_decode_validates():
     assert decode(cfg(), N=0, q=None, o=None) == K.KDA_OK
 
 
+def test_prefill_resume_validates():
+    c = cfg()
+    pool = K.kda_state_pool(FAKE, 4, FAKE, FAKE)
+
+    def call(pool=pool, pos0=None, N=2, ws_bytes=1 << 20):
+        return K.LIB.kda_prefill_resume(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, N, 128,
+                                        pos0, ctypes.byref(pool) if pool else None, FAKE, None,
+                                        FAKE, ws_bytes, None)
+    assert call(pool=False) == K.KDA_ERR_ARG and "pool is NULL" in last_error()
+    assert call(pool=K.kda_state_pool(FAKE, 0, FAKE, FAKE)) == K.KDA_ERR_ARG
+    assert call(pool=K.kda_state_pool(FAKE, 4, FAKE, None)) == K.KDA_ERR_ARG
+    assert "write_idx" in last_error()
+    assert call(pos0=FAKE + 4) == K.KDA_ERR_ALIGN and "pos0" in last_error()
+    assert call(ws_bytes=0) == K.KDA_ERR_WORKSPACE
+
+
 def test_errors_are_per_thread():
     import threading
     c = cfg(chunk=32)

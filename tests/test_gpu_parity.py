@@ -289,6 +289,77 @@ def test_segment_package_without_M(K):
 # full-size standard workloads, sampled units
 # ---------------------------------------------------------------------------
 # ---------------------------------------------------------------------------
+# Prefill resumed from a state pool
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 64)])
+def test_prefill_resume_parity(K, dtype, d):
+    """Four sequences continue from pool slots (in place, fork, zero state,
+    state discarded) at absolute positions 0, 128, 192, 4096 with rungs
+    every 128 tokens on the absolute grid; outputs, written slots and rungs
+    against the oracle, untouched slots bit-identical."""
+    import torch
+    lengths = [300, 64, 257, 100]
+    pos0 = [0, 128, 192, 4096]
+    w = make_workload("resume", lengths, 3, d, d, dtype, 4611, s0_std=None)
+    t = to_torch(w)
+    n_slots = 6
+    rng = np.random.default_rng(4612)
+    pool_np = (0.1 * rng.standard_normal((n_slots, 3, d, d))).astype(np.float32)
+    read = np.array([2, 4, -1, 1], dtype=np.int32)
+    write = np.array([2, 5, 0, -1], dtype=np.int32)
+    iv = 128
+    off = ckpt_offsets(lengths, iv, pos0=pos0)
+    say(f"prefill resume {dtype} d={d}: lengths {lengths} pos0 {pos0} rungs {int(off[-1])}")
+    pool = torch.from_numpy(pool_np).cuda()
+    before = pool.clone()
+    o, ck = K.kda_prefill_resume(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"],
+                                 pool, torch.from_numpy(read).cuda(), torch.from_numpy(write).cuda(),
+                                 pos0=torch.tensor(pos0, dtype=torch.int64, device="cuda"),
+                                 ckpt_interval=iv, ckpt_offsets=torch.from_numpy(off).cuda())
+    sync()
+    o_ref, pool_ref, ck_ref = oracle.prefill_resume(w.f64("q"), w.f64("k"), w.f64("v"),
+                                                    w.f64("g"), w.f64("beta"), w.cu_seqlens,
+                                                    pool_np, read, write, pos0=pos0,
+                                                    ckpt_interval=iv)
+    assert ck.shape[0] == ck_ref.shape[0] == int(off[-1])
+    assert_close("resume o", to_numpy_f64(o), o_ref, OUT_TOL[dtype])
+    assert_close("resume written slots", to_numpy_f64(pool[[0, 2, 5]]), pool_ref[[0, 2, 5]],
+                 STATE_TOL[dtype])
+    assert_close("resume rungs", to_numpy_f64(ck), ck_ref, STATE_TOL[dtype])
+    assert torch.equal(pool[[1, 3, 4]], before[[1, 3, 4]])
+
+
+def test_prefill_resume_from_own_rung_is_exact(K):
+    """Resuming from a rung the GPU wrote reproduces the GPU's continuous
+    run bit for bit: same chunk grid, same fp32 state, same arithmetic."""
+    import torch
+    lengths = [1000, 777]
+    w = make_workload("resume-own", lengths, 4, 128, 128, "bf16", 4613, s0_std=0.1)
+    iv = 256
+    o, Sf, ck = run_prefill_t(K, w, interval=iv)
+    # sequence 0 resumes at 512 (its rung 2), sequence 1 at 256 (its rung 1)
+    starts = [512, 256]
+    off = ckpt_offsets(lengths, iv)
+    t = to_torch(w)
+    sel = torch.cat([torch.arange(512, 1000), torch.arange(1000 + 256, 1777)]).cuda()
+    pool = torch.stack([ck[int(off[0]) + 1], ck[int(off[1]) + 0]]).contiguous()
+    cu = torch.tensor([0, 488, 488 + 521], dtype=torch.int64, device="cuda")
+    off2 = ckpt_offsets([488, 521], iv, pos0=starts)
+    idx = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    say("prefill resume from the GPU's own rungs, bf16 d=128")
+    o2, ck2 = K.kda_prefill_resume(t["q"][sel].contiguous(), t["k"][sel].contiguous(),
+                                   t["v"][sel].contiguous(), t["g"][sel].contiguous(),
+                                   t["beta"][sel].contiguous(), cu, pool, idx, idx,
+                                   pos0=torch.tensor(starts, dtype=torch.int64, device="cuda"),
+                                   ckpt_interval=iv, ckpt_offsets=torch.from_numpy(off2).cuda())
+    sync()
+    assert torch.equal(o2, o[sel])
+    assert torch.equal(pool, Sf)
+    # later rungs: sequence 0 at 768 (row 2 of 3), sequence 1 at 512 and 768 (rows 1, 2 of 3)
+    assert torch.equal(ck2, ck[[2, int(off[1]) + 1, int(off[1]) + 2]])
+
+
+# ---------------------------------------------------------------------------
 # Decode against a state pool
 # ---------------------------------------------------------------------------
 def _decode_case(K, b, name):

@@ -452,3 +452,41 @@ def test_decode_chain_equals_prefill():
     np.testing.assert_allclose(np.stack(outs), o_ref, rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(cur[1], Sf[0], rtol=1e-12, atol=1e-14)
     np.testing.assert_array_equal(cur[0], pool[0])
+
+
+def test_prefill_resume_matches_continuous_run():
+    """Two sequences resumed from pool slots holding the continuous run's
+    states at P1 = 128 (a rung) and P2 = 192 (on the chunk grid, between
+    rungs) reproduce the continuous run's outputs, its later rungs (at their
+    absolute positions) and its final states; the pool's other slots are
+    untouched.  The reference is the oracle's own rung logic on the whole
+    sequence, independent of the piecewise resume.  Catches: rungs counted
+    from the resume point instead of the sequence start, a rung missed at the
+    resumed prompt end, the initial state read from the wrong slot."""
+    T, H, dk, dv, iv = 448, 2, 8, 8, 128
+    q, k, v, g, beta = rnd_inputs(31, 2 * T, H, dk, dv, gate_shift=-3.0)
+    S0 = np.random.default_rng(32).standard_normal((2, H, dk, dv))
+    cu = [0, T, 2 * T]
+    o, Sf, ck = oracle.prefill(q, k, v, g, beta, cu, S0=S0, ckpt_interval=iv,
+                               ckpt_offsets=ckpt_offsets([T, T], iv))
+    # states at 128 (sequence 0) and 192 (sequence 1)
+    _, S128, _ = oracle.prefill(q[:128], k[:128], v[:128], g[:128], beta[:128], [0, 128], S0=S0[:1])
+    _, S192, _ = oracle.prefill(q[T:T + 192], k[T:T + 192], v[T:T + 192], g[T:T + 192],
+                                beta[T:T + 192], [0, 192], S0=S0[1:])
+    np.testing.assert_allclose(S128[0], ck[0], rtol=1e-12, atol=1e-14)
+    pool = np.zeros((5, H, dk, dv))
+    pool[3], pool[1], pool[4] = S128[0], S192[0], 7.0
+    sel = np.r_[128:T, T + 192:2 * T]
+    cu2 = [0, T - 128, T - 128 + T - 192]
+    o2, out, ck2 = oracle.prefill_resume(q[sel], k[sel], v[sel], g[sel], beta[sel], cu2, pool,
+                                         [3, 1], [0, 2], pos0=[128, 192], ckpt_interval=iv)
+    np.testing.assert_allclose(o2[:T - 128], o[128:T], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(o2[T - 128:], o[T + 192:], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(out[0], Sf[0], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(out[2], Sf[1], rtol=1e-10, atol=1e-12)
+    np.testing.assert_array_equal(out[[1, 3, 4]], pool[[1, 3, 4]])
+    # rungs of sequence 0 at 256, 384; of sequence 1 at 256, 384 (rows 1, 2 of each)
+    assert ck2.shape[0] == 4
+    np.testing.assert_allclose(ck2[0:2], ck[1:3], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(ck2[2:4], ck[4:6], rtol=1e-10, atol=1e-12)
+    assert list(ckpt_offsets([T - 128, T - 192], iv, pos0=[128, 192])) == [0, 2, 4]

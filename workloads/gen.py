@@ -231,10 +231,17 @@ def varlen_lengths(seed: int, n: int, lo: int = 512, hi: int = 32768) -> np.ndar
     return np.clip(np.floor(np.exp(u)).astype(np.int64), lo, hi)
 
 
-def ckpt_offsets(lengths, interval: int) -> np.ndarray:
-    """First checkpoint row of each sequence: rungs at p = m*interval <= len, m >= 1."""
+def ckpt_offsets(lengths, interval: int, pos0=None) -> np.ndarray:
+    """First checkpoint row of each sequence: rungs at p = m*interval <= len, m >= 1.
+
+    With pos0 (absolute start positions), rungs sit at absolute multiples P of
+    the interval with pos0 < P <= pos0 + len."""
     lengths = np.asarray(lengths, dtype=np.int64)
-    per = lengths // interval if interval > 0 else np.zeros_like(lengths)
+    if interval > 0 and pos0 is not None:
+        p0 = np.asarray(pos0, dtype=np.int64)
+        per = (p0 + lengths) // interval - p0 // interval
+    else:
+        per = lengths // interval if interval > 0 else np.zeros_like(lengths)
     off = np.zeros(len(lengths) + 1, dtype=np.int64)
     off[1:] = np.cumsum(per)
     return off
