@@ -79,6 +79,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-resume", action="store_true", help="skip the resume measurement")
+    ap.add_argument("--no-conv", action="store_true", help="skip the short-conv measurement")
     ap.add_argument("--decode-launches", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -172,6 +173,45 @@ def resume_measure(K, w, t, launches: int) -> dict:
             "kernel": "chunk_engine<prefill> from a state pool", "tokens_per_s": round(w.T / (ms * 1e-3), 1),
             "launch_ms": round(ms, 4), "launches_timed": launches, "rungs": int(off_np[-1]),
             "alg_bytes_per_launch": int(alg),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
+def conv_measure(K, w, t, launches: int) -> dict:
+    """kda_short_conv (width 4, SiLU, one sequence) over each of q, k, v of
+    the workload, three launches per repetition, HIP events around each
+    repetition.  Algorithmic bytes: every input element read once and every
+    output element written once, in the I/O dtype."""
+    import torch
+    C = w.H * w.dk
+    gen = torch.Generator(device="cuda").manual_seed(46006)
+    weights = [torch.randn((C, 4), generator=gen, device="cuda") * 0.5 for _ in range(3)]
+    bias = [0.1 * torch.randn(C, generator=gen, device="cuda") for _ in range(3)]
+    xs = [t[n].reshape(w.T, C) for n in ("q", "k", "v")]
+    ys = [torch.empty_like(x) for x in xs]
+    cu = t["cu_seqlens"]
+    stream = torch.cuda.current_stream()
+
+    def call():
+        for x, y, wt, b in zip(xs, ys, weights, bias):
+            K.kda_short_conv(x, cu, wt, b, activation=K.KDA_ACT_SILU, out=y)
+    call()
+    pairs = []
+    for _ in range(launches):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+    io_bytes = 2 if w.dtype == "bf16" else 4
+    alg = 3 * 2 * w.T * C * io_bytes
+    gbs = alg / (ms * 1e-3) / 1e9
+    return {"workload": f"q, k, v of {w.name} ({w.T} x {C} each), width 4, SiLU",
+            "kernel": "conv_kernel<bf16,4>", "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+            "ms_qkv": round(ms, 4), "launches_timed": 3 * launches, "alg_bytes": int(alg),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
@@ -362,6 +402,8 @@ def main():
     }
     if segmented and not args.no_resume:
         result["resume"] = resume_measure(K, w, t, args.roofline_launches)
+    if not args.no_conv:
+        result["short_conv"] = conv_measure(K, w, t, args.roofline_launches)
     if not args.no_decode:
         del t
         result["decode"] = decode_measure(K, args.decode_launches)

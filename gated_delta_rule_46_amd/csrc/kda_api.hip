@@ -355,3 +355,77 @@ int kda_decode(const kda_config *cfg, int32_t N, const void *q, const void *k, c
 }
 
 }  // extern "C"
+
+namespace {
+
+int check_conv_common(int32_t io_dtype, int32_t channels, int32_t width, const void *x, int64_t T) {
+    if (io_dtype != KDA_DTYPE_F32 && io_dtype != KDA_DTYPE_BF16)
+        return fail(KDA_ERR_ARG, "io_dtype must be KDA_DTYPE_F32 or KDA_DTYPE_BF16 (got %d)", io_dtype);
+    if (channels <= 0 || channels % 8 != 0)
+        return fail(KDA_ERR_UNSUPPORTED, "channels must be a positive multiple of 8 (got %d)", channels);
+    if (width < 2 || width > 8)
+        return fail(KDA_ERR_UNSUPPORTED, "width must be in [2, 8] (got %d)", width);
+    if (T < 0) return fail(KDA_ERR_ARG, "T must be >= 0 (got %lld)", (long long)T);
+    KDA_TRY(check_tensor(x, "x", T > 0));
+    return KDA_OK;
+}
+
+int check_conv_state(const kda_conv_state *st) {
+    if (!st) return KDA_OK;
+    if (st->n_slots <= 0)
+        return fail(KDA_ERR_ARG, "state->n_slots must be positive (got %lld)", (long long)st->n_slots);
+    KDA_TRY(check_tensor(st->states, "state->states", true));
+    KDA_TRY(check_tensor(st->read_idx, "state->read_idx", false, 4));
+    KDA_TRY(check_tensor(st->write_idx, "state->write_idx", false, 4));
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_short_conv(int32_t io_dtype, int32_t channels, int32_t width, int32_t activation,
+                   const void *x, int64_t T, const int64_t *cu_seqlens, int32_t N,
+                   const float *weight, const float *bias, const kda_conv_state *state, void *y,
+                   void *stream) {
+    KDA_TRY(check_conv_common(io_dtype, channels, width, x, T));
+    if (activation != KDA_ACT_NONE && activation != KDA_ACT_SILU)
+        return fail(KDA_ERR_ARG, "activation must be KDA_ACT_NONE or KDA_ACT_SILU (got %d)", activation);
+    if (N < 0) return fail(KDA_ERR_ARG, "N must be >= 0 (got %d)", N);
+    if (T > 0 && N == 0) return fail(KDA_ERR_ARG, "T > 0 needs at least one sequence");
+    if ((T + 63) / 64 > INT32_MAX) return fail(KDA_ERR_UNSUPPORTED, "T is too large for one launch");
+    KDA_TRY(check_conv_state(state));
+    if (N == 0) return ok();
+    KDA_TRY(check_tensor(cu_seqlens, "cu_seqlens", true, 8));
+    KDA_TRY(check_tensor(weight, "weight", true, 4));
+    KDA_TRY(check_tensor(bias, "bias", false, 4));
+    KDA_TRY(check_tensor(y, "y", T > 0));
+    if (T > 0 && x == y) return fail(KDA_ERR_ARG, "y must not alias x");
+    kda::ConvArgs a{};
+    a.x = x; a.y = y; a.weight = weight; a.bias = bias; a.cu = cu_seqlens;
+    a.N = N; a.C = channels; a.T = T; a.act = activation;
+    a.win = state ? state->states : nullptr;
+    a.n_slots = state ? state->n_slots : 0;
+    a.read_idx = state ? state->read_idx : nullptr;
+    a.write_idx = state ? state->write_idx : nullptr;
+    return launched(kda::launch_conv(io_dtype == KDA_DTYPE_BF16, width, a, (hipStream_t)stream),
+                    "short conv");
+}
+
+int kda_conv_halo(int32_t io_dtype, int32_t channels, int32_t width, const void *x, int64_t T,
+                  const int64_t *bounds, int32_t nseg, const kda_conv_state *dst, void *stream) {
+    KDA_TRY(check_conv_common(io_dtype, channels, width, x, T));
+    if (nseg < 0) return fail(KDA_ERR_ARG, "nseg must be >= 0 (got %d)", nseg);
+    if (!dst) return fail(KDA_ERR_ARG, "dst is NULL");
+    KDA_TRY(check_conv_state(dst));
+    if (nseg == 0) return ok();
+    KDA_TRY(check_tensor(dst->write_idx, "dst->write_idx", true, 4));
+    KDA_TRY(check_tensor(bounds, "bounds", true, 8));
+    kda::ConvArgs a{};
+    a.x = x; a.cu = bounds; a.N = nseg; a.C = channels; a.T = T;
+    a.win = dst->states; a.n_slots = dst->n_slots; a.write_idx = dst->write_idx;
+    return launched(kda::launch_conv_halo(io_dtype == KDA_DTYPE_BF16, width, a, (hipStream_t)stream),
+                    "conv halo");
+}
+
+}  // extern "C"

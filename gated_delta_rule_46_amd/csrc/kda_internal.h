@@ -84,4 +84,20 @@ struct DecodeArgs {
 bool decode_supported(int dk, int dv);
 hipError_t launch_decode(bool bf16, int dk, int dv, const DecodeArgs &a, hipStream_t s);
 
+// Short causal convolution over tokens (kda_conv.hip).
+struct ConvArgs {
+    const void *x;               // [T, C] I/O dtype
+    void *y;                     // [T, C] I/O dtype
+    void *win;                   // window slots [n_slots, W-1, C], I/O dtype (nullable)
+    const float *weight;         // [C, W]
+    const float *bias;           // [C] (nullable)
+    const int64_t *cu;           // [N+1] sequence (or segment) bounds
+    int32_t N, C;
+    int64_t T, n_slots;
+    const int32_t *read_idx, *write_idx;   // [N] (nullable)
+    int32_t act;                 // 0 none, 1 SiLU
+};
+hipError_t launch_conv(bool bf16, int width, const ConvArgs &a, hipStream_t s);
+hipError_t launch_conv_halo(bool bf16, int width, const ConvArgs &a, hipStream_t s);
+
 }  // namespace kda

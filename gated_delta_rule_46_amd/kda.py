@@ -21,8 +21,9 @@ CHUNK = 64
 
 EXPORTS = ("kda_prefill_workspace", "kda_prefill", "kda_prefill_resume", "kda_segment_package",
            "kda_segment_scan_workspace", "kda_segment_scan", "kda_output_fixup",
-           "kda_checkpoint_write", "kda_decode", "kda_status_string", "kda_last_error",
-           "kda_version")
+           "kda_checkpoint_write", "kda_decode", "kda_short_conv", "kda_conv_halo",
+           "kda_status_string", "kda_last_error", "kda_version")
+KDA_ACT_NONE, KDA_ACT_SILU = 0, 1
 
 
 class KdaError(RuntimeError):
@@ -47,6 +48,11 @@ class kda_state_pool(ctypes.Structure):
                 ("read_idx", ctypes.c_void_p), ("write_idx", ctypes.c_void_p)]
 
 
+class kda_conv_state(ctypes.Structure):
+    _fields_ = [("states", ctypes.c_void_p), ("n_slots", ctypes.c_int64),
+                ("read_idx", ctypes.c_void_p), ("write_idx", ctypes.c_void_p)]
+
+
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is missing: build it with "
@@ -55,6 +61,7 @@ def _load():
     P, S, I32, I64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
     cfgp, ckp = ctypes.POINTER(kda_config), ctypes.POINTER(kda_ckpt)
     poolp = ctypes.POINTER(kda_state_pool)
+    convp = ctypes.POINTER(kda_conv_state)
     sig = {
         "kda_prefill_workspace": (S, [cfgp, I64, I32]),
         "kda_prefill": (ctypes.c_int, [cfgp, P, P, P, P, P, P, I32, I64, P, P, P, ckp, P, S, P]),
@@ -67,6 +74,8 @@ def _load():
         "kda_output_fixup": (ctypes.c_int, [cfgp, P, P, P, P, I64, P, I32, P, P, P, S, P]),
         "kda_checkpoint_write": (ctypes.c_int, [cfgp, ckp, I64, P, I32, P, P, P, P]),
         "kda_decode": (ctypes.c_int, [cfgp, I32, P, P, P, P, P, I32, poolp, P, P]),
+        "kda_short_conv": (ctypes.c_int, [I32, I32, I32, I32, P, I64, P, I32, P, P, convp, P, P]),
+        "kda_conv_halo": (ctypes.c_int, [I32, I32, I32, P, I64, P, I32, convp, P]),
         "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "kda_last_error": (ctypes.c_char_p, []),
         "kda_version": (ctypes.c_char_p, []),
@@ -347,3 +356,65 @@ def kda_decode(q, k, v, g, beta, pool, read_idx, write_idx, *, gate_logits=False
                         int(bool(gate_logits)), ctypes.byref(pl), _p(o), _stream(stream))
     _check(st, "kda_decode")
     return o
+
+
+def _io_dtype(dtype):
+    if dtype == torch.bfloat16:
+        return KDA_DTYPE_BF16
+    if dtype == torch.float32:
+        return KDA_DTYPE_F32
+    raise TypeError(f"x must be bfloat16 or float32, got {dtype}")
+
+
+def _conv_state(windows, read_idx, write_idx, N, C, W, dtype, dev):
+    if windows is None:
+        return None
+    n_slots = windows.shape[0]
+    _need(windows, "windows", (n_slots, W - 1, C), dtype, dev)
+    if read_idx is not None:
+        _need(read_idx, "read_idx", (N,), torch.int32, dev)
+    if write_idx is not None:
+        _need(write_idx, "write_idx", (N,), torch.int32, dev)
+    return kda_conv_state(ctypes.c_void_p(windows.data_ptr()), n_slots, _p(read_idx), _p(write_idx))
+
+
+def kda_short_conv(x, cu_seqlens, weight, bias=None, *, windows=None, read_idx=None,
+                   write_idx=None, activation=KDA_ACT_NONE, out=None, stream=None):
+    """Causal depthwise convolution over tokens of x [T, C] (bf16 or fp32),
+    weight [C, W] fp32, bias [C] fp32 or None, sequences by cu_seqlens
+    (int64 [N+1]).  windows [n_slots, W-1, C] (x's dtype) with read_idx /
+    write_idx (int32 [N]) carry each sequence's window in and out; the new
+    windows are written in place.  Returns y [T, C]."""
+    T, C = x.shape
+    W = weight.shape[1]
+    dev = x.device
+    N = cu_seqlens.numel() - 1
+    _need(x, "x", (T, C), x.dtype, dev)
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int64, dev)
+    _need(weight, "weight", (C, W), torch.float32, dev)
+    if bias is not None:
+        _need(bias, "bias", (C,), torch.float32, dev)
+    y = out if out is not None else torch.empty((T, C), dtype=x.dtype, device=dev)
+    _need(y, "out", (T, C), x.dtype, dev)
+    st = _conv_state(windows, read_idx, write_idx, N, C, W, x.dtype, dev)
+    rc = LIB.kda_short_conv(_io_dtype(x.dtype), C, W, int(activation), _p(x), T, _p(cu_seqlens), N,
+                            _p(weight), _p(bias), ctypes.byref(st) if st is not None else None,
+                            _p(y), _stream(stream))
+    _check(rc, "kda_short_conv")
+    return y
+
+
+def kda_conv_halo(x, bounds, width, windows, write_idx, *, stream=None):
+    """Copies the width-1 rows before each bounds[j+1] of x [T, C] into
+    windows[write_idx[j]] (zeros before row 0); returns windows."""
+    T, C = x.shape
+    dev = x.device
+    nseg = bounds.numel() - 1
+    _need(bounds, "bounds", (nseg + 1,), torch.int64, dev)
+    st = _conv_state(windows, None, write_idx, nseg, C, width, x.dtype, dev)
+    if st is None:
+        raise ValueError("windows is required")
+    rc = LIB.kda_conv_halo(_io_dtype(x.dtype), C, int(width), _p(x), T, _p(bounds), nseg,
+                           ctypes.byref(st), _stream(stream))
+    _check(rc, "kda_conv_halo")
+    return windows

@@ -38,6 +38,10 @@
  *    PR #2709, Changes: prefix caching of KDA state; demand checkpoints and
  *    the prompt-end anchor floored onto the chunk grid).
  *
+ *  - Short convolution (kda_short_conv, kda_conv_halo): the causal
+ *    depthwise convolution KDA applies to q, k, v along tokens, with a
+ *    per-sequence window state and the halo between segments.
+ *
  *  - Decode (kda_decode): one new token per sequence against a pool of
  *    states addressed by read and write slots (ROCm/ATOM PR #2709, review
  *    notes: the fused sigmoid-gated delta-rule update takes a read-side state
@@ -50,10 +54,13 @@
  *    beta [T,H]; states [., H, dk, dv] (key-major); M [., H, dk, dk].
  *  - q, k, v, o are float32 (io_dtype KDA_DTYPE_F32) or bfloat16
  *    (KDA_DTYPE_BF16, raw 16-bit storage).  g, beta and all states are
- *    float32.  Arithmetic: fp32 accumulation; matrix products on MFMA with
- *    bf16 operands for bf16 I/O and fp32 operands for fp32 I/O.
+ *    float32 (the short convolution's windows are in the I/O dtype).
+ *    Arithmetic: fp32 accumulation; matrix products on MFMA with bf16
+ *    operands for bf16 I/O and fp32 operands for fp32 I/O.
  *  - Supported shapes: dk == dv in {64, 128} for bf16, dk == dv == 64 for
- *    fp32; chunk == 64.  Other shapes return KDA_ERR_UNSUPPORTED.
+ *    fp32; chunk == 64 (kda_decode: dk, dv in {64, 128} for both dtypes; the
+ *    short convolution: see there).  Other shapes return
+ *    KDA_ERR_UNSUPPORTED.
  *  - Every pointer is a device pointer unless stated.  Tensors (q, k, v, g,
  *    o, states, M, D, workspace) must be 16-byte aligned, beta 4-byte and the
  *    int64 index arrays 8-byte aligned (KDA_ERR_ALIGN otherwise).
@@ -264,6 +271,61 @@ int kda_checkpoint_write(const kda_config *cfg, const kda_ckpt *ckpt, int64_t T,
 int kda_decode(const kda_config *cfg, int32_t N, const void *q, const void *k, const void *v,
                const float *g, const float *beta, int32_t gate_logits,
                const kda_state_pool *pool, void *o, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Short causal convolution over tokens                                      */
+/* ------------------------------------------------------------------------ */
+
+#define KDA_ACT_NONE 0
+#define KDA_ACT_SILU 1
+
+/*
+ * Window slots of the short convolution: states [n_slots, width-1, channels]
+ * in the I/O dtype hold the last width-1 inputs of a sequence (oldest row
+ * first).  read_idx[n] is the slot read as sequence n's window (NULL, or an
+ * index outside [0, n_slots): zeros); write_idx[n] the slot that receives its
+ * new window (NULL or outside: not stored).  Windows are read before any is
+ * written, so a sequence may update its own slot in place; a call's write
+ * slots must differ from one another and from every other sequence's read
+ * slot.
+ */
+typedef struct {
+    void *states;
+    int64_t n_slots;
+    const int32_t *read_idx;
+    const int32_t *write_idx;
+} kda_conv_state;
+
+/*
+ * Depthwise causal convolution along tokens (kern PR #44: the varlen stage
+ * kernels gather the KDA short-conv inputs per sequence and update its
+ * window; ROCm/ATOM PR #2709: the conv state follows a fork through a read
+ * index).  For sequence n (rows cu_seqlens[n] .. cu_seqlens[n+1]-1 of
+ * x [T, channels]) and x~ = (its window, its rows):
+ *     y_t[c] = act(bias[c] + sum_{j<width} weight[c][j] * x~_{t-width+1+j}[c])
+ * (the last tap multiplies the current token); its new window is the last
+ * width-1 rows of x~.  act: KDA_ACT_NONE or KDA_ACT_SILU (z / (1 + e^-z)).
+ *   x, y [T, channels] in io_dtype, 16-byte aligned, y not aliasing x;
+ *   weight [channels, width] fp32, bias [channels] fp32 or NULL;
+ *   cu_seqlens device int64 [N+1]; state NULL (zero windows, none stored).
+ * channels a multiple of 8; width in [2, 8].  Decode is the case of one
+ * token per sequence.  Two launches: outputs, then the new windows.
+ */
+int kda_short_conv(int32_t io_dtype, int32_t channels, int32_t width, int32_t activation,
+                   const void *x, int64_t T, const int64_t *cu_seqlens, int32_t N,
+                   const float *weight, const float *bias, const kda_conv_state *state, void *y,
+                   void *stream);
+
+/*
+ * Conv halo of a split sequence (pegainfer PR #970: a context-parallel rank
+ * publishes its conv halo tail with its KDA packages): for every segment j of
+ * x [T, channels] (bounds device int64 [nseg+1]), the width-1 input rows
+ * before bounds[j+1] (zeros before row 0) are copied into slot
+ * dst->write_idx[j] of dst->states.  Reading segment j+1 with that slot as its
+ * window makes a per-segment kda_short_conv equal to the whole-sequence one.
+ */
+int kda_conv_halo(int32_t io_dtype, int32_t channels, int32_t width, const void *x, int64_t T,
+                  const int64_t *bounds, int32_t nseg, const kda_conv_state *dst, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Diagnostics                                                               */

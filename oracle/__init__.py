@@ -23,6 +23,11 @@ and never imports it.
   Changes: prefix caching of KDA state, checkpoints on the chunk grid): the
   token recurrence run piece by piece between rung positions, each piece's
   final state being the rung.
+* ``short_conv`` / ``conv_halo`` -- the causal depthwise convolution over
+  tokens that KDA applies to q, k, v, with per-sequence windows (kern PR #44:
+  short-conv gather and window update per sequence; ROCm/ATOM PR #2709: the
+  conv state follows a fork through a read index) and the halo tail a
+  segment publishes for the next (pegainfer PR #970), from the definition.
 * ``mirror`` -- the fp64 chunkwise form (used only to pin chunk-size
   independence and the chunk algebra; never as the oracle).
 """
@@ -41,7 +46,7 @@ _lib = None
 
 __all__ = ["build", "prefill", "package", "compose", "identity_package", "scan_sequential",
            "scan_blelloch", "rel_l2", "threads", "softplus", "sigmoid", "decode",
-           "prefill_resume"]
+           "prefill_resume", "silu", "short_conv", "conv_halo"]
 
 
 def build(force: bool = True) -> str:
@@ -221,6 +226,66 @@ def prefill_resume(q, k, v, g, beta, cu_seqlens, pool, read_idx, write_idx, pos0
             out[w] = finals[n]
     ck = np.stack(rungs) if rungs else (np.zeros((0, H, dk, dv)) if ckpt_interval else None)
     return o, out, ck
+
+
+# ---------------------------------------------------------------------------
+# Short causal convolution over tokens
+# ---------------------------------------------------------------------------
+def silu(z):
+    """z * sigmoid(z) in fp64."""
+    z = np.asarray(z, dtype=np.float64)
+    return z * sigmoid(z)
+
+
+def short_conv(x, cu_seqlens, weight, bias=None, windows=None, read_idx=None, write_idx=None,
+               activation=0):
+    """y_t[c] = act(bias[c] + sum_j weight[c, j] * xx[t + j, c]) for each
+    sequence, where xx is the sequence's window (W-1 rows, zeros when absent)
+    followed by its rows of x [T, C]; the last tap multiplies the current
+    token.  Returns (y [T, C], new windows [n_slots, W-1, C] or None); the new
+    window of sequence n (last W-1 rows of xx) goes to slot write_idx[n]
+    after every window has been read.  All fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    weight = np.asarray(weight, dtype=np.float64)
+    T, C = x.shape
+    W = weight.shape[1]
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    old = None if windows is None else np.asarray(windows, dtype=np.float64)
+    new = None if old is None else old.copy()
+    n_slots = 0 if old is None else old.shape[0]
+    y = np.zeros((T, C))
+    for n in range(N):
+        a, b = int(cu[n]), int(cu[n + 1])
+        r = -1 if read_idx is None else int(read_idx[n])
+        win = old[r] if 0 <= r < n_slots else np.zeros((W - 1, C))
+        xx = np.concatenate([win, x[a:b]], axis=0)
+        L = b - a
+        acc = np.zeros((L, C)) if bias is None else np.broadcast_to(
+            np.asarray(bias, dtype=np.float64), (L, C)).copy()
+        for j in range(W):
+            acc += weight[:, j] * xx[j:j + L]
+        y[a:b] = silu(acc) if activation == 1 else acc
+        w = -1 if write_idx is None else int(write_idx[n])
+        if 0 <= w < n_slots:
+            new[w] = xx[-(W - 1):]
+    return y, new
+
+
+def conv_halo(x, bounds, width, windows, write_idx):
+    """Slot write_idx[j] <- the width-1 rows of x before bounds[j+1] (zeros
+    before row 0).  Returns the new windows (fp64)."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.asarray(windows, dtype=np.float64).copy()
+    for j in range(len(bounds) - 1):
+        w = int(write_idx[j])
+        if not 0 <= w < out.shape[0]:
+            continue
+        e = int(bounds[j + 1])
+        for kk in range(width - 1):
+            row = e - (width - 1) + kk
+            out[w, kk] = x[row] if row >= 0 else 0.0
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -256,3 +256,27 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     mod = importlib.util.module_from_spec(spec)
     with pytest.raises(ImportError, match="libkda.so"):
         spec.loader.exec_module(mod)
+
+
+def test_short_conv_validates():
+    st = K.kda_conv_state(FAKE, 4, FAKE, FAKE)
+
+    def conv(dtype=1, C=64, W=4, act=0, x=FAKE, T=128, N=2, y=FAKE + 4096, state=st, weight=FAKE):
+        return K.LIB.kda_short_conv(dtype, C, W, act, x, T, FAKE, N, weight, None,
+                                    ctypes.byref(state) if state else None, y, None)
+    assert conv(dtype=3) == K.KDA_ERR_ARG
+    assert conv(C=60) == K.KDA_ERR_UNSUPPORTED and "multiple of 8" in last_error()
+    assert conv(W=1) == K.KDA_ERR_UNSUPPORTED and conv(W=9) == K.KDA_ERR_UNSUPPORTED
+    assert conv(act=2) == K.KDA_ERR_ARG
+    assert conv(N=0) == K.KDA_ERR_ARG            # T > 0 with no sequence
+    assert conv(T=0, N=0, x=None, y=None) == K.KDA_OK
+    assert conv(x=MISALIGNED) == K.KDA_ERR_ALIGN
+    assert conv(y=FAKE) == K.KDA_ERR_ARG and "alias" in last_error()
+    assert conv(weight=None) == K.KDA_ERR_ARG
+    assert conv(state=K.kda_conv_state(FAKE, 0, FAKE, FAKE)) == K.KDA_ERR_ARG
+    assert conv(state=K.kda_conv_state(FAKE, 4, FAKE + 2, FAKE)) == K.KDA_ERR_ALIGN
+    halo = K.LIB.kda_conv_halo(1, 64, 4, FAKE, 128, FAKE, 2, None, None)
+    assert halo == K.KDA_ERR_ARG and "dst is NULL" in last_error()
+    halo = K.LIB.kda_conv_halo(1, 64, 4, FAKE, 128, FAKE, 2,
+                               ctypes.byref(K.kda_conv_state(FAKE, 4, None, None)), None)
+    assert halo == K.KDA_ERR_ARG and "write_idx" in last_error()

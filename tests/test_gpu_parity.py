@@ -444,6 +444,98 @@ def test_decode_empty_batch(K):
     assert o.shape == (0, 1, 64) and torch.equal(pool, before)
 
 
+# ---------------------------------------------------------------------------
+# Short causal convolution
+# ---------------------------------------------------------------------------
+def _conv_case(K, c, act, name):
+    import torch
+    from workloads.device import conv_to_torch
+    W = c.weight.shape[1]
+    say(f"short conv {name}: T={c.x.shape[0]} C={c.x.shape[1]} W={W} {c.dtype} act={act}")
+    t = conv_to_torch(c)
+    before = t["windows"].clone()
+    y = K.kda_short_conv(t["x"], t["cu_seqlens"], t["weight"], t["bias"], windows=t["windows"],
+                         read_idx=t["read_idx"], write_idx=t["write_idx"], activation=act)
+    sync()
+    y_ref, win_ref = oracle.short_conv(c.f64("x"), c.cu_seqlens, c.weight, c.bias,
+                                       windows=c.f64("windows"), read_idx=c.read_idx,
+                                       write_idx=c.write_idx, activation=act)
+    assert_close(f"short conv {name} y", to_numpy_f64(y), y_ref, OUT_TOL[c.dtype])
+    # windows hold inputs: bit-exact
+    np.testing.assert_array_equal(to_numpy_f64(t["windows"]), win_ref)
+    n_slots = c.windows.shape[0]
+    written = {int(w) for w in c.write_idx if 0 <= w < n_slots}
+    kept = [i for i in range(n_slots) if i not in written]
+    assert torch.equal(t["windows"][kept], before[kept])
+
+
+@pytest.mark.parametrize("dtype,W,act", [("bf16", 4, 1), ("bf16", 2, 0), ("f32", 8, 1), ("f32", 3, 0)])
+def test_short_conv_parity(K, dtype, W, act):
+    """Ragged sequences (1 to 300 rows, one empty) across 64-row tiles, with
+    in-place, forked, fresh and discarded windows."""
+    from workloads import make_conv_case
+    c = make_conv_case("conv-small", [300, 1, 0, 65, 2, 130, 7, 64], 264, W, dtype, 4621)
+    _conv_case(K, c, act, f"{dtype} W={W}")
+
+
+def test_short_conv_decode_batch(K):
+    """One token per sequence (64 sequences) over q, k, v side by side:
+    the decode form of the convolution, windows shifted in their slots."""
+    from workloads import make_conv_case
+    c = make_conv_case("conv-decode", [1] * 64, 3 * 32 * 128, 4, "bf16", 4622)
+    _conv_case(K, c, 1, "decode n64")
+
+
+def test_short_conv_halo_equals_whole_sequence(K):
+    """Per-segment convolution fed by kda_conv_halo equals the whole
+    sequence's convolution bit for bit (same fp32 sums per output)."""
+    import torch
+    from workloads import make_conv_case
+    c = make_conv_case("conv-halo", [4096], 512, 4, "bf16", 4623, n_slots=1,
+                       read_idx=[-1], write_idx=[-1])
+    from workloads.device import conv_to_torch
+    t = conv_to_torch(c)
+    say("conv halo: 4096 rows, 512 channels, W=4, 5 segments")
+    y_all = K.kda_short_conv(t["x"], t["cu_seqlens"], t["weight"], t["bias"], activation=1)
+    bounds = torch.tensor([0, 640, 1280, 2048, 3072, 4096], dtype=torch.int64, device="cuda")
+    halos = torch.zeros((6, 3, 512), dtype=torch.bfloat16, device="cuda")
+    K.kda_conv_halo(t["x"], bounds, 4, halos, torch.arange(1, 6, dtype=torch.int32, device="cuda"))
+    y_seg = K.kda_short_conv(t["x"], bounds, t["weight"], t["bias"], windows=halos,
+                             read_idx=torch.arange(0, 5, dtype=torch.int32, device="cuda"),
+                             activation=1)
+    sync()
+    assert torch.equal(y_seg, y_all)
+    assert torch.equal(halos[1], t["x"][637:640])
+    assert float(halos[0].float().abs().max()) == 0.0
+
+
+def test_short_conv_full_size_sampled(K):
+    """q of the 131,072-token workload (4096 channels, bf16, W = 4, SiLU) in
+    the launch bench.py times; 512 sampled rows recomputed by the oracle from
+    their own W rows."""
+    import torch
+    w = standard_workload(3)
+    T, H, dk = w.q.shape
+    C = H * dk
+    rng = np.random.default_rng(4624)
+    weight = (rng.standard_normal((C, 4)) / 2.0).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(C)).astype(np.float32)
+    t = to_torch(w)
+    x = t["q"].reshape(T, C)
+    say("short conv full size: T=131072, C=4096, bf16")
+    y = K.kda_short_conv(x, torch.tensor([0, T], dtype=torch.int64, device="cuda"),
+                         torch.from_numpy(weight).cuda(), torch.from_numpy(bias).cuda(), activation=1)
+    sync()
+    rows = np.sort(rng.choice(T, 512, replace=False))
+    rows[0] = 0
+    got = to_numpy_f64(y[torch.from_numpy(rows).cuda()])
+    from workloads import to_f64
+    xq = w.q.reshape(T, C)
+    ref = np.stack([oracle.short_conv(to_f64(xq[max(0, r - 3):r + 1], "bf16"), [0, min(r, 3) + 1],
+                                      weight, bias, activation=1)[0][-1] for r in rows])
+    assert_close("short conv full-size sampled rows", got, ref, OUT_TOL["bf16"])
+
+
 def test_config1_full(K):
     say("config1: T=8192 H=32 d=128 bf16 chunked prefill (sampled heads 0, 17, 31)")
     import torch

@@ -490,3 +490,70 @@ def test_prefill_resume_matches_continuous_run():
     np.testing.assert_allclose(ck2[0:2], ck[1:3], rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(ck2[2:4], ck[4:6], rtol=1e-10, atol=1e-12)
     assert list(ckpt_offsets([T - 128, T - 192], iv, pos0=[128, 192])) == [0, 2, 4]
+
+
+# ---------------------------------------------------------------------------
+# Short causal convolution
+# ---------------------------------------------------------------------------
+def test_short_conv_identity_and_shift_taps():
+    """A tap on the current token is the identity; a tap on the oldest row
+    delays by W-1 rows, reading the window first.  Catches: reversed taps,
+    an off-by-one in the window, windows not stored or stored from x alone."""
+    rng = np.random.default_rng(41)
+    T, C, W = 10, 8, 4
+    x = rng.standard_normal((T, C))
+    win = rng.standard_normal((3, W - 1, C))
+    cu = [0, 2, 10]
+    ident = np.zeros((C, W)); ident[:, -1] = 1.0
+    y, new = oracle.short_conv(x, cu, ident, windows=win, read_idx=[1, -1], write_idx=[0, 2])
+    np.testing.assert_array_equal(y, x)
+    # sequence 0 has 2 rows: its new window is (oldest kept window row, its rows)
+    np.testing.assert_array_equal(new[0], np.concatenate([win[1][-1:], x[0:2]]))
+    np.testing.assert_array_equal(new[2], x[7:10])
+    np.testing.assert_array_equal(new[1], win[1])
+    shift = np.zeros((C, W)); shift[:, 0] = 1.0
+    y, _ = oracle.short_conv(x, cu, shift, windows=win, read_idx=[1, -1])
+    np.testing.assert_array_equal(y[0:2], win[1][0:2])
+    np.testing.assert_array_equal(y[2:5], 0.0)
+    np.testing.assert_array_equal(y[5:10], x[2:7])
+
+
+def test_short_conv_against_numpy_convolve():
+    """Each channel equals numpy's own 1-D convolution (kernel reversed,
+    'valid' over window + rows), plus bias, then SiLU = z * expit(z) from
+    scipy.  Catches: taps applied to the wrong rows, bias after the
+    activation, a wrong activation."""
+    from scipy.special import expit
+    rng = np.random.default_rng(42)
+    T, C, W = 37, 16, 5
+    x = rng.standard_normal((T, C))
+    w = rng.standard_normal((C, W))
+    bias = rng.standard_normal(C)
+    win = rng.standard_normal((1, W - 1, C))
+    y, _ = oracle.short_conv(x, [0, T], w, bias, windows=win, read_idx=[0], activation=1)
+    xx = np.concatenate([win[0], x])
+    for c in range(C):
+        z = np.convolve(xx[:, c], w[c, ::-1], mode="valid") + bias[c]
+        np.testing.assert_allclose(y[:, c], z * expit(z), rtol=1e-12, atol=1e-14)
+    assert oracle.silu(0.0) == 0.0
+
+
+def test_short_conv_window_chaining_and_halo():
+    """Convolving a sequence in two calls, the first call's window feeding
+    the second, equals one call; per-segment convolution with halo windows
+    equals the whole-sequence convolution.  Catches: windows holding outputs
+    instead of inputs, halo rows taken from the segment start."""
+    rng = np.random.default_rng(43)
+    T, C, W = 50, 8, 4
+    x = rng.standard_normal((T, C))
+    w = rng.standard_normal((C, W))
+    y_all, _ = oracle.short_conv(x, [0, T], w)
+    win = np.zeros((2, W - 1, C))
+    y1, win = oracle.short_conv(x[:21], [0, 21], w, windows=win, read_idx=[-1], write_idx=[1])
+    y2, _ = oracle.short_conv(x[21:], [0, T - 21], w, windows=win, read_idx=[1])
+    np.testing.assert_allclose(np.concatenate([y1, y2]), y_all, rtol=1e-13, atol=1e-14)
+    bounds = [0, 16, 30, 50]
+    halo = oracle.conv_halo(x, bounds, W, np.zeros((4, W - 1, C)), [1, 2, 3])
+    np.testing.assert_array_equal(halo[1], x[13:16])
+    y_seg, _ = oracle.short_conv(x, bounds, w, windows=halo, read_idx=[0, 1, 2])
+    np.testing.assert_allclose(y_seg, y_all, rtol=1e-13, atol=1e-14)

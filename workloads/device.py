@@ -43,3 +43,15 @@ def decode_to_torch(b, device="cuda") -> dict:
         "read_idx": torch.from_numpy(b.read_idx).to(device),
         "write_idx": torch.from_numpy(b.write_idx).to(device),
     }
+
+
+def conv_to_torch(c, device="cuda") -> dict:
+    return {
+        "x": _io_tensor(c.x, c.dtype, device),
+        "cu_seqlens": torch.from_numpy(c.cu_seqlens).to(device),
+        "weight": torch.from_numpy(c.weight).to(device),
+        "bias": torch.from_numpy(c.bias).to(device),
+        "windows": _io_tensor(c.windows, c.dtype, device),
+        "read_idx": torch.from_numpy(c.read_idx).to(device),
+        "write_idx": torch.from_numpy(c.write_idx).to(device),
+    }

@@ -32,9 +32,10 @@ __all__ = [
     "bf16_round_bits", "bf16_bits_to_f32", "to_f64", "leveled_segments",
     "varlen_lengths", "ckpt_offsets", "GATE_COST_Q", "SEGMENT_FLOOR",
     "DecodeBatch", "make_decode_batch", "decode_slots", "standard_decode_batch",
+    "ConvCase", "make_conv_case",
 ]
 
-T_Q, T_K, T_V, T_BETA, T_G, T_S0, T_POOL = 0, 1, 2, 3, 4, 5, 6
+T_Q, T_K, T_V, T_BETA, T_G, T_S0, T_POOL, T_CONV = 0, 1, 2, 3, 4, 5, 6, 7
 
 # Segment cost model coefficient and the per-segment token floor quoted by the
 # pegainfer "cross-process CP whale gang" PR (commit "whale rendezvous":
@@ -369,3 +370,50 @@ def standard_decode_batch(**over) -> DecodeBatch:
     """64 sequences (the varlen batch's count), H=32, d=128, bf16, 128-slot pool."""
     return make_decode_batch("kda-decode-n64-h32-d128-bf16", 64, 32, 128, 128, "bf16",
                              46005, **over)
+
+
+# ----------------------------------------------------------------------------
+# Short convolution cases
+# ----------------------------------------------------------------------------
+@dataclass
+class ConvCase:
+    name: str
+    dtype: str
+    x: np.ndarray                   # [T, C] uint16 bf16 bits or float32
+    cu_seqlens: np.ndarray          # int64 [N+1]
+    weight: np.ndarray              # [C, W] float32
+    bias: np.ndarray                # [C] float32
+    windows: np.ndarray             # [n_slots, W-1, C] in x's storage
+    read_idx: np.ndarray            # int32 [N]
+    write_idx: np.ndarray           # int32 [N]
+
+    def f64(self, name: str) -> np.ndarray:
+        a = getattr(self, name)
+        if name in ("x", "windows"):
+            return to_f64(a, self.dtype)
+        return np.asarray(a, dtype=np.float64)
+
+
+def make_conv_case(name: str, lengths, C: int, W: int, dtype: str, seed: int,
+                   n_slots: int | None = None, read_idx=None, write_idx=None) -> ConvCase:
+    """x ~ N(0,1) [T, C]; taps ~ N(0, 1/W); bias ~ N(0, 0.1^2); windows ~
+    N(0,1); slots by decode_slots unless given."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cu = np.zeros(len(lengths) + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(lengths)
+    T, N = int(cu[-1]), len(lengths)
+    n_slots = 2 * N if n_slots is None else n_slots
+    rng = np.random.default_rng([seed, T_CONV])
+    x = rng.standard_normal((T, C), dtype=np.float32)
+    win = rng.standard_normal((n_slots, W - 1, C), dtype=np.float32)
+    weight = (rng.standard_normal((C, W), dtype=np.float32) / np.float32(np.sqrt(W))).astype(np.float32)
+    bias = (rng.standard_normal(C, dtype=np.float32) * np.float32(0.1)).astype(np.float32)
+    if dtype == "bf16":
+        x, win = bf16_round_bits(x), bf16_round_bits(win)
+    if read_idx is None or write_idx is None:
+        r, w = decode_slots(N, n_slots)
+        read_idx = r if read_idx is None else read_idx
+        write_idx = w if write_idx is None else write_idx
+    return ConvCase(name=name, dtype=dtype, x=x, cu_seqlens=cu, weight=weight, bias=bias,
+                    windows=win, read_idx=np.asarray(read_idx, dtype=np.int32),
+                    write_idx=np.asarray(write_idx, dtype=np.int32))
