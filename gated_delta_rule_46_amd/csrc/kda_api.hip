@@ -11,6 +11,7 @@
 
 #include "kda.h"
 #include "kda_internal.h"
+#include "kda_ops.h"
 
 namespace {
 

@@ -24,7 +24,7 @@
 // stores the new windows in a separate launch, after every read of the old
 // ones.
 
-#include "kda_internal.h"
+#include "kda_ops.h"
 
 namespace kda {
 namespace {

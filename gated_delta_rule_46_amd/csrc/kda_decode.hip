@@ -15,7 +15,7 @@
 // registers from the read to the write.  A wave reads four 256-byte row
 // segments per instruction.
 
-#include "kda_internal.h"
+#include "kda_ops.h"
 
 namespace kda {
 namespace {
