@@ -78,11 +78,15 @@ template <int DK, int NB, bool BF> struct Lds {
     static constexpr int o_aoff = o_bv + 64 * LDV * ES;               // hand-off: -A blocks
     static constexpr int o_td = o_aoff + 6 * 16 * LDT * ES;           // hand-off: T_bb [2][4]
     static constexpr int o_ad = o_td + 2 * 4 * 16 * LDT * ES;         // producer scratch
-    static constexpr int o_ro = o_ad + 4 * 16 * LDAD * 4;             // producer scratch
-    static constexpr int size = o_ro + 48 * LDQ * ES;
+    static constexpr int o_ro = o_ad + 4 * 16 * LDAD * 4;             // rhs of blocks 0-2
+    static constexpr int o_lk = o_ro + 48 * LDQ * ES;                 // lhs (K) of blocks 2, 3
+    static constexpr int o_lq = o_lk + 32 * LDQ * ES;                 // lhs (Q) of blocks 2, 3
+    static constexpr int o_cf = o_lq + 32 * LDQ * ES;                 // f32 [3][DK] rescales
+    static constexpr int size = o_cf + 3 * DK * 4;
     static_assert(o_qbar % 16 == 0 && o_rk % 16 == 0 && o_kbt % 16 == 0 && o_p % 16 == 0 &&
                   o_bv % 16 == 0 && o_aoff % 16 == 0 && o_td % 16 == 0 && o_ad % 16 == 0 &&
-                  o_ro % 16 == 0, "LDS alignment");
+                  o_ro % 16 == 0 && o_lk % 16 == 0 && o_lq % 16 == 0 && o_cf % 16 == 0,
+                  "LDS alignment");
     static_assert(size <= 160 * 1024, "LDS budget");
 };
 
@@ -167,6 +171,8 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
     T *s_td = (T *)(smem + L::o_td);
     float *s_ad = (float *)(smem + L::o_ad);
     T *s_ro = (T *)(smem + L::o_ro);
+    T *s_lk = (T *)(smem + L::o_lk);
+    T *s_lq = (T *)(smem + L::o_lq);
 
     const int lane = threadIdx.x & 63;
     const int H = a.H;
@@ -335,7 +341,10 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
                 for (int j = 0; j < 8; ++j) lq[j] = qx[j] * fq * e1[j];
                 lhsQ[kk] = O::cvt8(lq);
                 Pd = O::mma32(Pd, lhsQ[kk], rhsD[kk]);
+                if (B >= 2) O::stf(s_lq + (prow - 32) * L::LDQ + c0, lhsQ[kk]);
             }
+            // the far off-diagonal blocks of rows 32..63 are formed by consumer waves
+            if (B >= 2) O::stf(s_lk + (prow - 32) * L::LDQ + c0, lhsK[kk]);
             Ad = O::mma32(Ad, lhsK[kk], rhsD[kk]);
             // one 32-channel step at a time keeps the fp32 temporaries short-lived
             __builtin_amdgcn_sched_barrier(0);
@@ -383,8 +392,6 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
         // Factors of block B (log2 domain, all <= 1), rho_a = decay at the end
         // of block a:  [0] e^{rho_{B-1}}   (Qbar, R_k)
         //              [1] e^{G_C - rho_{B-1}}   (Kbar)
-        //              [2] e^{rho_{B-1} - rho_0}  (rhs of block 0, B >= 2)
-        //              [3] e^{rho_2 - rho_1}      (rhs of block 1, B = 3)
         float *fac = s_fac + B * 4 * DK;
         for (int ch = opaque(lane); ch < DK; ch += 64) {
             const float u0 = s_tot[ch], u1 = s_tot[DK + ch], u2 = s_tot[2 * DK + ch], u3 = s_tot[3 * DK + ch];
@@ -392,8 +399,6 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
             const float gc = u0 + u1 + u2 + u3;
             if (B > 0) fac[ch] = ex2(rho);
             fac[DK + ch] = ex2(gc - rho);
-            if (B == 2) fac[2 * DK + ch] = ex2(u1);
-            if (B == 3) { fac[2 * DK + ch] = ex2(u1 + u2); fac[3 * DK + ch] = ex2(u2); }
             if (B == 0) s_gam[ch] = ex2(gc);
         }
         wave_sync_lds();
@@ -441,24 +446,16 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        // Off-diagonal blocks: rhs rows of block a2 are referenced to the end of
-        // a2; blocks further back are rescaled by e^{rho_{B-1} - rho_{a2}} <= 1.
-#pragma unroll
-        for (int a2 = 0; a2 < B; ++a2) {
+        // The adjacent off-diagonal block (B, B-1): rhs rows of block B-1 are
+        // referenced to its end, which is where block B's lhs starts, so no
+        // rescale.  Blocks further back are formed by consumer waves.
+        if (B >= 1) {
+            constexpr int a2 = B >= 1 ? B - 1 : 0;
             f32x4 Ao = {0.f, 0.f, 0.f, 0.f}, P_ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
                 const int c0 = 32 * kk + 8 * gq;
-                F8 Bf = O::ld8(s_ro + (16 * a2 + m) * L::LDQ + c0);
-                if (a2 < B - 1) {
-                    const float *fs = fac + ((B == 3 && a2 == 1) ? 3 : 2) * DK + c0;
-                    const f32x4 f0 = *(const f32x4 *)fs, f1 = *(const f32x4 *)(fs + 4);
-                    float x[8];
-                    O::unpack8(Bf, x);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) { x[j] *= f0[j]; x[j + 4] *= f1[j]; }
-                    Bf = O::cvt8(x);
-                }
+                const F8 Bf = O::ld8(s_ro + (16 * a2 + m) * L::LDQ + c0);
                 Ao = O::mma32(Ao, lhsK[kk], Bf);
                 if (R::HAS_O) P_ = O::mma32(P_, lhsQ[kk], Bf);
             }
@@ -468,7 +465,6 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
                 dst[(4 * gq + i) * L::LDT + m] = (T)(-Ao[i]);
                 if (R::HAS_O) s_p[(16 * B + 4 * gq + i) * L::LDP + 16 * a2 + m] = (T)P_[i];
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -722,6 +718,51 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
         }
     };
 
+    // The three off-diagonal blocks that need a rescale, for the chunk the
+    // producers are preparing (between the two barriers, after the block
+    // totals are complete): consumer 0 forms (3,0), consumer 1 (3,1) and
+    // consumer 2 (2,0).  The rhs rows of block a2 are referenced to its end
+    // and block B's lhs to the end of block B-1, so the product carries
+    // e^{rho_{B-1} - rho_{a2}} <= 1 per channel, computed here from the totals.
+    auto offdiag = [&]() {
+        if (pw >= 3) return;
+        const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
+        const float *s_tot = (const float *)(smem + L::o_tot);
+        const T *s_ro = (const T *)(smem + L::o_ro);
+        const T *s_lk = (const T *)(smem + L::o_lk);
+        const T *s_lq = (const T *)(smem + L::o_lq);
+        T *s_aoffw = (T *)(smem + L::o_aoff);
+        T *s_pw = (T *)(smem + L::o_p);
+        float *cf = (float *)(smem + L::o_cf) + pw * DK;
+        const int B = pw == 2 ? 2 : 3;
+        const int a2 = pw == 1 ? 1 : 0;
+        for (int ch = opaque(lane); ch < DK; ch += 64) {
+            const float u1 = s_tot[DK + ch], u2 = s_tot[2 * DK + ch];
+            cf[ch] = ex2(pw == 0 ? u1 + u2 : (pw == 1 ? u2 : u1));
+        }
+        wave_sync_lds();
+        f32x4 Ao = {0.f, 0.f, 0.f, 0.f}, P_ = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            const int c0 = 32 * kk + 8 * gq;
+            float x[8];
+            O::unpack8(O::ld8(s_ro + (16 * a2 + m) * L::LDQ + c0), x);
+            const f32x4 f0 = *(const f32x4 *)(cf + c0), f1 = *(const f32x4 *)(cf + c0 + 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { x[j] *= f0[j]; x[j + 4] *= f1[j]; }
+            const F8 Bf = O::cvt8(x);
+            const int lrow = (16 * (B - 2) + m) * L::LDQ + c0;
+            Ao = O::mma32(Ao, O::ld8(s_lk + lrow), Bf);
+            if (R::HAS_O) P_ = O::mma32(P_, O::ld8(s_lq + lrow), Bf);
+        }
+        T *dst = s_aoffw + aoff_idx(B, a2) * 16 * L::LDT;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            dst[(4 * gq + i) * L::LDT + m] = (T)(-Ao[i]);
+            if (R::HAS_O) s_pw[(16 * B + 4 * gq + i) * L::LDP + 16 * a2 + m] = (T)P_[i];
+        }
+    };
+
     // Rung stores and the zero test after chunk c.
     auto rungs = [&](int c) {
         const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
@@ -751,6 +792,7 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
 
     // prologue: the producers prepare chunk 0
     __syncthreads();                                                          // BA
+    if (nchunks > 0) offdiag();
     __syncthreads();                                                          // BB
     for (int c = 0; c < nchunks; ++c) {
         if (R::CHECK0 && c > 0 && !(s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3])) {
@@ -768,6 +810,7 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
         apply(c);
         __syncthreads();                                                      // BA
         rungs(c);
+        if (c + 1 < nchunks) offdiag();
         __syncthreads();                                                      // BB
     }
 
