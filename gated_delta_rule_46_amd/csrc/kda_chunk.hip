@@ -18,8 +18,10 @@
 // producers do all the work of chunk c+1 that only needs their own block:
 // norms, decay scan, exponentials, diagonal Gram blocks and T_bb.  Between the
 // first barrier and the second the producers combine the block totals into
-// the per-channel factors, write the hand-off tiles and the off-diagonal Gram
-// blocks, while the consumers store checkpoint rungs and run the zero test.
+// the per-channel factors, write the hand-off tiles and the adjacent
+// off-diagonal Gram blocks (b, b-1), while the consumers form the three
+// farther blocks (3,0), (3,1), (2,0), store checkpoint rungs and run the zero
+// test.
 // T_bb is written during the consumers' phase, so it is double-buffered by
 // chunk parity; every other hand-off tile has a single copy.
 //
@@ -260,7 +262,28 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
 #pragma unroll
         for (int e = 0; e < KS * 8; ++e) gl[e] = scan16(gl[e] * kLog2e);
         float fk, fq = 0.f;
-        {
+        if constexpr (BF) {
+            // |row|^2 of the raw bf16 rows as the diagonal of their 16x16 Gram
+            // block on the matrix core; entry (r, r) sits in lane r + 16*(r/4),
+            // element r % 4.
+            f32x4 Gk = {0.f, 0.f, 0.f, 0.f}, Gq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const uint4 *)&raw.k[W8 * kk]);
+                Gk = O::mma32(Gk, kf, kf);
+                if (R::HAS_O) {
+                    const bf16x8 qf = __builtin_bit_cast(bf16x8, *(const uint4 *)&raw.q[W8 * kk]);
+                    Gq = O::mma32(Gq, qf, qf);
+                }
+            }
+            const int src = m + 16 * (m >> 2), e = m & 3;
+            const float dk = e == 0 ? Gk[0] : e == 1 ? Gk[1] : e == 2 ? Gk[2] : Gk[3];
+            fk = (a.l2norm ? rsqrtf(__shfl(dk, src) + kEps) : 1.f) * vm;
+            if (R::HAS_O) {
+                const float dq = e == 0 ? Gq[0] : e == 1 ? Gq[1] : e == 2 ? Gq[2] : Gq[3];
+                fq = (a.l2norm ? a.scale * rsqrtf(__shfl(dq, src) + kEps) : a.scale) * vm;
+            }
+        } else {
             float sk = 0.f, sq = 0.f;
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
@@ -371,10 +394,11 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) nxt[q4] = *(const f32x4 *)(ad + (r + 1) * L::LDAD + 4 * q4);
                 }
-                float s = (r == m) ? 1.f : 0.f;
+                // four partial sums keep the dependent chain short
+                float sp[4] = {(r == m) ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < r; ++i) s = fmaf(-cur[i >> 2][i & 3], tc[i], s);
-                tc[r] = s;
+                for (int i = 0; i < r; ++i) sp[i & 3] = fmaf(-cur[i >> 2][i & 3], tc[i], sp[i & 3]);
+                tc[r] = (sp[0] + sp[1]) + (sp[2] + sp[3]);
                 __builtin_amdgcn_sched_barrier(0);
             }
             T *td = s_td + ((c & 1) * 4 + B) * 16 * L::LDT;
