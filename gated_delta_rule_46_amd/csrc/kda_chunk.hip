@@ -6,8 +6,7 @@
 //
 //   producers (waves 0-3, one per 16-row block b of the chunk) prepare chunk
 //     c+1: loads (prefetched one chunk ahead), L2 norms, in-block cumulative
-//     log2-decay, exponentials, the Gram matrices A and P on MFMA and the
-//     diagonal 16x16 inverses T_bb = (I + A_bb)^-1;
+//     log2-decay, exponentials and the Gram matrices A and P on MFMA;
 //   consumers (waves 4-7) own a quarter of the state's columns each (fp32 MFMA
 //     accumulators) and apply chunk c:
 //         U = (I + A)^-1 (beta V - R_k S)       R_k = beta K*Gam
@@ -16,14 +15,14 @@
 // Two workgroup barriers per chunk.  Between the second barrier and the first
 // the consumers apply chunk c (reading every hand-off tile) while the
 // producers do all the work of chunk c+1 that only needs their own block:
-// norms, decay scan, exponentials, diagonal Gram blocks and T_bb.  Between the
+// norms, decay scan, exponentials and diagonal Gram blocks.  Between the
 // first barrier and the second the producers combine the block totals into
 // the per-channel factors, write the hand-off tiles and the adjacent
-// off-diagonal Gram blocks (b, b-1), while the consumers form the three
-// farther blocks (3,0), (3,1), (2,0), store checkpoint rungs and run the zero
-// test.
-// T_bb is written during the consumers' phase, so it is double-buffered by
-// chunk parity; every other hand-off tile has a single copy.
+// off-diagonal Gram blocks (b, b-1), while consumers 0-2 form the three
+// farther blocks (3,0), (3,1), (2,0), consumer 3 the diagonal inverses
+// T_bb = (I + A_bb)^-1, and all of them store checkpoint rungs and run the
+// zero test.  Every hand-off tile has a single copy (T_bb keeps two, by chunk
+// parity).
 //
 // Numerical scheme: one reference point per 16-row block.  The diagonal block
 // uses the block start (lhs factor <= 1, rhs factor <= e^{span of 16 tokens}),
@@ -374,37 +373,10 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
         }
         if (more) issue_kq();
 
-        // T_bb = (I + A_bb)^-1: column m by forward substitution on the lanes of
-        // group 0; row r+1 of A_bb is read while row r is being reduced.
+        // A_bb for the substitution (consumer 3 forms T_bb between the barriers)
         float *ad = s_ad + B * 16 * L::LDAD;
 #pragma unroll
         for (int i = 0; i < 4; ++i) ad[(4 * gq + i) * L::LDAD + m] = Ad[i];
-        wave_sync_lds();
-        if (gq == 0) {
-            float tc[16];
-            f32x4 nxt[4];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) nxt[q4] = *(const f32x4 *)(ad + 4 * q4);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                f32x4 cur[4];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nxt[q4];
-                if (r < 15) {
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) nxt[q4] = *(const f32x4 *)(ad + (r + 1) * L::LDAD + 4 * q4);
-                }
-                // four partial sums keep the dependent chain short
-                float sp[4] = {(r == m) ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int i = 0; i < r; ++i) sp[i & 3] = fmaf(-cur[i >> 2][i & 3], tc[i], sp[i & 3]);
-                tc[r] = (sp[0] + sp[1]) + (sp[2] + sp[3]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            T *td = s_td + ((c & 1) * 4 + B) * 16 * L::LDT;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) td[r * L::LDT + m] = (T)tc[r];
-        }
     };
 
     // Cross-block work of chunk c (runs while the consumers store rungs):
@@ -787,6 +759,38 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
         }
     };
 
+    // T_bb = (I + A_bb)^-1 of the four diagonal blocks of chunk cn, formed by
+    // consumer 3 between the barriers (the producers wrote A_bb before the
+    // first one): lane group g solves block g, lane m its column m, by forward
+    // substitution with row r+1 read while row r is reduced.
+    auto tbb = [&](int cn) {
+        if (pw != 3) return;
+        const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
+        const float *ad = (const float *)(smem + L::o_ad) + gq * 16 * L::LDAD;
+        float tc[16];
+        f32x4 nxt[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) nxt[q4] = *(const f32x4 *)(ad + 4 * q4);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            f32x4 cur[4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nxt[q4];
+            if (r < 15) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) nxt[q4] = *(const f32x4 *)(ad + (r + 1) * L::LDAD + 4 * q4);
+            }
+            // four partial sums keep the dependent chain short
+            float sp[4] = {(r == m) ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < r; ++i) sp[i & 3] = fmaf(-cur[i >> 2][i & 3], tc[i], sp[i & 3]);
+            tc[r] = (sp[0] + sp[1]) + (sp[2] + sp[3]);
+        }
+        T *td = (T *)(smem + L::o_td) + ((cn & 1) * 4 + gq) * 16 * L::LDT;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) td[r * L::LDT + m] = (T)tc[r];
+    };
+
     // Rung stores and the zero test after chunk c.
     auto rungs = [&](int c) {
         const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
@@ -816,7 +820,10 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
 
     // prologue: the producers prepare chunk 0
     __syncthreads();                                                          // BA
-    if (nchunks > 0) offdiag();
+    if (nchunks > 0) {
+        offdiag();
+        tbb(0);
+    }
     __syncthreads();                                                          // BB
     for (int c = 0; c < nchunks; ++c) {
         if (R::CHECK0 && c > 0 && !(s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3])) {
@@ -834,7 +841,10 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
         apply(c);
         __syncthreads();                                                      // BA
         rungs(c);
-        if (c + 1 < nchunks) offdiag();
+        if (c + 1 < nchunks) {
+            offdiag();
+            tbb(c + 1);
+        }
         __syncthreads();                                                      // BB
     }
 
