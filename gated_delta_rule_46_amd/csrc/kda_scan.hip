@@ -32,6 +32,35 @@ __device__ __forceinline__ bool nonzero4(float4 x) {
             (__builtin_bit_cast(uint32_t, x.z) & m) | (__builtin_bit_cast(uint32_t, x.w) & m)) != 0u;
 }
 
+// Block-cooperative N-float tile held in registers (PER float4 per thread):
+// every load of a tile is issued before any of its stores, so a copy costs one
+// memory latency even where source and destination may alias.
+template <int N> struct Tile {
+    static constexpr int PER = N / 4 / NTH;
+    static_assert(PER * 4 * NTH == N, "block size");
+    f32x4 x[PER];
+    __device__ __forceinline__ void load(const float *p) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) x[i] = ((const f32x4 *)p)[threadIdx.x + i * NTH];
+    }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    __device__ __forceinline__ void store(float *p) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) ((f32x4 *)p)[threadIdx.x + i * NTH] = x[i];
+    }
+    __device__ __forceinline__ bool any_nonzero() const {
+        uint32_t acc = 0u;
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc |= __builtin_bit_cast(uint32_t, x[i][c]) & 0x7fffffffu;
+        return __syncthreads_or(acc != 0u) != 0;
+    }
+};
+
 // Workgroup-uniform test of N floats (N a multiple of 4 * NTH) for a nonzero
 // element; every load is issued before the first is used.
 template <int N>
@@ -173,7 +202,7 @@ __global__ __launch_bounds__(NTH) void scan_seq_kernel(int H, int nseg, const fl
 //   so each pair's slots are touched by one workgroup only.
 // ---------------------------------------------------------------------------
 template <int DK, int DV>
-__global__ __launch_bounds__(NTH) void blel_init_kernel(int H, int nseg, const float *M,
+__global__ __launch_bounds__(NTH, 1) void blel_init_kernel(int H, int nseg, const float *M,
                                                         const float *D, float *Pm, float *Pd,
                                                         int *Fz) {
     const int slot = blockIdx.x, h = blockIdx.y;
@@ -181,10 +210,13 @@ __global__ __launch_bounds__(NTH) void blel_init_kernel(int H, int nseg, const f
     float *pm = Pm + ((int64_t)slot * H + h) * mm;
     float *pd = Pd + ((int64_t)slot * H + h) * dd;
     if (slot < nseg) {
-        const float *m = M + ((int64_t)slot * H + h) * mm;
-        const bool nz = block_nonzero<DK * DK>(m);
-        copy_n<DK * DK>(pm, m);
-        copy_n<DK * DV>(pd, D + ((int64_t)slot * H + h) * dd);
+        Tile<DK * DK> tm;
+        Tile<DK * DV> td;
+        tm.load(M + ((int64_t)slot * H + h) * mm);
+        td.load(D + ((int64_t)slot * H + h) * dd);
+        const bool nz = tm.any_nonzero();
+        tm.store(pm);
+        td.store(pd);
         if (threadIdx.x == 0) Fz[slot * H + h] = nz ? 1 : 0;
     } else {
         for (int e = threadIdx.x; e < DK * DK; e += NTH) pm[e] = (e / DK == e % DK) ? 1.f : 0.f;
@@ -194,7 +226,7 @@ __global__ __launch_bounds__(NTH) void blel_init_kernel(int H, int nseg, const f
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(NTH) void blel_level_kernel(int H, int step, int down, float *Pm,
+__global__ __launch_bounds__(NTH, 1) void blel_level_kernel(int H, int step, int down, float *Pm,
                                                          float *Pd, int *Fz) {
     const int h = blockIdx.y;
     const int64_t i = (int64_t)(blockIdx.x + 1) * 2 * step - 1, j = i - step;
@@ -221,16 +253,20 @@ __global__ __launch_bounds__(NTH) void blel_level_kernel(int H, int step, int do
     // down-sweep: (P[j], P[i]) = (P[i], P[j] o P[i]) with P[j] o P[i] = (Mj Mi, Mj Di + Dj)
     const bool nz = fj ? block_nonzero<DK * DK>(Mj) : false;
     if (!nz) {
-        // Mj == 0: P[j] <- P[i]; P[i] <- (0, Dj), element by element
-        for (int64_t e = threadIdx.x; e < mm / 4; e += NTH) {
-            ((float4 *)Mj)[e] = ((const float4 *)Mi)[e];
-            ((float4 *)Mi)[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+        // Mj == 0: P[j] <- P[i]; P[i] <- (0, Dj); each thread moves only its
+        // own elements, all loaded before any is stored
+        {
+            Tile<DK * DK> t;
+            t.load(Mi);
+            t.store(Mj);
+            t.zero();
+            t.store(Mi);
         }
-        for (int64_t e = threadIdx.x; e < dd / 4; e += NTH) {
-            const float4 a = ((const float4 *)Di)[e], b = ((const float4 *)Dj)[e];
-            ((float4 *)Dj)[e] = a;
-            ((float4 *)Di)[e] = b;
-        }
+        Tile<DK * DV> a, b;
+        a.load(Di);
+        b.load(Dj);
+        a.store(Dj);
+        b.store(Di);
         if (threadIdx.x == 0) { Fz[j * H + h] = fi; Fz[i * H + h] = 0; }
         return;
     }
@@ -278,16 +314,25 @@ __global__ __launch_bounds__(NTH) void blel_root_kernel(int H, int size, float *
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
     float *lm = Pm + ((int64_t)(size - 1) * H + h) * mm, *ld = Pd + ((int64_t)(size - 1) * H + h) * dd;
     float *tm = Pm + ((int64_t)size * H + h) * mm, *td = Pd + ((int64_t)size * H + h) * dd;
-    for (int64_t e = threadIdx.x; e < mm / 4; e += NTH) {
-        const float4 x = ((const float4 *)lm)[e];
-        ((float4 *)tm)[e] = x;
-        const int r = (int)((4 * e) / DK), c = (int)((4 * e) % DK);
-        ((float4 *)lm)[e] = make_float4(r == c ? 1.f : 0.f, r == c + 1 ? 1.f : 0.f,
-                                        r == c + 2 ? 1.f : 0.f, r == c + 3 ? 1.f : 0.f);
+    {
+        Tile<DK * DK> t;
+        t.load(lm);
+        t.store(tm);
+#pragma unroll
+        for (int k = 0; k < Tile<DK * DK>::PER; ++k) {
+            const int64_t e = threadIdx.x + (int64_t)k * NTH;
+            const int r = (int)((4 * e) / DK), c = (int)((4 * e) % DK);
+            t.x[k] = f32x4{r == c ? 1.f : 0.f, r == c + 1 ? 1.f : 0.f, r == c + 2 ? 1.f : 0.f,
+                           r == c + 3 ? 1.f : 0.f};
+        }
+        t.store(lm);
     }
-    for (int64_t e = threadIdx.x; e < dd / 4; e += NTH) {
-        ((float4 *)td)[e] = ((const float4 *)ld)[e];
-        ((float4 *)ld)[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+    {
+        Tile<DK * DV> t;
+        t.load(ld);
+        t.store(td);
+        t.zero();
+        t.store(ld);
     }
     if (threadIdx.x == 0) { Fz[size * H + h] = Fz[(size - 1) * H + h]; Fz[(size - 1) * H + h] = 1; }
 }
@@ -304,8 +349,14 @@ __global__ __launch_bounds__(NTH) void blel_apply_kernel(int H, int nseg, int si
     const float *Lm = Pm + ((int64_t)slot * H + h) * mm;
     const float *Ad = Pd + ((int64_t)slot * H + h) * dd;
     float *out = jj < nseg ? S_in + ((int64_t)jj * H + h) * dd : S_final + (int64_t)h * dd;
+    Tile<DK * DV> ta;
+    ta.load(Ad);   // issued with the zero test: the usual case is a copy of Ad
     const bool nz = (S0 && Fz[slot * H + h]) ? block_nonzero<DK * DK>(Lm) : false;
-    affine<DK, DV>(Lm, nz, S0 ? S0 + (int64_t)h * dd : nullptr, Ad, out);
+    if (!nz) {
+        ta.store(out);
+        return;
+    }
+    affine<DK, DV>(Lm, true, S0 + (int64_t)h * dd, Ad, out);
 }
 
 // Segment-path checkpoints: grid (rows, H).  Rung row r sits at
