@@ -18,6 +18,7 @@ a 64-sequence batch against its own HBM roofline.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -338,7 +339,12 @@ def main():
             if timed:
                 mark("pkg1")
             return o
-        main_kernel = "chunk_engine<prefill>"
+        # one long sequence on few heads runs segmented inside kda_prefill
+        # (several launches); otherwise the call is one engine launch
+        main_kernel = ("kda_prefill (segmented: packages, scan, fix-up)"
+                       if w.N == 1 and K.LIB.kda_prefill_workspace(
+                           ctypes.byref(K.make_config(H, dk, dv, t["q"].dtype)), T, 1) > 256
+                       else "chunk_engine<prefill>")
         rows = int(ckpt_offsets(w.lengths, w.ckpt_interval)[-1]) if w.ckpt_interval else 0
         extra_bytes = 4 * H * dk * dv * (2 * w.N + rows)             # S0, S_final, checkpoints
 

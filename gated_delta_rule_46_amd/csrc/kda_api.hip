@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -87,6 +89,111 @@ size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 size_t prefill_ws_bytes(int32_t N) { return round256((size_t)(N > 0 ? N : 1) * sizeof(int32_t)); }
 
+// Compute units of the current device (queried once per device).
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+        v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+// One long sequence on too few workgroups runs faster as segments: packages
+// of every segment in parallel, a scan over them, then the outputs fixed up
+// from each segment's incoming state (the segment path), all inside the
+// caller's workspace.
+constexpr int64_t kMinSplit = 512;   // shortest segment worth a workgroup of its own
+
+struct SplitPlan {
+    int nseg = 0;
+    int64_t L = 0, rows = 0;
+    size_t off_M = 0, off_D = 0, off_Sin = 0, off_Sfin = 0, off_subM = 0, off_subD = 0,
+           off_bounds = 0, bytes = 0;
+};
+
+bool plan_split(const kda_config *cfg, int64_t T, int32_t N, const kda_ckpt *ckpt, SplitPlan *p) {
+    if (N != 1 || T < 2 * kMinSplit) return false;
+    if (ckpt && ckpt->offsets) return false;   // a device-side first rung row is not known here
+    if (ckpt && (ckpt->interval <= 0 || ckpt->interval % kda::kChunk != 0)) return false;
+    const bool bf = cfg->io_dtype == KDA_DTYPE_BF16;
+    const int H = cfg->num_heads;
+    if (!kda::engine_supported(bf, cfg->dk, cfg->dv, 64)) return false;
+    const int nb = kda::engine_pick_nb(bf, cfg->dk, cfg->dv, H, kda::kModePrefill);
+    const int cus = device_cus();
+    if ((int64_t)H * (cfg->dv / nb) >= cus) return false;
+    int64_t nseg = (cus + H - 1) / H;
+    nseg = std::min<int64_t>(nseg, T / kMinSplit);
+    if (nseg < 2) return false;
+    const int64_t L = (T + nseg - 1) / nseg;
+    p->L = (L + kda::kChunk - 1) / kda::kChunk * kda::kChunk;
+    p->nseg = (int)((T + p->L - 1) / p->L);
+    if (p->nseg < 2) return false;
+    p->rows = ckpt ? T / ckpt->interval : 0;
+    const size_t mm = (size_t)H * cfg->dk * cfg->dk * sizeof(float);
+    const size_t dd = (size_t)H * cfg->dk * cfg->dv * sizeof(float);
+    size_t at = 0;
+    auto take = [&](size_t b) { const size_t o = at; at += round256(b); return o; };
+    p->off_M = take(mm * p->nseg);
+    p->off_D = take(dd * p->nseg);
+    p->off_Sin = take(dd * p->nseg);
+    p->off_Sfin = take(dd);
+    p->off_subM = take(mm * (size_t)p->rows);
+    p->off_subD = take(dd * (size_t)p->rows);
+    p->off_bounds = take(sizeof(int64_t) * (size_t)(p->nseg + 1));
+    p->bytes = at;
+    return true;
+}
+
+int prefill_split(const SplitPlan &p, const kda_config *cfg, const void *q, const void *k,
+                  const void *v, const float *g, const float *beta, int64_t T, const float *S0,
+                  float *S_final, void *o, const kda_ckpt *ckpt, void *ws, hipStream_t s) {
+    unsigned char *w = (unsigned char *)ws;
+    float *M = (float *)(w + p.off_M), *D = (float *)(w + p.off_D);
+    float *S_in = (float *)(w + p.off_Sin);
+    float *S_fin = S_final ? S_final : (float *)(w + p.off_Sfin);
+    float *sub_M = p.rows ? (float *)(w + p.off_subM) : nullptr;
+    float *sub_D = p.rows ? (float *)(w + p.off_subD) : nullptr;
+    int64_t *bounds = (int64_t *)(w + p.off_bounds);
+    const bool bf = cfg->io_dtype == KDA_DTYPE_BF16;
+    const int H = cfg->num_heads, dk = cfg->dk, dv = cfg->dv;
+    hipError_t e = kda::launch_even_bounds(bounds, p.nseg, p.L, T, s);
+    if (e != hipSuccess) return launched(e, "prefill split (bounds)");
+    const int nb = kda::engine_pick_nb(bf, dk, dv, (int64_t)p.nseg * H, kda::kModePackage);
+    kda::EngineArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
+    a.bounds = bounds; a.order = nullptr; a.n_units = p.nseg; a.H = H;
+    a.S_init = nullptr; a.S_out = D; a.M_out = M;
+    a.interval = p.rows ? ckpt->interval : 0;
+    a.ckpt_off = nullptr; a.ckpt_S = sub_D; a.ckpt_M = sub_M;
+    a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;
+    a.ncb = dv / nb;
+    if ((e = kda::launch_engine(kda::kModePackage, bf, dk, dv, nb, a, s)) != hipSuccess)
+        return launched(e, "prefill split (package)");
+    a.ncb = dk / nb;
+    if ((e = kda::launch_engine(kda::kModePackageM, bf, dk, dv, nb, a, s)) != hipSuccess)
+        return launched(e, "prefill split (package M)");
+    if ((e = kda::launch_scan_sequential(dk, dv, H, p.nseg, M, D, S0, S_in, S_fin, s)) != hipSuccess)
+        return launched(e, "prefill split (scan)");
+    kda::EngineArgs f{};
+    f.q = q; f.k = k; f.v = nullptr; f.g = g; f.beta = beta; f.o = o;
+    f.bounds = bounds; f.order = nullptr; f.n_units = p.nseg; f.H = H;
+    f.S_init = S_in; f.scale = cfg->scale; f.l2norm = cfg->qk_l2norm;
+    const int nbf = kda::engine_pick_nb(bf, dk, dv, (int64_t)p.nseg * H, kda::kModeFixup);
+    f.ncb = dv / nbf;
+    if ((e = kda::launch_engine(kda::kModeFixup, bf, dk, dv, nbf, f, s)) != hipSuccess)
+        return launched(e, "prefill split (fix-up)");
+    if (p.rows) {
+        e = kda::launch_ckpt_write(dk, dv, H, T, bounds, p.nseg, ckpt->interval, S_in, sub_M,
+                                   sub_D, ckpt->states, s);
+        return launched(e, "prefill split (checkpoints)");
+    }
+    return ok();
+}
+
 // Chunked prefill with initial / final states either dense (S0, S_final) or
 // in a slot pool; pos0 (nullable) shifts the checkpoint grid.
 int prefill_impl(const char *what, const kda_config *cfg, const void *q, const void *k,
@@ -129,6 +236,9 @@ int prefill_impl(const char *what, const kda_config *cfg, const void *q, const v
     KDA_TRY(check_tensor(ws, "ws", true, 16));
 
     hipStream_t s = (hipStream_t)stream;
+    SplitPlan sp;
+    if (!pool && !pos0 && plan_split(cfg, T, N, ckpt, &sp) && ws_bytes >= sp.bytes)
+        return prefill_split(sp, cfg, q, k, v, g, beta, T, S0, S_final, o, ckpt, ws, s);
     const bool bf = cfg->io_dtype == KDA_DTYPE_BF16;
     const int nb = kda::engine_pick_nb(bf, cfg->dk, cfg->dv, (int64_t)N * cfg->num_heads,
                                        kda::kModePrefill);
@@ -178,9 +288,12 @@ const char *kda_last_error(void) { return g_last_error.c_str(); }
 const char *kda_version(void) { return "0.1.0"; }
 
 size_t kda_prefill_workspace(const kda_config *cfg, int64_t T, int32_t N) {
-    (void)cfg;
-    (void)T;
-    return prefill_ws_bytes(N);
+    size_t need = prefill_ws_bytes(N);
+    SplitPlan sp;
+    // room for the segmented path of a call without checkpoints
+    if (cfg && check_config(cfg) == KDA_OK && plan_split(cfg, T, N, nullptr, &sp))
+        need = std::max(need, sp.bytes);
+    return need;
 }
 
 int kda_prefill(const kda_config *cfg, const void *q, const void *k, const void *v,

@@ -63,6 +63,9 @@ hipError_t launch_scan_blelloch(int dk, int dv, int H, int nseg, const float *M,
                                 float *S_final, void *ws, hipStream_t s);
 size_t blelloch_workspace(int dk, int dv, int H, int nseg);
 
+// bounds[j] = min(j*L, T) for j = 0..nseg (device int64).
+hipError_t launch_even_bounds(int64_t *bounds, int nseg, int64_t L, int64_t T, hipStream_t s);
+
 // Segment-path checkpoints: states[row] = sub_M[row] S_in[j] + sub_D[row].
 hipError_t launch_ckpt_write(int dk, int dv, int H, int64_t T, const int64_t *seg_start,
                              int nseg, int interval, const float *S_in, const float *sub_M,

@@ -398,6 +398,12 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int64_t *cu, int n, in
     }
 }
 
+// Segment starts j*L (clipped to T) of an evenly split sequence.
+__global__ void bounds_kernel(int64_t *b, int nseg, int64_t L, int64_t T) {
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j <= nseg) b[j] = (int64_t)j * L < T ? (int64_t)j * L : T;
+}
+
 int pow2_at_least(int n) {
     int size = 1;
     while (size < n) size *= 2;
@@ -472,6 +478,12 @@ hipError_t launch_scan_blelloch(int dk, int dv, int H, int nseg, const float *M,
     if (dk == 64 && dv == 64) return scan_blel_t<64, 64>(H, nseg, M, D, S0, S_in, S_final, ws, s);
     if (dk == 128 && dv == 128) return scan_blel_t<128, 128>(H, nseg, M, D, S0, S_in, S_final, ws, s);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_even_bounds(int64_t *bounds, int nseg, int64_t L, int64_t T, hipStream_t s) {
+    hipLaunchKernelGGL(bounds_kernel, dim3((unsigned)((nseg + 1 + 255) / 256)), dim3(256), 0, s,
+                       bounds, nseg, L, T);
+    return hipGetLastError();
 }
 
 hipError_t launch_ckpt_write(int dk, int dv, int H, int64_t T, const int64_t *seg_start, int nseg,

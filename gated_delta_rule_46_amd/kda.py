@@ -148,13 +148,20 @@ def _inputs(q, k, v, g, beta):
     return T, H, dk, dv, dev
 
 
+def _round256(b):
+    return (b + 255) // 256 * 256
+
+
 def kda_prefill(q, k, v, g, beta, cu_seqlens, S0=None, *, want_final=True, ckpt_interval=0,
-                ckpt_offsets=None, scale=1.0, qk_l2norm=True, out=None, stream=None):
+                ckpt_offsets=None, scale=1.0, qk_l2norm=True, out=None, workspace=None,
+                stream=None):
     """Chunked prefill.  Returns (o, S_final or None, checkpoint states or None).
 
     cu_seqlens: int64 [N+1] device tensor.  ckpt_offsets: int64 [N+1] device
     tensor of first rung rows (required with ckpt_interval for N > 1); the
-    total rung count is read from its last element on the host.
+    total rung count is read from its last element on the host.  workspace:
+    a uint8 device tensor to use instead of one of the queried size (a single
+    sequence takes the segmented path only when it is large enough).
     """
     T, H, dk, dv, dev = _inputs(q, k, v, g, beta)
     N = cu_seqlens.numel() - 1
@@ -178,8 +185,15 @@ def kda_prefill(q, k, v, g, beta, cu_seqlens, S0=None, *, want_final=True, ckpt_
         ck = torch.empty((max(rows, 0), H, dk, dv), dtype=torch.float32, device=dev)
         ckp = ctypes.pointer(kda_ckpt(int(ckpt_interval), _p(ckpt_offsets), _p(ck) if rows else
                                       ctypes.c_void_p(torch.empty(1, device=dev).data_ptr())))
-    wsb = LIB.kda_prefill_workspace(ctypes.byref(cfg), T, N)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        ws, wsb = workspace, workspace.numel()
+    else:
+        wsb = LIB.kda_prefill_workspace(ctypes.byref(cfg), T, N)
+        if ckpt_interval and N == 1 and ckpt_offsets is None and wsb > 256:
+            # room for the rung sub-packages of the segmented path
+            rows = T // ckpt_interval
+            wsb += _round256(rows * H * dk * dk * 4) + _round256(rows * H * dk * dv * 4)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     st = LIB.kda_prefill(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(cu_seqlens),
                          N, T, _p(S0), _p(Sf), _p(o), ckp, _p(ws), wsb, _stream(stream))
     _check(st, "kda_prefill")
@@ -368,6 +382,8 @@ def _io_dtype(dtype):
 
 def _conv_state(windows, read_idx, write_idx, N, C, W, dtype, dev):
     if windows is None:
+        if read_idx is not None or write_idx is not None:
+            raise ValueError("read_idx / write_idx need windows")
         return None
     n_slots = windows.shape[0]
     _need(windows, "windows", (n_slots, W - 1, C), dtype, dev)

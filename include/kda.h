@@ -148,7 +148,9 @@ typedef struct {
 /* Chunked prefill                                                           */
 /* ------------------------------------------------------------------------ */
 
-/* Workspace bytes kda_prefill needs for N packed sequences (never 0). */
+/* Workspace bytes kda_prefill needs for N packed sequences (never 0): the
+ * longest-first schedule, or for one long sequence the buffers of its
+ * segmented processing (see kda_prefill). */
 size_t kda_prefill_workspace(const kda_config *cfg, int64_t T, int32_t N);
 
 /*
@@ -162,6 +164,17 @@ size_t kda_prefill_workspace(const kda_config *cfg, int64_t T, int32_t N);
  *   ckpt: NULL or checkpoints as described at kda_ckpt;
  *   ws / ws_bytes: scratch of at least kda_prefill_workspace() bytes.
  * Work is scheduled longest sequence first.  N = 0 or T = 0 is a no-op.
+ *
+ * A single sequence (N = 1) whose heads would occupy fewer workgroups than
+ * the device has compute units is processed as segments of at least 512
+ * tokens on the chunk grid (the segment path below, run inside ws: packages,
+ * a sequential scan, the output fix-up and checkpoint rungs), when ws_bytes
+ * holds its buffers; otherwise in one pass.  kda_prefill_workspace returns
+ * that size for calls without checkpoints.  With checkpoints (and
+ * ckpt->offsets NULL) the segmented path also needs
+ * round256(T/interval * H * dk * dk * 4) + round256(T/interval * H * dk * dv * 4)
+ * bytes more for the rung sub-packages.  Both paths give the same result up
+ * to fp32 rounding.
  */
 int kda_prefill(const kda_config *cfg, const void *q, const void *k, const void *v,
                 const float *g, const float *beta, const int64_t *cu_seqlens, int32_t N,

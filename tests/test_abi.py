@@ -130,9 +130,16 @@ def test_prefill_argument_checks():
 
 def test_workspace_queries():
     c = cfg()
-    sizes = [K.LIB.kda_prefill_workspace(ctypes.byref(c), 1 << 16, n) for n in (0, 1, 64, 5000)]
+    sizes = [K.LIB.kda_prefill_workspace(ctypes.byref(c), 1 << 16, n) for n in (0, 64, 5000)]
     assert all(s > 0 and s % 256 == 0 for s in sizes)
     assert sizes == sorted(sizes) and sizes[-1] >= 5000 * 4
+    # one long sequence on 4 heads: room for the segmented path (M, D and the
+    # incoming state of every segment of at least 512 tokens, fp32)
+    one = K.LIB.kda_prefill_workspace(ctypes.byref(c), 1 << 16, 1)
+    assert one % 256 == 0 and one >= 3 * 2 * 4 * 128 * 128 * 4
+    # too short to split, or enough heads to fill the device: the schedule only
+    assert K.LIB.kda_prefill_workspace(ctypes.byref(c), 600, 1) == 256
+    assert K.LIB.kda_prefill_workspace(ctypes.byref(cfg(H=512)), 1 << 16, 1) == 256
     assert K.LIB.kda_segment_scan_workspace(ctypes.byref(c), 16, K.KDA_SCAN_SEQUENTIAL) == 0
     b16 = K.LIB.kda_segment_scan_workspace(ctypes.byref(c), 16, K.KDA_SCAN_BLELLOCH)
     b17 = K.LIB.kda_segment_scan_workspace(ctypes.byref(c), 17, K.KDA_SCAN_BLELLOCH)

@@ -111,6 +111,29 @@ def test_prefill_fp32_long_memory(K):
     assert_close("S_final", Sf, rS, STATE_TOL["f32"])
 
 
+@pytest.mark.parametrize("dtype,d,H,T,iv", [("bf16", 128, 4, 8192, 1024), ("f32", 64, 2, 3000, 0),
+                                             ("bf16", 64, 8, 4160, 256)])
+def test_prefill_single_sequence_split_and_single_pass(K, dtype, d, H, T, iv):
+    """One sequence on few heads: kda_prefill splits it into segments when
+    the workspace holds them (the queried size), and runs one pass with a
+    minimal workspace; both against the oracle, with rungs at the sequence's
+    own positions."""
+    import torch
+    w = make_workload("split", [T], H, d, d, dtype, 4631, s0_std=0.1)
+    t = to_torch(w)
+    ref = oracle_full(w, iv)
+    for name, ws in (("split", None), ("one pass", torch.empty(256, dtype=torch.uint8, device="cuda"))):
+        say(f"prefill {name}: T={T} H={H} d={d} {dtype} interval={iv}")
+        o, Sf, ck = K.kda_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"],
+                                  t["S0"], ckpt_interval=iv, workspace=ws)
+        sync()
+        assert_close(f"{name} o", to_numpy_f64(o), ref[0], OUT_TOL[dtype])
+        assert_close(f"{name} S_final", to_numpy_f64(Sf), ref[1], STATE_TOL[dtype])
+        if iv:
+            assert ck.shape[0] == T // iv
+            assert_close(f"{name} rungs", to_numpy_f64(ck), ref[2], STATE_TOL[dtype])
+
+
 def test_prefill_varlen_checkpoints(K):
     lens = [70, 1, 128, 200, 0, 64, 129, 256]
     say(f"prefill varlen fp32 d=64 lens={lens} ckpt=64")
