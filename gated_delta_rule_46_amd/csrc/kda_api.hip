@@ -171,11 +171,9 @@ int prefill_split(const SplitPlan &p, const kda_config *cfg, const void *q, cons
     a.ckpt_off = nullptr; a.ckpt_S = sub_D; a.ckpt_M = sub_M;
     a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;
     a.ncb = dv / nb;
-    if ((e = kda::launch_engine(kda::kModePackage, bf, dk, dv, nb, a, s)) != hipSuccess)
+    a.ncb_m = dk / nb;
+    if ((e = kda::launch_engine(kda::kModePackageVM, bf, dk, dv, nb, a, s)) != hipSuccess)
         return launched(e, "prefill split (package)");
-    a.ncb = dk / nb;
-    if ((e = kda::launch_engine(kda::kModePackageM, bf, dk, dv, nb, a, s)) != hipSuccess)
-        return launched(e, "prefill split (package M)");
     if ((e = kda::launch_scan_sequential(dk, dv, H, p.nseg, M, D, S0, S_in, S_fin, s)) != hipSuccess)
         return launched(e, "prefill split (scan)");
     kda::EngineArgs f{};
@@ -349,15 +347,12 @@ int kda_segment_package(const kda_config *cfg, const void *q, const void *k, con
     a.interval = subs ? ckpt->interval : 0;
     a.ckpt_off = nullptr; a.ckpt_S = subs ? sub_D : nullptr; a.ckpt_M = subs ? sub_M : nullptr;
     a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;
-    // Two launches, value blocks then M blocks (which stop as soon as M is
-    // exactly zero).  Mixing short and long workgroups in one grid leaves the
-    // long ones unevenly spread over the CUs.
+    // Value blocks, and with M the M blocks after them in the same grid (they
+    // stop as soon as M is exactly zero and fill the value blocks' tail).
     a.ncb = cfg->dv / nb;
-    hipError_t e = kda::launch_engine(kda::kModePackage, bf, cfg->dk, cfg->dv, nb, a, s);
-    if (e != hipSuccess || !M) return launched(e, "package");
-    a.ncb = cfg->dk / nb;
-    return launched(kda::launch_engine(kda::kModePackageM, bf, cfg->dk, cfg->dv, nb, a, s),
-                    "package (M blocks)");
+    a.ncb_m = cfg->dk / nb;
+    return launched(kda::launch_engine(M ? kda::kModePackageVM : kda::kModePackage, bf, cfg->dk,
+                                       cfg->dv, nb, a, s), "package");
 }
 
 size_t kda_segment_scan_workspace(const kda_config *cfg, int32_t nseg, int32_t algo) {

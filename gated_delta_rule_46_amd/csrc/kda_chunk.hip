@@ -908,6 +908,45 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_engine(EngineArgs a) {
     engine_body<DK, DV, NB, BF, MODE, MODE == kModePackageM>(a, smem, u, h, cb * NB, t0, t1);
 }
 
+// Value blocks and M blocks of the segment packages in one grid, the M blocks
+// last.  M blocks stop once M is exactly zero, a few chunks in; dispatched
+// after every value block they fill the CUs that the shorter value blocks
+// leave idle while the longest ones finish.
+template <int DK, int DV, int NB, bool BF>
+__global__ __launch_bounds__(kThreads, 1) void package_engine(EngineArgs a, int grid_v) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int H = a.H;
+    const bool mblk = (int)blockIdx.x >= grid_v;
+    const int ncb = mblk ? a.ncb_m : a.ncb;
+    const int bx = mblk ? (int)blockIdx.x - grid_v : (int)blockIdx.x;
+    const int cb = (bx >> 3) % ncb;
+    const int item = ((bx >> 3) / ncb) * 8 + (bx & 7);
+    if (item >= a.n_units * H) return;
+    const int pos = item / H;
+    const int h = item - pos * H;
+    const int u = a.order ? a.order[pos] : pos;
+    const int64_t t0 = a.bounds[u], t1 = a.bounds[u + 1];
+    if (mblk)
+        engine_body<DK, DV, NB, BF, kModePackageM, true>(a, smem, u, h, cb * NB, t0, t1);
+    else
+        engine_body<DK, DV, NB, BF, kModePackage, false>(a, smem, u, h, cb * NB, t0, t1);
+}
+
+template <int DK, int DV, int NB, bool BF>
+hipError_t launch_package_vm(const EngineArgs &a, hipStream_t stream) {
+    using L = Lds<DK, NB, BF>;
+    auto kern = package_engine<DK, DV, NB, BF>;
+    hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, L::size);
+    if (e != hipSuccess) return e;
+    const int64_t items8 = ((int64_t)a.n_units * a.H + 7) / 8 * 8;
+    const int64_t grid_v = items8 * a.ncb, grid = grid_v + items8 * a.ncb_m;
+    if (grid == 0) return hipSuccess;
+    if (grid > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), L::size, stream, a, (int)grid_v);
+    return hipGetLastError();
+}
+
 template <int DK, int DV, int NB, bool BF, int MODE>
 hipError_t launch_one(const EngineArgs &a, hipStream_t stream) {
     using L = Lds<DK, NB, BF>;
@@ -930,6 +969,7 @@ hipError_t launch_modes(int mode, const EngineArgs &a, hipStream_t s) {
         case kModePackage: return launch_one<DK, DV, NB, BF, kModePackage>(a, s);
         case kModeFixup: return launch_one<DK, DV, NB, BF, kModeFixup>(a, s);
         case kModePackageM: return launch_one<DK, DV, NB, BF, kModePackageM>(a, s);
+        case kModePackageVM: return launch_package_vm<DK, DV, NB, BF>(a, s);
     }
     return hipErrorInvalidValue;
 }

@@ -10,8 +10,11 @@ constexpr int kChunk = 64;
 
 // Prefill: sequences from S0.  Package: value blocks of every segment from a
 // zero state (o_local, D, sub_D).  PackageM: the segment's linear part M (and
-// sub_M) from the identity.  Fixup: outputs corrected from S_in.
-enum EngineMode : int { kModePrefill = 0, kModePackage = 1, kModeFixup = 2, kModePackageM = 3 };
+// sub_M) from the identity.  Fixup: outputs corrected from S_in.  PackageVM:
+// value blocks and M blocks in one launch, the M blocks dispatched last.
+enum EngineMode : int {
+    kModePrefill = 0, kModePackage = 1, kModeFixup = 2, kModePackageM = 3, kModePackageVM = 4
+};
 
 // Arguments of the fused chunk engine (one workgroup per (unit, head,
 // column block); a unit is a sequence for prefill and a segment otherwise).
@@ -24,6 +27,7 @@ struct EngineArgs {
     int32_t n_units;
     int32_t H;
     int32_t ncb;                 // column blocks of the launch (dv / NB, or dk / NB for M)
+    int32_t ncb_m;               // PackageVM: column blocks of the M part (dk / NB)
     const float *S_init;         // prefill: S0 (nullable); fixup: S_in
     float *S_out;                // prefill: S_final (nullable); package: D
     float *M_out;                // package: M

@@ -221,7 +221,8 @@ int kda_prefill_resume(const kda_config *cfg, const void *q, const void *k, cons
  *   seg_start[j+1]]: the map from S_in^j to the state at p, at rung row
  *   p/interval - 1 of sub_M [rows,H,dk,dk] and sub_D [rows,H,dk,dv]
  *   (sub_M may be NULL only when M is NULL).
- * Two kernel launches: the value blocks (o_local, D, sub_D), then the M blocks.
+ * One kernel launch: the value blocks (o_local, D, sub_D) and, with M, the M
+ * blocks after them in the same grid.
  * No workspace is needed (ws may be NULL).
  */
 int kda_segment_package(const kda_config *cfg, const void *q, const void *k, const void *v,
