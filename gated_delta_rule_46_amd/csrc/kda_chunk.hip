@@ -59,13 +59,23 @@ __host__ __device__ constexpr int aoff_idx(int b, int a) { return b * (b - 1) / 
 
 template <int DK, int NB, bool BF> struct Lds {
     using T = typename Ops<BF>::T;
-    static constexpr int PAD = Ops<BF>::PAD;
+    // Row padding.  Tiles that the consumers read as 8-byte fragments (two
+    // per operand) keep a row stride of 2 mod 4 dwords in bf16: gfx950 serves
+    // an 8-byte LDS access 16 lanes at a time over 32 four-byte banks, so the
+    // 16 rows of a fragment then fall on 16 distinct bank pairs (a stride of
+    // 0 mod 4 dwords puts rows m and m+8 on the same pair).  Those rows are
+    // only 8-byte aligned and are written with 8-byte stores.  Producer-only
+    // tiles, read and written 16 bytes per lane, use a stride of 8 mod 16
+    // dwords, which measured free of conflicts for 16-byte accesses.
+    static constexpr int PAD = BF ? 4 : Ops<BF>::PAD;
+    static constexpr int PADR = BF ? 16 : Ops<BF>::PAD;
     static constexpr int ES = (int)sizeof(T);
     static constexpr int LDQ = DK + PAD;        // [64][DK] row-major tiles
     static constexpr int LDK = 64 + PAD;        // [DK][64] transposed Kbar
     static constexpr int LDP = 64 + PAD;        // [64][64] P
     static constexpr int LDV = NB + PAD;        // [64][NB] beta*V
     static constexpr int LDT = 16 + PAD;        // 16x16 blocks
+    static constexpr int LDR = DK + PADR;       // producer-side [rows][DK] tiles
     static constexpr int LDAD = 20;             // fp32 16x16 blocks
     static constexpr int o_flag = 0;                                  // int[16]
     static constexpr int o_gam = 64;                                  // f32 [DK]
@@ -80,14 +90,17 @@ template <int DK, int NB, bool BF> struct Lds {
     static constexpr int o_td = o_aoff + 6 * 16 * LDT * ES;           // hand-off: T_bb [2][4]
     static constexpr int o_ad = o_td + 2 * 4 * 16 * LDT * ES;         // producer scratch
     static constexpr int o_ro = o_ad + 4 * 16 * LDAD * 4;             // rhs of blocks 0-2
-    static constexpr int o_lk = o_ro + 48 * LDQ * ES;                 // lhs (K) of blocks 2, 3
-    static constexpr int o_lq = o_lk + 32 * LDQ * ES;                 // lhs (Q) of blocks 2, 3
-    static constexpr int o_cf = o_lq + 32 * LDQ * ES;                 // f32 [3][DK] rescales
+    static constexpr int o_lk = o_ro + 48 * LDR * ES;                 // lhs (K) of blocks 2, 3
+    static constexpr int o_lq = o_lk + 32 * LDR * ES;                 // lhs (Q) of blocks 2, 3
+    static constexpr int o_cf = o_lq + 32 * LDR * ES;                 // f32 [3][DK] rescales
     static constexpr int size = o_cf + 3 * DK * 4;
     static_assert(o_qbar % 16 == 0 && o_rk % 16 == 0 && o_kbt % 16 == 0 && o_p % 16 == 0 &&
                   o_bv % 16 == 0 && o_aoff % 16 == 0 && o_td % 16 == 0 && o_ad % 16 == 0 &&
                   o_ro % 16 == 0 && o_lk % 16 == 0 && o_lq % 16 == 0 && o_cf % 16 == 0,
                   "LDS alignment");
+    static_assert((LDQ * ES) % 8 == 0 && (LDK * ES) % 8 == 0 && (LDP * ES) % 8 == 0 &&
+                  (LDV * ES) % 8 == 0 && (LDT * ES) % 8 == 0 && (LDR * ES) % 16 == 0,
+                  "row alignment of 8-byte and 16-byte LDS accesses");
     static_assert(size <= 160 * 1024, "LDS budget");
 };
 
@@ -354,7 +367,7 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
                 float t8[8];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) { t8[j] = rd[j] * f0[j]; t8[j + 4] = rd[j + 4] * f1[j]; }
-                O::st8(s_ro + prow * L::LDQ + c0, t8);
+                O::st8(s_ro + prow * L::LDR + c0, t8);
             }
             if (R::HAS_O) {
                 float qx[8], lq[8];
@@ -363,10 +376,10 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
                 for (int j = 0; j < 8; ++j) lq[j] = qx[j] * fq * e1[j];
                 lhsQ[kk] = O::cvt8(lq);
                 Pd = O::mma32(Pd, lhsQ[kk], rhsD[kk]);
-                if (B >= 2) O::stf(s_lq + (prow - 32) * L::LDQ + c0, lhsQ[kk]);
+                if (B >= 2) O::stf(s_lq + (prow - 32) * L::LDR + c0, lhsQ[kk]);
             }
             // the far off-diagonal blocks of rows 32..63 are formed by consumer waves
-            if (B >= 2) O::stf(s_lk + (prow - 32) * L::LDQ + c0, lhsK[kk]);
+            if (B >= 2) O::stf(s_lk + (prow - 32) * L::LDR + c0, lhsK[kk]);
             Ad = O::mma32(Ad, lhsK[kk], rhsD[kk]);
             // one 32-channel step at a time keeps the fp32 temporaries short-lived
             __builtin_amdgcn_sched_barrier(0);
@@ -400,7 +413,7 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
         wave_sync_lds();
         if (R::HAS_V) {
 #pragma unroll
-            for (int kk = 0; kk < VS; ++kk) O::stf(s_bv + prow * L::LDV + 32 * kk + 8 * gq, bvp[kk]);
+            for (int kk = 0; kk < VS; ++kk) O::stf_h(s_bv + prow * L::LDV + 32 * kk + 8 * gq, bvp[kk]);
         }
         if (R::HAS_O) {
 #pragma unroll
@@ -424,20 +437,20 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
                 }
             }
             if (B == 0) {   // block 0 is referenced to the chunk start already
-                O::stf(s_rk + prow * L::LDQ + c0, O::neg(lhsK[kk]));
-                if (R::HAS_O) O::stf(s_qbar + prow * L::LDQ + c0, lhsQ[kk]);
+                O::stf_h(s_rk + prow * L::LDQ + c0, O::neg(lhsK[kk]));
+                if (R::HAS_O) O::stf_h(s_qbar + prow * L::LDQ + c0, lhsQ[kk]);
             } else {
                 const f32x4 f0 = *(const f32x4 *)(fac + c0), f1 = *(const f32x4 *)(fac + c0 + 4);
                 float x[8], t8[8];
                 O::unpack8(lhsK[kk], x);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) { t8[j] = -(x[j] * f0[j]); t8[j + 4] = -(x[j + 4] * f1[j]); }
-                O::st8(s_rk + prow * L::LDQ + c0, t8);
+                O::st8_h(s_rk + prow * L::LDQ + c0, t8);
                 if (R::HAS_O) {
                     O::unpack8(lhsQ[kk], x);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) { t8[j] = x[j] * f0[j]; t8[j + 4] = x[j + 4] * f1[j]; }
-                    O::st8(s_qbar + prow * L::LDQ + c0, t8);
+                    O::st8_h(s_qbar + prow * L::LDQ + c0, t8);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -451,7 +464,7 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
                 const int c0 = 32 * kk + 8 * gq;
-                const F8 Bf = O::ld8(s_ro + (16 * a2 + m) * L::LDQ + c0);
+                const F8 Bf = O::ld8(s_ro + (16 * a2 + m) * L::LDR + c0);
                 Ao = O::mma32(Ao, lhsK[kk], Bf);
                 if (R::HAS_O) P_ = O::mma32(P_, lhsQ[kk], Bf);
             }
@@ -742,12 +755,12 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
         for (int kk = 0; kk < KS; ++kk) {
             const int c0 = 32 * kk + 8 * gq;
             float x[8];
-            O::unpack8(O::ld8(s_ro + (16 * a2 + m) * L::LDQ + c0), x);
+            O::unpack8(O::ld8(s_ro + (16 * a2 + m) * L::LDR + c0), x);
             const f32x4 f0 = *(const f32x4 *)(cf + c0), f1 = *(const f32x4 *)(cf + c0 + 4);
 #pragma unroll
             for (int j = 0; j < 4; ++j) { x[j] *= f0[j]; x[j + 4] *= f1[j]; }
             const F8 Bf = O::cvt8(x);
-            const int lrow = (16 * (B - 2) + m) * L::LDQ + c0;
+            const int lrow = (16 * (B - 2) + m) * L::LDR + c0;
             Ao = O::mma32(Ao, O::ld8(s_lk + lrow), Bf);
             if (R::HAS_O) P_ = O::mma32(P_, O::ld8(s_lq + lrow), Bf);
         }

@@ -74,6 +74,12 @@ template <> struct Ops<true> {
     __device__ static void st8(T *p, const float *v) { *(F8 *)p = cvt8(v); }
     __device__ static void stf(T *p, F8 f) { *(F8 *)p = f; }
     __device__ static void st4(T *p, f32x4 v) { *(F4 *)p = cvt4(v); }
+    // the same stores as two 8-byte halves, for rows that are only 8-byte aligned
+    __device__ static void stf_h(T *p, F8 f) {
+        *(F4 *)p = __builtin_shufflevector(f, f, 0, 1, 2, 3);
+        *(F4 *)(p + 4) = __builtin_shufflevector(f, f, 4, 5, 6, 7);
+    }
+    __device__ static void st8_h(T *p, const float *v) { stf_h(p, cvt8(v)); }
     // sign flip of every element (bit operation, exact)
     __device__ static F8 neg(F8 f) {
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -127,6 +133,8 @@ template <> struct Ops<false> {
         *(f32x4 *)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
     }
     __device__ static void stf(T *p, F8 f) { *(f32x4 *)p = f.lo; *(f32x4 *)(p + 4) = f.hi; }
+    __device__ static void stf_h(T *p, F8 f) { stf(p, f); }
+    __device__ static void st8_h(T *p, const float *v) { st8(p, v); }
     __device__ static void st4(T *p, f32x4 v) { *(f32x4 *)p = v; }
     __device__ static F8 neg(F8 f) { return F8{-f.lo, -f.hi}; }
     __device__ static F8 cat(F4 a, F4 b) { return F8{a, b}; }
