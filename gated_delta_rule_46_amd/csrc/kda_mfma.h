@@ -24,13 +24,22 @@ __device__ __forceinline__ float row_shr(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
         0, __builtin_bit_cast(int, x), 0x110 | N, 0xF, 0xF, true));
 }
+// Hides x's definition from the optimiser (no instruction is emitted): keeps
+// each scan step a single DPP add instead of a multiply folded into the first
+// step or a step split into a DPP move and an add.
+__device__ __forceinline__ float dpp_src(float x) {
+    asm("" : "+v"(x));
+    return x;
+}
 // Inclusive prefix sum across the 16 lanes of a DPP row.
 __device__ __forceinline__ float scan16(float x) {
+    x = dpp_src(x);
     x += row_shr<1>(x);
     x += row_shr<2>(x);
     x += row_shr<4>(x);
+    x = dpp_src(x);
     x += row_shr<8>(x);
-    return x;
+    return dpp_src(x);
 }
 
 // ---------------------------------------------------------------------------
