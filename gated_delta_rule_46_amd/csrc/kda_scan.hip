@@ -199,7 +199,9 @@ __global__ __launch_bounds__(NTH) void scan_seq_kernel(int H, int nseg, const fl
 // Blelloch scan over packages in the workspace:
 //   Pm [size+1][H][DK][DK], Pd [size+1][H][DK][DV], Fz [size+1][H] (1 = M may
 //   be nonzero); slot `size` keeps the total.  One workgroup per (pair, head),
-//   so each pair's slots are touched by one workgroup only.
+//   so each pair's slots are touched by one workgroup only.  Fz is
+//   authoritative: a slot whose flag is 0 holds a zero M whatever its Pm
+//   memory contains, so zero matrices are never written, copied or read.
 // ---------------------------------------------------------------------------
 template <int DK, int DV>
 __global__ __launch_bounds__(NTH, 1) void blel_init_kernel(int H, int nseg, const float *M,
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(NTH, 1) void blel_init_kernel(int H, int nseg, cons
         tm.load(M + ((int64_t)slot * H + h) * mm);
         td.load(D + ((int64_t)slot * H + h) * dd);
         const bool nz = tm.any_nonzero();
-        tm.store(pm);
+        if (nz) tm.store(pm);
         td.store(pd);
         if (threadIdx.x == 0) Fz[slot * H + h] = nz ? 1 : 0;
     } else {
@@ -253,44 +255,46 @@ __global__ __launch_bounds__(NTH, 1) void blel_level_kernel(int H, int step, int
     // down-sweep: (P[j], P[i]) = (P[i], P[j] o P[i]) with P[j] o P[i] = (Mj Mi, Mj Di + Dj)
     const bool nz = fj ? block_nonzero<DK * DK>(Mj) : false;
     if (!nz) {
-        // Mj == 0: P[j] <- P[i]; P[i] <- (0, Dj); each thread moves only its
-        // own elements, all loaded before any is stored
-        {
+        // Mj == 0: P[j] <- P[i]; P[i] <- (0, Dj) (flag only); each thread
+        // moves only its own elements, all loaded before any is stored
+        if (fi) {
             Tile<DK * DK> t;
             t.load(Mi);
             t.store(Mj);
-            t.zero();
-            t.store(Mi);
         }
         Tile<DK * DV> a, b;
         a.load(Di);
         b.load(Dj);
         a.store(Dj);
         b.store(Di);
+        __syncthreads();   // every wave has read the flags before they change
         if (threadIdx.x == 0) { Fz[j * H + h] = fi; Fz[i * H + h] = 0; }
         return;
     }
     // general case: both products into accumulators, then each lane moves its
-    // own elements: P[j] <- old P[i], P[i] <- (Mj Mi, Mj Di + old Dj)
+    // own elements: P[j] <- old P[i], P[i] <- (Mj Mi, Mj Di + old Dj); a zero
+    // Mi (flag) leaves Mj Mi = 0 and moves no M
     Acc<DK, DK> am;
     Acc<DK, DV> ad;
-    mm_acc<DK, DK>(Mj, Mi, am);
+    if (fi) mm_acc<DK, DK>(Mj, Mi, am);
     mm_acc<DK, DV>(Mj, Di, ad);
     __syncthreads();
     {
         const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
         const int n = lane & 15, g = lane >> 4;
         const int r0 = w * (DK / 4);
+        if (fi) {
 #pragma unroll
-        for (int rt = 0; rt < Acc<DK, DK>::RT; ++rt)
+            for (int rt = 0; rt < Acc<DK, DK>::RT; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < Acc<DK, DK>::CT; ++ct)
+                for (int ct = 0; ct < Acc<DK, DK>::CT; ++ct)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int64_t e = (int64_t)(r0 + 16 * rt + 4 * g + q) * DK + 16 * ct + n;
-                    Mj[e] = Mi[e];
-                    Mi[e] = am.v[rt][ct][q];
-                }
+                    for (int q = 0; q < 4; ++q) {
+                        const int64_t e = (int64_t)(r0 + 16 * rt + 4 * g + q) * DK + 16 * ct + n;
+                        Mj[e] = Mi[e];
+                        Mi[e] = am.v[rt][ct][q];
+                    }
+        }
 #pragma unroll
         for (int rt = 0; rt < Acc<DK, DV>::RT; ++rt)
 #pragma unroll
@@ -314,10 +318,13 @@ __global__ __launch_bounds__(NTH) void blel_root_kernel(int H, int size, float *
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
     float *lm = Pm + ((int64_t)(size - 1) * H + h) * mm, *ld = Pd + ((int64_t)(size - 1) * H + h) * dd;
     float *tm = Pm + ((int64_t)size * H + h) * mm, *td = Pd + ((int64_t)size * H + h) * dd;
+    const int f_last = Fz[(size - 1) * H + h];
     {
         Tile<DK * DK> t;
-        t.load(lm);
-        t.store(tm);
+        if (f_last) {
+            t.load(lm);
+            t.store(tm);
+        }
 #pragma unroll
         for (int k = 0; k < Tile<DK * DK>::PER; ++k) {
             const int64_t e = threadIdx.x + (int64_t)k * NTH;
@@ -334,7 +341,8 @@ __global__ __launch_bounds__(NTH) void blel_root_kernel(int H, int size, float *
         t.zero();
         t.store(ld);
     }
-    if (threadIdx.x == 0) { Fz[size * H + h] = Fz[(size - 1) * H + h]; Fz[(size - 1) * H + h] = 1; }
+    __syncthreads();   // every wave has read the flags before they change
+    if (threadIdx.x == 0) { Fz[size * H + h] = f_last; Fz[(size - 1) * H + h] = 1; }
 }
 
 // S_in[j] = P[j].M S0 + P[j].D (j < nseg);  S_final = P[size].M S0 + P[size].D.

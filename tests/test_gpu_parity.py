@@ -269,6 +269,31 @@ def test_segment_path_long_memory(K, algo, dtype, d):
     assert_close("ckpt", r["ckpt"], rck, tol_s)
 
 
+@pytest.mark.parametrize("algo", [0, 1])
+@pytest.mark.parametrize("nseg,zero", [(13, (1, 4, 5, 9, 12)), (16, (0, 2, 3, 7, 8, 11, 15)),
+                                       (16, tuple(range(1, 16))), (5, ())])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("with_s0", [True, False])
+def test_scan_mixed_zero_packages(K, algo, nseg, zero, d, with_s0):
+    """Scans over packages where some M are exactly zero and others are not:
+    the zero flags decide which products and moves the scan skips."""
+    import torch
+    from workloads import make_packages
+    say(f"scan algo={algo} nseg={nseg} zero M at {list(zero)} d={d} S0={with_s0}")
+    M, D, S0 = make_packages(nseg, 3, d, d, 60 + nseg + d + len(zero), zero=zero)
+    tM, tD = torch.from_numpy(M).cuda(), torch.from_numpy(D).cuda()
+    tS0 = torch.from_numpy(S0).cuda() if with_s0 else None
+    S_in, S_fin = K.kda_segment_scan(tM, tD, tS0, algo=algo)
+    sync()
+    ref_S0 = S0.astype(np.float64) if with_s0 else np.zeros((3, d, d))
+    S_in_ref, S_fin_ref = oracle.scan_sequential([m.astype(np.float64) for m in M],
+                                                 [x.astype(np.float64) for x in D], ref_S0)
+    assert_close("S_in", to_numpy_f64(S_in), S_in_ref, OUT_TOL["f32"])
+    assert_close("S_final", to_numpy_f64(S_fin), S_fin_ref, STATE_TOL["f32"])
+    # the inputs are left as they were
+    assert np.array_equal(tM.cpu().numpy(), M) and np.array_equal(tD.cpu().numpy(), D)
+
+
 def test_segment_path_config_gates_bf16(K):
     """The configs' gates: M underflows to exactly zero after a few chunks."""
     say("segment path bf16 d=128 config gates, 4 segments of 512")

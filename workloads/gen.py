@@ -32,7 +32,7 @@ __all__ = [
     "bf16_round_bits", "bf16_bits_to_f32", "to_f64", "leveled_segments",
     "varlen_lengths", "ckpt_offsets", "GATE_COST_Q", "SEGMENT_FLOOR",
     "DecodeBatch", "make_decode_batch", "decode_slots", "standard_decode_batch",
-    "ConvCase", "make_conv_case",
+    "ConvCase", "make_conv_case", "make_packages",
 ]
 
 T_Q, T_K, T_V, T_BETA, T_G, T_S0, T_POOL, T_CONV = 0, 1, 2, 3, 4, 5, 6, 7
@@ -417,3 +417,18 @@ def make_conv_case(name: str, lengths, C: int, W: int, dtype: str, seed: int,
     return ConvCase(name=name, dtype=dtype, x=x, cu_seqlens=cu, weight=weight, bias=bias,
                     windows=win, read_idx=np.asarray(read_idx, dtype=np.int32),
                     write_idx=np.asarray(write_idx, dtype=np.int32))
+
+
+def make_packages(nseg: int, H: int, dk: int, dv: int, seed: int, zero=(), m_std: float | None = None):
+    """Random fp32 segment packages for scan tests: M ~ N(0, m_std^2) (default
+    0.5/sqrt(dk), spectral norm about 1), D ~ N(0, 1), S0 ~ N(0, 0.1^2); the M
+    of every segment listed in `zero` is exactly zero.  Returns (M [nseg,H,dk,dk],
+    D [nseg,H,dk,dv], S0 [H,dk,dv]), all float32."""
+    rng = np.random.default_rng([seed, 8])
+    sd = 0.5 / np.sqrt(dk) if m_std is None else m_std
+    M = (rng.standard_normal((nseg, H, dk, dk)) * sd).astype(np.float32)
+    D = rng.standard_normal((nseg, H, dk, dv)).astype(np.float32)
+    S0 = (rng.standard_normal((H, dk, dv)) * 0.1).astype(np.float32)
+    for j in zero:
+        M[j] = 0.0
+    return M, D, S0
