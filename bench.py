@@ -71,6 +71,23 @@ def recorded_traffic(workload: str, kernel_mode: str, entry: str | None = None):
     return rec["traffic_bytes"] if h.hexdigest() == rec["source_sha256"] else None
 
 
+def recorded_mfma(workload: str, kernel_mode: str, launch_ms: float):
+    """Matrix-core figures of the dominant kernel from the same record's
+    rocprofv3 --pmc run (SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16):
+    the busy fraction of the MFMA pipes, and the hardware MFMA flops per launch
+    over this run's launch time against the dense bf16 peak.  None when the
+    record is for another workload or the kernel's sources changed since."""
+    if recorded_traffic(workload, kernel_mode) is None:
+        return None
+    rec = json.load(open(os.path.join(ROOT, "profiles", "hbm_traffic.json"))).get("mfma")
+    if not rec:
+        return None
+    tf = rec["mfma_flops_per_launch"] / (launch_ms * 1e-3) / 1e12
+    return {"busy_frac": rec["mfma_busy_frac"], "flops_per_launch": rec["mfma_flops_per_launch"],
+            "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "source": "profiles/hbm_traffic.json"}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -406,6 +423,9 @@ def main():
                      "launch_ms": round(kernel_ms, 4), "launches_timed": args.roofline_launches},
         "breakdown_ms": breakdown,
     }
+    mf = recorded_mfma(w.name, "package" if segmented else "prefill", kernel_ms)
+    if mf is not None:
+        result["roofline"]["mfma_rocprof"] = mf
     if segmented and not args.no_resume:
         result["resume"] = resume_measure(K, w, t, args.roofline_launches)
     if not args.no_conv:
