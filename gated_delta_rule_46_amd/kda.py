@@ -110,6 +110,21 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _ckpt_rows(ckpt_offsets, ckpt_out):
+    """Rung rows: from a caller-supplied output tensor (no host sync), else
+    read from the last offset on the host (a device-to-host copy)."""
+    if ckpt_out is not None:
+        return int(ckpt_out.shape[0])
+    return int(ckpt_offsets[-1].item())
+
+
+def _ckpt_tensor(ckpt_out, rows, H, dk, dv, dev):
+    if ckpt_out is not None:
+        _need(ckpt_out, "ckpt_out", (rows, H, dk, dv), torch.float32, dev)
+        return ckpt_out
+    return torch.empty((max(rows, 0), H, dk, dv), dtype=torch.float32, device=dev)
+
+
 def make_config(H: int, dk: int, dv: int, dtype: torch.dtype, scale: float = 1.0,
                 qk_l2norm: bool = True) -> kda_config:
     if dtype == torch.bfloat16:
@@ -153,13 +168,16 @@ def _round256(b):
 
 
 def kda_prefill(q, k, v, g, beta, cu_seqlens, S0=None, *, want_final=True, ckpt_interval=0,
-                ckpt_offsets=None, scale=1.0, qk_l2norm=True, out=None, workspace=None,
-                stream=None):
+                ckpt_offsets=None, ckpt_out=None, scale=1.0, qk_l2norm=True, out=None,
+                workspace=None, stream=None):
     """Chunked prefill.  Returns (o, S_final or None, checkpoint states or None).
 
     cu_seqlens: int64 [N+1] device tensor.  ckpt_offsets: int64 [N+1] device
     tensor of first rung rows (required with ckpt_interval for N > 1); the
-    total rung count is read from its last element on the host.  workspace:
+    total rung count is read from its last element on the host, unless
+    ckpt_out (fp32 [rows,H,dk,dv], rows = ckpt_offsets[-1], the caller's
+    guarantee, as the kernels write the rows the offsets name) is given: then
+    the call makes no host synchronisation.  workspace:
     a uint8 device tensor to use instead of one of the queried size (a single
     sequence takes the segmented path only when it is large enough).
     """
@@ -181,8 +199,8 @@ def kda_prefill(q, k, v, g, beta, cu_seqlens, S0=None, *, want_final=True, ckpt_
             rows = T // ckpt_interval
         else:
             _need(ckpt_offsets, "ckpt_offsets", (N + 1,), torch.int64, dev)
-            rows = int(ckpt_offsets[-1].item())
-        ck = torch.empty((max(rows, 0), H, dk, dv), dtype=torch.float32, device=dev)
+            rows = _ckpt_rows(ckpt_offsets, ckpt_out)
+        ck = _ckpt_tensor(ckpt_out, rows, H, dk, dv, dev)
         ckp = ctypes.pointer(kda_ckpt(int(ckpt_interval), _p(ckpt_offsets), _p(ck) if rows else
                                       ctypes.c_void_p(torch.empty(1, device=dev).data_ptr())))
     if workspace is not None:
@@ -201,13 +219,15 @@ def kda_prefill(q, k, v, g, beta, cu_seqlens, S0=None, *, want_final=True, ckpt_
 
 
 def kda_prefill_resume(q, k, v, g, beta, cu_seqlens, pool, read_idx, write_idx, *, pos0=None,
-                       ckpt_interval=0, ckpt_offsets=None, scale=1.0, qk_l2norm=True, out=None,
-                       stream=None):
+                       ckpt_interval=0, ckpt_offsets=None, ckpt_out=None, scale=1.0,
+                       qk_l2norm=True, out=None, stream=None):
     """Chunked prefill continuing each sequence from pool[read_idx[n]]; the
     final state goes to pool[write_idx[n]] (pool updated in place).  pos0:
     int64 [N] absolute start positions (multiples of 64) that place the
     checkpoint rungs; ckpt_offsets: int64 [N+1] first rung rows (required
-    with ckpt_interval for N > 1).  Returns (o, checkpoint states or None)."""
+    with ckpt_interval for N > 1); ckpt_out: optional preallocated rung
+    states, as in kda_prefill (no host synchronisation then).  Returns (o,
+    checkpoint states or None)."""
     T, H, dk, dv, dev = _inputs(q, k, v, g, beta)
     N = cu_seqlens.numel() - 1
     _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int64, dev)
@@ -226,8 +246,8 @@ def kda_prefill_resume(q, k, v, g, beta, cu_seqlens, pool, read_idx, write_idx, 
         if ckpt_offsets is None:
             raise ValueError("ckpt_offsets is required with ckpt_interval")
         _need(ckpt_offsets, "ckpt_offsets", (N + 1,), torch.int64, dev)
-        rows = int(ckpt_offsets[-1].item())
-        ck = torch.empty((max(rows, 0), H, dk, dv), dtype=torch.float32, device=dev)
+        rows = _ckpt_rows(ckpt_offsets, ckpt_out)
+        ck = _ckpt_tensor(ckpt_out, rows, H, dk, dv, dev)
         ckp = ctypes.pointer(kda_ckpt(int(ckpt_interval), _p(ckpt_offsets), _p(ck) if rows else
                                       ctypes.c_void_p(torch.empty(1, device=dev).data_ptr())))
     pl = kda_state_pool(ctypes.c_void_p(pool.data_ptr()), n_slots,

@@ -146,6 +146,39 @@ def test_prefill_varlen_checkpoints(K):
     assert_close("ckpt", ck, rck, STATE_TOL["f32"])
 
 
+def test_prefill_ckpt_out_preallocated(K):
+    """Rung states in a caller-supplied tensor (no host synchronisation in
+    the binding) are the same bits as in the binding's own allocation, for
+    prefill and for resume from a pool."""
+    import torch
+    lens = [300, 64, 513, 1]
+    say(f"prefill / resume with preallocated rung states, bf16 d=128 lens={lens} ckpt=128")
+    w = make_workload("t", lens, 2, 128, 128, "bf16", 9, s0_std=0.2)
+    t = to_torch(w)
+    off_np = ckpt_offsets(w.lengths, 128)
+    off = torch.from_numpy(off_np).cuda()
+    o1, S1, c1 = K.kda_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"], t["S0"],
+                               ckpt_interval=128, ckpt_offsets=off)
+    buf = torch.full((int(off_np[-1]), 2, 128, 128), float("nan"), device="cuda")
+    o2, S2, c2 = K.kda_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"], t["S0"],
+                               ckpt_interval=128, ckpt_offsets=off, ckpt_out=buf)
+    sync()
+    assert c2.data_ptr() == buf.data_ptr()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2) and torch.equal(c1, c2)
+    pool = t["S0"].clone()
+    idx = torch.arange(len(lens), dtype=torch.int32, device="cuda")
+    pos0 = torch.zeros(len(lens), dtype=torch.int64, device="cuda")
+    r1, d1 = K.kda_prefill_resume(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"],
+                                  pool.clone(), idx, idx, pos0=pos0, ckpt_interval=128,
+                                  ckpt_offsets=off)
+    buf2 = torch.full_like(buf, float("nan"))
+    r2, d2 = K.kda_prefill_resume(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"],
+                                  pool.clone(), idx, idx, pos0=pos0, ckpt_interval=128,
+                                  ckpt_offsets=off, ckpt_out=buf2)
+    sync()
+    assert torch.equal(r1, r2) and torch.equal(d1, d2) and torch.equal(d2, c1)
+
+
 def test_prefill_varlen_bf16(K):
     lens = [513, 64, 1000, 31, 2048]
     say(f"prefill varlen bf16 d=128 lens={lens} ckpt=512")
