@@ -299,8 +299,8 @@ def main():
         copy_probe(args.copy_probe)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1 "
+                                   "(the library has no cross-GPU package exchange)"}))
         sys.exit(2)
     import torch
     from workloads import standard_workload, ckpt_offsets
