@@ -189,8 +189,16 @@ __global__ __launch_bounds__(NTH) void scan_seq_kernel(int H, int nseg, const fl
         const float *Sj = S_in + ((int64_t)j * H + h) * ss;
         float *dst = (j + 1 < nseg) ? S_in + ((int64_t)(j + 1) * H + h) * ss : S_final + (int64_t)h * ss;
         const float *Mj = M + ((int64_t)j * H + h) * mm;
-        const bool nz = block_nonzero<DK * DK>(Mj);
-        affine<DK, DV>(Mj, nz, Sj, D + ((int64_t)j * H + h) * ss, dst);
+        const float *Dj = D + ((int64_t)j * H + h) * ss;
+        // D_j is loaded with the zero test of M_j (one memory latency per
+        // step in the usual case, where S_in[j+1] = D_j)
+        Tile<DK * DV> td;
+        td.load(Dj);
+        if (!block_nonzero<DK * DK>(Mj)) {
+            td.store(dst);
+        } else {
+            affine<DK, DV>(Mj, true, Sj, Dj, dst);
+        }
         __syncthreads();
     }
 }
