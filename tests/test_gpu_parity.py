@@ -179,6 +179,42 @@ def test_prefill_ckpt_out_preallocated(K):
     assert torch.equal(r1, r2) and torch.equal(d1, d2) and torch.equal(d2, c1)
 
 
+@pytest.mark.parametrize("dtype,d,l2,scale", [("bf16", 128, 0, 1.0), ("bf16", 128, 1, 0.08838834764831845),
+                                          ("f32", 64, 0, 0.5), ("bf16", 64, 1, 0.125)])
+def test_prefill_scale_and_no_l2norm(K, dtype, d, l2, scale):
+    """Chunked prefill with a query scale and with the in-kernel L2 norm off
+    (q, k scaled by 2^-4 so that the recurrence contracts)."""
+    from workloads import scale_qk_pow2
+    lens = [200, 77, 129]
+    say(f"prefill {dtype} d={d} l2norm={l2} scale={scale:g} lens={lens}")
+    w = make_workload("t", lens, 2, d, d, dtype, 31 + d + l2, s0_std=0.2, scale=scale, qk_l2norm=l2)
+    if not l2:
+        scale_qk_pow2(w, -4)
+    o, Sf, ck = run_prefill(K, w, interval=64)
+    ro, rS, rck = oracle_full(w, interval=64)
+    assert_close("o", o, ro, OUT_TOL[dtype])
+    assert_close("S_final", Sf, rS, STATE_TOL[dtype])
+    assert_close("ckpt", ck, rck, STATE_TOL[dtype])
+
+
+@pytest.mark.parametrize("algo", [0, 1])
+def test_segment_path_scale_and_no_l2norm(K, algo):
+    """The segment path (packages, scan, fix-up, rungs) with a query scale and
+    the L2 norm off, long-memory gates so every stage carries a nonzero M."""
+    from workloads import scale_qk_pow2
+    say(f"segment path bf16 d=128 l2norm=0 scale=0.5 algo={algo} long-memory")
+    seg = [0, 192, 640, 704, 1090]
+    w = make_workload("t", [1090], 2, 128, 128, "bf16", 40 + algo, s0_std=0.5, gate_shift=-9.0,
+                      beta_shift=-6.0, seg_start=seg, scale=0.5, qk_l2norm=0)
+    scale_qk_pow2(w, -4)
+    r = _segment_case(K, w, algo, interval=128)
+    assert np.count_nonzero(r["M"]) > 0
+    ro, rS, rck = oracle_full(w, interval=128)
+    assert_close("o", r["o"], ro, OUT_TOL["bf16"])
+    assert_close("S_final", r["S_final"], rS[0], STATE_TOL["bf16"])
+    assert_close("ckpt", r["ckpt"], rck, STATE_TOL["bf16"])
+
+
 def test_prefill_varlen_bf16(K):
     lens = [513, 64, 1000, 31, 2048]
     say(f"prefill varlen bf16 d=128 lens={lens} ckpt=512")
@@ -474,6 +510,18 @@ def test_decode_parity(K, dtype, dk, dv, logits):
     from workloads import make_decode_batch
     b = make_decode_batch("decode-small", 20, 3, dk, dv, dtype, 4601, gate_logits=logits)
     _decode_case(K, b, f"{dtype} {dk}x{dv}")
+
+
+@pytest.mark.parametrize("dtype,d,l2,scale", [("bf16", 128, 0, 1.0), ("f32", 64, 1, 0.125)])
+def test_decode_scale_and_no_l2norm(K, dtype, d, l2, scale):
+    """Decode with a query scale and with the in-kernel L2 norm off (q, k
+    scaled by 2^-4 so that the update contracts)."""
+    from workloads import make_decode_batch, scale_qk_pow2
+    b = make_decode_batch("decode-opts", 24, 3, d, d, dtype, 4602, gate_logits=True)
+    b.scale, b.qk_l2norm = scale, l2
+    if not l2:
+        scale_qk_pow2(b, -4)
+    _decode_case(K, b, f"{dtype} d={d} l2norm={l2} scale={scale}")
 
 
 def test_decode_standard_batch(K):

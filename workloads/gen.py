@@ -32,7 +32,7 @@ __all__ = [
     "bf16_round_bits", "bf16_bits_to_f32", "to_f64", "leveled_segments",
     "varlen_lengths", "ckpt_offsets", "GATE_COST_Q", "SEGMENT_FLOOR",
     "DecodeBatch", "make_decode_batch", "decode_slots", "standard_decode_batch",
-    "ConvCase", "make_conv_case", "make_packages",
+    "ConvCase", "make_conv_case", "make_packages", "scale_qk_pow2",
 ]
 
 T_Q, T_K, T_V, T_BETA, T_G, T_S0, T_POOL, T_CONV = 0, 1, 2, 3, 4, 5, 6, 7
@@ -432,3 +432,16 @@ def make_packages(nseg: int, H: int, dk: int, dv: int, seed: int, zero=(), m_std
     for j in zero:
         M[j] = 0.0
     return M, D, S0
+
+
+def scale_qk_pow2(w, e: int):
+    """Multiplies the stored q and k of a workload or decode batch by 2**e in
+    place (exact in fp32 and bf16 for these magnitudes): inputs for runs
+    without the in-kernel L2 norm, whose keys must stay short enough for the
+    delta rule to contract (|k|^2 = dk * 4**e on average)."""
+    for name in ("q", "k"):
+        a = getattr(w, name)
+        if w.dtype == "bf16":
+            a[...] = bf16_round_bits(bf16_bits_to_f32(a) * np.float32(2.0 ** e))
+        else:
+            a *= np.float32(2.0 ** e)
