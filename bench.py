@@ -101,6 +101,10 @@ def parse():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-resume", action="store_true", help="skip the resume measurement")
     ap.add_argument("--no-conv", action="store_true", help="skip the short-conv measurement")
+    ap.add_argument("--no-long-memory", action="store_true",
+                    help="skip the long-memory segment-path measurement")
+    ap.add_argument("--no-chunked", action="store_true",
+                    help="skip the 8,192-token single-sequence measurement (both paths)")
     ap.add_argument("--decode-launches", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -244,6 +248,130 @@ def conv_measure(K, w, t, launches: int) -> dict:
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
+def _time_calls(call, launches: int, warm: int = 3) -> float:
+    """Mean milliseconds per call, HIP events on the current stream around each."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warm):
+        call()
+    torch.cuda.synchronize()
+    pairs = []
+    for _ in range(launches):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+
+
+def long_memory_measure(K, w, t, launches: int) -> dict:
+    """The segment step on the same q, k, v and segmentation with long-memory
+    gates: log alpha = -softplus(N(0,1) - 9) (about -1.2e-4 per token) and
+    beta = sigmoid(N(0,1) - 6), drawn on the device from a seeded generator.
+    Every M stays far from zero, so the M blocks run their whole segment,
+    the scan forms every product, the fix-up runs every segment to its end
+    and the checkpoint writer multiplies every rung.  Algorithmic bytes: the
+    package pass (1540 B per token-head at d = 128 bf16) plus the M blocks'
+    reads of k, g, beta, plus the fix-up's reads of q, k, g, beta and its
+    read and write of o; states and packages as in the step."""
+    import torch
+    import torch.nn.functional as F
+    gen = torch.Generator(device="cuda").manual_seed(46007)
+    T, H, dk, dv = w.T, w.H, w.dk, w.dv
+    g = -F.softplus(torch.randn((T, H, dk), generator=gen, device="cuda") - 9.0)
+    beta = torch.sigmoid(torch.randn((T, H), generator=gen, device="cuda") - 6.0)
+    S0 = None if t["S0"] is None else t["S0"][0].contiguous()
+    interval = w.ckpt_interval
+    ev = {}
+    stream = torch.cuda.current_stream()
+
+    def mark(name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        ev.setdefault(name, []).append(e)
+
+    def step(timed):
+        if timed:
+            mark("a")
+        o, M, D, sM, sD = K.kda_segment_package(t["q"], t["k"], t["v"], g, beta, t["seg_start"],
+                                                ckpt_interval=interval)
+        if timed:
+            mark("b")
+        S_in, _ = K.kda_segment_scan(M, D, S0, algo=w.scan_algo)
+        if timed:
+            mark("c")
+        K.kda_output_fixup(t["q"], t["k"], g, beta, t["seg_start"], S_in, o)
+        if timed:
+            mark("d")
+        if interval:
+            K.kda_checkpoint_write(t["seg_start"], S_in, sM, sD, T=T, interval=interval)
+        if timed:
+            mark("e")
+        return M
+
+    M = step(False)
+    torch.cuda.synchronize()
+    m_norm_min = float(torch.linalg.matrix_norm(M).min())
+    for _ in range(3):
+        step(False)
+    torch.cuda.synchronize()
+    for _ in range(launches):
+        step(True)
+    torch.cuda.synchronize()
+
+    def avg(a, b):
+        return float(np.mean([x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]))
+    ms = avg("a", "e")
+    nseg = len(w.seg_start) - 1
+    rows = T // interval if interval else 0
+    io = 2 if w.dtype == "bf16" else 4
+    per_tok = (bytes_per_token_head(dk, dv, io) + (io * dk + 4 * dk + 4)
+               + (2 * io * dk + 4 * dk + 4 + 2 * io * dv))
+    alg = T * H * per_tok + 4 * H * (dk * dv + dk * dk) * (nseg + rows)
+    gbs = alg / (ms * 1e-3) / 1e9
+    return {"workload": f"{w.name} with long-memory gates (log alpha ~ -1.2e-4 per token)",
+            "min_frobenius_norm_M": round(m_norm_min, 4),
+            "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+            "steps_timed": launches,
+            "breakdown_ms": {"package": round(avg("a", "b"), 4), "scan": round(avg("b", "c"), 4),
+                             "fixup": round(avg("c", "d"), 4), "ckpt": round(avg("d", "e"), 4)},
+            "alg_bytes_per_step": int(alg),
+            "hbm": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
+def single_sequence_measure(K, launches: int) -> dict:
+    """kda_prefill on the 8,192-token single sequence (H = 32, d = 128,
+    bf16, S0 ~ N(0, 0.1^2)) by both of its paths: the chunked engine in one
+    pass (a 256-byte workspace: one workgroup per head and value-column
+    block) and the queried workspace, with which kda_prefill runs the
+    sequence as segments (packages, sequential scan, fix-up).  HIP events
+    around each call; algorithmic bytes as for prefill."""
+    import torch
+    from workloads import standard_workload
+    from workloads.device import to_torch
+    w = standard_workload(1)
+    t = to_torch(w)
+    o = torch.empty_like(t["v"])
+    Sf = torch.empty((1, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    tiny = torch.empty(256, dtype=torch.uint8, device="cuda")
+    out = {"workload": w.name}
+    io = 2 if w.dtype == "bf16" else 4
+    alg = w.T * w.H * bytes_per_token_head(w.dk, w.dv, io) + 4 * w.H * w.dk * w.dv * 2
+    for name, ws in (("one_pass", tiny), ("segmented", None)):
+        def call():
+            K.kda_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"], t["S0"],
+                          out=o, workspace=ws)
+        ms = _time_calls(call, max(launches, 10))
+        gbs = alg / (ms * 1e-3) / 1e9
+        out[name] = {"tokens_per_s": round(w.T / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def decode_measure(K, launches: int) -> dict:
     """kda_decode on 64 sequences x 32 heads (d=128, bf16, gate logits,
     128-slot pool with in-place rows, forks, fresh and discarded states).
@@ -344,13 +472,19 @@ def main():
             if timed:
                 mark("ck1")
             return o
-        main_kernel = "chunk_engine<package, value blocks>"
+        main_kernel = "package_engine (value blocks, then M blocks, one launch)"
         rows = T // interval if interval else 0
         nseg = len(w.seg_start) - 1
-        extra_bytes = 4 * H * dk * dv * (nseg + rows)                # D and rung sub_D
+        # D and rung sub_D, M and rung sub_M written by the launch
+        extra_bytes = 4 * H * dk * dv * (nseg + rows) + 4 * H * dk * dk * (nseg + rows)
 
         def dominant():
-            # the value-block launch alone: kda_segment_package without M
+            # the launch the step runs first: kda_segment_package with M
+            K.kda_segment_package(t["q"], t["k"], t["v"], t["g"], t["beta"], t["seg_start"],
+                                  ckpt_interval=interval)
+
+        def value_blocks():
+            # the value blocks alone (kda_segment_package without M)
             K.kda_segment_package(t["q"], t["k"], t["v"], t["g"], t["beta"], t["seg_start"],
                                   ckpt_interval=interval, want_M=False)
     else:
@@ -381,6 +515,7 @@ def main():
 
         def dominant():
             step(False)
+        value_blocks = None
 
     for _ in range(args.warmup):
         step(False)
@@ -400,6 +535,11 @@ def main():
         mark("dom0")
         dominant()
         mark("dom1")
+    if value_blocks is not None:
+        for _ in range(args.roofline_launches):
+            mark("vb0")
+            value_blocks()
+            mark("vb1")
     torch.cuda.synchronize()
     kernel_ms = avg_ms("dom0", "dom1")
     breakdown = {"package" if segmented else "prefill": round(avg_ms("pkg0", "pkg1"), 4)}
@@ -432,20 +572,34 @@ def main():
         "mfma_tflops_alg": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
         "roofline": {"bound": "hbm", "kernel": main_kernel, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(w.name, "package" if segmented else "prefill"),
+                     "traffic": recorded_traffic(w.name, "package_engine" if segmented else "prefill"),
                      "alg_bytes_per_launch": int(alg_bytes),
                      "launch_ms": round(kernel_ms, 4), "launches_timed": args.roofline_launches},
         "breakdown_ms": breakdown,
     }
-    mf = recorded_mfma(w.name, "package" if segmented else "prefill", kernel_ms)
+    if value_blocks is not None:
+        vb_ms = avg_ms("vb0", "vb1")
+        vb_bytes = T * H * bytes_per_token_head(dk, dv, io_bytes) + 4 * H * dk * dv * (nseg + rows)
+        vb_gbs = vb_bytes / (vb_ms * 1e-3) / 1e9
+        result["roofline_value_blocks"] = {
+            "kernel": "chunk_engine<package> value blocks alone (kda_segment_package without M)",
+            "achieved": round(vb_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(vb_gbs / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": int(vb_bytes),
+            "launch_ms": round(vb_ms, 4), "launches_timed": args.roofline_launches}
+    mf = recorded_mfma(w.name, "package_engine" if segmented else "prefill", kernel_ms)
     if mf is not None:
         result["roofline"]["mfma_rocprof"] = mf
+    if segmented and not args.no_long_memory:
+        result["long_memory"] = long_memory_measure(K, w, t, args.roofline_launches)
     if segmented and not args.no_resume:
         result["resume"] = resume_measure(K, w, t, args.roofline_launches)
     if not args.no_conv:
         result["short_conv"] = conv_measure(K, w, t, args.roofline_launches)
+    t = None   # the workload's device tensors are not needed past this point
+    torch.cuda.empty_cache()
+    if args.config == 3 and not args.no_chunked:
+        result["single_sequence_8192"] = single_sequence_measure(K, args.roofline_launches)
     if not args.no_decode:
-        del t
         result["decode"] = decode_measure(K, args.decode_launches)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -971,6 +971,7 @@ hipError_t launch_one(const EngineArgs &a, hipStream_t stream) {
     const int64_t items = (int64_t)a.n_units * a.H;
     const int64_t grid = ((items + 7) / 8) * 8 * ncb;
     if (grid == 0) return hipSuccess;
+    if (grid > INT32_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), L::size, stream, a);
     return hipGetLastError();
 }

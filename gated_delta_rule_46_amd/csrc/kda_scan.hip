@@ -32,6 +32,10 @@ __device__ __forceinline__ bool nonzero4(float4 x) {
             (__builtin_bit_cast(uint32_t, x.z) & m) | (__builtin_bit_cast(uint32_t, x.w) & m)) != 0u;
 }
 
+__device__ __forceinline__ bool nonfinite1(float x) {
+    return (__builtin_bit_cast(uint32_t, x) & 0x7f800000u) == 0x7f800000u;
+}
+
 // Block-cooperative N-float tile held in registers (PER float4 per thread):
 // every load of a tile is issued before any of its stores, so a copy costs one
 // memory latency even where source and destination may alias.
@@ -58,6 +62,15 @@ template <int N> struct Tile {
 #pragma unroll
             for (int c = 0; c < 4; ++c) acc |= __builtin_bit_cast(uint32_t, x[i][c]) & 0x7fffffffu;
         return __syncthreads_or(acc != 0u) != 0;
+    }
+    // workgroup-uniform: some element is an infinity or a NaN
+    __device__ __forceinline__ bool any_nonfinite() const {
+        bool bad = false;
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) bad |= nonfinite1(x[i][c]);
+        return __syncthreads_or(bad) != 0;
     }
 };
 
@@ -98,8 +111,13 @@ template <int DK, int NC> struct Acc {
 
 // acc = L R (L row-major DK x DK, R row-major DK x NC), fp32 MFMA.  Lane
 // (n, g) of wave w holds rows w*DK/4 + 16 rt + 4 g + i of column 16 ct + n.
+//
+// lz / rz: the operand is exactly zero and its memory is not read (zeros are
+// multiplied instead), so that a zero matrix times a non-finite operand gives
+// NaN where the product would.
 template <int DK, int NC>
-__device__ __forceinline__ void mm_acc(const float *L, const float *R, Acc<DK, NC> &acc) {
+__device__ __forceinline__ void mm_acc(const float *L, const float *R, Acc<DK, NC> &acc,
+                                       bool lz = false, bool rz = false) {
     constexpr int RT = Acc<DK, NC>::RT, CT = Acc<DK, NC>::CT;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
@@ -114,9 +132,9 @@ __device__ __forceinline__ void mm_acc(const float *L, const float *R, Acc<DK, N
     for (int k0 = 0; k0 < DK; k0 += 4) {
         float a[RT], b[CT];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) a[rt] = L[(int64_t)(r0 + 16 * rt + n) * DK + k0 + g];
+        for (int rt = 0; rt < RT; ++rt) a[rt] = lz ? 0.f : L[(int64_t)(r0 + 16 * rt + n) * DK + k0 + g];
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) b[ct] = R[(int64_t)(k0 + g) * NC + 16 * ct + n];
+        for (int ct = 0; ct < CT; ++ct) b[ct] = rz ? 0.f : R[(int64_t)(k0 + g) * NC + 16 * ct + n];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -160,17 +178,24 @@ __device__ __forceinline__ void store_acc(const Acc<DK, NC> &acc, const float *A
     }
 }
 
-// out = L R + Add, or a copy of Add when L is zero (nz false).  out must not
-// alias L, R or Add.
+// out = L R + Add.  With nz false L is exactly zero and is not read: out is
+// a copy of Add, unless R holds an infinity or a NaN, in which case the
+// product is formed with zeros for L (0 * inf and 0 * NaN are NaN, as in the
+// product itself).  out must not alias L, R or Add.
 template <int DK, int NC>
 __device__ __forceinline__ void affine(const float *L, bool nz, const float *R, const float *Add,
                                        float *out) {
     if (!nz) {
-        copy_n<DK * NC>(out, Add);
-        return;
+        Tile<DK * NC> ta, tr;   // both loads in flight together
+        ta.load(Add);
+        tr.load(R);
+        if (!tr.any_nonfinite()) {
+            ta.store(out);
+            return;
+        }
     }
     Acc<DK, NC> acc;
-    mm_acc<DK, NC>(L, R, acc);
+    mm_acc<DK, NC>(L, R, acc, !nz);
     store_acc<DK, NC>(acc, Add, out);
 }
 
@@ -192,9 +217,12 @@ __global__ __launch_bounds__(NTH) void scan_seq_kernel(int H, int nseg, const fl
         const float *Dj = D + ((int64_t)j * H + h) * ss;
         // D_j is loaded with the zero test of M_j (one memory latency per
         // step in the usual case, where S_in[j+1] = D_j)
-        Tile<DK * DV> td;
+        Tile<DK * DV> td, ts;
         td.load(Dj);
-        if (!block_nonzero<DK * DK>(Mj)) {
+        ts.load(Sj);
+        // a zero M_j passes D_j on, unless S_in[j] holds an infinity or a NaN
+        // (0 * NaN is NaN): then the product is formed
+        if (!block_nonzero<DK * DK>(Mj) && !ts.any_nonfinite()) {
             td.store(dst);
         } else {
             affine<DK, DV>(Mj, true, Sj, Dj, dst);
@@ -205,12 +233,19 @@ __global__ __launch_bounds__(NTH) void scan_seq_kernel(int H, int nseg, const fl
 
 // ---------------------------------------------------------------------------
 // Blelloch scan over packages in the workspace:
-//   Pm [size+1][H][DK][DK], Pd [size+1][H][DK][DV], Fz [size+1][H] (1 = M may
-//   be nonzero); slot `size` keeps the total.  One workgroup per (pair, head),
-//   so each pair's slots are touched by one workgroup only.  Fz is
-//   authoritative: a slot whose flag is 0 holds a zero M whatever its Pm
-//   memory contains, so zero matrices are never written, copied or read.
+//   Pm [size+1][H][DK][DK], Pd [size+1][H][DK][DV], Fz [size+1][H]; slot
+//   `size` keeps the total.  One workgroup per (pair, head), so each pair's
+//   slots are touched by one workgroup only.  Flags per slot:
+//     kFlagM    M may be nonzero; without it the slot's M is exactly zero
+//               whatever its Pm memory holds (zero matrices are never
+//               written, copied or read);
+//     kFlagBad  M or D may hold an infinity or a NaN.
+//   A product with a zero M is skipped only when the other factor is finite:
+//   0 * inf and 0 * NaN are NaN, so against a flagged factor the product is
+//   formed with zeros in place of the unread M.
 // ---------------------------------------------------------------------------
+constexpr int kFlagM = 1, kFlagBad = 2;
+
 template <int DK, int DV>
 __global__ __launch_bounds__(NTH, 1) void blel_init_kernel(int H, int nseg, const float *M,
                                                         const float *D, float *Pm, float *Pd,
@@ -225,97 +260,83 @@ __global__ __launch_bounds__(NTH, 1) void blel_init_kernel(int H, int nseg, cons
         tm.load(M + ((int64_t)slot * H + h) * mm);
         td.load(D + ((int64_t)slot * H + h) * dd);
         const bool nz = tm.any_nonzero();
+        const bool bad = tm.any_nonfinite() || td.any_nonfinite();
         if (nz) tm.store(pm);
         td.store(pd);
-        if (threadIdx.x == 0) Fz[slot * H + h] = nz ? 1 : 0;
+        if (threadIdx.x == 0) Fz[slot * H + h] = (nz ? kFlagM : 0) | (bad ? kFlagBad : 0);
     } else {
         for (int e = threadIdx.x; e < DK * DK; e += NTH) pm[e] = (e / DK == e % DK) ? 1.f : 0.f;
         copy_n<DK * DV>(pd, nullptr);
-        if (threadIdx.x == 0) Fz[slot * H + h] = 1;
+        if (threadIdx.x == 0) Fz[slot * H + h] = kFlagM;
     }
 }
 
+// One combine of a level, P[later] o P[earlier] = (Ml Me, Ml De + Dl):
+//   up-sweep   (down = 0): P[i] <- P[i] o P[j]
+//   down-sweep (down = 1): (P[j], P[i]) <- (P[i], P[j] o P[i])
+// with i = (blockIdx.x + 1) * 2 * step - 1 and j = i - step.
 template <int DK, int DV>
 __global__ __launch_bounds__(NTH, 1) void blel_level_kernel(int H, int step, int down, float *Pm,
                                                          float *Pd, int *Fz) {
     const int h = blockIdx.y;
     const int64_t i = (int64_t)(blockIdx.x + 1) * 2 * step - 1, j = i - step;
+    const int64_t lat = down ? j : i, ear = down ? i : j;
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
-    float *Mi = Pm + (i * H + h) * mm, *Di = Pd + (i * H + h) * dd;
-    float *Mj = Pm + (j * H + h) * mm, *Dj = Pd + (j * H + h) * dd;
-    const int fi = Fz[i * H + h], fj = Fz[j * H + h];
-    if (!down) {
-        // P[i] = P[i] o P[j] = (Mi Mj, Mi Dj + Di); unchanged when Mi == 0
-        if (!fi) return;
-        const bool nz = block_nonzero<DK * DK>(Mi);
-        if (nz) {
-            Acc<DK, DK> am;
-            Acc<DK, DV> ad;
-            mm_acc<DK, DK>(Mi, Mj, am);
-            mm_acc<DK, DV>(Mi, Dj, ad);
-            __syncthreads();                       // every read of Mi precedes its overwrite
-            store_acc<DK, DK>(am, nullptr, Mi);
-            store_acc<DK, DV>(ad, Di, Di);
-        }
-        if (threadIdx.x == 0) Fz[i * H + h] = (nz && fj) ? 1 : 0;
-        return;
-    }
-    // down-sweep: (P[j], P[i]) = (P[i], P[j] o P[i]) with P[j] o P[i] = (Mj Mi, Mj Di + Dj)
-    const bool nz = fj ? block_nonzero<DK * DK>(Mj) : false;
-    if (!nz) {
-        // Mj == 0: P[j] <- P[i]; P[i] <- (0, Dj) (flag only); each thread
-        // moves only its own elements, all loaded before any is stored
-        if (fi) {
-            Tile<DK * DK> t;
-            t.load(Mi);
-            t.store(Mj);
-        }
-        Tile<DK * DV> a, b;
-        a.load(Di);
-        b.load(Dj);
-        a.store(Dj);
-        b.store(Di);
-        __syncthreads();   // every wave has read the flags before they change
-        if (threadIdx.x == 0) { Fz[j * H + h] = fi; Fz[i * H + h] = 0; }
-        return;
-    }
-    // general case: both products into accumulators, then each lane moves its
-    // own elements: P[j] <- old P[i], P[i] <- (Mj Mi, Mj Di + old Dj); a zero
-    // Mi (flag) leaves Mj Mi = 0 and moves no M
+    float *Ml = Pm + (lat * H + h) * mm, *Dl = Pd + (lat * H + h) * dd;
+    float *Me = Pm + (ear * H + h) * mm, *De = Pd + (ear * H + h) * dd;
+    const int fl = Fz[lat * H + h], fe = Fz[ear * H + h];
+    // exact zero tests: flags first, then the memory of a flagged later M
+    const bool zl = !(fl & kFlagM) || !block_nonzero<DK * DK>(Ml);
+    const bool ze = !(fe & kFlagM);
+    const bool bl = fl & kFlagBad, be = fe & kFlagBad;
+    // Ml Me is exactly zero when both are zero, or one is zero and the other finite
+    const bool need_mm = !((zl && ze) || (zl && !be) || (ze && !bl));
+    // Ml De is exactly zero when Ml is zero and De finite
+    const bool need_md = !(zl && !be);
     Acc<DK, DK> am;
     Acc<DK, DV> ad;
-    if (fi) mm_acc<DK, DK>(Mj, Mi, am);
-    mm_acc<DK, DV>(Mj, Di, ad);
-    __syncthreads();
-    {
-        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-        const int n = lane & 15, g = lane >> 4;
-        const int r0 = w * (DK / 4);
-        if (fi) {
+    if (need_mm) mm_acc<DK, DK>(Ml, Me, am, zl, ze);
+    if (need_md) mm_acc<DK, DV>(Ml, De, ad, zl, false);
+    __syncthreads();                       // every operand read precedes the first store
+    const int flags = (need_mm ? kFlagM : 0) | ((bl || be) ? kFlagBad : 0);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int r0 = w * (DK / 4);
+    // each lane moves exactly the elements it owns in the accumulator layout
+    if (!down) {
+        // result into slot i (= later)
+        if (need_mm) store_acc<DK, DK>(am, nullptr, Ml);
+        if (need_md) store_acc<DK, DV>(ad, Dl, Dl);
+        __syncthreads();                   // every wave has read the flags
+        if (threadIdx.x == 0) Fz[i * H + h] = flags;
+        return;
+    }
+    // down-sweep: slot j (= later) takes the old P[i] (= earlier), slot i the result
+    if ((fe & kFlagM) || need_mm) {
 #pragma unroll
-            for (int rt = 0; rt < Acc<DK, DK>::RT; ++rt)
+        for (int rt = 0; rt < Acc<DK, DK>::RT; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < Acc<DK, DK>::CT; ++ct)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int64_t e = (int64_t)(r0 + 16 * rt + 4 * g + q) * DK + 16 * ct + n;
-                        Mj[e] = Mi[e];
-                        Mi[e] = am.v[rt][ct][q];
-                    }
-        }
-#pragma unroll
-        for (int rt = 0; rt < Acc<DK, DV>::RT; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < Acc<DK, DV>::CT; ++ct)
+            for (int ct = 0; ct < Acc<DK, DK>::CT; ++ct)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int64_t e = (int64_t)(r0 + 16 * rt + 4 * g + q) * DV + 16 * ct + n;
-                    const float oj = Dj[e];
-                    Dj[e] = Di[e];
-                    Di[e] = ad.v[rt][ct][q] + oj;
+                    const int64_t e = (int64_t)(r0 + 16 * rt + 4 * g + q) * DK + 16 * ct + n;
+                    if (fe & kFlagM) Ml[e] = Me[e];
+                    if (need_mm) Me[e] = am.v[rt][ct][q];
                 }
     }
-    if (threadIdx.x == 0) { Fz[j * H + h] = fi; Fz[i * H + h] = fi ? 1 : 0; }
+#pragma unroll
+    for (int rt = 0; rt < Acc<DK, DV>::RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < Acc<DK, DV>::CT; ++ct)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t e = (int64_t)(r0 + 16 * rt + 4 * g + q) * DV + 16 * ct + n;
+                const float od = Dl[e];
+                Dl[e] = De[e];
+                De[e] = need_md ? ad.v[rt][ct][q] + od : od;
+            }
+    __syncthreads();                       // every wave has read the flags
+    if (threadIdx.x == 0) { Fz[j * H + h] = fe; Fz[i * H + h] = flags; }
 }
 
 // After the up-sweep: slot `size` = total, slot size-1 = identity.
@@ -329,7 +350,7 @@ __global__ __launch_bounds__(NTH) void blel_root_kernel(int H, int size, float *
     const int f_last = Fz[(size - 1) * H + h];
     {
         Tile<DK * DK> t;
-        if (f_last) {
+        if (f_last & kFlagM) {
             t.load(lm);
             t.store(tm);
         }
@@ -350,7 +371,7 @@ __global__ __launch_bounds__(NTH) void blel_root_kernel(int H, int size, float *
         t.store(ld);
     }
     __syncthreads();   // every wave has read the flags before they change
-    if (threadIdx.x == 0) { Fz[size * H + h] = f_last; Fz[(size - 1) * H + h] = 1; }
+    if (threadIdx.x == 0) { Fz[size * H + h] = f_last; Fz[(size - 1) * H + h] = kFlagM; }
 }
 
 // S_in[j] = P[j].M S0 + P[j].D (j < nseg);  S_final = P[size].M S0 + P[size].D.
@@ -365,14 +386,15 @@ __global__ __launch_bounds__(NTH) void blel_apply_kernel(int H, int nseg, int si
     const float *Lm = Pm + ((int64_t)slot * H + h) * mm;
     const float *Ad = Pd + ((int64_t)slot * H + h) * dd;
     float *out = jj < nseg ? S_in + ((int64_t)jj * H + h) * dd : S_final + (int64_t)h * dd;
-    Tile<DK * DV> ta;
-    ta.load(Ad);   // issued with the zero test: the usual case is a copy of Ad
-    const bool nz = (S0 && Fz[slot * H + h]) ? block_nonzero<DK * DK>(Lm) : false;
-    if (!nz) {
-        ta.store(out);
+    if (!S0) {   // a zero incoming state
+        copy_n<DK * DV>(out, Ad);
         return;
     }
-    affine<DK, DV>(Lm, true, S0 + (int64_t)h * dd, Ad, out);
+    const float *s0 = S0 + (int64_t)h * dd;
+    const bool nz = (Fz[slot * H + h] & kFlagM) ? block_nonzero<DK * DK>(Lm) : false;
+    // a zero prefix M (not read when flagged zero) passes Ad on unless S0 is
+    // not finite
+    affine<DK, DV>(Lm, nz, s0, Ad, out);
 }
 
 // Segment-path checkpoints: grid (rows, H).  Rung row r sits at

@@ -331,8 +331,9 @@ def kda_output_fixup(q, k, g, beta, seg_start, S_in, o, *, scale=1.0, qk_l2norm=
 
 
 def kda_checkpoint_write(seg_start, S_in, sub_M, sub_D, *, T, interval, dtype=torch.bfloat16,
-                         stream=None):
-    """Segment-path checkpoint states [T // interval, H, dk, dv]."""
+                         out=None, stream=None):
+    """Segment-path checkpoint states [T // interval, H, dk, dv] (into `out`
+    when given)."""
     rows, H, dk, dv = sub_D.shape
     dev = S_in.device
     nseg = seg_start.numel() - 1
@@ -340,7 +341,9 @@ def kda_checkpoint_write(seg_start, S_in, sub_M, sub_D, *, T, interval, dtype=to
     _need(S_in, "S_in", (nseg, H, dk, dv), torch.float32, dev)
     _need(sub_M, "sub_M", (rows, H, dk, dk), torch.float32, dev)
     cfg = make_config(H, dk, dv, dtype)
-    states = torch.empty((rows, H, dk, dv), dtype=torch.float32, device=dev)
+    states = out if out is not None else torch.empty((rows, H, dk, dv), dtype=torch.float32,
+                                                     device=dev)
+    _need(states, "out", (rows, H, dk, dv), torch.float32, dev)
     if rows == 0:
         return states
     ck = kda_ckpt(int(interval), None, ctypes.c_void_p(states.data_ptr()))

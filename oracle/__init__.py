@@ -344,9 +344,16 @@ def scan_blelloch(Ms, Ds, S0):
 
 
 def rel_l2(x, ref) -> float:
-    """||x - ref||_2 / ||ref||_2 over the whole tensor, in fp64."""
+    """||x - ref||_2 / ||ref||_2 over the whole tensor, in fp64.
+
+    The two arrays must have the same shape (no broadcasting).  A NaN or an
+    infinity anywhere in either makes the result NaN or infinite, which fails
+    every ``<= tol`` comparison.  With ref all zeros the absolute norm of x is
+    returned."""
     x = np.asarray(x, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
+    if x.shape != ref.shape:
+        raise ValueError(f"rel_l2: shapes differ: {x.shape} vs {ref.shape}")
     den = np.linalg.norm(ref.ravel())
     num = np.linalg.norm((x - ref).ravel())
     if den == 0.0:

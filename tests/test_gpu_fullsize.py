@@ -1,0 +1,277 @@
+"""GPU parity at the full workload sizes, in the launch configurations
+bench.py times, compared unit by unit with the fp64 oracle.
+
+* The 8,192-token single sequence: every head, both through the one-pass
+  chunked engine (minimal workspace) and through kda_prefill's segmented
+  processing (queried workspace).
+* The 16,384- and 131,072-token segment workloads: every head, per head over
+  the whole sequence, per (segment, head) over each segment's first rows, the
+  incoming states S_in, the rungs, and the output fix-up on its own: the
+  library's kda_output_fixup run from the oracle's S_in^j on zero outputs
+  against the oracle's correction (the segment run from S_in^j with zero
+  values).
+* The 64-sequence varlen batch: every sequence, on a head that rotates with
+  the sequence index.
+* Long-memory gates (log-decay ~ -1.2e-4 per token, beta ~ 2.5e-3) on the
+  16,384- and 131,072-token segmentations: M nonzero in every segment, the
+  scans' products and a fix-up that runs the whole segment.
+
+Tolerances: rel-L2 1e-4 for fp32 I/O; 2e-2 on outputs and 1e-2 on states for
+bf16 I/O; the worst unit decides.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from checks import (OUT_TOL, STATE_TOL, SegmentChecks, UnitErrors, per_head, seg_walk,
+                    slice_inputs)
+from workloads import ckpt_offsets, make_workload, standard_workload, to_f64, leveled_segments
+from workloads.device import to_numpy_f64, to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def K():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import gated_delta_rule_46_amd.kda as kda
+    return kda
+
+
+def sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# one sequence, 8,192 tokens, 32 heads
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def w1():
+    w = standard_workload(1)
+    ro, rS, _ = oracle.prefill(w.f64("q"), w.f64("k"), w.f64("v"), w.f64("g"), w.f64("beta"),
+                               w.cu_seqlens, S0=w.S0)
+    return w, ro, rS
+
+
+@pytest.mark.parametrize("path", ["one pass", "segmented"])
+def test_config1_all_heads(K, w1, path):
+    """kda_prefill on the 8,192-token sequence.  With a 256-byte workspace
+    the call runs the chunked engine in one pass (one workgroup per head and
+    value-column block); with the queried workspace it runs the sequence as
+    segments.  Every head against the oracle."""
+    import torch
+    w, ro, rS = w1
+    t = to_torch(w)
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda") if path == "one pass" else None
+    say(f"config1 T=8192 H=32 d=128 bf16, {path}, all heads")
+    o, Sf, _ = K.kda_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"], t["S0"],
+                             workspace=ws)
+    sync()
+    eo, es = UnitErrors(f"{path}: o per head"), UnitErrors(f"{path}: S_final per head")
+    heads = list(range(w.H))
+    per_head(eo, None, heads, to_numpy_f64(o), ro)
+    for h in heads:
+        es.add(h, to_numpy_f64(Sf[0, h]), rS[0, h])
+    eo.check(OUT_TOL["bf16"], say)
+    es.check(STATE_TOL["bf16"], say)
+
+
+# ---------------------------------------------------------------------------
+# segment workloads
+# ---------------------------------------------------------------------------
+def run_segment_path(K, w, t, algo, interval):
+    """package -> scan -> fix-up -> rungs, as one step of bench.py.  Returns
+    device tensors (o, o_local, M, D, S_in, S_final, rungs or None)."""
+    S0 = None if t["S0"] is None else t["S0"][0].contiguous()
+    ol, M, D, sM, sD = K.kda_segment_package(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                             t["seg_start"], ckpt_interval=interval,
+                                             scale=w.scale, qk_l2norm=bool(w.qk_l2norm))
+    S_in, S_fin = K.kda_segment_scan(M, D, S0, algo=algo)
+    o = ol.clone()
+    K.kda_output_fixup(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o,
+                       scale=w.scale, qk_l2norm=bool(w.qk_l2norm))
+    ck = None
+    if interval:
+        ck = K.kda_checkpoint_write(t["seg_start"], S_in, sM, sD, T=w.T, interval=interval,
+                                    dtype=t["q"].dtype)
+    sync()
+    return dict(o=o, o_local=ol, M=M, D=D, S_in=S_in, S_final=S_fin, ckpt=ck)
+
+
+def segment_parity(K, w, heads, algo, interval, check_packages=False):
+    """The segment path on all heads of w; the listed heads compared with the
+    oracle walked segment by segment (outputs, first rows, S_in, rungs,
+    S_final, and the fix-up alone from the oracle's S_in); with
+    check_packages also M, D and o_local per (segment, head)."""
+    import torch
+    t = to_torch(w)
+    r = run_segment_path(K, w, t, algo, interval)
+    hs = list(heads)
+    ht = torch.tensor(hs, device="cuda")
+    dt = "bf16" if w.dtype == "bf16" else "f32"
+    c = SegmentChecks(hs)
+    pk = {n: UnitErrors(f"{n} per (segment, head)") for n in ("M", "D", "o_local")}
+    rungs_got = None if r["ckpt"] is None else to_numpy_f64(r["ckpt"][:, ht])
+    S_in_got = to_numpy_f64(r["S_in"][:, ht])
+    nseg = len(w.seg_start) - 1
+    S_in_ref = np.zeros((nseg, w.H, w.dk, w.dv), dtype=np.float32)
+    corr_ref = {}
+    last = None
+    for s in seg_walk(w, hs, interval=interval, corrections=True):
+        j, a, b = s["j"], s["a"], s["b"]
+        o_got = to_numpy_f64(r["o"][a:b][:, ht])
+        c.add(s, o=o_got, S_in=S_in_got[j],
+              rungs=None if rungs_got is None else {row: rungs_got[row] for row, _ in s["rungs"]})
+        S_in_ref[j][hs] = s["S_in"].astype(np.float32)
+        corr_ref[j] = s["corr"].astype(np.float32)
+        if check_packages:
+            q, k, v, g, be = slice_inputs(w, a, b, hs)
+            Mr, Dr, olr = oracle.package(q, k, v, g, be, 0, b - a, scale=w.scale,
+                                         qk_l2norm=w.qk_l2norm)
+            for i, h in enumerate(hs):
+                pk["M"].add((j, h), to_numpy_f64(r["M"][j, h]), Mr[i])
+                pk["D"].add((j, h), to_numpy_f64(r["D"][j, h]), Dr[i])
+            per_head(pk["o_local"], j, hs, to_numpy_f64(r["o_local"][a:b][:, ht]), olr)
+        last = s
+        say(f"  segment {j} [{a}, {b}) compared")
+    # the fix-up alone, from the oracle's incoming states, on zero outputs
+    # (every head runs; the compared heads carry the oracle's S_in)
+    S_in_t = torch.from_numpy(S_in_ref).cuda()
+    z = torch.zeros_like(r["o"])
+    K.kda_output_fixup(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in_t, z,
+                       scale=w.scale, qk_l2norm=bool(w.qk_l2norm))
+    sync()
+    for s in seg_walk_meta(w):
+        j, a, b = s
+        corr_got = to_numpy_f64(z[a:b][:, ht])
+        per_head(c.corr, j, hs, corr_got, corr_ref[j].astype(np.float64))
+    worst = c.check(OUT_TOL[dt], STATE_TOL[dt], say)
+    ef = UnitErrors("S_final per head")
+    Sf = to_numpy_f64(r["S_final"][ht])
+    for i, h in enumerate(hs):
+        ef.add(h, Sf[i], last["S_out"][i])
+    worst["S_final"] = ef.check(STATE_TOL[dt], say)
+    if check_packages:
+        for n, e in pk.items():
+            worst[n] = e.check(OUT_TOL[dt] if n == "o_local" else STATE_TOL[dt], say)
+    return r, worst
+
+
+def seg_walk_meta(w):
+    seg = w.seg_start
+    for j in range(len(seg) - 1):
+        yield j, int(seg[j]), int(seg[j + 1])
+
+
+def test_config2_all_heads(K):
+    w = standard_workload(2)
+    say("config2: T=16384 H=32 d=128 bf16, 4 x 4096 segments, sequential scan, all heads")
+    segment_parity(K, w, range(w.H), algo=0, interval=0)
+
+
+def test_config3_all_heads(K):
+    w = standard_workload(3)
+    say("config3: T=131072 H=32 d=128 bf16, 16 leveled segments, Blelloch, rungs every 4096, "
+        "all heads")
+    r, _ = segment_parity(K, w, range(w.H), algo=1, interval=w.ckpt_interval)
+    assert r["ckpt"].shape[0] == 32
+
+
+def test_config4_every_sequence(K):
+    """The 64-sequence varlen batch: every sequence compared, each on its own
+    head (h = (5 n + 3) mod 32), with its S_final and rungs."""
+    import torch
+    w = standard_workload(4)
+    say("config4: 64 varlen sequences (447,540 tokens) H=32 d=128 bf16, ckpt 4096, "
+        "every sequence")
+    t = to_torch(w)
+    off_np = ckpt_offsets(w.lengths, w.ckpt_interval)
+    off = torch.from_numpy(off_np).cuda()
+    o_t, Sf_t, ck_t = K.kda_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"],
+                                    t["S0"], ckpt_interval=w.ckpt_interval, ckpt_offsets=off)
+    sync()
+    assert ck_t.shape[0] == 82
+    N = w.N
+    hsel = (5 * np.arange(N) + 3) % w.H
+    cu = w.cu_seqlens
+    # one-head inputs: the rows of sequence n from head hsel[n]
+    rowh = np.repeat(hsel, w.lengths)
+    ar = np.arange(w.T)
+
+    def pick(x):
+        return x[ar, rowh][:, None]
+    q, k, v = (to_f64(pick(getattr(w, n)), w.dtype) for n in ("q", "k", "v"))
+    g = pick(w.g).astype(np.float64)
+    beta = w.beta[ar, rowh][:, None].astype(np.float64)
+    S0 = w.S0[np.arange(N), hsel][:, None].astype(np.float64)
+    ro, rS, rck = oracle.prefill(q, k, v, g, beta, cu, S0=S0, ckpt_interval=w.ckpt_interval,
+                                 ckpt_offsets=off_np)
+    rowh_t = torch.from_numpy(rowh).cuda()
+    o_got = to_numpy_f64(o_t[torch.arange(w.T, device="cuda"), rowh_t])
+    Sf = to_numpy_f64(Sf_t[torch.arange(N, device="cuda"), torch.from_numpy(hsel).cuda()])
+    eo, es, ec = (UnitErrors(f"{x} per (sequence, head)") for x in ("o", "S_final", "rungs"))
+    ck = to_numpy_f64(ck_t)
+    for n in range(N):
+        a, b = int(cu[n]), int(cu[n + 1])
+        eo.add((n, int(hsel[n])), o_got[a:b], ro[a:b, 0])
+        es.add((n, int(hsel[n])), Sf[n], rS[n, 0])
+        for row in range(int(off_np[n]), int(off_np[n + 1])):
+            ec.add((n, row), ck[row, hsel[n]], rck[row, 0])
+    eo.check(OUT_TOL["bf16"], say)
+    es.check(STATE_TOL["bf16"], say)
+    ec.check(STATE_TOL["bf16"], say)
+
+
+# ---------------------------------------------------------------------------
+# long-memory gates at length
+# ---------------------------------------------------------------------------
+LONG = dict(gate_shift=-9.0, beta_shift=-6.0)
+
+
+@pytest.mark.parametrize("segmentation", ["4x4096", "16 leveled"])
+def test_long_memory_fp32_d64(K, segmentation):
+    """fp32 I/O, d = 64, 2 heads, long-memory gates on the segmentations of
+    the 16,384- and 131,072-token workloads: M stays far from zero in every
+    segment, the scan multiplies every package and the fix-up runs every
+    segment to its end."""
+    if segmentation == "4x4096":
+        T, seg, algo, iv = 16384, np.arange(0, 16385, 4096), 0, 0
+    else:
+        T, seg, algo, iv = 131072, leveled_segments(131072, 16), 1, 4096
+    w = make_workload(f"long-f32-{T}", [T], 2, 64, 64, "f32", 4800 + algo, s0_std=0.5,
+                      seg_start=seg, **LONG)
+    say(f"long memory fp32 d=64 H=2 T={T} segments {segmentation} algo={algo}")
+    r, worst = segment_parity(K, w, range(2), algo=algo, interval=iv, check_packages=True)
+    M = to_numpy_f64(r["M"])
+    norms = np.linalg.norm(M.reshape(M.shape[0], M.shape[1], -1), axis=-1)
+    say(f"  |M|_F per segment: min {norms.min():.3f} max {norms.max():.3f}")
+    assert norms.min() > 0.1
+
+
+@pytest.mark.parametrize("segmentation", ["4x4096", "16 leveled"])
+def test_long_memory_bf16_d128(K, segmentation):
+    """bf16 I/O, d = 128, 32 heads (the workloads' shape), long-memory gates:
+    three sampled heads compared, including M, D and o_local per segment; the
+    bf16 state operand of the products is exercised over thousands of chunks."""
+    if segmentation == "4x4096":
+        w = standard_workload(2, **LONG)
+        algo, iv, heads = 0, 0, (0, 13, 31)
+    else:
+        w = standard_workload(3, **LONG)
+        algo, iv, heads = 1, w.ckpt_interval, (2, 17, 30)
+    say(f"long memory bf16 d=128 H=32 T={w.T} segments {segmentation} algo={algo}, "
+        f"heads {heads}")
+    r, worst = segment_parity(K, w, heads, algo=algo, interval=iv, check_packages=True)
+    M = to_numpy_f64(r["M"][:, list(heads)])
+    norms = np.linalg.norm(M.reshape(M.shape[0], M.shape[1], -1), axis=-1)
+    say(f"  |M|_F per segment: min {norms.min():.3f} max {norms.max():.3f}")
+    assert norms.min() > 0.1

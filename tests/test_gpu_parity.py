@@ -1,8 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
 Tolerances are rel-L2 over the compared tensor: 1e-4 for fp32 I/O; for bf16
-I/O 2e-2 on outputs and 1e-2 on states.  Full-size workloads are compared on
-sampled (sequence, head) units that the oracle recomputes one by one.
+I/O 2e-2 on outputs and 1e-2 on states.  The full-size workloads are in
+test_gpu_fullsize.py.
 """
 import sys
 
@@ -403,9 +403,6 @@ def test_segment_package_without_M(K):
 
 
 # ---------------------------------------------------------------------------
-# full-size standard workloads, sampled units
-# ---------------------------------------------------------------------------
-# ---------------------------------------------------------------------------
 # Prefill resumed from a state pool
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 64)])
@@ -665,54 +662,162 @@ def test_short_conv_full_size_sampled(K):
     assert_close("short conv full-size sampled rows", got, ref, OUT_TOL["bf16"])
 
 
-def test_config1_full(K):
-    say("config1: T=8192 H=32 d=128 bf16 chunked prefill (sampled heads 0, 17, 31)")
+# ---------------------------------------------------------------------------
+# Non-finite inputs propagate; exact-zero shortcuts do not mask them
+# ---------------------------------------------------------------------------
+BF16_NAN = 0x7FC0
+
+
+def test_nan_propagation_prefill(K):
+    """A NaN in one key channel of one token reaches every later output of
+    that (sequence, head) and its final state and later rungs (the oracle's
+    answer: the normalised key, then the state, is NaN from that token on).
+    Chunks before it and every other sequence and head match the oracle."""
+    lens = [300, 500, 200]
+    w = make_workload("nan", lens, 2, 128, 128, "bf16", 4900, s0_std=0.1)
+    n, h, rel = 1, 1, 150
+    tok = lens[0] + rel
+    w.k[tok, h, 5] = BF16_NAN
+    say(f"NaN in k at token {tok} (sequence {n}, head {h}), prefill bf16 d=128, rungs every 128")
+    o, Sf, ck = run_prefill(K, w, interval=128)
+    ro, rS, rck = oracle_full(w, interval=128)
+    off = ckpt_offsets(w.lengths, 128)
+    # the oracle itself: NaN from the token on, finite before
+    assert np.isnan(ro[tok:tok + lens[1] - rel, h]).all() and np.isfinite(ro[:tok, h]).all()
+    chunk0 = lens[0] + (rel // 64) * 64          # first row of the chunk holding the NaN
+    end = lens[0] + lens[1]
+    assert np.isnan(o[tok:end, h]).all(), "rows from the NaN token on must all be NaN"
+    assert np.isnan(Sf[n, h]).all()
+    assert_close("o before the NaN's chunk", o[lens[0]:chunk0, h], ro[lens[0]:chunk0, h], OUT_TOL["bf16"])
+    for m in range(3):
+        for hh in range(2):
+            if (m, hh) == (n, h):
+                continue
+            a, b = w.cu_seqlens[m], w.cu_seqlens[m + 1]
+            assert_close(f"o[seq {m}, head {hh}]", o[a:b, hh], ro[a:b, hh], OUT_TOL["bf16"])
+            assert_close(f"S_final[seq {m}, head {hh}]", Sf[m, hh], rS[m, hh], STATE_TOL["bf16"])
+    rows = range(int(off[n]), int(off[n + 1]))   # rungs at 128, 256, 384 of sequence 1
+    assert_close("rung before the NaN", ck[rows[0], h], rck[rows[0], h], STATE_TOL["bf16"])
+    for r in rows[1:]:
+        assert np.isnan(ck[r, h]).all()
+    assert np.isfinite(ck[:, 0]).all()
+
+
+@pytest.mark.parametrize("algo", [0, 1])
+@pytest.mark.parametrize("gates", ["config", "long"])
+def test_nan_propagation_segment_path(K, algo, gates):
+    """A NaN in a key of segment 1 (head 1) reaches every later output of
+    that head, its final state and later rungs through the packages, the
+    scan, the fix-up and the checkpoint writer.  With the configs' gates the
+    next segment's M is exactly zero: the scans must still form 0 * NaN
+    rather than pass D on.  Head 0 and segment 0 match the oracle."""
+    shift = {} if gates == "config" else dict(gate_shift=-9.0, beta_shift=-6.0)
+    seg = [0, 512, 1024, 1536, 2048]
+    w = make_workload("nan-seg", [2048], 2, 128, 128, "bf16", 4901 + algo, s0_std=0.3,
+                      seg_start=seg, **shift)
+    h, tok = 1, 600
+    w.k[tok, h, 77] = BF16_NAN
+    say(f"NaN in k at token {tok} head {h}, segment path algo={algo} gates={gates}")
+    r = _segment_case(K, w, algo, interval=128)
+    ro, rS, rck = oracle_full(w, interval=128)
+    if gates == "config":
+        assert np.count_nonzero(r["M"][2, h]) == 0     # the shortcut is really taken
+    else:
+        assert np.count_nonzero(r["M"][2, h]) > 0
+    assert np.isnan(r["M"][1, h]).all() and np.isnan(r["D"][1, h]).all()
+    assert np.isnan(r["S_in"][2:, h]).all()
+    assert np.isnan(r["o"][tok:, h]).all(), "rows from the NaN token on must all be NaN"
+    assert np.isnan(r["S_final"][h]).all()
+    assert_close("o, segment 0, head 1", r["o"][:512, h], ro[:512, h], OUT_TOL["bf16"])
+    assert_close("o, head 0", r["o"][:, 0], ro[:, 0], OUT_TOL["bf16"])
+    assert_close("S_final, head 0", r["S_final"][0], rS[0, 0], STATE_TOL["bf16"])
+    assert_close("rungs 128 .. 512, head 1", r["ckpt"][:4, h], rck[:4, h], STATE_TOL["bf16"])
+    assert np.isnan(r["ckpt"][4:, h]).all()
+    assert_close("rungs, head 0", r["ckpt"][:, 0], rck[:, 0], STATE_TOL["bf16"])
+
+
+@pytest.mark.parametrize("algo", [0, 1])
+def test_scan_zero_M_against_nonfinite(K, algo):
+    """Scans over random packages where a zero M meets an infinite or NaN
+    operand: the zero shortcut is taken only against finite values, so the
+    result has NaN exactly in the columns the product 0 * x makes NaN, and
+    every other column equals the oracle's scan."""
     import torch
-    w = standard_workload(1)
-    o, Sf, _ = run_prefill_t(K, w)
-    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(Sf).all())
-    for h in (0, 17, 31):
-        ro, rS, _ = oracle_unit(w, 0, h)
-        assert_close(f"o[h={h}]", to_numpy_f64(o[:, h]), ro[:, 0], OUT_TOL["bf16"])
-        assert_close(f"S_final[h={h}]", to_numpy_f64(Sf[0, h]), rS[0, 0], STATE_TOL["bf16"])
+    from workloads import make_packages
+    nseg, H, d = 6, 2, 64
+    M, D, S0 = make_packages(nseg, H, d, d, 4950 + algo, zero=(1, 2, 4))
+    D[0, 1, 3, 7] = np.inf         # head 1: column 7 of D_0, then of S_in[1]
+    S0[0, 5, 9] = np.nan           # head 0: column 9 of S0
+    say(f"scan algo={algo} with inf / NaN operands against zero M")
+    tM, tD, tS0 = (torch.from_numpy(x).cuda() for x in (M, D, S0))
+    S_in, S_fin = K.kda_segment_scan(tM, tD, tS0, algo=algo)
+    sync()
+    S_in, S_fin = to_numpy_f64(S_in), to_numpy_f64(S_fin)
+    with np.errstate(invalid="ignore"):
+        ref_in, ref_fin = oracle.scan_sequential([m.astype(np.float64) for m in M],
+                                                 [x.astype(np.float64) for x in D],
+                                                 S0.astype(np.float64))
+    # numpy's matmul is IEEE: the oracle marks the same columns
+    for name, got, ref in (("S_in", S_in, ref_in), ("S_final", S_fin, ref_fin)):
+        assert np.array_equal(np.isnan(got), np.isnan(ref)), f"{name}: NaN pattern differs"
+        assert np.array_equal(np.isinf(got), np.isinf(ref)), f"{name}: inf pattern differs"
+        fin = np.isfinite(ref)
+        assert_close(f"{name} (finite entries)", got[fin], ref[fin], 1e-4)
+    # the NaN columns really appear after a zero M
+    assert np.isnan(ref_in[2, 1, :, 7]).all() and np.isnan(ref_in[1, 0, :, 9]).all()
 
 
-def test_config2_full(K):
-    say("config2: T=16384 H=32 d=128 bf16, 4x4096 segments, sequential scan (heads 3, 30)")
-    w = standard_workload(2)
-    heads = (3, 30)
-    r = _segment_case(K, w, 0, interval=0, heads=heads)
-    for i, h in enumerate(heads):
-        ro, rS, _ = oracle_unit(w, 0, h)
-        assert_close(f"o[h={h}]", r["o"][:, i], ro[:, 0], OUT_TOL["bf16"])
-        assert_close(f"S_final[h={h}]", r["S_final"][i], rS[0, 0], STATE_TOL["bf16"])
-
-
-def test_config3_full(K):
-    say("config3: T=131072 H=32 d=128 bf16, 16 leveled segments, Blelloch, ckpt 4096 (head 5)")
-    w = standard_workload(3)
-    h = 5
-    r = _segment_case(K, w, 1, interval=w.ckpt_interval, heads=(h,))
-    assert np.all(np.isfinite(r["o"]))
-    ro, rS, rck = oracle_unit(w, 0, h, interval=w.ckpt_interval)
-    assert_close(f"o[h={h}]", r["o"][:, 0], ro[:, 0], OUT_TOL["bf16"])
-    assert_close(f"S_final[h={h}]", r["S_final"][0], rS[0, 0], STATE_TOL["bf16"])
-    assert_close(f"ckpt[h={h}]", r["ckpt"][:, 0], rck[:, 0], STATE_TOL["bf16"])
-
-
-def test_config4_full(K):
-    say("config4: 64 varlen sequences (447,540 tokens) H=32 d=128 bf16, ckpt 4096")
-    w = standard_workload(4)
-    o_t, Sf_t, ck_t = run_prefill_t(K, w, interval=w.ckpt_interval)
-    assert ck_t.shape[0] == 82
-    Sf, ck = to_numpy_f64(Sf_t), to_numpy_f64(ck_t)
-    off = ckpt_offsets(w.lengths, w.ckpt_interval)
-    L = w.lengths
-    picks = [int(np.argmax(L)), int(np.argmin(L)), 7]
-    for n, h in zip(picks, (0, 13, 31)):
-        ro, rS, rck = oracle_unit(w, n, h, interval=w.ckpt_interval)
-        a, b = w.cu_seqlens[n], w.cu_seqlens[n + 1]
-        assert_close(f"o[n={n},h={h}]", to_numpy_f64(o_t[a:b, h]), ro[:, 0], OUT_TOL["bf16"])
-        assert_close(f"S_final[n={n},h={h}]", Sf[n, h], rS[0, 0], STATE_TOL["bf16"])
-        if rck is not None and rck.shape[0]:
-            assert_close(f"ckpt[n={n},h={h}]", ck[off[n]:off[n + 1], h], rck[:, 0], STATE_TOL["bf16"])
+# ---------------------------------------------------------------------------
+# Stream ordering of checkpoint stores
+# ---------------------------------------------------------------------------
+def test_checkpoint_stream_ordering(K):
+    """Rung states read on a second stream after an event recorded on the
+    compute stream right after the producing call are the fresh ones: every
+    kernel of kda_prefill and of the segment path runs on the stream it is
+    given.  Each rung buffer is filled with NaN first, behind a long queue of
+    work on the compute stream.  The copy made without waiting on the event
+    is reported (how much of it was fresh), not asserted."""
+    import torch
+    w = make_workload("order", [8192], 4, 128, 128, "bf16", 4960, s0_std=0.1,
+                      seg_start=[0, 2048, 4096, 6144, 8192])
+    t = to_torch(w)
+    compute, store = torch.cuda.Stream(), torch.cuda.Stream()
+    ref = None
+    fresh_unfenced = []
+    for rep in range(3):
+        for path in ("prefill", "segment"):
+            ck = torch.full((8192 // 1024, 4, 128, 128), float("nan"), dtype=torch.float32,
+                            device="cuda")
+            torch.cuda.synchronize()    # the NaN sentinel is in place before anything runs
+            with torch.cuda.stream(compute):
+                for _ in range(4):      # queue ahead of the producer
+                    K.kda_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"], t["S0"],
+                                  workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
+                if path == "prefill":
+                    K.kda_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"], t["S0"],
+                                  ckpt_interval=1024, ckpt_out=ck,
+                                  ckpt_offsets=torch.tensor([0, 8], device="cuda"),
+                                  workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
+                else:
+                    o, M, D, sM, sD = K.kda_segment_package(t["q"], t["k"], t["v"], t["g"],
+                                                            t["beta"], t["seg_start"],
+                                                            ckpt_interval=1024)
+                    S_in, _ = K.kda_segment_scan(M, D, t["S0"][0].contiguous(), algo=1)
+                    K.kda_checkpoint_write(t["seg_start"], S_in, sM, sD, T=8192, interval=1024,
+                                           out=ck)
+                ev = torch.cuda.Event()
+                ev.record(compute)
+            with torch.cuda.stream(store):
+                early = ck.clone()      # no wait: may read the buffer before the rungs land
+                store.wait_event(ev)
+                late = ck.clone()
+            ck.record_stream(store)
+            torch.cuda.synchronize()
+            fresh_unfenced.append(float(torch.isfinite(early).float().mean()))
+            assert bool(torch.isfinite(late).all()), f"{path}: a fenced read saw a stale rung"
+            got = to_numpy_f64(late)
+            if ref is None:
+                ref = oracle_full(w, interval=1024)[2]
+            assert_close(f"{path} rungs read on the store stream (rep {rep})", got, ref,
+                         STATE_TOL["bf16"])
+    say(f"fresh fraction of the copies made without the fence: {fresh_unfenced}")
