@@ -312,6 +312,24 @@ __global__ __launch_bounds__(NTH, 1) void blel_level_kernel(int H, int step, int
         return;
     }
     // down-sweep: slot j (= later) takes the old P[i] (= earlier), slot i the result
+    if (!need_mm && !need_md) {
+        // the usual case (Ml zero against finite factors): P[j] <- P[i],
+        // P[i] <- (0, Dj); whole tiles through registers, every load before
+        // any store
+        if (fe & kFlagM) {
+            Tile<DK * DK> t;
+            t.load(Me);
+            t.store(Ml);
+        }
+        Tile<DK * DV> a, b;
+        a.load(De);
+        b.load(Dl);
+        a.store(Dl);
+        b.store(De);
+        __syncthreads();                   // every wave has read the flags
+        if (threadIdx.x == 0) { Fz[j * H + h] = fe; Fz[i * H + h] = flags; }
+        return;
+    }
     if ((fe & kFlagM) || need_mm) {
 #pragma unroll
         for (int rt = 0; rt < Acc<DK, DK>::RT; ++rt)
@@ -412,9 +430,25 @@ __global__ __launch_bounds__(NTH) void ckpt_kernel(int H, int nseg, const int64_
     while (j + 1 < nseg && seg_start[j + 1] < p) ++j;
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
     const float *Lm = sub_M + (r * H + h) * mm;
-    const bool nz = block_nonzero<DK * DK>(Lm);
-    affine<DK, DV>(Lm, nz, S_in + ((int64_t)j * H + h) * dd, sub_D + (r * H + h) * dd,
-                   states + (r * H + h) * dd);
+    const float *Sj = S_in + ((int64_t)j * H + h) * dd;
+    bool nz, bad;
+    {   // the zero test of sub_M and the finiteness test of S_in^j, all loads in flight
+        Tile<DK * DK> tl;
+        Tile<DK * DV> ts;
+        tl.load(Lm);
+        ts.load(Sj);
+        nz = tl.any_nonzero();
+        bad = ts.any_nonfinite();
+    }
+    const float *Dr = sub_D + (r * H + h) * dd;
+    float *out = states + (r * H + h) * dd;
+    if (!nz && !bad) {
+        copy_n<DK * DV>(out, Dr);
+        return;
+    }
+    Acc<DK, DV> acc;
+    mm_acc<DK, DV>(Lm, Sj, acc, !nz);
+    store_acc<DK, DV>(acc, Dr, out);
 }
 
 // Longest-first order of up to kPlanMax sequences (rank sort on chunk counts,
