@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "kda.h"
@@ -192,13 +193,44 @@ int prefill_split(const SplitPlan &p, const kda_config *cfg, const void *q, cons
     return ok();
 }
 
+// Scratch of kda_prefill_noalloc: one fixed array per device, held for the
+// life of the process, in place of the caller's workspace.  In host code the
+// array's name only stands in for the symbol; the device address of each
+// device's copy comes from hipGetSymbolAddress, called once per device with
+// that device current, and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+int scratch_address(void **out) {
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(KDA_ERR_UNSUPPORTED, "device index %d beyond the %d the library tracks", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(KDA_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return KDA_OK;
+}
+
 // Chunked prefill with initial / final states either dense (S0, S_final) or
 // in a slot pool; pos0 (nullable) shifts the checkpoint grid.
 int prefill_impl(const char *what, const kda_config *cfg, const void *q, const void *k,
                  const void *v, const float *g, const float *beta, const int64_t *cu_seqlens,
                  int32_t N, int64_t T, const float *S0, float *S_final,
                  const kda_state_pool *pool, const int64_t *pos0, void *o, const kda_ckpt *ckpt,
-                 void *ws, size_t ws_bytes, void *stream) {
+                 void *ws, size_t ws_bytes, void *stream, bool noalloc = false) {
     KDA_TRY(check_config(cfg));
     if (T < 0) return fail(KDA_ERR_ARG, "T must be >= 0 (got %lld)", (long long)T);
     if (N < 0) return fail(KDA_ERR_ARG, "N must be >= 0 (got %d)", N);
@@ -229,6 +261,15 @@ int prefill_impl(const char *what, const kda_config *cfg, const void *q, const v
         KDA_TRY(check_tensor(ckpt->offsets, "ckpt->offsets", N > 1, 8));
     }
     const size_t need = prefill_ws_bytes(N);
+    if (noalloc) {
+        // the library's fixed scratch stands in for the workspace
+        if (need > (size_t)KDA_NOALLOC_SCRATCH_BYTES)
+            return fail(KDA_ERR_WORKSPACE,
+                        "N = %d sequences need %zu bytes of scratch, more than the fixed %zu", N,
+                        need, (size_t)KDA_NOALLOC_SCRATCH_BYTES);
+        KDA_TRY(scratch_address(&ws));
+        ws_bytes = KDA_NOALLOC_SCRATCH_BYTES;
+    }
     if (!ws || ws_bytes < need)
         return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, ws_bytes);
     KDA_TRY(check_tensor(ws, "ws", true, 16));
@@ -300,6 +341,17 @@ int kda_prefill(const kda_config *cfg, const void *q, const void *k, const void 
                 void *ws, size_t ws_bytes, void *stream) {
     return prefill_impl("prefill", cfg, q, k, v, g, beta, cu_seqlens, N, T, S0, S_final, nullptr,
                         nullptr, o, ckpt, ws, ws_bytes, stream);
+}
+
+int kda_prefill_noalloc(const kda_config *cfg, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta, const int64_t *cu_seqlens, int32_t N,
+                        int64_t T, const float *S0, float *S_final, void *o, const kda_ckpt *ckpt,
+                        void *stream) {
+    // arguments are checked first; the scratch then stands in for a caller's
+    // workspace of KDA_NOALLOC_SCRATCH_BYTES (the one-pass schedule needs N
+    // int32 entries, the segmented path of one sequence runs when it fits)
+    return prefill_impl("prefill (no allocation)", cfg, q, k, v, g, beta, cu_seqlens, N, T, S0,
+                        S_final, nullptr, nullptr, o, ckpt, nullptr, 0, stream, true);
 }
 
 int kda_prefill_resume(const kda_config *cfg, const void *q, const void *k, const void *v,

@@ -19,7 +19,8 @@ KDA_DTYPE_F32, KDA_DTYPE_BF16 = 0, 1
 KDA_SCAN_SEQUENTIAL, KDA_SCAN_BLELLOCH = 0, 1
 CHUNK = 64
 
-EXPORTS = ("kda_prefill_workspace", "kda_prefill", "kda_prefill_resume", "kda_segment_package",
+EXPORTS = ("kda_prefill_workspace", "kda_prefill", "kda_prefill_noalloc", "kda_prefill_resume",
+           "kda_segment_package",
            "kda_segment_scan_workspace", "kda_segment_scan", "kda_output_fixup",
            "kda_checkpoint_write", "kda_decode", "kda_short_conv", "kda_conv_halo",
            "kda_status_string", "kda_last_error", "kda_version")
@@ -65,6 +66,7 @@ def _load():
     sig = {
         "kda_prefill_workspace": (S, [cfgp, I64, I32]),
         "kda_prefill": (ctypes.c_int, [cfgp, P, P, P, P, P, P, I32, I64, P, P, P, ckp, P, S, P]),
+        "kda_prefill_noalloc": (ctypes.c_int, [cfgp, P, P, P, P, P, P, I32, I64, P, P, P, ckp, P]),
         "kda_prefill_resume": (ctypes.c_int, [cfgp, P, P, P, P, P, P, I32, I64, P, poolp, P, ckp,
                                               P, S, P]),
         "kda_segment_package": (ctypes.c_int, [cfgp, P, P, P, P, P, I64, P, I32, P, P, P, ckp,
@@ -215,6 +217,49 @@ def kda_prefill(q, k, v, g, beta, cu_seqlens, S0=None, *, want_final=True, ckpt_
     st = LIB.kda_prefill(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(cu_seqlens),
                          N, T, _p(S0), _p(Sf), _p(o), ckp, _p(ws), wsb, _stream(stream))
     _check(st, "kda_prefill")
+    return o, Sf, ck
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # KDA_NOALLOC_SCRATCH_BYTES
+
+
+def kda_prefill_noalloc(q, k, v, g, beta, cu_seqlens, S0=None, *, ckpt_interval=0,
+                        ckpt_offsets=None, ckpt_out=None, scale=1.0, qk_l2norm=True, out=None,
+                        final_out=None, want_final=True, stream=None):
+    """kda_prefill through the entry point that allocates nothing: the
+    library's fixed per-device scratch replaces the workspace.  Outputs are
+    allocated here unless passed (out, final_out, ckpt_out), so a caller that
+    passes all of them makes no allocation at all.  Returns (o, S_final or
+    None, checkpoint states or None)."""
+    T, H, dk, dv, dev = _inputs(q, k, v, g, beta)
+    N = cu_seqlens.numel() - 1
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int64, dev)
+    cfg = make_config(H, dk, dv, q.dtype, scale, qk_l2norm)
+    if S0 is not None:
+        _need(S0, "S0", (N, H, dk, dv), torch.float32, dev)
+    o = out if out is not None else torch.empty((T, H, dv), dtype=q.dtype, device=dev)
+    _need(o, "out", (T, H, dv), q.dtype, dev)
+    Sf = final_out
+    if Sf is None and want_final:
+        Sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    if Sf is not None:
+        _need(Sf, "final_out", (N, H, dk, dv), torch.float32, dev)
+    ck = None
+    ckp = None
+    if ckpt_interval:
+        if ckpt_offsets is None:
+            if N != 1:
+                raise ValueError("ckpt_offsets is required for more than one sequence")
+            rows = T // ckpt_interval
+        else:
+            _need(ckpt_offsets, "ckpt_offsets", (N + 1,), torch.int64, dev)
+            rows = _ckpt_rows(ckpt_offsets, ckpt_out)
+        ck = _ckpt_tensor(ckpt_out, rows, H, dk, dv, dev)
+        ckp = ctypes.pointer(kda_ckpt(int(ckpt_interval), _p(ckpt_offsets),
+                                      _p(ck) if rows else ctypes.c_void_p(o.data_ptr())))
+    st = LIB.kda_prefill_noalloc(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(g), _p(beta),
+                                 _p(cu_seqlens), N, T, _p(S0), _p(Sf), _p(o), ckp, _stream(stream))
+    _check(st, "kda_prefill_noalloc")
     return o, Sf, ck
 
 

@@ -65,8 +65,9 @@
  *    o, states, M, D, workspace) must be 16-byte aligned, beta 4-byte and the
  *    int64 index arrays 8-byte aligned (KDA_ERR_ALIGN otherwise).
  *  - Ownership: the caller owns every buffer.  The library allocates no
- *    device memory and keeps none between calls; scratch comes from the
- *    caller's workspace, sized by the matching *_workspace query.
+ *    device memory; scratch comes from the caller's workspace, sized by the
+ *    matching *_workspace query (kda_prefill_noalloc: a fixed array inside
+ *    the library, the only device memory it holds between calls).
  *  - Asynchrony: all work is enqueued on `stream` (a hipStream_t; NULL = the
  *    null stream) without synchronising.  Argument errors are detected on
  *    the host and returned before anything is launched.  A failed launch
@@ -76,7 +77,7 @@
  *    16-token block must stay above about -80 (a mean alpha above ~0.007
  *    per token); beyond it intermediate exponentials leave fp32 range.
  *  - Threading: reentrant; the only process state is a per-thread error
- *    string.
+ *    string and, for kda_prefill_noalloc, its fixed per-device scratch.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -180,6 +181,28 @@ int kda_prefill(const kda_config *cfg, const void *q, const void *k, const void 
                 const float *g, const float *beta, const int64_t *cu_seqlens, int32_t N,
                 int64_t T, const float *S0, float *S_final, void *o, const kda_ckpt *ckpt,
                 void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * kda_prefill for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and arguments, with no workspace argument.  Its
+ * scratch is a fixed array of KDA_NOALLOC_SCRATCH_BYTES inside the library,
+ * one per device, held until the process ends; the call makes no hipMalloc
+ * or hipFree and calls no allocating routine.  The result is the one
+ * kda_prefill gives with a workspace of that size: a single sequence runs as
+ * segments when their buffers fit (64 MiB holds them for 8,192 tokens at
+ * H = 32, d = 128 without checkpoints), otherwise in one pass.
+ * KDA_ERR_WORKSPACE when N * 4 bytes of schedule exceed the scratch.  Every
+ * call on one device shares that device's scratch: calls that overlap on a
+ * device (other streams, other threads) race and must be serialised by the
+ * caller.  No byte of the scratch needs to start at zero: a call reads only
+ * what it wrote earlier in the same call.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int kda_prefill_noalloc(const kda_config *cfg, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta, const int64_t *cu_seqlens, int32_t N,
+                        int64_t T, const float *S0, float *S_final, void *o, const kda_ckpt *ckpt,
+                        void *stream);
 
 /*
  * Chunked prefill that continues N sequences from states in a pool.

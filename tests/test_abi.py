@@ -287,3 +287,31 @@ def test_short_conv_validates():
     halo = K.LIB.kda_conv_halo(1, 64, 4, FAKE, 128, FAKE, 2,
                                ctypes.byref(K.kda_conv_state(FAKE, 4, None, None)), None)
     assert halo == K.KDA_ERR_ARG and "write_idx" in last_error()
+
+
+def test_prefill_noalloc_validates_before_touching_the_device():
+    """The no-allocation entry point checks its arguments like kda_prefill
+    and refuses a schedule larger than its fixed scratch, all before any
+    device call (so these run without a GPU)."""
+    c = cfg()
+
+    def call(q=FAKE, N=2, T=128, c_=c):
+        return K.LIB.kda_prefill_noalloc(ctypes.byref(c_) if c_ is not None else None, q, FAKE,
+                                         FAKE, FAKE, FAKE, FAKE, N, T, None, None, FAKE, None,
+                                         None)
+    assert call(c_=None) == K.KDA_ERR_ARG
+    assert call(q=None) == K.KDA_ERR_ARG
+    assert call(q=MISALIGNED) == K.KDA_ERR_ALIGN
+    assert call(N=-1) == K.KDA_ERR_ARG
+    assert call(N=0, T=0) == K.KDA_OK
+    assert call(c_=cfg(dk=96, dv=96)) == K.KDA_ERR_UNSUPPORTED
+    big = K.NOALLOC_SCRATCH_BYTES // 4 + 1
+    assert call(N=big, T=big) == K.KDA_ERR_WORKSPACE
+    assert "scratch" in last_error()
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+KDA_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", text)
+    assert m, "KDA_NOALLOC_SCRATCH_BYTES not found"
+    assert int(m.group(1)) << int(m.group(2)) == K.NOALLOC_SCRATCH_BYTES
