@@ -172,7 +172,7 @@ int prefill_split(const SplitPlan &p, const kda_config *cfg, const void *q, cons
     a.ckpt_off = nullptr; a.ckpt_S = sub_D; a.ckpt_M = sub_M;
     a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;
     a.ncb = dv / nb;
-    a.ncb_m = dk / nb;
+    a.ncb_m = dk / std::min(nb, dk);   // M has dk columns
     if ((e = kda::launch_engine(kda::kModePackageVM, bf, dk, dv, nb, a, s)) != hipSuccess)
         return launched(e, "prefill split (package)");
     if ((e = kda::launch_scan_sequential(dk, dv, H, p.nseg, M, D, S0, S_in, S_fin, s)) != hipSuccess)
@@ -402,7 +402,7 @@ int kda_segment_package(const kda_config *cfg, const void *q, const void *k, con
     // Value blocks, and with M the M blocks after them in the same grid (they
     // stop as soon as M is exactly zero and fill the value blocks' tail).
     a.ncb = cfg->dv / nb;
-    a.ncb_m = cfg->dk / nb;
+    a.ncb_m = cfg->dk / std::min(nb, cfg->dk);   // M has dk columns
     return launched(kda::launch_engine(M ? kda::kModePackageVM : kda::kModePackage, bf, cfg->dk,
                                        cfg->dv, nb, a, s), "package");
 }

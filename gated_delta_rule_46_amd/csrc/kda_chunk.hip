@@ -1,1005 +1,28 @@
-// kda_chunk.hip -- warp-specialised chunkwise KDA engine for gfx950 (MI355X).
-//
-// One workgroup (8 wave64s) walks one (unit, head, column block) through its
-// chunks of 64 tokens in order.  A unit is a sequence (prefill) or a segment
-// (package / fix-up).  The waves split into two roles that run concurrently:
-//
-//   producers (waves 0-3, one per 16-row block b of the chunk) prepare chunk
-//     c+1: loads (prefetched one chunk ahead), L2 norms, in-block cumulative
-//     log2-decay, exponentials and the Gram matrices A and P on MFMA;
-//   consumers (waves 4-7) own a quarter of the state's columns each (fp32 MFMA
-//     accumulators) and apply chunk c:
-//         U = (I + A)^-1 (beta V - R_k S)       R_k = beta K*Gam
-//         O = (Q*Gam) S + P U,   S <- Diag(gamma_C) S + Kbar^T U.
-//
-// Two workgroup barriers per chunk.  Between the second barrier and the first
-// the consumers apply chunk c (reading every hand-off tile) while the
-// producers do all the work of chunk c+1 that only needs their own block:
-// norms, decay scan, exponentials and diagonal Gram blocks.  Between the
-// first barrier and the second the producers combine the block totals into
-// the per-channel factors, write the hand-off tiles and the adjacent
-// off-diagonal Gram blocks (b, b-1), while consumers 0-2 form the three
-// farther blocks (3,0), (3,1), (2,0), consumer 3 the diagonal inverses
-// T_bb = (I + A_bb)^-1, and all of them store checkpoint rungs and run the
-// zero test.  Every hand-off tile has a single copy (T_bb keeps two, by chunk
-// parity).
-//
-// Numerical scheme: one reference point per 16-row block.  The diagonal block
-// uses the block start (lhs factor <= 1, rhs factor <= e^{span of 16 tokens}),
-// off-diagonal blocks use the end of the earlier block (all factors <= 1).
-// Valid while a channel's log-decay over any aligned 16 tokens stays above
-// about -80.  Per element only two exponentials are evaluated; every other
-// factor is a per-channel constant computed once per channel.
-//
-// The chunkwise algebra is derived from the KDA recurrence (pegainfer PR #970
-// names the (M,D) segment packages built on it; the chunk form is the WY / UT
-// form of the delta rule).
+// kda_chunk.hip -- shape dispatch of the chunk engine (kda_engine.h), whose
+// instantiations live in one translation unit per shape family
+// (kda_chunk_*.hip).
 
 #include "kda_internal.h"
-#include "kda_mfma.h"
 
 namespace kda {
-namespace {
 
-using namespace mf;
-
-constexpr int kThreads = 512;
-
-// Returns x unchanged, but hides its value from the optimiser.  Lane indices
-// are laundered through it at the top of every phase so that LDS addresses are
-// recomputed inside the phase instead of being hoisted out of the chunk loop
-// (hundreds of hoisted addresses otherwise exhaust the register file).
-__device__ __forceinline__ int opaque(int x) {
-    asm volatile("" : "+v"(x));
-    return x;
-}
-
-// Compact storage of the six strictly-lower 16x16 blocks (b, a), a < b.
-__host__ __device__ constexpr int aoff_idx(int b, int a) { return b * (b - 1) / 2 + a; }
-
-template <int DK, int NB, bool BF> struct Lds {
-    using T = typename Ops<BF>::T;
-    // Row padding.  Tiles that the consumers read as 8-byte fragments (two
-    // per operand) keep a row stride of 2 mod 4 dwords in bf16: gfx950 serves
-    // an 8-byte LDS access 16 lanes at a time over 32 four-byte banks, so the
-    // 16 rows of a fragment then fall on 16 distinct bank pairs (a stride of
-    // 0 mod 4 dwords puts rows m and m+8 on the same pair).  Those rows are
-    // only 8-byte aligned and are written with 8-byte stores.  Producer-only
-    // tiles, read and written 16 bytes per lane, use a stride of 8 mod 16
-    // dwords, which measured free of conflicts for 16-byte accesses.
-    static constexpr int PAD = BF ? 4 : Ops<BF>::PAD;
-    static constexpr int PADR = BF ? 16 : Ops<BF>::PAD;
-    static constexpr int ES = (int)sizeof(T);
-    static constexpr int LDQ = DK + PAD;        // [64][DK] row-major tiles
-    static constexpr int LDK = 64 + PAD;        // [DK][64] transposed Kbar
-    static constexpr int LDP = 64 + PAD;        // [64][64] P
-    static constexpr int LDV = NB + PAD;        // [64][NB] beta*V
-    static constexpr int LDT = 16 + PAD;        // 16x16 blocks
-    static constexpr int LDR = DK + PADR;       // producer-side [rows][DK] tiles
-    static constexpr int LDAD = 20;             // fp32 16x16 blocks
-    static constexpr int o_flag = 0;                                  // int[16]
-    static constexpr int o_gam = 64;                                  // f32 [DK]
-    static constexpr int o_tot = o_gam + DK * 4;                      // f32 [4][DK]
-    static constexpr int o_fac = o_tot + 4 * DK * 4;                  // f32 [4][4][DK]
-    static constexpr int o_qbar = o_fac + 16 * DK * 4;                // hand-off: Q Gam
-    static constexpr int o_rk = o_qbar + 64 * LDQ * ES;               // hand-off: -R_k
-    static constexpr int o_kbt = o_rk + 64 * LDQ * ES;                // hand-off: Kbar^T
-    static constexpr int o_p = o_kbt + DK * LDK * ES;                 // hand-off: P
-    static constexpr int o_bv = o_p + 64 * LDP * ES;                  // hand-off: beta V
-    static constexpr int o_aoff = o_bv + 64 * LDV * ES;               // hand-off: -A blocks
-    static constexpr int o_td = o_aoff + 6 * 16 * LDT * ES;           // hand-off: T_bb [2][4]
-    static constexpr int o_ad = o_td + 2 * 4 * 16 * LDT * ES;         // producer scratch
-    static constexpr int o_ro = o_ad + 4 * 16 * LDAD * 4;             // rhs of blocks 0-2
-    static constexpr int o_lk = o_ro + 48 * LDR * ES;                 // lhs (K) of blocks 2, 3
-    static constexpr int o_lq = o_lk + 32 * LDR * ES;                 // lhs (Q) of blocks 2, 3
-    static constexpr int o_cf = o_lq + 32 * LDR * ES;                 // f32 [3][DK] rescales
-    static constexpr int size = o_cf + 3 * DK * 4;
-    static_assert(o_qbar % 16 == 0 && o_rk % 16 == 0 && o_kbt % 16 == 0 && o_p % 16 == 0 &&
-                  o_bv % 16 == 0 && o_aoff % 16 == 0 && o_td % 16 == 0 && o_ad % 16 == 0 &&
-                  o_ro % 16 == 0 && o_lk % 16 == 0 && o_lq % 16 == 0 && o_cf % 16 == 0,
-                  "LDS alignment");
-    static_assert((LDQ * ES) % 8 == 0 && (LDK * ES) % 8 == 0 && (LDP * ES) % 8 == 0 &&
-                  (LDV * ES) % 8 == 0 && (LDT * ES) % 8 == 0 && (LDR * ES) % 16 == 0,
-                  "row alignment of 8-byte and 16-byte LDS accesses");
-    static_assert(size <= 160 * 1024, "LDS budget");
-};
-
-// Raw rows of one chunk held in registers between the prefetch and its use.
-template <bool BF, int KS, int VS> struct Raw {
-    static constexpr int W8 = BF ? 4 : 8;      // 32-bit words per 8 elements
-    uint32_t q[KS * W8], k[KS * W8], g[KS * 8], v[VS * W8];
-    float b;
-};
-
-template <bool BF>
-__device__ __forceinline__ void ld_words(const void *base, int64_t idx, uint32_t *w) {
-    if (BF) {
-        const uint4 x = *(const uint4 *)((const __bf16 *)base + idx);
-        w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
-    } else {
-        const uint4 x = *(const uint4 *)((const float *)base + idx);
-        const uint4 y = *(const uint4 *)((const float *)base + idx + 4);
-        w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
-        w[4] = y.x; w[5] = y.y; w[6] = y.z; w[7] = y.w;
-    }
-}
-
-template <bool BF>
-__device__ __forceinline__ void unpack_words(const uint32_t *w, float *out) {
-    if (BF) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            out[2 * j] = __builtin_bit_cast(float, w[j] << 16);
-            out[2 * j + 1] = __builtin_bit_cast(float, w[j] & 0xffff0000u);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) out[j] = __builtin_bit_cast(float, w[j]);
-    }
-}
-
-template <int DKT, int NTW>
-__device__ __forceinline__ void store_state(float *dst, int ld, int col0, int gq, int m,
-                                            const f32x4 (&S)[DKT][NTW], bool zero) {
-#pragma unroll
-    for (int r = 0; r < DKT; ++r)
-#pragma unroll
-        for (int n = 0; n < NTW; ++n)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                dst[(int64_t)(16 * r + 4 * gq + i) * ld + col0 + 16 * n + m] = zero ? 0.f : S[r][n][i];
-}
-
-template <int MODE, bool MB> struct Roles {
-    static constexpr bool HAS_V = (MODE != kModeFixup) && !MB;   // beta V enters U
-    static constexpr bool HAS_O = !MB;                           // outputs are produced
-    static constexpr bool CHECK0 = (MODE == kModeFixup) || MB;   // stop once S is exactly 0
-};
-
-// ===========================================================================
-// Producer wave for row block B of every chunk.
-// ===========================================================================
-template <int DK, int DV, int NB, bool BF, int MODE, bool MB, int B>
-__device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *smem, const int h,
-                                         const int cbase, const int64_t t0, const int64_t t1,
-                                         const int nchunks) {
-    using O = Ops<BF>;
-    using T = typename O::T;
-    using F8 = typename O::F8;
-    using L = Lds<DK, NB, BF>;
-    using R = Roles<MODE, MB>;
-    constexpr int KS = DK / 32;      // 32-channel steps of a row
-    constexpr int VS = NB / 32;      // 32-column steps of the value block
-    constexpr int W8 = BF ? 4 : 8;
-
-    int *s_flag = (int *)(smem + L::o_flag);
-    float *s_gam = (float *)(smem + L::o_gam);
-    float *s_tot = (float *)(smem + L::o_tot);
-    float *s_fac = (float *)(smem + L::o_fac);
-    T *s_qbar = (T *)(smem + L::o_qbar);
-    T *s_rk = (T *)(smem + L::o_rk);
-    T *s_kbt = (T *)(smem + L::o_kbt);
-    T *s_p = (T *)(smem + L::o_p);
-    T *s_bv = (T *)(smem + L::o_bv);
-    T *s_aoff = (T *)(smem + L::o_aoff);
-    T *s_td = (T *)(smem + L::o_td);
-    float *s_ad = (float *)(smem + L::o_ad);
-    T *s_ro = (T *)(smem + L::o_ro);
-    T *s_lk = (T *)(smem + L::o_lk);
-    T *s_lq = (T *)(smem + L::o_lq);
-
-    const int lane = threadIdx.x & 63;
-    const int H = a.H;
-
-    // Blocks of P right of the diagonal are zero in every chunk.
-    if (R::HAS_O) {
-        const int m = lane & 15, gq = lane >> 4;
-#pragma unroll
-        for (int a2 = B + 1; a2 < 4; ++a2)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s_p[(16 * B + 4 * gq + i) * L::LDP + 16 * a2 + m] = (T)0.f;
-    }
-    // Identity selectors: an MFMA of a row-layout fragment with isel[hh]
-    // returns channels 16hh..16hh+15 of the 32-channel step transposed.
-    F8 isel[2];
-    {
-        const int n = lane & 15, g = lane >> 4;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            float e[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) e[j] = (8 * g + j == 16 * hh + n) ? 1.f : 0.f;
-            isel[hh] = O::cvt8(e);
-        }
-    }
-
-    Raw<BF, KS, VS> raw;
-    bool raw_valid = false;
-    int64_t ld_tok = t0;
-    // Rows of chunk c.  A row past the end of the unit is read from the unit's
-    // first row (always in bounds) and masked to zero when used, so the loads
-    // need no branches.
-    auto set_rows = [&](int c) {
-        const int m = opaque(lane) & 15;
-        const int64_t r = t0 + (int64_t)c * kChunk + 16 * B + m;
-        raw_valid = r < t1;
-        ld_tok = raw_valid ? r : t0;
-    };
-    auto issue_g = [&]() {
-        const int gq = opaque(lane) >> 4;
-        const int64_t base = (ld_tok * H + h) * DK;
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) ld_words<false>(a.g, base + 32 * kk + 8 * gq, &raw.g[8 * kk]);
-        raw.b = a.beta[ld_tok * H + h];
-    };
-    auto issue_kq = [&]() {
-        const int gq = opaque(lane) >> 4;
-        const int64_t base = (ld_tok * H + h) * DK;
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) ld_words<BF>(a.k, base + 32 * kk + 8 * gq, &raw.k[W8 * kk]);
-        if (R::HAS_O) {
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) ld_words<BF>(a.q, base + 32 * kk + 8 * gq, &raw.q[W8 * kk]);
-        }
-    };
-    auto issue_v = [&]() {
-        const int gq = opaque(lane) >> 4;
-        const int64_t vb = (ld_tok * H + h) * DV + cbase;
-#pragma unroll
-        for (int kk = 0; kk < VS; ++kk) ld_words<BF>(a.v, vb + 32 * kk + 8 * gq, &raw.v[W8 * kk]);
-    };
-
-    float bt = 0.f;
-    F8 lhsK[KS], rhsD[KS], lhsQ[KS], bvp[VS];
-    f32x4 Pd;
-
-    // Own-block work of chunk c (runs while the consumers apply chunk c-1):
-    // decay scan and block totals, norms, two exponentials per element, the
-    // Gram fragments, the rhs tile R_o of later blocks, the diagonal Gram
-    // blocks and T_bb.  Issues the loads of chunk c+1 as registers free up.
-    auto phase_own = [&](int c) {
-        const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
-        const int prow = 16 * B + m;
-        const bool more = c + 1 < nchunks;
-        const bool partial = t0 + (int64_t)(c + 1) * kChunk > t1;
-        const float vm = raw_valid ? 1.f : 0.f;
-        float gl[KS * 8];
-#pragma unroll
-        for (int e = 0; e < KS * 8; ++e) gl[e] = __builtin_bit_cast(float, raw.g[e]);
-        if (partial) {   // padded rows act as identity: g = 0, k = q = v = 0, beta = 0
-#pragma unroll
-            for (int e = 0; e < KS * 8; ++e) gl[e] *= vm;
-        }
-        bt = raw.b * vm;
-#pragma unroll
-        for (int e = 0; e < KS * 8; ++e) gl[e] = scan16(gl[e] * kLog2e);
-        float fk, fq = 0.f;
-        if constexpr (BF) {
-            // |row|^2 of the raw bf16 rows as the diagonal of their 16x16 Gram
-            // block on the matrix core; entry (r, r) sits in lane r + 16*(r/4),
-            // element r % 4.
-            f32x4 Gk = {0.f, 0.f, 0.f, 0.f}, Gq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const uint4 *)&raw.k[W8 * kk]);
-                Gk = O::mma32(Gk, kf, kf);
-                if (R::HAS_O) {
-                    const bf16x8 qf = __builtin_bit_cast(bf16x8, *(const uint4 *)&raw.q[W8 * kk]);
-                    Gq = O::mma32(Gq, qf, qf);
-                }
-            }
-            const int src = m + 16 * (m >> 2), e = m & 3;
-            const float dk = e == 0 ? Gk[0] : e == 1 ? Gk[1] : e == 2 ? Gk[2] : Gk[3];
-            fk = (a.l2norm ? rsqrtf(__shfl(dk, src) + kEps) : 1.f) * vm;
-            if (R::HAS_O) {
-                const float dq = e == 0 ? Gq[0] : e == 1 ? Gq[1] : e == 2 ? Gq[2] : Gq[3];
-                fq = (a.l2norm ? a.scale * rsqrtf(__shfl(dq, src) + kEps) : a.scale) * vm;
-            }
-        } else {
-            float sk = 0.f, sq = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                float x[8];
-                unpack_words<BF>(&raw.k[W8 * kk], x);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) sk += x[j] * x[j];
-                if (R::HAS_O) {
-                    unpack_words<BF>(&raw.q[W8 * kk], x);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) sq += x[j] * x[j];
-                }
-            }
-            sk += __shfl_xor(sk, 16); sk += __shfl_xor(sk, 32);
-            fk = (a.l2norm ? rsqrtf(sk + kEps) : 1.f) * vm;
-            if (R::HAS_O) {
-                sq += __shfl_xor(sq, 16); sq += __shfl_xor(sq, 32);
-                fq = (a.l2norm ? a.scale * rsqrtf(sq + kEps) : a.scale) * vm;
-            }
-        }
-        if (R::HAS_V) {
-#pragma unroll
-            for (int kk = 0; kk < VS; ++kk) {
-                float x[8];
-                unpack_words<BF>(&raw.v[W8 * kk], x);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] *= bt;
-                bvp[kk] = O::cvt8(x);
-            }
-        }
-        if (more) {
-            set_rows(c + 1);
-            issue_g();
-            if (R::HAS_V) issue_v();
-        }
-        if (m == 15) {
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                float *d = s_tot + B * DK + 32 * kk + 8 * gq;
-                *(f32x4 *)d = f32x4{gl[8 * kk], gl[8 * kk + 1], gl[8 * kk + 2], gl[8 * kk + 3]};
-                *(f32x4 *)(d + 4) = f32x4{gl[8 * kk + 4], gl[8 * kk + 5], gl[8 * kk + 6], gl[8 * kk + 7]};
-            }
-        }
-        float *fown = s_fac + B * 4 * DK;   // e^{tot_B}: rhs of later blocks
-        if (B < 3) {
-            wave_sync_lds();
-            for (int ch = opaque(lane); ch < DK; ch += 64) fown[ch] = ex2(s_tot[B * DK + ch]);
-            wave_sync_lds();
-        }
-        const float fkb = fk * bt;
-        f32x4 Ad = {0.f, 0.f, 0.f, 0.f};
-        Pd = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            const int c0 = 32 * kk + 8 * gq;
-            float e1[8], e2[8], kx[8], lk[8], rd[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) { e1[j] = ex2(gl[8 * kk + j]); e2[j] = ex2(-gl[8 * kk + j]); }
-            unpack_words<BF>(&raw.k[W8 * kk], kx);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                lk[j] = kx[j] * fkb * e1[j];
-                rd[j] = kx[j] * fk * e2[j];
-            }
-            lhsK[kk] = O::cvt8(lk);
-            rhsD[kk] = O::cvt8(rd);
-            if (B < 3) {
-                const f32x4 f0 = *(const f32x4 *)(fown + c0), f1 = *(const f32x4 *)(fown + c0 + 4);
-                float t8[8];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) { t8[j] = rd[j] * f0[j]; t8[j + 4] = rd[j + 4] * f1[j]; }
-                O::st8(s_ro + prow * L::LDR + c0, t8);
-            }
-            if (R::HAS_O) {
-                float qx[8], lq[8];
-                unpack_words<BF>(&raw.q[W8 * kk], qx);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) lq[j] = qx[j] * fq * e1[j];
-                lhsQ[kk] = O::cvt8(lq);
-                Pd = O::mma32(Pd, lhsQ[kk], rhsD[kk]);
-                if (B >= 2) O::stf(s_lq + (prow - 32) * L::LDR + c0, lhsQ[kk]);
-            }
-            // the far off-diagonal blocks of rows 32..63 are formed by consumer waves
-            if (B >= 2) O::stf(s_lk + (prow - 32) * L::LDR + c0, lhsK[kk]);
-            Ad = O::mma32(Ad, lhsK[kk], rhsD[kk]);
-            // one 32-channel step at a time keeps the fp32 temporaries short-lived
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (more) issue_kq();
-
-        // A_bb for the substitution (consumer 3 forms T_bb between the barriers)
-        float *ad = s_ad + B * 16 * L::LDAD;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ad[(4 * gq + i) * L::LDAD + m] = Ad[i];
-    };
-
-    // Cross-block work of chunk c (runs while the consumers store rungs):
-    // per-channel factors from the four block totals, the hand-off tiles and
-    // the off-diagonal Gram blocks (B, a2), a2 < B.
-    auto phase_cross = [&]() {
-        const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
-        const int prow = 16 * B + m;
-        // Factors of block B (log2 domain, all <= 1), rho_a = decay at the end
-        // of block a:  [0] e^{rho_{B-1}}   (Qbar, R_k)
-        //              [1] e^{G_C - rho_{B-1}}   (Kbar)
-        float *fac = s_fac + B * 4 * DK;
-        for (int ch = opaque(lane); ch < DK; ch += 64) {
-            const float u0 = s_tot[ch], u1 = s_tot[DK + ch], u2 = s_tot[2 * DK + ch], u3 = s_tot[3 * DK + ch];
-            const float rho = (B >= 1 ? u0 : 0.f) + (B >= 2 ? u1 : 0.f) + (B >= 3 ? u2 : 0.f);
-            const float gc = u0 + u1 + u2 + u3;
-            if (B > 0) fac[ch] = ex2(rho);
-            fac[DK + ch] = ex2(gc - rho);
-            if (B == 0) s_gam[ch] = ex2(gc);
-        }
-        wave_sync_lds();
-        if (R::HAS_V) {
-#pragma unroll
-            for (int kk = 0; kk < VS; ++kk) O::stf_h(s_bv + prow * L::LDV + 32 * kk + 8 * gq, bvp[kk]);
-        }
-        if (R::HAS_O) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                s_p[(16 * B + 4 * gq + i) * L::LDP + 16 * B + m] = (T)((m <= 4 * gq + i) ? Pd[i] : 0.f);
-        }
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            const int c0 = 32 * kk + 8 * gq;
-            {   // Kbar = rd * e^{G_C - rho_{B-1}}, stored transposed via two MFMAs
-                float rd[8], kb[8];
-                O::unpack8(rhsD[kk], rd);
-                const f32x4 f0 = *(const f32x4 *)(fac + DK + c0), f1 = *(const f32x4 *)(fac + DK + c0 + 4);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) { kb[j] = rd[j] * f0[j]; kb[j + 4] = rd[j + 4] * f1[j]; }
-                const F8 kbf = O::cvt8(kb);
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const f32x4 tr = O::mma32(f32x4{0.f, 0.f, 0.f, 0.f}, kbf, isel[hh]);
-                    O::st4(s_kbt + (32 * kk + 16 * hh + m) * L::LDK + 16 * B + 4 * gq, tr);
-                }
-            }
-            if (B == 0) {   // block 0 is referenced to the chunk start already
-                O::stf_h(s_rk + prow * L::LDQ + c0, O::neg(lhsK[kk]));
-                if (R::HAS_O) O::stf_h(s_qbar + prow * L::LDQ + c0, lhsQ[kk]);
-            } else {
-                const f32x4 f0 = *(const f32x4 *)(fac + c0), f1 = *(const f32x4 *)(fac + c0 + 4);
-                float x[8], t8[8];
-                O::unpack8(lhsK[kk], x);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) { t8[j] = -(x[j] * f0[j]); t8[j + 4] = -(x[j + 4] * f1[j]); }
-                O::st8_h(s_rk + prow * L::LDQ + c0, t8);
-                if (R::HAS_O) {
-                    O::unpack8(lhsQ[kk], x);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) { t8[j] = x[j] * f0[j]; t8[j + 4] = x[j + 4] * f1[j]; }
-                    O::st8_h(s_qbar + prow * L::LDQ + c0, t8);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // The adjacent off-diagonal block (B, B-1): rhs rows of block B-1 are
-        // referenced to its end, which is where block B's lhs starts, so no
-        // rescale.  Blocks further back are formed by consumer waves.
-        if (B >= 1) {
-            constexpr int a2 = B >= 1 ? B - 1 : 0;
-            f32x4 Ao = {0.f, 0.f, 0.f, 0.f}, P_ = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const int c0 = 32 * kk + 8 * gq;
-                const F8 Bf = O::ld8(s_ro + (16 * a2 + m) * L::LDR + c0);
-                Ao = O::mma32(Ao, lhsK[kk], Bf);
-                if (R::HAS_O) P_ = O::mma32(P_, lhsQ[kk], Bf);
-            }
-            T *dst = s_aoff + aoff_idx(B, a2) * 16 * L::LDT;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                dst[(4 * gq + i) * L::LDT + m] = (T)(-Ao[i]);
-                if (R::HAS_O) s_p[(16 * B + 4 * gq + i) * L::LDP + 16 * a2 + m] = (T)P_[i];
-            }
-        }
-    };
-
-    // prologue: chunk 0
-    if (nchunks > 0) {
-        set_rows(0);
-        issue_g();
-        issue_kq();
-        if (R::HAS_V) issue_v();
-        phase_own(0);
-    }
-    __syncthreads();                                                          // BA
-    if (nchunks > 0) phase_cross();
-    __syncthreads();                                                          // BB
-    for (int c = 0; c < nchunks; ++c) {
-        if (R::CHECK0 && c > 0 && !(s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3])) return;
-        const bool next = c + 1 < nchunks;
-        if (next) phase_own(c + 1);
-        __syncthreads();                                                      // BA
-        if (next) phase_cross();
-        __syncthreads();                                                      // BB
-    }
-}
-
-// ===========================================================================
-// Consumer wave pw: state columns cbase + pw*NB/4 .. + NB/4 - 1.
-// ===========================================================================
-template <int DK, int DV, int NB, bool BF, int MODE, bool MB>
-__device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *smem, const int u,
-                                         const int h, const int cbase, const int64_t t0,
-                                         const int64_t t1, const int nchunks, const int pw) {
-    using O = Ops<BF>;
-    using T = typename O::T;
-    using F8 = typename O::F8;
-    using F4 = typename O::F4;
-    using L = Lds<DK, NB, BF>;
-    using R = Roles<MODE, MB>;
-    constexpr int KS = DK / 32;
-    constexpr int NBW = NB / 4;      // state columns per consumer wave
-    constexpr int NTW = NBW / 16;    // state column tiles per consumer wave
-    constexpr int DKT = DK / 16;     // state row tiles
-    constexpr int LDST = MB ? DK : DV;
-    static_assert(NTW >= 1, "tile shape");
-
-    int *s_flag = (int *)(smem + L::o_flag);
-    const float *s_gam = (const float *)(smem + L::o_gam);
-    const T *s_qbar = (const T *)(smem + L::o_qbar);
-    const T *s_rk = (const T *)(smem + L::o_rk);
-    const T *s_kbt = (const T *)(smem + L::o_kbt);
-    const T *s_p = (const T *)(smem + L::o_p);
-    const T *s_bv = (const T *)(smem + L::o_bv);
-    const T *s_aoff = (const T *)(smem + L::o_aoff);
-    const T *s_td = (const T *)(smem + L::o_td);
-
-    const int lane = threadIdx.x & 63;
-    const int m = lane & 15, gq = lane >> 4;
-    const int H = a.H;
-    const int64_t len = t1 - t0;
-    const int wcol = cbase + pw * NBW;
-
-    f32x4 S[DKT][NTW];
-    // rungs sit at absolute positions pbase + p (p sequence-relative)
-    const int64_t pbase = (MODE == kModePrefill && a.pos0) ? a.pos0[u] : 0;
-    {
-        const float *src = nullptr;
-        if (MODE == kModePrefill && a.s_in_idx) {
-            const int32_t slot = a.s_in_idx[u];
-            if (slot >= 0 && slot < a.n_slots) src = a.S_init + ((int64_t)slot * H + h) * DK * DV;
-        } else if (MODE == kModePrefill && a.S_init) {
-            src = a.S_init + (int64_t)(u * H + h) * DK * DV;
-        }
-        if (MODE == kModeFixup) src = a.S_init + (int64_t)(u * H + h) * DK * DV;
-#pragma unroll
-        for (int r = 0; r < DKT; ++r)
-#pragma unroll
-            for (int n = 0; n < NTW; ++n)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * r + 4 * gq + i, col = wcol + 16 * n + m;
-                    float val = src ? src[(int64_t)row * DV + col] : 0.f;
-                    if (MB) val = (row == col) ? 1.f : 0.f;
-                    S[r][n][i] = val;
-                }
-    }
-    auto state_nonzero = [&]() -> bool {
-        bool nz = false;
-#pragma unroll
-        for (int r = 0; r < DKT; ++r)
-#pragma unroll
-            for (int n = 0; n < NTW; ++n)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    nz |= (__builtin_bit_cast(uint32_t, S[r][n][i]) & 0x7fffffffu) != 0u;
-        return __ballot(nz) != 0ull;
-    };
-    if (MODE == kModeFixup) {
-        // An all-zero incoming state leaves o_local final: skip the unit.
-        const bool nz = state_nonzero();
-        if (lane == 0) s_flag[pw] = nz ? 1 : 0;
-        __syncthreads();
-        const bool any = s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3];
-        __syncthreads();
-        if (!any) return;
-    }
-
-    // beta V enters U through an MFMA with an identity selector: the A operand
-    // is a 32-column window of the beta V tile, isel[n] picks this wave's
-    // column tile n out of it in the MFMA output layout.
-    const int win = (pw * NBW) & ~31;
-    F8 isel[NTW];
-#pragma unroll
-    for (int n = 0; n < NTW; ++n) {
-        const int off = pw * NBW + 16 * n - win;
-        float e[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = (4 * gq + (j & 3) + 16 * (j >> 2) == off + m) ? 1.f : 0.f;
-        isel[n] = O::cvt8(e);
-    }
-
-    // Applies chunk c: U, outputs, state update.
-    auto apply = [&](int c) {
-        const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
-        F8 Sb[KS][NTW];
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-            for (int n = 0; n < NTW; ++n) Sb[kk][n] = O::cvt44(S[2 * kk][n], S[2 * kk + 1][n]);
-        // U = beta V - R_k S
-        f32x4 U[4][NTW];
-#pragma unroll
-        for (int mu = 0; mu < 4; ++mu)
-#pragma unroll
-            for (int n = 0; n < NTW; ++n) U[mu][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int mu = 0; mu < 4; ++mu) {
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const T *p = s_rk + (16 * mu + m) * L::LDQ + 32 * kk + 4 * gq;
-                const F8 Af = O::ld44(p, p + 16);
-#pragma unroll
-                for (int n = 0; n < NTW; ++n) U[mu][n] = O::mma32(U[mu][n], Af, Sb[kk][n]);
-            }
-            if (R::HAS_V) {
-                const T *p = s_bv + (16 * mu + m) * L::LDV + win + 4 * gq;
-                const F8 Af = O::ld44(p, p + 16);
-#pragma unroll
-                for (int n = 0; n < NTW; ++n) U[mu][n] = O::mma32(U[mu][n], Af, isel[n]);
-            }
-        }
-        // (I + A) X = U by block forward substitution; X overwrites U.  The
-        // off-diagonal terms accumulate onto U with the same 32-deep MFMA that
-        // produced U, two 16-blocks per instruction (a zero half where a block
-        // row has an odd count): an accumulator chain must not switch MFMA
-        // opcodes, gfx950 does not order a srcC read after a different-shape
-        // MFMA that has just written it.  T_bb starts from a zero accumulator.
-        const T *td = s_td + (c & 1) * 4 * 16 * L::LDT;
-        const F4 z4 = O::cvt4(f32x4{0.f, 0.f, 0.f, 0.f});
-        auto negA = [&](int b, int a2) { return O::ld4(s_aoff + (aoff_idx(b, a2) * 16 + m) * L::LDT + 4 * gq); };
-        F4 Xb[4][NTW];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            F8 A01, A2;
-            if (b == 1) A01 = O::cat(negA(1, 0), z4);
-            if (b >= 2) A01 = O::cat(negA(b, 0), negA(b, 1));
-            if (b == 3) A2 = O::cat(negA(3, 2), z4);
-            const typename O::F4 Tf = O::ld4(td + (16 * b + m) * L::LDT + 4 * gq);
-#pragma unroll
-            for (int n = 0; n < NTW; ++n) {
-                f32x4 Y = U[b][n];
-                if (b == 1) Y = O::mma32(Y, A01, O::cat(Xb[0][n], z4));
-                if (b >= 2) Y = O::mma32(Y, A01, O::cat(Xb[0][n], Xb[1][n]));
-                if (b == 3) Y = O::mma32(Y, A2, O::cat(Xb[2][n], z4));
-                U[b][n] = O::mma16(f32x4{0.f, 0.f, 0.f, 0.f}, Tf, O::cvt4(Y));
-                Xb[b][n] = O::cvt4(U[b][n]);
-            }
-        }
-        F8 Ub[2][NTW];
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-            for (int n = 0; n < NTW; ++n) Ub[k2][n] = O::cat(Xb[2 * k2][n], Xb[2 * k2 + 1][n]);
-
-        if (R::HAS_O) {
-            // O^T = S^T Qbar^T + U^T P^T: the MFMA output then holds four
-            // consecutive columns of one token per lane (row-contiguous stores).
-            f32x4 Ot[4][NTW];
-#pragma unroll
-            for (int mu = 0; mu < 4; ++mu)
-#pragma unroll
-                for (int n = 0; n < NTW; ++n) Ot[mu][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int mu = 0; mu < 4; ++mu) {
-#pragma unroll
-                for (int kk = 0; kk < KS; ++kk) {
-                    const T *p = s_qbar + (16 * mu + m) * L::LDQ + 32 * kk + 4 * gq;
-                    const F8 Bq = O::ld44(p, p + 16);
-#pragma unroll
-                    for (int n = 0; n < NTW; ++n) Ot[mu][n] = O::mma32(Ot[mu][n], Sb[kk][n], Bq);
-                }
-#pragma unroll
-                for (int k2 = 0; k2 <= (mu >> 1); ++k2) {
-                    const T *p = s_p + (16 * mu + m) * L::LDP + 32 * k2 + 4 * gq;
-                    const F8 Bp = O::ld44(p, p + 16);
-#pragma unroll
-                    for (int n = 0; n < NTW; ++n) Ot[mu][n] = O::mma32(Ot[mu][n], Ub[k2][n], Bp);
-                }
-            }
-            const int64_t r0 = t0 + (int64_t)c * kChunk;
-#pragma unroll
-            for (int mu = 0; mu < 4; ++mu) {
-                const int64_t tok = r0 + 16 * mu + m;
-                if (tok < t1) {
-#pragma unroll
-                    for (int n = 0; n < NTW; ++n) {
-                        const int64_t idx = (tok * H + h) * DV + wcol + 16 * n + 4 * gq;
-                        f32x4 val = Ot[mu][n];
-                        if (BF) {
-                            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                            u32x2 *o = (u32x2 *)((bf16_t *)a.o + idx);
-                            if (MODE == kModeFixup) {
-                                const u32x2 w = *o;
-                                val[0] += __builtin_bit_cast(float, w[0] << 16);
-                                val[1] += __builtin_bit_cast(float, w[0] & 0xffff0000u);
-                                val[2] += __builtin_bit_cast(float, w[1] << 16);
-                                val[3] += __builtin_bit_cast(float, w[1] & 0xffff0000u);
-                            }
-                            *(bf16x4 *)o = Ops<true>::cvt4(val);
-                        } else {
-                            f32x4 *o = (f32x4 *)((float *)a.o + idx);
-                            if (MODE == kModeFixup) val += *o;
-                            *o = val;
-                        }
-                    }
-                }
-            }
-        }
-
-        // S <- Diag(gamma_C) S + Kbar^T U
-#pragma unroll
-        for (int r = 0; r < DKT; ++r) {
-            const f32x4 gm = *(const f32x4 *)(s_gam + 16 * r + 4 * gq);
-#pragma unroll
-            for (int n = 0; n < NTW; ++n) S[r][n] *= gm;
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-                const T *p = s_kbt + (16 * r + m) * L::LDK + 32 * k2 + 4 * gq;
-                const F8 Af = O::ld44(p, p + 16);
-#pragma unroll
-                for (int n = 0; n < NTW; ++n) S[r][n] = O::mma32(S[r][n], Af, Ub[k2][n]);
-            }
-        }
-    };
-
-    // The three off-diagonal blocks that need a rescale, for the chunk the
-    // producers are preparing (between the two barriers, after the block
-    // totals are complete): consumer 0 forms (3,0), consumer 1 (3,1) and
-    // consumer 2 (2,0).  The rhs rows of block a2 are referenced to its end
-    // and block B's lhs to the end of block B-1, so the product carries
-    // e^{rho_{B-1} - rho_{a2}} <= 1 per channel, computed here from the totals.
-    auto offdiag = [&]() {
-        if (pw >= 3) return;
-        const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
-        const float *s_tot = (const float *)(smem + L::o_tot);
-        const T *s_ro = (const T *)(smem + L::o_ro);
-        const T *s_lk = (const T *)(smem + L::o_lk);
-        const T *s_lq = (const T *)(smem + L::o_lq);
-        T *s_aoffw = (T *)(smem + L::o_aoff);
-        T *s_pw = (T *)(smem + L::o_p);
-        float *cf = (float *)(smem + L::o_cf) + pw * DK;
-        const int B = pw == 2 ? 2 : 3;
-        const int a2 = pw == 1 ? 1 : 0;
-        for (int ch = opaque(lane); ch < DK; ch += 64) {
-            const float u1 = s_tot[DK + ch], u2 = s_tot[2 * DK + ch];
-            cf[ch] = ex2(pw == 0 ? u1 + u2 : (pw == 1 ? u2 : u1));
-        }
-        wave_sync_lds();
-        f32x4 Ao = {0.f, 0.f, 0.f, 0.f}, P_ = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            const int c0 = 32 * kk + 8 * gq;
-            float x[8];
-            O::unpack8(O::ld8(s_ro + (16 * a2 + m) * L::LDR + c0), x);
-            const f32x4 f0 = *(const f32x4 *)(cf + c0), f1 = *(const f32x4 *)(cf + c0 + 4);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) { x[j] *= f0[j]; x[j + 4] *= f1[j]; }
-            const F8 Bf = O::cvt8(x);
-            const int lrow = (16 * (B - 2) + m) * L::LDR + c0;
-            Ao = O::mma32(Ao, O::ld8(s_lk + lrow), Bf);
-            if (R::HAS_O) P_ = O::mma32(P_, O::ld8(s_lq + lrow), Bf);
-        }
-        T *dst = s_aoffw + aoff_idx(B, a2) * 16 * L::LDT;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            dst[(4 * gq + i) * L::LDT + m] = (T)(-Ao[i]);
-            if (R::HAS_O) s_pw[(16 * B + 4 * gq + i) * L::LDP + 16 * a2 + m] = (T)P_[i];
-        }
-    };
-
-    // T_bb = (I + A_bb)^-1 of the four diagonal blocks of chunk cn, formed by
-    // consumer 3 between the barriers (the producers wrote A_bb before the
-    // first one): lane group g solves block g, lane m its column m, by forward
-    // substitution with row r+1 read while row r is reduced.
-    auto tbb = [&](int cn) {
-        if (pw != 3) return;
-        const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
-        const float *ad = (const float *)(smem + L::o_ad) + gq * 16 * L::LDAD;
-        float tc[16];
-        f32x4 nxt[4];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) nxt[q4] = *(const f32x4 *)(ad + 4 * q4);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            f32x4 cur[4];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nxt[q4];
-            if (r < 15) {
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) nxt[q4] = *(const f32x4 *)(ad + (r + 1) * L::LDAD + 4 * q4);
-            }
-            // four partial sums keep the dependent chain short
-            float sp[4] = {(r == m) ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int i = 0; i < r; ++i) sp[i & 3] = fmaf(-cur[i >> 2][i & 3], tc[i], sp[i & 3]);
-            tc[r] = (sp[0] + sp[1]) + (sp[2] + sp[3]);
-        }
-        T *td = (T *)(smem + L::o_td) + ((cn & 1) * 4 + gq) * 16 * L::LDT;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) td[r * L::LDT + m] = (T)tc[r];
-    };
-
-    // Rung stores and the zero test after chunk c.
-    auto rungs = [&](int c) {
-        const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
-        if (a.interval > 0) {
-            if (MODE == kModePrefill && a.ckpt_S) {
-                const int64_t p = (int64_t)(c + 1) * kChunk;
-                if (p <= len && (pbase + p) % a.interval == 0) {
-                    const int64_t rowc = (a.ckpt_off ? a.ckpt_off[u] : 0) +
-                                         (pbase + p) / a.interval - pbase / a.interval - 1;
-                    store_state<DKT, NTW>(a.ckpt_S + (rowc * H + h) * DK * DV, DV, wcol, gq, m, S, false);
-                }
-            }
-            if (MODE == kModePackage || MODE == kModePackageM) {
-                const int64_t p = t0 + (int64_t)(c + 1) * kChunk;   // sequence-relative (one sequence)
-                float *dst = MB ? a.ckpt_M : a.ckpt_S;
-                if (dst && p <= t1 && p % a.interval == 0) {
-                    const int64_t rowc = p / a.interval - 1;
-                    store_state<DKT, NTW>(dst + (rowc * H + h) * DK * LDST, LDST, wcol, gq, m, S, false);
-                }
-            }
-        }
-        if (R::CHECK0) {
-            const bool nz = state_nonzero();
-            if (lane == 0) s_flag[pw] = nz ? 1 : 0;
-        }
-    };
-
-    // prologue: the producers prepare chunk 0
-    __syncthreads();                                                          // BA
-    if (nchunks > 0) {
-        offdiag();
-        tbb(0);
-    }
-    __syncthreads();                                                          // BB
-    for (int c = 0; c < nchunks; ++c) {
-        if (R::CHECK0 && c > 0 && !(s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3])) {
-            // The state after chunk c-1 is exactly zero and stays zero.
-            if (MB) {
-                if (a.interval > 0 && a.ckpt_M) {
-                    const int64_t first = (t0 + (int64_t)c * kChunk) / a.interval + 1;
-                    for (int64_t mm = first; mm * a.interval <= t1; ++mm)
-                        store_state<DKT, NTW>(a.ckpt_M + ((mm - 1) * H + h) * DK * DK, DK, wcol, gq, m, S, true);
-                }
-                store_state<DKT, NTW>(a.M_out + (int64_t)(u * H + h) * DK * DK, DK, wcol, gq, m, S, true);
-            }
-            return;
-        }
-        apply(c);
-        __syncthreads();                                                      // BA
-        rungs(c);
-        if (c + 1 < nchunks) {
-            offdiag();
-            tbb(c + 1);
-        }
-        __syncthreads();                                                      // BB
-    }
-
-    if (MODE == kModePrefill) {
-        float *dst = nullptr;
-        if (a.s_out_idx) {
-            const int32_t slot = a.s_out_idx[u];
-            if (slot >= 0 && slot < a.n_slots) dst = a.S_out + ((int64_t)slot * H + h) * DK * DV;
-        } else if (a.S_out) {
-            dst = a.S_out + (int64_t)(u * H + h) * DK * DV;
-        }
-        if (dst) store_state<DKT, NTW>(dst, DV, wcol, gq, m, S, false);
-    }
-    if (MODE == kModePackage || MODE == kModePackageM) {
-        if (MB) store_state<DKT, NTW>(a.M_out + (int64_t)(u * H + h) * DK * DK, DK, wcol, gq, m, S, false);
-        else store_state<DKT, NTW>(a.S_out + (int64_t)(u * H + h) * DK * DV, DV, wcol, gq, m, S, false);
-    }
-}
-
-template <int DK, int DV, int NB, bool BF, int MODE, bool MB>
-__device__ __forceinline__ void engine_body(const EngineArgs &a, unsigned char *smem, const int u,
-                                            const int h, const int cbase, const int64_t t0,
-                                            const int64_t t1) {
-    const int nchunks = (int)((t1 - t0 + kChunk - 1) / kChunk);
-    // wave index as a scalar: the role branches below are wave-uniform
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (wv >= 4) {
-        consumer<DK, DV, NB, BF, MODE, MB>(a, smem, u, h, cbase, t0, t1, nchunks, wv - 4);
-        return;
-    }
-    if (MODE == kModeFixup) {   // mirror the consumers' test of the incoming state
-        const int *s_flag = (const int *)smem;
-        __syncthreads();
-        const bool any = s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3];
-        __syncthreads();
-        if (!any) return;
-    }
-    switch (wv) {
-        case 0: producer<DK, DV, NB, BF, MODE, MB, 0>(a, smem, h, cbase, t0, t1, nchunks); break;
-        case 1: producer<DK, DV, NB, BF, MODE, MB, 1>(a, smem, h, cbase, t0, t1, nchunks); break;
-        case 2: producer<DK, DV, NB, BF, MODE, MB, 2>(a, smem, h, cbase, t0, t1, nchunks); break;
-        default: producer<DK, DV, NB, BF, MODE, MB, 3>(a, smem, h, cbase, t0, t1, nchunks); break;
-    }
-}
-
-template <int DK, int DV, int NB, bool BF, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void chunk_engine(EngineArgs a) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int H = a.H;
-    // Block -> (item, column block).  The column blocks of one item share
-    // blockIdx mod 8, so they run on the same XCD and share its L2.
-    const int ncb = a.ncb;
-    const int bx = blockIdx.x;
-    const int cb = (bx >> 3) % ncb;
-    const int item = ((bx >> 3) / ncb) * 8 + (bx & 7);
-    if (item >= a.n_units * H) return;
-    const int pos = item / H;
-    const int h = item - pos * H;
-    const int u = a.order ? a.order[pos] : pos;
-    const int64_t t0 = a.bounds[u], t1 = a.bounds[u + 1];
-    engine_body<DK, DV, NB, BF, MODE, MODE == kModePackageM>(a, smem, u, h, cb * NB, t0, t1);
-}
-
-// Value blocks and M blocks of the segment packages in one grid, the M blocks
-// last.  M blocks stop once M is exactly zero, a few chunks in; dispatched
-// after every value block they fill the CUs that the shorter value blocks
-// leave idle while the longest ones finish.
-template <int DK, int DV, int NB, bool BF>
-__global__ __launch_bounds__(kThreads, 1) void package_engine(EngineArgs a, int grid_v) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int H = a.H;
-    const bool mblk = (int)blockIdx.x >= grid_v;
-    const int ncb = mblk ? a.ncb_m : a.ncb;
-    const int bx = mblk ? (int)blockIdx.x - grid_v : (int)blockIdx.x;
-    const int cb = (bx >> 3) % ncb;
-    const int item = ((bx >> 3) / ncb) * 8 + (bx & 7);
-    if (item >= a.n_units * H) return;
-    const int pos = item / H;
-    const int h = item - pos * H;
-    const int u = a.order ? a.order[pos] : pos;
-    const int64_t t0 = a.bounds[u], t1 = a.bounds[u + 1];
-    if (mblk)
-        engine_body<DK, DV, NB, BF, kModePackageM, true>(a, smem, u, h, cb * NB, t0, t1);
-    else
-        engine_body<DK, DV, NB, BF, kModePackage, false>(a, smem, u, h, cb * NB, t0, t1);
-}
-
-template <int DK, int DV, int NB, bool BF>
-hipError_t launch_package_vm(const EngineArgs &a, hipStream_t stream) {
-    using L = Lds<DK, NB, BF>;
-    auto kern = package_engine<DK, DV, NB, BF>;
-    hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, L::size);
-    if (e != hipSuccess) return e;
-    const int64_t items8 = ((int64_t)a.n_units * a.H + 7) / 8 * 8;
-    const int64_t grid_v = items8 * a.ncb, grid = grid_v + items8 * a.ncb_m;
-    if (grid == 0) return hipSuccess;
-    if (grid > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), L::size, stream, a, (int)grid_v);
-    return hipGetLastError();
-}
-
-template <int DK, int DV, int NB, bool BF, int MODE>
-hipError_t launch_one(const EngineArgs &a, hipStream_t stream) {
-    using L = Lds<DK, NB, BF>;
-    auto kern = chunk_engine<DK, DV, NB, BF, MODE>;
-    hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, L::size);
-    if (e != hipSuccess) return e;
-    const int ncb = a.ncb;
-    const int64_t items = (int64_t)a.n_units * a.H;
-    const int64_t grid = ((items + 7) / 8) * 8 * ncb;
-    if (grid == 0) return hipSuccess;
-    if (grid > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), L::size, stream, a);
-    return hipGetLastError();
-}
-
-template <int DK, int DV, int NB, bool BF>
-hipError_t launch_modes(int mode, const EngineArgs &a, hipStream_t s) {
-    switch (mode) {
-        case kModePrefill: return launch_one<DK, DV, NB, BF, kModePrefill>(a, s);
-        case kModePackage: return launch_one<DK, DV, NB, BF, kModePackage>(a, s);
-        case kModeFixup: return launch_one<DK, DV, NB, BF, kModeFixup>(a, s);
-        case kModePackageM: return launch_one<DK, DV, NB, BF, kModePackageM>(a, s);
-        case kModePackageVM: return launch_package_vm<DK, DV, NB, BF>(a, s);
-    }
-    return hipErrorInvalidValue;
-}
-
-}  // namespace
+hipError_t launch_engine_bf16_128x128(int mode, int dv, int nb, const EngineArgs &a, hipStream_t s);
+hipError_t launch_engine_bf16_64x128(int mode, int dv, int nb, const EngineArgs &a, hipStream_t s);
+hipError_t launch_engine_bf16_128x64(int mode, int dv, int nb, const EngineArgs &a, hipStream_t s);
+hipError_t launch_engine_bf16_64x64(int mode, int dv, int nb, const EngineArgs &a, hipStream_t s);
+hipError_t launch_engine_f32_64(int mode, int dv, int nb, const EngineArgs &a, hipStream_t s);
 
 bool engine_supported(bool bf16, int dk, int dv, int nb) {
-    if (dk != dv) return false;
-    if (bf16) return (dk == 64 && nb == 64) || (dk == 128 && (nb == 64 || nb == 128));
-    return dk == 64 && nb == 64;
+    const bool dims = (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
+    if (bf16) return dims && (nb == 64 || (nb == 128 && dv == 128));
+    // fp32 operands: the hand-off tiles of dk = 128 do not fit in LDS
+    return dims && dk == 64 && nb == 64;
 }
 
 int engine_pick_nb(bool bf16, int dk, int dv, int64_t units, int mode) {
-    (void)dv;
+    (void)dk;
     (void)mode;
-    if (!bf16 || dk == 64) return 64;
+    if (!bf16 || dv == 64) return 64;
     // Split the value columns when the grid would leave most CUs idle.
     return units >= 256 ? 128 : 64;
 }
@@ -1007,12 +30,11 @@ int engine_pick_nb(bool bf16, int dk, int dv, int64_t units, int mode) {
 hipError_t launch_engine(int mode, bool bf16, int dk, int dv, int nb, const EngineArgs &a,
                          hipStream_t s) {
     if (!engine_supported(bf16, dk, dv, nb)) return hipErrorInvalidValue;
-    if (bf16) {
-        if (dk == 64) return launch_modes<64, 64, 64, true>(mode, a, s);
-        if (nb == 128) return launch_modes<128, 128, 128, true>(mode, a, s);
-        return launch_modes<128, 128, 64, true>(mode, a, s);
-    }
-    return launch_modes<64, 64, 64, false>(mode, a, s);
+    if (!bf16) return launch_engine_f32_64(mode, dv, nb, a, s);
+    if (dk == 128) return dv == 128 ? launch_engine_bf16_128x128(mode, dv, nb, a, s)
+                                    : launch_engine_bf16_128x64(mode, dv, nb, a, s);
+    return dv == 128 ? launch_engine_bf16_64x128(mode, dv, nb, a, s)
+                     : launch_engine_bf16_64x64(mode, dv, nb, a, s);
 }
 
 }  // namespace kda

@@ -27,7 +27,7 @@ struct EngineArgs {
     int32_t n_units;
     int32_t H;
     int32_t ncb;                 // column blocks of the launch (dv / NB, or dk / NB for M)
-    int32_t ncb_m;               // PackageVM: column blocks of the M part (dk / NB)
+    int32_t ncb_m;               // PackageVM: column blocks of the M part (dk / min(NB, dk))
     const float *S_init;         // prefill: S0 (nullable); fixup: S_in
     float *S_out;                // prefill: S_final (nullable); package: D
     float *M_out;                // package: M

@@ -540,6 +540,8 @@ size_t blelloch_workspace(int dk, int dv, int H, int nseg) {
 hipError_t launch_scan_sequential(int dk, int dv, int H, int nseg, const float *M, const float *D,
                                   const float *S0, float *S_in, float *S_final, hipStream_t s) {
     if (dk == 64 && dv == 64) return scan_seq_t<64, 64>(H, nseg, M, D, S0, S_in, S_final, s);
+    if (dk == 64 && dv == 128) return scan_seq_t<64, 128>(H, nseg, M, D, S0, S_in, S_final, s);
+    if (dk == 128 && dv == 64) return scan_seq_t<128, 64>(H, nseg, M, D, S0, S_in, S_final, s);
     if (dk == 128 && dv == 128) return scan_seq_t<128, 128>(H, nseg, M, D, S0, S_in, S_final, s);
     return hipErrorInvalidValue;
 }
@@ -548,6 +550,8 @@ hipError_t launch_scan_blelloch(int dk, int dv, int H, int nseg, const float *M,
                                 const float *S0, float *S_in, float *S_final, void *ws,
                                 hipStream_t s) {
     if (dk == 64 && dv == 64) return scan_blel_t<64, 64>(H, nseg, M, D, S0, S_in, S_final, ws, s);
+    if (dk == 64 && dv == 128) return scan_blel_t<64, 128>(H, nseg, M, D, S0, S_in, S_final, ws, s);
+    if (dk == 128 && dv == 64) return scan_blel_t<128, 64>(H, nseg, M, D, S0, S_in, S_final, ws, s);
     if (dk == 128 && dv == 128) return scan_blel_t<128, 128>(H, nseg, M, D, S0, S_in, S_final, ws, s);
     return hipErrorInvalidValue;
 }
@@ -563,6 +567,10 @@ hipError_t launch_ckpt_write(int dk, int dv, int H, int64_t T, const int64_t *se
                              const float *sub_D, float *states, hipStream_t s) {
     if (dk == 64 && dv == 64)
         return ckpt_t<64, 64>(H, T, seg_start, nseg, interval, S_in, sub_M, sub_D, states, s);
+    if (dk == 64 && dv == 128)
+        return ckpt_t<64, 128>(H, T, seg_start, nseg, interval, S_in, sub_M, sub_D, states, s);
+    if (dk == 128 && dv == 64)
+        return ckpt_t<128, 64>(H, T, seg_start, nseg, interval, S_in, sub_M, sub_D, states, s);
     if (dk == 128 && dv == 128)
         return ckpt_t<128, 128>(H, T, seg_start, nseg, interval, S_in, sub_M, sub_D, states, s);
     return hipErrorInvalidValue;

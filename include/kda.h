@@ -57,10 +57,11 @@
  *    float32 (the short convolution's windows are in the I/O dtype).
  *    Arithmetic: fp32 accumulation; matrix products on MFMA with bf16
  *    operands for bf16 I/O and fp32 operands for fp32 I/O.
- *  - Supported shapes: dk == dv in {64, 128} for bf16, dk == dv == 64 for
- *    fp32; chunk == 64 (kda_decode: dk, dv in {64, 128} for both dtypes; the
- *    short convolution: see there).  Other shapes return
- *    KDA_ERR_UNSUPPORTED.
+ *  - Supported shapes: dk, dv in {64, 128} (dk == dv or not) for bf16 I/O;
+ *    dk == 64 with dv in {64, 128} for fp32 I/O (the fp32 hand-off tiles of a
+ *    128-wide key do not fit in the 160 KiB of LDS a workgroup has); chunk ==
+ *    64 (kda_decode: dk, dv in {64, 128} for both dtypes; the short
+ *    convolution: see there).  Other shapes return KDA_ERR_UNSUPPORTED.
  *  - Every pointer is a device pointer unless stated.  Tensors (q, k, v, g,
  *    o, states, M, D, workspace) must be 16-byte aligned, beta 4-byte and the
  *    int64 index arrays 8-byte aligned (KDA_ERR_ALIGN otherwise).

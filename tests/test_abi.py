@@ -98,8 +98,11 @@ def test_config_validation():
     assert prefill(cfg(chunk=32)) == K.KDA_ERR_UNSUPPORTED
     assert "chunk" in last_error()
     assert prefill(cfg(dk=96, dv=96)) == K.KDA_ERR_UNSUPPORTED
-    assert prefill(cfg(dk=128, dv=64)) == K.KDA_ERR_UNSUPPORTED
-    assert prefill(cfg(dk=128, dv=128, dtype=0)) == K.KDA_ERR_UNSUPPORTED   # fp32 I/O: d=64 only
+    assert prefill(cfg(dk=64, dv=256)) == K.KDA_ERR_UNSUPPORTED
+    assert prefill(cfg(dk=32, dv=64)) == K.KDA_ERR_UNSUPPORTED
+    # fp32 I/O: dk = 64 only (dv 64 or 128)
+    assert prefill(cfg(dk=128, dv=128, dtype=0)) == K.KDA_ERR_UNSUPPORTED
+    assert prefill(cfg(dk=128, dv=64, dtype=0)) == K.KDA_ERR_UNSUPPORTED
 
 
 def test_prefill_argument_checks():

@@ -824,3 +824,76 @@ def test_checkpoint_stream_ordering(K):
             assert_close(f"{path} rungs read on the store stream (rep {rep})", got, ref,
                          STATE_TOL["bf16"])
     say(f"fresh fraction of the copies made without the fence: {fresh_unfenced}")
+
+
+# ---------------------------------------------------------------------------
+# Head dims dk != dv
+# ---------------------------------------------------------------------------
+SHAPES = [("bf16", 64, 128), ("bf16", 128, 64), ("f32", 64, 128)]
+
+
+@pytest.mark.parametrize("dtype,dk,dv", SHAPES)
+@pytest.mark.parametrize("H", [2, 32])
+def test_prefill_dk_ne_dv(K, dtype, dk, dv, H):
+    """Chunked prefill of varlen sequences with dk != dv, rungs every 64
+    tokens; with 32 heads x 8 sequences the value columns run as 128-wide
+    blocks where dv = 128 (bf16), with 2 heads as 64-wide blocks."""
+    lens = [300, 77, 129, 64, 1, 200, 33, 130] if H == 32 else [300, 77, 129, 1]
+    say(f"prefill {dtype} dk={dk} dv={dv} H={H} lens={lens}")
+    w = make_workload("shape", lens, H, dk, dv, dtype, 5000 + dk + 3 * dv + H, s0_std=0.2)
+    o, Sf, ck = run_prefill(K, w, interval=64)
+    ro, rS, rck = oracle_full(w, interval=64)
+    assert_close("o", o, ro, OUT_TOL[dtype])
+    assert_close("S_final", Sf, rS, STATE_TOL[dtype])
+    assert_close("ckpt", ck, rck, STATE_TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype,dk,dv", SHAPES)
+@pytest.mark.parametrize("algo", [0, 1])
+@pytest.mark.parametrize("H", [2, 32])
+def test_segment_path_dk_ne_dv(K, dtype, dk, dv, algo, H):
+    """The segment path with dk != dv and long-memory gates (nonzero M in
+    every segment): M, D, o_local per segment, S_in, outputs, final state and
+    rungs.  With 32 heads x 8 segments the value blocks are 128 wide where
+    dv = 128 (bf16) while the M blocks stay dk wide."""
+    seg = [0, 256, 320, 768, 1024, 1300] if H == 2 else [0, 128, 256, 384, 512, 640, 768, 832, 960]
+    T = seg[-1]
+    say(f"segment path {dtype} dk={dk} dv={dv} H={H} algo={algo}, {len(seg) - 1} segments, long memory")
+    w = make_workload("shape-seg", [T], H, dk, dv, dtype, 5100 + dk + 3 * dv + algo + H,
+                      s0_std=0.5, gate_shift=-9.0, beta_shift=-6.0, seg_start=seg)
+    r = _segment_case(K, w, algo, interval=128)
+    q, k, v, g, b = (w.f64(x) for x in ("q", "k", "v", "g", "beta"))
+    tol_o, tol_s = OUT_TOL[dtype], STATE_TOL[dtype]
+    Ms, Ds = [], []
+    for j in range(len(seg) - 1):
+        Mr, Dr, olr = oracle.package(q, k, v, g, b, seg[j], seg[j + 1])
+        Ms.append(Mr)
+        Ds.append(Dr)
+        assert_close(f"M[{j}]", r["M"][j], Mr, tol_s)
+        assert_close(f"D[{j}]", r["D"][j], Dr, tol_s)
+        assert_close(f"o_local[{j}]", r["o_local"][seg[j]:seg[j + 1]], olr[seg[j]:seg[j + 1]], tol_o)
+    S_in_ref, _ = oracle.scan_sequential(Ms, Ds, w.S0[0].astype(np.float64))
+    assert_close("S_in", r["S_in"], S_in_ref, tol_s)
+    ro, rS, rck = oracle_full(w, interval=128)
+    assert_close("S_final", r["S_final"], rS[0], tol_s)
+    assert_close("o", r["o"], ro, tol_o)
+    assert_close("ckpt", r["ckpt"], rck, tol_s)
+
+
+@pytest.mark.parametrize("dtype,dk,dv", SHAPES)
+def test_single_sequence_split_dk_ne_dv(K, dtype, dk, dv):
+    """One 4,096-token sequence on 4 heads: kda_prefill runs it as segments
+    (queried workspace) and in one pass (minimal workspace); both against the
+    oracle, with rungs every 512 tokens."""
+    import torch
+    w = make_workload("split-shape", [4096], 4, dk, dv, dtype, 5200 + dk + dv, s0_std=0.1)
+    t = to_torch(w)
+    ref = oracle_full(w, 512)
+    for name, ws in (("split", None), ("one pass", torch.empty(256, dtype=torch.uint8, device="cuda"))):
+        say(f"prefill {name}: T=4096 H=4 {dtype} dk={dk} dv={dv}")
+        o, Sf, ck = K.kda_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"],
+                                  t["S0"], ckpt_interval=512, workspace=ws)
+        sync()
+        assert_close(f"{name} o", to_numpy_f64(o), ref[0], OUT_TOL[dtype])
+        assert_close(f"{name} S_final", to_numpy_f64(Sf), ref[1], STATE_TOL[dtype])
+        assert_close(f"{name} rungs", to_numpy_f64(ck), ref[2], STATE_TOL[dtype])
