@@ -5,8 +5,8 @@
 
 One step is one full KDA layer over the workload: for the segment-path
 workloads (default: 131,072 tokens, H=32, d=128, bf16, 16 leveled segments,
-Blelloch scan, checkpoints every 4096 tokens) package -> scan -> fix-up ->
-checkpoint write; for the chunked workloads one kda_prefill call.  Inputs are
+Blelloch scan, checkpoints every 4096 tokens) package -> scan -> fix-up
+writing the checkpoint rungs; for the chunked workloads one kda_prefill call.  Inputs are
 seeded synthetic tensors already resident in HBM when timing starts.
 
 Prints one JSON line with tokens/s per layer, the dominant kernel's roofline
@@ -273,10 +273,10 @@ def long_memory_measure(K, w, t, launches: int) -> dict:
     beta = sigmoid(N(0,1) - 6), drawn on the device from a seeded generator.
     Every M stays far from zero, so the M blocks run their whole segment,
     the scan forms every product, the fix-up runs every segment to its end
-    and the checkpoint writer multiplies every rung.  Algorithmic bytes: the
-    package pass (1540 B per token-head at d = 128 bf16) plus the M blocks'
-    reads of k, g, beta, plus the fix-up's reads of q, k, g, beta and its
-    read and write of o; states and packages as in the step."""
+    and every rung carries the propagated incoming state.  Algorithmic
+    bytes: the package pass (1540 B per token-head at d = 128 bf16) plus the
+    M blocks' reads of k, g, beta, plus the fix-up's reads of q, k, g, beta
+    and its read and write of o; states, packages and rungs as in the step."""
     import torch
     import torch.nn.functional as F
     gen = torch.Generator(device="cuda").manual_seed(46007)
@@ -296,20 +296,20 @@ def long_memory_measure(K, w, t, launches: int) -> dict:
     def step(timed):
         if timed:
             mark("a")
-        o, M, D, sM, sD = K.kda_segment_package(t["q"], t["k"], t["v"], g, beta, t["seg_start"],
-                                                ckpt_interval=interval)
+        o, M, D, _, sD = K.kda_segment_package(t["q"], t["k"], t["v"], g, beta, t["seg_start"],
+                                               ckpt_interval=interval, want_sub_M=False)
         if timed:
             mark("b")
         S_in, _ = K.kda_segment_scan(M, D, S0, algo=w.scan_algo)
         if timed:
             mark("c")
-        K.kda_output_fixup(t["q"], t["k"], g, beta, t["seg_start"], S_in, o)
+        if interval:
+            K.kda_output_fixup_ckpt(t["q"], t["k"], g, beta, t["seg_start"], S_in, o, sD,
+                                    interval=interval)
+        else:
+            K.kda_output_fixup(t["q"], t["k"], g, beta, t["seg_start"], S_in, o)
         if timed:
             mark("d")
-        if interval:
-            K.kda_checkpoint_write(t["seg_start"], S_in, sM, sD, T=T, interval=interval)
-        if timed:
-            mark("e")
         return M
 
     M = step(False)
@@ -324,20 +324,20 @@ def long_memory_measure(K, w, t, launches: int) -> dict:
 
     def avg(a, b):
         return float(np.mean([x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]))
-    ms = avg("a", "e")
+    ms = avg("a", "d")
     nseg = len(w.seg_start) - 1
     rows = T // interval if interval else 0
     io = 2 if w.dtype == "bf16" else 4
     per_tok = (bytes_per_token_head(dk, dv, io) + (io * dk + 4 * dk + 4)
                + (2 * io * dk + 4 * dk + 4 + 2 * io * dv))
-    alg = T * H * per_tok + 4 * H * (dk * dv + dk * dk) * (nseg + rows)
+    alg = T * H * per_tok + 4 * H * (dk * dv + dk * dk) * nseg + 2 * 4 * H * dk * dv * rows
     gbs = alg / (ms * 1e-3) / 1e9
     return {"workload": f"{w.name} with long-memory gates (log alpha ~ -1.2e-4 per token)",
             "min_frobenius_norm_M": round(m_norm_min, 4),
             "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
             "steps_timed": launches,
             "breakdown_ms": {"package": round(avg("a", "b"), 4), "scan": round(avg("b", "c"), 4),
-                             "fixup": round(avg("c", "d"), 4), "ckpt": round(avg("d", "e"), 4)},
+                             "fixup_and_rungs": round(avg("c", "d"), 4)},
             "alg_bytes_per_step": int(alg),
             "hbm": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gbs / HBM_PEAK_GBS, 4)}}
@@ -457,31 +457,32 @@ def main():
         def step(timed):
             if timed:
                 mark("pkg0")
-            o, M, D, sM, sD = K.kda_segment_package(t["q"], t["k"], t["v"], t["g"], t["beta"],
-                                                    t["seg_start"], ckpt_interval=interval)
+            o, M, D, _, sD = K.kda_segment_package(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                                   t["seg_start"], ckpt_interval=interval,
+                                                   want_sub_M=False)
             if timed:
                 mark("pkg1")
             S_in, S_fin = K.kda_segment_scan(M, D, S0, algo=w.scan_algo)
             if timed:
                 mark("scan1")
-            K.kda_output_fixup(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o)
+            if interval:   # the fix-up writes the checkpoint rungs in the same launch
+                K.kda_output_fixup_ckpt(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in,
+                                        o, sD, interval=interval)
+            else:
+                K.kda_output_fixup(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o)
             if timed:
                 mark("fix1")
-            if interval:
-                K.kda_checkpoint_write(t["seg_start"], S_in, sM, sD, T=T, interval=interval)
-            if timed:
-                mark("ck1")
             return o
         main_kernel = "package_engine (value blocks, then M blocks, one launch)"
         rows = T // interval if interval else 0
         nseg = len(w.seg_start) - 1
-        # D and rung sub_D, M and rung sub_M written by the launch
-        extra_bytes = 4 * H * dk * dv * (nseg + rows) + 4 * H * dk * dk * (nseg + rows)
+        # D and rung sub_D, and M, written by the launch
+        extra_bytes = 4 * H * dk * dv * (nseg + rows) + 4 * H * dk * dk * nseg
 
         def dominant():
             # the launch the step runs first: kda_segment_package with M
             K.kda_segment_package(t["q"], t["k"], t["v"], t["g"], t["beta"], t["seg_start"],
-                                  ckpt_interval=interval)
+                                  ckpt_interval=interval, want_sub_M=False)
 
         def value_blocks():
             # the value blocks alone (kda_segment_package without M)
@@ -544,8 +545,8 @@ def main():
     kernel_ms = avg_ms("dom0", "dom1")
     breakdown = {"package" if segmented else "prefill": round(avg_ms("pkg0", "pkg1"), 4)}
     if segmented:
-        breakdown.update(scan=round(avg_ms("pkg1", "scan1"), 4), fixup=round(avg_ms("scan1", "fix1"), 4),
-                         ckpt=round(avg_ms("fix1", "ck1"), 4))
+        breakdown.update(scan=round(avg_ms("pkg1", "scan1"), 4),
+                         fixup_and_rungs=round(avg_ms("scan1", "fix1"), 4))
     alg_bytes = T * H * bytes_per_token_head(dk, dv, io_bytes) + extra_bytes
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
     flops = T * H * chunk_flops_per_token_head(64, dk, dv)

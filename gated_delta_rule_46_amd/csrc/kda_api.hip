@@ -112,8 +112,8 @@ constexpr int64_t kMinSplit = 512;   // shortest segment worth a workgroup of it
 struct SplitPlan {
     int nseg = 0;
     int64_t L = 0, rows = 0;
-    size_t off_M = 0, off_D = 0, off_Sin = 0, off_Sfin = 0, off_subM = 0, off_subD = 0,
-           off_bounds = 0, bytes = 0;
+    size_t off_M = 0, off_D = 0, off_Sin = 0, off_Sfin = 0, off_subD = 0, off_bounds = 0,
+           bytes = 0;
 };
 
 bool plan_split(const kda_config *cfg, int64_t T, int32_t N, const kda_ckpt *ckpt, SplitPlan *p) {
@@ -142,7 +142,6 @@ bool plan_split(const kda_config *cfg, int64_t T, int32_t N, const kda_ckpt *ckp
     p->off_D = take(dd * p->nseg);
     p->off_Sin = take(dd * p->nseg);
     p->off_Sfin = take(dd);
-    p->off_subM = take(mm * (size_t)p->rows);
     p->off_subD = take(dd * (size_t)p->rows);
     p->off_bounds = take(sizeof(int64_t) * (size_t)(p->nseg + 1));
     p->bytes = at;
@@ -156,7 +155,6 @@ int prefill_split(const SplitPlan &p, const kda_config *cfg, const void *q, cons
     float *M = (float *)(w + p.off_M), *D = (float *)(w + p.off_D);
     float *S_in = (float *)(w + p.off_Sin);
     float *S_fin = S_final ? S_final : (float *)(w + p.off_Sfin);
-    float *sub_M = p.rows ? (float *)(w + p.off_subM) : nullptr;
     float *sub_D = p.rows ? (float *)(w + p.off_subD) : nullptr;
     int64_t *bounds = (int64_t *)(w + p.off_bounds);
     const bool bf = cfg->io_dtype == KDA_DTYPE_BF16;
@@ -169,7 +167,7 @@ int prefill_split(const SplitPlan &p, const kda_config *cfg, const void *q, cons
     a.bounds = bounds; a.order = nullptr; a.n_units = p.nseg; a.H = H;
     a.S_init = nullptr; a.S_out = D; a.M_out = M;
     a.interval = p.rows ? ckpt->interval : 0;
-    a.ckpt_off = nullptr; a.ckpt_S = sub_D; a.ckpt_M = sub_M;
+    a.ckpt_off = nullptr; a.ckpt_S = sub_D; a.ckpt_M = nullptr;   // rungs come from the fix-up
     a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;
     a.ncb = dv / nb;
     a.ncb_m = dk / std::min(nb, dk);   // M has dk columns
@@ -181,16 +179,13 @@ int prefill_split(const SplitPlan &p, const kda_config *cfg, const void *q, cons
     f.q = q; f.k = k; f.v = nullptr; f.g = g; f.beta = beta; f.o = o;
     f.bounds = bounds; f.order = nullptr; f.n_units = p.nseg; f.H = H;
     f.S_init = S_in; f.scale = cfg->scale; f.l2norm = cfg->qk_l2norm;
+    if (p.rows) {   // the fix-up writes the rungs: its propagated state plus sub_D
+        f.interval = ckpt->interval; f.ckpt_S = ckpt->states; f.ckpt_in = sub_D;
+    }
     const int nbf = kda::engine_pick_nb(bf, dk, dv, (int64_t)p.nseg * H, kda::kModeFixup);
     f.ncb = dv / nbf;
-    if ((e = kda::launch_engine(kda::kModeFixup, bf, dk, dv, nbf, f, s)) != hipSuccess)
-        return launched(e, "prefill split (fix-up)");
-    if (p.rows) {
-        e = kda::launch_ckpt_write(dk, dv, H, T, bounds, p.nseg, ckpt->interval, S_in, sub_M,
-                                   sub_D, ckpt->states, s);
-        return launched(e, "prefill split (checkpoints)");
-    }
-    return ok();
+    return launched(kda::launch_engine(kda::kModeFixup, bf, dk, dv, nbf, f, s),
+                    "prefill split (fix-up)");
 }
 
 // Scratch of kda_prefill_noalloc: one fixed array per device, held for the
@@ -384,7 +379,7 @@ int kda_segment_package(const kda_config *cfg, const void *q, const void *k, con
     const bool subs = ckpt && (sub_M || sub_D);
     if (subs) {
         KDA_TRY(check_ckpt_interval(ckpt->interval));
-        KDA_TRY(check_tensor(sub_M, "sub_M", M != nullptr));
+        KDA_TRY(check_tensor(sub_M, "sub_M", false));
         KDA_TRY(check_tensor(sub_D, "sub_D", true));
         if (sub_M && !M) return fail(KDA_ERR_ARG, "sub_M needs M (M is NULL)");
     }
@@ -439,9 +434,22 @@ int kda_segment_scan(const kda_config *cfg, int32_t nseg, const float *M, const 
 int kda_output_fixup(const kda_config *cfg, const void *q, const void *k, const float *g,
                      const float *beta, int64_t T, const int64_t *seg_start, int32_t nseg,
                      const float *S_in, void *o, void *ws, size_t ws_bytes, void *stream) {
+    return kda_output_fixup_ckpt(cfg, q, k, g, beta, T, seg_start, nseg, S_in, o, nullptr,
+                                 nullptr, ws, ws_bytes, stream);
+}
+
+int kda_output_fixup_ckpt(const kda_config *cfg, const void *q, const void *k, const float *g,
+                          const float *beta, int64_t T, const int64_t *seg_start, int32_t nseg,
+                          const float *S_in, void *o, const kda_ckpt *ckpt, const float *sub_D,
+                          void *ws, size_t ws_bytes, void *stream) {
     (void)ws;
     (void)ws_bytes;
     KDA_TRY(check_config(cfg));
+    if (ckpt) {
+        KDA_TRY(check_ckpt_interval(ckpt->interval));
+        KDA_TRY(check_tensor(ckpt->states, "ckpt->states", true));
+        KDA_TRY(check_tensor(sub_D, "sub_D", true));
+    }
     if (T <= 0) return fail(KDA_ERR_ARG, "T must be positive (got %lld)", (long long)T);
     if (nseg <= 0) return fail(KDA_ERR_ARG, "nseg must be positive (got %d)", nseg);
     KDA_TRY(check_tensor(q, "q", true));
@@ -460,7 +468,9 @@ int kda_output_fixup(const kda_config *cfg, const void *q, const void *k, const 
     a.bounds = seg_start; a.order = nullptr; a.n_units = nseg; a.H = cfg->num_heads;
     a.ncb = cfg->dv / nb;
     a.S_init = S_in; a.S_out = nullptr; a.M_out = nullptr;
-    a.interval = 0; a.ckpt_off = nullptr; a.ckpt_S = nullptr; a.ckpt_M = nullptr;
+    a.interval = ckpt ? ckpt->interval : 0; a.ckpt_off = nullptr;
+    a.ckpt_S = ckpt ? ckpt->states : nullptr; a.ckpt_in = ckpt ? sub_D : nullptr;
+    a.ckpt_M = nullptr;
     a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;
     return launched(kda::launch_engine(kda::kModeFixup, bf, cfg->dk, cfg->dv, nb, a, s), "fixup");
 }

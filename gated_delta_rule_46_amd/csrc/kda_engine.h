@@ -155,6 +155,57 @@ __device__ __forceinline__ void store_state(float *dst, int ld, int col0, int gq
                 dst[(int64_t)(16 * r + 4 * gq + i) * ld + col0 + 16 * n + m] = zero ? 0.f : S[r][n][i];
 }
 
+// dst = S + add at the state positions this lane owns (add laid out like
+// dst).  Two row tiles at a time, every load of a batch before its stores:
+// dst and add may alias as far as the compiler knows, so interleaved
+// accesses would each wait a full memory round trip.
+template <int DKT, int NTW>
+__device__ __forceinline__ void store_state_add(float *dst, const float *add, int ld, int col0,
+                                                int gq, int m, const f32x4 (&S)[DKT][NTW]) {
+    static_assert(DKT % 2 == 0, "row tiles in pairs");
+#pragma unroll
+    for (int r0 = 0; r0 < DKT; r0 += 2) {
+        float x[2][NTW][4];
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    x[r][n][i] = add[(int64_t)(16 * (r0 + r) + 4 * gq + i) * ld + col0 + 16 * n + m];
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    dst[(int64_t)(16 * (r0 + r) + 4 * gq + i) * ld + col0 + 16 * n + m] =
+                        S[r0 + r][n][i] + x[r][n][i];
+    }
+}
+
+// dst = src over rows [0, DK) and columns [col0, col0 + NB) of a [DK x ld]
+// state, by the 256 threads of the consumer waves (ct = 0..255), 16 bytes per
+// access, every load before any store.
+template <int DK, int NB>
+__device__ __forceinline__ void copy_state_block(float *dst, const float *src, int ld, int col0,
+                                                 int ct) {
+    constexpr int Q = NB / 4;                  // float4 per row
+    constexpr int PER = DK * Q / 256;
+    static_assert(PER * 256 == DK * Q, "block shape");
+    f32x4 t[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int idx = ct + 256 * i, row = idx / Q, c4 = idx - row * Q;
+        t[i] = *(const f32x4 *)(src + (int64_t)row * ld + col0 + 4 * c4);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int idx = ct + 256 * i, row = idx / Q, c4 = idx - row * Q;
+        *(f32x4 *)(dst + (int64_t)row * ld + col0 + 4 * c4) = t[i];
+    }
+}
+
 template <int MODE, bool MB> struct Roles {
     static constexpr bool HAS_V = (MODE != kModeFixup) && !MB;   // beta V enters U
     static constexpr bool HAS_O = !MB;                           // outputs are produced
@@ -574,6 +625,17 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
                     nz |= (__builtin_bit_cast(uint32_t, S[r][n][i]) & 0x7fffffffu) != 0u;
         return __ballot(nz) != 0ull;
     };
+    // Fix-up with rungs: once the propagated state is exactly zero, every
+    // later rung p of the segment is its own part sub_D[p]; copied here for
+    // the rungs after position `from`.
+    auto copy_rungs_after = [&](int64_t from) {
+        if (MODE != kModeFixup || !a.ckpt_S || a.interval <= 0) return;
+        for (int64_t p = (from / a.interval + 1) * a.interval; p <= t1; p += a.interval) {
+            const int64_t off = ((p / a.interval - 1) * H + h) * DK * DV;
+            copy_state_block<DK, NB>(a.ckpt_S + off, a.ckpt_in + off, DV, cbase,
+                                     (int)threadIdx.x - 256);
+        }
+    };
     if (MODE == kModeFixup) {
         // An all-zero incoming state leaves o_local final: skip the unit.
         const bool nz = state_nonzero();
@@ -581,7 +643,10 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
         __syncthreads();
         const bool any = s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3];
         __syncthreads();
-        if (!any) return;
+        if (!any) {
+            copy_rungs_after(t0);
+            return;
+        }
     }
 
     // beta V enters U through an MFMA with an identity selector: the A operand
@@ -821,6 +886,15 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
                     store_state<DKT, NTW>(a.ckpt_S + (rowc * H + h) * DK * DV, DV, wcol, gq, m, S, false);
                 }
             }
+            if (MODE == kModeFixup && a.ckpt_S) {
+                // rung p of this segment: the propagated incoming state plus the
+                // segment's own part (sub_D), i.e. Pi_p S_in + S0_p
+                const int64_t p = t0 + (int64_t)(c + 1) * kChunk;   // sequence-relative
+                if (p <= t1 && p % a.interval == 0) {
+                    const int64_t off = ((p / a.interval - 1) * H + h) * DK * DV;
+                    store_state_add<DKT, NTW>(a.ckpt_S + off, a.ckpt_in + off, DV, wcol, gq, m, S);
+                }
+            }
             if (MODE == kModePackage || MODE == kModePackageM) {
                 const int64_t p = t0 + (int64_t)(c + 1) * kChunk;   // sequence-relative (one sequence)
                 float *dst = MB ? a.ckpt_M : a.ckpt_S;
@@ -854,6 +928,7 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
                 }
                 store_state<DKT, NTW>(a.M_out + (int64_t)(u * H + h) * DK * DK, DK, wcol, gq, m, S, true);
             }
+            copy_rungs_after(t0 + (int64_t)c * kChunk);
             return;
         }
         apply(c);

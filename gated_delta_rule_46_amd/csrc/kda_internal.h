@@ -33,7 +33,9 @@ struct EngineArgs {
     float *M_out;                // package: M
     int32_t interval;            // checkpoint interval in tokens, 0 = none
     const int64_t *ckpt_off;     // prefill: first rung row per sequence (nullable)
-    float *ckpt_S;               // prefill: checkpoint states; package: sub_D (nullable)
+    float *ckpt_S;               // prefill: checkpoint states; package: sub_D; fixup: rung
+                                 //   states written beside the outputs (nullable)
+    const float *ckpt_in;        // fixup with rungs: sub_D of every rung (read)
     float *ckpt_M;               // package: sub_M (nullable)
     float scale;
     int32_t l2norm;

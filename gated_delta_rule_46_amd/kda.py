@@ -22,6 +22,7 @@ CHUNK = 64
 EXPORTS = ("kda_prefill_workspace", "kda_prefill", "kda_prefill_noalloc", "kda_prefill_resume",
            "kda_segment_package",
            "kda_segment_scan_workspace", "kda_segment_scan", "kda_output_fixup",
+           "kda_output_fixup_ckpt",
            "kda_checkpoint_write", "kda_decode", "kda_short_conv", "kda_conv_halo",
            "kda_status_string", "kda_last_error", "kda_version")
 KDA_ACT_NONE, KDA_ACT_SILU = 0, 1
@@ -74,6 +75,8 @@ def _load():
         "kda_segment_scan_workspace": (S, [cfgp, I32, I32]),
         "kda_segment_scan": (ctypes.c_int, [cfgp, I32, P, P, P, P, P, I32, P, S, P]),
         "kda_output_fixup": (ctypes.c_int, [cfgp, P, P, P, P, I64, P, I32, P, P, P, S, P]),
+        "kda_output_fixup_ckpt": (ctypes.c_int, [cfgp, P, P, P, P, I64, P, I32, P, P, ckp, P, P,
+                                                 S, P]),
         "kda_checkpoint_write": (ctypes.c_int, [cfgp, ckp, I64, P, I32, P, P, P, P]),
         "kda_decode": (ctypes.c_int, [cfgp, I32, P, P, P, P, P, I32, poolp, P, P]),
         "kda_short_conv": (ctypes.c_int, [I32, I32, I32, I32, P, I64, P, I32, P, P, convp, P, P]),
@@ -212,7 +215,7 @@ def kda_prefill(q, k, v, g, beta, cu_seqlens, S0=None, *, want_final=True, ckpt_
         if ckpt_interval and N == 1 and ckpt_offsets is None and wsb > 256:
             # room for the rung sub-packages of the segmented path
             rows = T // ckpt_interval
-            wsb += _round256(rows * H * dk * dk * 4) + _round256(rows * H * dk * dv * 4)
+            wsb += _round256(rows * H * dk * dv * 4)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     st = LIB.kda_prefill(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(cu_seqlens),
                          N, T, _p(S0), _p(Sf), _p(o), ckp, _p(ws), wsb, _stream(stream))
@@ -307,9 +310,10 @@ def kda_prefill_resume(q, k, v, g, beta, cu_seqlens, pool, read_idx, write_idx, 
 
 
 def kda_segment_package(q, k, v, g, beta, seg_start, *, ckpt_interval=0, scale=1.0,
-                        qk_l2norm=True, want_M=True, stream=None):
+                        qk_l2norm=True, want_M=True, want_sub_M=True, stream=None):
     """Per-segment packages.  Returns (o_local, M, D, sub_M, sub_D); M and
-    sub_M are None when want_M is False (the M launch is then skipped)."""
+    sub_M are None when want_M is False (the M launch is then skipped), sub_M
+    also when want_sub_M is False (rungs then from kda_output_fixup_ckpt)."""
     T, H, dk, dv, dev = _inputs(q, k, v, g, beta)
     nseg = seg_start.numel() - 1
     _need(seg_start, "seg_start", (nseg + 1,), torch.int64, dev)
@@ -321,14 +325,14 @@ def kda_segment_package(q, k, v, g, beta, seg_start, *, ckpt_interval=0, scale=1
     ckp = None
     if ckpt_interval:
         rows = T // ckpt_interval
-        if want_M:
+        if want_M and want_sub_M:
             sub_M = torch.empty((rows, H, dk, dk), dtype=torch.float32, device=dev)
         sub_D = torch.empty((rows, H, dk, dv), dtype=torch.float32, device=dev)
         if rows:
             ckp = ctypes.pointer(kda_ckpt(int(ckpt_interval), None, None))
     st = LIB.kda_segment_package(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(g), _p(beta), T,
                                  _p(seg_start), nseg, _p(o_local), _p(M), _p(D), ckp,
-                                 _p(sub_M) if (ckp and want_M) else None,
+                                 _p(sub_M) if (ckp and sub_M is not None) else None,
                                  _p(sub_D) if ckp else None,
                                  None, 0, _stream(stream))
     _check(st, "kda_segment_package")
@@ -375,6 +379,35 @@ def kda_output_fixup(q, k, g, beta, seg_start, S_in, o, *, scale=1.0, qk_l2norm=
     return o
 
 
+def kda_output_fixup_ckpt(q, k, g, beta, seg_start, S_in, o, sub_D, *, interval, out=None,
+                          scale=1.0, qk_l2norm=True, stream=None):
+    """The fix-up of o (in place) and the checkpoint rungs [T // interval, H,
+    dk, dv] in one launch; returns the rung states (into `out` when given)."""
+    T, H, dk = q.shape
+    dev = q.device
+    dv = o.shape[2]
+    nseg = seg_start.numel() - 1
+    rows = T // interval
+    _need(k, "k", (T, H, dk), q.dtype, dev)
+    _need(g, "g", (T, H, dk), torch.float32, dev)
+    _need(beta, "beta", (T, H), torch.float32, dev)
+    _need(o, "o", (T, H, dv), q.dtype, dev)
+    _need(seg_start, "seg_start", (nseg + 1,), torch.int64, dev)
+    _need(S_in, "S_in", (nseg, H, dk, dv), torch.float32, dev)
+    _need(sub_D, "sub_D", (rows, H, dk, dv), torch.float32, dev)
+    states = out if out is not None else torch.empty((rows, H, dk, dv), dtype=torch.float32,
+                                                     device=dev)
+    _need(states, "out", (rows, H, dk, dv), torch.float32, dev)
+    cfg = make_config(H, dk, dv, q.dtype, scale, qk_l2norm)
+    ck = kda_ckpt(int(interval), None, ctypes.c_void_p(states.data_ptr()))
+    st = LIB.kda_output_fixup_ckpt(ctypes.byref(cfg), _p(q), _p(k), _p(g), _p(beta), T,
+                                   _p(seg_start), nseg, _p(S_in), _p(o),
+                                   ctypes.byref(ck) if rows else None, _p(sub_D) if rows else None,
+                                   None, 0, _stream(stream))
+    _check(st, "kda_output_fixup_ckpt")
+    return states
+
+
 def kda_checkpoint_write(seg_start, S_in, sub_M, sub_D, *, T, interval, dtype=torch.bfloat16,
                          out=None, stream=None):
     """Segment-path checkpoint states [T // interval, H, dk, dv] (into `out`
@@ -400,19 +433,20 @@ def kda_checkpoint_write(seg_start, S_in, sub_M, sub_D, *, T, interval, dtype=to
 
 def kda_segment_prefill(q, k, v, g, beta, seg_start, S0=None, *, algo=KDA_SCAN_BLELLOCH,
                         ckpt_interval=0, scale=1.0, qk_l2norm=True, stream=None):
-    """The whole segment path on one stream: package -> scan -> fix-up ->
-    checkpoint write.  Returns (o, S_final, checkpoint states or None)."""
-    o, M, D, sub_M, sub_D = kda_segment_package(q, k, v, g, beta, seg_start,
-                                                ckpt_interval=ckpt_interval, scale=scale,
-                                                qk_l2norm=qk_l2norm, stream=stream)
+    """The whole segment path on one stream: package -> scan -> fix-up with
+    the checkpoint rungs.  Returns (o, S_final, checkpoint states or None)."""
+    o, M, D, _, sub_D = kda_segment_package(q, k, v, g, beta, seg_start,
+                                            ckpt_interval=ckpt_interval, scale=scale,
+                                            qk_l2norm=qk_l2norm, want_sub_M=False, stream=stream)
     S_in, S_final = kda_segment_scan(M, D, S0, algo=algo, stream=stream)
+    if ckpt_interval:
+        ck = kda_output_fixup_ckpt(q, k, g, beta, seg_start, S_in, o, sub_D,
+                                   interval=ckpt_interval, scale=scale, qk_l2norm=qk_l2norm,
+                                   stream=stream)
+        return o, S_final, ck
     kda_output_fixup(q, k, g, beta, seg_start, S_in, o, scale=scale, qk_l2norm=qk_l2norm,
                      stream=stream)
-    ck = None
-    if ckpt_interval:
-        ck = kda_checkpoint_write(seg_start, S_in, sub_M, sub_D, T=q.shape[0],
-                                  interval=ckpt_interval, dtype=q.dtype, stream=stream)
-    return o, S_final, ck
+    return o, S_final, None
 
 
 def kda_decode(q, k, v, g, beta, pool, read_idx, write_idx, *, gate_logits=False, scale=1.0,

@@ -174,8 +174,8 @@ size_t kda_prefill_workspace(const kda_config *cfg, int64_t T, int32_t N);
  * holds its buffers; otherwise in one pass.  kda_prefill_workspace returns
  * that size for calls without checkpoints.  With checkpoints (and
  * ckpt->offsets NULL) the segmented path also needs
- * round256(T/interval * H * dk * dk * 4) + round256(T/interval * H * dk * dv * 4)
- * bytes more for the rung sub-packages.  Both paths give the same result up
+ * round256(T/interval * H * dk * dv * 4) bytes more for the rungs' own
+ * parts (the fix-up writes the rungs).  Both paths give the same result up
  * to fp32 rounding.
  */
 int kda_prefill(const kda_config *cfg, const void *q, const void *k, const void *v,
@@ -244,7 +244,8 @@ int kda_prefill_resume(const kda_config *cfg, const void *q, const void *k, cons
  *   sub-package (Pi_p, S0_p) of every rung p inside (seg_start[j],
  *   seg_start[j+1]]: the map from S_in^j to the state at p, at rung row
  *   p/interval - 1 of sub_M [rows,H,dk,dk] and sub_D [rows,H,dk,dv]
- *   (sub_M may be NULL only when M is NULL).
+ *   (sub_M = NULL skips Pi_p: kda_output_fixup_ckpt needs only sub_D;
+ *   sub_M needs M).
  * One kernel launch: the value blocks (o_local, D, sub_D) and, with M, the M
  * blocks after them in the same grid.
  * No workspace is needed (ws may be NULL).
@@ -280,6 +281,25 @@ int kda_segment_scan(const kda_config *cfg, int32_t nseg, const float *M, const 
 int kda_output_fixup(const kda_config *cfg, const void *q, const void *k, const float *g,
                      const float *beta, int64_t T, const int64_t *seg_start, int32_t nseg,
                      const float *S_in, void *o, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The output fix-up and the segment path's checkpoint rungs in one launch
+ * (the fused form of kda_output_fixup followed by kda_checkpoint_write, for
+ * callers that skip the rung sub-packages sub_M): while the fix-up
+ * propagates S_in^j through segment j it has Pi_p S_in^j at every rung p
+ * inside (seg_start[j], seg_start[j+1]], and writes
+ *     ckpt->states[p/interval - 1] = Pi_p S_in^j + sub_D[p/interval - 1];
+ * once the propagated state is exactly zero the remaining rungs of the
+ * segment are copies of their sub_D rows.  ckpt->offsets is unused (one
+ * sequence, rows from 0); sub_D [rows, H, dk, dv] as written by
+ * kda_segment_package.  ckpt = NULL is kda_output_fixup.  The rung states
+ * equal kda_checkpoint_write's up to fp32 rounding (the same map applied by
+ * the chunk recurrence instead of one product with sub_M).
+ */
+int kda_output_fixup_ckpt(const kda_config *cfg, const void *q, const void *k, const float *g,
+                          const float *beta, int64_t T, const int64_t *seg_start, int32_t nseg,
+                          const float *S_in, void *o, const kda_ckpt *ckpt, const float *sub_D,
+                          void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Checkpoint states of the segment path: for every rung p (see kda_ckpt;

@@ -318,3 +318,20 @@ def test_noalloc_scratch_size_matches_header():
     m = re.search(r"#define\s+KDA_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", text)
     assert m, "KDA_NOALLOC_SCRATCH_BYTES not found"
     assert int(m.group(1)) << int(m.group(2)) == K.NOALLOC_SCRATCH_BYTES
+
+
+def test_fixup_ckpt_validates():
+    c = cfg()
+
+    def call(ckpt=None, sub_D=FAKE, S_in=FAKE, nseg=2):
+        return K.LIB.kda_output_fixup_ckpt(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 256, FAKE, nseg,
+                                           S_in, FAKE, ckpt, sub_D, None, 0, None)
+    bad = K.kda_ckpt(100, None, FAKE)
+    assert call(ckpt=ctypes.byref(bad)) == K.KDA_ERR_ARG
+    no_states = K.kda_ckpt(128, None, None)
+    assert call(ckpt=ctypes.byref(no_states)) == K.KDA_ERR_ARG
+    ok = K.kda_ckpt(128, None, FAKE)
+    assert call(ckpt=ctypes.byref(ok), sub_D=None) == K.KDA_ERR_ARG
+    assert call(ckpt=ctypes.byref(ok), sub_D=MISALIGNED) == K.KDA_ERR_ALIGN
+    assert call(S_in=None) == K.KDA_ERR_ARG
+    assert call(nseg=0) == K.KDA_ERR_ARG

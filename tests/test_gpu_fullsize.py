@@ -6,7 +6,9 @@ bench.py times, compared unit by unit with the fp64 oracle.
   processing (queried workspace).
 * The 16,384- and 131,072-token segment workloads: every head, per head over
   the whole sequence, per (segment, head) over each segment's first rows, the
-  incoming states S_in, the rungs, and the output fix-up on its own: the
+  incoming states S_in, the rungs (written by the fix-up launch, as bench.py
+  runs it, and by kda_checkpoint_write from the sub-packages), and the output
+  fix-up on its own: the
   library's kda_output_fixup run from the oracle's S_in^j on zero outputs
   against the oracle's correction (the segment run from S_in^j with zero
   values).
@@ -89,22 +91,32 @@ def test_config1_all_heads(K, w1, path):
 # segment workloads
 # ---------------------------------------------------------------------------
 def run_segment_path(K, w, t, algo, interval):
-    """package -> scan -> fix-up -> rungs, as one step of bench.py.  Returns
-    device tensors (o, o_local, M, D, S_in, S_final, rungs or None)."""
+    """package -> scan -> fix-up writing the rungs, as one step of bench.py;
+    with rungs also kda_checkpoint_write from the sub-packages (a second
+    package call with sub_M).  Returns device tensors (o, o_local, M, D, S_in,
+    S_final, rungs or None, rungs of kda_checkpoint_write or None)."""
     S0 = None if t["S0"] is None else t["S0"][0].contiguous()
-    ol, M, D, sM, sD = K.kda_segment_package(t["q"], t["k"], t["v"], t["g"], t["beta"],
-                                             t["seg_start"], ckpt_interval=interval,
-                                             scale=w.scale, qk_l2norm=bool(w.qk_l2norm))
+    ol, M, D, _, sD = K.kda_segment_package(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                            t["seg_start"], ckpt_interval=interval,
+                                            scale=w.scale, qk_l2norm=bool(w.qk_l2norm),
+                                            want_sub_M=False)
     S_in, S_fin = K.kda_segment_scan(M, D, S0, algo=algo)
     o = ol.clone()
-    K.kda_output_fixup(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o,
-                       scale=w.scale, qk_l2norm=bool(w.qk_l2norm))
-    ck = None
+    ck = ck2 = None
     if interval:
-        ck = K.kda_checkpoint_write(t["seg_start"], S_in, sM, sD, T=w.T, interval=interval,
-                                    dtype=t["q"].dtype)
+        ck = K.kda_output_fixup_ckpt(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o,
+                                     sD, interval=interval, scale=w.scale,
+                                     qk_l2norm=bool(w.qk_l2norm))
+        _, _, _, sM2, sD2 = K.kda_segment_package(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                                  t["seg_start"], ckpt_interval=interval,
+                                                  scale=w.scale, qk_l2norm=bool(w.qk_l2norm))
+        ck2 = K.kda_checkpoint_write(t["seg_start"], S_in, sM2, sD2, T=w.T, interval=interval,
+                                     dtype=t["q"].dtype)
+    else:
+        K.kda_output_fixup(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o,
+                           scale=w.scale, qk_l2norm=bool(w.qk_l2norm))
     sync()
-    return dict(o=o, o_local=ol, M=M, D=D, S_in=S_in, S_final=S_fin, ckpt=ck)
+    return dict(o=o, o_local=ol, M=M, D=D, S_in=S_in, S_final=S_fin, ckpt=ck, ckpt2=ck2)
 
 
 def segment_parity(K, w, heads, algo, interval, check_packages=False):
@@ -121,6 +133,8 @@ def segment_parity(K, w, heads, algo, interval, check_packages=False):
     c = SegmentChecks(hs)
     pk = {n: UnitErrors(f"{n} per (segment, head)") for n in ("M", "D", "o_local")}
     rungs_got = None if r["ckpt"] is None else to_numpy_f64(r["ckpt"][:, ht])
+    rungs2 = UnitErrors("rungs of kda_checkpoint_write per (row, head)")
+    rungs2_got = None if r["ckpt2"] is None else to_numpy_f64(r["ckpt2"][:, ht])
     S_in_got = to_numpy_f64(r["S_in"][:, ht])
     nseg = len(w.seg_start) - 1
     S_in_ref = np.zeros((nseg, w.H, w.dk, w.dv), dtype=np.float32)
@@ -131,6 +145,10 @@ def segment_parity(K, w, heads, algo, interval, check_packages=False):
         o_got = to_numpy_f64(r["o"][a:b][:, ht])
         c.add(s, o=o_got, S_in=S_in_got[j],
               rungs=None if rungs_got is None else {row: rungs_got[row] for row, _ in s["rungs"]})
+        if rungs2_got is not None:
+            for row, ref in s["rungs"]:
+                for i, h in enumerate(hs):
+                    rungs2.add((row, h), rungs2_got[row][i], ref[i])
         S_in_ref[j][hs] = s["S_in"].astype(np.float32)
         corr_ref[j] = s["corr"].astype(np.float32)
         if check_packages:
@@ -155,6 +173,8 @@ def segment_parity(K, w, heads, algo, interval, check_packages=False):
         corr_got = to_numpy_f64(z[a:b][:, ht])
         per_head(c.corr, j, hs, corr_got, corr_ref[j].astype(np.float64))
     worst = c.check(OUT_TOL[dt], STATE_TOL[dt], say)
+    if rungs2.num:
+        worst[rungs2.what] = rungs2.check(STATE_TOL[dt], say)
     ef = UnitErrors("S_final per head")
     Sf = to_numpy_f64(r["S_final"][ht])
     for i, h in enumerate(hs):

@@ -897,3 +897,41 @@ def test_single_sequence_split_dk_ne_dv(K, dtype, dk, dv):
         assert_close(f"{name} o", to_numpy_f64(o), ref[0], OUT_TOL[dtype])
         assert_close(f"{name} S_final", to_numpy_f64(Sf), ref[1], STATE_TOL[dtype])
         assert_close(f"{name} rungs", to_numpy_f64(ck), ref[2], STATE_TOL[dtype])
+
+
+# ---------------------------------------------------------------------------
+# Fix-up writing the checkpoint rungs (one launch)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("gates", ["config", "long"])
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 128, 128), ("f32", 64, 64), ("bf16", 64, 128)])
+def test_fixup_ckpt_equals_checkpoint_write(K, gates, dtype, dk, dv):
+    """kda_output_fixup_ckpt leaves the same outputs as kda_output_fixup (bit
+    for bit) and writes the rungs that kda_checkpoint_write forms from the
+    sub-packages (same map, other rounding), both against the oracle; rungs
+    at segment ends, inside segments, right after a segment start, and after
+    the propagated state has reached zero."""
+    import torch
+    shift = {} if gates == "config" else dict(gate_shift=-9.0, beta_shift=-6.0)
+    seg = [0, 448, 512, 1216, 1536, 2112]
+    w = make_workload("fixup-rungs", [2112], 2, dk, dv, dtype, 5300 + dk + dv, s0_std=0.5,
+                      seg_start=seg, **shift)
+    say(f"fix-up with rungs {dtype} dk={dk} dv={dv} gates={gates}")
+    t = to_torch(w)
+    iv = 64 if gates == "config" else 128
+    ol, M, D, sM, sD = K.kda_segment_package(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                             t["seg_start"], ckpt_interval=iv)
+    S_in, _ = K.kda_segment_scan(M, D, t["S0"][0].contiguous(), algo=1)
+    o1, o2 = ol.clone(), ol.clone()
+    K.kda_output_fixup(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o1)
+    ck_fused = K.kda_output_fixup_ckpt(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o2,
+                                       sD, interval=iv)
+    ck_two = K.kda_checkpoint_write(t["seg_start"], S_in, sM, sD, T=w.T, interval=iv,
+                                    dtype=t["q"].dtype)
+    sync()
+    assert torch.equal(o1, o2)
+    ro, rS, rck = oracle_full(w, interval=iv)
+    tol = STATE_TOL[dtype]
+    assert_close("rungs, fused", to_numpy_f64(ck_fused), rck, tol)
+    assert_close("rungs, checkpoint write", to_numpy_f64(ck_two), rck, tol)
+    assert_close("fused vs two-call rungs", to_numpy_f64(ck_fused), to_numpy_f64(ck_two), tol)
+    assert_close("o", to_numpy_f64(o2), ro, OUT_TOL[dtype])
