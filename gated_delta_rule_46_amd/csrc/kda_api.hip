@@ -423,6 +423,9 @@ int kda_segment_scan(const kda_config *cfg, int32_t nseg, const float *M, const 
     if (algo == KDA_SCAN_SEQUENTIAL)
         return launched(kda::launch_scan_sequential(cfg->dk, cfg->dv, cfg->num_heads, nseg, M, D,
                                                     S0, S_in, S_final, s), "sequential scan");
+    if (nseg > kda::blelloch_max_segments())
+        return fail(KDA_ERR_UNSUPPORTED, "the Blelloch scan takes at most %d segments (got %d)",
+                    kda::blelloch_max_segments(), nseg);
     const size_t need = kda_segment_scan_workspace(cfg, nseg, algo);
     if (!ws || ws_bytes < need)
         return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, ws_bytes);

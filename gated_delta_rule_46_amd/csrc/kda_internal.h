@@ -68,6 +68,7 @@ hipError_t launch_scan_blelloch(int dk, int dv, int H, int nseg, const float *M,
                                 const float *D, const float *S0, float *S_in,
                                 float *S_final, void *ws, hipStream_t s);
 size_t blelloch_workspace(int dk, int dv, int H, int nseg);
+int blelloch_max_segments();   // largest nseg the Blelloch scan takes
 
 // bounds[j] = min(j*L, T) for j = 0..nseg (device int64).
 hipError_t launch_even_bounds(int64_t *bounds, int nseg, int64_t L, int64_t T, hipStream_t s);

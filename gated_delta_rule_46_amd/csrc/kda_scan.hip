@@ -112,14 +112,18 @@ template <int DK, int NC> struct Acc {
 // acc = L R (L row-major DK x DK, R row-major DK x NC), fp32 MFMA.  Lane
 // (n, g) of wave w holds rows w*DK/4 + 16 rt + 4 g + i of column 16 ct + n.
 //
-// lz / rz: the operand is exactly zero and its memory is not read (zeros are
-// multiplied instead), so that a zero matrix times a non-finite operand gives
-// NaN where the product would.
+// lk / rk: kMem reads the operand; kZero multiplies zeros and kIdent the
+// identity without reading it, so that a zero or identity matrix times a
+// non-finite operand gives NaN where the IEEE product would.
+constexpr int kMem = 0, kZero = 1, kIdent = 2;
+// w: the wave's index among the four that share the product (default: the
+// workgroup's own wave index, four-wave workgroups).
 template <int DK, int NC>
 __device__ __forceinline__ void mm_acc(const float *L, const float *R, Acc<DK, NC> &acc,
-                                       bool lz = false, bool rz = false) {
+                                       int lk = kMem, int rk = kMem, int w = -1) {
     constexpr int RT = Acc<DK, NC>::RT, CT = Acc<DK, NC>::CT;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    if (w < 0) w = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
     const int r0 = w * (DK / 4);
 #pragma unroll
@@ -132,9 +136,15 @@ __device__ __forceinline__ void mm_acc(const float *L, const float *R, Acc<DK, N
     for (int k0 = 0; k0 < DK; k0 += 4) {
         float a[RT], b[CT];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) a[rt] = lz ? 0.f : L[(int64_t)(r0 + 16 * rt + n) * DK + k0 + g];
+        for (int rt = 0; rt < RT; ++rt) {
+            const int row = r0 + 16 * rt + n, col = k0 + g;
+            a[rt] = lk == kMem ? L[(int64_t)row * DK + col] : (lk == kIdent && row == col) ? 1.f : 0.f;
+        }
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) b[ct] = rz ? 0.f : R[(int64_t)(k0 + g) * NC + 16 * ct + n];
+        for (int ct = 0; ct < CT; ++ct) {
+            const int row = k0 + g, col = 16 * ct + n;
+            b[ct] = rk == kMem ? R[(int64_t)row * NC + col] : (rk == kIdent && row == col) ? 1.f : 0.f;
+        }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -146,9 +156,11 @@ __device__ __forceinline__ void mm_acc(const float *L, const float *R, Acc<DK, N
 // out = acc + Add (Add may be null); each element is read and written by the
 // lane that owns it.
 template <int DK, int NC>
-__device__ __forceinline__ void store_acc(const Acc<DK, NC> &acc, const float *Add, float *out) {
+__device__ __forceinline__ void store_acc(const Acc<DK, NC> &acc, const float *Add, float *out,
+                                          int w = -1) {
     constexpr int RT = Acc<DK, NC>::RT, CT = Acc<DK, NC>::CT;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    if (w < 0) w = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
     const int r0 = w * (DK / 4);
     if (Add) {
@@ -195,7 +207,7 @@ __device__ __forceinline__ void affine(const float *L, bool nz, const float *R, 
         }
     }
     Acc<DK, NC> acc;
-    mm_acc<DK, NC>(L, R, acc, !nz);
+    mm_acc<DK, NC>(L, R, acc, nz ? kMem : kZero);
     store_acc<DK, NC>(acc, Add, out);
 }
 
@@ -232,187 +244,233 @@ __global__ __launch_bounds__(NTH) void scan_seq_kernel(int H, int nseg, const fl
 }
 
 // ---------------------------------------------------------------------------
-// Blelloch scan over packages in the workspace:
-//   Pm [size+1][H][DK][DK], Pd [size+1][H][DK][DV], Fz [size+1][H]; slot
-//   `size` keeps the total.  One workgroup per (pair, head), so each pair's
-//   slots are touched by one workgroup only.  Flags per slot:
-//     kFlagM    M may be nonzero; without it the slot's M is exactly zero
-//               whatever its Pm memory holds (zero matrices are never
-//               written, copied or read);
-//     kFlagBad  M or D may hold an infinity or a NaN.
-//   A product with a zero M is skipped only when the other factor is finite:
-//   0 * inf and 0 * NaN are NaN, so against a flagged factor the product is
-//   formed with zeros in place of the unread M.
+// Blelloch scan over packages (exclusive up-sweep / down-sweep over the
+// composition, identity-padded to a power of two), in three launches:
+//
+//   blel_flags_kernel  grid (nseg + 1, H): per package, whether M is exactly
+//                      zero and whether M or D holds an infinity or a NaN;
+//                      block nseg tests S0;
+//   blel_tree_kernel   grid (H): the whole tree of one head in one
+//                      workgroup.  Slots hold buffer ids, not matrices: an id
+//                      names a caller package, a fresh workspace buffer, the
+//                      zero matrix or the identity.  Moving a slot moves ids;
+//                      only a composition that really multiplies writes a
+//                      fresh buffer (all four waves, fp32 MFMA);
+//   blel_apply_kernel  grid (nseg + 1, H): S_in[j] = Pre_j.M S0 + Pre_j.D and
+//                      S_final = Total.M S0 + Total.D from the ids.
+//
+// A product with a zero factor is formed only when the other factor may hold
+// an infinity or a NaN (0 * inf and 0 * NaN are NaN), with zeros in place of
+// the zero factor; otherwise it is exactly zero and skipped.
 // ---------------------------------------------------------------------------
-constexpr int kFlagM = 1, kFlagBad = 2;
+constexpr int kIdZero = -1, kIdIdent = -2;
+constexpr int kMaxSize = 1 << 12;   // padded package count (slot kMaxSize + 1 parks a slot)
+
+struct BlelWs {
+    float *Mw, *Dw;          // fresh buffers [2 * size][H][dk][dk] and [2 * size][H][dk][dv]
+    int *fz, *fb;            // [nseg][H]: M nonzero, M or D not finite
+    int *s0bad;              // [H]
+    int *out;                // [(nseg + 1)][H][3]: ids of the exclusive prefixes and the total
+};
 
 template <int DK, int DV>
-__global__ __launch_bounds__(NTH, 1) void blel_init_kernel(int H, int nseg, const float *M,
-                                                        const float *D, float *Pm, float *Pd,
-                                                        int *Fz) {
-    const int slot = blockIdx.x, h = blockIdx.y;
+__global__ __launch_bounds__(NTH) void blel_flags_kernel(int H, int nseg, const float *M,
+                                                         const float *D, const float *S0,
+                                                         BlelWs w) {
+    const int j = blockIdx.x, h = blockIdx.y;
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
-    float *pm = Pm + ((int64_t)slot * H + h) * mm;
-    float *pd = Pd + ((int64_t)slot * H + h) * dd;
-    if (slot < nseg) {
-        Tile<DK * DK> tm;
-        Tile<DK * DV> td;
-        tm.load(M + ((int64_t)slot * H + h) * mm);
-        td.load(D + ((int64_t)slot * H + h) * dd);
-        const bool nz = tm.any_nonzero();
-        const bool bad = tm.any_nonfinite() || td.any_nonfinite();
-        if (nz) tm.store(pm);
-        td.store(pd);
-        if (threadIdx.x == 0) Fz[slot * H + h] = (nz ? kFlagM : 0) | (bad ? kFlagBad : 0);
-    } else {
-        for (int e = threadIdx.x; e < DK * DK; e += NTH) pm[e] = (e / DK == e % DK) ? 1.f : 0.f;
-        copy_n<DK * DV>(pd, nullptr);
-        if (threadIdx.x == 0) Fz[slot * H + h] = kFlagM;
-    }
-}
-
-// One combine of a level, P[later] o P[earlier] = (Ml Me, Ml De + Dl):
-//   up-sweep   (down = 0): P[i] <- P[i] o P[j]
-//   down-sweep (down = 1): (P[j], P[i]) <- (P[i], P[j] o P[i])
-// with i = (blockIdx.x + 1) * 2 * step - 1 and j = i - step.
-template <int DK, int DV>
-__global__ __launch_bounds__(NTH, 1) void blel_level_kernel(int H, int step, int down, float *Pm,
-                                                         float *Pd, int *Fz) {
-    const int h = blockIdx.y;
-    const int64_t i = (int64_t)(blockIdx.x + 1) * 2 * step - 1, j = i - step;
-    const int64_t lat = down ? j : i, ear = down ? i : j;
-    const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
-    float *Ml = Pm + (lat * H + h) * mm, *Dl = Pd + (lat * H + h) * dd;
-    float *Me = Pm + (ear * H + h) * mm, *De = Pd + (ear * H + h) * dd;
-    const int fl = Fz[lat * H + h], fe = Fz[ear * H + h];
-    // exact zero tests: flags first, then the memory of a flagged later M
-    const bool zl = !(fl & kFlagM) || !block_nonzero<DK * DK>(Ml);
-    const bool ze = !(fe & kFlagM);
-    const bool bl = fl & kFlagBad, be = fe & kFlagBad;
-    // Ml Me is exactly zero when both are zero, or one is zero and the other finite
-    const bool need_mm = !((zl && ze) || (zl && !be) || (ze && !bl));
-    // Ml De is exactly zero when Ml is zero and De finite
-    const bool need_md = !(zl && !be);
-    Acc<DK, DK> am;
-    Acc<DK, DV> ad;
-    if (need_mm) mm_acc<DK, DK>(Ml, Me, am, zl, ze);
-    if (need_md) mm_acc<DK, DV>(Ml, De, ad, zl, false);
-    __syncthreads();                       // every operand read precedes the first store
-    const int flags = (need_mm ? kFlagM : 0) | ((bl || be) ? kFlagBad : 0);
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int n = lane & 15, g = lane >> 4;
-    const int r0 = w * (DK / 4);
-    // each lane moves exactly the elements it owns in the accumulator layout
-    if (!down) {
-        // result into slot i (= later)
-        if (need_mm) store_acc<DK, DK>(am, nullptr, Ml);
-        if (need_md) store_acc<DK, DV>(ad, Dl, Dl);
-        __syncthreads();                   // every wave has read the flags
-        if (threadIdx.x == 0) Fz[i * H + h] = flags;
-        return;
-    }
-    // down-sweep: slot j (= later) takes the old P[i] (= earlier), slot i the result
-    if (!need_mm && !need_md) {
-        // the usual case (Ml zero against finite factors): P[j] <- P[i],
-        // P[i] <- (0, Dj); whole tiles through registers, every load before
-        // any store
-        if (fe & kFlagM) {
-            Tile<DK * DK> t;
-            t.load(Me);
-            t.store(Ml);
+    if (j == nseg) {
+        if (!S0) {
+            if (threadIdx.x == 0) w.s0bad[h] = 0;
+            return;
         }
-        Tile<DK * DV> a, b;
-        a.load(De);
-        b.load(Dl);
-        a.store(Dl);
-        b.store(De);
-        __syncthreads();                   // every wave has read the flags
-        if (threadIdx.x == 0) { Fz[j * H + h] = fe; Fz[i * H + h] = flags; }
+        Tile<DK * DV> t;
+        t.load(S0 + (int64_t)h * dd);
+        const bool bad = t.any_nonfinite();
+        if (threadIdx.x == 0) w.s0bad[h] = bad ? 1 : 0;
         return;
     }
-    if ((fe & kFlagM) || need_mm) {
-#pragma unroll
-        for (int rt = 0; rt < Acc<DK, DK>::RT; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < Acc<DK, DK>::CT; ++ct)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int64_t e = (int64_t)(r0 + 16 * rt + 4 * g + q) * DK + 16 * ct + n;
-                    if (fe & kFlagM) Ml[e] = Me[e];
-                    if (need_mm) Me[e] = am.v[rt][ct][q];
-                }
+    Tile<DK * DK> tm;
+    Tile<DK * DV> td;
+    tm.load(M + ((int64_t)j * H + h) * mm);
+    td.load(D + ((int64_t)j * H + h) * dd);
+    const bool nz = tm.any_nonzero();
+    const bool bad = tm.any_nonfinite() || td.any_nonfinite();
+    if (threadIdx.x == 0) {
+        w.fz[j * H + h] = nz ? 1 : 0;
+        w.fb[j * H + h] = bad ? 1 : 0;
     }
-#pragma unroll
-    for (int rt = 0; rt < Acc<DK, DV>::RT; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < Acc<DK, DV>::CT; ++ct)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t e = (int64_t)(r0 + 16 * rt + 4 * g + q) * DV + 16 * ct + n;
-                const float od = Dl[e];
-                Dl[e] = De[e];
-                De[e] = need_md ? ad.v[rt][ct][q] + od : od;
-            }
-    __syncthreads();                       // every wave has read the flags
-    if (threadIdx.x == 0) { Fz[j * H + h] = fe; Fz[i * H + h] = flags; }
 }
 
-// After the up-sweep: slot `size` = total, slot size-1 = identity.
+// dst = a + b over N floats by NTH threads (tid = 0..NTH-1), every load
+// before any store.
+template <int N>
+__device__ __forceinline__ void add_n(float *dst, const float *a, const float *b,
+                                      int tid = threadIdx.x) {
+    constexpr int PER = N / 4 / NTH;
+    static_assert(PER * 4 * NTH == N, "block size");
+    f32x4 x[PER], y[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        x[i] = ((const f32x4 *)a)[tid + i * NTH];
+        y[i] = ((const f32x4 *)b)[tid + i * NTH];
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) ((f32x4 *)dst)[tid + i * NTH] = x[i] + y[i];
+}
+
+// Two groups of four waves: the M product of a composition on group 0 and
+// its D product (or sum) on group 1, at the same time.
+constexpr int NTH_TREE = 2 * NTH;
+
 template <int DK, int DV>
-__global__ __launch_bounds__(NTH) void blel_root_kernel(int H, int size, float *Pm, float *Pd,
-                                                        int *Fz) {
+__global__ __launch_bounds__(NTH_TREE, 1) void blel_tree_kernel(int H, int nseg, int size,
+                                                        const float *M, const float *D,
+                                                        BlelWs w) {
     const int h = blockIdx.x;
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
-    float *lm = Pm + ((int64_t)(size - 1) * H + h) * mm, *ld = Pd + ((int64_t)(size - 1) * H + h) * dd;
-    float *tm = Pm + ((int64_t)size * H + h) * mm, *td = Pd + ((int64_t)size * H + h) * dd;
-    const int f_last = Fz[(size - 1) * H + h];
-    {
-        Tile<DK * DK> t;
-        if (f_last & kFlagM) {
-            t.load(lm);
-            t.store(tm);
+    __shared__ int s_m[kMaxSize + 2], s_d[kMaxSize + 2], s_b[kMaxSize + 2];
+    constexpr int kPark = kMaxSize + 1;
+    const int grp = threadIdx.x / NTH, gw = (threadIdx.x / 64) % 4, gt = threadIdx.x % NTH;
+    for (int j = threadIdx.x; j < size; j += NTH_TREE) {
+        if (j < nseg) {
+            s_m[j] = w.fz[j * H + h] ? j : kIdZero;
+            s_d[j] = j;
+            s_b[j] = w.fb[j * H + h];
+        } else {   // identity padding
+            s_m[j] = kIdIdent;
+            s_d[j] = kIdZero;
+            s_b[j] = 0;
         }
-#pragma unroll
-        for (int k = 0; k < Tile<DK * DK>::PER; ++k) {
-            const int64_t e = threadIdx.x + (int64_t)k * NTH;
-            const int r = (int)((4 * e) / DK), c = (int)((4 * e) % DK);
-            t.x[k] = f32x4{r == c ? 1.f : 0.f, r == c + 1 ? 1.f : 0.f, r == c + 2 ? 1.f : 0.f,
-                           r == c + 3 ? 1.f : 0.f};
+    }
+    __syncthreads();
+    int nM = 0, nD = 0;   // fresh buffers used (uniform across the workgroup)
+    auto mptr = [&](int id) -> const float * {
+        return id < 0 ? nullptr : id < nseg ? M + ((int64_t)id * H + h) * mm
+                                            : w.Mw + ((int64_t)(id - nseg) * H + h) * mm;
+    };
+    auto dptr = [&](int id) -> const float * {
+        return id < 0 ? nullptr : id < nseg ? D + ((int64_t)id * H + h) * dd
+                                            : w.Dw + ((int64_t)(id - nseg) * H + h) * dd;
+    };
+    // r <- l o e = (Ml Me, Ml De + Dl); reads the slots, writes slot r after
+    // a barrier (r may be l or e).  Every thread takes the same decisions.
+    auto compose = [&](int l, int e, int r) {
+        const int ml = s_m[l], dl = s_d[l], bl = s_b[l];
+        const int me = s_m[e], de = s_d[e], be = s_b[e];
+        const bool zl = ml == kIdZero, il = ml == kIdIdent;
+        const bool ze = me == kIdZero, ie = me == kIdIdent;
+        const bool dze = de == kIdZero, dzl = dl == kIdZero;
+        // a zero or identity factor is used as such only against finite
+        // values: under IEEE arithmetic 0 * inf is NaN and I X spreads an inf
+        // or a NaN of X over its column, so against a non-finite factor the
+        // product is formed (with the zero or identity substituted)
+        const int lk = zl ? kZero : il ? kIdent : kMem, ek = ze ? kZero : ie ? kIdent : kMem;
+        int rm, rd;
+        // M part
+        if ((zl && (ze || !be)) || (ze && !bl)) {
+            rm = kIdZero;
+        } else if (il && !be) {
+            rm = me;
+        } else if (ie && !bl) {
+            rm = ml;
+        } else {
+            rm = nseg + nM++;
+            if (grp == 0) {
+                Acc<DK, DK> am;
+                mm_acc<DK, DK>(mptr(ml), mptr(me), am, lk, ek, gw);
+                store_acc<DK, DK>(am, nullptr, (float *)mptr(rm), gw);
+            }
         }
-        t.store(lm);
+        // D part: T = Ml De, then T + Dl
+        if ((zl && !be) || (dze && !bl)) {
+            rd = dl;
+        } else if (il && !be) {
+            if (dzl) {
+                rd = de;
+            } else {
+                rd = nseg + nD++;
+                if (grp == 1) add_n<DK * DV>((float *)dptr(rd), dptr(de), dptr(dl), gt);
+            }
+        } else {
+            rd = nseg + nD++;
+            if (grp == 1) {
+                Acc<DK, DV> ad;
+                mm_acc<DK, DV>(mptr(ml), dptr(de), ad, lk, dze ? kZero : kMem, gw);
+                store_acc<DK, DV>(ad, dzl ? nullptr : dptr(dl), (float *)dptr(rd), gw);
+            }
+        }
+        __syncthreads();   // every thread has read the slots
+        if (threadIdx.x == 0) {
+            s_m[r] = rm;
+            s_d[r] = rd;
+            s_b[r] = bl | be;
+        }
+        __syncthreads();
+    };
+    for (int step = 1; step < size; step *= 2)             // up-sweep
+        for (int i = 2 * step - 1; i < size; i += 2 * step) compose(i, i - step, i);
+    if (threadIdx.x == 0) {                                  // root
+        s_m[size] = s_m[size - 1];
+        s_d[size] = s_d[size - 1];
+        s_b[size] = s_b[size - 1];
+        s_m[size - 1] = kIdIdent;
+        s_d[size - 1] = kIdZero;
+        s_b[size - 1] = 0;
     }
-    {
-        Tile<DK * DV> t;
-        t.load(ld);
-        t.store(td);
-        t.zero();
-        t.store(ld);
+    __syncthreads();
+    for (int step = size / 2; step >= 1; step /= 2) {       // down-sweep
+        for (int i = 2 * step - 1; i < size; i += 2 * step) {
+            // (P[i-step], P[i]) <- (P[i], P[i-step] o P[i])
+            const int lm = s_m[i - step], ld = s_d[i - step], lb = s_b[i - step];
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                s_m[i - step] = s_m[i];
+                s_d[i - step] = s_d[i];
+                s_b[i - step] = s_b[i];
+                s_m[kPark] = lm;          // the old P[i-step], parked in the spare slot
+                s_d[kPark] = ld;
+                s_b[kPark] = lb;
+            }
+            __syncthreads();
+            compose(kPark, i, i);
+        }
     }
-    __syncthreads();   // every wave has read the flags before they change
-    if (threadIdx.x == 0) { Fz[size * H + h] = f_last; Fz[(size - 1) * H + h] = kFlagM; }
+    for (int j = threadIdx.x; j <= nseg; j += NTH_TREE) {
+        const int slot = j < nseg ? j : size;
+        w.out[(j * H + h) * 3 + 0] = s_m[slot];
+        w.out[(j * H + h) * 3 + 1] = s_d[slot];
+        w.out[(j * H + h) * 3 + 2] = s_b[slot];
+    }
 }
 
-// S_in[j] = P[j].M S0 + P[j].D (j < nseg);  S_final = P[size].M S0 + P[size].D.
-// grid (nseg+1, H).
+// S_in[j] = Pre_j.M S0 + Pre_j.D (j < nseg); S_final = Total.M S0 + Total.D.
 template <int DK, int DV>
-__global__ __launch_bounds__(NTH) void blel_apply_kernel(int H, int nseg, int size, const float *Pm,
-                                                         const float *Pd, const int *Fz,
-                                                         const float *S0, float *S_in, float *S_final) {
+__global__ __launch_bounds__(NTH) void blel_apply_kernel(int H, int nseg, const float *M,
+                                                         const float *D, const float *S0,
+                                                         float *S_in, float *S_final, BlelWs w) {
     const int jj = blockIdx.x, h = blockIdx.y;
-    const int slot = jj < nseg ? jj : size;
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
-    const float *Lm = Pm + ((int64_t)slot * H + h) * mm;
-    const float *Ad = Pd + ((int64_t)slot * H + h) * dd;
+    const int idm = w.out[(jj * H + h) * 3 + 0], idd = w.out[(jj * H + h) * 3 + 1];
+    const float *Lm = idm < 0 ? nullptr : idm < nseg ? M + ((int64_t)idm * H + h) * mm
+                                                     : w.Mw + ((int64_t)(idm - nseg) * H + h) * mm;
+    const float *Ad = idd < 0 ? nullptr : idd < nseg ? D + ((int64_t)idd * H + h) * dd
+                                                     : w.Dw + ((int64_t)(idd - nseg) * H + h) * dd;
     float *out = jj < nseg ? S_in + ((int64_t)jj * H + h) * dd : S_final + (int64_t)h * dd;
-    if (!S0) {   // a zero incoming state
-        copy_n<DK * DV>(out, Ad);
+    const float *s0 = S0 ? S0 + (int64_t)h * dd : nullptr;
+    const bool s0bad = s0 && w.s0bad[h];
+    if (!s0 || (idm == kIdZero && !s0bad)) {
+        copy_n<DK * DV>(out, Ad);   // zeros when Ad is null
         return;
     }
-    const float *s0 = S0 + (int64_t)h * dd;
-    const bool nz = (Fz[slot * H + h] & kFlagM) ? block_nonzero<DK * DK>(Lm) : false;
-    // a zero prefix M (not read when flagged zero) passes Ad on unless S0 is
-    // not finite
-    affine<DK, DV>(Lm, nz, s0, Ad, out);
+    if (idm == kIdIdent && !s0bad) {
+        if (Ad) add_n<DK * DV>(out, s0, Ad);
+        else copy_n<DK * DV>(out, s0);
+        return;
+    }
+    Acc<DK, DV> acc;
+    mm_acc<DK, DV>(Lm, s0, acc, idm == kIdZero ? kZero : idm == kIdIdent ? kIdent : kMem);
+    store_acc<DK, DV>(acc, Ad, out);
 }
 
 // Segment-path checkpoints: grid (rows, H).  Rung row r sits at
@@ -447,7 +505,7 @@ __global__ __launch_bounds__(NTH) void ckpt_kernel(int H, int nseg, const int64_
         return;
     }
     Acc<DK, DV> acc;
-    mm_acc<DK, DV>(Lm, Sj, acc, !nz);
+    mm_acc<DK, DV>(Lm, Sj, acc, nz ? kMem : kZero);
     store_acc<DK, DV>(acc, Dr, out);
 }
 
@@ -491,30 +549,33 @@ hipError_t scan_seq_t(int H, int nseg, const float *M, const float *D, const flo
 }
 
 template <int DK, int DV>
+BlelWs blel_ws(void *ws, int H, int nseg) {
+    const int size = pow2_at_least(nseg);
+    BlelWs w;
+    w.Mw = (float *)ws;
+    w.Dw = w.Mw + (int64_t)2 * size * H * DK * DK;
+    w.fz = (int *)(w.Dw + (int64_t)2 * size * H * DK * DV);
+    w.fb = w.fz + (int64_t)nseg * H;
+    w.s0bad = w.fb + (int64_t)nseg * H;
+    w.out = w.s0bad + H;
+    return w;
+}
+
+template <int DK, int DV>
 hipError_t scan_blel_t(int H, int nseg, const float *M, const float *D, const float *S0,
                        float *S_in, float *S_final, void *ws, hipStream_t s) {
     const int size = pow2_at_least(nseg);
-    float *Pm = (float *)ws;
-    float *Pd = Pm + (int64_t)(size + 1) * H * DK * DK;
-    int *Fz = (int *)(Pd + (int64_t)(size + 1) * H * DK * DV);
+    if (size > kMaxSize) return hipErrorInvalidValue;
+    const BlelWs w = blel_ws<DK, DV>(ws, H, nseg);
     hipError_t e;
-    hipLaunchKernelGGL((blel_init_kernel<DK, DV>), dim3(size, H), dim3(NTH), 0, s, H, nseg, M, D, Pm,
-                       Pd, Fz);
+    hipLaunchKernelGGL((blel_flags_kernel<DK, DV>), dim3(nseg + 1, H), dim3(NTH), 0, s, H, nseg,
+                       M, D, S0, w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    for (int step = 1; step < size; step *= 2) {
-        hipLaunchKernelGGL((blel_level_kernel<DK, DV>), dim3(size / (2 * step), H), dim3(NTH), 0,
-                           s, H, step, 0, Pm, Pd, Fz);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((blel_root_kernel<DK, DV>), dim3(H), dim3(NTH), 0, s, H, size, Pm, Pd, Fz);
+    hipLaunchKernelGGL((blel_tree_kernel<DK, DV>), dim3(H), dim3(NTH_TREE), 0, s, H, nseg, size, M,
+                       D, w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    for (int step = size / 2; step >= 1; step /= 2) {
-        hipLaunchKernelGGL((blel_level_kernel<DK, DV>), dim3(size / (2 * step), H), dim3(NTH), 0,
-                           s, H, step, 1, Pm, Pd, Fz);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((blel_apply_kernel<DK, DV>), dim3(nseg + 1, H), dim3(NTH), 0, s, H, nseg,
-                       size, Pm, Pd, Fz, S0, S_in, S_final);
+    hipLaunchKernelGGL((blel_apply_kernel<DK, DV>), dim3(nseg + 1, H), dim3(NTH), 0, s, H, nseg, M,
+                       D, S0, S_in, S_final, w);
     return hipGetLastError();
 }
 
@@ -531,10 +592,12 @@ hipError_t ckpt_t(int H, int64_t T, const int64_t *seg_start, int nseg, int inte
 
 }  // namespace
 
+int blelloch_max_segments() { return kMaxSize; }
+
 size_t blelloch_workspace(int dk, int dv, int H, int nseg) {
     const int size = pow2_at_least(nseg);
-    return (size_t)(size + 1) * H * ((size_t)dk * dk + (size_t)dk * dv) * sizeof(float) +
-           (size_t)(size + 1) * H * sizeof(int);
+    return (size_t)2 * size * H * ((size_t)dk * dk + (size_t)dk * dv) * sizeof(float) +
+           ((size_t)2 * nseg * H + H + (size_t)3 * (nseg + 1) * H) * sizeof(int);
 }
 
 hipError_t launch_scan_sequential(int dk, int dv, int H, int nseg, const float *M, const float *D,

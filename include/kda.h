@@ -265,8 +265,10 @@ size_t kda_segment_scan_workspace(const kda_config *cfg, int32_t nseg, int32_t a
  * S_final [H,dk,dv].  algo KDA_SCAN_SEQUENTIAL walks the segments in order;
  * KDA_SCAN_BLELLOCH runs a work-efficient up-sweep / down-sweep exclusive
  * scan over the composition (Mb,Db) o (Ma,Da) = (Mb Ma, Mb Da + Db), padded
- * with identity packages to a power of two, in the workspace.
- * M and D are not modified.
+ * with identity packages to a power of two, in the workspace (at most 4096
+ * segments; more return KDA_ERR_UNSUPPORTED).  Products with an exactly
+ * zero or identity factor are not formed unless the other factor holds an
+ * infinity or a NaN.  M and D are not modified.
  */
 int kda_segment_scan(const kda_config *cfg, int32_t nseg, const float *M, const float *D,
                      const float *S0, float *S_in, float *S_final, int32_t algo,

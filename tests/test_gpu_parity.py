@@ -340,7 +340,8 @@ def test_segment_path_long_memory(K, algo, dtype, d):
 
 @pytest.mark.parametrize("algo", [0, 1])
 @pytest.mark.parametrize("nseg,zero", [(13, (1, 4, 5, 9, 12)), (16, (0, 2, 3, 7, 8, 11, 15)),
-                                       (16, tuple(range(1, 16))), (5, ())])
+                                       (16, tuple(range(1, 16))), (5, ()), (1, ()), (1, (0,)),
+                                       (2, (0,)), (3, (1,)), (33, (0, 5, 6, 7, 20, 31, 32))])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("with_s0", [True, False])
 def test_scan_mixed_zero_packages(K, algo, nseg, zero, d, with_s0):
