@@ -188,6 +188,89 @@ int prefill_split(const SplitPlan &p, const kda_config *cfg, const void *q, cons
                     "prefill split (fix-up)");
 }
 
+// Segments whose (segment, head) units would leave compute units idle (or run
+// with half-width value blocks that repeat the producer work) are split into
+// f sub-segments of at least kMinSubSplit tokens on average; their packages
+// are merged in the workspace (kda_segment_package).
+constexpr int64_t kMinSubSplit = 512;
+
+struct PackageSplit {
+    int f = 1;
+    size_t off_sb = 0, off_ord = 0, off_M = 0, off_D = 0, bytes = 0;
+};
+
+bool plan_package_split(const kda_config *cfg, int64_t T, int32_t nseg, PackageSplit *p) {
+    if (nseg <= 0 || T <= 0) return false;
+    const int64_t units = (int64_t)nseg * cfg->num_heads;
+    const int cus = device_cus();
+    if (units >= cus) return false;
+    int64_t f = (cus + units - 1) / units;
+    f = std::min<int64_t>(f, 8);
+    f = std::min<int64_t>(f, T / nseg / kMinSubSplit);
+    if (f < 2) return false;
+    p->f = (int)f;
+    const size_t nsub = (size_t)f * nseg, H = (size_t)cfg->num_heads;
+    size_t at = 0;
+    auto take = [&](size_t b) { const size_t o = at; at += round256(b); return o; };
+    p->off_sb = take(sizeof(int64_t) * (nsub + 1));
+    p->off_ord = take(sizeof(int32_t) * (size_t)(f - 1) * nseg);
+    p->off_M = take(sizeof(float) * nsub * H * cfg->dk * cfg->dk);
+    p->off_D = take(sizeof(float) * nsub * H * cfg->dk * cfg->dv);
+    p->bytes = at;
+    return true;
+}
+
+int package_split(const PackageSplit &p, const kda_config *cfg, const void *q, const void *k,
+                  const void *v, const float *g, const float *beta, int64_t T,
+                  const int64_t *seg_start, int32_t nseg, void *o_local, float *M, float *D,
+                  int32_t interval, float *sub_M, float *sub_D, void *ws, hipStream_t s) {
+    unsigned char *w = (unsigned char *)ws;
+    int64_t *sb = (int64_t *)(w + p.off_sb);
+    int32_t *ord = (int32_t *)(w + p.off_ord);
+    float *Ms = (float *)(w + p.off_M), *Ds = (float *)(w + p.off_D);
+    const bool bf = cfg->io_dtype == KDA_DTYPE_BF16;
+    const int H = cfg->num_heads, dk = cfg->dk, dv = cfg->dv, f = p.f;
+    const int nsub = f * nseg;
+    hipError_t e = kda::launch_split_bounds(seg_start, nseg, f, sb, ord, s);
+    if (e != hipSuccess) return launched(e, "package split (bounds)");
+    // packages of every sub-segment, M included (the merge needs it)
+    const int nb = kda::engine_pick_nb(bf, dk, dv, (int64_t)nsub * H, kda::kModePackage);
+    kda::EngineArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o_local;
+    a.bounds = sb; a.order = nullptr; a.n_units = nsub; a.H = H;
+    a.S_init = nullptr; a.S_out = Ds; a.M_out = Ms;
+    a.interval = interval; a.ckpt_off = nullptr; a.ckpt_S = sub_D; a.ckpt_M = sub_M;
+    a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;
+    a.ncb = dv / nb;
+    a.ncb_m = dk / std::min(nb, dk);
+    if ((e = kda::launch_engine(kda::kModePackageVM, bf, dk, dv, nb, a, s)) != hipSuccess)
+        return launched(e, "package split (packages)");
+    const int nbf = kda::engine_pick_nb(bf, dk, dv, (int64_t)nseg * H, kda::kModeFixup);
+    const size_t slot = (size_t)H * dk * dv;
+    for (int kk = 1; kk < f; ++kk) {
+        // sub-segment kk of every segment fixed up from the accumulated state
+        // of sub-segments 0..kk-1, kept in the slot before it (S_init[u] = Ds[u-1])
+        kda::EngineArgs fx{};
+        fx.q = q; fx.k = k; fx.v = nullptr; fx.g = g; fx.beta = beta; fx.o = o_local;
+        fx.bounds = sb; fx.order = ord + (size_t)(kk - 1) * nseg; fx.n_units = nseg; fx.H = H;
+        fx.S_init = (const float *)((uintptr_t)Ds - slot * sizeof(float));
+        fx.scale = cfg->scale; fx.l2norm = cfg->qk_l2norm;
+        if (interval > 0 && sub_D) {   // rungs inside it: in place
+            fx.interval = interval; fx.ckpt_S = sub_D; fx.ckpt_in = sub_D;
+        }
+        fx.ncb = dv / nbf;
+        if ((e = kda::launch_engine(kda::kModeFixup, bf, dk, dv, nbf, fx, s)) != hipSuccess)
+            return launched(e, "package split (fix-up)");
+        if (interval > 0 && sub_M) {
+            e = kda::launch_split_rung_m(dk, H, nseg, f, kk, sb, interval, T / interval, Ms, sub_M, s);
+            if (e != hipSuccess) return launched(e, "package split (rungs)");
+        }
+        if ((e = kda::launch_split_compose(dk, dv, H, nseg, f, kk, Ms, Ds, M, D, s)) != hipSuccess)
+            return launched(e, "package split (compose)");
+    }
+    return ok();
+}
+
 // Scratch of kda_prefill_noalloc: one fixed array per device, held for the
 // life of the process, in place of the caller's workspace.  In host code the
 // array's name only stands in for the symbol; the device address of each
@@ -358,12 +441,16 @@ int kda_prefill_resume(const kda_config *cfg, const void *q, const void *k, cons
                         nullptr, pool, pos0, o, ckpt, ws, ws_bytes, stream);
 }
 
+size_t kda_segment_package_workspace(const kda_config *cfg, int64_t T, int32_t nseg) {
+    PackageSplit p;
+    if (!cfg || check_config(cfg) != KDA_OK || !plan_package_split(cfg, T, nseg, &p)) return 0;
+    return p.bytes;
+}
+
 int kda_segment_package(const kda_config *cfg, const void *q, const void *k, const void *v,
                         const float *g, const float *beta, int64_t T, const int64_t *seg_start,
                         int32_t nseg, void *o_local, float *M, float *D, const kda_ckpt *ckpt,
                         float *sub_M, float *sub_D, void *ws, size_t ws_bytes, void *stream) {
-    (void)ws;
-    (void)ws_bytes;
     KDA_TRY(check_config(cfg));
     if (T <= 0) return fail(KDA_ERR_ARG, "T must be positive (got %lld)", (long long)T);
     if (nseg <= 0) return fail(KDA_ERR_ARG, "nseg must be positive (got %d)", nseg);
@@ -384,6 +471,13 @@ int kda_segment_package(const kda_config *cfg, const void *q, const void *k, con
         if (sub_M && !M) return fail(KDA_ERR_ARG, "sub_M needs M (M is NULL)");
     }
     hipStream_t s = (hipStream_t)stream;
+    PackageSplit sp;
+    if (ws && plan_package_split(cfg, T, nseg, &sp) && ws_bytes >= sp.bytes) {
+        KDA_TRY(check_tensor(ws, "ws", true));
+        return package_split(sp, cfg, q, k, v, g, beta, T, seg_start, nseg, o_local, M, D,
+                             subs ? ckpt->interval : 0, subs ? sub_M : nullptr,
+                             subs ? sub_D : nullptr, ws, s);
+    }
     const bool bf = cfg->io_dtype == KDA_DTYPE_BF16;
     const int nb = kda::engine_pick_nb(bf, cfg->dk, cfg->dv, (int64_t)nseg * cfg->num_heads,
                                        kda::kModePackage);

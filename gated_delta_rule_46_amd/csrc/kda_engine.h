@@ -629,7 +629,7 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
     // later rung p of the segment is its own part sub_D[p]; copied here for
     // the rungs after position `from`.
     auto copy_rungs_after = [&](int64_t from) {
-        if (MODE != kModeFixup || !a.ckpt_S || a.interval <= 0) return;
+        if (MODE != kModeFixup || !a.ckpt_S || a.interval <= 0 || a.ckpt_S == a.ckpt_in) return;
         for (int64_t p = (from / a.interval + 1) * a.interval; p <= t1; p += a.interval) {
             const int64_t off = ((p / a.interval - 1) * H + h) * DK * DV;
             copy_state_block<DK, NB>(a.ckpt_S + off, a.ckpt_in + off, DV, cbase,

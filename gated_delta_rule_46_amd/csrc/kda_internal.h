@@ -73,6 +73,16 @@ int blelloch_max_segments();   // largest nseg the Blelloch scan takes
 // bounds[j] = min(j*L, T) for j = 0..nseg (device int64).
 hipError_t launch_even_bounds(int64_t *bounds, int nseg, int64_t L, int64_t T, hipStream_t s);
 
+// Segments split into f sub-segments (kda_segment_package): bounds and merge
+// orders, the in-place composition of step k, and the sub_M rungs of step k.
+hipError_t launch_split_bounds(const int64_t *seg_start, int nseg, int f, int64_t *sb,
+                               int32_t *ord, hipStream_t s);
+hipError_t launch_split_compose(int dk, int dv, int H, int nseg, int f, int k, float *Ms,
+                                float *Ds, float *M_out, float *D_out, hipStream_t s);
+hipError_t launch_split_rung_m(int dk, int H, int nseg, int f, int k, const int64_t *sb,
+                               int interval, int64_t rows, const float *Ms, float *sub_M,
+                               hipStream_t s);
+
 // Segment-path checkpoints: states[row] = sub_M[row] S_in[j] + sub_D[row].
 hipError_t launch_ckpt_write(int dk, int dv, int H, int64_t T, const int64_t *seg_start,
                              int nseg, int interval, const float *S_in, const float *sub_M,

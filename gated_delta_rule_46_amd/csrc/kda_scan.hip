@@ -473,6 +473,113 @@ __global__ __launch_bounds__(NTH) void blel_apply_kernel(int H, int nseg, const 
     store_acc<DK, DV>(acc, Ad, out);
 }
 
+// ---------------------------------------------------------------------------
+// Segments split into f sub-segments (kda_segment_package on a device whose
+// compute units the segments alone would leave idle).  Sub-segment k of
+// segment j is unit u = f j + k; its packages are computed like a segment's,
+// then merged left to right: step k fixes sub-segment k up from the
+// accumulated state of sub-segments 0..k-1 (the chunk engine's fix-up mode)
+// and composes the packages, P_u <- P_u o P_{u-1}, in place.
+// ---------------------------------------------------------------------------
+
+// sb[f j + k] = seg_start[j] + chunk-aligned k/f of segment j, sb[f nseg] = T;
+// ord[(k-1) nseg + j] = f j + k for k = 1..f-1.
+__global__ void split_bounds_kernel(const int64_t *seg_start, int nseg, int f, int64_t *sb,
+                                    int32_t *ord) {
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx > f * nseg) return;
+    if (idx == f * nseg) {
+        sb[idx] = seg_start[nseg];
+        return;
+    }
+    const int j = idx / f, k = idx - j * f;
+    const int64_t a = seg_start[j], len = seg_start[j + 1] - a;
+    sb[idx] = a + (len * k / f) / kChunk * kChunk;
+    if (k > 0) ord[(k - 1) * nseg + j] = idx;
+}
+
+// Step k of the merge, grid (nseg, H): with u = f j + k,
+//   (M_u, D_u) <- (M_u M_{u-1}, M_u D_{u-1} + D_u)
+// into the sub-segment slots, or into M_out[j], D_out[j] at the last step
+// (M_out may be NULL).  A zero factor is skipped against finite values.
+template <int DK, int DV>
+__global__ __launch_bounds__(NTH) void split_compose_kernel(int H, int nseg, int f, int k,
+                                                            float *Ms, float *Ds, float *M_out,
+                                                            float *D_out) {
+    const int j = blockIdx.x, h = blockIdx.y;
+    const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
+    const int64_t u = (int64_t)f * j + k;
+    float *Ml = Ms + (u * H + h) * mm, *Dl = Ds + (u * H + h) * dd;
+    const float *Me = Ms + ((u - 1) * H + h) * mm, *De = Ds + ((u - 1) * H + h) * dd;
+    const bool last = k == f - 1;
+    float *Mo = last ? (M_out ? M_out + ((int64_t)j * H + h) * mm : nullptr) : Ml;
+    float *Do = last ? D_out + ((int64_t)j * H + h) * dd : Dl;
+    bool zl, ze, bl, be;
+    {
+        Tile<DK * DK> tl, te;
+        tl.load(Ml);
+        te.load(Me);
+        zl = !tl.any_nonzero();
+        ze = !te.any_nonzero();
+        bl = tl.any_nonfinite();
+        be = te.any_nonfinite();
+    }
+    {
+        Tile<DK * DV> tl, te;
+        tl.load(Dl);
+        te.load(De);
+        bl = tl.any_nonfinite() || bl;
+        be = te.any_nonfinite() || be;
+    }
+    const bool need_mm = !((zl && ze) || (zl && !be) || (ze && !bl));
+    const bool need_md = !(zl && !be);
+    Acc<DK, DK> am;
+    Acc<DK, DV> ad;
+    if (need_mm && Mo) mm_acc<DK, DK>(Ml, Me, am, zl ? kZero : kMem, ze ? kZero : kMem);
+    if (need_md) mm_acc<DK, DV>(Ml, De, ad, zl ? kZero : kMem);
+    __syncthreads();   // every operand read precedes the first store
+    if (Mo) {
+        if (need_mm) store_acc<DK, DK>(am, nullptr, Mo);
+        else copy_n<DK * DK>(Mo, nullptr);
+    }
+    if (need_md) store_acc<DK, DV>(ad, Dl, Do);
+    else if (last) copy_n<DK * DV>(Do, Dl);
+}
+
+// Rungs of the sub-packages inside sub-segment k >= 1 (grid (rows, H)):
+// sub_M[r] <- sub_M[r] M_{f j + k - 1}, the map from the segment's start
+// instead of the sub-segment's.
+template <int DK>
+__global__ __launch_bounds__(NTH) void split_rung_m_kernel(int H, int nseg, int f, int k,
+                                                           const int64_t *sb, int interval,
+                                                           const float *Ms, float *sub_M) {
+    const int64_t r = blockIdx.x;
+    const int h = blockIdx.y;
+    const int64_t p = (r + 1) * interval;
+    int u = 0;
+    while (u + 1 < f * nseg && sb[u + 1] < p) ++u;   // p in (sb[u], sb[u+1]]
+    if (u % f != k) return;
+    const int64_t mm = (int64_t)DK * DK;
+    float *L = sub_M + (r * H + h) * mm;
+    const float *R = Ms + ((int64_t)(u - 1) * H + h) * mm;
+    bool zl, zr, bl, br;
+    {
+        Tile<DK * DK> tl, tr;
+        tl.load(L);
+        tr.load(R);
+        zl = !tl.any_nonzero();
+        zr = !tr.any_nonzero();
+        bl = tl.any_nonfinite();
+        br = tr.any_nonfinite();
+    }
+    if ((zl && zr) || (zl && !br)) return;   // stays exactly zero
+    Acc<DK, DK> am;
+    if (!(zr && !bl)) mm_acc<DK, DK>(L, R, am, zl ? kZero : kMem, zr ? kZero : kMem);
+    __syncthreads();
+    if (zr && !bl) copy_n<DK * DK>(L, nullptr);
+    else store_acc<DK, DK>(am, nullptr, L);
+}
+
 // Segment-path checkpoints: grid (rows, H).  Rung row r sits at
 // p = (r+1)*interval inside segment j (seg_start[j] < p <= seg_start[j+1]):
 // states[r] = sub_M[r] S_in[j] + sub_D[r].
@@ -637,6 +744,45 @@ hipError_t launch_ckpt_write(int dk, int dv, int H, int64_t T, const int64_t *se
     if (dk == 128 && dv == 128)
         return ckpt_t<128, 128>(H, T, seg_start, nseg, interval, S_in, sub_M, sub_D, states, s);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_split_bounds(const int64_t *seg_start, int nseg, int f, int64_t *sb,
+                               int32_t *ord, hipStream_t s) {
+    const int n = f * nseg + 1;
+    hipLaunchKernelGGL(split_bounds_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       seg_start, nseg, f, sb, ord);
+    return hipGetLastError();
+}
+
+hipError_t launch_split_compose(int dk, int dv, int H, int nseg, int f, int k, float *Ms,
+                                float *Ds, float *M_out, float *D_out, hipStream_t s) {
+#define KDA_SPLIT_COMPOSE(DK_, DV_)                                                             \
+    if (dk == DK_ && dv == DV_) {                                                               \
+        hipLaunchKernelGGL((split_compose_kernel<DK_, DV_>), dim3(nseg, H), dim3(NTH), 0, s, H,  \
+                           nseg, f, k, Ms, Ds, M_out, D_out);                                   \
+        return hipGetLastError();                                                               \
+    }
+    KDA_SPLIT_COMPOSE(64, 64)
+    KDA_SPLIT_COMPOSE(64, 128)
+    KDA_SPLIT_COMPOSE(128, 64)
+    KDA_SPLIT_COMPOSE(128, 128)
+#undef KDA_SPLIT_COMPOSE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_split_rung_m(int dk, int H, int nseg, int f, int k, const int64_t *sb,
+                               int interval, int64_t rows, const float *Ms, float *sub_M,
+                               hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    if (dk == 64)
+        hipLaunchKernelGGL((split_rung_m_kernel<64>), dim3((unsigned)rows, H), dim3(NTH), 0, s, H,
+                           nseg, f, k, sb, interval, Ms, sub_M);
+    else if (dk == 128)
+        hipLaunchKernelGGL((split_rung_m_kernel<128>), dim3((unsigned)rows, H), dim3(NTH), 0, s, H,
+                           nseg, f, k, sb, interval, Ms, sub_M);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 hipError_t launch_plan(const int64_t *cu_seqlens, int32_t n, int32_t *order, hipStream_t s) {

@@ -20,7 +20,7 @@ KDA_SCAN_SEQUENTIAL, KDA_SCAN_BLELLOCH = 0, 1
 CHUNK = 64
 
 EXPORTS = ("kda_prefill_workspace", "kda_prefill", "kda_prefill_noalloc", "kda_prefill_resume",
-           "kda_segment_package",
+           "kda_segment_package", "kda_segment_package_workspace",
            "kda_segment_scan_workspace", "kda_segment_scan", "kda_output_fixup",
            "kda_output_fixup_ckpt",
            "kda_checkpoint_write", "kda_decode", "kda_short_conv", "kda_conv_halo",
@@ -73,6 +73,7 @@ def _load():
         "kda_segment_package": (ctypes.c_int, [cfgp, P, P, P, P, P, I64, P, I32, P, P, P, ckp,
                                                P, P, P, S, P]),
         "kda_segment_scan_workspace": (S, [cfgp, I32, I32]),
+        "kda_segment_package_workspace": (S, [cfgp, I64, I32]),
         "kda_segment_scan": (ctypes.c_int, [cfgp, I32, P, P, P, P, P, I32, P, S, P]),
         "kda_output_fixup": (ctypes.c_int, [cfgp, P, P, P, P, I64, P, I32, P, P, P, S, P]),
         "kda_output_fixup_ckpt": (ctypes.c_int, [cfgp, P, P, P, P, I64, P, I32, P, P, ckp, P, P,
@@ -310,10 +311,12 @@ def kda_prefill_resume(q, k, v, g, beta, cu_seqlens, pool, read_idx, write_idx, 
 
 
 def kda_segment_package(q, k, v, g, beta, seg_start, *, ckpt_interval=0, scale=1.0,
-                        qk_l2norm=True, want_M=True, want_sub_M=True, stream=None):
+                        qk_l2norm=True, want_M=True, want_sub_M=True, split=True, stream=None):
     """Per-segment packages.  Returns (o_local, M, D, sub_M, sub_D); M and
     sub_M are None when want_M is False (the M launch is then skipped), sub_M
-    also when want_sub_M is False (rungs then from kda_output_fixup_ckpt)."""
+    also when want_sub_M is False (rungs then from kda_output_fixup_ckpt).
+    split: hand the library the workspace that lets it split segments into
+    sub-segments when they would leave compute units idle."""
     T, H, dk, dv, dev = _inputs(q, k, v, g, beta)
     nseg = seg_start.numel() - 1
     _need(seg_start, "seg_start", (nseg + 1,), torch.int64, dev)
@@ -330,11 +333,13 @@ def kda_segment_package(q, k, v, g, beta, seg_start, *, ckpt_interval=0, scale=1
         sub_D = torch.empty((rows, H, dk, dv), dtype=torch.float32, device=dev)
         if rows:
             ckp = ctypes.pointer(kda_ckpt(int(ckpt_interval), None, None))
+    wsb = LIB.kda_segment_package_workspace(ctypes.byref(cfg), T, nseg) if split else 0
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
     st = LIB.kda_segment_package(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(g), _p(beta), T,
                                  _p(seg_start), nseg, _p(o_local), _p(M), _p(D), ckp,
                                  _p(sub_M) if (ckp and sub_M is not None) else None,
                                  _p(sub_D) if ckp else None,
-                                 None, 0, _stream(stream))
+                                 _p(ws), wsb, _stream(stream))
     _check(st, "kda_segment_package")
     return o_local, M, D, sub_M, sub_D
 

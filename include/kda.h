@@ -247,9 +247,19 @@ int kda_prefill_resume(const kda_config *cfg, const void *q, const void *k, cons
  *   (sub_M = NULL skips Pi_p: kda_output_fixup_ckpt needs only sub_D;
  *   sub_M needs M).
  * One kernel launch: the value blocks (o_local, D, sub_D) and, with M, the M
- * blocks after them in the same grid.
- * No workspace is needed (ws may be NULL).
+ * blocks after them in the same grid.  No workspace is needed (ws may be
+ * NULL).  When nseg * H would leave compute units idle, a workspace of at
+ * least kda_segment_package_workspace(cfg, T, nseg) bytes (a nonzero query)
+ * lets the call split every segment into f chunk-aligned sub-segments, run
+ * their packages in one launch, and merge them left to right (sub-segment k
+ * fixed up from the accumulated state of 0..k-1, its rungs included, then
+ * (M, D) composed); the results equal the unsplit call's up to fp32
+ * rounding.
  */
+/* Workspace bytes that let kda_segment_package split its segments (0 when it
+ * would not split them: enough units already, or segments too short). */
+size_t kda_segment_package_workspace(const kda_config *cfg, int64_t T, int32_t nseg);
+
 int kda_segment_package(const kda_config *cfg, const void *q, const void *k, const void *v,
                         const float *g, const float *beta, int64_t T, const int64_t *seg_start,
                         int32_t nseg, void *o_local, float *M, float *D, const kda_ckpt *ckpt,

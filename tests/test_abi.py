@@ -335,3 +335,13 @@ def test_fixup_ckpt_validates():
     assert call(ckpt=ctypes.byref(ok), sub_D=MISALIGNED) == K.KDA_ERR_ALIGN
     assert call(S_in=None) == K.KDA_ERR_ARG
     assert call(nseg=0) == K.KDA_ERR_ARG
+
+
+def test_package_split_workspace_query():
+    """The query is zero when the units already fill the device or the
+    segments are too short to split, and grows with the split otherwise."""
+    c = cfg(H=32)
+    assert K.LIB.kda_segment_package_workspace(ctypes.byref(c), 131072, 16) == 0   # 512 units
+    assert K.LIB.kda_segment_package_workspace(ctypes.byref(c), 16384, 4) > 0      # 128 units
+    assert K.LIB.kda_segment_package_workspace(ctypes.byref(cfg(H=2)), 1300, 5) == 0   # short
+    assert K.LIB.kda_segment_package_workspace(None, 16384, 4) == 0

@@ -936,3 +936,73 @@ def test_fixup_ckpt_equals_checkpoint_write(K, gates, dtype, dk, dv):
     assert_close("rungs, checkpoint write", to_numpy_f64(ck_two), rck, tol)
     assert_close("fused vs two-call rungs", to_numpy_f64(ck_fused), to_numpy_f64(ck_two), tol)
     assert_close("o", to_numpy_f64(o2), ro, OUT_TOL[dtype])
+
+
+# ---------------------------------------------------------------------------
+# Packages of segments split into sub-segments (CUs otherwise idle)
+# ---------------------------------------------------------------------------
+SPLIT_CASES = [
+    # dtype, dk, dv, H, T, seg_start, gates, rung interval
+    ("bf16", 128, 128, 2, 4096, [0, 640, 1984, 2048, 4096], "config", 128),
+    ("bf16", 128, 128, 2, 4096, [0, 640, 1984, 2048, 4096], "long", 128),
+    ("f32", 64, 64, 4, 16384, [0, 8192, 16384], "long", 1024),
+    ("bf16", 64, 128, 2, 8192, [0, 4096, 8192], "config", 512),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}-H{c[3]}-T{c[4]}-{c[6]}")
+def test_package_split_into_subsegments(K, case):
+    """With its workspace, kda_segment_package splits segments whose
+    (segment, head) units would leave compute units idle (2 to 8
+    sub-segments here, one segment of a single chunk), merges the
+    sub-packages, and gives the unsplit call's o_local, M, D and rung
+    sub-packages; each against the oracle too."""
+    import ctypes
+    import torch
+    dtype, dk, dv, H, T, seg, gates, iv = case
+    shift = {} if gates == "config" else dict(gate_shift=-9.0, beta_shift=-6.0)
+    w = make_workload("split-pkg", [T], H, dk, dv, dtype, 5400 + dk + dv + H, s0_std=0.3,
+                      seg_start=seg, **shift)
+    t = to_torch(w)
+    cfg = K.make_config(H, dk, dv, t["q"].dtype)
+    wsb = K.LIB.kda_segment_package_workspace(ctypes.byref(cfg), T, len(seg) - 1)
+    say(f"package split {case}: workspace {wsb} bytes")
+    assert wsb > 0, "the call should split these segments"
+    args = (t["q"], t["k"], t["v"], t["g"], t["beta"], t["seg_start"])
+    sp = K.kda_segment_package(*args, ckpt_interval=iv)
+    un = K.kda_segment_package(*args, ckpt_interval=iv, split=False)
+    sync()
+    tol_o, tol_s = OUT_TOL[dtype], STATE_TOL[dtype]
+    for name, i, tol in (("o_local", 0, tol_o), ("M", 1, tol_s), ("D", 2, tol_s),
+                         ("sub_M", 3, tol_s), ("sub_D", 4, tol_s)):
+        assert_close(f"split vs unsplit {name}", to_numpy_f64(sp[i]), to_numpy_f64(un[i]), tol)
+    q, k, v, g, b = (w.f64(x) for x in ("q", "k", "v", "g", "beta"))
+    rows = T // iv
+    ref_sM = np.zeros((rows, H, dk, dk))
+    ref_sD = np.zeros((rows, H, dk, dv))
+    for j in range(len(seg) - 1):
+        Mr, Dr, olr = oracle.package(q, k, v, g, b, seg[j], seg[j + 1])
+        assert_close(f"M[{j}]", to_numpy_f64(sp[1][j]), Mr, tol_s)
+        assert_close(f"D[{j}]", to_numpy_f64(sp[2][j]), Dr, tol_s)
+        assert_close(f"o_local[{j}]", to_numpy_f64(sp[0][seg[j]:seg[j + 1]]),
+                     olr[seg[j]:seg[j + 1]], tol_o)
+        for p in range((seg[j] // iv + 1) * iv, seg[j + 1] + 1, iv):
+            Mp, Dp, _ = oracle.package(q, k, v, g, b, seg[j], p)
+            ref_sM[p // iv - 1], ref_sD[p // iv - 1] = Mp, Dp
+    # with the configs' gates a rung 512 tokens into a segment has a map below
+    # fp32 range (|Pi_p| ~ 1e-150 in fp64, exactly 0 in fp32): such rungs are
+    # compared in absolute terms against the O(1) states they act on
+    got_sM = to_numpy_f64(sp[3])
+    for r in range(rows):
+        if np.linalg.norm(ref_sM[r]) < 1e-20:
+            assert np.abs(got_sM[r] - ref_sM[r]).max() < 1e-20, f"sub_M row {r}"
+        else:
+            assert_close(f"sub_M row {r}", got_sM[r], ref_sM[r], tol_s)
+    assert_close("sub_D", to_numpy_f64(sp[4]), ref_sD, tol_s)
+    # the whole path through the split packages
+    o, Sf, ck = K.kda_segment_prefill(*args, t["S0"][0].contiguous(), algo=1, ckpt_interval=iv)
+    sync()
+    ro, rS, rck = oracle_full(w, interval=iv)
+    assert_close("o", to_numpy_f64(o), ro, tol_o)
+    assert_close("S_final", to_numpy_f64(Sf), rS[0], tol_s)
+    assert_close("rungs", to_numpy_f64(ck), rck, tol_s)
