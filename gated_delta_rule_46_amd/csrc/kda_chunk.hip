@@ -15,8 +15,9 @@ hipError_t launch_engine_f32_64(int mode, int dv, int nb, const EngineArgs &a, h
 bool engine_supported(bool bf16, int dk, int dv, int nb) {
     const bool dims = (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
     if (bf16) return dims && (nb == 64 || (nb == 128 && dv == 128));
-    // fp32 operands: the hand-off tiles of dk = 128 do not fit in LDS
-    return dims && dk == 64 && nb == 64;
+    // fp32 operands: dk = 128 (whose hand-off tiles do not fit in LDS) runs
+    // the token-recurrent kernel
+    return dims && nb == 64;
 }
 
 int engine_pick_nb(bool bf16, int dk, int dv, int64_t units, int mode) {
@@ -30,6 +31,7 @@ int engine_pick_nb(bool bf16, int dk, int dv, int64_t units, int mode) {
 hipError_t launch_engine(int mode, bool bf16, int dk, int dv, int nb, const EngineArgs &a,
                          hipStream_t s) {
     if (!engine_supported(bf16, dk, dv, nb)) return hipErrorInvalidValue;
+    if (recurrent_supported(bf16, dk, dv)) return launch_recurrent(mode, dk, dv, a, s);
     if (!bf16) return launch_engine_f32_64(mode, dv, nb, a, s);
     if (dk == 128) return dv == 128 ? launch_engine_bf16_128x128(mode, dv, nb, a, s)
                                     : launch_engine_bf16_128x64(mode, dv, nb, a, s);

@@ -54,6 +54,11 @@ struct EngineArgs {
 // error code.  `grid_units` is n_units (the launch covers every unit).
 hipError_t launch_engine(int mode, bool bf16, int dk, int dv, int nb, const EngineArgs &a,
                          hipStream_t stream);
+// Token-recurrent kernel for the shapes whose fp32 hand-off tiles do not fit
+// the chunk engine's LDS (fp32 I/O, dk = 128); same modes and arguments, with
+// a.ncb = dv / 64 and a.ncb_m = dk / 64 (kda_recurrent.hip).
+bool recurrent_supported(bool bf16, int dk, int dv);
+hipError_t launch_recurrent(int mode, int dk, int dv, const EngineArgs &a, hipStream_t stream);
 bool engine_supported(bool bf16, int dk, int dv, int nb);
 int engine_pick_nb(bool bf16, int dk, int dv, int64_t units, int mode);
 

@@ -57,11 +57,13 @@
  *    float32 (the short convolution's windows are in the I/O dtype).
  *    Arithmetic: fp32 accumulation; matrix products on MFMA with bf16
  *    operands for bf16 I/O and fp32 operands for fp32 I/O.
- *  - Supported shapes: dk, dv in {64, 128} (dk == dv or not) for bf16 I/O;
- *    dk == 64 with dv in {64, 128} for fp32 I/O (the fp32 hand-off tiles of a
- *    128-wide key do not fit in the 160 KiB of LDS a workgroup has); chunk ==
- *    64 (kda_decode: dk, dv in {64, 128} for both dtypes; the short
- *    convolution: see there).  Other shapes return KDA_ERR_UNSUPPORTED.
+ *  - Supported shapes: dk, dv in {64, 128} (dk == dv or not) for both I/O
+ *    dtypes; chunk == 64 (the short convolution: see there).  Other shapes
+ *    return KDA_ERR_UNSUPPORTED.  fp32 I/O with dk = 128 runs a
+ *    token-recurrent kernel (one token at a time, the state in registers):
+ *    its fp32 hand-off tiles would not fit in the 160 KiB of LDS the chunked
+ *    engine's workgroup has.  It computes the same results (fp32) far slower
+ *    than the chunked engine.
  *  - Every pointer is a device pointer unless stated.  Tensors (q, k, v, g,
  *    o, states, M, D, workspace) must be 16-byte aligned, beta 4-byte and the
  *    int64 index arrays 8-byte aligned (KDA_ERR_ALIGN otherwise).

@@ -100,9 +100,7 @@ def test_config_validation():
     assert prefill(cfg(dk=96, dv=96)) == K.KDA_ERR_UNSUPPORTED
     assert prefill(cfg(dk=64, dv=256)) == K.KDA_ERR_UNSUPPORTED
     assert prefill(cfg(dk=32, dv=64)) == K.KDA_ERR_UNSUPPORTED
-    # fp32 I/O: dk = 64 only (dv 64 or 128)
-    assert prefill(cfg(dk=128, dv=128, dtype=0)) == K.KDA_ERR_UNSUPPORTED
-    assert prefill(cfg(dk=128, dv=64, dtype=0)) == K.KDA_ERR_UNSUPPORTED
+    assert prefill(cfg(dk=256, dv=128, dtype=0)) == K.KDA_ERR_UNSUPPORTED
 
 
 def test_prefill_argument_checks():

@@ -277,6 +277,20 @@ def test_long_memory_fp32_d64(K, segmentation):
     assert norms.min() > 0.1
 
 
+def test_long_memory_fp32_d128(K):
+    """fp32 I/O with d = 128 (the token-recurrent kernel), 2 heads, long-memory
+    gates on the 16,384-token workload's 4 x 4096 segmentation, packages
+    split into sub-segments and merged."""
+    w = make_workload("long-f32-d128", [16384], 2, 128, 128, "f32", 4810, s0_std=0.5,
+                      seg_start=np.arange(0, 16385, 4096), **LONG)
+    say("long memory fp32 d=128 H=2 T=16384 segments 4x4096 algo=1")
+    r, worst = segment_parity(K, w, range(2), algo=1, interval=2048, check_packages=True)
+    M = to_numpy_f64(r["M"])
+    norms = np.linalg.norm(M.reshape(M.shape[0], M.shape[1], -1), axis=-1)
+    say(f"  |M|_F per segment: min {norms.min():.3f} max {norms.max():.3f}")
+    assert norms.min() > 0.1
+
+
 @pytest.mark.parametrize("segmentation", ["4x4096", "16 leveled"])
 def test_long_memory_bf16_d128(K, segmentation):
     """bf16 I/O, d = 128, 32 heads (the workloads' shape), long-memory gates:

@@ -830,7 +830,8 @@ def test_checkpoint_stream_ordering(K):
 # ---------------------------------------------------------------------------
 # Head dims dk != dv
 # ---------------------------------------------------------------------------
-SHAPES = [("bf16", 64, 128), ("bf16", 128, 64), ("f32", 64, 128)]
+SHAPES = [("bf16", 64, 128), ("bf16", 128, 64), ("f32", 64, 128), ("f32", 128, 128),
+          ("f32", 128, 64)]
 
 
 @pytest.mark.parametrize("dtype,dk,dv", SHAPES)
@@ -904,7 +905,8 @@ def test_single_sequence_split_dk_ne_dv(K, dtype, dk, dv):
 # Fix-up writing the checkpoint rungs (one launch)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("gates", ["config", "long"])
-@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 128, 128), ("f32", 64, 64), ("bf16", 64, 128)])
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 128, 128), ("f32", 64, 64), ("bf16", 64, 128),
+                                         ("f32", 128, 128)])
 def test_fixup_ckpt_equals_checkpoint_write(K, gates, dtype, dk, dv):
     """kda_output_fixup_ckpt leaves the same outputs as kda_output_fixup (bit
     for bit) and writes the rungs that kda_checkpoint_write forms from the
@@ -947,6 +949,7 @@ SPLIT_CASES = [
     ("bf16", 128, 128, 2, 4096, [0, 640, 1984, 2048, 4096], "long", 128),
     ("f32", 64, 64, 4, 16384, [0, 8192, 16384], "long", 1024),
     ("bf16", 64, 128, 2, 8192, [0, 4096, 8192], "config", 512),
+    ("f32", 128, 128, 2, 4096, [0, 1536, 4096], "long", 512),
 ]
 
 
