@@ -8,24 +8,26 @@
 // (package / fix-up).  The waves split into two roles that run concurrently:
 //
 //   producers (waves 0-3, one per 16-row block b of the chunk) prepare chunk
-//     c+1: loads (prefetched one chunk ahead), L2 norms, in-block cumulative
-//     log2-decay, exponentials and the Gram matrices A and P on MFMA;
+//     c+1: loads of q, k, g, beta (prefetched one chunk ahead), L2 norms,
+//     in-block cumulative log2-decay, exponentials, the Gram matrices A and P
+//     and the diagonal inverses T_bb on the matrix cores;
 //   consumers (waves 4-7) own a quarter of the state's columns each (fp32 MFMA
-//     accumulators) and apply chunk c:
+//     accumulators), read their value columns of V themselves, and apply
+//     chunk c:
 //         U = (I + A)^-1 (beta V - R_k S)       R_k = beta K*Gam
 //         O = (Q*Gam) S + P U,   S <- Diag(gamma_C) S + Kbar^T U.
 //
 // Two workgroup barriers per chunk.  Between the second barrier and the first
-// the consumers apply chunk c (reading every hand-off tile) while the
-// producers do all the work of chunk c+1 that only needs their own block:
-// norms, decay scan, exponentials and diagonal Gram blocks.  Between the
-// first barrier and the second the producers combine the block totals into
-// the per-channel factors, write the hand-off tiles and the adjacent
-// off-diagonal Gram blocks (b, b-1), while consumers 0-2 form the three
-// farther blocks (3,0), (3,1), (2,0), consumer 3 the diagonal inverses
-// T_bb = (I + A_bb)^-1, and all of them store checkpoint rungs and run the
-// zero test.  Every hand-off tile has a single copy (T_bb keeps two, by chunk
-// parity).
+// the consumers apply chunk c while the producers prepare all of chunk c+1:
+// norms, decay scan and block totals; then, once the four producers have
+// published their totals (a counter in LDS), the per-channel factors, the
+// hand-off tiles already rescaled to the chunk start, the diagonal Gram
+// blocks, T_bb = (I + A_bb)^-1 on the fp32 matrix core and, after a second
+// counter, the off-diagonal blocks.  Every tile written in that phase (-R_k,
+// Kbar^T, P, -A, T_bb) has two copies, by chunk parity.  Between the first
+// barrier and the second the producers only copy the single-copy tiles (Qbar,
+// beta, gamma; -R_k where LDS holds one copy only) from registers while the
+// consumers store checkpoint rungs and run the zero test.
 //
 // Numerical scheme: one reference point per 16-row block.  The diagonal block
 // uses the block start (lhs factor <= 1, rhs factor <= e^{span of 16 tokens}),
@@ -39,6 +41,8 @@
 // form of the delta rule).
 
 #pragma once
+
+#include <type_traits>
 
 #include "kda_internal.h"
 #include "kda_mfma.h"
@@ -62,7 +66,7 @@ __device__ __forceinline__ int opaque(int x) {
 // Compact storage of the six strictly-lower 16x16 blocks (b, a), a < b.
 __host__ __device__ constexpr int aoff_idx(int b, int a) { return b * (b - 1) / 2 + a; }
 
-template <int DK, int NB, bool BF> struct Lds {
+template <int DK, int NB, bool BF, int RKN_> struct LdsL {
     using T = typename Ops<BF>::T;
     // Row padding.  Tiles that the consumers read as 8-byte fragments (two
     // per operand) keep a row stride of 2 mod 4 dwords in bf16: gfx950 serves
@@ -78,41 +82,102 @@ template <int DK, int NB, bool BF> struct Lds {
     static constexpr int LDQ = DK + PAD;        // [64][DK] row-major tiles
     static constexpr int LDK = 64 + PAD;        // [DK][64] transposed Kbar
     static constexpr int LDP = 64 + PAD;        // [64][64] P
-    static constexpr int LDV = NB + PAD;        // [64][NB] beta*V
     static constexpr int LDT = 16 + PAD;        // 16x16 blocks
     static constexpr int LDR = DK + PADR;       // producer-side [rows][DK] tiles
-    static constexpr int LDAD = 20;             // fp32 16x16 blocks
-    static constexpr int o_flag = 0;                                  // int[16]
-    static constexpr int o_gam = 64;                                  // f32 [DK]
+    static constexpr int o_flag = 0;                                  // int[16]: consumer zero flags
+    static constexpr int o_sync = 64;                                 // int[8]: producer counters
+    static constexpr int o_gam = 96;                                  // f32 [DK]
     static constexpr int o_tot = o_gam + DK * 4;                      // f32 [4][DK]
     static constexpr int o_fac = o_tot + 4 * DK * 4;                  // f32 [4][4][DK]
     static constexpr int o_qbar = o_fac + 16 * DK * 4;                // hand-off: Q Gam
-    static constexpr int o_rk = o_qbar + 64 * LDQ * ES;               // hand-off: -R_k
-    static constexpr int o_kbt = o_rk + 64 * LDQ * ES;                // hand-off: Kbar^T
-    static constexpr int o_p = o_kbt + DK * LDK * ES;                 // hand-off: P
-    static constexpr int o_bv = o_p + 64 * LDP * ES;                  // hand-off: beta V
-    static constexpr int o_aoff = o_bv + 64 * LDV * ES;               // hand-off: -A blocks
-    static constexpr int o_td = o_aoff + 6 * 16 * LDT * ES;           // hand-off: T_bb [2][4]
-    static constexpr int o_ad = o_td + 2 * 4 * 16 * LDT * ES;         // producer scratch
-    static constexpr int o_ro = o_ad + 4 * 16 * LDAD * 4;             // rhs of blocks 0-2
-    static constexpr int o_lk = o_ro + 48 * LDR * ES;                 // lhs (K) of blocks 2, 3
-    static constexpr int o_lq = o_lk + 32 * LDR * ES;                 // lhs (Q) of blocks 2, 3
-    static constexpr int o_cf = o_lq + 32 * LDR * ES;                 // f32 [3][DK] rescales
-    static constexpr int size = o_cf + 3 * DK * 4;
-    static_assert(o_qbar % 16 == 0 && o_rk % 16 == 0 && o_kbt % 16 == 0 && o_p % 16 == 0 &&
-                  o_bv % 16 == 0 && o_aoff % 16 == 0 && o_td % 16 == 0 && o_ad % 16 == 0 &&
-                  o_ro % 16 == 0 && o_lk % 16 == 0 && o_lq % 16 == 0 && o_cf % 16 == 0,
-                  "LDS alignment");
+    static constexpr int RKN = RKN_;
+    static constexpr int o_rk = o_qbar + 64 * LDQ * ES;               // hand-off: -R_k [RKN]
+    static constexpr int o_kbt = o_rk + RKN * 64 * LDQ * ES;          // hand-off: Kbar^T [2]
+    static constexpr int o_beta = o_kbt + 2 * DK * LDK * ES;          // hand-off: beta [64] f32
+    static constexpr int o_p = o_beta + 64 * 4;                       // hand-off: P [2]
+    static constexpr int o_aoff = o_p + 2 * 64 * LDP * ES;            // hand-off: -A blocks [2]
+    static constexpr int o_td = o_aoff + 2 * 6 * 16 * LDT * ES;       // hand-off: T_bb [2][4]
+    static constexpr int o_ro = o_td + 2 * 4 * 16 * LDT * ES;         // rhs of blocks 0-2
+    static constexpr int o_lk = o_ro + 48 * LDR * ES;                 // lhs (K) of block 2
+    static constexpr int o_lq = o_lk + 16 * LDR * ES;                 // lhs (Q) of block 2
+    static constexpr int size = o_lq + 16 * LDR * ES;
+    static constexpr int P_BUF = 64 * LDP;                            // elements per buffer
+    static constexpr int AOFF_BUF = 6 * 16 * LDT;
+    static constexpr int TD_BUF = 4 * 16 * LDT;
+    static constexpr int KBT_BUF = DK * LDK;
+    static constexpr int RK_BUF = 64 * LDQ;
+    static_assert(o_gam % 16 == 0 && o_qbar % 16 == 0 && o_rk % 16 == 0 && o_kbt % 16 == 0 &&
+                  o_p % 16 == 0 && o_beta % 16 == 0 && o_aoff % 16 == 0 && o_td % 16 == 0 &&
+                  o_ro % 16 == 0 && o_lk % 16 == 0 && o_lq % 16 == 0 && (P_BUF * ES) % 16 == 0 &&
+                  (AOFF_BUF * ES) % 16 == 0 && (TD_BUF * ES) % 16 == 0, "LDS alignment");
     static_assert((LDQ * ES) % 8 == 0 && (LDK * ES) % 8 == 0 && (LDP * ES) % 8 == 0 &&
-                  (LDV * ES) % 8 == 0 && (LDT * ES) % 8 == 0 && (LDR * ES) % 16 == 0,
+                  (LDT * ES) % 8 == 0 && (LDR * ES) % 16 == 0,
                   "row alignment of 8-byte and 16-byte LDS accesses");
-    static_assert(size <= 160 * 1024, "LDS budget");
 };
+// -R_k is double-buffered (written in the own phase) where the LDS budget
+// allows it, else single (written from registers between the barriers).
+template <int DK, int NB, bool BF>
+using Lds = typename std::conditional<(LdsL<DK, NB, BF, 2>::size <= 160 * 1024), LdsL<DK, NB, BF, 2>,
+                                      LdsL<DK, NB, BF, 1>>::type;
+
+// Producer counters in LDS.  A producer publishes chunk c once its LDS writes
+// of that chunk are done (LDS operations of a wave complete in order, so a
+// wait on the LDS counter suffices; no wait on its outstanding global loads),
+// and waits until the other producers have published chunk c.  All waves of a
+// workgroup are resident together, so the waits end; the wait is bounded all
+// the same (2^16 polls), so that a broken protocol shows as wrong values
+// rather than as a hang.
+typedef __attribute__((address_space(3))) int lds_int;
+__device__ __forceinline__ void publish(int *cnt, int c) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if ((threadIdx.x & 63) == 0)
+        __hip_atomic_store((lds_int *)cnt, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void wait_all4(const int *cnt, int c) {
+    for (int it = 0; it < (1 << 16); ++it) {
+        lds_int *p = (lds_int *)cnt;
+        const int a = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        const int b = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        const int d = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(p + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        const int e = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(p + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if (a >= c && b >= c && d >= c && e >= c) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+}
+
+// T = (I + N)^-1 for a strictly lower 16x16 N, from N and N^T in the MFMA
+// accumulator layout (lane (n, g) element i: row 4g+i, column n), as
+// (I - N)(I + N^2)(I + N^4)(I + N^8), exact for N^16 = 0, on the fp32 matrix
+// core: X1 = I + N^4 + N^8 + N^4 N^8, X2 = X1 + N^2 X1, T = X2 - N X2.
+// mul(X^T, Y) = X Y: with k = 4g + s, the B operand of step s is element s
+// of Y's accumulator and the A operand element s of X^T's.
+__device__ __forceinline__ f32x4 mul_acc(f32x4 xt, f32x4 y) {
+    f32x4 r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) r = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[s], y[s], r, 0, 0, 0);
+    return r;
+}
+__device__ __forceinline__ f32x4 inv_unit_lower(f32x4 N, f32x4 Nt, int n, int g) {
+    f32x4 I;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) I[i] = (4 * g + i == n) ? 1.f : 0.f;
+    const f32x4 N2 = mul_acc(Nt, N), N2t = mul_acc(N, Nt);
+    const f32x4 N4 = mul_acc(N2t, N2), N4t = mul_acc(N2, N2t);
+    const f32x4 N8 = mul_acc(N4t, N4);
+    const f32x4 X1 = I + N4 + N8 + mul_acc(N4t, N8);
+    const f32x4 X2 = X1 + mul_acc(N2t, X1);
+    return X2 - mul_acc(Nt, X2);
+}
 
 // Raw rows of one chunk held in registers between the prefetch and its use.
-template <bool BF, int KS, int VS> struct Raw {
+template <bool BF, int KS> struct Raw {
     static constexpr int W8 = BF ? 4 : 8;      // 32-bit words per 8 elements
-    uint32_t q[KS * W8], k[KS * W8], g[KS * 8], v[VS * W8];
+    uint32_t q[KS * W8], k[KS * W8], g[KS * 8];
     float b;
 };
 
@@ -206,6 +271,12 @@ __device__ __forceinline__ void copy_state_block(float *dst, const float *src, i
     }
 }
 
+// Some consumer wave flagged a nonzero state (four consumer waves).
+__device__ __forceinline__ bool s_flag_any(const unsigned char *smem) {
+    const int *f = (const int *)smem;
+    return (f[0] | f[1] | f[2] | f[3]) != 0;
+}
+
 template <int MODE, bool MB> struct Roles {
     static constexpr bool HAS_V = (MODE != kModeFixup) && !MB;   // beta V enters U
     static constexpr bool HAS_O = !MB;                           // outputs are produced
@@ -222,13 +293,13 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
     using O = Ops<BF>;
     using T = typename O::T;
     using F8 = typename O::F8;
+    using F4 = typename O::F4;
     using L = Lds<DK, NB, BF>;
     using R = Roles<MODE, MB>;
     constexpr int KS = DK / 32;      // 32-channel steps of a row
-    constexpr int VS = NB / 32;      // 32-column steps of the value block
     constexpr int W8 = BF ? 4 : 8;
 
-    int *s_flag = (int *)(smem + L::o_flag);
+    int *s_sync = (int *)(smem + L::o_sync);
     float *s_gam = (float *)(smem + L::o_gam);
     float *s_tot = (float *)(smem + L::o_tot);
     float *s_fac = (float *)(smem + L::o_fac);
@@ -236,10 +307,9 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
     T *s_rk = (T *)(smem + L::o_rk);
     T *s_kbt = (T *)(smem + L::o_kbt);
     T *s_p = (T *)(smem + L::o_p);
-    T *s_bv = (T *)(smem + L::o_bv);
+    float *s_beta = (float *)(smem + L::o_beta);
     T *s_aoff = (T *)(smem + L::o_aoff);
     T *s_td = (T *)(smem + L::o_td);
-    float *s_ad = (float *)(smem + L::o_ad);
     T *s_ro = (T *)(smem + L::o_ro);
     T *s_lk = (T *)(smem + L::o_lk);
     T *s_lq = (T *)(smem + L::o_lq);
@@ -247,13 +317,16 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
     const int lane = threadIdx.x & 63;
     const int H = a.H;
 
-    // Blocks of P right of the diagonal are zero in every chunk.
+    // Blocks of P right of the diagonal are zero in every chunk (both buffers).
     if (R::HAS_O) {
         const int m = lane & 15, gq = lane >> 4;
 #pragma unroll
-        for (int a2 = B + 1; a2 < 4; ++a2)
+        for (int pb = 0; pb < 2; ++pb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s_p[(16 * B + 4 * gq + i) * L::LDP + 16 * a2 + m] = (T)0.f;
+            for (int a2 = B + 1; a2 < 4; ++a2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    s_p[pb * L::P_BUF + (16 * B + 4 * gq + i) * L::LDP + 16 * a2 + m] = (T)0.f;
     }
     // Identity selectors: an MFMA of a row-layout fragment with isel[hh]
     // returns channels 16hh..16hh+15 of the 32-channel step transposed.
@@ -269,7 +342,7 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
         }
     }
 
-    Raw<BF, KS, VS> raw;
+    Raw<BF, KS> raw;
     bool raw_valid = false;
     int64_t ld_tok = t0;
     // Rows of chunk c.  A row past the end of the unit is read from the unit's
@@ -298,24 +371,54 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
             for (int kk = 0; kk < KS; ++kk) ld_words<BF>(a.q, base + 32 * kk + 8 * gq, &raw.q[W8 * kk]);
         }
     };
-    auto issue_v = [&]() {
-        const int gq = opaque(lane) >> 4;
-        const int64_t vb = (ld_tok * H + h) * DV + cbase;
+    // Fragments of chunk c kept in registers from the own phase to the
+    // hand-off phase: lhs of the Gram blocks (block-start reference), the
+    // single-buffered hand-off tiles already rescaled to the chunk start, and
+    // e^{G_C} of this lane's channels (block 0).
+    F8 lhsK[KS], lhsQ[KS], qbf[KS], rkf[L::RKN == 1 ? KS : 1];
+    float gamr[DK / 64], btc = 0.f;
+
+    // An off-diagonal block (B2, A2) of A and P: lhs rows of block B2 (lk,
+    // lq, referenced to the end of block B2-1) times rhs rows of block A2
+    // (s_ro, referenced to the end of block A2), times e^{rho_{B2-1} -
+    // rho_{A2}} per channel when the blocks are not adjacent (cf != null).
+    auto offdiag = [&](int buf, int B2, int A2, const F8 *lk, const F8 *lq, const T *lkp,
+                       const T *lqp, const float *cf) {
+        const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
+        f32x4 Ao = {0.f, 0.f, 0.f, 0.f}, P_ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < VS; ++kk) ld_words<BF>(a.v, vb + 32 * kk + 8 * gq, &raw.v[W8 * kk]);
+        for (int kk = 0; kk < KS; ++kk) {
+            const int c0 = 32 * kk + 8 * gq;
+            F8 Bf = O::ld8(s_ro + (16 * A2 + m) * L::LDR + c0);
+            if (cf) {
+                float x[8];
+                O::unpack8(Bf, x);
+                const f32x4 f0 = *(const f32x4 *)(cf + c0), f1 = *(const f32x4 *)(cf + c0 + 4);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) { x[jj] *= f0[jj]; x[jj + 4] *= f1[jj]; }
+                Bf = O::cvt8(x);
+            }
+            const F8 Kf = lk ? lk[kk] : O::ld8(lkp + m * L::LDR + c0);
+            Ao = O::mma32(Ao, Kf, Bf);
+            if (R::HAS_O) {
+                const F8 Qf = lq ? lq[kk] : O::ld8(lqp + m * L::LDR + c0);
+                P_ = O::mma32(P_, Qf, Bf);
+            }
+        }
+        T *dst = s_aoff + buf * L::AOFF_BUF + aoff_idx(B2, A2) * 16 * L::LDT;
+        T *pd = s_p + buf * L::P_BUF;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            dst[(4 * gq + i) * L::LDT + m] = (T)(-Ao[i]);
+            if (R::HAS_O) pd[(16 * B2 + 4 * gq + i) * L::LDP + 16 * A2 + m] = (T)P_[i];
+        }
     };
 
-    float bt = 0.f;
-    F8 lhsK[KS], rhsD[KS], lhsQ[KS], bvp[VS];
-    f32x4 Pd;
-
-    // Own-block work of chunk c (runs while the consumers apply chunk c-1):
-    // decay scan and block totals, norms, two exponentials per element, the
-    // Gram fragments, the rhs tile R_o of later blocks, the diagonal Gram
-    // blocks and T_bb.  Issues the loads of chunk c+1 as registers free up.
+    // All the work of chunk c (runs while the consumers apply chunk c-1).
     auto phase_own = [&](int c) {
         const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
         const int prow = 16 * B + m;
+        const int buf = c & 1;
         const bool more = c + 1 < nchunks;
         const bool partial = t0 + (int64_t)(c + 1) * kChunk > t1;
         const float vm = raw_valid ? 1.f : 0.f;
@@ -326,9 +429,18 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
 #pragma unroll
             for (int e = 0; e < KS * 8; ++e) gl[e] *= vm;
         }
-        bt = raw.b * vm;
+        const float bt = raw.b * vm;
 #pragma unroll
         for (int e = 0; e < KS * 8; ++e) gl[e] = scan16(gl[e] * kLog2e);
+        if (m == 15) {   // block totals, published for the other producers
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                float *d = s_tot + B * DK + 32 * kk + 8 * gq;
+                *(f32x4 *)d = f32x4{gl[8 * kk], gl[8 * kk + 1], gl[8 * kk + 2], gl[8 * kk + 3]};
+                *(f32x4 *)(d + 4) = f32x4{gl[8 * kk + 4], gl[8 * kk + 5], gl[8 * kk + 6], gl[8 * kk + 7]};
+            }
+        }
+        publish(s_sync + B, c);
         float fk, fq = 0.f;
         if constexpr (BF) {
             // |row|^2 of the raw bf16 rows as the diagonal of their 16x16 Gram
@@ -372,42 +484,38 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
                 fq = (a.l2norm ? a.scale * rsqrtf(sq + kEps) : a.scale) * vm;
             }
         }
-        if (R::HAS_V) {
-#pragma unroll
-            for (int kk = 0; kk < VS; ++kk) {
-                float x[8];
-                unpack_words<BF>(&raw.v[W8 * kk], x);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] *= bt;
-                bvp[kk] = O::cvt8(x);
-            }
-        }
+        btc = bt;
         if (more) {
             set_rows(c + 1);
             issue_g();
-            if (R::HAS_V) issue_v();
         }
-        if (m == 15) {
+        // Per-channel factors of block B (log2 domain, all <= 1); rho_a is the
+        // decay at the end of block a, G_C the chunk's:
+        //   [0] e^{tot_B} (rhs rows of later blocks; block 3: e^{tot_1+tot_2})
+        //   [1] e^{rho_{B-1}} (Qbar, R_k)   [2] e^{G_C - rho_{B-1}} (Kbar)
+        //   [3] block 0: e^{tot_1} (block (2,0)); block 3: e^{tot_2} (block (3,1))
+        wait_all4(s_sync, c);
+        float *fac = s_fac + B * 4 * DK;
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                float *d = s_tot + B * DK + 32 * kk + 8 * gq;
-                *(f32x4 *)d = f32x4{gl[8 * kk], gl[8 * kk + 1], gl[8 * kk + 2], gl[8 * kk + 3]};
-                *(f32x4 *)(d + 4) = f32x4{gl[8 * kk + 4], gl[8 * kk + 5], gl[8 * kk + 6], gl[8 * kk + 7]};
-            }
+        for (int i = 0; i < DK / 64; ++i) {
+            const int ch = opaque(lane) + 64 * i;
+            const float u0 = s_tot[ch], u1 = s_tot[DK + ch], u2 = s_tot[2 * DK + ch], u3 = s_tot[3 * DK + ch];
+            const float rho = (B >= 1 ? u0 : 0.f) + (B >= 2 ? u1 : 0.f) + (B >= 3 ? u2 : 0.f);
+            const float gc = u0 + u1 + u2 + u3;
+            fac[ch] = ex2(B == 0 ? u0 : B == 1 ? u1 : B == 2 ? u2 : u1 + u2);
+            if (B > 0) fac[DK + ch] = ex2(rho);
+            fac[2 * DK + ch] = ex2(gc - rho);
+            if (B == 0) fac[3 * DK + ch] = ex2(u1);
+            if (B == 3) fac[3 * DK + ch] = ex2(u2);
+            if (B == 0) gamr[i] = ex2(gc);
         }
-        float *fown = s_fac + B * 4 * DK;   // e^{tot_B}: rhs of later blocks
-        if (B < 3) {
-            wave_sync_lds();
-            for (int ch = opaque(lane); ch < DK; ch += 64) fown[ch] = ex2(s_tot[B * DK + ch]);
-            wave_sync_lds();
-        }
+        wave_sync_lds();
         const float fkb = fk * bt;
-        f32x4 Ad = {0.f, 0.f, 0.f, 0.f};
-        Pd = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 Ad = {0.f, 0.f, 0.f, 0.f}, Adt = {0.f, 0.f, 0.f, 0.f}, Pd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
             const int c0 = 32 * kk + 8 * gq;
-            float e1[8], e2[8], kx[8], lk[8], rd[8];
+            float e1[8], e2[8], kx[8], lk[8], rd[8], t8[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) { e1[j] = ex2(gl[8 * kk + j]); e2[j] = ex2(-gl[8 * kk + j]); }
             unpack_words<BF>(&raw.k[W8 * kk], kx);
@@ -417,13 +525,40 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
                 rd[j] = kx[j] * fk * e2[j];
             }
             lhsK[kk] = O::cvt8(lk);
-            rhsD[kk] = O::cvt8(rd);
-            if (B < 3) {
-                const f32x4 f0 = *(const f32x4 *)(fown + c0), f1 = *(const f32x4 *)(fown + c0 + 4);
-                float t8[8];
+            const F8 rhsD = O::cvt8(rd);
+            if (B < 3) {   // rhs rows of later blocks, referenced to the end of block B
+                const f32x4 f0 = *(const f32x4 *)(fac + c0), f1 = *(const f32x4 *)(fac + c0 + 4);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) { t8[j] = rd[j] * f0[j]; t8[j + 4] = rd[j + 4] * f1[j]; }
                 O::st8(s_ro + prow * L::LDR + c0, t8);
+            }
+            {   // Kbar = rd * e^{G_C - rho_{B-1}}, transposed through the matrix core
+                const f32x4 f0 = *(const f32x4 *)(fac + 2 * DK + c0), f1 = *(const f32x4 *)(fac + 2 * DK + c0 + 4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) { t8[j] = rd[j] * f0[j]; t8[j + 4] = rd[j + 4] * f1[j]; }
+                const F8 kbf = O::cvt8(t8);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    O::st4(s_kbt + buf * L::KBT_BUF + (32 * kk + 16 * hh + m) * L::LDK + 16 * B + 4 * gq,
+                           O::mma32(f32x4{0.f, 0.f, 0.f, 0.f}, kbf, isel[hh]));
+            }
+            float f0r[8];   // e^{rho_{B-1}}
+            if (B > 0) {
+                const f32x4 f0 = *(const f32x4 *)(fac + DK + c0), f1 = *(const f32x4 *)(fac + DK + c0 + 4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) { f0r[j] = f0[j]; f0r[j + 4] = f1[j]; }
+            }
+            {   // -R_k: -lk rescaled to the chunk start
+                F8 r;
+                if (B == 0) {
+                    r = O::neg(lhsK[kk]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) t8[j] = -(lk[j] * f0r[j]);
+                    r = O::cvt8(t8);
+                }
+                if constexpr (L::RKN == 2) O::stf_h(s_rk + buf * L::RK_BUF + prow * L::LDQ + c0, r);
+                else rkf[kk] = r;
             }
             if (R::HAS_O) {
                 float qx[8], lq[8];
@@ -431,106 +566,75 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
 #pragma unroll
                 for (int j = 0; j < 8; ++j) lq[j] = qx[j] * fq * e1[j];
                 lhsQ[kk] = O::cvt8(lq);
-                Pd = O::mma32(Pd, lhsQ[kk], rhsD[kk]);
-                if (B >= 2) O::stf(s_lq + (prow - 32) * L::LDR + c0, lhsQ[kk]);
+                if (B == 0) {
+                    qbf[kk] = lhsQ[kk];
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) t8[j] = lq[j] * f0r[j];
+                    qbf[kk] = O::cvt8(t8);
+                }
+                Pd = O::mma32(Pd, lhsQ[kk], rhsD);
+                if (B == 2) O::stf(s_lq + m * L::LDR + c0, lhsQ[kk]);
             }
-            // the far off-diagonal blocks of rows 32..63 are formed by consumer waves
-            if (B >= 2) O::stf(s_lk + (prow - 32) * L::LDR + c0, lhsK[kk]);
-            Ad = O::mma32(Ad, lhsK[kk], rhsD[kk]);
+            if (B == 2) O::stf(s_lk + m * L::LDR + c0, lhsK[kk]);
+            Ad = O::mma32(Ad, lhsK[kk], rhsD);
+            Adt = O::mma32(Adt, rhsD, lhsK[kk]);
             // one 32-channel step at a time keeps the fp32 temporaries short-lived
             __builtin_amdgcn_sched_barrier(0);
         }
         if (more) issue_kq();
+        publish(s_sync + 4 + B, c);   // s_ro (and block 2's lhs rows) written
 
-        // A_bb for the substitution (consumer 3 forms T_bb between the barriers)
-        float *ad = s_ad + B * 16 * L::LDAD;
+        // T_bb = (I + A_bb)^-1 from the strictly lower part of A_bb
+        {
+            f32x4 N, Nt;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ad[(4 * gq + i) * L::LDAD + m] = Ad[i];
+            for (int i = 0; i < 4; ++i) {
+                N[i] = (m < 4 * gq + i) ? Ad[i] : 0.f;
+                Nt[i] = (4 * gq + i < m) ? Adt[i] : 0.f;
+            }
+            const f32x4 Tb = inv_unit_lower(N, Nt, m, gq);
+            T *td = s_td + buf * L::TD_BUF + B * 16 * L::LDT;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) td[(4 * gq + i) * L::LDT + m] = (T)Tb[i];
+        }
+        if (R::HAS_O) {   // diagonal block of P (lower triangle incl. the diagonal)
+            T *pd = s_p + buf * L::P_BUF;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                pd[(16 * B + 4 * gq + i) * L::LDP + 16 * B + m] = (T)((m <= 4 * gq + i) ? Pd[i] : 0.f);
+        }
+        wait_all4(s_sync + 4, c);
+        // Off-diagonal blocks: (B, B-1) needs no rescale (the rhs rows of
+        // block B-1 are referenced to its end, where block B's lhs starts);
+        // block 0 also forms (2,0) from block 2's lhs rows, block 3 also
+        // (3,0) and (3,1).
+        if (B >= 1) offdiag(buf, B, B - 1, lhsK, lhsQ, nullptr, nullptr, nullptr);
+        if (B == 0) offdiag(buf, 2, 0, nullptr, nullptr, s_lk, s_lq, fac + 3 * DK);
+        if (B == 3) {
+            offdiag(buf, 3, 0, lhsK, lhsQ, nullptr, nullptr, fac);
+            offdiag(buf, 3, 1, lhsK, lhsQ, nullptr, nullptr, fac + 3 * DK);
+        }
     };
 
-    // Cross-block work of chunk c (runs while the consumers store rungs):
-    // per-channel factors from the four block totals, the hand-off tiles and
-    // the off-diagonal Gram blocks (B, a2), a2 < B.
+    // Hand-off of chunk c (between the barriers, while the consumers store
+    // rungs): the single-buffered tiles, from registers.
     auto phase_cross = [&]() {
         const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
         const int prow = 16 * B + m;
-        // Factors of block B (log2 domain, all <= 1), rho_a = decay at the end
-        // of block a:  [0] e^{rho_{B-1}}   (Qbar, R_k)
-        //              [1] e^{G_C - rho_{B-1}}   (Kbar)
-        float *fac = s_fac + B * 4 * DK;
-        for (int ch = opaque(lane); ch < DK; ch += 64) {
-            const float u0 = s_tot[ch], u1 = s_tot[DK + ch], u2 = s_tot[2 * DK + ch], u3 = s_tot[3 * DK + ch];
-            const float rho = (B >= 1 ? u0 : 0.f) + (B >= 2 ? u1 : 0.f) + (B >= 3 ? u2 : 0.f);
-            const float gc = u0 + u1 + u2 + u3;
-            if (B > 0) fac[ch] = ex2(rho);
-            fac[DK + ch] = ex2(gc - rho);
-            if (B == 0) s_gam[ch] = ex2(gc);
-        }
-        wave_sync_lds();
-        if (R::HAS_V) {
+        if (B == 0) {
 #pragma unroll
-            for (int kk = 0; kk < VS; ++kk) O::stf_h(s_bv + prow * L::LDV + 32 * kk + 8 * gq, bvp[kk]);
+            for (int i = 0; i < DK / 64; ++i) s_gam[opaque(lane) + 64 * i] = gamr[i];
         }
         if (R::HAS_O) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                s_p[(16 * B + 4 * gq + i) * L::LDP + 16 * B + m] = (T)((m <= 4 * gq + i) ? Pd[i] : 0.f);
+            for (int kk = 0; kk < KS; ++kk) O::stf_h(s_qbar + prow * L::LDQ + 32 * kk + 8 * gq, qbf[kk]);
         }
+        if constexpr (L::RKN == 1) {
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            const int c0 = 32 * kk + 8 * gq;
-            {   // Kbar = rd * e^{G_C - rho_{B-1}}, stored transposed via two MFMAs
-                float rd[8], kb[8];
-                O::unpack8(rhsD[kk], rd);
-                const f32x4 f0 = *(const f32x4 *)(fac + DK + c0), f1 = *(const f32x4 *)(fac + DK + c0 + 4);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) { kb[j] = rd[j] * f0[j]; kb[j + 4] = rd[j + 4] * f1[j]; }
-                const F8 kbf = O::cvt8(kb);
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const f32x4 tr = O::mma32(f32x4{0.f, 0.f, 0.f, 0.f}, kbf, isel[hh]);
-                    O::st4(s_kbt + (32 * kk + 16 * hh + m) * L::LDK + 16 * B + 4 * gq, tr);
-                }
-            }
-            if (B == 0) {   // block 0 is referenced to the chunk start already
-                O::stf_h(s_rk + prow * L::LDQ + c0, O::neg(lhsK[kk]));
-                if (R::HAS_O) O::stf_h(s_qbar + prow * L::LDQ + c0, lhsQ[kk]);
-            } else {
-                const f32x4 f0 = *(const f32x4 *)(fac + c0), f1 = *(const f32x4 *)(fac + c0 + 4);
-                float x[8], t8[8];
-                O::unpack8(lhsK[kk], x);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) { t8[j] = -(x[j] * f0[j]); t8[j + 4] = -(x[j + 4] * f1[j]); }
-                O::st8_h(s_rk + prow * L::LDQ + c0, t8);
-                if (R::HAS_O) {
-                    O::unpack8(lhsQ[kk], x);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) { t8[j] = x[j] * f0[j]; t8[j + 4] = x[j + 4] * f1[j]; }
-                    O::st8_h(s_qbar + prow * L::LDQ + c0, t8);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
+            for (int kk = 0; kk < KS; ++kk) O::stf_h(s_rk + prow * L::LDQ + 32 * kk + 8 * gq, rkf[kk]);
         }
-        // The adjacent off-diagonal block (B, B-1): rhs rows of block B-1 are
-        // referenced to its end, which is where block B's lhs starts, so no
-        // rescale.  Blocks further back are formed by consumer waves.
-        if (B >= 1) {
-            constexpr int a2 = B >= 1 ? B - 1 : 0;
-            f32x4 Ao = {0.f, 0.f, 0.f, 0.f}, P_ = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const int c0 = 32 * kk + 8 * gq;
-                const F8 Bf = O::ld8(s_ro + (16 * a2 + m) * L::LDR + c0);
-                Ao = O::mma32(Ao, lhsK[kk], Bf);
-                if (R::HAS_O) P_ = O::mma32(P_, lhsQ[kk], Bf);
-            }
-            T *dst = s_aoff + aoff_idx(B, a2) * 16 * L::LDT;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                dst[(4 * gq + i) * L::LDT + m] = (T)(-Ao[i]);
-                if (R::HAS_O) s_p[(16 * B + 4 * gq + i) * L::LDP + 16 * a2 + m] = (T)P_[i];
-            }
-        }
+        if (R::HAS_V && gq == 0) s_beta[prow] = btc;   // zero on padded rows
     };
 
     // prologue: chunk 0
@@ -538,14 +642,13 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
         set_rows(0);
         issue_g();
         issue_kq();
-        if (R::HAS_V) issue_v();
         phase_own(0);
     }
     __syncthreads();                                                          // BA
     if (nchunks > 0) phase_cross();
     __syncthreads();                                                          // BB
     for (int c = 0; c < nchunks; ++c) {
-        if (R::CHECK0 && c > 0 && !(s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3])) return;
+        if (R::CHECK0 && c > 0 && !(s_flag_any(smem))) return;
         const bool next = c + 1 < nchunks;
         if (next) phase_own(c + 1);
         __syncthreads();                                                      // BA
@@ -580,7 +683,7 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
     const T *s_rk = (const T *)(smem + L::o_rk);
     const T *s_kbt = (const T *)(smem + L::o_kbt);
     const T *s_p = (const T *)(smem + L::o_p);
-    const T *s_bv = (const T *)(smem + L::o_bv);
+    const float *s_beta = (const float *)(smem + L::o_beta);
     const T *s_aoff = (const T *)(smem + L::o_aoff);
     const T *s_td = (const T *)(smem + L::o_td);
 
@@ -649,19 +752,33 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
         }
     }
 
-    // beta V enters U through an MFMA with an identity selector: the A operand
-    // is a 32-column window of the beta V tile, isel[n] picks this wave's
-    // column tile n out of it in the MFMA output layout.
-    const int win = (pw * NBW) & ~31;
-    F8 isel[NTW];
+    // V enters U through a 16x16x16 MFMA with an identity selector, which
+    // puts the rows of this wave's column tiles in the accumulator layout
+    // (lane (m, gq) loads 4 consecutive columns of row m); beta scales the
+    // result in fp32.  The rows of chunk c+1 are loaded while chunk c is
+    // applied; rows past the end of the unit are read from its first row and
+    // meet beta = 0.
+    typename O::F4 isel16, vf[4][NTW];
+    {
+        float e[4];
 #pragma unroll
-    for (int n = 0; n < NTW; ++n) {
-        const int off = pw * NBW + 16 * n - win;
-        float e[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = (4 * gq + (j & 3) + 16 * (j >> 2) == off + m) ? 1.f : 0.f;
-        isel[n] = O::cvt8(e);
+        for (int j = 0; j < 4; ++j) e[j] = (4 * gq + j == m) ? 1.f : 0.f;
+        isel16 = O::cvt4(f32x4{e[0], e[1], e[2], e[3]});
     }
+    auto load_v = [&](int c) {
+        if (!R::HAS_V) return;
+        const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
+#pragma unroll
+        for (int mu = 0; mu < 4; ++mu) {
+            const int64_t r = t0 + (int64_t)c * kChunk + 16 * mu + m;
+            const int64_t tok = r < t1 ? r : t0;
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+                vf[mu][n] = *(const typename O::F4 *)((const T *)a.v + (tok * H + h) * DV + wcol +
+                                                      16 * n + 4 * gq);
+        }
+    };
+    if (nchunks > 0) load_v(0);
 
     // Applies chunk c: U, outputs, state update.
     auto apply = [&](int c) {
@@ -681,27 +798,32 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
         for (int mu = 0; mu < 4; ++mu) {
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
-                const T *p = s_rk + (16 * mu + m) * L::LDQ + 32 * kk + 4 * gq;
+                const T *p = s_rk + (L::RKN == 2 ? (c & 1) * L::RK_BUF : 0) + (16 * mu + m) * L::LDQ +
+                             32 * kk + 4 * gq;
                 const F8 Af = O::ld44(p, p + 16);
 #pragma unroll
                 for (int n = 0; n < NTW; ++n) U[mu][n] = O::mma32(U[mu][n], Af, Sb[kk][n]);
             }
-            if (R::HAS_V) {
-                const T *p = s_bv + (16 * mu + m) * L::LDV + win + 4 * gq;
-                const F8 Af = O::ld44(p, p + 16);
+            if (R::HAS_V) {   // U += beta * V (a separate chain: MFMA shapes never mix)
+                const f32x4 b4 = *(const f32x4 *)(s_beta + 16 * mu + 4 * gq);
 #pragma unroll
-                for (int n = 0; n < NTW; ++n) U[mu][n] = O::mma32(U[mu][n], Af, isel[n]);
+                for (int n = 0; n < NTW; ++n) {
+                    const f32x4 vv = O::mma16(f32x4{0.f, 0.f, 0.f, 0.f}, vf[mu][n], isel16);
+                    U[mu][n] = vv * b4 + U[mu][n];
+                }
             }
         }
+        if (c + 1 < nchunks) load_v(c + 1);
         // (I + A) X = U by block forward substitution; X overwrites U.  The
         // off-diagonal terms accumulate onto U with the same 32-deep MFMA that
         // produced U, two 16-blocks per instruction (a zero half where a block
         // row has an odd count): an accumulator chain must not switch MFMA
         // opcodes, gfx950 does not order a srcC read after a different-shape
         // MFMA that has just written it.  T_bb starts from a zero accumulator.
-        const T *td = s_td + (c & 1) * 4 * 16 * L::LDT;
+        const T *td = s_td + (c & 1) * L::TD_BUF;
+        const T *aoff = s_aoff + (c & 1) * L::AOFF_BUF;
         const F4 z4 = O::cvt4(f32x4{0.f, 0.f, 0.f, 0.f});
-        auto negA = [&](int b, int a2) { return O::ld4(s_aoff + (aoff_idx(b, a2) * 16 + m) * L::LDT + 4 * gq); };
+        auto negA = [&](int b, int a2) { return O::ld4(aoff + (aoff_idx(b, a2) * 16 + m) * L::LDT + 4 * gq); };
         F4 Xb[4][NTW];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
@@ -745,7 +867,7 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
                 }
 #pragma unroll
                 for (int k2 = 0; k2 <= (mu >> 1); ++k2) {
-                    const T *p = s_p + (16 * mu + m) * L::LDP + 32 * k2 + 4 * gq;
+                    const T *p = s_p + (c & 1) * L::P_BUF + (16 * mu + m) * L::LDP + 32 * k2 + 4 * gq;
                     const F8 Bp = O::ld44(p, p + 16);
 #pragma unroll
                     for (int n = 0; n < NTW; ++n) Ot[mu][n] = O::mma32(Ot[mu][n], Ub[k2][n], Bp);
@@ -789,89 +911,12 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
             for (int n = 0; n < NTW; ++n) S[r][n] *= gm;
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
-                const T *p = s_kbt + (16 * r + m) * L::LDK + 32 * k2 + 4 * gq;
+                const T *p = s_kbt + (c & 1) * L::KBT_BUF + (16 * r + m) * L::LDK + 32 * k2 + 4 * gq;
                 const F8 Af = O::ld44(p, p + 16);
 #pragma unroll
                 for (int n = 0; n < NTW; ++n) S[r][n] = O::mma32(S[r][n], Af, Ub[k2][n]);
             }
         }
-    };
-
-    // The three off-diagonal blocks that need a rescale, for the chunk the
-    // producers are preparing (between the two barriers, after the block
-    // totals are complete): consumer 0 forms (3,0), consumer 1 (3,1) and
-    // consumer 2 (2,0).  The rhs rows of block a2 are referenced to its end
-    // and block B's lhs to the end of block B-1, so the product carries
-    // e^{rho_{B-1} - rho_{a2}} <= 1 per channel, computed here from the totals.
-    auto offdiag = [&]() {
-        if (pw >= 3) return;
-        const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
-        const float *s_tot = (const float *)(smem + L::o_tot);
-        const T *s_ro = (const T *)(smem + L::o_ro);
-        const T *s_lk = (const T *)(smem + L::o_lk);
-        const T *s_lq = (const T *)(smem + L::o_lq);
-        T *s_aoffw = (T *)(smem + L::o_aoff);
-        T *s_pw = (T *)(smem + L::o_p);
-        float *cf = (float *)(smem + L::o_cf) + pw * DK;
-        const int B = pw == 2 ? 2 : 3;
-        const int a2 = pw == 1 ? 1 : 0;
-        for (int ch = opaque(lane); ch < DK; ch += 64) {
-            const float u1 = s_tot[DK + ch], u2 = s_tot[2 * DK + ch];
-            cf[ch] = ex2(pw == 0 ? u1 + u2 : (pw == 1 ? u2 : u1));
-        }
-        wave_sync_lds();
-        f32x4 Ao = {0.f, 0.f, 0.f, 0.f}, P_ = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            const int c0 = 32 * kk + 8 * gq;
-            float x[8];
-            O::unpack8(O::ld8(s_ro + (16 * a2 + m) * L::LDR + c0), x);
-            const f32x4 f0 = *(const f32x4 *)(cf + c0), f1 = *(const f32x4 *)(cf + c0 + 4);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) { x[j] *= f0[j]; x[j + 4] *= f1[j]; }
-            const F8 Bf = O::cvt8(x);
-            const int lrow = (16 * (B - 2) + m) * L::LDR + c0;
-            Ao = O::mma32(Ao, O::ld8(s_lk + lrow), Bf);
-            if (R::HAS_O) P_ = O::mma32(P_, O::ld8(s_lq + lrow), Bf);
-        }
-        T *dst = s_aoffw + aoff_idx(B, a2) * 16 * L::LDT;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            dst[(4 * gq + i) * L::LDT + m] = (T)(-Ao[i]);
-            if (R::HAS_O) s_pw[(16 * B + 4 * gq + i) * L::LDP + 16 * a2 + m] = (T)P_[i];
-        }
-    };
-
-    // T_bb = (I + A_bb)^-1 of the four diagonal blocks of chunk cn, formed by
-    // consumer 3 between the barriers (the producers wrote A_bb before the
-    // first one): lane group g solves block g, lane m its column m, by forward
-    // substitution with row r+1 read while row r is reduced.
-    auto tbb = [&](int cn) {
-        if (pw != 3) return;
-        const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
-        const float *ad = (const float *)(smem + L::o_ad) + gq * 16 * L::LDAD;
-        float tc[16];
-        f32x4 nxt[4];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) nxt[q4] = *(const f32x4 *)(ad + 4 * q4);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            f32x4 cur[4];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nxt[q4];
-            if (r < 15) {
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) nxt[q4] = *(const f32x4 *)(ad + (r + 1) * L::LDAD + 4 * q4);
-            }
-            // four partial sums keep the dependent chain short
-            float sp[4] = {(r == m) ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int i = 0; i < r; ++i) sp[i & 3] = fmaf(-cur[i >> 2][i & 3], tc[i], sp[i & 3]);
-            tc[r] = (sp[0] + sp[1]) + (sp[2] + sp[3]);
-        }
-        T *td = (T *)(smem + L::o_td) + ((cn & 1) * 4 + gq) * 16 * L::LDT;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) td[r * L::LDT + m] = (T)tc[r];
     };
 
     // Rung stores and the zero test after chunk c.
@@ -912,10 +957,6 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
 
     // prologue: the producers prepare chunk 0
     __syncthreads();                                                          // BA
-    if (nchunks > 0) {
-        offdiag();
-        tbb(0);
-    }
     __syncthreads();                                                          // BB
     for (int c = 0; c < nchunks; ++c) {
         if (R::CHECK0 && c > 0 && !(s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3])) {
@@ -934,10 +975,6 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
         apply(c);
         __syncthreads();                                                      // BA
         rungs(c);
-        if (c + 1 < nchunks) {
-            offdiag();
-            tbb(c + 1);
-        }
         __syncthreads();                                                      // BB
     }
 
@@ -962,6 +999,8 @@ __device__ __forceinline__ void engine_body(const EngineArgs &a, unsigned char *
                                             const int h, const int cbase, const int64_t t0,
                                             const int64_t t1) {
     const int nchunks = (int)((t1 - t0 + kChunk - 1) / kChunk);
+    if (threadIdx.x < 8) ((int *)(smem + Lds<DK, NB, BF>::o_sync))[threadIdx.x] = -1;
+    __syncthreads();
     // wave index as a scalar: the role branches below are wave-uniform
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (wv >= 4) {
@@ -1033,6 +1072,7 @@ hipError_t launch_package_vm(const EngineArgs &a, hipStream_t stream) {
     constexpr int NBM = nb_m<DK, NB>();
     constexpr int lds = Lds<DK, NB, BF>::size > Lds<DK, NBM, BF>::size ? Lds<DK, NB, BF>::size
                                                                        : Lds<DK, NBM, BF>::size;
+    static_assert(lds <= 160 * 1024, "LDS budget");
     auto kern = package_engine<DK, DV, NB, NBM, BF>;
     hipError_t e = hipFuncSetAttribute((const void *)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -1048,6 +1088,7 @@ hipError_t launch_package_vm(const EngineArgs &a, hipStream_t stream) {
 template <int DK, int DV, int NB, bool BF, int MODE>
 hipError_t launch_one(const EngineArgs &a, hipStream_t stream) {
     using L = Lds<DK, NB, BF>;
+    static_assert(L::size <= 160 * 1024, "LDS budget");
     auto kern = chunk_engine<DK, DV, NB, BF, MODE>;
     hipError_t e = hipFuncSetAttribute((const void *)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, L::size);
