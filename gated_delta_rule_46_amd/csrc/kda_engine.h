@@ -54,6 +54,12 @@ using namespace mf;
 
 constexpr int kThreads = 512;
 
+// Destination of the output stores of padded rows (rows past the end of a
+// unit in its last chunk): the stores stay unconditional, so the compiler's
+// wait counts for the value-row loads issued before them stay exact.  Nothing
+// reads it; concurrent writes of discarded values are harmless.
+__device__ __align__(16) uint32_t g_discard[64 * 4 * 2];
+
 // Returns x unchanged, but hides its value from the optimiser.  Lane indices
 // are laundered through it at the top of every phase so that LDS addresses are
 // recomputed inside the phase instead of being hoisted out of the chunk loop
@@ -877,27 +883,29 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
 #pragma unroll
             for (int mu = 0; mu < 4; ++mu) {
                 const int64_t tok = r0 + 16 * mu + m;
-                if (tok < t1) {
+                const bool valid = tok < t1;
 #pragma unroll
-                    for (int n = 0; n < NTW; ++n) {
-                        const int64_t idx = (tok * H + h) * DV + wcol + 16 * n + 4 * gq;
-                        f32x4 val = Ot[mu][n];
-                        if (BF) {
-                            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                            u32x2 *o = (u32x2 *)((bf16_t *)a.o + idx);
-                            if (MODE == kModeFixup) {
-                                const u32x2 w = *o;
-                                val[0] += __builtin_bit_cast(float, w[0] << 16);
-                                val[1] += __builtin_bit_cast(float, w[0] & 0xffff0000u);
-                                val[2] += __builtin_bit_cast(float, w[1] << 16);
-                                val[3] += __builtin_bit_cast(float, w[1] & 0xffff0000u);
-                            }
-                            *(bf16x4 *)o = Ops<true>::cvt4(val);
-                        } else {
-                            f32x4 *o = (f32x4 *)((float *)a.o + idx);
-                            if (MODE == kModeFixup) val += *o;
-                            *o = val;
+                for (int n = 0; n < NTW; ++n) {
+                    const int64_t idx = (tok * H + h) * DV + wcol + 16 * n + 4 * gq;
+                    f32x4 val = Ot[mu][n];
+                    // padded rows store to the discard array (no branch)
+                    uint32_t *dst = valid ? (uint32_t *)((unsigned char *)a.o + idx * (BF ? 2 : 4))
+                                          : g_discard + 8 * lane;
+                    if (BF) {
+                        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                        u32x2 *o = (u32x2 *)dst;
+                        if (MODE == kModeFixup) {
+                            const u32x2 w = *o;
+                            val[0] += __builtin_bit_cast(float, w[0] << 16);
+                            val[1] += __builtin_bit_cast(float, w[0] & 0xffff0000u);
+                            val[2] += __builtin_bit_cast(float, w[1] << 16);
+                            val[3] += __builtin_bit_cast(float, w[1] & 0xffff0000u);
                         }
+                        *(bf16x4 *)o = Ops<true>::cvt4(val);
+                    } else {
+                        f32x4 *o = (f32x4 *)dst;
+                        if (MODE == kModeFixup) val += *o;
+                        *o = val;
                     }
                 }
             }
