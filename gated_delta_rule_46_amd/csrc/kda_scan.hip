@@ -17,6 +17,9 @@
 // kernel here uses LDS beyond the barrier's own, so many workgroups share a
 // CU and the copies run at streaming bandwidth.
 
+#include <algorithm>
+#include <mutex>
+
 #include "kda_internal.h"
 
 namespace kda {
@@ -250,12 +253,17 @@ __global__ __launch_bounds__(NTH) void scan_seq_kernel(int H, int nseg, const fl
 //   blel_flags_kernel  grid (nseg + 1, H): per package, whether M is exactly
 //                      zero and whether M or D holds an infinity or a NaN;
 //                      block nseg tests S0;
-//   blel_tree_kernel   grid (H): the whole tree of one head in one
-//                      workgroup.  Slots hold buffer ids, not matrices: an id
-//                      names a caller package, a fresh workspace buffer, the
-//                      zero matrix or the identity.  Moving a slot moves ids;
-//                      only a composition that really multiplies writes a
-//                      fresh buffer (all four waves, fp32 MFMA);
+//   blel_tree_kernel   grid (H, P): the tree of one head on P workgroups.
+//                      Slots hold buffer ids, not matrices: an id names a
+//                      caller package, a fresh workspace buffer, the zero
+//                      matrix or the identity.  Moving a slot moves ids; only
+//                      a composition that really multiplies writes a fresh
+//                      buffer (fp32 MFMA).  Every workgroup of a head replays
+//                      the whole tree on ids (the same decisions everywhere);
+//                      the products of one tree level are shared out over
+//                      the P workgroups, which meet at a counter in the
+//                      workspace after every level that formed a product
+//                      (see head_barrier);
 //   blel_apply_kernel  grid (nseg + 1, H): S_in[j] = Pre_j.M S0 + Pre_j.D and
 //                      S_final = Total.M S0 + Total.D from the ids.
 //
@@ -271,6 +279,7 @@ struct BlelWs {
     int *fz, *fb;            // [nseg][H]: M nonzero, M or D not finite
     int *s0bad;              // [H]
     int *out;                // [(nseg + 1)][H][3]: ids of the exclusive prefixes and the total
+    int *bar;                // [2][H]: arrivals at the tree's level barriers (plain, fenced)
 };
 
 template <int DK, int DV>
@@ -280,6 +289,7 @@ __global__ __launch_bounds__(NTH) void blel_flags_kernel(int H, int nseg, const 
     const int j = blockIdx.x, h = blockIdx.y;
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
     if (j == nseg) {
+        if (threadIdx.x == 0) w.bar[h] = w.bar[H + h] = 0;   // the tree kernel runs after this one
         if (!S0) {
             if (threadIdx.x == 0) w.s0bad[h] = 0;
             return;
@@ -323,11 +333,65 @@ __device__ __forceinline__ void add_n(float *dst, const float *a, const float *b
 // its D product (or sum) on group 1, at the same time.
 constexpr int NTH_TREE = 2 * NTH;
 
+// XCD (accelerator complex die) the wave runs on: hardware register
+// HW_REG_XCC_ID (20), bits [3:0].
+__device__ __forceinline__ int xcc_id() {
+    return __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & 15;
+}
+
+// The P workgroups of one head meet here after a tree level that formed a
+// product.  Workgroups are dispatched to the eight XCDs round-robin by linear
+// index, and the grid (H, P) with H a multiple of 8 puts the P workgroups of
+// a head on one XCD, whose L2 they share: a workgroup waits for its own
+// product stores (they reach L2), arrives at the head's counter and waits
+// for the other arrivals, and the products are then read through that L2.
+// At the first barrier every workgroup also reports whether it really runs
+// on the XCD its index implies (bit 16 of the count); if one does not, every
+// barrier of that head also writes the L2 back and invalidates it (device
+// fences) around a second count, which makes the products visible across
+// XCDs.  The waits are bounded (2^20 polls each), so a broken count shows as
+// wrong values, not as a hang; every workgroup of the launch fits on the
+// device at once (at most half of what it holds), so the waits end.
+__device__ __forceinline__ void head_barrier(int *cnt, int *cnt2, int P, int round, bool first,
+                                             bool misplaced, int &mixed) {
+    __shared__ int s_mixed;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int add = (first && misplaced) ? 1 + (1 << 16) : 1;
+        __hip_atomic_fetch_add(cnt, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int v = 0;
+        for (int it = 0; it < (1 << 20); ++it) {
+            v = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((v & 0xffff) >= P * round) break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (first) s_mixed = (v >> 16) != 0;
+    }
+    __syncthreads();
+    if (first) mixed = s_mixed;
+    if (mixed) {
+        if (threadIdx.x == 0) {
+            __threadfence();
+            __hip_atomic_fetch_add(cnt2, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            for (int it = 0; it < (1 << 20); ++it) {
+                if (__hip_atomic_load(cnt2, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= P * round) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+            __threadfence();
+        }
+        __syncthreads();
+    }
+    asm volatile("" ::: "memory");
+}
+
 template <int DK, int DV>
 __global__ __launch_bounds__(NTH_TREE, 1) void blel_tree_kernel(int H, int nseg, int size,
                                                         const float *M, const float *D,
-                                                        BlelWs w) {
-    const int h = blockIdx.x;
+                                                        BlelWs w, int P) {
+    const int h = blockIdx.x, wp = blockIdx.y;   // head, workgroup of the head
+    // the XCD round-robin dispatch by linear index would give this workgroup
+    const bool misplaced = P > 1 && xcc_id() != (int)((blockIdx.y * gridDim.x + blockIdx.x) & 7);
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
     __shared__ int s_m[kMaxSize + 2], s_d[kMaxSize + 2], s_b[kMaxSize + 2];
     constexpr int kPark = kMaxSize + 1;
@@ -345,6 +409,18 @@ __global__ __launch_bounds__(NTH_TREE, 1) void blel_tree_kernel(int H, int nseg,
     }
     __syncthreads();
     int nM = 0, nD = 0;   // fresh buffers used (uniform across the workgroup)
+    int kl = 0;           // compositions so far in this tree level
+    bool formed = false;  // this level formed a product (any workgroup)
+    int rounds = 0;       // level barriers passed
+    int mixed = 0;        // a workgroup of this head is not on the head's XCD
+    auto end_level = [&]() {
+        if (P > 1 && formed) {
+            ++rounds;
+            head_barrier(w.bar + h, w.bar + H + h, P, rounds, rounds == 1, misplaced, mixed);
+        }
+        kl = 0;
+        formed = false;
+    };
     auto mptr = [&](int id) -> const float * {
         return id < 0 ? nullptr : id < nseg ? M + ((int64_t)id * H + h) * mm
                                             : w.Mw + ((int64_t)(id - nseg) * H + h) * mm;
@@ -356,6 +432,7 @@ __global__ __launch_bounds__(NTH_TREE, 1) void blel_tree_kernel(int H, int nseg,
     // r <- l o e = (Ml Me, Ml De + Dl); reads the slots, writes slot r after
     // a barrier (r may be l or e).  Every thread takes the same decisions.
     auto compose = [&](int l, int e, int r) {
+        const bool mine = (kl++ % P) == wp;   // this workgroup forms this composition's products
         const int ml = s_m[l], dl = s_d[l], bl = s_b[l];
         const int me = s_m[e], de = s_d[e], be = s_b[e];
         const bool zl = ml == kIdZero, il = ml == kIdIdent;
@@ -376,7 +453,8 @@ __global__ __launch_bounds__(NTH_TREE, 1) void blel_tree_kernel(int H, int nseg,
             rm = ml;
         } else {
             rm = nseg + nM++;
-            if (grp == 0) {
+            formed = true;
+            if (mine && grp == 0) {
                 Acc<DK, DK> am;
                 mm_acc<DK, DK>(mptr(ml), mptr(me), am, lk, ek, gw);
                 store_acc<DK, DK>(am, nullptr, (float *)mptr(rm), gw);
@@ -390,11 +468,13 @@ __global__ __launch_bounds__(NTH_TREE, 1) void blel_tree_kernel(int H, int nseg,
                 rd = de;
             } else {
                 rd = nseg + nD++;
-                if (grp == 1) add_n<DK * DV>((float *)dptr(rd), dptr(de), dptr(dl), gt);
+                formed = true;
+                if (mine && grp == 1) add_n<DK * DV>((float *)dptr(rd), dptr(de), dptr(dl), gt);
             }
         } else {
             rd = nseg + nD++;
-            if (grp == 1) {
+            formed = true;
+            if (mine && grp == 1) {
                 Acc<DK, DV> ad;
                 mm_acc<DK, DV>(mptr(ml), dptr(de), ad, lk, dze ? kZero : kMem, gw);
                 store_acc<DK, DV>(ad, dzl ? nullptr : dptr(dl), (float *)dptr(rd), gw);
@@ -408,8 +488,10 @@ __global__ __launch_bounds__(NTH_TREE, 1) void blel_tree_kernel(int H, int nseg,
         }
         __syncthreads();
     };
-    for (int step = 1; step < size; step *= 2)             // up-sweep
+    for (int step = 1; step < size; step *= 2) {           // up-sweep
         for (int i = 2 * step - 1; i < size; i += 2 * step) compose(i, i - step, i);
+        end_level();
+    }
     if (threadIdx.x == 0) {                                  // root
         s_m[size] = s_m[size - 1];
         s_d[size] = s_d[size - 1];
@@ -435,7 +517,9 @@ __global__ __launch_bounds__(NTH_TREE, 1) void blel_tree_kernel(int H, int nseg,
             __syncthreads();
             compose(kPark, i, i);
         }
+        end_level();
     }
+    if (wp != 0) return;
     for (int j = threadIdx.x; j <= nseg; j += NTH_TREE) {
         const int slot = j < nseg ? j : size;
         w.out[(j * H + h) * 3 + 0] = s_m[slot];
@@ -665,7 +749,46 @@ BlelWs blel_ws(void *ws, int H, int nseg) {
     w.fb = w.fz + (int64_t)nseg * H;
     w.s0bad = w.fb + (int64_t)nseg * H;
     w.out = w.s0bad + H;
+    w.bar = w.out + (int64_t)3 * (nseg + 1) * H;
     return w;
+}
+
+// Workgroups per head for the tree: up to 8 when H is a multiple of 8 (the
+// P workgroups of a head then share an XCD) and H x P is at most half of the
+// workgroups the device holds at once (per device, queried once); else 1.
+template <int DK, int DV>
+int tree_width(int H) {
+    if (H % 8 != 0) return 1;
+    static std::mutex mu;
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+    int per_dev;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        per_dev = cached[dev];
+    }
+    if (per_dev == 0) {
+        int cus = 0, nb = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, blel_tree_kernel<DK, DV>, NTH_TREE, 0) !=
+            hipSuccess)
+            nb = 0;
+        per_dev = std::max(1, nb * cus);
+        std::lock_guard<std::mutex> lock(mu);
+        cached[dev] = per_dev;
+    }
+    return std::max(1, std::min(8, per_dev / (2 * H)));
+}
+
+template <int DK, int DV>
+hipError_t launch_tree(int H, int nseg, int size, const float *M, const float *D, BlelWs w,
+                       hipStream_t s) {
+    const int P = tree_width<DK, DV>(H);
+    hipLaunchKernelGGL((blel_tree_kernel<DK, DV>), dim3(H, P), dim3(NTH_TREE), 0, s, H, nseg, size,
+                       M, D, w, P);
+    return hipGetLastError();
 }
 
 template <int DK, int DV>
@@ -678,9 +801,8 @@ hipError_t scan_blel_t(int H, int nseg, const float *M, const float *D, const fl
     hipLaunchKernelGGL((blel_flags_kernel<DK, DV>), dim3(nseg + 1, H), dim3(NTH), 0, s, H, nseg,
                        M, D, S0, w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((blel_tree_kernel<DK, DV>), dim3(H), dim3(NTH_TREE), 0, s, H, nseg, size, M,
-                       D, w);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = launch_tree<DK, DV>(H, nseg, size, M, D, w, s);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((blel_apply_kernel<DK, DV>), dim3(nseg + 1, H), dim3(NTH), 0, s, H, nseg, M,
                        D, S0, S_in, S_final, w);
     return hipGetLastError();
@@ -704,7 +826,7 @@ int blelloch_max_segments() { return kMaxSize; }
 size_t blelloch_workspace(int dk, int dv, int H, int nseg) {
     const int size = pow2_at_least(nseg);
     return (size_t)2 * size * H * ((size_t)dk * dk + (size_t)dk * dv) * sizeof(float) +
-           ((size_t)2 * nseg * H + H + (size_t)3 * (nseg + 1) * H) * sizeof(int);
+           ((size_t)2 * nseg * H + H + (size_t)3 * (nseg + 1) * H + 2 * (size_t)H) * sizeof(int);
 }
 
 hipError_t launch_scan_sequential(int dk, int dv, int H, int nseg, const float *M, const float *D,
