@@ -341,15 +341,16 @@ __device__ __forceinline__ int xcc_id() {
 
 // The P workgroups of one head meet here after a tree level that formed a
 // product.  Workgroups are dispatched to the eight XCDs round-robin by linear
-// index, and the grid (H, P) with H a multiple of 8 puts the P workgroups of
-// a head on one XCD, whose L2 they share: a workgroup waits for its own
-// product stores (they reach L2), arrives at the head's counter and waits
+// index, and in the grid (H, P) with H a multiple of 8 the P workgroups of a
+// head then run on one XCD, whose L2 they share: a workgroup waits for its
+// own product stores (they reach L2), arrives at the head's counter and waits
 // for the other arrivals, and the products are then read through that L2.
-// At the first barrier every workgroup also reports whether it really runs
-// on the XCD its index implies (bit 16 of the count); if one does not, every
-// barrier of that head also writes the L2 back and invalidates it (device
-// fences) around a second count, which makes the products visible across
-// XCDs.  The waits are bounded (2^20 polls each), so a broken count shows as
+// At the first barrier every workgroup also reports whether it runs on a
+// different XCD than the head's first workgroup would by that dispatch (bit
+// 16 of the count: always so for some workgroups when H is not a multiple of
+// 8); if one does, every barrier of that head also writes the L2 back and
+// invalidates it (device fences) around a second count, which makes the
+// products visible across XCDs.  The waits are bounded (2^20 polls each), so a broken count shows as
 // wrong values, not as a hang; every workgroup of the launch fits on the
 // device at once (at most half of what it holds), so the waits end.
 __device__ __forceinline__ void head_barrier(int *cnt, int *cnt2, int P, int round, bool first,
@@ -390,8 +391,8 @@ __global__ __launch_bounds__(NTH_TREE, 1) void blel_tree_kernel(int H, int nseg,
                                                         const float *M, const float *D,
                                                         BlelWs w, int P) {
     const int h = blockIdx.x, wp = blockIdx.y;   // head, workgroup of the head
-    // the XCD round-robin dispatch by linear index would give this workgroup
-    const bool misplaced = P > 1 && xcc_id() != (int)((blockIdx.y * gridDim.x + blockIdx.x) & 7);
+    // not on the XCD the round-robin dispatch gives the head's first workgroup
+    const bool misplaced = P > 1 && xcc_id() != (h & 7);
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
     __shared__ int s_m[kMaxSize + 2], s_d[kMaxSize + 2], s_b[kMaxSize + 2];
     constexpr int kPark = kMaxSize + 1;
@@ -753,12 +754,10 @@ BlelWs blel_ws(void *ws, int H, int nseg) {
     return w;
 }
 
-// Workgroups per head for the tree: up to 8 when H is a multiple of 8 (the
-// P workgroups of a head then share an XCD) and H x P is at most half of the
-// workgroups the device holds at once (per device, queried once); else 1.
+// Workgroups per head for the tree: up to 8, while H x P is at most half of
+// the workgroups the device holds at once (per device, queried once).
 template <int DK, int DV>
 int tree_width(int H) {
-    if (H % 8 != 0) return 1;
     static std::mutex mu;
     static int cached[64] = {};
     int dev = 0;
