@@ -268,7 +268,8 @@ int kda_segment_package(const kda_config *cfg, const void *q, const void *k, con
                         float *sub_M, float *sub_D, void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace bytes kda_segment_scan needs (0 for the sequential scan; for the
- * Blelloch scan the padded packages plus one flag per package). */
+ * Blelloch scan the padded packages, flags per package and two counters per
+ * head).  Concurrent scans need separate workspaces. */
 size_t kda_segment_scan_workspace(const kda_config *cfg, int32_t nseg, int32_t algo);
 
 /*
@@ -280,7 +281,11 @@ size_t kda_segment_scan_workspace(const kda_config *cfg, int32_t nseg, int32_t a
  * with identity packages to a power of two, in the workspace (at most 4096
  * segments; more return KDA_ERR_UNSUPPORTED).  Products with an exactly
  * zero or identity factor are not formed unless the other factor holds an
- * infinity or a NaN.  M and D are not modified.
+ * infinity or a NaN.  The products of one tree level are shared out over up
+ * to 8 workgroups per head, which wait for each other inside the launch
+ * (bounded waits; the launch uses at most half of the workgroups the device
+ * holds at once).  The results do not depend on that split.  M and D are
+ * not modified.
  */
 int kda_segment_scan(const kda_config *cfg, int32_t nseg, const float *M, const float *D,
                      const float *S0, float *S_in, float *S_final, int32_t algo,
