@@ -72,7 +72,7 @@ __device__ __forceinline__ void load_raw(const void *p, int64_t i, RawRow<BF> &r
 template <bool BF>
 __device__ __forceinline__ float raw_at(const RawRow<BF> &r, int j) {
     if (BF) return __builtin_bit_cast(float, (j & 1) ? (r.u[j >> 1] & 0xffff0000u) : (r.u[j >> 1] << 16));
-    return __builtin_bit_cast(float, r.u[j]);
+    return bits_f32(r.u[j]);
 }
 
 // z * sigmoid(z) with the hardware exp2 and reciprocal (about 1 ulp each)

@@ -210,7 +210,7 @@ __device__ __forceinline__ void unpack_words(const uint32_t *w, float *out) {
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) out[j] = __builtin_bit_cast(float, w[j]);
+        for (int j = 0; j < 8; ++j) out[j] = bits_f32(w[j]);
     }
 }
 
@@ -430,7 +430,7 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
         const float vm = raw_valid ? 1.f : 0.f;
         float gl[KS * 8];
 #pragma unroll
-        for (int e = 0; e < KS * 8; ++e) gl[e] = __builtin_bit_cast(float, raw.g[e]);
+        for (int e = 0; e < KS * 8; ++e) gl[e] = bits_f32(raw.g[e]);
         if (partial) {   // padded rows act as identity: g = 0, k = q = v = 0, beta = 0
 #pragma unroll
             for (int e = 0; e < KS * 8; ++e) gl[e] *= vm;
@@ -731,7 +731,7 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
             for (int n = 0; n < NTW; ++n)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    nz |= (__builtin_bit_cast(uint32_t, S[r][n][i]) & 0x7fffffffu) != 0u;
+                    nz |= (f32_bits(S[r][n][i]) & 0x7fffffffu) != 0u;
         return __ballot(nz) != 0ull;
     };
     // Fix-up with rungs: once the propagated state is exactly zero, every

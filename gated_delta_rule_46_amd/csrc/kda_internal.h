@@ -8,6 +8,13 @@ namespace kda {
 
 constexpr int kChunk = 64;
 
+// Bit patterns by value.  __builtin_bit_cast whose operand is an element of an
+// ext_vector_type vector (v[i]) reads element 0 whatever i is (hipcc of
+// ROCm 7.2), so every bit-level test or reinterpretation of a single element
+// goes through these helpers, whose parameter is a value.
+__device__ __forceinline__ uint32_t f32_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float bits_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
+
 // Prefill: sequences from S0.  Package: value blocks of every segment from a
 // zero state (o_local, D, sub_D).  PackageM: the segment's linear part M (and
 // sub_M) from the identity.  Fixup: outputs corrected from S_in.  PackageVM:

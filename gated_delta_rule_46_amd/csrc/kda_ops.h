@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kda_internal.h"
+
 namespace kda {
 
 // One-token step against a state pool (kda_decode.hip).

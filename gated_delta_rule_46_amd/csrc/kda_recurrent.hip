@@ -57,7 +57,7 @@ __device__ void recurrent_body(const EngineArgs &a, const int u, const int h, co
     auto nonzero = [&]() -> bool {
         uint32_t acc = 0u;
 #pragma unroll
-        for (int i = 0; i < DK; ++i) acc |= __builtin_bit_cast(uint32_t, S[i]) & 0x7fffffffu;
+        for (int i = 0; i < DK; ++i) acc |= f32_bits(S[i]) & 0x7fffffffu;
         return __ballot(acc != 0u) != 0ull;
     };
     auto store = [&](float *dst, const float *add) {

@@ -6,16 +6,18 @@
 // Blelloch prefix scan) map a segment's incoming state to S_out = M S_in + D.
 // Composition, later after earlier: (Mb,Db) o (Ma,Da) = (Mb Ma, Mb Da + Db).
 //
-// Every product here is "out[DK x NC] = L[DK x DK] R[DK x NC] + Add" in fp32
-// by one workgroup of four waves.  A zero L -- the usual case once a segment
-// has forgotten its incoming state -- turns the product into a copy of Add,
-// which is exact; the zero test reads L once with all loads in flight.  A
-// nonzero L is multiplied on the fp32 matrix cores (v_mfma_f32_16x16x4_f32)
-// with both operands read straight from L2; wave w owns output rows
-// [w*DK/4, (w+1)*DK/4) and the whole product stays in accumulators until it
-// is stored, so the output may overwrite an operand after a barrier.  No
-// kernel here uses LDS beyond the barrier's own, so many workgroups share a
-// CU and the copies run at streaming bandwidth.
+// Every product here is "out[DK x NC] = L[DK x DK] R[DK x NC] + Add" in fp32.
+// A zero L -- the usual case once a segment has forgotten its incoming state
+// -- turns the product into a copy of Add, which is exact; the zero test
+// reads L once with all loads in flight.  In the Blelloch and split kernels a
+// nonzero L is multiplied by one workgroup of four waves on the fp32 matrix
+// cores (v_mfma_f32_16x16x4_f32) with both operands read straight from L2;
+// wave w owns output rows [w*DK/4, (w+1)*DK/4) and the whole product stays in
+// accumulators until it is stored, so the output may overwrite an operand
+// after a barrier.  The sequential scan splits a head's columns over several
+// workgroups and forms its products on the VALU (see there).  The kernels use
+// little LDS, so many workgroups share a CU and the copies run at streaming
+// bandwidth.
 
 #include <algorithm>
 #include <mutex>
@@ -31,12 +33,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bool nonzero4(float4 x) {
     const uint32_t m = 0x7fffffffu;
-    return ((__builtin_bit_cast(uint32_t, x.x) & m) | (__builtin_bit_cast(uint32_t, x.y) & m) |
-            (__builtin_bit_cast(uint32_t, x.z) & m) | (__builtin_bit_cast(uint32_t, x.w) & m)) != 0u;
+    return ((f32_bits(x.x) & m) | (f32_bits(x.y) & m) | (f32_bits(x.z) & m) | (f32_bits(x.w) & m)) != 0u;
 }
 
 __device__ __forceinline__ bool nonfinite1(float x) {
-    return (__builtin_bit_cast(uint32_t, x) & 0x7f800000u) == 0x7f800000u;
+    return (f32_bits(x) & 0x7f800000u) == 0x7f800000u;
 }
 
 // Block-cooperative N-float tile held in registers (PER float4 per thread):
@@ -63,7 +64,7 @@ template <int N> struct Tile {
 #pragma unroll
         for (int i = 0; i < PER; ++i)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc |= __builtin_bit_cast(uint32_t, x[i][c]) & 0x7fffffffu;
+            for (int c = 0; c < 4; ++c) acc |= f32_bits(x[i][c]) & 0x7fffffffu;
         return __syncthreads_or(acc != 0u) != 0;
     }
     // workgroup-uniform: some element is an infinity or a NaN
@@ -215,34 +216,141 @@ __device__ __forceinline__ void affine(const float *L, bool nz, const float *R, 
 }
 
 // ---------------------------------------------------------------------------
-// Sequential scan: one workgroup per head.  S_in[0] = S0, S_in[j+1] = M_j S_in[j] + D_j.
+// Sequential scan: S_in[0] = S0, S_in[j+1] = M_j S_in[j] + D_j.
+//
+// Column c of S_in[j+1] depends only on column c of S_in[j] (and all of M_j),
+// so a head's value columns are split over SEQ_P = DV / 16 workgroups that
+// never wait for each other; with H a multiple of 8 the workgroups of one
+// head share the XCD of blockIdx mod 8 (and its L2, where M_j is read once
+// from HBM).  Each
+// workgroup keeps its 16 columns of the running state in registers and walks
+// the packages in batches of SEQ_NB: the loads of a batch (all of M_j for the
+// zero test, its own columns of D_j) are issued together, then each step is
+// either a copy of D_j -- when M_j is exactly zero and the state's columns
+// are finite, which is the product's exact value -- or the product, formed
+// in fp32 on the VALU from the state staged in LDS (0 * inf and 0 * NaN
+// spread over a column as the product would).
 // ---------------------------------------------------------------------------
+constexpr int SEQ_CW = 16;   // value columns per workgroup
+constexpr int SEQ_NB = 8;    // packages per batch
+
+__device__ __forceinline__ bool nonfinite4(f32x4 x) {
+    return nonfinite1(x[0]) | nonfinite1(x[1]) | nonfinite1(x[2]) | nonfinite1(x[3]);
+}
+
 template <int DK, int DV>
 __global__ __launch_bounds__(NTH) void scan_seq_kernel(int H, int nseg, const float *M,
                                                        const float *D, const float *S0,
                                                        float *S_in, float *S_final) {
-    const int h = blockIdx.x;
+    constexpr int P = DV / SEQ_CW;                 // workgroups per head
+    constexpr int PS = DK * SEQ_CW / 4 / NTH;      // float4 of the state's columns per thread
+    constexpr int PM = DK * DK / 4 / NTH;          // float4 of an M per thread (zero test)
+    static_assert(PS >= 1 && PS * 4 * NTH == DK * SEQ_CW && PM * 4 * NTH == DK * DK, "shape");
+    __shared__ f32x4 s_S[DK * SEQ_CW / 4];         // state columns for a product
+    __shared__ unsigned s_fl[2];
+    // blocks in groups of up to 8 heads x P: head h's workgroups are the
+    // blocks of the group congruent to h mod (heads in the group)
+    int h, wp;
+    {
+        const int b = blockIdx.x, g = b / (8 * P), w = b - g * 8 * P;
+        const int hn = H - 8 * g < 8 ? H - 8 * g : 8;
+        h = 8 * g + w % hn;
+        wp = w / hn;
+    }
+    const int t = threadIdx.x, q = t & 3;
     const int64_t ss = (int64_t)DK * DV, mm = (int64_t)DK * DK;
-    copy_n<DK * DV>(S_in + (int64_t)h * ss, S0 ? S0 + (int64_t)h * ss : nullptr);
-    __syncthreads();
-    for (int j = 0; j < nseg; ++j) {
-        const float *Sj = S_in + ((int64_t)j * H + h) * ss;
-        float *dst = (j + 1 < nseg) ? S_in + ((int64_t)(j + 1) * H + h) * ss : S_final + (int64_t)h * ss;
-        const float *Mj = M + ((int64_t)j * H + h) * mm;
-        const float *Dj = D + ((int64_t)j * H + h) * ss;
-        // D_j is loaded with the zero test of M_j (one memory latency per
-        // step in the usual case, where S_in[j+1] = D_j)
-        Tile<DK * DV> td, ts;
-        td.load(Dj);
-        ts.load(Sj);
-        // a zero M_j passes D_j on, unless S_in[j] holds an infinity or a NaN
-        // (0 * NaN is NaN): then the product is formed
-        if (!block_nonzero<DK * DK>(Mj) && !ts.any_nonfinite()) {
-            td.store(dst);
-        } else {
-            affine<DK, DV>(Mj, true, Sj, Dj, dst);
+    // element offset of this thread's i-th float4 inside a state
+    auto eoff = [&](int i) -> int64_t {
+        return (int64_t)((t + i * NTH) >> 2) * DV + wp * SEQ_CW + 4 * q;
+    };
+    auto st_ptr = [&](int j) -> float * {   // S_in[j]; j = nseg: S_final
+        return j < nseg ? S_in + ((int64_t)j * H + h) * ss : S_final + (int64_t)h * ss;
+    };
+    // running state S_in[j] (this workgroup's columns) and whether it is finite
+    f32x4 cur[PS];
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < PS; ++i) {
+        cur[i] = S0 ? *(const f32x4 *)(S0 + (int64_t)h * ss + eoff(i)) : f32x4{0.f, 0.f, 0.f, 0.f};
+        bad |= nonfinite4(cur[i]);
+        *(f32x4 *)(st_ptr(0) + eoff(i)) = cur[i];
+    }
+    bool fin = !__syncthreads_or(bad);
+    for (int j0 = 0; j0 < nseg; j0 += SEQ_NB) {
+        // bit jj of mz: M_{j0+jj} has a nonzero element; of db: this
+        // workgroup's columns of D_{j0+jj} hold an infinity or a NaN
+        f32x4 dr[SEQ_NB][PS];
+        unsigned mz = 0u, db = 0u;
+#pragma unroll
+        for (int jj = 0; jj < SEQ_NB; ++jj) {
+            const int j = j0 + jj;
+            if (j >= nseg) break;
+            const float *Dj = D + ((int64_t)j * H + h) * ss;
+            const f32x4 *Mj = (const f32x4 *)(M + ((int64_t)j * H + h) * mm);
+            uint32_t acc = 0u;
+            bool b2 = false;
+#pragma unroll
+            for (int i = 0; i < PS; ++i) {
+                dr[jj][i] = *(const f32x4 *)(Dj + eoff(i));
+                b2 |= nonfinite4(dr[jj][i]);
+            }
+#pragma unroll
+            for (int i = 0; i < PM; ++i) {
+                const f32x4 x = Mj[t + i * NTH];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc |= f32_bits(x[c]) & 0x7fffffffu;
+            }
+            mz |= (unsigned)(acc != 0u) << jj;
+            db |= (unsigned)b2 << jj;
         }
+        if (t == 0) s_fl[0] = s_fl[1] = 0u;
         __syncthreads();
+        if (mz) atomicOr(&s_fl[0], mz);
+        if (db) atomicOr(&s_fl[1], db);
+        __syncthreads();
+        mz = s_fl[0];
+        db = s_fl[1];
+#pragma unroll
+        for (int jj = 0; jj < SEQ_NB; ++jj) {
+            const int j = j0 + jj;
+            if (j >= nseg) break;
+            if (!((mz >> jj) & 1u) && fin) {   // S_in[j+1] = D_j exactly
+#pragma unroll
+                for (int i = 0; i < PS; ++i) cur[i] = dr[jj][i];
+                fin = !((db >> jj) & 1u);
+            } else {   // S_in[j+1] = M_j S_in[j] + D_j, k ascending in fp32
+                __syncthreads();   // the previous product has read s_S
+#pragma unroll
+                for (int i = 0; i < PS; ++i) s_S[t + i * NTH] = cur[i];
+                __syncthreads();
+                const float *Mj = M + ((int64_t)j * H + h) * mm;
+                f32x4 acc[PS];
+#pragma unroll
+                for (int i = 0; i < PS; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int k = 0; k < DK; k += 4) {
+                    f32x4 mr[PS], sk[4];
+#pragma unroll
+                    for (int i = 0; i < PS; ++i)
+                        mr[i] = *(const f32x4 *)(Mj + (int64_t)((t + i * NTH) >> 2) * DK + k);
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) sk[kk] = s_S[(k + kk) * (SEQ_CW / 4) + q];
+#pragma unroll
+                    for (int i = 0; i < PS; ++i)
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) acc[i] += mr[i][kk] * sk[kk];
+                }
+                bool b2 = false;
+#pragma unroll
+                for (int i = 0; i < PS; ++i) {
+                    cur[i] = acc[i] + dr[jj][i];
+                    b2 |= nonfinite4(cur[i]);
+                }
+                fin = !__syncthreads_or(b2);
+            }
+#pragma unroll
+            for (int i = 0; i < PS; ++i) *(f32x4 *)(st_ptr(j + 1) + eoff(i)) = cur[i];
+        }
+        __syncthreads();   // s_fl is rewritten by the next batch
     }
 }
 
@@ -735,8 +843,8 @@ int pow2_at_least(int n) {
 template <int DK, int DV>
 hipError_t scan_seq_t(int H, int nseg, const float *M, const float *D, const float *S0,
                       float *S_in, float *S_final, hipStream_t s) {
-    hipLaunchKernelGGL((scan_seq_kernel<DK, DV>), dim3(H), dim3(NTH), 0, s, H, nseg, M, D, S0,
-                       S_in, S_final);
+    hipLaunchKernelGGL((scan_seq_kernel<DK, DV>), dim3(H * (DV / SEQ_CW)), dim3(NTH), 0, s, H,
+                       nseg, M, D, S0, S_in, S_final);
     return hipGetLastError();
 }
 

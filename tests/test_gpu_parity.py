@@ -339,6 +339,68 @@ def test_segment_path_long_memory(K, algo, dtype, d):
 
 
 @pytest.mark.parametrize("algo", [0, 1])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+def test_segment_path_memory_off_every_fourth_channel(K, algo, dtype, d):
+    """beta = 0 makes every M diagonal.  Channels 0 mod 4 get the configs'
+    fast gates and forget within a few chunks; the others get long-memory
+    gates.  So M, and the fix-up's propagated state, keep nonzero rows only
+    in the channels that are not 0 mod 4.  These are the elements a zero test
+    misses if it reads one float in four.  Each stage is compared with the
+    oracle."""
+    say(f"segment path {dtype} d={d} algo={algo}: beta=0, fast gates on channels 0 mod 4")
+    T = 1300
+    seg = [0, 448, 896, 1300]
+    w = make_workload("t", [T], 2, d, d, dtype, 4100 + d + algo, s0_std=0.5, seg_start=seg)
+    slow = make_workload("t", [T], 2, d, d, dtype, 4100 + d + algo, gate_shift=-9.0)
+    keep = np.arange(d) % 4 != 0
+    w.g[:, :, keep] = slow.g[:, :, keep]
+    w.beta[...] = 0.0
+    r = _segment_case(K, w, algo, interval=128)
+    q, k, v, g, b = (w.f64(x) for x in ("q", "k", "v", "g", "beta"))
+    tol_o, tol_s = OUT_TOL[dtype], STATE_TOL[dtype]
+    Ms, Ds = [], []
+    for j in range(len(seg) - 1):
+        Mr, Dr, olr = oracle.package(q, k, v, g, b, seg[j], seg[j + 1])
+        # the premise: M diagonal, below fp32's smallest value on the fast
+        # channels and near 1 on the others
+        diag = np.abs(np.diagonal(Mr, axis1=1, axis2=2))
+        assert np.count_nonzero(Mr - np.stack([np.diag(x) for x in np.diagonal(Mr, axis1=1, axis2=2)])) == 0
+        assert diag[:, ~keep].max() < 1e-46 and diag[:, keep].min() > 0.5
+        Ms.append(Mr)
+        Ds.append(Dr)
+        assert_close(f"M[{j}]", r["M"][j], Mr, tol_s)
+        assert_close(f"D[{j}]", r["D"][j], Dr, tol_s)
+    S_in_ref, _ = oracle.scan_sequential(Ms, Ds, w.S0[0].astype(np.float64))
+    assert_close("S_in", r["S_in"], S_in_ref, tol_s)
+    ro, rS, rck = oracle_full(w, interval=128)
+    assert_close("S_final", r["S_final"], rS[0], tol_s)
+    assert_close("o", r["o"], ro, tol_o)
+    assert_close("ckpt", r["ckpt"], rck, tol_s)
+
+
+@pytest.mark.parametrize("algo", [0, 1])
+def test_scan_M_nonzero_off_every_fourth_column(K, algo):
+    """Packages whose M is nonzero only in columns that are not 0 mod 4 are
+    not zero packages: the scans form their products."""
+    import torch
+    from workloads import make_packages
+    nseg, H, d = 6, 3, 128
+    M, D, S0 = make_packages(nseg, H, d, d, 4170 + algo)
+    M[:, :, :, 0::4] = 0.0
+    M[2, 1] = 0.0
+    M[2, 1, 7, 5] = 0.5           # one nonzero element
+    say(f"scan algo={algo}: M zero in every column 0 mod 4")
+    tM, tD, tS0 = (torch.from_numpy(x).cuda() for x in (M, D, S0))
+    S_in, S_fin = K.kda_segment_scan(tM, tD, tS0, algo=algo)
+    sync()
+    S_in_ref, S_fin_ref = oracle.scan_sequential([m.astype(np.float64) for m in M],
+                                                 [x.astype(np.float64) for x in D],
+                                                 S0.astype(np.float64))
+    assert_close("S_in", to_numpy_f64(S_in), S_in_ref, OUT_TOL["f32"])
+    assert_close("S_final", to_numpy_f64(S_fin), S_fin_ref, STATE_TOL["f32"])
+
+
+@pytest.mark.parametrize("algo", [0, 1])
 @pytest.mark.parametrize("nseg,zero", [(13, (1, 4, 5, 9, 12)), (16, (0, 2, 3, 7, 8, 11, 15)),
                                        (16, tuple(range(1, 16))), (5, ()), (1, ()), (1, (0,)),
                                        (2, (0,)), (3, (1,)), (33, (0, 5, 6, 7, 20, 31, 32))])
@@ -362,6 +424,28 @@ def test_scan_mixed_zero_packages(K, algo, nseg, zero, d, with_s0):
     assert_close("S_final", to_numpy_f64(S_fin), S_fin_ref, STATE_TOL["f32"])
     # the inputs are left as they were
     assert np.array_equal(tM.cpu().numpy(), M) and np.array_equal(tD.cpu().numpy(), D)
+
+
+@pytest.mark.parametrize("H,dk,dv,nseg,zero", [(10, 128, 64, 9, (0, 3, 4, 8)),
+                                               (17, 64, 128, 17, (2, 5, 6, 9, 16)),
+                                               (8, 128, 128, 8, tuple(range(8)))])
+def test_scan_sequential_heads_and_shapes(K, H, dk, dv, nseg, zero):
+    """Sequential scan with head counts that are not (or are) a multiple of 8,
+    dk != dv, and package counts across the batches of the walk."""
+    import torch
+    from workloads import make_packages
+    say(f"sequential scan H={H} dk={dk} dv={dv} nseg={nseg} zero M at {list(zero)}")
+    M, D, S0 = make_packages(nseg, H, dk, dv, 7100 + H + nseg, zero=zero)
+    tM, tD, tS0 = (torch.from_numpy(x).cuda() for x in (M, D, S0))
+    S_in, S_fin = K.kda_segment_scan(tM, tD, tS0, algo=0)
+    sync()
+    S_in_ref, S_fin_ref = oracle.scan_sequential([m.astype(np.float64) for m in M],
+                                                 [x.astype(np.float64) for x in D],
+                                                 S0.astype(np.float64))
+    assert_close("S_in", to_numpy_f64(S_in), S_in_ref, OUT_TOL["f32"])
+    assert_close("S_final", to_numpy_f64(S_fin), S_fin_ref, STATE_TOL["f32"])
+    if len(zero) == nseg:   # every step a copy: exact
+        assert np.array_equal(to_numpy_f64(S_fin), D[-1].astype(np.float64))
 
 
 def test_segment_path_config_gates_bf16(K):
