@@ -305,7 +305,7 @@ def long_memory_measure(K, w, t, launches: int) -> dict:
             mark("c")
         if interval:
             K.kda_output_fixup_ckpt(t["q"], t["k"], g, beta, t["seg_start"], S_in, o, sD,
-                                    interval=interval)
+                                    interval=interval, out=sD)
         else:
             K.kda_output_fixup(t["q"], t["k"], g, beta, t["seg_start"], S_in, o)
         if timed:
@@ -465,9 +465,10 @@ def main():
             S_in, S_fin = K.kda_segment_scan(M, D, S0, algo=w.scan_algo)
             if timed:
                 mark("scan1")
-            if interval:   # the fix-up writes the checkpoint rungs in the same launch
+            if interval:   # the fix-up forms the checkpoint rungs in the same launch, in
+                # place in sub_D (rows past the propagated state's end are final already)
                 K.kda_output_fixup_ckpt(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in,
-                                        o, sD, interval=interval)
+                                        o, sD, interval=interval, out=sD)
             else:
                 K.kda_output_fixup(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o)
             if timed:

@@ -60,15 +60,6 @@ constexpr int kThreads = 512;
 // reads it; concurrent writes of discarded values are harmless.
 __device__ __align__(16) uint32_t g_discard[64 * 4 * 2];
 
-// Returns x unchanged, but hides its value from the optimiser.  Lane indices
-// are laundered through it at the top of every phase so that LDS addresses are
-// recomputed inside the phase instead of being hoisted out of the chunk loop
-// (hundreds of hoisted addresses otherwise exhaust the register file).
-__device__ __forceinline__ int opaque(int x) {
-    asm volatile("" : "+v"(x));
-    return x;
-}
-
 // Compact storage of the six strictly-lower 16x16 blocks (b, a), a < b.
 __host__ __device__ constexpr int aoff_idx(int b, int a) { return b * (b - 1) / 2 + a; }
 

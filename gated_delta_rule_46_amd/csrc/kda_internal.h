@@ -15,6 +15,16 @@ constexpr int kChunk = 64;
 __device__ __forceinline__ uint32_t f32_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ __forceinline__ float bits_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
 
+// Returns x unchanged, but hides its value from the optimiser.  Lane indices
+// are laundered through it at the top of a phase or a product so that the
+// addresses and masks derived from them are recomputed there instead of being
+// hoisted out of the loops around it (hundreds of hoisted values otherwise
+// exhaust the register file).
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // Prefill: sequences from S0.  Package: value blocks of every segment from a
 // zero state (o_local, D, sub_D).  PackageM: the segment's linear part M (and
 // sub_M) from the identity.  Fixup: outputs corrected from S_in.  PackageVM:

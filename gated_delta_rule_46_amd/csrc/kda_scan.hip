@@ -20,6 +20,7 @@
 // bandwidth.
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "kda_internal.h"
@@ -95,15 +96,15 @@ __device__ __forceinline__ bool block_nonzero(const float *p) {
 
 // dst = src over N floats (zeros when src is null), 16-byte accesses.
 template <int N>
-__device__ __forceinline__ void copy_n(float *dst, const float *src) {
+__device__ __forceinline__ void copy_n(float *dst, const float *src, int tid = threadIdx.x) {
     constexpr int PER = N / 4 / NTH;
     static_assert(PER * 4 * NTH == N, "block size");
     float4 x[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-        x[i] = src ? ((const float4 *)src)[threadIdx.x + i * NTH] : make_float4(0.f, 0.f, 0.f, 0.f);
+        x[i] = src ? ((const float4 *)src)[tid + i * NTH] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) ((float4 *)dst)[threadIdx.x + i * NTH] = x[i];
+    for (int i = 0; i < PER; ++i) ((float4 *)dst)[tid + i * NTH] = x[i];
 }
 
 // Accumulators of one wave's rows of a DK x NC product.
@@ -126,7 +127,7 @@ template <int DK, int NC>
 __device__ __forceinline__ void mm_acc(const float *L, const float *R, Acc<DK, NC> &acc,
                                        int lk = kMem, int rk = kMem, int w = -1) {
     constexpr int RT = Acc<DK, NC>::RT, CT = Acc<DK, NC>::CT;
-    const int lane = threadIdx.x & 63;
+    const int lane = opaque(threadIdx.x & 63);
     if (w < 0) w = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
     const int r0 = w * (DK / 4);
@@ -168,21 +169,22 @@ __device__ __forceinline__ void store_acc(const Acc<DK, NC> &acc, const float *A
     const int n = lane & 15, g = lane >> 4;
     const int r0 = w * (DK / 4);
     if (Add) {
-        float add[RT][CT][4];
+        // one 16-row tile at a time: its loads in flight together, and half
+        // the registers of loading all of Add first
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    add[rt][ct][i] = Add[(int64_t)(r0 + 16 * rt + 4 * g + i) * NC + 16 * ct + n];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt) {
+            float add[CT][4];
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    out[(int64_t)(r0 + 16 * rt + 4 * g + i) * NC + 16 * ct + n] = acc.v[rt][ct][i] + add[rt][ct][i];
+                    add[ct][i] = Add[(int64_t)(r0 + 16 * rt + 4 * g + i) * NC + 16 * ct + n];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    out[(int64_t)(r0 + 16 * rt + 4 * g + i) * NC + 16 * ct + n] = acc.v[rt][ct][i] + add[ct][i];
+        }
     } else {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -192,27 +194,6 @@ __device__ __forceinline__ void store_acc(const Acc<DK, NC> &acc, const float *A
                 for (int i = 0; i < 4; ++i)
                     out[(int64_t)(r0 + 16 * rt + 4 * g + i) * NC + 16 * ct + n] = acc.v[rt][ct][i];
     }
-}
-
-// out = L R + Add.  With nz false L is exactly zero and is not read: out is
-// a copy of Add, unless R holds an infinity or a NaN, in which case the
-// product is formed with zeros for L (0 * inf and 0 * NaN are NaN, as in the
-// product itself).  out must not alias L, R or Add.
-template <int DK, int NC>
-__device__ __forceinline__ void affine(const float *L, bool nz, const float *R, const float *Add,
-                                       float *out) {
-    if (!nz) {
-        Tile<DK * NC> ta, tr;   // both loads in flight together
-        ta.load(Add);
-        tr.load(R);
-        if (!tr.any_nonfinite()) {
-            ta.store(out);
-            return;
-        }
-    }
-    Acc<DK, NC> acc;
-    mm_acc<DK, NC>(L, R, acc, nz ? kMem : kZero);
-    store_acc<DK, NC>(acc, Add, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -356,24 +337,24 @@ __global__ __launch_bounds__(NTH) void scan_seq_kernel(int H, int nseg, const fl
 
 // ---------------------------------------------------------------------------
 // Blelloch scan over packages (exclusive up-sweep / down-sweep over the
-// composition, identity-padded to a power of two), in three launches:
+// composition, identity-padded to a power of two) in one launch, grid (H, P):
+// the P workgroups of a head (two groups of four waves each)
 //
-//   blel_flags_kernel  grid (nseg + 1, H): per package, whether M is exactly
-//                      zero and whether M or D holds an infinity or a NaN;
-//                      block nseg tests S0;
-//   blel_tree_kernel   grid (H, P): the tree of one head on P workgroups.
-//                      Slots hold buffer ids, not matrices: an id names a
-//                      caller package, a fresh workspace buffer, the zero
-//                      matrix or the identity.  Moving a slot moves ids; only
-//                      a composition that really multiplies writes a fresh
-//                      buffer (fp32 MFMA).  Every workgroup of a head replays
-//                      the whole tree on ids (the same decisions everywhere);
-//                      the products of one tree level are shared out over
-//                      the P workgroups, which meet at a counter in the
-//                      workspace after every level that formed a product
-//                      (see head_barrier);
-//   blel_apply_kernel  grid (nseg + 1, H): S_in[j] = Pre_j.M S0 + Pre_j.D and
-//                      S_final = Total.M S0 + Total.D from the ids.
+//   1. test the units: unit u (package u, or S0 for u = nseg) on workgroup
+//      u mod P, group (u / P) mod 2: whether M is exactly zero, and whether
+//      M and D (or S0) hold an infinity or a NaN.  The flags go to the
+//      workspace and the head's workgroups meet (head_barrier);
+//   2. walk the tree on buffer ids.  Slots hold ids, not matrices: an id
+//      names a caller package, a fresh workspace buffer, the zero matrix or
+//      the identity.  For each tree level, wave 0 replays the level's
+//      compositions on the ids alone.  A wave's LDS accesses complete in
+//      order, so this needs no barrier.  It lists the compositions that
+//      really multiply; only those write a fresh buffer.  The workgroups
+//      share the list out: the M product on group 0, the D product or sum on
+//      group 1, fp32 MFMA.  They meet after every level that formed one.
+//      Every workgroup replays the same decisions;
+//   3. apply: S_in[j] = Pre_j.M S0 + Pre_j.D and S_final = Total.M S0 +
+//      Total.D.  Output j goes to workgroup j mod P, group (j / P) mod 2.
 //
 // A product with a zero factor is formed only when the other factor may hold
 // an infinity or a NaN (0 * inf and 0 * NaN are NaN), with zeros in place of
@@ -383,42 +364,11 @@ constexpr int kIdZero = -1, kIdIdent = -2;
 constexpr int kMaxSize = 1 << 12;   // padded package count (slot kMaxSize + 1 parks a slot)
 
 struct BlelWs {
-    float *Mw, *Dw;          // fresh buffers [2 * size][H][dk][dk] and [2 * size][H][dk][dv]
-    int *fz, *fb;            // [nseg][H]: M nonzero, M or D not finite
-    int *s0bad;              // [H]
-    int *out;                // [(nseg + 1)][H][3]: ids of the exclusive prefixes and the total
-    int *bar;                // [2][H]: arrivals at the tree's level barriers (plain, fenced)
+    float *Mw, *Dw;                // fresh buffers [2 * size][H][dk][dk] and [2 * size][H][dk][dv]
+    unsigned long long *bar;       // [2][H]: arrivals at the head's barriers (plain, fenced)
+    int *fz, *fb;                  // [nseg][H]: M nonzero, M or D not finite
+    int *s0bad;                    // [H]
 };
-
-template <int DK, int DV>
-__global__ __launch_bounds__(NTH) void blel_flags_kernel(int H, int nseg, const float *M,
-                                                         const float *D, const float *S0,
-                                                         BlelWs w) {
-    const int j = blockIdx.x, h = blockIdx.y;
-    const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
-    if (j == nseg) {
-        if (threadIdx.x == 0) w.bar[h] = w.bar[H + h] = 0;   // the tree kernel runs after this one
-        if (!S0) {
-            if (threadIdx.x == 0) w.s0bad[h] = 0;
-            return;
-        }
-        Tile<DK * DV> t;
-        t.load(S0 + (int64_t)h * dd);
-        const bool bad = t.any_nonfinite();
-        if (threadIdx.x == 0) w.s0bad[h] = bad ? 1 : 0;
-        return;
-    }
-    Tile<DK * DK> tm;
-    Tile<DK * DV> td;
-    tm.load(M + ((int64_t)j * H + h) * mm);
-    td.load(D + ((int64_t)j * H + h) * dd);
-    const bool nz = tm.any_nonzero();
-    const bool bad = tm.any_nonfinite() || td.any_nonfinite();
-    if (threadIdx.x == 0) {
-        w.fz[j * H + h] = nz ? 1 : 0;
-        w.fb[j * H + h] = bad ? 1 : 0;
-    }
-}
 
 // dst = a + b over N floats by NTH threads (tid = 0..NTH-1), every load
 // before any store.
@@ -447,32 +397,62 @@ __device__ __forceinline__ int xcc_id() {
     return __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & 15;
 }
 
-// The P workgroups of one head meet here after a tree level that formed a
-// product.  Workgroups are dispatched to the eight XCDs round-robin by linear
-// index, and in the grid (H, P) with H a multiple of 8 the P workgroups of a
-// head then run on one XCD, whose L2 they share: a workgroup waits for its
-// own product stores (they reach L2), arrives at the head's counter and waits
-// for the other arrivals, and the products are then read through that L2.
-// At the first barrier every workgroup also reports whether it runs on a
-// different XCD than the head's first workgroup would by that dispatch (bit
-// 16 of the count: always so for some workgroups when H is not a multiple of
-// 8); if one does, every barrier of that head also writes the L2 back and
-// invalidates it (device fences) around a second count, which makes the
-// products visible across XCDs.  The waits are bounded (2^20 polls each), so a broken count shows as
-// wrong values, not as a hang; every workgroup of the launch fits on the
-// device at once (at most half of what it holds), so the waits end.
-__device__ __forceinline__ void head_barrier(int *cnt, int *cnt2, int P, int round, bool first,
-                                             bool misplaced, int &mixed) {
+// Barrier counters tagged with the launch that uses them: the high word of a
+// counter holds that launch's epoch, the low word the arrivals in it.  A
+// counter that holds another epoch (left by an earlier launch, or never
+// written) counts as zero and is restarted by the first arrival, so nothing
+// has to clear the counters between launches.
+__device__ __forceinline__ void arrive(unsigned long long *cnt, uint32_t epoch, uint32_t add,
+                                       int order) {
+    unsigned long long old = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int it = 0; it < (1 << 20); ++it) {
+        const unsigned long long nw = (uint32_t)(old >> 32) == epoch
+                                          ? old + add
+                                          : ((unsigned long long)epoch << 32) | add;
+        if (order == __ATOMIC_RELEASE) {
+            if (__hip_atomic_compare_exchange_strong(cnt, &old, nw, __ATOMIC_RELEASE,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                return;
+        } else if (__hip_atomic_compare_exchange_strong(cnt, &old, nw, __ATOMIC_RELAXED,
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+            return;
+        }
+    }
+}
+__device__ __forceinline__ uint32_t arrivals(const unsigned long long *cnt, uint32_t epoch,
+                                             int order) {
+    const unsigned long long v = order == __ATOMIC_ACQUIRE
+        ? __hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT)
+        : __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return (uint32_t)(v >> 32) == epoch ? (uint32_t)v : 0u;
+}
+
+// The P workgroups of one head meet here.  Workgroups are dispatched to the
+// eight XCDs round-robin by linear index, and in the grid (H, P) with H a
+// multiple of 8 the P workgroups of a head then run on one XCD, whose L2 they
+// share: a workgroup waits for its own stores (they reach L2), arrives at the
+// head's counter and waits for the other arrivals; what the others stored is
+// then read through that L2.  At the first barrier every workgroup also
+// reports whether it runs on a different XCD than the head's first workgroup
+// would by that dispatch (bit 16 of the count: always so for some workgroups
+// when H is not a multiple of 8).  If one does, every barrier of that head
+// also writes the L2 back and invalidates it (device fences) around a second
+// count, which makes the stores visible across XCDs.  The waits are bounded
+// (2^20 polls each), so a broken count shows as wrong values, not as a hang;
+// every workgroup of the launch fits on the device at once (at most half of
+// what it holds), so the waits end.
+__device__ __forceinline__ void head_barrier(unsigned long long *cnt, unsigned long long *cnt2,
+                                             int P, int round, bool first, bool misplaced,
+                                             int &mixed, uint32_t epoch) {
     __shared__ int s_mixed;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
-        const int add = (first && misplaced) ? 1 + (1 << 16) : 1;
-        __hip_atomic_fetch_add(cnt, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        int v = 0;
+        arrive(cnt, epoch, (first && misplaced) ? 1u + (1u << 16) : 1u, __ATOMIC_RELAXED);
+        uint32_t v = 0;
         for (int it = 0; it < (1 << 20); ++it) {
-            v = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if ((v & 0xffff) >= P * round) break;
+            v = arrivals(cnt, epoch, __ATOMIC_RELAXED);
+            if ((int)(v & 0xffffu) >= P * round) break;
             __builtin_amdgcn_s_sleep(2);
         }
         if (first) s_mixed = (v >> 16) != 0;
@@ -482,9 +462,9 @@ __device__ __forceinline__ void head_barrier(int *cnt, int *cnt2, int P, int rou
     if (mixed) {
         if (threadIdx.x == 0) {
             __threadfence();
-            __hip_atomic_fetch_add(cnt2, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            arrive(cnt2, epoch, 1u, __ATOMIC_RELEASE);
             for (int it = 0; it < (1 << 20); ++it) {
-                if (__hip_atomic_load(cnt2, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= P * round) break;
+                if ((int)arrivals(cnt2, epoch, __ATOMIC_ACQUIRE) >= P * round) break;
                 __builtin_amdgcn_s_sleep(2);
             }
             __threadfence();
@@ -494,41 +474,40 @@ __device__ __forceinline__ void head_barrier(int *cnt, int *cnt2, int P, int rou
     asm volatile("" ::: "memory");
 }
 
+// A flag another workgroup stored before a barrier, read past the vector L1.
+__device__ __forceinline__ int load_flag(const int *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int DK, int DV>
-__global__ __launch_bounds__(NTH_TREE, 1) void blel_tree_kernel(int H, int nseg, int size,
-                                                        const float *M, const float *D,
-                                                        BlelWs w, int P) {
+__global__ __launch_bounds__(NTH_TREE, 1) void blel_kernel(int H, int nseg, int size,
+                                                           const float *M, const float *D,
+                                                           const float *S0, float *S_in,
+                                                           float *S_final, BlelWs w, int P,
+                                                           uint32_t epoch) {
     const int h = blockIdx.x, wp = blockIdx.y;   // head, workgroup of the head
     // not on the XCD the round-robin dispatch gives the head's first workgroup
     const bool misplaced = P > 1 && xcc_id() != (h & 7);
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
     __shared__ int s_m[kMaxSize + 2], s_d[kMaxSize + 2], s_b[kMaxSize + 2];
+    // compositions of one level that multiply: {ml, me, rm, lk | ek << 2 | 16 (M product)},
+    // {dl, de, rd, kind (1 sum, 2 product) | dze << 2 | dzl << 3}
+    __shared__ int4 s_plan[kMaxSize / 2][2];
+    __shared__ int s_np;
     constexpr int kPark = kMaxSize + 1;
     const int grp = threadIdx.x / NTH, gw = (threadIdx.x / 64) % 4, gt = threadIdx.x % NTH;
-    for (int j = threadIdx.x; j < size; j += NTH_TREE) {
-        if (j < nseg) {
-            s_m[j] = w.fz[j * H + h] ? j : kIdZero;
-            s_d[j] = j;
-            s_b[j] = w.fb[j * H + h];
-        } else {   // identity padding
-            s_m[j] = kIdIdent;
-            s_d[j] = kIdZero;
-            s_b[j] = 0;
-        }
-    }
-    __syncthreads();
-    int nM = 0, nD = 0;   // fresh buffers used (uniform across the workgroup)
-    int kl = 0;           // compositions so far in this tree level
-    bool formed = false;  // this level formed a product (any workgroup)
-    int rounds = 0;       // level barriers passed
-    int mixed = 0;        // a workgroup of this head is not on the head's XCD
-    auto end_level = [&]() {
-        if (P > 1 && formed) {
+    const int lane = threadIdx.x & 63;
+    int rounds = 0;   // barriers passed
+    int mixed = 0;    // a workgroup of this head is not on the head's XCD
+    // every workgroup of the head has stored what it formed
+    auto meet = [&]() __attribute__((always_inline)) {
+        if (P > 1) {
             ++rounds;
-            head_barrier(w.bar + h, w.bar + H + h, P, rounds, rounds == 1, misplaced, mixed);
+            head_barrier(w.bar + h, w.bar + H + h, P, rounds, rounds == 1, misplaced, mixed, epoch);
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
         }
-        kl = 0;
-        formed = false;
     };
     auto mptr = [&](int id) -> const float * {
         return id < 0 ? nullptr : id < nseg ? M + ((int64_t)id * H + h) * mm
@@ -538,10 +517,79 @@ __global__ __launch_bounds__(NTH_TREE, 1) void blel_tree_kernel(int H, int nseg,
         return id < 0 ? nullptr : id < nseg ? D + ((int64_t)id * H + h) * dd
                                             : w.Dw + ((int64_t)(id - nseg) * H + h) * dd;
     };
-    // r <- l o e = (Ml Me, Ml De + Dl); reads the slots, writes slot r after
-    // a barrier (r may be l or e).  Every thread takes the same decisions.
-    auto compose = [&](int l, int e, int r) {
-        const bool mine = (kl++ % P) == wp;   // this workgroup forms this composition's products
+
+    // 1. flags of this workgroup's units (s_m, s_b as scratch)
+    for (int u = wp + P * grp; u <= nseg; u += 2 * P)
+        if (gt == 0) s_m[u] = s_b[u] = 0;
+    __syncthreads();
+    for (int u = wp + P * grp; u <= nseg; u += 2 * P) {
+        constexpr int PM = DK * DK / 4 / NTH, PD = DK * DV / 4 / NTH;
+        bool nz = false, bad = false;
+        if (u < nseg) {
+            const f32x4 *Mu = (const f32x4 *)(M + ((int64_t)u * H + h) * mm);
+            const f32x4 *Du = (const f32x4 *)(D + ((int64_t)u * H + h) * dd);
+            f32x4 a[PM], b[PD];
+#pragma unroll
+            for (int i = 0; i < PM; ++i) a[i] = Mu[gt + i * NTH];
+#pragma unroll
+            for (int i = 0; i < PD; ++i) b[i] = Du[gt + i * NTH];
+            uint32_t acc = 0u;
+#pragma unroll
+            for (int i = 0; i < PM; ++i)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    acc |= f32_bits(a[i][c]) & 0x7fffffffu;
+                    bad |= nonfinite1(a[i][c]);
+                }
+#pragma unroll
+            for (int i = 0; i < PD; ++i)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) bad |= nonfinite1(b[i][c]);
+            nz = acc != 0u;
+        } else if (S0) {
+            const f32x4 *Su = (const f32x4 *)(S0 + (int64_t)h * dd);
+            f32x4 b[PD];
+#pragma unroll
+            for (int i = 0; i < PD; ++i) b[i] = Su[gt + i * NTH];
+#pragma unroll
+            for (int i = 0; i < PD; ++i)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) bad |= nonfinite1(b[i][c]);
+        }
+        const bool wnz = __ballot(nz) != 0ull, wbad = __ballot(bad) != 0ull;
+        if (lane == 0 && wnz) atomicOr(&s_m[u], 1);
+        if (lane == 0 && wbad) atomicOr(&s_b[u], 1);
+    }
+    __syncthreads();
+    for (int u = wp + P * grp; u <= nseg; u += 2 * P) {
+        if (gt != 0) continue;
+        if (u < nseg) {
+            w.fz[u * H + h] = s_m[u];
+            w.fb[u * H + h] = s_b[u];
+        } else {
+            w.s0bad[h] = s_b[u];
+        }
+    }
+    meet();
+
+    // 2. the tree
+    for (int j = threadIdx.x; j < size; j += NTH_TREE) {
+        if (j < nseg) {
+            s_m[j] = load_flag(w.fz + j * H + h) ? j : kIdZero;
+            s_d[j] = j;
+            s_b[j] = load_flag(w.fb + j * H + h);
+        } else {   // identity padding
+            s_m[j] = kIdIdent;
+            s_d[j] = kIdZero;
+            s_b[j] = 0;
+        }
+    }
+    const bool s0bad = S0 && load_flag(w.s0bad + h);
+    __syncthreads();
+    int nM = 0, nD = 0;   // fresh buffers used (wave 0's count)
+    // r <- l o e = (Ml Me, Ml De + Dl) on ids, by the 64 lanes of wave 0 alike;
+    // the compositions that multiply are appended to s_plan
+    auto compose = [&](int l, int e, int r, int &np) __attribute__((always_inline)) {
         const int ml = s_m[l], dl = s_d[l], bl = s_b[l];
         const int me = s_m[e], de = s_d[e], be = s_b[e];
         const bool zl = ml == kIdZero, il = ml == kIdIdent;
@@ -552,8 +600,7 @@ __global__ __launch_bounds__(NTH_TREE, 1) void blel_tree_kernel(int H, int nseg,
         // or a NaN of X over its column, so against a non-finite factor the
         // product is formed (with the zero or identity substituted)
         const int lk = zl ? kZero : il ? kIdent : kMem, ek = ze ? kZero : ie ? kIdent : kMem;
-        int rm, rd;
-        // M part
+        int rm, rd, mprod = 0, dkind = 0;
         if ((zl && (ze || !be)) || (ze && !bl)) {
             rm = kIdZero;
         } else if (il && !be) {
@@ -562,12 +609,7 @@ __global__ __launch_bounds__(NTH_TREE, 1) void blel_tree_kernel(int H, int nseg,
             rm = ml;
         } else {
             rm = nseg + nM++;
-            formed = true;
-            if (mine && grp == 0) {
-                Acc<DK, DK> am;
-                mm_acc<DK, DK>(mptr(ml), mptr(me), am, lk, ek, gw);
-                store_acc<DK, DK>(am, nullptr, (float *)mptr(rm), gw);
-            }
+            mprod = 1;
         }
         // D part: T = Ml De, then T + Dl
         if ((zl && !be) || (dze && !bl)) {
@@ -577,93 +619,105 @@ __global__ __launch_bounds__(NTH_TREE, 1) void blel_tree_kernel(int H, int nseg,
                 rd = de;
             } else {
                 rd = nseg + nD++;
-                formed = true;
-                if (mine && grp == 1) add_n<DK * DV>((float *)dptr(rd), dptr(de), dptr(dl), gt);
+                dkind = 1;
             }
         } else {
             rd = nseg + nD++;
-            formed = true;
-            if (mine && grp == 1) {
+            dkind = 2;
+        }
+        if (mprod | dkind) {
+            s_plan[np][0] = int4{ml, me, rm, lk | (ek << 2) | (mprod << 4)};
+            s_plan[np][1] = int4{dl, de, rd, dkind | ((int)dze << 2) | ((int)dzl << 3)};
+            ++np;
+        }
+        s_m[r] = rm;
+        s_d[r] = rd;
+        s_b[r] = bl | be;
+    };
+    // the listed compositions of a level, shared out over the head's workgroups
+    auto form = [&](int np) __attribute__((always_inline)) {
+        for (int k = wp; k < np; k += P) {
+            const int4 pm = s_plan[k][0], pd = s_plan[k][1];
+            if (grp == 0 && (pm.w & 16)) {
+                Acc<DK, DK> am;
+                mm_acc<DK, DK>(mptr(pm.x), mptr(pm.y), am, pm.w & 3, (pm.w >> 2) & 3, gw);
+                store_acc<DK, DK>(am, nullptr, (float *)mptr(pm.z), gw);
+            }
+            if (grp == 1 && (pd.w & 3) == 1) {
+                add_n<DK * DV>((float *)dptr(pd.z), dptr(pd.y), dptr(pd.x), gt);
+            } else if (grp == 1 && (pd.w & 3) == 2) {
                 Acc<DK, DV> ad;
-                mm_acc<DK, DV>(mptr(ml), dptr(de), ad, lk, dze ? kZero : kMem, gw);
-                store_acc<DK, DV>(ad, dzl ? nullptr : dptr(dl), (float *)dptr(rd), gw);
+                mm_acc<DK, DV>(mptr(pm.x), dptr(pd.y), ad, pm.w & 3, (pd.w & 4) ? kZero : kMem, gw);
+                store_acc<DK, DV>(ad, (pd.w & 8) ? nullptr : dptr(pd.x), (float *)dptr(pd.z), gw);
             }
         }
-        __syncthreads();   // every thread has read the slots
-        if (threadIdx.x == 0) {
-            s_m[r] = rm;
-            s_d[r] = rd;
-            s_b[r] = bl | be;
+    };
+    // Levels lv < nlev: up-sweep with step 2^lv; lv == nlev: the root takes
+    // the identity; lv > nlev: down-sweep with step size / 2^(lv - nlev).
+    // Wave 0 replays a level on the ids, then its products are formed.
+    int nlev = 0;
+    while ((1 << nlev) < size) ++nlev;
+    for (int lv = 0; lv <= 2 * nlev; ++lv) {
+        if (lv == nlev) {
+            if (threadIdx.x == 0) {
+                s_m[size] = s_m[size - 1];
+                s_d[size] = s_d[size - 1];
+                s_b[size] = s_b[size - 1];
+                s_m[size - 1] = kIdIdent;
+                s_d[size - 1] = kIdZero;
+                s_b[size - 1] = 0;
+            }
+            __syncthreads();
+            continue;
+        }
+        const bool up = lv < nlev;
+        const int step = up ? 1 << lv : size >> (lv - nlev);
+        if (threadIdx.x < 64) {
+            int np = 0;
+            for (int i = 2 * step - 1; i < size; i += 2 * step) {
+                int l = i, e = i - step;
+                if (!up) {
+                    // (P[i-step], P[i]) <- (P[i], P[i-step] o P[i]); the old
+                    // P[i-step] waits in the spare slot
+                    s_m[kPark] = s_m[i - step];
+                    s_d[kPark] = s_d[i - step];
+                    s_b[kPark] = s_b[i - step];
+                    s_m[i - step] = s_m[i];
+                    s_d[i - step] = s_d[i];
+                    s_b[i - step] = s_b[i];
+                    l = kPark;
+                    e = i;
+                }
+                compose(l, e, i, np);
+            }
+            s_np = np;
         }
         __syncthreads();
-    };
-    for (int step = 1; step < size; step *= 2) {           // up-sweep
-        for (int i = 2 * step - 1; i < size; i += 2 * step) compose(i, i - step, i);
-        end_level();
+        const int np = s_np;
+        form(np);
+        if (np > 0) meet();      // the products are visible to the next level
+        else __syncthreads();    // s_plan and s_np are rewritten by the next level
     }
-    if (threadIdx.x == 0) {                                  // root
-        s_m[size] = s_m[size - 1];
-        s_d[size] = s_d[size - 1];
-        s_b[size] = s_b[size - 1];
-        s_m[size - 1] = kIdIdent;
-        s_d[size - 1] = kIdZero;
-        s_b[size - 1] = 0;
-    }
-    __syncthreads();
-    for (int step = size / 2; step >= 1; step /= 2) {       // down-sweep
-        for (int i = 2 * step - 1; i < size; i += 2 * step) {
-            // (P[i-step], P[i]) <- (P[i], P[i-step] o P[i])
-            const int lm = s_m[i - step], ld = s_d[i - step], lb = s_b[i - step];
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                s_m[i - step] = s_m[i];
-                s_d[i - step] = s_d[i];
-                s_b[i - step] = s_b[i];
-                s_m[kPark] = lm;          // the old P[i-step], parked in the spare slot
-                s_d[kPark] = ld;
-                s_b[kPark] = lb;
-            }
-            __syncthreads();
-            compose(kPark, i, i);
-        }
-        end_level();
-    }
-    if (wp != 0) return;
-    for (int j = threadIdx.x; j <= nseg; j += NTH_TREE) {
-        const int slot = j < nseg ? j : size;
-        w.out[(j * H + h) * 3 + 0] = s_m[slot];
-        w.out[(j * H + h) * 3 + 1] = s_d[slot];
-        w.out[(j * H + h) * 3 + 2] = s_b[slot];
-    }
-}
 
-// S_in[j] = Pre_j.M S0 + Pre_j.D (j < nseg); S_final = Total.M S0 + Total.D.
-template <int DK, int DV>
-__global__ __launch_bounds__(NTH) void blel_apply_kernel(int H, int nseg, const float *M,
-                                                         const float *D, const float *S0,
-                                                         float *S_in, float *S_final, BlelWs w) {
-    const int jj = blockIdx.x, h = blockIdx.y;
-    const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
-    const int idm = w.out[(jj * H + h) * 3 + 0], idd = w.out[(jj * H + h) * 3 + 1];
-    const float *Lm = idm < 0 ? nullptr : idm < nseg ? M + ((int64_t)idm * H + h) * mm
-                                                     : w.Mw + ((int64_t)(idm - nseg) * H + h) * mm;
-    const float *Ad = idd < 0 ? nullptr : idd < nseg ? D + ((int64_t)idd * H + h) * dd
-                                                     : w.Dw + ((int64_t)(idd - nseg) * H + h) * dd;
-    float *out = jj < nseg ? S_in + ((int64_t)jj * H + h) * dd : S_final + (int64_t)h * dd;
+    // 3. S_in[j] = Pre_j.M S0 + Pre_j.D (slot j), S_final from the total (slot size)
     const float *s0 = S0 ? S0 + (int64_t)h * dd : nullptr;
-    const bool s0bad = s0 && w.s0bad[h];
-    if (!s0 || (idm == kIdZero && !s0bad)) {
-        copy_n<DK * DV>(out, Ad);   // zeros when Ad is null
-        return;
+    for (int j = wp + P * grp; j <= nseg; j += 2 * P) {
+        const int slot = j < nseg ? j : size;
+        const int idm = s_m[slot], idd = s_d[slot];
+        float *out = j < nseg ? S_in + ((int64_t)j * H + h) * dd : S_final + (int64_t)h * dd;
+        const float *Ad = dptr(idd);
+        if (!s0 || (idm == kIdZero && !s0bad)) {
+            copy_n<DK * DV>(out, Ad, gt);   // zeros when Ad is null
+        } else if (idm == kIdIdent && !s0bad) {
+            if (Ad) add_n<DK * DV>(out, s0, Ad, gt);
+            else copy_n<DK * DV>(out, s0, gt);
+        } else {
+            Acc<DK, DV> acc;
+            mm_acc<DK, DV>(mptr(idm), s0, acc, idm == kIdZero ? kZero : idm == kIdIdent ? kIdent : kMem,
+                           kMem, gw);
+            store_acc<DK, DV>(acc, Ad, out, gw);
+        }
     }
-    if (idm == kIdIdent && !s0bad) {
-        if (Ad) add_n<DK * DV>(out, s0, Ad);
-        else copy_n<DK * DV>(out, s0);
-        return;
-    }
-    Acc<DK, DV> acc;
-    mm_acc<DK, DV>(Lm, s0, acc, idm == kIdZero ? kZero : idm == kIdIdent ? kIdent : kMem);
-    store_acc<DK, DV>(acc, Ad, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -854,18 +908,17 @@ BlelWs blel_ws(void *ws, int H, int nseg) {
     BlelWs w;
     w.Mw = (float *)ws;
     w.Dw = w.Mw + (int64_t)2 * size * H * DK * DK;
-    w.fz = (int *)(w.Dw + (int64_t)2 * size * H * DK * DV);
+    w.bar = (unsigned long long *)(w.Dw + (int64_t)2 * size * H * DK * DV);
+    w.fz = (int *)(w.bar + 2 * (int64_t)H);
     w.fb = w.fz + (int64_t)nseg * H;
     w.s0bad = w.fb + (int64_t)nseg * H;
-    w.out = w.s0bad + H;
-    w.bar = w.out + (int64_t)3 * (nseg + 1) * H;
     return w;
 }
 
-// Workgroups per head for the tree: up to 8, while H x P is at most half of
-// the workgroups the device holds at once (per device, queried once).
+// Workgroups per head: up to 8, while H x P is at most half of the
+// workgroups the device holds at once (per device, queried once).
 template <int DK, int DV>
-int tree_width(int H) {
+int blel_width(int H) {
     static std::mutex mu;
     static int cached[64] = {};
     int dev = 0;
@@ -879,7 +932,7 @@ int tree_width(int H) {
         int cus = 0, nb = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, blel_tree_kernel<DK, DV>, NTH_TREE, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, blel_kernel<DK, DV>, NTH_TREE, 0) !=
             hipSuccess)
             nb = 0;
         per_dev = std::max(1, nb * cus);
@@ -889,13 +942,11 @@ int tree_width(int H) {
     return std::max(1, std::min(8, per_dev / (2 * H)));
 }
 
-template <int DK, int DV>
-hipError_t launch_tree(int H, int nseg, int size, const float *M, const float *D, BlelWs w,
-                       hipStream_t s) {
-    const int P = tree_width<DK, DV>(H);
-    hipLaunchKernelGGL((blel_tree_kernel<DK, DV>), dim3(H, P), dim3(NTH_TREE), 0, s, H, nseg, size,
-                       M, D, w, P);
-    return hipGetLastError();
+// A fresh epoch per launch for the barrier counters (odd multiples of a large
+// odd constant: never zero, and unlike small integers or common bit patterns).
+uint32_t next_epoch() {
+    static std::atomic<uint32_t> n{0};
+    return (n.fetch_add(1, std::memory_order_relaxed) + 1u) * 0x9E3779B1u | 1u;
 }
 
 template <int DK, int DV>
@@ -904,14 +955,9 @@ hipError_t scan_blel_t(int H, int nseg, const float *M, const float *D, const fl
     const int size = pow2_at_least(nseg);
     if (size > kMaxSize) return hipErrorInvalidValue;
     const BlelWs w = blel_ws<DK, DV>(ws, H, nseg);
-    hipError_t e;
-    hipLaunchKernelGGL((blel_flags_kernel<DK, DV>), dim3(nseg + 1, H), dim3(NTH), 0, s, H, nseg,
-                       M, D, S0, w);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    e = launch_tree<DK, DV>(H, nseg, size, M, D, w, s);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((blel_apply_kernel<DK, DV>), dim3(nseg + 1, H), dim3(NTH), 0, s, H, nseg, M,
-                       D, S0, S_in, S_final, w);
+    const int P = blel_width<DK, DV>(H);
+    hipLaunchKernelGGL((blel_kernel<DK, DV>), dim3(H, P), dim3(NTH_TREE), 0, s, H, nseg, size, M,
+                       D, S0, S_in, S_final, w, P, next_epoch());
     return hipGetLastError();
 }
 
@@ -933,7 +979,7 @@ int blelloch_max_segments() { return kMaxSize; }
 size_t blelloch_workspace(int dk, int dv, int H, int nseg) {
     const int size = pow2_at_least(nseg);
     return (size_t)2 * size * H * ((size_t)dk * dk + (size_t)dk * dv) * sizeof(float) +
-           ((size_t)2 * nseg * H + H + (size_t)3 * (nseg + 1) * H + 2 * (size_t)H) * sizeof(int);
+           (size_t)2 * H * sizeof(unsigned long long) + ((size_t)2 * nseg * H + H) * sizeof(int);
 }
 
 hipError_t launch_scan_sequential(int dk, int dv, int H, int nseg, const float *M, const float *D,

@@ -313,7 +313,10 @@ int kda_output_fixup(const kda_config *cfg, const void *q, const void *k, const 
  * sequence, rows from 0); sub_D [rows, H, dk, dv] as written by
  * kda_segment_package.  ckpt = NULL is kda_output_fixup.  The rung states
  * equal kda_checkpoint_write's up to fp32 rounding (the same map applied by
- * the chunk recurrence instead of one product with sub_M).
+ * the chunk recurrence instead of one product with sub_M).  ckpt->states may
+ * be sub_D itself: the rungs are then formed in place, and the rows after
+ * the propagated state has reached zero are left as they are (already their
+ * values), which saves copying them; otherwise the two must not overlap.
  */
 int kda_output_fixup_ckpt(const kda_config *cfg, const void *q, const void *k, const float *g,
                           const float *beta, int64_t T, const int64_t *seg_start, int32_t nseg,

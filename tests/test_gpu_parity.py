@@ -378,6 +378,26 @@ def test_segment_path_memory_off_every_fourth_channel(K, algo, dtype, d):
     assert_close("ckpt", r["ckpt"], rck, tol_s)
 
 
+@pytest.mark.parametrize("nseg", [4096, 2500])
+def test_scan_blelloch_largest_tree(K, nseg):
+    """The Blelloch scan at its largest padded size (4096 packages): a tree
+    level lists up to 2048 products.  A few M are zero."""
+    import torch
+    from workloads import make_packages
+    H, d = 2, 64
+    zero = tuple(range(5, nseg, 97))
+    say(f"Blelloch scan nseg={nseg} (padded 4096), H={H}, d={d}, {len(zero)} zero M")
+    M, D, S0 = make_packages(nseg, H, d, d, 7300 + nseg, zero=zero)
+    tM, tD, tS0 = (torch.from_numpy(x).cuda() for x in (M, D, S0))
+    S_in, S_fin = K.kda_segment_scan(tM, tD, tS0, algo=1)
+    sync()
+    S_in_ref, S_fin_ref = oracle.scan_sequential([m.astype(np.float64) for m in M],
+                                                 [x.astype(np.float64) for x in D],
+                                                 S0.astype(np.float64))
+    assert_close("S_in", to_numpy_f64(S_in), S_in_ref, OUT_TOL["f32"])
+    assert_close("S_final", to_numpy_f64(S_fin), S_fin_ref, STATE_TOL["f32"])
+
+
 @pytest.mark.parametrize("algo", [0, 1])
 def test_scan_M_nonzero_off_every_fourth_column(K, algo):
     """Packages whose M is nonzero only in columns that are not 0 mod 4 are
@@ -994,7 +1014,8 @@ def test_single_sequence_split_dk_ne_dv(K, dtype, dk, dv):
 def test_fixup_ckpt_equals_checkpoint_write(K, gates, dtype, dk, dv):
     """kda_output_fixup_ckpt leaves the same outputs as kda_output_fixup (bit
     for bit) and writes the rungs that kda_checkpoint_write forms from the
-    sub-packages (same map, other rounding), both against the oracle; rungs
+    sub-packages (same map, other rounding), both against the oracle, and
+    the same rungs bit for bit when they are formed in place in sub_D; rungs
     at segment ends, inside segments, right after a segment start, and after
     the propagated state has reached zero."""
     import torch
@@ -1014,8 +1035,13 @@ def test_fixup_ckpt_equals_checkpoint_write(K, gates, dtype, dk, dv):
                                        sD, interval=iv)
     ck_two = K.kda_checkpoint_write(t["seg_start"], S_in, sM, sD, T=w.T, interval=iv,
                                     dtype=t["q"].dtype)
+    # the rungs formed in place in sub_D: the same values, bit for bit
+    o3, sD3 = ol.clone(), sD.clone()
+    ck_inplace = K.kda_output_fixup_ckpt(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in,
+                                         o3, sD3, interval=iv, out=sD3)
     sync()
-    assert torch.equal(o1, o2)
+    assert torch.equal(o1, o2) and torch.equal(o2, o3)
+    assert ck_inplace.data_ptr() == sD3.data_ptr() and torch.equal(ck_inplace, ck_fused)
     ro, rS, rck = oracle_full(w, interval=iv)
     tol = STATE_TOL[dtype]
     assert_close("rungs, fused", to_numpy_f64(ck_fused), rck, tol)
