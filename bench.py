@@ -293,21 +293,23 @@ def long_memory_measure(K, w, t, launches: int) -> dict:
         e.record(stream)
         ev.setdefault(name, []).append(e)
 
+    # the step as the headline runs it, with the fix-up operator (no identity
+    # vanishes here: every segment walks the recurrence in the fix-up)
+    fx = K.FixOp(len(w.seg_start) - 1, H, dk, t["q"].dtype, "cuda", interval=interval)
+
     def step(timed):
         if timed:
             mark("a")
-        o, M, D, _, sD = K.kda_segment_package(t["q"], t["k"], t["v"], g, beta, t["seg_start"],
-                                               ckpt_interval=interval, want_sub_M=False)
+        o, M, D, _, sD = K.kda_segment_package_fx(t["q"], t["k"], t["v"], g, beta,
+                                                  t["seg_start"], fx, ckpt_interval=interval,
+                                                  want_sub_M=False)
         if timed:
             mark("b")
         S_in, _ = K.kda_segment_scan(M, D, S0, algo=w.scan_algo)
         if timed:
             mark("c")
-        if interval:
-            K.kda_output_fixup_ckpt(t["q"], t["k"], g, beta, t["seg_start"], S_in, o, sD,
-                                    interval=interval, out=sD)
-        else:
-            K.kda_output_fixup(t["q"], t["k"], g, beta, t["seg_start"], S_in, o)
+        K.kda_output_fixup_fx(t["q"], t["k"], g, beta, t["seg_start"], S_in, o, fx, sub_D=sD,
+                              interval=interval, out=sD)
         if timed:
             mark("d")
         return M
@@ -453,37 +455,39 @@ def main():
     if segmented:
         S0 = None if t["S0"] is None else t["S0"][0].contiguous()
         interval = w.ckpt_interval
+        nseg = len(w.seg_start) - 1
+        # the fix-up operator: the M blocks keep the identity's outputs of the
+        # first chunks of each segment, and the fix-up is a product with them
+        fx = K.FixOp(nseg, H, dk, t["q"].dtype, dev, interval=interval)
 
         def step(timed):
             if timed:
                 mark("pkg0")
-            o, M, D, _, sD = K.kda_segment_package(t["q"], t["k"], t["v"], t["g"], t["beta"],
-                                                   t["seg_start"], ckpt_interval=interval,
-                                                   want_sub_M=False)
+            o, M, D, _, sD = K.kda_segment_package_fx(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                                      t["seg_start"], fx, ckpt_interval=interval,
+                                                      want_sub_M=False)
             if timed:
                 mark("pkg1")
             S_in, S_fin = K.kda_segment_scan(M, D, S0, algo=w.scan_algo)
             if timed:
                 mark("scan1")
-            if interval:   # the fix-up forms the checkpoint rungs in the same launch, in
-                # place in sub_D (rows past the propagated state's end are final already)
-                K.kda_output_fixup_ckpt(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in,
-                                        o, sD, interval=interval, out=sD)
-            else:
-                K.kda_output_fixup(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o)
+            # the fix-up forms the checkpoint rungs in the same launch, in place in
+            # sub_D (rows past the propagated state's end are final already)
+            K.kda_output_fixup_fx(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o, fx,
+                                  sub_D=sD, interval=interval, out=sD)
             if timed:
                 mark("fix1")
             return o
-        main_kernel = "package_engine (value blocks, then M blocks, one launch)"
+        main_kernel = "package_engine (value blocks, then M blocks with the fix-up operator)"
         rows = T // interval if interval else 0
-        nseg = len(w.seg_start) - 1
-        # D and rung sub_D, and M, written by the launch
+        # D and rung sub_D, and M, written by the launch; the rows of X it writes
+        # are counted once the warm-up has filled the operator (len)
         extra_bytes = 4 * H * dk * dv * (nseg + rows) + 4 * H * dk * dk * nseg
 
         def dominant():
-            # the launch the step runs first: kda_segment_package with M
-            K.kda_segment_package(t["q"], t["k"], t["v"], t["g"], t["beta"], t["seg_start"],
-                                  ckpt_interval=interval, want_sub_M=False)
+            # the launch the step runs first: kda_segment_package_fx
+            K.kda_segment_package_fx(t["q"], t["k"], t["v"], t["g"], t["beta"], t["seg_start"],
+                                     fx, ckpt_interval=interval, want_sub_M=False)
 
         def value_blocks():
             # the value blocks alone (kda_segment_package without M)
@@ -522,6 +526,13 @@ def main():
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
+    x_rows = 0
+    if segmented:   # rows of X the package launch writes (per 64-column block)
+        lens = fx.len.cpu().numpy().astype(np.int64)
+        seg_len = np.diff(np.asarray(w.seg_start, dtype=np.int64))
+        for j in range(nseg):
+            x_rows += int(np.minimum(np.clip(lens[j], 0, None) * 64, seg_len[j]).sum())
+        extra_bytes += x_rows * 64 * io_bytes
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(True)

@@ -109,14 +109,19 @@ int device_cus() {
 // caller's workspace.
 constexpr int64_t kMinSplit = 512;   // shortest segment worth a workgroup of its own
 
+// Chunks of rows the internal split keeps of each segment's fix-up operator.
+constexpr int kSplitFixopChunks = 6;
+
 struct SplitPlan {
     int nseg = 0;
     int64_t L = 0, rows = 0;
     size_t off_M = 0, off_D = 0, off_Sin = 0, off_Sfin = 0, off_subD = 0, off_bounds = 0,
-           bytes = 0;
+           off_X = 0, off_Xlen = 0, off_route = 0, off_Pi = 0, bytes = 0;
+    bool fixop = false;
 };
 
-bool plan_split(const kda_config *cfg, int64_t T, int32_t N, const kda_ckpt *ckpt, SplitPlan *p) {
+bool plan_split(const kda_config *cfg, int64_t T, int32_t N, const kda_ckpt *ckpt, SplitPlan *p,
+                bool fixop = true) {
     if (N != 1 || T < 2 * kMinSplit) return false;
     if (ckpt && ckpt->offsets) return false;   // a device-side first rung row is not known here
     if (ckpt && (ckpt->interval <= 0 || ckpt->interval % kda::kChunk != 0)) return false;
@@ -144,6 +149,15 @@ bool plan_split(const kda_config *cfg, int64_t T, int32_t N, const kda_ckpt *ckp
     p->off_Sfin = take(dd);
     p->off_subD = take(dd * (size_t)p->rows);
     p->off_bounds = take(sizeof(int64_t) * (size_t)(p->nseg + 1));
+    // the fix-up operator (the chunked engine's shapes only)
+    p->fixop = fixop && !kda::recurrent_supported(bf, cfg->dk, cfg->dv);
+    if (p->fixop) {
+        const size_t io = bf ? 2 : 4;
+        p->off_X = take((size_t)p->nseg * kSplitFixopChunks * kda::kChunk * H * cfg->dk * io);
+        p->off_Xlen = take((size_t)p->nseg * H * (cfg->dk / 64) * sizeof(int32_t));
+        p->off_route = take((size_t)p->nseg * H * sizeof(int32_t));
+        if (p->rows) p->off_Pi = take(mm * p->nseg);   // Pi at the rungs' interval
+    }
     p->bytes = at;
     return true;
 }
@@ -171,6 +185,12 @@ int prefill_split(const SplitPlan &p, const kda_config *cfg, const void *q, cons
     a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;
     a.ncb = dv / nb;
     a.ncb_m = dk / std::min(nb, dk);   // M has dk columns
+    if (p.fixop) {   // the M blocks keep the fix-up operator of their first chunks
+        a.X = w + p.off_X; a.X_len = (int32_t *)(w + p.off_Xlen); a.X_chunks = kSplitFixopChunks;
+        if (p.rows) {
+            a.X_Pi = (float *)(w + p.off_Pi); a.X_interval = ckpt->interval;
+        }
+    }
     if ((e = kda::launch_engine(kda::kModePackageVM, bf, dk, dv, nb, a, s)) != hipSuccess)
         return launched(e, "prefill split (package)");
     if ((e = kda::launch_scan_sequential(dk, dv, H, p.nseg, M, D, S0, S_in, S_fin, s)) != hipSuccess)
@@ -184,6 +204,15 @@ int prefill_split(const SplitPlan &p, const kda_config *cfg, const void *q, cons
     }
     const int nbf = kda::engine_pick_nb(bf, dk, dv, (int64_t)p.nseg * H, kda::kModeFixup);
     f.ncb = dv / nbf;
+    if (p.fixop) {   // the units the operator covers, then the recurrence for the rest
+        kda::EngineArgs x = f;
+        x.X = a.X; x.X_len = a.X_len; x.X_chunks = a.X_chunks;
+        x.X_Pi = a.X_Pi; x.X_interval = a.X_interval;
+        x.X_route = (int32_t *)(w + p.off_route);
+        if ((e = kda::launch_engine(kda::kModeFixOp, bf, dk, dv, nbf, x, s)) != hipSuccess)
+            return launched(e, "prefill split (fix-up operator)");
+        f.X_route = x.X_route;
+    }
     return launched(kda::launch_engine(kda::kModeFixup, bf, dk, dv, nbf, f, s),
                     "prefill split (fix-up)");
 }
@@ -223,7 +252,8 @@ bool plan_package_split(const kda_config *cfg, int64_t T, int32_t nseg, PackageS
 int package_split(const PackageSplit &p, const kda_config *cfg, const void *q, const void *k,
                   const void *v, const float *g, const float *beta, int64_t T,
                   const int64_t *seg_start, int32_t nseg, void *o_local, float *M, float *D,
-                  int32_t interval, float *sub_M, float *sub_D, void *ws, hipStream_t s) {
+                  int32_t interval, float *sub_M, float *sub_D, const kda_fixop *fxo, void *ws,
+                  hipStream_t s) {
     unsigned char *w = (unsigned char *)ws;
     int64_t *sb = (int64_t *)(w + p.off_sb);
     int32_t *ord = (int32_t *)(w + p.off_ord);
@@ -243,6 +273,10 @@ int package_split(const PackageSplit &p, const kda_config *cfg, const void *q, c
     a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;
     a.ncb = dv / nb;
     a.ncb_m = dk / std::min(nb, dk);
+    if (fxo) {   // the operator of each segment from its first sub-segment's M blocks
+        a.X = fxo->X; a.X_len = fxo->len; a.X_chunks = fxo->chunks; a.X_per = f;
+        a.X_Pi = fxo->interval > 0 ? fxo->Pi : nullptr; a.X_interval = fxo->interval;
+    }
     if ((e = kda::launch_engine(kda::kModePackageVM, bf, dk, dv, nb, a, s)) != hipSuccess)
         return launched(e, "package split (packages)");
     const int nbf = kda::engine_pick_nb(bf, dk, dv, (int64_t)nseg * H, kda::kModeFixup);
@@ -354,7 +388,9 @@ int prefill_impl(const char *what, const kda_config *cfg, const void *q, const v
 
     hipStream_t s = (hipStream_t)stream;
     SplitPlan sp;
-    if (!pool && !pos0 && plan_split(cfg, T, N, ckpt, &sp) && ws_bytes >= sp.bytes)
+    // the segmented path, with the fix-up operator when the workspace holds it
+    if (!pool && !pos0 && plan_split(cfg, T, N, ckpt, &sp) &&
+        (ws_bytes >= sp.bytes || (plan_split(cfg, T, N, ckpt, &sp, false) && ws_bytes >= sp.bytes)))
         return prefill_split(sp, cfg, q, k, v, g, beta, T, S0, S_final, o, ckpt, ws, s);
     const bool bf = cfg->io_dtype == KDA_DTYPE_BF16;
     const int nb = kda::engine_pick_nb(bf, cfg->dk, cfg->dv, (int64_t)N * cfg->num_heads,
@@ -447,10 +483,26 @@ size_t kda_segment_package_workspace(const kda_config *cfg, int64_t T, int32_t n
     return p.bytes;
 }
 
-int kda_segment_package(const kda_config *cfg, const void *q, const void *k, const void *v,
-                        const float *g, const float *beta, int64_t T, const int64_t *seg_start,
-                        int32_t nseg, void *o_local, float *M, float *D, const kda_ckpt *ckpt,
-                        float *sub_M, float *sub_D, void *ws, size_t ws_bytes, void *stream) {
+// Arguments of a fix-up operator (kda_fixop) for the chunked engine's shapes.
+int check_fixop(const kda_config *cfg, const kda_fixop *fx) {
+    if (fx->chunks <= 0) return fail(KDA_ERR_ARG, "fx->chunks must be positive (got %d)", fx->chunks);
+    KDA_TRY(check_tensor(fx->X, "fx->X", true));
+    KDA_TRY(check_tensor(fx->len, "fx->len", true, 4));
+    KDA_TRY(check_tensor(fx->route, "fx->route", true, 4));
+    KDA_TRY(check_tensor(fx->Pi, "fx->Pi", false));
+    if (fx->interval < 0) return fail(KDA_ERR_ARG, "fx->interval must be >= 0 (got %d)", fx->interval);
+    if (fx->interval > 0) KDA_TRY(check_ckpt_interval(fx->interval));
+    if (kda::recurrent_supported(cfg->io_dtype == KDA_DTYPE_BF16, cfg->dk, cfg->dv))
+        return fail(KDA_ERR_UNSUPPORTED, "a fix-up operator needs the chunked engine "
+                                         "(not fp32 I/O with dk = 128)");
+    return KDA_OK;
+}
+
+int package_impl(const kda_config *cfg, const void *q, const void *k, const void *v,
+                 const float *g, const float *beta, int64_t T, const int64_t *seg_start,
+                 int32_t nseg, void *o_local, float *M, float *D, const kda_ckpt *ckpt,
+                 float *sub_M, float *sub_D, const kda_fixop *fx, void *ws, size_t ws_bytes,
+                 void *stream) {
     KDA_TRY(check_config(cfg));
     if (T <= 0) return fail(KDA_ERR_ARG, "T must be positive (got %lld)", (long long)T);
     if (nseg <= 0) return fail(KDA_ERR_ARG, "nseg must be positive (got %d)", nseg);
@@ -470,13 +522,17 @@ int kda_segment_package(const kda_config *cfg, const void *q, const void *k, con
         KDA_TRY(check_tensor(sub_D, "sub_D", true));
         if (sub_M && !M) return fail(KDA_ERR_ARG, "sub_M needs M (M is NULL)");
     }
+    if (fx) {
+        KDA_TRY(check_fixop(cfg, fx));
+        if (!M) return fail(KDA_ERR_ARG, "a fix-up operator needs M (M is NULL)");
+    }
     hipStream_t s = (hipStream_t)stream;
     PackageSplit sp;
     if (ws && plan_package_split(cfg, T, nseg, &sp) && ws_bytes >= sp.bytes) {
         KDA_TRY(check_tensor(ws, "ws", true));
         return package_split(sp, cfg, q, k, v, g, beta, T, seg_start, nseg, o_local, M, D,
                              subs ? ckpt->interval : 0, subs ? sub_M : nullptr,
-                             subs ? sub_D : nullptr, ws, s);
+                             subs ? sub_D : nullptr, fx, ws, s);
     }
     const bool bf = cfg->io_dtype == KDA_DTYPE_BF16;
     const int nb = kda::engine_pick_nb(bf, cfg->dk, cfg->dv, (int64_t)nseg * cfg->num_heads,
@@ -488,12 +544,34 @@ int kda_segment_package(const kda_config *cfg, const void *q, const void *k, con
     a.interval = subs ? ckpt->interval : 0;
     a.ckpt_off = nullptr; a.ckpt_S = subs ? sub_D : nullptr; a.ckpt_M = subs ? sub_M : nullptr;
     a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;
+    if (fx) {
+        a.X = fx->X; a.X_len = fx->len; a.X_chunks = fx->chunks;
+        a.X_Pi = fx->interval > 0 ? fx->Pi : nullptr; a.X_interval = fx->interval;
+    }
     // Value blocks, and with M the M blocks after them in the same grid (they
     // stop as soon as M is exactly zero and fill the value blocks' tail).
     a.ncb = cfg->dv / nb;
     a.ncb_m = cfg->dk / std::min(nb, cfg->dk);   // M has dk columns
     return launched(kda::launch_engine(M ? kda::kModePackageVM : kda::kModePackage, bf, cfg->dk,
                                        cfg->dv, nb, a, s), "package");
+}
+
+int kda_segment_package(const kda_config *cfg, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta, int64_t T, const int64_t *seg_start,
+                        int32_t nseg, void *o_local, float *M, float *D, const kda_ckpt *ckpt,
+                        float *sub_M, float *sub_D, void *ws, size_t ws_bytes, void *stream) {
+    return package_impl(cfg, q, k, v, g, beta, T, seg_start, nseg, o_local, M, D, ckpt, sub_M,
+                        sub_D, nullptr, ws, ws_bytes, stream);
+}
+
+int kda_segment_package_fx(const kda_config *cfg, const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, int64_t T,
+                           const int64_t *seg_start, int32_t nseg, void *o_local, float *M,
+                           float *D, const kda_ckpt *ckpt, float *sub_M, float *sub_D,
+                           const kda_fixop *fx, void *ws, size_t ws_bytes, void *stream) {
+    if (!fx) return fail(KDA_ERR_ARG, "fx is NULL");
+    return package_impl(cfg, q, k, v, g, beta, T, seg_start, nseg, o_local, M, D, ckpt, sub_M,
+                        sub_D, fx, ws, ws_bytes, stream);
 }
 
 size_t kda_segment_scan_workspace(const kda_config *cfg, int32_t nseg, int32_t algo) {
@@ -535,13 +613,12 @@ int kda_output_fixup(const kda_config *cfg, const void *q, const void *k, const 
                                  nullptr, ws, ws_bytes, stream);
 }
 
-int kda_output_fixup_ckpt(const kda_config *cfg, const void *q, const void *k, const float *g,
-                          const float *beta, int64_t T, const int64_t *seg_start, int32_t nseg,
-                          const float *S_in, void *o, const kda_ckpt *ckpt, const float *sub_D,
-                          void *ws, size_t ws_bytes, void *stream) {
-    (void)ws;
-    (void)ws_bytes;
+int fixup_impl(const kda_config *cfg, const void *q, const void *k, const float *g,
+               const float *beta, int64_t T, const int64_t *seg_start, int32_t nseg,
+               const float *S_in, void *o, const kda_ckpt *ckpt, const float *sub_D,
+               const kda_fixop *fx, void *stream) {
     KDA_TRY(check_config(cfg));
+    if (fx) KDA_TRY(check_fixop(cfg, fx));
     if (ckpt) {
         KDA_TRY(check_ckpt_interval(ckpt->interval));
         KDA_TRY(check_tensor(ckpt->states, "ckpt->states", true));
@@ -569,7 +646,32 @@ int kda_output_fixup_ckpt(const kda_config *cfg, const void *q, const void *k, c
     a.ckpt_S = ckpt ? ckpt->states : nullptr; a.ckpt_in = ckpt ? sub_D : nullptr;
     a.ckpt_M = nullptr;
     a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;
+    if (fx) {   // the units the operator covers first; the launch below skips them
+        kda::EngineArgs x = a;
+        x.X = fx->X; x.X_len = fx->len; x.X_chunks = fx->chunks; x.X_route = fx->route;
+        x.X_Pi = fx->interval > 0 ? fx->Pi : nullptr; x.X_interval = fx->interval;
+        hipError_t e = kda::launch_engine(kda::kModeFixOp, bf, cfg->dk, cfg->dv, nb, x, s);
+        if (e != hipSuccess) return launched(e, "fixup (operator)");
+        a.X_route = fx->route;
+    }
     return launched(kda::launch_engine(kda::kModeFixup, bf, cfg->dk, cfg->dv, nb, a, s), "fixup");
+}
+
+int kda_output_fixup_ckpt(const kda_config *cfg, const void *q, const void *k, const float *g,
+                          const float *beta, int64_t T, const int64_t *seg_start, int32_t nseg,
+                          const float *S_in, void *o, const kda_ckpt *ckpt, const float *sub_D,
+                          void *ws, size_t ws_bytes, void *stream) {
+    (void)ws;
+    (void)ws_bytes;
+    return fixup_impl(cfg, q, k, g, beta, T, seg_start, nseg, S_in, o, ckpt, sub_D, nullptr,
+                      stream);
+}
+
+int kda_output_fixup_fx(const kda_config *cfg, const void *q, const void *k, const float *g,
+                        const float *beta, int64_t T, const int64_t *seg_start, int32_t nseg,
+                        const float *S_in, void *o, const kda_ckpt *ckpt, const float *sub_D,
+                        const kda_fixop *fx, void *stream) {
+    return fixup_impl(cfg, q, k, g, beta, T, seg_start, nseg, S_in, o, ckpt, sub_D, fx, stream);
 }
 
 int kda_checkpoint_write(const kda_config *cfg, const kda_ckpt *ckpt, int64_t T,

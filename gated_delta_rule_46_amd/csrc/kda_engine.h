@@ -280,11 +280,44 @@ template <int MODE, bool MB> struct Roles {
     static constexpr bool CHECK0 = (MODE == kModeFixup) || MB;   // stop once S is exactly 0
 };
 
+// Fix-up of unit u from the operator X (fixop_kernel): the chunks of rows to
+// correct, or -1 when the unit walks the recurrence instead.  That is the case
+// with no operator; with a 64-column block whose identity had not vanished
+// within X_chunks chunks, or a count outside [0, X_chunks] (the bound keeps
+// every row of X read in range); with an incoming state holding an infinity or
+// a NaN (bit 1 of flags); and with a checkpoint rung among the corrected rows
+// that the operator's Pi does not cover.  Pi covers only the first rung after
+// the segment start, and only at the operator's interval; a second rung among
+// the rows needs the recurrence.  pi_rung returns the covered rung (or -1).
+template <int DK>
+__device__ __forceinline__ int fixup_x_chunks(const EngineArgs &a, int u, int h, int64_t t0,
+                                              int64_t t1, int flags, int64_t &pi_rung) {
+    pi_rung = -1;
+    if (!a.X || !a.X_len || (flags & 2)) return -1;
+    int lmax = 0;
+#pragma unroll
+    for (int j = 0; j < DK / 64; ++j) {
+        const int l = a.X_len[((int64_t)u * a.H + h) * (DK / 64) + j];
+        if (l < 0 || l > a.X_chunks) return -1;
+        lmax = l > lmax ? l : lmax;
+    }
+    if (a.ckpt_S && a.interval > 0 && lmax > 0) {
+        const int64_t first = (t0 / a.interval + 1) * a.interval;
+        const int64_t end = t0 + (int64_t)lmax * kChunk;   // the propagated identity is 0 here
+        if (first <= t1 && first < end) {
+            if (!a.X_Pi || a.X_interval != a.interval || first + a.interval < end) return -1;
+            pi_rung = first;
+        }
+    }
+    return lmax;
+}
+
 // ===========================================================================
 // Producer wave for row block B of every chunk.
 // ===========================================================================
 template <int DK, int DV, int NB, bool BF, int MODE, bool MB, int B>
-__device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *smem, const int h,
+__device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *smem, const int u,
+                                         const int h,
                                          const int cbase, const int64_t t0, const int64_t t1,
                                          const int nchunks) {
     using O = Ops<BF>;
@@ -294,6 +327,11 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
     using L = Lds<DK, NB, BF>;
     using R = Roles<MODE, MB>;
     constexpr int KS = DK / 32;      // 32-channel steps of a row
+    // M blocks with a fix-up operator also form the outputs of their first
+    // X_chunks chunks (the rows of X); other M blocks form none.  (Of split
+    // segments only the first sub-segment writes the operator.)
+    const int xch = (MB && a.X && (a.X_per <= 1 || u % a.X_per == 0)) ? a.X_chunks : 0;
+    auto out_on = [&](int c) { return R::HAS_O || c < xch; };
     constexpr int W8 = BF ? 4 : 8;
 
     int *s_sync = (int *)(smem + L::o_sync);
@@ -315,7 +353,7 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
     const int H = a.H;
 
     // Blocks of P right of the diagonal are zero in every chunk (both buffers).
-    if (R::HAS_O) {
+    if (R::HAS_O || xch > 0) {
         const int m = lane & 15, gq = lane >> 4;
 #pragma unroll
         for (int pb = 0; pb < 2; ++pb)
@@ -358,12 +396,12 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
         for (int kk = 0; kk < KS; ++kk) ld_words<false>(a.g, base + 32 * kk + 8 * gq, &raw.g[8 * kk]);
         raw.b = a.beta[ld_tok * H + h];
     };
-    auto issue_kq = [&]() {
+    auto issue_kq = [&](int c) {   // rows of chunk c (set_rows(c) before)
         const int gq = opaque(lane) >> 4;
         const int64_t base = (ld_tok * H + h) * DK;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) ld_words<BF>(a.k, base + 32 * kk + 8 * gq, &raw.k[W8 * kk]);
-        if (R::HAS_O) {
+        if (out_on(c)) {
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) ld_words<BF>(a.q, base + 32 * kk + 8 * gq, &raw.q[W8 * kk]);
         }
@@ -378,9 +416,10 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
     // An off-diagonal block (B2, A2) of A and P: lhs rows of block B2 (lk,
     // lq, referenced to the end of block B2-1) times rhs rows of block A2
     // (s_ro, referenced to the end of block A2), times e^{rho_{B2-1} -
-    // rho_{A2}} per channel when the blocks are not adjacent (cf != null).
+    // rho_{A2}} per channel when the blocks are not adjacent (cf != null);
+    // with po also the block of P.
     auto offdiag = [&](int buf, int B2, int A2, const F8 *lk, const F8 *lq, const T *lkp,
-                       const T *lqp, const float *cf) {
+                       const T *lqp, const float *cf, bool po) {
         const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
         f32x4 Ao = {0.f, 0.f, 0.f, 0.f}, P_ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -397,7 +436,7 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
             }
             const F8 Kf = lk ? lk[kk] : O::ld8(lkp + m * L::LDR + c0);
             Ao = O::mma32(Ao, Kf, Bf);
-            if (R::HAS_O) {
+            if (po) {
                 const F8 Qf = lq ? lq[kk] : O::ld8(lqp + m * L::LDR + c0);
                 P_ = O::mma32(P_, Qf, Bf);
             }
@@ -407,7 +446,7 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             dst[(4 * gq + i) * L::LDT + m] = (T)(-Ao[i]);
-            if (R::HAS_O) pd[(16 * B2 + 4 * gq + i) * L::LDP + 16 * A2 + m] = (T)P_[i];
+            if (po) pd[(16 * B2 + 4 * gq + i) * L::LDP + 16 * A2 + m] = (T)P_[i];
         }
     };
 
@@ -418,6 +457,7 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
         const int buf = c & 1;
         const bool more = c + 1 < nchunks;
         const bool partial = t0 + (int64_t)(c + 1) * kChunk > t1;
+        const bool oc = out_on(c);   // the outputs' tiles (Qbar, P) of chunk c
         const float vm = raw_valid ? 1.f : 0.f;
         float gl[KS * 8];
 #pragma unroll
@@ -448,7 +488,7 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
             for (int kk = 0; kk < KS; ++kk) {
                 const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const uint4 *)&raw.k[W8 * kk]);
                 Gk = O::mma32(Gk, kf, kf);
-                if (R::HAS_O) {
+                if (oc) {
                     const bf16x8 qf = __builtin_bit_cast(bf16x8, *(const uint4 *)&raw.q[W8 * kk]);
                     Gq = O::mma32(Gq, qf, qf);
                 }
@@ -456,7 +496,7 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
             const int src = m + 16 * (m >> 2), e = m & 3;
             const float dk = e == 0 ? Gk[0] : e == 1 ? Gk[1] : e == 2 ? Gk[2] : Gk[3];
             fk = (a.l2norm ? rsqrtf(__shfl(dk, src) + kEps) : 1.f) * vm;
-            if (R::HAS_O) {
+            if (oc) {
                 const float dq = e == 0 ? Gq[0] : e == 1 ? Gq[1] : e == 2 ? Gq[2] : Gq[3];
                 fq = (a.l2norm ? a.scale * rsqrtf(__shfl(dq, src) + kEps) : a.scale) * vm;
             }
@@ -468,7 +508,7 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
                 unpack_words<BF>(&raw.k[W8 * kk], x);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) sk += x[j] * x[j];
-                if (R::HAS_O) {
+                if (oc) {
                     unpack_words<BF>(&raw.q[W8 * kk], x);
 #pragma unroll
                     for (int j = 0; j < 8; ++j) sq += x[j] * x[j];
@@ -476,7 +516,7 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
             }
             sk += __shfl_xor(sk, 16); sk += __shfl_xor(sk, 32);
             fk = (a.l2norm ? rsqrtf(sk + kEps) : 1.f) * vm;
-            if (R::HAS_O) {
+            if (oc) {
                 sq += __shfl_xor(sq, 16); sq += __shfl_xor(sq, 32);
                 fq = (a.l2norm ? a.scale * rsqrtf(sq + kEps) : a.scale) * vm;
             }
@@ -557,7 +597,7 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
                 if constexpr (L::RKN == 2) O::stf_h(s_rk + buf * L::RK_BUF + prow * L::LDQ + c0, r);
                 else rkf[kk] = r;
             }
-            if (R::HAS_O) {
+            if (oc) {
                 float qx[8], lq[8];
                 unpack_words<BF>(&raw.q[W8 * kk], qx);
 #pragma unroll
@@ -579,7 +619,7 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
             // one 32-channel step at a time keeps the fp32 temporaries short-lived
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (more) issue_kq();
+        if (more) issue_kq(c + 1);
         publish(s_sync + 4 + B, c);   // s_ro (and block 2's lhs rows) written
 
         // T_bb = (I + A_bb)^-1 from the strictly lower part of A_bb
@@ -595,7 +635,7 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
 #pragma unroll
             for (int i = 0; i < 4; ++i) td[(4 * gq + i) * L::LDT + m] = (T)Tb[i];
         }
-        if (R::HAS_O) {   // diagonal block of P (lower triangle incl. the diagonal)
+        if (oc) {   // diagonal block of P (lower triangle incl. the diagonal)
             T *pd = s_p + buf * L::P_BUF;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -606,24 +646,24 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
         // block B-1 are referenced to its end, where block B's lhs starts);
         // block 0 also forms (2,0) from block 2's lhs rows, block 3 also
         // (3,0) and (3,1).
-        if (B >= 1) offdiag(buf, B, B - 1, lhsK, lhsQ, nullptr, nullptr, nullptr);
-        if (B == 0) offdiag(buf, 2, 0, nullptr, nullptr, s_lk, s_lq, fac + 3 * DK);
+        if (B >= 1) offdiag(buf, B, B - 1, lhsK, lhsQ, nullptr, nullptr, nullptr, oc);
+        if (B == 0) offdiag(buf, 2, 0, nullptr, nullptr, s_lk, s_lq, fac + 3 * DK, oc);
         if (B == 3) {
-            offdiag(buf, 3, 0, lhsK, lhsQ, nullptr, nullptr, fac);
-            offdiag(buf, 3, 1, lhsK, lhsQ, nullptr, nullptr, fac + 3 * DK);
+            offdiag(buf, 3, 0, lhsK, lhsQ, nullptr, nullptr, fac, oc);
+            offdiag(buf, 3, 1, lhsK, lhsQ, nullptr, nullptr, fac + 3 * DK, oc);
         }
     };
 
     // Hand-off of chunk c (between the barriers, while the consumers store
     // rungs): the single-buffered tiles, from registers.
-    auto phase_cross = [&]() {
+    auto phase_cross = [&](int c) {
         const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
         const int prow = 16 * B + m;
         if (B == 0) {
 #pragma unroll
             for (int i = 0; i < DK / 64; ++i) s_gam[opaque(lane) + 64 * i] = gamr[i];
         }
-        if (R::HAS_O) {
+        if (out_on(c)) {
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) O::stf_h(s_qbar + prow * L::LDQ + 32 * kk + 8 * gq, qbf[kk]);
         }
@@ -638,18 +678,18 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
     if (nchunks > 0) {
         set_rows(0);
         issue_g();
-        issue_kq();
+        issue_kq(0);
         phase_own(0);
     }
     __syncthreads();                                                          // BA
-    if (nchunks > 0) phase_cross();
+    if (nchunks > 0) phase_cross(0);
     __syncthreads();                                                          // BB
     for (int c = 0; c < nchunks; ++c) {
         if (R::CHECK0 && c > 0 && !(s_flag_any(smem))) return;
         const bool next = c + 1 < nchunks;
         if (next) phase_own(c + 1);
         __syncthreads();                                                      // BA
-        if (next) phase_cross();
+        if (next) phase_cross(c + 1);
         __syncthreads();                                                      // BB
     }
 }
@@ -673,6 +713,13 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
     constexpr int DKT = DK / 16;     // state row tiles
     constexpr int LDST = MB ? DK : DV;
     static_assert(NTW >= 1, "tile shape");
+    // M blocks with a fix-up operator also form the outputs of their first
+    // X_chunks chunks, into X (the producers prepare their Qbar and P).  Of
+    // split segments (X_per sub-segments each) the first sub-segment writes
+    // the operator of its segment, ux.
+    const int xch = (MB && a.X && (a.X_per <= 1 || u % a.X_per == 0)) ? a.X_chunks : 0;
+    const int ux = a.X_per > 1 ? u / a.X_per : u;
+    auto out_on = [&](int c) { return R::HAS_O || c < xch; };
 
     int *s_flag = (int *)(smem + L::o_flag);
     const float *s_gam = (const float *)(smem + L::o_gam);
@@ -734,6 +781,44 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
             const int64_t off = ((p / a.interval - 1) * H + h) * DK * DV;
             copy_state_block<DK, NB>(a.ckpt_S + off, a.ckpt_in + off, DV, cbase,
                                      (int)threadIdx.x - 256);
+        }
+    };
+    // Output rows of chunk c from the O^T tiles (four consecutive columns of
+    // one token per lane, row-contiguous stores): to o, added to it in the
+    // fix-up; for M blocks to the rows of X.  Padded rows store to the
+    // discard array (no branch).
+    auto put_rows = [&](int c, const f32x4 (&Ot)[4][NTW]) {
+        const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
+        const int64_t r0 = t0 + (int64_t)c * kChunk;
+        unsigned char *base = MB ? (unsigned char *)a.X : (unsigned char *)a.o;
+#pragma unroll
+        for (int mu = 0; mu < 4; ++mu) {
+            const int64_t tok = r0 + 16 * mu + m;
+            const bool valid = tok < t1;
+            const int64_t row = MB ? ((int64_t)ux * a.X_chunks * kChunk + (tok - t0)) * H + h
+                                   : tok * H + h;
+#pragma unroll
+            for (int n = 0; n < NTW; ++n) {
+                const int64_t idx = row * LDST + wcol + 16 * n + 4 * gq;
+                f32x4 val = Ot[mu][n];
+                uint32_t *dst = valid ? (uint32_t *)(base + idx * (BF ? 2 : 4)) : g_discard + 8 * lane;
+                if (BF) {
+                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                    u32x2 *o = (u32x2 *)dst;
+                    if (MODE == kModeFixup) {
+                        const u32x2 w = *o;
+                        val[0] += __builtin_bit_cast(float, w[0] << 16);
+                        val[1] += __builtin_bit_cast(float, w[0] & 0xffff0000u);
+                        val[2] += __builtin_bit_cast(float, w[1] << 16);
+                        val[3] += __builtin_bit_cast(float, w[1] & 0xffff0000u);
+                    }
+                    *(bf16x4 *)o = Ops<true>::cvt4(val);
+                } else {
+                    f32x4 *o = (f32x4 *)dst;
+                    if (MODE == kModeFixup) val += *o;
+                    *o = val;
+                }
+            }
         }
     };
     if (MODE == kModeFixup) {
@@ -845,7 +930,7 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
 #pragma unroll
             for (int n = 0; n < NTW; ++n) Ub[k2][n] = O::cat(Xb[2 * k2][n], Xb[2 * k2 + 1][n]);
 
-        if (R::HAS_O) {
+        if (out_on(c)) {
             // O^T = S^T Qbar^T + U^T P^T: the MFMA output then holds four
             // consecutive columns of one token per lane (row-contiguous stores).
             f32x4 Ot[4][NTW];
@@ -870,36 +955,7 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
                     for (int n = 0; n < NTW; ++n) Ot[mu][n] = O::mma32(Ot[mu][n], Ub[k2][n], Bp);
                 }
             }
-            const int64_t r0 = t0 + (int64_t)c * kChunk;
-#pragma unroll
-            for (int mu = 0; mu < 4; ++mu) {
-                const int64_t tok = r0 + 16 * mu + m;
-                const bool valid = tok < t1;
-#pragma unroll
-                for (int n = 0; n < NTW; ++n) {
-                    const int64_t idx = (tok * H + h) * DV + wcol + 16 * n + 4 * gq;
-                    f32x4 val = Ot[mu][n];
-                    // padded rows store to the discard array (no branch)
-                    uint32_t *dst = valid ? (uint32_t *)((unsigned char *)a.o + idx * (BF ? 2 : 4))
-                                          : g_discard + 8 * lane;
-                    if (BF) {
-                        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                        u32x2 *o = (u32x2 *)dst;
-                        if (MODE == kModeFixup) {
-                            const u32x2 w = *o;
-                            val[0] += __builtin_bit_cast(float, w[0] << 16);
-                            val[1] += __builtin_bit_cast(float, w[0] & 0xffff0000u);
-                            val[2] += __builtin_bit_cast(float, w[1] << 16);
-                            val[3] += __builtin_bit_cast(float, w[1] & 0xffff0000u);
-                        }
-                        *(bf16x4 *)o = Ops<true>::cvt4(val);
-                    } else {
-                        f32x4 *o = (f32x4 *)dst;
-                        if (MODE == kModeFixup) val += *o;
-                        *o = val;
-                    }
-                }
-            }
+            put_rows(c, Ot);
         }
 
         // S <- Diag(gamma_C) S + Kbar^T U
@@ -948,9 +1004,28 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
                 }
             }
         }
+        // M blocks with an operator: the propagated identity at the first rung
+        // of the operator's interval after the segment start, within its chunks
+        if (MB && xch > 0 && a.X_Pi && a.X_interval > 0 && c < a.X_chunks) {
+            const int64_t p = t0 + (int64_t)(c + 1) * kChunk;
+            if (p <= t1 && p == (t0 / a.X_interval + 1) * a.X_interval)
+                store_state<DKT, NTW>(a.X_Pi + ((int64_t)ux * H + h) * DK * DK, DK, wcol, gq, m, S, false);
+        }
         if (R::CHECK0) {
             const bool nz = state_nonzero();
             if (lane == 0) s_flag[pw] = nz ? 1 : 0;
+        }
+    };
+
+    // M blocks with an operator: the chunks after which this block's columns
+    // of the propagated identity are exactly zero (c, when it vanished, or
+    // the end of a whole segment), or -1: past X_chunks, or the end of a
+    // first sub-segment that did not vanish.
+    auto put_len = [&](int c, bool vanished) {
+        if (xch > 0 && pw == 0 && lane == 0) {
+            const int l = (vanished || a.X_per <= 1) && c <= a.X_chunks ? c : -1;
+            for (int j = cbase / 64; j < (cbase + NB) / 64; ++j)
+                a.X_len[((int64_t)ux * H + h) * (DK / 64) + j] = l;
         }
     };
 
@@ -961,6 +1036,14 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
         if (R::CHECK0 && c > 0 && !(s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3])) {
             // The state after chunk c-1 is exactly zero and stays zero.
             if (MB) {
+                put_len(c, true);
+                if (xch > 0 && a.X_Pi && a.X_interval > 0) {   // Pi of a rung not reached: zero
+                    const int64_t first = (t0 / a.X_interval + 1) * a.X_interval;
+                    if (first >= t0 + (int64_t)c * kChunk && first <= t1 &&
+                        first <= t0 + (int64_t)a.X_chunks * kChunk)
+                        store_state<DKT, NTW>(a.X_Pi + ((int64_t)ux * H + h) * DK * DK, DK, wcol, gq,
+                                              m, S, true);
+                }
                 if (a.interval > 0 && a.ckpt_M) {
                     const int64_t first = (t0 + (int64_t)c * kChunk) / a.interval + 1;
                     for (int64_t mm = first; mm * a.interval <= t1; ++mm)
@@ -988,6 +1071,7 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
         if (dst) store_state<DKT, NTW>(dst, DV, wcol, gq, m, S, false);
     }
     if (MODE == kModePackage || MODE == kModePackageM) {
+        put_len(nchunks, false);
         if (MB) store_state<DKT, NTW>(a.M_out + (int64_t)(u * H + h) * DK * DK, DK, wcol, gq, m, S, false);
         else store_state<DKT, NTW>(a.S_out + (int64_t)(u * H + h) * DK * DV, DV, wcol, gq, m, S, false);
     }
@@ -998,6 +1082,9 @@ __device__ __forceinline__ void engine_body(const EngineArgs &a, unsigned char *
                                             const int h, const int cbase, const int64_t t0,
                                             const int64_t t1) {
     const int nchunks = (int)((t1 - t0 + kChunk - 1) / kChunk);
+    // with a fix-up operator the unit was corrected by fixop_kernel unless it
+    // routed the unit here (route 1: the recurrence)
+    if (MODE == kModeFixup && a.X_route && a.X_route[(int64_t)u * a.H + h] == 0) return;
     if (threadIdx.x < 8) ((int *)(smem + Lds<DK, NB, BF>::o_sync))[threadIdx.x] = -1;
     __syncthreads();
     // wave index as a scalar: the role branches below are wave-uniform
@@ -1014,10 +1101,10 @@ __device__ __forceinline__ void engine_body(const EngineArgs &a, unsigned char *
         if (!any) return;
     }
     switch (wv) {
-        case 0: producer<DK, DV, NB, BF, MODE, MB, 0>(a, smem, h, cbase, t0, t1, nchunks); break;
-        case 1: producer<DK, DV, NB, BF, MODE, MB, 1>(a, smem, h, cbase, t0, t1, nchunks); break;
-        case 2: producer<DK, DV, NB, BF, MODE, MB, 2>(a, smem, h, cbase, t0, t1, nchunks); break;
-        default: producer<DK, DV, NB, BF, MODE, MB, 3>(a, smem, h, cbase, t0, t1, nchunks); break;
+        case 0: producer<DK, DV, NB, BF, MODE, MB, 0>(a, smem, u, h, cbase, t0, t1, nchunks); break;
+        case 1: producer<DK, DV, NB, BF, MODE, MB, 1>(a, smem, u, h, cbase, t0, t1, nchunks); break;
+        case 2: producer<DK, DV, NB, BF, MODE, MB, 2>(a, smem, u, h, cbase, t0, t1, nchunks); break;
+        default: producer<DK, DV, NB, BF, MODE, MB, 3>(a, smem, u, h, cbase, t0, t1, nchunks); break;
     }
 }
 
@@ -1037,6 +1124,166 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_engine(EngineArgs a) {
     const int u = a.order ? a.order[pos] : pos;
     const int64_t t0 = a.bounds[u], t1 = a.bounds[u + 1];
     engine_body<DK, DV, NB, BF, MODE, MODE == kModePackageM>(a, smem, u, h, cb * NB, t0, t1);
+}
+
+// Fix-up from the operator, one workgroup of four waves per (segment, head).
+// It tests the incoming state (zero, finite) and decides the unit's route
+// (fixup_x_chunks).  Route 1 leaves the unit to the recurrence of the engine's
+// fix-up launch that follows.  Otherwise it adds
+//     o_t += S_in^T X_t
+// over the rows of the chunks X covers.  A rung among those rows gets
+//     Pi S_in + sub_D
+// (Pi: the propagated identity there); the unit's other rungs are sub_D
+// (copied when they go to their own buffer).  The products run on the matrix
+// cores as the engine's output product does: wave w holds S_in's value-column
+// tiles w*CT/4.. as operands (in the operand dtype) and multiplies every
+// 16-row tile of X, then of Pi, in place of Qbar.
+template <int DK, int DV, bool BF>
+__global__ __launch_bounds__(256) void fixop_kernel(EngineArgs a) {
+    using O = Ops<BF>;
+    using T = typename O::T;
+    using F8 = typename O::F8;
+    using F4 = typename O::F4;
+    constexpr int KS = DK / 32;        // 32-deep steps
+    constexpr int CTW = DV / 16 / 4;   // value-column tiles per wave
+    constexpr int TB = 4;              // row tiles whose loads are issued together
+    constexpr int LDS_ROW = DV + 8 / (int)sizeof(T) * 2;   // padded row of the staged S_in
+    __shared__ __align__(16) T s_S[DK * LDS_ROW];
+    const int H = a.H;
+    const int u = blockIdx.x / H, h = blockIdx.x - u * H;
+    const int64_t t0 = a.bounds[u], t1 = a.bounds[u + 1];
+    const int64_t unit = (int64_t)u * H + h;
+    const float *Sin = a.S_init + unit * DK * DV;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // the incoming state: zero and finiteness tests, staged in LDS in the
+    // operand dtype on the way
+    bool nz = false, bad = false;
+    for (int i = tid; i < DK * DV / 4; i += 256) {
+        const f32x4 x = ((const f32x4 *)Sin)[i];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            nz |= (f32_bits(x[c]) & 0x7fffffffu) != 0u;
+            bad |= (f32_bits(x[c]) & 0x7f800000u) == 0x7f800000u;
+        }
+        const int row = (4 * i) / DV, col = (4 * i) % DV;
+        *(F4 *)(s_S + row * LDS_ROW + col) = O::cvt4(x);
+    }
+    const int fl = (__syncthreads_or(nz) ? 1 : 0) | (__syncthreads_or(bad) ? 2 : 0);
+    int64_t pi_rung = -1;
+    const int xl = (fl & 1) ? fixup_x_chunks<DK>(a, u, h, t0, t1, fl, pi_rung) : 0;
+    if (tid == 0) a.X_route[unit] = xl < 0 ? 1 : 0;
+    if (xl < 0) return;
+    if (a.ckpt_S && a.interval > 0 && a.ckpt_S != a.ckpt_in) {
+        for (int64_t p = (t0 / a.interval + 1) * a.interval; p <= t1; p += a.interval) {
+            if (p == pi_rung) continue;   // formed below
+            const int64_t off = ((p / a.interval - 1) * H + h) * DK * DV;
+            for (int i = tid; i < DK * DV / 4; i += 256)
+                ((f32x4 *)(a.ckpt_S + off))[i] = ((const f32x4 *)(a.ckpt_in + off))[i];
+        }
+    }
+    if (!(fl & 1)) return;   // a zero incoming state leaves o_local final
+    int lb[DK / 64];
+#pragma unroll
+    for (int j = 0; j < DK / 64; ++j) lb[j] = a.X_len[unit * (DK / 64) + j];
+    // operands: S_in's column 16n + m, rows 32kk + 8gq .. + 7 of lane (m, gq),
+    // from LDS; the rows of X and Pi are loaded with the same k in the same order
+    const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
+    const int n0 = w * CTW;
+    F8 A[CTW][KS];
+#pragma unroll
+    for (int n = 0; n < CTW; ++n)
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                v[j] = (float)s_S[(32 * kk + 8 * gq + j) * LDS_ROW + 16 * (n0 + n) + m];
+            A[n][kk] = O::cvt8(v);
+        }
+    const T *Xu = (const T *)a.X + (int64_t)u * a.X_chunks * kChunk * H * DK;
+    const int64_t rows = (int64_t)xl * kChunk < t1 - t0 ? (int64_t)xl * kChunk : t1 - t0;
+    const int ntx = (int)((rows + 15) / 16);           // tiles of X
+    const int ntp = pi_rung >= 0 ? DK / 16 : 0;         // tiles of Pi
+    const float *Pi = a.X_Pi + unit * DK * DK;
+    float *rung = pi_rung >= 0 ? a.ckpt_S + ((pi_rung / a.interval - 1) * H + h) * DK * DV : nullptr;
+    const float *rung_in = pi_rung >= 0 ? a.ckpt_in + ((pi_rung / a.interval - 1) * H + h) * DK * DV
+                                        : nullptr;
+    // o_t += S_in^T X_t, TB row tiles at a time: every load of a batch (rows
+    // of X, the outputs to add to) issued before its products
+    for (int tb = 0; tb < ntx; tb += TB) {
+        F8 B[TB][KS];
+        f32x4 ov[TB][CTW];
+#pragma unroll
+        for (int q = 0; q < TB; ++q) {
+            const int tt = tb + q < ntx ? tb + q : ntx - 1;   // past the last tile: repeat it
+            const int r = 16 * tt + m;
+            const int ch = (16 * tt) / kChunk;
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                // a block of X whose identity had vanished is zero here
+                B[q][kk] = ch < lb[(32 * kk) / 64]
+                               ? O::ld8(Xu + ((int64_t)r * H + h) * DK + 32 * kk + 8 * gq)
+                               : O::cvt8((const float[8]){0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f});
+            }
+            const int64_t tok = t0 + r < t1 ? t0 + r : t1 - 1;
+#pragma unroll
+            for (int n = 0; n < CTW; ++n) {
+                const int64_t idx = (tok * H + h) * DV + 16 * (n0 + n) + 4 * gq;
+                if (BF) {
+                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                    const u32x2 wv = *(const u32x2 *)((const bf16_t *)a.o + idx);
+                    ov[q][n] = f32x4{bits_f32(wv[0] << 16), bits_f32(wv[0] & 0xffff0000u),
+                                     bits_f32(wv[1] << 16), bits_f32(wv[1] & 0xffff0000u)};
+                } else {
+                    ov[q][n] = *(const f32x4 *)((const float *)a.o + idx);
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < TB; ++q) {
+            if (tb + q >= ntx) break;
+            const int64_t tok = t0 + 16 * (tb + q) + m;
+#pragma unroll
+            for (int n = 0; n < CTW; ++n) {
+                f32x4 acc = ov[q][n];
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) acc = O::mma32(acc, A[n][kk], B[q][kk]);
+                if (tok >= t1) continue;
+                // lane (m, gq) holds value columns 16n + 4gq .. + 3 of token tok
+                const int64_t idx = (tok * H + h) * DV + 16 * (n0 + n) + 4 * gq;
+                if (BF) *(bf16x4 *)((bf16_t *)a.o + idx) = Ops<true>::cvt4(acc);
+                else *(f32x4 *)((float *)a.o + idx) = acc;
+            }
+        }
+    }
+    // the rung among the corrected rows: Pi S_in + sub_D (fp32 result)
+    for (int tt = 0; tt < ntp; ++tt) {
+        const int r = 16 * tt + m;
+        F8 B[KS];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            float v[8];
+            load8f(Pi + (int64_t)r * DK + 32 * kk + 8 * gq, v);
+            B[kk] = O::cvt8(v);
+        }
+#pragma unroll
+        for (int n = 0; n < CTW; ++n) {
+            const int64_t idx = (int64_t)r * DV + 16 * (n0 + n) + 4 * gq;
+            f32x4 acc = *(const f32x4 *)(rung_in + idx);
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) acc = O::mma32(acc, A[n][kk], B[kk]);
+            *(f32x4 *)(rung + idx) = acc;
+        }
+    }
+}
+
+template <int DK, int DV, bool BF>
+hipError_t launch_fixop_t(const EngineArgs &a, hipStream_t stream) {
+    const int64_t grid = (int64_t)a.n_units * a.H;
+    if (grid == 0) return hipSuccess;
+    if (grid > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((fixop_kernel<DK, DV, BF>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+    return hipGetLastError();
 }
 
 // Value blocks and M blocks of the segment packages in one grid, the M blocks
@@ -1109,6 +1356,7 @@ hipError_t launch_modes(int mode, const EngineArgs &a, hipStream_t s) {
         case kModeFixup: return launch_one<DK, DV, NB, BF, kModeFixup>(a, s);
         case kModePackageM: return launch_one<DK, DV, nb_m<DK, NB>(), BF, kModePackageM>(a, s);
         case kModePackageVM: return launch_package_vm<DK, DV, NB, BF>(a, s);
+        case kModeFixOp: return launch_fixop_t<DK, DV, BF>(a, s);
     }
     return hipErrorInvalidValue;
 }

@@ -29,8 +29,10 @@ __device__ __forceinline__ int opaque(int x) {
 // zero state (o_local, D, sub_D).  PackageM: the segment's linear part M (and
 // sub_M) from the identity.  Fixup: outputs corrected from S_in.  PackageVM:
 // value blocks and M blocks in one launch, the M blocks dispatched last.
+// FixOp: the fix-up of the units a fix-up operator covers (fixop_kernel).
 enum EngineMode : int {
-    kModePrefill = 0, kModePackage = 1, kModeFixup = 2, kModePackageM = 3, kModePackageVM = 4
+    kModePrefill = 0, kModePackage = 1, kModeFixup = 2, kModePackageM = 3, kModePackageVM = 4,
+    kModeFixOp = 5
 };
 
 // Arguments of the fused chunk engine (one workgroup per (unit, head,
@@ -64,6 +66,25 @@ struct EngineArgs {
     const int32_t *s_in_idx, *s_out_idx;
     int64_t n_slots;
     const int64_t *pos0;
+    // Fix-up operator (nullable).  Package: the M blocks write, for the first
+    // X_chunks chunks of unit u, X[u][t - t0][h] = their outputs (the
+    // identity's map to output t) and X_len[u][h][b] = the chunks after which
+    // columns 64b..64b+63 of the propagated identity are exactly zero (-1:
+    // not within X_chunks).  Fix-up: units whose X_len are all >= 0 are
+    // corrected from X instead of the recurrence.
+    void *X;                     // [n_units, X_chunks * 64, H, dk], io dtype
+    int32_t *X_len;              // [n_units, H, dk / 64]
+    int32_t X_chunks;
+    // and the propagated identity at the first rung of X_interval after the
+    // unit's start when it falls within the X_chunks chunks (nullable)
+    float *X_Pi;                 // [n_units, H, dk, dk]
+    int32_t X_interval;
+    // package of split segments: X_per sub-segments per segment, the operator
+    // of segment u / X_per written by its first sub-segment (0 or 1: none split)
+    int32_t X_per;
+    // FixOp writes the route of every unit (1: the recurrence), the fix-up
+    // launch after it skips the units with route 0 (nullable: none skipped).
+    int32_t *X_route;            // [n_units, H]
 };
 
 // Launches the engine.  bf16 selects bf16 I/O (bf16 MFMA operands) versus

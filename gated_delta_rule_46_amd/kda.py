@@ -22,7 +22,7 @@ CHUNK = 64
 EXPORTS = ("kda_prefill_workspace", "kda_prefill", "kda_prefill_noalloc", "kda_prefill_resume",
            "kda_segment_package", "kda_segment_package_workspace",
            "kda_segment_scan_workspace", "kda_segment_scan", "kda_output_fixup",
-           "kda_output_fixup_ckpt",
+           "kda_output_fixup_ckpt", "kda_segment_package_fx", "kda_output_fixup_fx",
            "kda_checkpoint_write", "kda_decode", "kda_short_conv", "kda_conv_halo",
            "kda_status_string", "kda_last_error", "kda_version")
 KDA_ACT_NONE, KDA_ACT_SILU = 0, 1
@@ -45,6 +45,11 @@ class kda_ckpt(ctypes.Structure):
                 ("states", ctypes.c_void_p)]
 
 
+class kda_fixop(ctypes.Structure):
+    _fields_ = [("chunks", ctypes.c_int32), ("interval", ctypes.c_int32), ("X", ctypes.c_void_p),
+                ("len", ctypes.c_void_p), ("route", ctypes.c_void_p), ("Pi", ctypes.c_void_p)]
+
+
 class kda_state_pool(ctypes.Structure):
     _fields_ = [("states", ctypes.c_void_p), ("n_slots", ctypes.c_int64),
                 ("read_idx", ctypes.c_void_p), ("write_idx", ctypes.c_void_p)]
@@ -63,6 +68,7 @@ def _load():
     P, S, I32, I64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
     cfgp, ckp = ctypes.POINTER(kda_config), ctypes.POINTER(kda_ckpt)
     poolp = ctypes.POINTER(kda_state_pool)
+    fxp = ctypes.POINTER(kda_fixop)
     convp = ctypes.POINTER(kda_conv_state)
     sig = {
         "kda_prefill_workspace": (S, [cfgp, I64, I32]),
@@ -78,6 +84,10 @@ def _load():
         "kda_output_fixup": (ctypes.c_int, [cfgp, P, P, P, P, I64, P, I32, P, P, P, S, P]),
         "kda_output_fixup_ckpt": (ctypes.c_int, [cfgp, P, P, P, P, I64, P, I32, P, P, ckp, P, P,
                                                  S, P]),
+        "kda_segment_package_fx": (ctypes.c_int, [cfgp, P, P, P, P, P, I64, P, I32, P, P, P,
+                                                  ckp, P, P, fxp, P, S, P]),
+        "kda_output_fixup_fx": (ctypes.c_int, [cfgp, P, P, P, P, I64, P, I32, P, P, ckp, P, fxp,
+                                               P]),
         "kda_checkpoint_write": (ctypes.c_int, [cfgp, ckp, I64, P, I32, P, P, P, P]),
         "kda_decode": (ctypes.c_int, [cfgp, I32, P, P, P, P, P, I32, poolp, P, P]),
         "kda_short_conv": (ctypes.c_int, [I32, I32, I32, I32, P, I64, P, I32, P, P, convp, P, P]),
@@ -344,6 +354,61 @@ def kda_segment_package(q, k, v, g, beta, seg_start, *, ckpt_interval=0, scale=1
     return o_local, M, D, sub_M, sub_D
 
 
+class FixOp:
+    """Fix-up operator buffers (kda_fixop): X [nseg, chunks * 64, H, dk] in
+    the I/O dtype, len [nseg, H, dk // 64] and route [nseg, H] int32, and with
+    a checkpoint interval Pi [nseg, H, dk, dk] fp32."""
+
+    def __init__(self, nseg, H, dk, dtype, device, chunks=6, interval=0):
+        self.chunks = int(chunks)
+        self.interval = int(interval)
+        self.Pi = (torch.empty((nseg, H, dk, dk), dtype=torch.float32, device=device)
+                   if self.interval else None)
+        self.X = torch.empty((nseg, self.chunks * CHUNK, H, dk), dtype=dtype, device=device)
+        self.len = torch.empty((nseg, H, dk // 64), dtype=torch.int32, device=device)
+        self.route = torch.empty((nseg, H), dtype=torch.int32, device=device)
+
+    def c(self):
+        return kda_fixop(self.chunks, self.interval, ctypes.c_void_p(self.X.data_ptr()),
+                         ctypes.c_void_p(self.len.data_ptr()),
+                         ctypes.c_void_p(self.route.data_ptr()),
+                         ctypes.c_void_p(self.Pi.data_ptr()) if self.Pi is not None else None)
+
+
+def kda_segment_package_fx(q, k, v, g, beta, seg_start, fx, *, ckpt_interval=0, scale=1.0,
+                           qk_l2norm=True, want_sub_M=True, split=True, stream=None):
+    """kda_segment_package that also fills the fix-up operator fx (a FixOp).
+    Returns (o_local, M, D, sub_M, sub_D).  split: as kda_segment_package."""
+    T, H, dk, dv, dev = _inputs(q, k, v, g, beta)
+    nseg = seg_start.numel() - 1
+    _need(seg_start, "seg_start", (nseg + 1,), torch.int64, dev)
+    _need(fx.X, "fx.X", (nseg, fx.chunks * CHUNK, H, dk), q.dtype, dev)
+    _need(fx.len, "fx.len", (nseg, H, dk // 64), torch.int32, dev)
+    cfg = make_config(H, dk, dv, q.dtype, scale, qk_l2norm)
+    o_local = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
+    M = torch.empty((nseg, H, dk, dk), dtype=torch.float32, device=dev)
+    D = torch.empty((nseg, H, dk, dv), dtype=torch.float32, device=dev)
+    sub_M = sub_D = None
+    ckp = None
+    if ckpt_interval:
+        rows = T // ckpt_interval
+        if want_sub_M:
+            sub_M = torch.empty((rows, H, dk, dk), dtype=torch.float32, device=dev)
+        sub_D = torch.empty((rows, H, dk, dv), dtype=torch.float32, device=dev)
+        if rows:
+            ckp = ctypes.pointer(kda_ckpt(int(ckpt_interval), None, None))
+    fxc = fx.c()
+    wsb = LIB.kda_segment_package_workspace(ctypes.byref(cfg), T, nseg) if split else 0
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+    st = LIB.kda_segment_package_fx(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(g), _p(beta), T,
+                                    _p(seg_start), nseg, _p(o_local), _p(M), _p(D), ckp,
+                                    _p(sub_M) if (ckp and sub_M is not None) else None,
+                                    _p(sub_D) if ckp else None, ctypes.byref(fxc), _p(ws), wsb,
+                                    _stream(stream))
+    _check(st, "kda_segment_package_fx")
+    return o_local, M, D, sub_M, sub_D
+
+
 def kda_segment_scan(M, D, S0=None, *, algo=KDA_SCAN_SEQUENTIAL, stream=None):
     """Prefix scan of the packages.  Returns (S_in [nseg,H,dk,dv], S_final [H,dk,dv])."""
     nseg, H, dk, _ = M.shape
@@ -410,6 +475,44 @@ def kda_output_fixup_ckpt(q, k, g, beta, seg_start, S_in, o, sub_D, *, interval,
                                    ctypes.byref(ck) if rows else None, _p(sub_D) if rows else None,
                                    None, 0, _stream(stream))
     _check(st, "kda_output_fixup_ckpt")
+    return states
+
+
+def kda_output_fixup_fx(q, k, g, beta, seg_start, S_in, o, fx, *, sub_D=None, interval=0,
+                        out=None, scale=1.0, qk_l2norm=True, stream=None):
+    """The fix-up of o (in place) with the operator fx (a FixOp, or None), and
+    with sub_D and interval also the checkpoint rungs (into `out` when given,
+    which may be sub_D itself); returns the rung states or None."""
+    T, H, dk = q.shape
+    dev = q.device
+    dv = o.shape[2]
+    nseg = seg_start.numel() - 1
+    _need(k, "k", (T, H, dk), q.dtype, dev)
+    _need(g, "g", (T, H, dk), torch.float32, dev)
+    _need(beta, "beta", (T, H), torch.float32, dev)
+    _need(o, "o", (T, H, dv), q.dtype, dev)
+    _need(seg_start, "seg_start", (nseg + 1,), torch.int64, dev)
+    _need(S_in, "S_in", (nseg, H, dk, dv), torch.float32, dev)
+    states = None
+    ck = None
+    rows = T // interval if interval else 0
+    if rows:
+        _need(sub_D, "sub_D", (rows, H, dk, dv), torch.float32, dev)
+        states = out if out is not None else torch.empty((rows, H, dk, dv), dtype=torch.float32,
+                                                         device=dev)
+        _need(states, "out", (rows, H, dk, dv), torch.float32, dev)
+        ck = kda_ckpt(int(interval), None, ctypes.c_void_p(states.data_ptr()))
+    if fx is not None:
+        _need(fx.X, "fx.X", (nseg, fx.chunks * CHUNK, H, dk), q.dtype, dev)
+        _need(fx.len, "fx.len", (nseg, H, dk // 64), torch.int32, dev)
+    fxc = fx.c() if fx is not None else None
+    cfg = make_config(H, dk, dv, q.dtype, scale, qk_l2norm)
+    st = LIB.kda_output_fixup_fx(ctypes.byref(cfg), _p(q), _p(k), _p(g), _p(beta), T,
+                                 _p(seg_start), nseg, _p(S_in), _p(o),
+                                 ctypes.byref(ck) if ck is not None else None,
+                                 _p(sub_D) if rows else None,
+                                 ctypes.byref(fxc) if fxc is not None else None, _stream(stream))
+    _check(st, "kda_output_fixup_fx")
     return states
 
 

@@ -324,6 +324,66 @@ int kda_output_fixup_ckpt(const kda_config *cfg, const void *q, const void *k, c
                           void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Fix-up operator of the segment packages (the chunked engine's shapes: not
+ * fp32 I/O with dk = 128).  The M blocks of the package launch propagate the
+ * identity through each segment until it is exactly zero; with the configs'
+ * gates that takes a few chunks.  With an operator they also keep, for the
+ * first `chunks` chunks of segment j, what that identity gives output row t:
+ *     X[j][t - seg_start[j]][h][:] = Pi_t^T qhat_t
+ * Pi_t maps segment j's incoming state to its state after token t, and qhat_t
+ * is the query as the outputs use it (normalised and scaled).  They also write
+ *     len[j][h][b] = the chunks after which columns 64b..64b+63 of the
+ *                    propagated identity are exactly zero,
+ * or -1 if that does not happen within `chunks` chunks.  Since every later
+ * row's correction is then exactly zero, the fix-up corrects a segment whose
+ * len are all >= 0 as o_t += (S_in^j)^T X_t over those rows, with no
+ * recurrence.  A segment walks the recurrence as kda_output_fixup_ckpt does
+ * when one of its len is -1, when its incoming state holds an infinity or a
+ * NaN, or when a checkpoint rung falls among the corrected rows and Pi does
+ * not cover it.  Pi covers the first rung after the segment start when the
+ * fix-up's checkpoint interval is fx->interval, as Pi S_in + sub_D; a second
+ * rung among the rows needs the recurrence.  The results equal the
+ * recurrence's up to rounding (X is rounded once to the I/O dtype).
+ * This recasts the pages' fix-up step; it is not a step the pages name.
+ */
+typedef struct kda_fixop {
+    int32_t chunks;    /* chunks of rows kept per segment, >= 1 */
+    int32_t interval;  /* checkpoint interval of Pi (a multiple of chunk), 0: no Pi */
+    void *X;           /* [nseg, chunks * chunk, H, dk] in io_dtype, 16-byte aligned;
+                          rows past a segment's end are not written */
+    int32_t *len;      /* [nseg, H, dk / 64], 4-byte aligned */
+    int32_t *route;    /* [nseg, H], 4-byte aligned: written and read by the
+                          fix-up (1 where a segment walks the recurrence) */
+    float *Pi;         /* [nseg, H, dk, dk], 16-byte aligned, or NULL: the
+                          propagated identity at the segment's first multiple
+                          of `interval` when it falls within the kept chunks */
+} kda_fixop;
+
+/* kda_segment_package that also writes the fix-up operator *fx.  M is
+ * required (the M blocks form the operator).  With the workspace that
+ * kda_segment_package_workspace asks for, the segments are split into
+ * sub-segments as kda_segment_package splits them; the operator then comes
+ * from each segment's first sub-segment (a segment whose identity has not
+ * vanished by the end of its first sub-segment gets len -1).
+ * KDA_ERR_UNSUPPORTED for fp32 I/O with dk = 128. */
+int kda_segment_package_fx(const kda_config *cfg, const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, int64_t T,
+                           const int64_t *seg_start, int32_t nseg, void *o_local, float *M,
+                           float *D, const kda_ckpt *ckpt, float *sub_M, float *sub_D,
+                           const kda_fixop *fx, void *ws, size_t ws_bytes, void *stream);
+
+/* kda_output_fixup_ckpt (ckpt may be NULL) with the operator that
+ * kda_segment_package_fx wrote for the same inputs, segments and chunks
+ * (fx = NULL: kda_output_fixup_ckpt).  Two launches: the segments the
+ * operator covers, one light workgroup each, then the recurrence for the
+ * others (its workgroups for covered segments end at once).  No workspace;
+ * calls sharing one fx must not overlap (route). */
+int kda_output_fixup_fx(const kda_config *cfg, const void *q, const void *k, const float *g,
+                        const float *beta, int64_t T, const int64_t *seg_start, int32_t nseg,
+                        const float *S_in, void *o, const kda_ckpt *ckpt, const float *sub_D,
+                        const kda_fixop *fx, void *stream);
+
+/*
  * Checkpoint states of the segment path: for every rung p (see kda_ckpt;
  * one sequence, so rows start at 0) inside segment j,
  *     states[p/interval - 1] = sub_M[row] S_in^j + sub_D[row]

@@ -76,6 +76,10 @@ def test_struct_layouts():
     # kda_state_pool: pointer, int64, two pointers
     assert ctypes.sizeof(K.kda_state_pool) == 32
     assert K.kda_state_pool.n_slots.offset == 8 and K.kda_state_pool.write_idx.offset == 24
+    # kda_fixop: two int32 + four pointers
+    assert K.kda_fixop.interval.offset == 4 and K.kda_fixop.X.offset == 8
+    assert K.kda_fixop.len.offset == 16 and K.kda_fixop.route.offset == 24
+    assert K.kda_fixop.Pi.offset == 32 and ctypes.sizeof(K.kda_fixop) == 40
 
 
 def test_status_strings_and_version():
@@ -333,6 +337,39 @@ def test_fixup_ckpt_validates():
     assert call(ckpt=ctypes.byref(ok), sub_D=MISALIGNED) == K.KDA_ERR_ALIGN
     assert call(S_in=None) == K.KDA_ERR_ARG
     assert call(nseg=0) == K.KDA_ERR_ARG
+
+
+def test_fixop_entry_points_validate():
+    """kda_segment_package_fx / kda_output_fixup_fx: the operator's fields,
+    M required for the package, fp32 dk = 128 (token-recurrent kernel) not
+    supported.  No call reaches the device."""
+    P = K.LIB
+
+    def pk(c, fx, M=FAKE):
+        return P.kda_segment_package_fx(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 2,
+                                        FAKE, M, FAKE, None, None, None,
+                                        ctypes.byref(fx) if fx is not None else None, None, 0,
+                                        None)
+
+    def fu(c, fx):
+        return P.kda_output_fixup_fx(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 128, FAKE, 2, FAKE,
+                                     FAKE, None, None, ctypes.byref(fx), None)
+    c = cfg()
+    assert pk(c, None) == K.KDA_ERR_ARG and "fx" in last_error()
+    assert pk(c, K.kda_fixop(0, 0, FAKE, FAKE, FAKE, None)) == K.KDA_ERR_ARG
+    assert pk(c, K.kda_fixop(4, 0, None, FAKE, FAKE, None)) == K.KDA_ERR_ARG
+    assert pk(c, K.kda_fixop(4, 0, MISALIGNED, FAKE, FAKE, None)) == K.KDA_ERR_ALIGN
+    assert pk(c, K.kda_fixop(4, 0, FAKE, FAKE + 2, FAKE, None)) == K.KDA_ERR_ALIGN
+    assert pk(c, K.kda_fixop(4, 0, FAKE, FAKE, None, None)) == K.KDA_ERR_ARG
+    assert pk(c, K.kda_fixop(4, 0, FAKE, FAKE, FAKE, None), M=None) == K.KDA_ERR_ARG
+    assert "needs M" in last_error()
+    assert fu(c, K.kda_fixop(-1, 0, FAKE, FAKE, FAKE, None)) == K.KDA_ERR_ARG
+    f32 = cfg(dk=128, dv=128, dtype=0)
+    assert pk(f32, K.kda_fixop(4, 0, FAKE, FAKE, FAKE, None)) == K.KDA_ERR_UNSUPPORTED
+    assert fu(f32, K.kda_fixop(4, 0, FAKE, FAKE, FAKE, None)) == K.KDA_ERR_UNSUPPORTED
+    assert pk(c, K.kda_fixop(4, 100, FAKE, FAKE, FAKE, FAKE)) == K.KDA_ERR_ARG     # not a chunk multiple
+    assert pk(c, K.kda_fixop(4, -64, FAKE, FAKE, FAKE, FAKE)) == K.KDA_ERR_ARG
+    assert pk(c, K.kda_fixop(4, 64, FAKE, FAKE, FAKE, MISALIGNED)) == K.KDA_ERR_ALIGN
 
 
 def test_package_split_workspace_query():

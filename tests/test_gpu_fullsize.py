@@ -91,32 +91,44 @@ def test_config1_all_heads(K, w1, path):
 # segment workloads
 # ---------------------------------------------------------------------------
 def run_segment_path(K, w, t, algo, interval):
-    """package -> scan -> fix-up writing the rungs, as one step of bench.py;
-    with rungs also kda_checkpoint_write from the sub-packages (a second
-    package call with sub_M).  Returns device tensors (o, o_local, M, D, S_in,
-    S_final, rungs or None, rungs of kda_checkpoint_write or None)."""
+    """package -> scan -> fix-up writing the rungs, as one step of bench.py:
+    the package with the fix-up operator, the fix-up from it with the rungs
+    formed in place in sub_D (fp32 I/O with dk = 128, which has no operator:
+    the plain package and fix-up).  With rungs also kda_checkpoint_write from
+    the sub-packages (a second package call with sub_M).  Returns device
+    tensors (o, o_local, M, D, S_in, S_final, rungs or None, rungs of
+    kda_checkpoint_write or None, the operator or None)."""
     S0 = None if t["S0"] is None else t["S0"][0].contiguous()
-    ol, M, D, _, sD = K.kda_segment_package(t["q"], t["k"], t["v"], t["g"], t["beta"],
-                                            t["seg_start"], ckpt_interval=interval,
-                                            scale=w.scale, qk_l2norm=bool(w.qk_l2norm),
-                                            want_sub_M=False)
+    nseg = len(w.seg_start) - 1
+    fx = None
+    if not (w.dtype == "f32" and w.dk == 128):
+        fx = K.FixOp(nseg, w.H, w.dk, t["q"].dtype, "cuda", interval=interval)
+        ol, M, D, _, sD = K.kda_segment_package_fx(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                                   t["seg_start"], fx, ckpt_interval=interval,
+                                                   scale=w.scale, qk_l2norm=bool(w.qk_l2norm),
+                                                   want_sub_M=False)
+    else:
+        ol, M, D, _, sD = K.kda_segment_package(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                                t["seg_start"], ckpt_interval=interval,
+                                                scale=w.scale, qk_l2norm=bool(w.qk_l2norm),
+                                                want_sub_M=False)
     S_in, S_fin = K.kda_segment_scan(M, D, S0, algo=algo)
     o = ol.clone()
     ck = ck2 = None
     if interval:
-        ck = K.kda_output_fixup_ckpt(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o,
-                                     sD, interval=interval, scale=w.scale,
-                                     qk_l2norm=bool(w.qk_l2norm))
+        ck = K.kda_output_fixup_fx(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o,
+                                   fx, sub_D=sD, interval=interval, out=sD, scale=w.scale,
+                                   qk_l2norm=bool(w.qk_l2norm))
         _, _, _, sM2, sD2 = K.kda_segment_package(t["q"], t["k"], t["v"], t["g"], t["beta"],
                                                   t["seg_start"], ckpt_interval=interval,
                                                   scale=w.scale, qk_l2norm=bool(w.qk_l2norm))
         ck2 = K.kda_checkpoint_write(t["seg_start"], S_in, sM2, sD2, T=w.T, interval=interval,
                                      dtype=t["q"].dtype)
     else:
-        K.kda_output_fixup(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o,
-                           scale=w.scale, qk_l2norm=bool(w.qk_l2norm))
+        K.kda_output_fixup_fx(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o, fx,
+                              scale=w.scale, qk_l2norm=bool(w.qk_l2norm))
     sync()
-    return dict(o=o, o_local=ol, M=M, D=D, S_in=S_in, S_final=S_fin, ckpt=ck, ckpt2=ck2)
+    return dict(o=o, o_local=ol, M=M, D=D, S_in=S_in, S_final=S_fin, ckpt=ck, ckpt2=ck2, fx=fx)
 
 
 def segment_parity(K, w, heads, algo, interval, check_packages=False):
@@ -167,12 +179,26 @@ def segment_parity(K, w, heads, algo, interval, check_packages=False):
     z = torch.zeros_like(r["o"])
     K.kda_output_fixup(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in_t, z,
                        scale=w.scale, qk_l2norm=bool(w.qk_l2norm))
+    # and the same from the fix-up operator (the recurrence where it declines)
+    zx = None
+    corr_x = UnitErrors("fix-up from the operator alone per (segment, head)")
+    if r["fx"] is not None:
+        zx = torch.zeros_like(r["o"])
+        K.kda_output_fixup_fx(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in_t, zx,
+                              r["fx"], scale=w.scale, qk_l2norm=bool(w.qk_l2norm))
+        lens = r["fx"].len.cpu().numpy()
+        say(f"  operator: {int((lens >= 0).all(axis=2).sum())} of {lens.shape[0] * lens.shape[1]} "
+            f"(segment, head) units corrected from X, len up to {int(lens.max())} chunks")
     sync()
     for s in seg_walk_meta(w):
         j, a, b = s
         corr_got = to_numpy_f64(z[a:b][:, ht])
         per_head(c.corr, j, hs, corr_got, corr_ref[j].astype(np.float64))
+        if zx is not None:
+            per_head(corr_x, j, hs, to_numpy_f64(zx[a:b][:, ht]), corr_ref[j].astype(np.float64))
     worst = c.check(OUT_TOL[dt], STATE_TOL[dt], say)
+    if corr_x.num:
+        worst[corr_x.what] = corr_x.check(OUT_TOL[dt], say)
     if rungs2.num:
         worst[rungs2.what] = rungs2.check(STATE_TOL[dt], say)
     ef = UnitErrors("S_final per head")

@@ -1051,6 +1051,179 @@ def test_fixup_ckpt_equals_checkpoint_write(K, gates, dtype, dk, dv):
 
 
 # ---------------------------------------------------------------------------
+# Fix-up operator: X from the M blocks, the fix-up as a product with X
+# ---------------------------------------------------------------------------
+FIXOP_SEG = [0, 448, 512, 1216, 1536, 2112]
+# segment [960, 1216) has the rung at 1024 among its first rows
+FIXOP_SEG_RUNG = [0, 448, 960, 1216, 1536, 2112]
+
+
+def _fixop_case(K, w, iv, chunks=6):
+    """package_fx -> Blelloch scan -> fix-up from the operator with the rungs
+    formed in place, beside the plain package and the recurrence's fix-up."""
+    import torch
+    t = to_torch(w)
+    nseg = len(w.seg_start) - 1
+    fx = K.FixOp(nseg, w.H, w.dk, t["q"].dtype, "cuda", chunks=chunks, interval=iv)
+    S0 = t["S0"][0].contiguous()
+    ol, M, D, _, sD = K.kda_segment_package_fx(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                               t["seg_start"], fx, ckpt_interval=iv,
+                                               want_sub_M=False)
+    S_in, S_fin = K.kda_segment_scan(M, D, S0, algo=1)
+    o = ol.clone()
+    ck = K.kda_output_fixup_fx(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o, fx,
+                               sub_D=sD, interval=iv, out=sD)
+    ol2, M2, D2, _, sD2 = K.kda_segment_package(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                                t["seg_start"], ckpt_interval=iv,
+                                                want_sub_M=False, split=False)
+    o2 = ol2.clone()
+    ck2 = K.kda_output_fixup_ckpt(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o2,
+                                  sD2, interval=iv)
+    sync()
+    return dict(t=t, fx=fx, o_local=(ol, ol2), M=(M, M2), D=(D, D2), o=(o, o2), ck=(ck, ck2),
+                S_in=S_in)
+
+
+@pytest.mark.parametrize("gates,iv,seg", [("config", 1024, FIXOP_SEG), ("config", 64, FIXOP_SEG),
+                                          ("long", 1024, FIXOP_SEG), ("config", 1024, FIXOP_SEG_RUNG),
+                                          ("config", 128, FIXOP_SEG_RUNG)],
+                         ids=["rungs-past", "rungs-64", "long", "rung-in-rows", "rungs-128"])
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 128, 128), ("f32", 64, 64), ("bf16", 64, 128),
+                                         ("bf16", 128, 64)])
+def test_fixop_segment_path(K, gates, iv, seg, dtype, dk, dv):
+    """The fix-up operator path against the oracle and against the
+    recurrence's fix-up.  The packages are the plain call's, bit for bit.
+    With the configs' gates the identity vanishes within a few chunks
+    (len >= 0).  With rungs every 1024 tokens every segment is corrected from
+    X; a single rung among a segment's corrected rows (the segment starting at
+    960) is formed from Pi.  Two rungs among those rows (rungs every 64 tokens)
+    send the segment to the recurrence, bit for bit as the plain fix-up.  With
+    long-memory gates the segments longer than the
+    operator's 6 chunks never vanish (len = -1) and walk the recurrence; the
+    shorter ones are covered whole by X."""
+    import torch
+    shift = {} if gates == "config" else dict(gate_shift=-9.0, beta_shift=-6.0)
+    w = make_workload("fixop", [2112], 2, dk, dv, dtype, 5400 + dk + dv + iv, s0_std=0.5,
+                      seg_start=seg, **shift)
+    say(f"fix-up operator {dtype} dk={dk} dv={dv} gates={gates} rungs every {iv} segments {seg}")
+    r = _fixop_case(K, w, iv)
+    lens = r["fx"].len.cpu().numpy()
+    say(f"  len per (segment, head, 64-column block): {lens.reshape(len(seg) - 1, -1).tolist()}")
+    route = r["fx"].route.cpu().numpy()
+    say(f"  route per (segment, head): {route.tolist()}")
+    nch = np.diff(seg) // 64 + (np.diff(seg) % 64 > 0)
+    if gates == "config":
+        assert (lens >= 1).all() and (lens <= 6).all()
+    else:   # a segment of at most 6 chunks is covered whole; the longer ones never vanish
+        for j, n in enumerate(nch):
+            assert (lens[j] == (n if n <= 6 else -1)).all(), (j, lens[j].tolist())
+    for name in ("o_local", "M", "D"):
+        assert torch.equal(*r[name]), f"{name} differs from the plain package call"
+    ro, rS, rck = oracle_full(w, interval=iv)
+    o, o2 = (to_numpy_f64(x) for x in r["o"])
+    ck, ck2 = (to_numpy_f64(x) for x in r["ck"])
+    assert_close("o (operator)", o, ro, OUT_TOL[dtype])
+    assert_close("rungs (operator, in place)", ck, rck, STATE_TOL[dtype])
+    assert_close("o: operator vs recurrence", o, o2, OUT_TOL[dtype])
+    assert_close("rungs: operator vs recurrence", ck, ck2, STATE_TOL[dtype])
+    # a segment routed to the recurrence is the plain fix-up's, bit for bit
+    for j in range(len(seg) - 1):
+        for hh in range(w.H):
+            if route[j, hh]:
+                assert np.array_equal(o[seg[j]:seg[j + 1], hh], o2[seg[j]:seg[j + 1], hh]), (j, hh)
+    if gates == "config" and iv == 64:   # two rungs among the first rows of segment 0
+        assert route[0].all()
+    if gates == "config" and seg is FIXOP_SEG_RUNG:   # one rung among them: Pi
+        assert not route[2].any()
+
+
+@pytest.mark.parametrize("gates", ["config", "long"])
+def test_fixop_split_segments(K, gates):
+    """The operator when kda_segment_package splits segments into
+    sub-segments (4 segments of 4096 tokens on 2 heads).  The first
+    sub-segment of each segment writes its operator.  With the configs' gates
+    the identity vanishes inside it; with long-memory gates it does not
+    (len = -1, the recurrence).  Outputs and rungs against the oracle, and
+    against the recurrence's fix-up."""
+    import torch
+    shift = {} if gates == "config" else dict(gate_shift=-9.0, beta_shift=-6.0)
+    seg = [0, 4096, 8192, 12288, 16384]
+    w = make_workload("fixop-split", [16384], 2, 128, 128, "bf16", 5495, s0_std=0.5,
+                      seg_start=seg, **shift)
+    say(f"fix-up operator on split segments (4 x 4096, H=2, bf16 d=128), gates={gates}")
+    t = to_torch(w)
+    iv = 1024
+    fx = K.FixOp(4, 2, 128, t["q"].dtype, "cuda", interval=iv)
+    ol, M, D, _, sD = K.kda_segment_package_fx(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                               t["seg_start"], fx, ckpt_interval=iv,
+                                               want_sub_M=False)
+    S_in, _ = K.kda_segment_scan(M, D, t["S0"][0].contiguous(), algo=0)
+    o = ol.clone()
+    ck = K.kda_output_fixup_fx(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o, fx,
+                               sub_D=sD, interval=iv, out=sD)
+    o2 = ol.clone()
+    ck2 = K.kda_output_fixup_ckpt(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o2,
+                                  sD.clone(), interval=iv)
+    sync()
+    lens, route = fx.len.cpu().numpy(), fx.route.cpu().numpy()
+    say(f"  len {lens.reshape(4, -1).tolist()} route {route.tolist()}")
+    if gates == "config":
+        assert (lens >= 1).all() and (route == 0).all()
+    else:
+        assert (lens == -1).all() and (route == 1).all()
+    ro, rS, rck = oracle_full(w, interval=iv)
+    assert_close("o (operator)", to_numpy_f64(o), ro, OUT_TOL["bf16"])
+    assert_close("rungs (operator)", to_numpy_f64(ck), rck, STATE_TOL["bf16"])
+    assert_close("o: operator vs recurrence", to_numpy_f64(o), to_numpy_f64(o2), OUT_TOL["bf16"])
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 128, 128), ("f32", 64, 64)])
+def test_fixop_rows_are_the_identity_outputs(K, dtype, dk, dv):
+    """Rows of X against the oracle's definition: the outputs of segment j
+    run from the identity as its incoming state (dk value columns), with
+    zero values.  Compared over the chunks its len covers."""
+    w = make_workload("fixop-x", [2112], 2, dk, dv, dtype, 5480 + dk, s0_std=0.5,
+                      seg_start=FIXOP_SEG)
+    say(f"fix-up operator rows vs the identity's outputs, {dtype} dk={dk}")
+    r = _fixop_case(K, w, 1024)
+    X = to_numpy_f64(r["fx"].X)
+    lens = r["fx"].len.cpu().numpy()
+    q, k, g, b = (w.f64(x) for x in ("q", "k", "g", "beta"))
+    H = w.H
+    for j in range(len(FIXOP_SEG) - 1):
+        a, e = FIXOP_SEG[j], FIXOP_SEG[j + 1]
+        n = e - a
+        S0 = np.broadcast_to(np.eye(dk), (1, H, dk, dk)).copy()
+        xo, _, _ = oracle.prefill(q[a:e], k[a:e], np.zeros((n, H, dk)), g[a:e], b[a:e], [0, n],
+                                  S0=S0, scale=w.scale, qk_l2norm=w.qk_l2norm)
+        for h in range(H):
+            for blk in range(dk // 64):
+                rows = min(n, int(lens[j, h, blk]) * 64)
+                cols = slice(64 * blk, 64 * blk + 64)
+                assert_close(f"X[{j}] head {h} columns {cols.start}..{cols.stop - 1}, {rows} rows",
+                             X[j, :rows, h, cols], xo[:rows, h, cols], OUT_TOL[dtype])
+                # past the vanishing point the identity's outputs are exactly zero
+                assert np.abs(xo[rows:, h, cols]).max(initial=0.0) < 1e-30
+
+
+def test_fixop_nonfinite_incoming_state(K):
+    """An incoming state with a NaN walks the recurrence: the outputs carry
+    NaN exactly where the plain fix-up puts it (the NaN reaches every S_in of
+    head 1 through the scan), and head 0's segments are corrected from X."""
+    import torch
+    w = make_workload("fixop-nan", [2112], 2, 128, 128, "bf16", 5490, s0_std=0.5,
+                      seg_start=FIXOP_SEG)
+    w.S0[0, 1, 3, 7] = np.nan
+    say("fix-up operator with a NaN in S0 (segment 0, head 1)")
+    r = _fixop_case(K, w, 1024)
+    o, o2 = (to_numpy_f64(x) for x in r["o"])
+    assert np.isnan(o).any()
+    assert np.array_equal(np.isnan(o), np.isnan(o2))
+    fin = ~np.isnan(o2)
+    assert_close("o (finite entries): operator vs recurrence", o[fin], o2[fin], OUT_TOL["bf16"])
+
+
+# ---------------------------------------------------------------------------
 # Packages of segments split into sub-segments (CUs otherwise idle)
 # ---------------------------------------------------------------------------
 SPLIT_CASES = [
