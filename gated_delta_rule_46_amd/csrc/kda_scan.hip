@@ -337,24 +337,26 @@ __global__ __launch_bounds__(NTH) void scan_seq_kernel(int H, int nseg, const fl
 
 // ---------------------------------------------------------------------------
 // Blelloch scan over packages (exclusive up-sweep / down-sweep over the
-// composition, identity-padded to a power of two) in one launch, grid (H, P):
-// the P workgroups of a head (two groups of four waves each)
+// composition, identity-padded to a power of two) in two launches:
 //
-//   1. test the units: unit u (package u, or S0 for u = nseg) on workgroup
-//      u mod P, group (u / P) mod 2: whether M is exactly zero, and whether
-//      M and D (or S0) hold an infinity or a NaN.  The flags go to the
-//      workspace and the head's workgroups meet (head_barrier);
-//   2. walk the tree on buffer ids.  Slots hold ids, not matrices: an id
-//      names a caller package, a fresh workspace buffer, the zero matrix or
-//      the identity.  For each tree level, wave 0 replays the level's
-//      compositions on the ids alone.  A wave's LDS accesses complete in
-//      order, so this needs no barrier.  It lists the compositions that
-//      really multiply; only those write a fresh buffer.  The workgroups
-//      share the list out: the M product on group 0, the D product or sum on
-//      group 1, fp32 MFMA.  They meet after every level that formed one.
-//      Every workgroup replays the same decisions;
-//   3. apply: S_in[j] = Pre_j.M S0 + Pre_j.D and S_final = Total.M S0 +
-//      Total.D.  Output j goes to workgroup j mod P, group (j / P) mod 2.
+//   blel_flags_kernel  grid (nseg + 1, H): per package, whether M is exactly
+//                      zero and whether M or D holds an infinity or a NaN;
+//                      block nseg tests S0;
+//   blel_kernel        grid (H, P), P workgroups of four waves per head (two
+//                      fit on a CU): the tree on buffer ids, then the outputs
+//                      S_in[j] = Pre_j.M S0 + Pre_j.D and S_final = Total.M S0
+//                      + Total.D, output j on workgroup j mod P.
+//
+// Slots hold buffer ids, not matrices: an id names a caller package, a fresh
+// workspace buffer, the zero matrix or the identity.  Wave 0 replays the tree
+// on the ids -- in registers, one slot per lane, when it has at most 64 slots,
+// else in LDS one level at a time (a wave's LDS accesses complete in order, so
+// either way without barriers) -- and lists the compositions that really
+// multiply; only those write a fresh buffer.  The head's workgroups share each
+// level's list out (a composition's M product, then its D product or sum, fp32
+// MFMA) and meet after every level that formed one (head_barrier).  Every
+// workgroup replays the same decisions.  With a zero M in every package (the
+// configs' gates) nothing is multiplied and no workgroup waits for another.
 //
 // A product with a zero factor is formed only when the other factor may hold
 // an infinity or a NaN (0 * inf and 0 * NaN are NaN), with zeros in place of
@@ -387,9 +389,9 @@ __device__ __forceinline__ void add_n(float *dst, const float *a, const float *b
     for (int i = 0; i < PER; ++i) ((f32x4 *)dst)[tid + i * NTH] = x[i] + y[i];
 }
 
-// Two groups of four waves: the M product of a composition on group 0 and
-// its D product (or sum) on group 1, at the same time.
-constexpr int NTH_TREE = 2 * NTH;
+// Four waves per workgroup; the slot ids and the level's list are 16-bit, so
+// that two workgroups fit in a CU's LDS.
+constexpr int NTH_TREE = NTH;
 
 // XCD (accelerator complex die) the wave runs on: hardware register
 // HW_REG_XCC_ID (20), bits [3:0].
@@ -479,8 +481,117 @@ __device__ __forceinline__ int load_flag(const int *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Flags of one unit per workgroup, grid (nseg + 1, H): package u (M exactly
+// zero or not; M or D holding an infinity or a NaN), or S0 for u = nseg.
 template <int DK, int DV>
-__global__ __launch_bounds__(NTH_TREE, 1) void blel_kernel(int H, int nseg, int size,
+__global__ __launch_bounds__(NTH) void blel_flags_kernel(int H, int nseg, const float *M,
+                                                         const float *D, const float *S0,
+                                                         BlelWs w) {
+    constexpr int PM = DK * DK / 4 / NTH, PD = DK * DV / 4 / NTH;
+    const int u = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+    const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
+    bool nz = false, bad = false;
+    if (u < nseg) {
+        const f32x4 *Mu = (const f32x4 *)(M + ((int64_t)u * H + h) * mm);
+        const f32x4 *Du = (const f32x4 *)(D + ((int64_t)u * H + h) * dd);
+        f32x4 a[PM], b[PD];
+#pragma unroll
+        for (int i = 0; i < PM; ++i) a[i] = Mu[t + i * NTH];
+#pragma unroll
+        for (int i = 0; i < PD; ++i) b[i] = Du[t + i * NTH];
+        uint32_t acc = 0u;
+#pragma unroll
+        for (int i = 0; i < PM; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                acc |= f32_bits(a[i][c]) & 0x7fffffffu;
+                bad |= nonfinite1(a[i][c]);
+            }
+#pragma unroll
+        for (int i = 0; i < PD; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) bad |= nonfinite1(b[i][c]);
+        nz = acc != 0u;
+    } else if (S0) {
+        const f32x4 *Su = (const f32x4 *)(S0 + (int64_t)h * dd);
+        f32x4 b[PD];
+#pragma unroll
+        for (int i = 0; i < PD; ++i) b[i] = Su[t + i * NTH];
+#pragma unroll
+        for (int i = 0; i < PD; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) bad |= nonfinite1(b[i][c]);
+    }
+    const int fnz = __syncthreads_or(nz) ? 1 : 0, fbad = __syncthreads_or(bad) ? 1 : 0;
+    if (t == 0) {
+        if (u < nseg) {
+            w.fz[u * H + h] = fnz;
+            w.fb[u * H + h] = fbad;
+        } else {
+            w.s0bad[h] = fbad;
+        }
+    }
+}
+
+// r <- l o e = (Ml Me, Ml De + Dl) on ids: the ids r takes, the products it
+// needs (M: mprod; D: dkind 1 a sum, 2 a product) and the operand kinds.  A
+// zero or identity factor is used as such only against finite values: under
+// IEEE arithmetic 0 * inf is NaN and I X spreads an inf or a NaN of X over
+// its column, so against a non-finite factor the product is formed (with the
+// zero or identity substituted).
+struct Decision {
+    int rm, rd, mprod, dkind, lk, ek;
+};
+__device__ __forceinline__ Decision decide(int ml, int dl, int bl, int me, int de, int be,
+                                           int nseg, int &nM, int &nD) {
+    const bool zl = ml == kIdZero, il = ml == kIdIdent;
+    const bool ze = me == kIdZero, ie = me == kIdIdent;
+    const bool dze = de == kIdZero, dzl = dl == kIdZero;
+    Decision r;
+    r.lk = zl ? kZero : il ? kIdent : kMem;
+    r.ek = ze ? kZero : ie ? kIdent : kMem;
+    r.mprod = 0;
+    r.dkind = 0;
+    if ((zl && (ze || !be)) || (ze && !bl)) {
+        r.rm = kIdZero;
+    } else if (il && !be) {
+        r.rm = me;
+    } else if (ie && !bl) {
+        r.rm = ml;
+    } else {
+        r.rm = nseg + nM++;
+        r.mprod = 1;
+    }
+    // D part: T = Ml De, then T + Dl
+    if ((zl && !be) || (dze && !bl)) {
+        r.rd = dl;
+    } else if (il && !be) {
+        if (dzl) {
+            r.rd = de;
+        } else {
+            r.rd = nseg + nD++;
+            r.dkind = 1;
+        }
+    } else {
+        r.rd = nseg + nD++;
+        r.dkind = 2;
+    }
+    return r;
+}
+
+// A record of a composition that multiplies: ml, me, rm, lk | ek << 2 | 16
+// (M product), dl, de, rd, dkind | dze << 2 | dzl << 3.
+__device__ __forceinline__ void put_record(short *pl, int ml, int me, int dl, int de,
+                                           const Decision &c) {
+    pl[0] = (short)ml; pl[1] = (short)me; pl[2] = (short)c.rm;
+    pl[3] = (short)(c.lk | (c.ek << 2) | (c.mprod << 4));
+    pl[4] = (short)dl; pl[5] = (short)de; pl[6] = (short)c.rd;
+    pl[7] = (short)(c.dkind | ((int)(de == kIdZero) << 2) | ((int)(dl == kIdZero) << 3));
+}
+
+// The tree and the outputs, grid (H, P), after blel_flags_kernel.
+template <int DK, int DV>
+__global__ __launch_bounds__(NTH_TREE, 2) void blel_kernel(int H, int nseg, int size,
                                                            const float *M, const float *D,
                                                            const float *S0, float *S_in,
                                                            float *S_final, BlelWs w, int P,
@@ -489,13 +600,15 @@ __global__ __launch_bounds__(NTH_TREE, 1) void blel_kernel(int H, int nseg, int 
     // not on the XCD the round-robin dispatch gives the head's first workgroup
     const bool misplaced = P > 1 && xcc_id() != (h & 7);
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
-    __shared__ int s_m[kMaxSize + 2], s_d[kMaxSize + 2], s_b[kMaxSize + 2];
-    // compositions of one level that multiply: {ml, me, rm, lk | ek << 2 | 16 (M product)},
-    // {dl, de, rd, kind (1 sum, 2 product) | dze << 2 | dzl << 3}
-    __shared__ int4 s_plan[kMaxSize / 2][2];
+    // slot ids (at most nseg + 4 * kMaxSize) and flags
+    __shared__ short s_m[kMaxSize + 2], s_d[kMaxSize + 2], s_b[kMaxSize + 2];
+    // the compositions that multiply (put_record): one level's, or with the
+    // tree in registers every level's, level lv from s_lvl[lv] to s_lvl[lv + 1]
+    __shared__ short s_plan[kMaxSize / 2][8];
     __shared__ int s_np;
+    __shared__ int s_lvl[2 * 6 + 2];
     constexpr int kPark = kMaxSize + 1;
-    const int grp = threadIdx.x / NTH, gw = (threadIdx.x / 64) % 4, gt = threadIdx.x % NTH;
+    const int gw = threadIdx.x / 64, gt = threadIdx.x;
     const int lane = threadIdx.x & 63;
     int rounds = 0;   // barriers passed
     int mixed = 0;    // a workgroup of this head is not on the head's XCD
@@ -517,191 +630,181 @@ __global__ __launch_bounds__(NTH_TREE, 1) void blel_kernel(int H, int nseg, int 
         return id < 0 ? nullptr : id < nseg ? D + ((int64_t)id * H + h) * dd
                                             : w.Dw + ((int64_t)(id - nseg) * H + h) * dd;
     };
-
-    // 1. flags of this workgroup's units (s_m, s_b as scratch)
-    for (int u = wp + P * grp; u <= nseg; u += 2 * P)
-        if (gt == 0) s_m[u] = s_b[u] = 0;
-    __syncthreads();
-    for (int u = wp + P * grp; u <= nseg; u += 2 * P) {
-        constexpr int PM = DK * DK / 4 / NTH, PD = DK * DV / 4 / NTH;
-        bool nz = false, bad = false;
-        if (u < nseg) {
-            const f32x4 *Mu = (const f32x4 *)(M + ((int64_t)u * H + h) * mm);
-            const f32x4 *Du = (const f32x4 *)(D + ((int64_t)u * H + h) * dd);
-            f32x4 a[PM], b[PD];
-#pragma unroll
-            for (int i = 0; i < PM; ++i) a[i] = Mu[gt + i * NTH];
-#pragma unroll
-            for (int i = 0; i < PD; ++i) b[i] = Du[gt + i * NTH];
-            uint32_t acc = 0u;
-#pragma unroll
-            for (int i = 0; i < PM; ++i)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    acc |= f32_bits(a[i][c]) & 0x7fffffffu;
-                    bad |= nonfinite1(a[i][c]);
-                }
-#pragma unroll
-            for (int i = 0; i < PD; ++i)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) bad |= nonfinite1(b[i][c]);
-            nz = acc != 0u;
-        } else if (S0) {
-            const f32x4 *Su = (const f32x4 *)(S0 + (int64_t)h * dd);
-            f32x4 b[PD];
-#pragma unroll
-            for (int i = 0; i < PD; ++i) b[i] = Su[gt + i * NTH];
-#pragma unroll
-            for (int i = 0; i < PD; ++i)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) bad |= nonfinite1(b[i][c]);
-        }
-        const bool wnz = __ballot(nz) != 0ull, wbad = __ballot(bad) != 0ull;
-        if (lane == 0 && wnz) atomicOr(&s_m[u], 1);
-        if (lane == 0 && wbad) atomicOr(&s_b[u], 1);
-    }
-    __syncthreads();
-    for (int u = wp + P * grp; u <= nseg; u += 2 * P) {
-        if (gt != 0) continue;
-        if (u < nseg) {
-            w.fz[u * H + h] = s_m[u];
-            w.fb[u * H + h] = s_b[u];
-        } else {
-            w.s0bad[h] = s_b[u];
-        }
-    }
-    meet();
-
-    // 2. the tree
-    for (int j = threadIdx.x; j < size; j += NTH_TREE) {
-        if (j < nseg) {
-            s_m[j] = load_flag(w.fz + j * H + h) ? j : kIdZero;
-            s_d[j] = j;
-            s_b[j] = load_flag(w.fb + j * H + h);
-        } else {   // identity padding
-            s_m[j] = kIdIdent;
-            s_d[j] = kIdZero;
-            s_b[j] = 0;
-        }
-    }
-    const bool s0bad = S0 && load_flag(w.s0bad + h);
-    __syncthreads();
-    int nM = 0, nD = 0;   // fresh buffers used (wave 0's count)
-    // r <- l o e = (Ml Me, Ml De + Dl) on ids, by the 64 lanes of wave 0 alike;
-    // the compositions that multiply are appended to s_plan
-    auto compose = [&](int l, int e, int r, int &np) __attribute__((always_inline)) {
-        const int ml = s_m[l], dl = s_d[l], bl = s_b[l];
-        const int me = s_m[e], de = s_d[e], be = s_b[e];
-        const bool zl = ml == kIdZero, il = ml == kIdIdent;
-        const bool ze = me == kIdZero, ie = me == kIdIdent;
-        const bool dze = de == kIdZero, dzl = dl == kIdZero;
-        // a zero or identity factor is used as such only against finite
-        // values: under IEEE arithmetic 0 * inf is NaN and I X spreads an inf
-        // or a NaN of X over its column, so against a non-finite factor the
-        // product is formed (with the zero or identity substituted)
-        const int lk = zl ? kZero : il ? kIdent : kMem, ek = ze ? kZero : ie ? kIdent : kMem;
-        int rm, rd, mprod = 0, dkind = 0;
-        if ((zl && (ze || !be)) || (ze && !bl)) {
-            rm = kIdZero;
-        } else if (il && !be) {
-            rm = me;
-        } else if (ie && !bl) {
-            rm = ml;
-        } else {
-            rm = nseg + nM++;
-            mprod = 1;
-        }
-        // D part: T = Ml De, then T + Dl
-        if ((zl && !be) || (dze && !bl)) {
-            rd = dl;
-        } else if (il && !be) {
-            if (dzl) {
-                rd = de;
-            } else {
-                rd = nseg + nD++;
-                dkind = 1;
-            }
-        } else {
-            rd = nseg + nD++;
-            dkind = 2;
-        }
-        if (mprod | dkind) {
-            s_plan[np][0] = int4{ml, me, rm, lk | (ek << 2) | (mprod << 4)};
-            s_plan[np][1] = int4{dl, de, rd, dkind | ((int)dze << 2) | ((int)dzl << 3)};
-            ++np;
-        }
-        s_m[r] = rm;
-        s_d[r] = rd;
-        s_b[r] = bl | be;
-    };
-    // the listed compositions of a level, shared out over the head's workgroups
-    auto form = [&](int np) __attribute__((always_inline)) {
-        for (int k = wp; k < np; k += P) {
-            const int4 pm = s_plan[k][0], pd = s_plan[k][1];
-            if (grp == 0 && (pm.w & 16)) {
+    // the listed compositions from record k0 to k1, shared out over the head's workgroups
+    auto form = [&](int k0, int k1) __attribute__((always_inline)) {
+        for (int k = k0 + wp; k < k1; k += P) {
+            const short *pl = s_plan[k];
+            const int ml = pl[0], me = pl[1], rm = pl[2], mw = pl[3];
+            const int dl = pl[4], de = pl[5], rd = pl[6], dw = pl[7];
+            if (mw & 16) {
                 Acc<DK, DK> am;
-                mm_acc<DK, DK>(mptr(pm.x), mptr(pm.y), am, pm.w & 3, (pm.w >> 2) & 3, gw);
-                store_acc<DK, DK>(am, nullptr, (float *)mptr(pm.z), gw);
+                mm_acc<DK, DK>(mptr(ml), mptr(me), am, mw & 3, (mw >> 2) & 3, gw);
+                store_acc<DK, DK>(am, nullptr, (float *)mptr(rm), gw);
             }
-            if (grp == 1 && (pd.w & 3) == 1) {
-                add_n<DK * DV>((float *)dptr(pd.z), dptr(pd.y), dptr(pd.x), gt);
-            } else if (grp == 1 && (pd.w & 3) == 2) {
+            if ((dw & 3) == 1) {
+                add_n<DK * DV>((float *)dptr(rd), dptr(de), dptr(dl), gt);
+            } else if ((dw & 3) == 2) {
                 Acc<DK, DV> ad;
-                mm_acc<DK, DV>(mptr(pm.x), dptr(pd.y), ad, pm.w & 3, (pd.w & 4) ? kZero : kMem, gw);
-                store_acc<DK, DV>(ad, (pd.w & 8) ? nullptr : dptr(pd.x), (float *)dptr(pd.z), gw);
+                mm_acc<DK, DV>(mptr(ml), dptr(de), ad, mw & 3, (dw & 4) ? kZero : kMem, gw);
+                store_acc<DK, DV>(ad, (dw & 8) ? nullptr : dptr(dl), (float *)dptr(rd), gw);
             }
         }
     };
+    const bool s0bad = S0 && load_flag(w.s0bad + h);
     // Levels lv < nlev: up-sweep with step 2^lv; lv == nlev: the root takes
     // the identity; lv > nlev: down-sweep with step size / 2^(lv - nlev).
-    // Wave 0 replays a level on the ids, then its products are formed.
     int nlev = 0;
     while ((1 << nlev) < size) ++nlev;
-    for (int lv = 0; lv <= 2 * nlev; ++lv) {
-        if (lv == nlev) {
-            if (threadIdx.x == 0) {
-                s_m[size] = s_m[size - 1];
-                s_d[size] = s_d[size - 1];
-                s_b[size] = s_b[size - 1];
-                s_m[size - 1] = kIdIdent;
-                s_d[size - 1] = kIdZero;
-                s_b[size - 1] = 0;
-            }
-            __syncthreads();
-            continue;
-        }
-        const bool up = lv < nlev;
-        const int step = up ? 1 << lv : size >> (lv - nlev);
+    int nM = 0, nD = 0;   // fresh buffers used (wave 0's count)
+    if (size <= 64) {
+        // Wave 0 replays the whole tree with the slots in registers (lane L
+        // holds slot L; the spare slot and the root's total are scalars) and
+        // lists every composition that multiplies; with none (a zero M
+        // everywhere) no workgroup waits for another.
         if (threadIdx.x < 64) {
-            int np = 0;
-            for (int i = 2 * step - 1; i < size; i += 2 * step) {
-                int l = i, e = i - step;
-                if (!up) {
-                    // (P[i-step], P[i]) <- (P[i], P[i-step] o P[i]); the old
-                    // P[i-step] waits in the spare slot
-                    s_m[kPark] = s_m[i - step];
-                    s_d[kPark] = s_d[i - step];
-                    s_b[kPark] = s_b[i - step];
-                    s_m[i - step] = s_m[i];
-                    s_d[i - step] = s_d[i];
-                    s_b[i - step] = s_b[i];
-                    l = kPark;
-                    e = i;
-                }
-                compose(l, e, i, np);
+            int sm, sd, sb;   // this lane's slot
+            if (lane < nseg) {
+                sm = load_flag(w.fz + lane * H + h) ? lane : kIdZero;
+                sd = lane;
+                sb = load_flag(w.fb + lane * H + h);
+            } else {   // identity padding
+                sm = kIdIdent;
+                sd = kIdZero;
+                sb = 0;
             }
-            s_np = np;
+            int tm = 0, td = 0, tb = 0;   // the total (root slot)
+            int np = 0;
+            auto rd_m = [&](int i) { return __builtin_amdgcn_readlane(sm, i); };
+            auto rd_d = [&](int i) { return __builtin_amdgcn_readlane(sd, i); };
+            auto rd_b = [&](int i) { return __builtin_amdgcn_readlane(sb, i); };
+            for (int lv = 0; lv <= 2 * nlev; ++lv) {
+                s_lvl[lv] = np;
+                if (lv == nlev) {
+                    tm = rd_m(size - 1);
+                    td = rd_d(size - 1);
+                    tb = rd_b(size - 1);
+                    if (lane == size - 1) {
+                        sm = kIdIdent;
+                        sd = kIdZero;
+                        sb = 0;
+                    }
+                    continue;
+                }
+                const bool up = lv < nlev;
+                const int step = up ? 1 << lv : size >> (lv - nlev);
+                for (int i = 2 * step - 1; i < size; i += 2 * step) {
+                    int ml, dl, bl;
+                    if (up) {
+                        ml = rd_m(i); dl = rd_d(i); bl = rd_b(i);
+                    } else {
+                        // (P[i-step], P[i]) <- (P[i], P[i-step] o P[i])
+                        ml = rd_m(i - step); dl = rd_d(i - step); bl = rd_b(i - step);
+                        const int pm = rd_m(i), pd = rd_d(i), pb = rd_b(i);
+                        if (lane == i - step) {
+                            sm = pm;
+                            sd = pd;
+                            sb = pb;
+                        }
+                    }
+                    const int e = up ? i - step : i;
+                    const int me = rd_m(e), de = rd_d(e), be = rd_b(e);
+                    const Decision c = decide(ml, dl, bl, me, de, be, nseg, nM, nD);
+                    if (c.mprod | c.dkind) put_record(s_plan[np++], ml, me, dl, de, c);
+                    if (lane == i) {
+                        sm = c.rm;
+                        sd = c.rd;
+                        sb = bl | be;
+                    }
+                }
+            }
+            s_lvl[2 * nlev + 1] = np;
+            if (lane < size) {
+                s_m[lane] = (short)sm;
+                s_d[lane] = (short)sd;
+                s_b[lane] = (short)sb;
+            }
+            if (lane == 0) {
+                s_m[size] = (short)tm;
+                s_d[size] = (short)td;
+                s_b[size] = (short)tb;
+            }
         }
         __syncthreads();
-        const int np = s_np;
-        form(np);
-        if (np > 0) meet();      // the products are visible to the next level
-        else __syncthreads();    // s_plan and s_np are rewritten by the next level
+        for (int lv = 0; lv <= 2 * nlev; ++lv) {
+            const int k0 = s_lvl[lv], k1 = s_lvl[lv + 1];
+            if (k1 == k0) continue;
+            form(k0, k1);
+            meet();   // the products are visible to the next level
+        }
+    } else {
+        // larger trees: slots in LDS; wave 0 replays one level at a time
+        for (int j = threadIdx.x; j < size; j += NTH_TREE) {
+            if (j < nseg) {
+                s_m[j] = (short)(load_flag(w.fz + j * H + h) ? j : kIdZero);
+                s_d[j] = (short)j;
+                s_b[j] = (short)load_flag(w.fb + j * H + h);
+            } else {   // identity padding
+                s_m[j] = kIdIdent;
+                s_d[j] = kIdZero;
+                s_b[j] = 0;
+            }
+        }
+        __syncthreads();
+        auto compose = [&](int l, int e, int r, int &np) __attribute__((always_inline)) {
+            const int ml = s_m[l], dl = s_d[l], bl = s_b[l];
+            const int me = s_m[e], de = s_d[e], be = s_b[e];
+            const Decision c = decide(ml, dl, bl, me, de, be, nseg, nM, nD);
+            if (c.mprod | c.dkind) put_record(s_plan[np++], ml, me, dl, de, c);
+            s_m[r] = (short)c.rm;
+            s_d[r] = (short)c.rd;
+            s_b[r] = (short)(bl | be);
+        };
+        for (int lv = 0; lv <= 2 * nlev; ++lv) {
+            if (lv == nlev) {
+                if (threadIdx.x == 0) {
+                    s_m[size] = s_m[size - 1];
+                    s_d[size] = s_d[size - 1];
+                    s_b[size] = s_b[size - 1];
+                    s_m[size - 1] = kIdIdent;
+                    s_d[size - 1] = kIdZero;
+                    s_b[size - 1] = 0;
+                }
+                __syncthreads();
+                continue;
+            }
+            const bool up = lv < nlev;
+            const int step = up ? 1 << lv : size >> (lv - nlev);
+            if (threadIdx.x < 64) {   // a wave's LDS accesses complete in order
+                int np = 0;
+                for (int i = 2 * step - 1; i < size; i += 2 * step) {
+                    int l = i, e = i - step;
+                    if (!up) {
+                        // (P[i-step], P[i]) <- (P[i], P[i-step] o P[i]); the
+                        // old P[i-step] waits in the spare slot
+                        s_m[kPark] = s_m[i - step];
+                        s_d[kPark] = s_d[i - step];
+                        s_b[kPark] = s_b[i - step];
+                        s_m[i - step] = s_m[i];
+                        s_d[i - step] = s_d[i];
+                        s_b[i - step] = s_b[i];
+                        l = kPark;
+                        e = i;
+                    }
+                    compose(l, e, i, np);
+                }
+                s_np = np;
+            }
+            __syncthreads();
+            const int np = s_np;
+            form(0, np);
+            if (np > 0) meet();      // the products are visible to the next level
+            else __syncthreads();    // s_plan and s_np are rewritten by the next level
+        }
     }
 
     // 3. S_in[j] = Pre_j.M S0 + Pre_j.D (slot j), S_final from the total (slot size)
     const float *s0 = S0 ? S0 + (int64_t)h * dd : nullptr;
-    for (int j = wp + P * grp; j <= nseg; j += 2 * P) {
+    for (int j = wp; j <= nseg; j += P) {
         const int slot = j < nseg ? j : size;
         const int idm = s_m[slot], idd = s_d[slot];
         float *out = j < nseg ? S_in + ((int64_t)j * H + h) * dd : S_final + (int64_t)h * dd;
@@ -956,6 +1059,10 @@ hipError_t scan_blel_t(int H, int nseg, const float *M, const float *D, const fl
     if (size > kMaxSize) return hipErrorInvalidValue;
     const BlelWs w = blel_ws<DK, DV>(ws, H, nseg);
     const int P = blel_width<DK, DV>(H);
+    hipLaunchKernelGGL((blel_flags_kernel<DK, DV>), dim3(nseg + 1, H), dim3(NTH), 0, s, H, nseg, M,
+                       D, S0, w);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((blel_kernel<DK, DV>), dim3(H, P), dim3(NTH_TREE), 0, s, H, nseg, size, M,
                        D, S0, S_in, S_final, w, P, next_epoch());
     return hipGetLastError();
