@@ -526,19 +526,19 @@ def main():
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
-    x_rows = 0
-    if segmented:   # rows of X the package launch writes (per 64-column block)
-        lens = fx.len.cpu().numpy().astype(np.int64)
-        seg_len = np.diff(np.asarray(w.seg_start, dtype=np.int64))
-        for j in range(nseg):
-            x_rows += int(np.minimum(np.clip(lens[j], 0, None) * 64, seg_len[j]).sum())
-        extra_bytes += x_rows * 64 * io_bytes
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(True)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = 1000.0 * elapsed / args.steps
+    if segmented:   # rows of X the package launch writes (per 64-column block), read after the steps
+        step(False)
+        torch.cuda.synchronize()
+        lens = np.clip(fx.len.cpu().numpy().astype(np.int64), 0, fx.chunks)
+        seg_len = np.diff(np.asarray(w.seg_start, dtype=np.int64))
+        x_rows = sum(int(np.minimum(lens[j] * 64, seg_len[j]).sum()) for j in range(nseg))
+        extra_bytes += x_rows * 64 * io_bytes
 
     def avg_ms(a, b):
         return float(np.mean([x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]))

@@ -1158,15 +1158,21 @@ __global__ __launch_bounds__(256) void fixop_kernel(EngineArgs a) {
     // the incoming state: zero and finiteness tests, staged in LDS in the
     // operand dtype on the way
     bool nz = false, bad = false;
-    for (int i = tid; i < DK * DV / 4; i += 256) {
-        const f32x4 x = ((const f32x4 *)Sin)[i];
+    {
+        constexpr int PS = DK * DV / 4 / 256;   // every load issued before the first is used
+        f32x4 x[PS];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            nz |= (f32_bits(x[c]) & 0x7fffffffu) != 0u;
-            bad |= (f32_bits(x[c]) & 0x7f800000u) == 0x7f800000u;
+        for (int q = 0; q < PS; ++q) x[q] = ((const f32x4 *)Sin)[tid + 256 * q];
+#pragma unroll
+        for (int q = 0; q < PS; ++q) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                nz |= (f32_bits(x[q][c]) & 0x7fffffffu) != 0u;
+                bad |= (f32_bits(x[q][c]) & 0x7f800000u) == 0x7f800000u;
+            }
+            const int i = tid + 256 * q, row = (4 * i) / DV, col = (4 * i) % DV;
+            *(F4 *)(s_S + row * LDS_ROW + col) = O::cvt4(x[q]);
         }
-        const int row = (4 * i) / DV, col = (4 * i) % DV;
-        *(F4 *)(s_S + row * LDS_ROW + col) = O::cvt4(x);
     }
     const int fl = (__syncthreads_or(nz) ? 1 : 0) | (__syncthreads_or(bad) ? 2 : 0);
     int64_t pi_rung = -1;
@@ -1256,23 +1262,41 @@ __global__ __launch_bounds__(256) void fixop_kernel(EngineArgs a) {
             }
         }
     }
-    // the rung among the corrected rows: Pi S_in + sub_D (fp32 result)
-    for (int tt = 0; tt < ntp; ++tt) {
-        const int r = 16 * tt + m;
-        F8 B[KS];
+    // the rung among the corrected rows: Pi S_in + sub_D (fp32 result), TB
+    // row tiles of Pi at a time with their loads issued together
+    for (int tb = 0; tb < ntp; tb += TB) {
+        f32x4 pv[TB][KS][2], rv[TB][CTW];
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            float v[8];
-            load8f(Pi + (int64_t)r * DK + 32 * kk + 8 * gq, v);
-            B[kk] = O::cvt8(v);
+        for (int q = 0; q < TB; ++q) {
+            const int r = 16 * (tb + q < ntp ? tb + q : ntp - 1) + m;
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                const f32x4 *pp = (const f32x4 *)(Pi + (int64_t)r * DK + 32 * kk + 8 * gq);
+                pv[q][kk][0] = pp[0];
+                pv[q][kk][1] = pp[1];
+            }
+#pragma unroll
+            for (int n = 0; n < CTW; ++n)
+                rv[q][n] = *(const f32x4 *)(rung_in + (int64_t)r * DV + 16 * (n0 + n) + 4 * gq);
         }
 #pragma unroll
-        for (int n = 0; n < CTW; ++n) {
-            const int64_t idx = (int64_t)r * DV + 16 * (n0 + n) + 4 * gq;
-            f32x4 acc = *(const f32x4 *)(rung_in + idx);
+        for (int q = 0; q < TB; ++q) {
+            if (tb + q >= ntp) break;
+            const int r = 16 * (tb + q) + m;
+            F8 B[KS];
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) acc = O::mma32(acc, A[n][kk], B[kk]);
-            *(f32x4 *)(rung + idx) = acc;
+            for (int kk = 0; kk < KS; ++kk) {
+                const float v[8] = {pv[q][kk][0][0], pv[q][kk][0][1], pv[q][kk][0][2], pv[q][kk][0][3],
+                                    pv[q][kk][1][0], pv[q][kk][1][1], pv[q][kk][1][2], pv[q][kk][1][3]};
+                B[kk] = O::cvt8(v);
+            }
+#pragma unroll
+            for (int n = 0; n < CTW; ++n) {
+                f32x4 acc = rv[q][n];
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) acc = O::mma32(acc, A[n][kk], B[kk]);
+                *(f32x4 *)(rung + (int64_t)r * DV + 16 * (n0 + n) + 4 * gq) = acc;
+            }
         }
     }
 }
