@@ -225,10 +225,13 @@ constexpr int64_t kMinSubSplit = 512;
 
 struct PackageSplit {
     int f = 1;
-    size_t off_sb = 0, off_ord = 0, off_M = 0, off_D = 0, bytes = 0;
+    size_t off_sb = 0, off_ord = 0, off_M = 0, off_D = 0, off_X = 0, off_Xlen = 0, off_Pi = 0,
+           off_route = 0, bytes = 0;
+    bool fixop = false;   // the later sub-segments keep their fix-up operators
 };
 
-bool plan_package_split(const kda_config *cfg, int64_t T, int32_t nseg, PackageSplit *p) {
+bool plan_package_split(const kda_config *cfg, int64_t T, int32_t nseg, PackageSplit *p,
+                        bool fixop = true) {
     if (nseg <= 0 || T <= 0) return false;
     const int64_t units = (int64_t)nseg * cfg->num_heads;
     const int cus = device_cus();
@@ -245,6 +248,16 @@ bool plan_package_split(const kda_config *cfg, int64_t T, int32_t nseg, PackageS
     p->off_ord = take(sizeof(int32_t) * (size_t)(f - 1) * nseg);
     p->off_M = take(sizeof(float) * nsub * H * cfg->dk * cfg->dk);
     p->off_D = take(sizeof(float) * nsub * H * cfg->dk * cfg->dv);
+    // the fix-up operators of sub-segments 1..f-1 (the chunked engine's shapes only)
+    const bool bf = cfg->io_dtype == KDA_DTYPE_BF16;
+    p->fixop = fixop && !kda::recurrent_supported(bf, cfg->dk, cfg->dv);
+    if (p->fixop) {
+        const size_t later = (size_t)(f - 1) * nseg, io = bf ? 2 : 4;
+        p->off_X = take(later * kSplitFixopChunks * kda::kChunk * H * cfg->dk * io);
+        p->off_Xlen = take(later * H * (cfg->dk / 64) * sizeof(int32_t));
+        p->off_Pi = take(later * H * cfg->dk * cfg->dk * sizeof(float));
+        p->off_route = take(nsub * H * sizeof(int32_t));
+    }
     p->bytes = at;
     return true;
 }
@@ -273,9 +286,20 @@ int package_split(const PackageSplit &p, const kda_config *cfg, const void *q, c
     a.scale = cfg->scale; a.l2norm = cfg->qk_l2norm;
     a.ncb = dv / nb;
     a.ncb_m = dk / std::min(nb, dk);
+    a.X_per = f;
+    a.S_last = D; a.M_last = M;   // the last sub-segments' packages: where the merge ends
     if (fxo) {   // the operator of each segment from its first sub-segment's M blocks
-        a.X = fxo->X; a.X_len = fxo->len; a.X_chunks = fxo->chunks; a.X_per = f;
+        a.X = fxo->X; a.X_len = fxo->len; a.X_chunks = fxo->chunks;
         a.X_Pi = fxo->interval > 0 ? fxo->Pi : nullptr; a.X_interval = fxo->interval;
+    }
+    const bool rung_pi = interval > 0 && sub_D;
+    const size_t x_slot = (size_t)kSplitFixopChunks * kda::kChunk * H * dk * (bf ? 2 : 4);
+    if (p.fixop) {   // and the operators of the later sub-segments, for the merge below
+        a.Xs = w + p.off_X; a.Xs_len = (int32_t *)(w + p.off_Xlen);
+        a.Xs_chunks = kSplitFixopChunks;
+        if (rung_pi) {
+            a.Xs_Pi = (float *)(w + p.off_Pi); a.Xs_interval = interval;
+        }
     }
     if ((e = kda::launch_engine(kda::kModePackageVM, bf, dk, dv, nb, a, s)) != hipSuccess)
         return launched(e, "package split (packages)");
@@ -289,10 +313,24 @@ int package_split(const PackageSplit &p, const kda_config *cfg, const void *q, c
         fx.bounds = sb; fx.order = ord + (size_t)(kk - 1) * nseg; fx.n_units = nseg; fx.H = H;
         fx.S_init = (const float *)((uintptr_t)Ds - slot * sizeof(float));
         fx.scale = cfg->scale; fx.l2norm = cfg->qk_l2norm;
-        if (interval > 0 && sub_D) {   // rungs inside it: in place
+        if (rung_pi) {   // rungs inside it: in place
             fx.interval = interval; fx.ckpt_S = sub_D; fx.ckpt_in = sub_D;
         }
         fx.ncb = dv / nbf;
+        if (p.fixop) {   // the sub-segments their operators cover, then the recurrence for the rest
+            const size_t at = (size_t)(kk - 1) * nseg;
+            kda::EngineArgs x = fx;
+            x.X = w + p.off_X + at * x_slot;
+            x.X_len = (int32_t *)(w + p.off_Xlen) + at * H * (dk / 64);
+            x.X_chunks = kSplitFixopChunks;
+            if (rung_pi) {
+                x.X_Pi = (float *)(w + p.off_Pi) + at * H * dk * dk; x.X_interval = interval;
+            }
+            x.X_route = (int32_t *)(w + p.off_route);
+            if ((e = kda::launch_engine(kda::kModeFixOp, bf, dk, dv, nbf, x, s)) != hipSuccess)
+                return launched(e, "package split (fix-up operator)");
+            fx.X_route = x.X_route;
+        }
         if ((e = kda::launch_engine(kda::kModeFixup, bf, dk, dv, nbf, fx, s)) != hipSuccess)
             return launched(e, "package split (fix-up)");
         if (interval > 0 && sub_M) {
@@ -528,7 +566,10 @@ int package_impl(const kda_config *cfg, const void *q, const void *k, const void
     }
     hipStream_t s = (hipStream_t)stream;
     PackageSplit sp;
-    if (ws && plan_package_split(cfg, T, nseg, &sp) && ws_bytes >= sp.bytes) {
+    // the split with the sub-segments' fix-up operators, else without them
+    // when the workspace holds only that
+    if (ws && ((plan_package_split(cfg, T, nseg, &sp) && ws_bytes >= sp.bytes) ||
+               (plan_package_split(cfg, T, nseg, &sp, false) && ws_bytes >= sp.bytes))) {
         KDA_TRY(check_tensor(ws, "ws", true));
         return package_split(sp, cfg, q, k, v, g, beta, T, seg_start, nseg, o_local, M, D,
                              subs ? ckpt->interval : 0, subs ? sub_M : nullptr,

@@ -42,6 +42,7 @@
 
 #pragma once
 
+#include <atomic>
 #include <type_traits>
 
 #include "kda_internal.h"
@@ -280,8 +281,31 @@ template <int MODE, bool MB> struct Roles {
     static constexpr bool CHECK0 = (MODE == kModeFixup) || MB;   // stop once S is exactly 0
 };
 
-// Fix-up of unit u from the operator X (fixop_kernel): the chunks of rows to
-// correct, or -1 when the unit walks the recurrence instead.  That is the case
+// The operator that the M block of unit u writes.  Unsplit units and the
+// first sub-segment of a split segment write their segment's (X, at u /
+// X_per); a later sub-segment writes its own (Xs, when given).  `whole`: the
+// operator covers the block's unit and no more, so a count at the block's end
+// is valid without the identity having vanished.
+struct XOut {
+    void *X;
+    int32_t *len;
+    float *Pi;
+    int64_t slot;
+    int chunks, interval;
+    bool whole;
+};
+__device__ __forceinline__ XOut x_out(const EngineArgs &a, int u) {
+    if (a.X_per > 1 && u % a.X_per != 0)
+        return {a.Xs, a.Xs_len, a.Xs_Pi,
+                (int64_t)(u % a.X_per - 1) * (a.n_units / a.X_per) + u / a.X_per, a.Xs_chunks,
+                a.Xs_interval, true};
+    return {a.X, a.X_len, a.X_Pi, a.X_per > 1 ? u / a.X_per : u, a.X_chunks, a.X_interval,
+            a.X_per <= 1};
+}
+
+// Fix-up of a unit [t0, t1) from the operator X at index xu (fixop_kernel):
+// the chunks of rows to correct, or -1 when the unit walks the recurrence
+// instead.  That is the case
 // with no operator; with a 64-column block whose identity had not vanished
 // within X_chunks chunks, or a count outside [0, X_chunks] (the bound keeps
 // every row of X read in range); with an incoming state holding an infinity or
@@ -290,14 +314,14 @@ template <int MODE, bool MB> struct Roles {
 // the segment start, and only at the operator's interval; a second rung among
 // the rows needs the recurrence.  pi_rung returns the covered rung (or -1).
 template <int DK>
-__device__ __forceinline__ int fixup_x_chunks(const EngineArgs &a, int u, int h, int64_t t0,
+__device__ __forceinline__ int fixup_x_chunks(const EngineArgs &a, int xu, int h, int64_t t0,
                                               int64_t t1, int flags, int64_t &pi_rung) {
     pi_rung = -1;
     if (!a.X || !a.X_len || (flags & 2)) return -1;
     int lmax = 0;
 #pragma unroll
     for (int j = 0; j < DK / 64; ++j) {
-        const int l = a.X_len[((int64_t)u * a.H + h) * (DK / 64) + j];
+        const int l = a.X_len[((int64_t)xu * a.H + h) * (DK / 64) + j];
         if (l < 0 || l > a.X_chunks) return -1;
         lmax = l > lmax ? l : lmax;
     }
@@ -327,10 +351,9 @@ __device__ __forceinline__ void producer(const EngineArgs &a, unsigned char *sme
     using L = Lds<DK, NB, BF>;
     using R = Roles<MODE, MB>;
     constexpr int KS = DK / 32;      // 32-channel steps of a row
-    // M blocks with a fix-up operator also form the outputs of their first
-    // X_chunks chunks (the rows of X); other M blocks form none.  (Of split
-    // segments only the first sub-segment writes the operator.)
-    const int xch = (MB && a.X && (a.X_per <= 1 || u % a.X_per == 0)) ? a.X_chunks : 0;
+    // M blocks with a fix-up operator also form the outputs of its first
+    // chunks (the rows of X); other M blocks form none.
+    const int xch = MB ? (x_out(a, u).X ? x_out(a, u).chunks : 0) : 0;
     auto out_on = [&](int c) { return R::HAS_O || c < xch; };
     constexpr int W8 = BF ? 4 : 8;
 
@@ -713,12 +736,11 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
     constexpr int DKT = DK / 16;     // state row tiles
     constexpr int LDST = MB ? DK : DV;
     static_assert(NTW >= 1, "tile shape");
-    // M blocks with a fix-up operator also form the outputs of their first
-    // X_chunks chunks, into X (the producers prepare their Qbar and P).  Of
-    // split segments (X_per sub-segments each) the first sub-segment writes
-    // the operator of its segment, ux.
-    const int xch = (MB && a.X && (a.X_per <= 1 || u % a.X_per == 0)) ? a.X_chunks : 0;
-    const int ux = a.X_per > 1 ? u / a.X_per : u;
+    // M blocks with a fix-up operator also form the outputs of its first
+    // chunks, into its rows (the producers prepare their Qbar and P).
+    const XOut xo = MB ? x_out(a, u) : XOut{};
+    const int xch = MB && xo.X ? xo.chunks : 0;
+    const int64_t ux = xo.slot;
     auto out_on = [&](int c) { return R::HAS_O || c < xch; };
 
     int *s_flag = (int *)(smem + L::o_flag);
@@ -790,12 +812,12 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
     auto put_rows = [&](int c, const f32x4 (&Ot)[4][NTW]) {
         const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
         const int64_t r0 = t0 + (int64_t)c * kChunk;
-        unsigned char *base = MB ? (unsigned char *)a.X : (unsigned char *)a.o;
+        unsigned char *base = MB ? (unsigned char *)xo.X : (unsigned char *)a.o;
 #pragma unroll
         for (int mu = 0; mu < 4; ++mu) {
             const int64_t tok = r0 + 16 * mu + m;
             const bool valid = tok < t1;
-            const int64_t row = MB ? ((int64_t)ux * a.X_chunks * kChunk + (tok - t0)) * H + h
+            const int64_t row = MB ? (ux * xch * kChunk + (tok - t0)) * H + h
                                    : tok * H + h;
 #pragma unroll
             for (int n = 0; n < NTW; ++n) {
@@ -1006,10 +1028,10 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
         }
         // M blocks with an operator: the propagated identity at the first rung
         // of the operator's interval after the segment start, within its chunks
-        if (MB && xch > 0 && a.X_Pi && a.X_interval > 0 && c < a.X_chunks) {
+        if (MB && xch > 0 && xo.Pi && xo.interval > 0 && c < xch) {
             const int64_t p = t0 + (int64_t)(c + 1) * kChunk;
-            if (p <= t1 && p == (t0 / a.X_interval + 1) * a.X_interval)
-                store_state<DKT, NTW>(a.X_Pi + ((int64_t)ux * H + h) * DK * DK, DK, wcol, gq, m, S, false);
+            if (p <= t1 && p == (t0 / xo.interval + 1) * xo.interval)
+                store_state<DKT, NTW>(xo.Pi + (ux * H + h) * DK * DK, DK, wcol, gq, m, S, false);
         }
         if (R::CHECK0) {
             const bool nz = state_nonzero();
@@ -1023,9 +1045,9 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
     // first sub-segment that did not vanish.
     auto put_len = [&](int c, bool vanished) {
         if (xch > 0 && pw == 0 && lane == 0) {
-            const int l = (vanished || a.X_per <= 1) && c <= a.X_chunks ? c : -1;
+            const int l = (vanished || xo.whole) && c <= xch ? c : -1;
             for (int j = cbase / 64; j < (cbase + NB) / 64; ++j)
-                a.X_len[((int64_t)ux * H + h) * (DK / 64) + j] = l;
+                xo.len[(ux * H + h) * (DK / 64) + j] = l;
         }
     };
 
@@ -1037,19 +1059,19 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
             // The state after chunk c-1 is exactly zero and stays zero.
             if (MB) {
                 put_len(c, true);
-                if (xch > 0 && a.X_Pi && a.X_interval > 0) {   // Pi of a rung not reached: zero
-                    const int64_t first = (t0 / a.X_interval + 1) * a.X_interval;
+                if (xch > 0 && xo.Pi && xo.interval > 0) {   // Pi of a rung not reached: zero
+                    const int64_t first = (t0 / xo.interval + 1) * xo.interval;
                     if (first >= t0 + (int64_t)c * kChunk && first <= t1 &&
-                        first <= t0 + (int64_t)a.X_chunks * kChunk)
-                        store_state<DKT, NTW>(a.X_Pi + ((int64_t)ux * H + h) * DK * DK, DK, wcol, gq,
-                                              m, S, true);
+                        first <= t0 + (int64_t)xch * kChunk)
+                        store_state<DKT, NTW>(xo.Pi + (ux * H + h) * DK * DK, DK, wcol, gq, m, S, true);
                 }
                 if (a.interval > 0 && a.ckpt_M) {
                     const int64_t first = (t0 + (int64_t)c * kChunk) / a.interval + 1;
                     for (int64_t mm = first; mm * a.interval <= t1; ++mm)
                         store_state<DKT, NTW>(a.ckpt_M + ((mm - 1) * H + h) * DK * DK, DK, wcol, gq, m, S, true);
                 }
-                store_state<DKT, NTW>(a.M_out + (int64_t)(u * H + h) * DK * DK, DK, wcol, gq, m, S, true);
+                store_state<DKT, NTW>(package_slot(a.M_out, a.M_last, a.X_per, u, H, h, DK * DK), DK,
+                                      wcol, gq, m, S, true);
             }
             copy_rungs_after(t0 + (int64_t)c * kChunk);
             return;
@@ -1072,8 +1094,12 @@ __device__ __forceinline__ void consumer(const EngineArgs &a, unsigned char *sme
     }
     if (MODE == kModePackage || MODE == kModePackageM) {
         put_len(nchunks, false);
-        if (MB) store_state<DKT, NTW>(a.M_out + (int64_t)(u * H + h) * DK * DK, DK, wcol, gq, m, S, false);
-        else store_state<DKT, NTW>(a.S_out + (int64_t)(u * H + h) * DK * DV, DV, wcol, gq, m, S, false);
+        if (MB)
+            store_state<DKT, NTW>(package_slot(a.M_out, a.M_last, a.X_per, u, H, h, DK * DK), DK, wcol,
+                                  gq, m, S, false);
+        else
+            store_state<DKT, NTW>(package_slot(a.S_out, a.S_last, a.X_per, u, H, h, DK * DV), DV, wcol,
+                                  gq, m, S, false);
     }
 }
 
@@ -1126,187 +1152,221 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_engine(EngineArgs a) {
     engine_body<DK, DV, NB, BF, MODE, MODE == kModePackageM>(a, smem, u, h, cb * NB, t0, t1);
 }
 
-// Fix-up from the operator, one workgroup of four waves per (segment, head).
-// It tests the incoming state (zero, finite) and decides the unit's route
-// (fixup_x_chunks).  Route 1 leaves the unit to the recurrence of the engine's
-// fix-up launch that follows.  Otherwise it adds
+// Workgroups per unit of the fix-up operator (host side): about two per
+// compute unit over the launch, at most one per item.  (Measured on the
+// 131,072-token workload's 512 units: one workgroup per unit beats spreading
+// the items, since each extra workgroup reads S_in again; with 128 units,
+// three or four per unit are fastest.)
+inline int fixop_spread(int64_t units, int items) {
+    static std::atomic<int> cache[64];
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+        cus = cache[dev].load(std::memory_order_relaxed);
+        if (cus <= 0) {
+            if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+                cus <= 0)
+                cus = 256;
+            cache[dev].store(cus, std::memory_order_relaxed);
+        }
+    }
+    const int64_t y = (2 * (int64_t)cus + units - 1) / units;
+    return (int)(y < 1 ? 1 : y > items ? items : y);
+}
+
+// Fix-up from the operator.  Grid (n_units * H, Y), four waves per
+// workgroup; the segment of x-index i * H + h is order[i] when an order is
+// given, and its operator is read at i.  The unit's items are its chunks
+// c < X_chunks, each adding
 //     o_t += S_in^T X_t
-// over the rows of the chunks X covers.  A rung among those rows gets
-//     Pi S_in + sub_D
-// (Pi: the propagated identity there); the unit's other rungs are sub_D
-// (copied when they go to their own buffer).  The products run on the matrix
-// cores as the engine's output product does: wave w holds S_in's value-column
-// tiles w*CT/4.. as operands (in the operand dtype) and multiplies every
-// 16-row tile of X, then of Pi, in place of Qbar.
+// over the chunk's 64 rows when the operator covers them, and the four
+// quarters of the rung among the corrected rows (rows 32p..32p+31 of
+// Pi S_in + sub_D, Pi: the propagated identity there); workgroup y takes
+// items y, y + Y, ...  Every workgroup with work loads S_in and tests it
+// (zero, finite), and all take the same route decision (fixup_x_chunks);
+// workgroup 0 writes it and copies the unit's other rungs when they go to
+// their own buffer (they are sub_D).  Route 1 leaves the unit to the
+// recurrence of the engine's fix-up launch that follows.  Each wave loads
+// its value columns of S_in straight into matrix-core operand registers (the
+// four waves read S_in once), with the rows of its first item and the values
+// they update, so a workgroup with one item waits for memory once.  With
+// n_units * H a multiple of 8 the workgroups of a unit run on one XCD and
+// share S_in through its L2.
 template <int DK, int DV, bool BF>
 __global__ __launch_bounds__(256) void fixop_kernel(EngineArgs a) {
     using O = Ops<BF>;
     using T = typename O::T;
     using F8 = typename O::F8;
-    using F4 = typename O::F4;
     constexpr int KS = DK / 32;        // 32-deep steps
     constexpr int CTW = DV / 16 / 4;   // value-column tiles per wave
-    constexpr int TB = 4;              // row tiles whose loads are issued together
-    constexpr int LDS_ROW = DV + 8 / (int)sizeof(T) * 2;   // padded row of the staged S_in
-    __shared__ __align__(16) T s_S[DK * LDS_ROW];
+    constexpr int NPI = DK / 32;       // quarters of the rung
     const int H = a.H;
-    const int u = blockIdx.x / H, h = blockIdx.x - u * H;
+    const int pos = blockIdx.x / H, h = blockIdx.x - pos * H;
+    const int u = a.order ? a.order[pos] : pos;
     const int64_t t0 = a.bounds[u], t1 = a.bounds[u + 1];
-    const int64_t unit = (int64_t)u * H + h;
-    const float *Sin = a.S_init + unit * DK * DV;
+    const int64_t unit = (int64_t)u * H + h, xunit = (int64_t)pos * H + h;
+    const int y = blockIdx.y, Y = gridDim.y;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    // the incoming state: zero and finiteness tests, staged in LDS in the
-    // operand dtype on the way
-    bool nz = false, bad = false;
-    {
-        constexpr int PS = DK * DV / 4 / 256;   // every load issued before the first is used
-        f32x4 x[PS];
+    const bool copies = a.ckpt_S && a.interval > 0 && a.ckpt_S != a.ckpt_in;
+    // the operator's counts decide which items have work
+    bool valid = a.X && a.X_len;
+    int lb[DK / 64];
+    int lmax = 0;
 #pragma unroll
-        for (int q = 0; q < PS; ++q) x[q] = ((const f32x4 *)Sin)[tid + 256 * q];
-#pragma unroll
-        for (int q = 0; q < PS; ++q) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                nz |= (f32_bits(x[q][c]) & 0x7fffffffu) != 0u;
-                bad |= (f32_bits(x[q][c]) & 0x7f800000u) == 0x7f800000u;
-            }
-            const int i = tid + 256 * q, row = (4 * i) / DV, col = (4 * i) % DV;
-            *(F4 *)(s_S + row * LDS_ROW + col) = O::cvt4(x[q]);
-        }
+    for (int j = 0; j < DK / 64; ++j) {
+        lb[j] = valid ? a.X_len[xunit * (DK / 64) + j] : 0;
+        valid = valid && lb[j] >= 0 && lb[j] <= a.X_chunks;
+        lmax = lb[j] > lmax ? lb[j] : lmax;
     }
+    const int64_t rows = valid ? ((int64_t)lmax * kChunk < t1 - t0 ? (int64_t)lmax * kChunk : t1 - t0) : 0;
+    // the rung the operator's Pi may cover (fixup_x_chunks decides)
+    const int64_t first = a.interval > 0 ? (t0 / a.interval + 1) * a.interval : 0;
+    const bool pi_maybe = valid && a.ckpt_S && a.interval > 0 && a.X_Pi && lmax > 0 &&
+                          first <= t1 && first < t0 + (int64_t)lmax * kChunk;
+    // items: chunks 0 .. X_chunks-1, then the rung's quarters
+    const int nchk = (int)((rows + kChunk - 1) / kChunk);
+    auto active = [&](int it) { return it < a.X_chunks ? it < nchk : pi_maybe; };
+    const int n_items = a.X_chunks + NPI;
+    int it0 = y;
+    while (it0 < n_items && !active(it0)) it0 += Y;
+    if (it0 >= n_items && y != 0) return;
+
+    const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
+    const int n0 = w * CTW;
+    F8 B[4][KS];            // chunk: rows 64c + 16q + m of X; rung: rows 32p + 16q + m of Pi
+    f32x4 ov[4][CTW];       // the values the products add to
+    const T *Xu = (const T *)a.X + (int64_t)pos * a.X_chunks * kChunk * H * DK;
+    const float *Pi = a.X_Pi + xunit * DK * DK;
+    const int64_t rung_off = a.interval > 0 ? ((first / a.interval - 1) * H + h) * DK * DV : 0;
+    auto load_item = [&](int it) {
+        if (it < a.X_chunks) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = kChunk * it + 16 * q + m;   // < X_chunks * 64
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk)   // a block of X whose identity had vanished is zero
+                    B[q][kk] = it < lb[(32 * kk) / 64]
+                                   ? O::ld8(Xu + ((int64_t)r * H + h) * DK + 32 * kk + 8 * gq)
+                                   : O::cvt8((const float[8]){0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f});
+                const int64_t tok = t0 + r < t1 ? t0 + r : t1 - 1;
+#pragma unroll
+                for (int n = 0; n < CTW; ++n) {
+                    const int64_t idx = (tok * H + h) * DV + 16 * (n0 + n) + 4 * gq;
+                    if (BF) {
+                        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                        const u32x2 wv = *(const u32x2 *)((const bf16_t *)a.o + idx);
+                        ov[q][n] = f32x4{bits_f32(wv[0] << 16), bits_f32(wv[0] & 0xffff0000u),
+                                         bits_f32(wv[1] << 16), bits_f32(wv[1] & 0xffff0000u)};
+                    } else {
+                        ov[q][n] = *(const f32x4 *)((const float *)a.o + idx);
+                    }
+                }
+            }
+        } else {
+            const float *rung_in = a.ckpt_in + rung_off;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int r = 32 * (it - a.X_chunks) + 16 * q + m;
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) {
+                    const f32x4 *pp = (const f32x4 *)(Pi + (int64_t)r * DK + 32 * kk + 8 * gq);
+                    B[q][kk] = O::cvt44(pp[0], pp[1]);
+                }
+#pragma unroll
+                for (int n = 0; n < CTW; ++n)
+                    ov[q][n] = *(const f32x4 *)(rung_in + (int64_t)r * DV + 16 * (n0 + n) + 4 * gq);
+            }
+        }
+    };
+    // every load of the first item issued with S_in's
+    const float *Sin = a.S_init + unit * DK * DV;
+    float sv[CTW][KS][8];   // S_in's column 16(n0+n)+m, rows 32kk+8gq .. +7
+#pragma unroll
+    for (int n = 0; n < CTW; ++n)
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                sv[n][kk][j] = Sin[(32 * kk + 8 * gq + j) * DV + 16 * (n0 + n) + m];
+    if (it0 < n_items) load_item(it0);
+    // the incoming state: zero and finiteness tests over the four waves' columns
+    bool nz = false, bad = false;
+#pragma unroll
+    for (int n = 0; n < CTW; ++n)
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                nz |= (f32_bits(sv[n][kk][j]) & 0x7fffffffu) != 0u;
+                bad |= (f32_bits(sv[n][kk][j]) & 0x7f800000u) == 0x7f800000u;
+            }
     const int fl = (__syncthreads_or(nz) ? 1 : 0) | (__syncthreads_or(bad) ? 2 : 0);
     int64_t pi_rung = -1;
-    const int xl = (fl & 1) ? fixup_x_chunks<DK>(a, u, h, t0, t1, fl, pi_rung) : 0;
-    if (tid == 0) a.X_route[unit] = xl < 0 ? 1 : 0;
+    const int xl = (fl & 1) ? fixup_x_chunks<DK>(a, pos, h, t0, t1, fl, pi_rung) : 0;
+    if (y == 0 && tid == 0) a.X_route[unit] = xl < 0 ? 1 : 0;
     if (xl < 0) return;
-    if (a.ckpt_S && a.interval > 0 && a.ckpt_S != a.ckpt_in) {
-        for (int64_t p = (t0 / a.interval + 1) * a.interval; p <= t1; p += a.interval) {
-            if (p == pi_rung) continue;   // formed below
+    if (y == 0 && copies) {
+        for (int64_t p = first; p <= t1; p += a.interval) {
+            if (p == pi_rung) continue;   // formed from Pi
             const int64_t off = ((p / a.interval - 1) * H + h) * DK * DV;
             for (int i = tid; i < DK * DV / 4; i += 256)
                 ((f32x4 *)(a.ckpt_S + off))[i] = ((const f32x4 *)(a.ckpt_in + off))[i];
         }
     }
     if (!(fl & 1)) return;   // a zero incoming state leaves o_local final
-    int lb[DK / 64];
-#pragma unroll
-    for (int j = 0; j < DK / 64; ++j) lb[j] = a.X_len[unit * (DK / 64) + j];
-    // operands: S_in's column 16n + m, rows 32kk + 8gq .. + 7 of lane (m, gq),
-    // from LDS; the rows of X and Pi are loaded with the same k in the same order
-    const int m = opaque(lane) & 15, gq = opaque(lane) >> 4;
-    const int n0 = w * CTW;
+    // from here xl == lmax, and pi_rung == first exactly when pi_maybe
     F8 A[CTW][KS];
 #pragma unroll
     for (int n = 0; n < CTW; ++n)
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            float v[8];
+        for (int kk = 0; kk < KS; ++kk) A[n][kk] = O::cvt8(sv[n][kk]);
+    for (int it = it0; it < n_items; it += Y) {
+        if (!active(it)) continue;
+        if (it != it0) load_item(it);
+        if (it < a.X_chunks) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                v[j] = (float)s_S[(32 * kk + 8 * gq + j) * LDS_ROW + 16 * (n0 + n) + m];
-            A[n][kk] = O::cvt8(v);
-        }
-    const T *Xu = (const T *)a.X + (int64_t)u * a.X_chunks * kChunk * H * DK;
-    const int64_t rows = (int64_t)xl * kChunk < t1 - t0 ? (int64_t)xl * kChunk : t1 - t0;
-    const int ntx = (int)((rows + 15) / 16);           // tiles of X
-    const int ntp = pi_rung >= 0 ? DK / 16 : 0;         // tiles of Pi
-    const float *Pi = a.X_Pi + unit * DK * DK;
-    float *rung = pi_rung >= 0 ? a.ckpt_S + ((pi_rung / a.interval - 1) * H + h) * DK * DV : nullptr;
-    const float *rung_in = pi_rung >= 0 ? a.ckpt_in + ((pi_rung / a.interval - 1) * H + h) * DK * DV
-                                        : nullptr;
-    // o_t += S_in^T X_t, TB row tiles at a time: every load of a batch (rows
-    // of X, the outputs to add to) issued before its products
-    for (int tb = 0; tb < ntx; tb += TB) {
-        F8 B[TB][KS];
-        f32x4 ov[TB][CTW];
+            for (int q = 0; q < 4; ++q) {
+                const int64_t tok = t0 + kChunk * it + 16 * q + m;
 #pragma unroll
-        for (int q = 0; q < TB; ++q) {
-            const int tt = tb + q < ntx ? tb + q : ntx - 1;   // past the last tile: repeat it
-            const int r = 16 * tt + m;
-            const int ch = (16 * tt) / kChunk;
+                for (int n = 0; n < CTW; ++n) {
+                    f32x4 acc = ov[q][n];
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                // a block of X whose identity had vanished is zero here
-                B[q][kk] = ch < lb[(32 * kk) / 64]
-                               ? O::ld8(Xu + ((int64_t)r * H + h) * DK + 32 * kk + 8 * gq)
-                               : O::cvt8((const float[8]){0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f});
-            }
-            const int64_t tok = t0 + r < t1 ? t0 + r : t1 - 1;
-#pragma unroll
-            for (int n = 0; n < CTW; ++n) {
-                const int64_t idx = (tok * H + h) * DV + 16 * (n0 + n) + 4 * gq;
-                if (BF) {
-                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                    const u32x2 wv = *(const u32x2 *)((const bf16_t *)a.o + idx);
-                    ov[q][n] = f32x4{bits_f32(wv[0] << 16), bits_f32(wv[0] & 0xffff0000u),
-                                     bits_f32(wv[1] << 16), bits_f32(wv[1] & 0xffff0000u)};
-                } else {
-                    ov[q][n] = *(const f32x4 *)((const float *)a.o + idx);
+                    for (int kk = 0; kk < KS; ++kk) acc = O::mma32(acc, A[n][kk], B[q][kk]);
+                    if (tok >= t1) continue;
+                    // lane (m, gq) holds value columns 16n + 4gq .. + 3 of token tok
+                    const int64_t idx = (tok * H + h) * DV + 16 * (n0 + n) + 4 * gq;
+                    if (BF) *(bf16x4 *)((bf16_t *)a.o + idx) = Ops<true>::cvt4(acc);
+                    else *(f32x4 *)((float *)a.o + idx) = acc;
                 }
             }
-        }
+        } else {
+            float *rung = a.ckpt_S + rung_off;
 #pragma unroll
-        for (int q = 0; q < TB; ++q) {
-            if (tb + q >= ntx) break;
-            const int64_t tok = t0 + 16 * (tb + q) + m;
+            for (int q = 0; q < 2; ++q) {
+                const int r = 32 * (it - a.X_chunks) + 16 * q + m;
 #pragma unroll
-            for (int n = 0; n < CTW; ++n) {
-                f32x4 acc = ov[q][n];
+                for (int n = 0; n < CTW; ++n) {
+                    f32x4 acc = ov[q][n];
 #pragma unroll
-                for (int kk = 0; kk < KS; ++kk) acc = O::mma32(acc, A[n][kk], B[q][kk]);
-                if (tok >= t1) continue;
-                // lane (m, gq) holds value columns 16n + 4gq .. + 3 of token tok
-                const int64_t idx = (tok * H + h) * DV + 16 * (n0 + n) + 4 * gq;
-                if (BF) *(bf16x4 *)((bf16_t *)a.o + idx) = Ops<true>::cvt4(acc);
-                else *(f32x4 *)((float *)a.o + idx) = acc;
-            }
-        }
-    }
-    // the rung among the corrected rows: Pi S_in + sub_D (fp32 result), TB
-    // row tiles of Pi at a time with their loads issued together
-    for (int tb = 0; tb < ntp; tb += TB) {
-        f32x4 pv[TB][KS][2], rv[TB][CTW];
-#pragma unroll
-        for (int q = 0; q < TB; ++q) {
-            const int r = 16 * (tb + q < ntp ? tb + q : ntp - 1) + m;
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const f32x4 *pp = (const f32x4 *)(Pi + (int64_t)r * DK + 32 * kk + 8 * gq);
-                pv[q][kk][0] = pp[0];
-                pv[q][kk][1] = pp[1];
-            }
-#pragma unroll
-            for (int n = 0; n < CTW; ++n)
-                rv[q][n] = *(const f32x4 *)(rung_in + (int64_t)r * DV + 16 * (n0 + n) + 4 * gq);
-        }
-#pragma unroll
-        for (int q = 0; q < TB; ++q) {
-            if (tb + q >= ntp) break;
-            const int r = 16 * (tb + q) + m;
-            F8 B[KS];
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const float v[8] = {pv[q][kk][0][0], pv[q][kk][0][1], pv[q][kk][0][2], pv[q][kk][0][3],
-                                    pv[q][kk][1][0], pv[q][kk][1][1], pv[q][kk][1][2], pv[q][kk][1][3]};
-                B[kk] = O::cvt8(v);
-            }
-#pragma unroll
-            for (int n = 0; n < CTW; ++n) {
-                f32x4 acc = rv[q][n];
-#pragma unroll
-                for (int kk = 0; kk < KS; ++kk) acc = O::mma32(acc, A[n][kk], B[kk]);
-                *(f32x4 *)(rung + (int64_t)r * DV + 16 * (n0 + n) + 4 * gq) = acc;
+                    for (int kk = 0; kk < KS; ++kk) acc = O::mma32(acc, A[n][kk], B[q][kk]);
+                    *(f32x4 *)(rung + (int64_t)r * DV + 16 * (n0 + n) + 4 * gq) = acc;
+                }
             }
         }
     }
 }
 
+// Workgroups per unit of the fix-up operator: every item on its own
+// workgroup while the units leave room on the device, else fewer, each
+// walking several items with S_in loaded once.
 template <int DK, int DV, bool BF>
 hipError_t launch_fixop_t(const EngineArgs &a, hipStream_t stream) {
     const int64_t grid = (int64_t)a.n_units * a.H;
     if (grid == 0) return hipSuccess;
-    if (grid > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fixop_kernel<DK, DV, BF>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+    if (grid > INT32_MAX || a.X_chunks <= 0 || a.X_chunks > 4096) return hipErrorInvalidValue;
+    const int items = a.X_chunks + DK / 32;
+    const int Y = fixop_spread(grid, items);
+    hipLaunchKernelGGL((fixop_kernel<DK, DV, BF>), dim3((unsigned)grid, (unsigned)Y), dim3(256), 0,
+                       stream, a);
     return hipGetLastError();
 }
 

@@ -82,10 +82,34 @@ struct EngineArgs {
     // package of split segments: X_per sub-segments per segment, the operator
     // of segment u / X_per written by its first sub-segment (0 or 1: none split)
     int32_t X_per;
+    // and, of the later sub-segments (u % X_per != 0), each sub-segment's own
+    // operator (nullable: none), in slot (u % X_per - 1) * (n_units / X_per) +
+    // u / X_per: it corrects the sub-segment's rows from the state that the
+    // sub-segments before it accumulated.  Its counts are valid at the
+    // sub-segment's end without vanishing.
+    void *Xs;                    // [X_per - 1, n_units / X_per, Xs_chunks * 64, H, dk]
+    int32_t *Xs_len;             // [X_per - 1, n_units / X_per, H, dk / 64]
+    float *Xs_Pi;                // [X_per - 1, n_units / X_per, H, dk, dk] (nullable)
+    int32_t Xs_chunks;
+    int32_t Xs_interval;
+    // Package of split segments: the last sub-segment of segment j (u % X_per
+    // == X_per - 1) writes its D and M into slot j of S_last and M_last, where
+    // the merge composes them in place (nullable: slot u of S_out / M_out).
+    float *S_last, *M_last;
     // FixOp writes the route of every unit (1: the recurrence), the fix-up
     // launch after it skips the units with route 0 (nullable: none skipped).
+    // FixOp reads X, X_len and X_Pi at the unit's position in `order` and the
+    // incoming state and the route at the unit itself.
     int32_t *X_route;            // [n_units, H]
 };
+
+// Slot of a package output (`size` floats per head) of unit u: slot u of
+// base, or slot u / per of last for the last sub-segment of a split segment.
+__device__ __forceinline__ float *package_slot(float *base, float *last, int per, int u, int H,
+                                               int h, int64_t size) {
+    if (last && per > 1 && u % per == per - 1) return last + ((int64_t)(u / per) * H + h) * size;
+    return base + ((int64_t)u * H + h) * size;
+}
 
 // Launches the engine.  bf16 selects bf16 I/O (bf16 MFMA operands) versus
 // fp32 I/O (fp32 MFMA).  nb is the value-column block width.  Returns a HIP

@@ -109,7 +109,7 @@ __device__ void recurrent_body(const EngineArgs &a, const int u, const int h, co
     };
     if (CHECK0 && !nonzero()) {   // nothing to propagate
         zero_rungs_after(t0);
-        if (MB) store(a.M_out + ((int64_t)u * H + h) * DK * DK, nullptr);
+        if (MB) store(package_slot(a.M_out, a.M_last, a.X_per, u, H, h, DK * DK), nullptr);
         return;
     }
     for (int64_t t = 0; t < len; ++t) {
@@ -166,7 +166,7 @@ __device__ void recurrent_body(const EngineArgs &a, const int u, const int h, co
             rung(p);
             if (CHECK0 && p < len && !nonzero()) {   // exact zero: stays zero
                 zero_rungs_after(t0 + p);
-                if (MB) store(a.M_out + ((int64_t)u * H + h) * DK * DK, nullptr);
+                if (MB) store(package_slot(a.M_out, a.M_last, a.X_per, u, H, h, DK * DK), nullptr);
                 return;
             }
         }
@@ -182,8 +182,8 @@ __device__ void recurrent_body(const EngineArgs &a, const int u, const int h, co
         if (dst) store(dst, nullptr);
     }
     if (MODE == kModePackage || MODE == kModePackageM) {
-        if (MB) store(a.M_out + ((int64_t)u * H + h) * DK * DK, nullptr);
-        else store(a.S_out + ((int64_t)u * H + h) * DK * DV, nullptr);
+        if (MB) store(package_slot(a.M_out, a.M_last, a.X_per, u, H, h, DK * DK), nullptr);
+        else store(package_slot(a.S_out, a.S_last, a.X_per, u, H, h, DK * DV), nullptr);
     }
 }
 

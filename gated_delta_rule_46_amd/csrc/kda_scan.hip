@@ -850,8 +850,11 @@ __global__ void split_bounds_kernel(const int64_t *seg_start, int nseg, int f, i
 
 // Step k of the merge, grid (nseg, H): with u = f j + k,
 //   (M_u, D_u) <- (M_u M_{u-1}, M_u D_{u-1} + D_u)
-// into the sub-segment slots, or into M_out[j], D_out[j] at the last step
-// (M_out may be NULL).  A zero factor is skipped against finite values.
+// in place: in the sub-segment slots, or at the last step in M_out[j] and
+// D_out[j], where the package launch wrote the last sub-segment's M and D (its
+// M stays in slot u when M_out is NULL, and only D is composed).  A zero factor
+// is skipped against finite values, and an output that keeps its value is not
+// written: with M_u exactly zero (a short memory) the step only reads.
 template <int DK, int DV>
 __global__ __launch_bounds__(NTH) void split_compose_kernel(int H, int nseg, int f, int k,
                                                             float *Ms, float *Ds, float *M_out,
@@ -859,11 +862,11 @@ __global__ __launch_bounds__(NTH) void split_compose_kernel(int H, int nseg, int
     const int j = blockIdx.x, h = blockIdx.y;
     const int64_t mm = (int64_t)DK * DK, dd = (int64_t)DK * DV;
     const int64_t u = (int64_t)f * j + k;
-    float *Ml = Ms + (u * H + h) * mm, *Dl = Ds + (u * H + h) * dd;
-    const float *Me = Ms + ((u - 1) * H + h) * mm, *De = Ds + ((u - 1) * H + h) * dd;
     const bool last = k == f - 1;
-    float *Mo = last ? (M_out ? M_out + ((int64_t)j * H + h) * mm : nullptr) : Ml;
-    float *Do = last ? D_out + ((int64_t)j * H + h) * dd : Dl;
+    float *Ml = last && M_out ? M_out + ((int64_t)j * H + h) * mm : Ms + (u * H + h) * mm;
+    float *Dl = last ? D_out + ((int64_t)j * H + h) * dd : Ds + (u * H + h) * dd;
+    const float *Me = Ms + ((u - 1) * H + h) * mm, *De = Ds + ((u - 1) * H + h) * dd;
+    float *Mo = last && !M_out ? nullptr : Ml;   // M is composed where it is kept
     bool zl, ze, bl, be;
     {
         Tile<DK * DK> tl, te;
@@ -890,10 +893,9 @@ __global__ __launch_bounds__(NTH) void split_compose_kernel(int H, int nseg, int
     __syncthreads();   // every operand read precedes the first store
     if (Mo) {
         if (need_mm) store_acc<DK, DK>(am, nullptr, Mo);
-        else copy_n<DK * DK>(Mo, nullptr);
+        else if (!zl) copy_n<DK * DK>(Mo, nullptr);   // a zero M_{u-1} against a finite M_u
     }
-    if (need_md) store_acc<DK, DV>(ad, Dl, Do);
-    else if (last) copy_n<DK * DV>(Do, Dl);
+    if (need_md) store_acc<DK, DV>(ad, Dl, Dl);
 }
 
 // Rungs of the sub-packages inside sub-segment k >= 1 (grid (rows, H)):

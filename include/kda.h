@@ -256,7 +256,11 @@ int kda_prefill_resume(const kda_config *cfg, const void *q, const void *k, cons
  * their packages in one launch, and merge them left to right (sub-segment k
  * fixed up from the accumulated state of 0..k-1, its rungs included, then
  * (M, D) composed); the results equal the unsplit call's up to fp32
- * rounding.
+ * rounding.  With the bf16 or fp32 chunked shapes the queried size also holds
+ * the fix-up operators (as kda_fixop describes) of sub-segments 1..f-1, kept
+ * by their M blocks, so that a merge step corrects those sub-segments as a
+ * product; a workspace large enough only for the split without them merges
+ * by the recurrence alone.
  */
 /* Workspace bytes that let kda_segment_package split its segments (0 when it
  * would not split them: enough units already, or segments too short). */

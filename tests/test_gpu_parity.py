@@ -507,6 +507,29 @@ def test_segment_package_without_M(K):
     assert torch.equal(full[4], part[4])
 
 
+@pytest.mark.parametrize("gates", ["config", "long"])
+def test_package_split_without_M(K, gates):
+    """Split packages without M (2 segments of 4096 tokens on 2 heads, 8
+    sub-segments each): the merge composes D alone, the last sub-segments'
+    M staying in the workspace.  o_local, D and sub_D are bit-identical to
+    the split call with M, which the split tests compare with the oracle."""
+    import torch
+    shift = {} if gates == "config" else dict(gate_shift=-9.0, beta_shift=-6.0)
+    w = make_workload("split-noM", [8192], 2, 128, 128, "bf16", 5530, s0_std=None,
+                      seg_start=[0, 4096, 8192], **shift)
+    say(f"split package without M, gates={gates}")
+    t = to_torch(w)
+    args = (t["q"], t["k"], t["v"], t["g"], t["beta"], t["seg_start"])
+    full = K.kda_segment_package(*args, ckpt_interval=512)
+    part = K.kda_segment_package(*args, ckpt_interval=512, want_M=False)
+    sync()
+    assert part[1] is None and part[3] is None
+    if gates == "long":
+        assert float(full[1].abs().max()) > 1e-3, "long-memory gates should leave M nonzero"
+    for name, i in (("o_local", 0), ("D", 2), ("sub_D", 4)):
+        assert torch.equal(full[i], part[i]), name
+
+
 # ---------------------------------------------------------------------------
 # Prefill resumed from a state pool
 # ---------------------------------------------------------------------------
