@@ -116,7 +116,7 @@ struct SplitPlan {
     int nseg = 0;
     int64_t L = 0, rows = 0;
     size_t off_M = 0, off_D = 0, off_Sin = 0, off_Sfin = 0, off_subD = 0, off_bounds = 0,
-           off_X = 0, off_Xlen = 0, off_route = 0, off_Pi = 0, bytes = 0;
+           off_X = 0, off_Xlen = 0, off_route = 0, off_Pi = 0, off_flags = 0, bytes = 0;
     bool fixop = false;
 };
 
@@ -149,6 +149,7 @@ bool plan_split(const kda_config *cfg, int64_t T, int32_t N, const kda_ckpt *ckp
     p->off_Sfin = take(dd);
     p->off_subD = take(dd * (size_t)p->rows);
     p->off_bounds = take(sizeof(int64_t) * (size_t)(p->nseg + 1));
+    p->off_flags = take(kda::sequential_workspace(H, p->nseg));   // the scan's zero tests of M
     // the fix-up operator (the chunked engine's shapes only)
     p->fixop = fixop && !kda::recurrent_supported(bf, cfg->dk, cfg->dv);
     if (p->fixop) {
@@ -193,7 +194,8 @@ int prefill_split(const SplitPlan &p, const kda_config *cfg, const void *q, cons
     }
     if ((e = kda::launch_engine(kda::kModePackageVM, bf, dk, dv, nb, a, s)) != hipSuccess)
         return launched(e, "prefill split (package)");
-    if ((e = kda::launch_scan_sequential(dk, dv, H, p.nseg, M, D, S0, S_in, S_fin, s)) != hipSuccess)
+    if ((e = kda::launch_scan_sequential(dk, dv, H, p.nseg, M, D, S0, S_in, S_fin,
+                                         (int *)(w + p.off_flags), s)) != hipSuccess)
         return launched(e, "prefill split (scan)");
     kda::EngineArgs f{};
     f.q = q; f.k = k; f.v = nullptr; f.g = g; f.beta = beta; f.o = o;
@@ -616,7 +618,9 @@ int kda_segment_package_fx(const kda_config *cfg, const void *q, const void *k, 
 }
 
 size_t kda_segment_scan_workspace(const kda_config *cfg, int32_t nseg, int32_t algo) {
-    if (!cfg || nseg <= 0 || algo != KDA_SCAN_BLELLOCH) return 0;
+    if (!cfg || nseg <= 0 || cfg->num_heads <= 0) return 0;
+    if (algo == KDA_SCAN_SEQUENTIAL) return round256(kda::sequential_workspace(cfg->num_heads, nseg));
+    if (algo != KDA_SCAN_BLELLOCH) return 0;
     return round256(kda::blelloch_workspace(cfg->dk, cfg->dv, cfg->num_heads, nseg));
 }
 
@@ -633,9 +637,14 @@ int kda_segment_scan(const kda_config *cfg, int32_t nseg, const float *M, const 
     KDA_TRY(check_tensor(S_in, "S_in", true));
     KDA_TRY(check_tensor(S_final, "S_final", true));
     hipStream_t s = (hipStream_t)stream;
-    if (algo == KDA_SCAN_SEQUENTIAL)
+    if (algo == KDA_SCAN_SEQUENTIAL) {   // the workspace is optional: M tested once per package
+        const bool flags = ws && ws_bytes >= kda::sequential_workspace(cfg->num_heads, nseg);
+        if (flags) KDA_TRY(check_tensor(ws, "ws", true, 4));
         return launched(kda::launch_scan_sequential(cfg->dk, cfg->dv, cfg->num_heads, nseg, M, D,
-                                                    S0, S_in, S_final, s), "sequential scan");
+                                                    S0, S_in, S_final, flags ? (int *)ws : nullptr,
+                                                    s),
+                        "sequential scan");
+    }
     if (nseg > kda::blelloch_max_segments())
         return fail(KDA_ERR_UNSUPPORTED, "the Blelloch scan takes at most %d segments (got %d)",
                     kda::blelloch_max_segments(), nseg);

@@ -128,9 +128,12 @@ int engine_pick_nb(bool bf16, int dk, int dv, int64_t units, int mode);
 hipError_t launch_plan(const int64_t *cu_seqlens, int32_t n, int32_t *order, hipStream_t s);
 
 // Package scans (fp32).
+// flags (nullable): sequential_workspace(H, nseg) bytes, where a first launch
+// tests every M once for the scan.
+size_t sequential_workspace(int H, int nseg);
 hipError_t launch_scan_sequential(int dk, int dv, int H, int nseg, const float *M,
                                   const float *D, const float *S0, float *S_in,
-                                  float *S_final, hipStream_t s);
+                                  float *S_final, int *flags, hipStream_t s);
 hipError_t launch_scan_blelloch(int dk, int dv, int H, int nseg, const float *M,
                                 const float *D, const float *S0, float *S_in,
                                 float *S_final, void *ws, hipStream_t s);

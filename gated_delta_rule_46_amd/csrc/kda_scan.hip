@@ -219,10 +219,33 @@ __device__ __forceinline__ bool nonfinite4(f32x4 x) {
     return nonfinite1(x[0]) | nonfinite1(x[1]) | nonfinite1(x[2]) | nonfinite1(x[3]);
 }
 
+// Whether each package's M has a nonzero element (grid (nseg, H)): one
+// workgroup per M, so the scan's workgroups need not read M to test it.
+template <int DK>
+__global__ __launch_bounds__(NTH) void seq_flags_kernel(int H, const float *M, int *nz) {
+    constexpr int PM = DK * DK / 4 / NTH;
+    const int j = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+    const f32x4 *Mj = (const f32x4 *)(M + ((int64_t)j * H + h) * DK * DK);
+    f32x4 a[PM];
+#pragma unroll
+    for (int i = 0; i < PM; ++i) a[i] = Mj[t + i * NTH];
+    uint32_t acc = 0u;
+#pragma unroll
+    for (int i = 0; i < PM; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc |= f32_bits(a[i][c]) & 0x7fffffffu;
+    const int f = __syncthreads_or(acc != 0u) ? 1 : 0;
+    if (t == 0) nz[j * H + h] = f;
+}
+
+// mz_flags (nullable): package j of head h has a nonzero M exactly when
+// mz_flags[j * H + h] != 0 (seq_flags_kernel); without them every workgroup
+// tests each M itself.
 template <int DK, int DV>
 __global__ __launch_bounds__(NTH) void scan_seq_kernel(int H, int nseg, const float *M,
                                                        const float *D, const float *S0,
-                                                       float *S_in, float *S_final) {
+                                                       float *S_in, float *S_final,
+                                                       const int *mz_flags) {
     constexpr int P = DV / SEQ_CW;                 // workgroups per head
     constexpr int PS = DK * SEQ_CW / 4 / NTH;      // float4 of the state's columns per thread
     constexpr int PM = DK * DK / 4 / NTH;          // float4 of an M per thread (zero test)
@@ -275,11 +298,15 @@ __global__ __launch_bounds__(NTH) void scan_seq_kernel(int H, int nseg, const fl
                 dr[jj][i] = *(const f32x4 *)(Dj + eoff(i));
                 b2 |= nonfinite4(dr[jj][i]);
             }
+            if (mz_flags) {
+                acc = mz_flags[j * H + h] != 0 ? 1u : 0u;
+            } else {
 #pragma unroll
-            for (int i = 0; i < PM; ++i) {
-                const f32x4 x = Mj[t + i * NTH];
+                for (int i = 0; i < PM; ++i) {
+                    const f32x4 x = Mj[t + i * NTH];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) acc |= f32_bits(x[c]) & 0x7fffffffu;
+                    for (int c = 0; c < 4; ++c) acc |= f32_bits(x[c]) & 0x7fffffffu;
+                }
             }
             mz |= (unsigned)(acc != 0u) << jj;
             db |= (unsigned)b2 << jj;
@@ -1001,9 +1028,14 @@ int pow2_at_least(int n) {
 
 template <int DK, int DV>
 hipError_t scan_seq_t(int H, int nseg, const float *M, const float *D, const float *S0,
-                      float *S_in, float *S_final, hipStream_t s) {
+                      float *S_in, float *S_final, int *flags, hipStream_t s) {
+    if (flags) {
+        hipLaunchKernelGGL((seq_flags_kernel<DK>), dim3(nseg, H), dim3(NTH), 0, s, H, M, flags);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((scan_seq_kernel<DK, DV>), dim3(H * (DV / SEQ_CW)), dim3(NTH), 0, s, H,
-                       nseg, M, D, S0, S_in, S_final);
+                       nseg, M, D, S0, S_in, S_final, (const int *)flags);
     return hipGetLastError();
 }
 
@@ -1091,12 +1123,15 @@ size_t blelloch_workspace(int dk, int dv, int H, int nseg) {
            (size_t)2 * H * sizeof(unsigned long long) + ((size_t)2 * nseg * H + H) * sizeof(int);
 }
 
+size_t sequential_workspace(int H, int nseg) { return (size_t)nseg * H * sizeof(int); }
+
 hipError_t launch_scan_sequential(int dk, int dv, int H, int nseg, const float *M, const float *D,
-                                  const float *S0, float *S_in, float *S_final, hipStream_t s) {
-    if (dk == 64 && dv == 64) return scan_seq_t<64, 64>(H, nseg, M, D, S0, S_in, S_final, s);
-    if (dk == 64 && dv == 128) return scan_seq_t<64, 128>(H, nseg, M, D, S0, S_in, S_final, s);
-    if (dk == 128 && dv == 64) return scan_seq_t<128, 64>(H, nseg, M, D, S0, S_in, S_final, s);
-    if (dk == 128 && dv == 128) return scan_seq_t<128, 128>(H, nseg, M, D, S0, S_in, S_final, s);
+                                  const float *S0, float *S_in, float *S_final, int *flags,
+                                  hipStream_t s) {
+    if (dk == 64 && dv == 64) return scan_seq_t<64, 64>(H, nseg, M, D, S0, S_in, S_final, flags, s);
+    if (dk == 64 && dv == 128) return scan_seq_t<64, 128>(H, nseg, M, D, S0, S_in, S_final, flags, s);
+    if (dk == 128 && dv == 64) return scan_seq_t<128, 64>(H, nseg, M, D, S0, S_in, S_final, flags, s);
+    if (dk == 128 && dv == 128) return scan_seq_t<128, 128>(H, nseg, M, D, S0, S_in, S_final, flags, s);
     return hipErrorInvalidValue;
 }
 

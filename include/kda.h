@@ -271,9 +271,12 @@ int kda_segment_package(const kda_config *cfg, const void *q, const void *k, con
                         int32_t nseg, void *o_local, float *M, float *D, const kda_ckpt *ckpt,
                         float *sub_M, float *sub_D, void *ws, size_t ws_bytes, void *stream);
 
-/* Workspace bytes kda_segment_scan needs (0 for the sequential scan; for the
- * Blelloch scan the padded packages, flags per package and two counters per
- * head).  Concurrent scans need separate workspaces. */
+/* Workspace bytes for kda_segment_scan.  Blelloch scan: required; the padded
+ * packages, flags per package and two counters per head.  Sequential scan:
+ * optional; one flag per package (a first launch tests each M once for zero,
+ * instead of every workgroup of a head testing every M), and with ws = NULL or
+ * fewer bytes the scan runs without it, with the same results.  Concurrent
+ * scans need separate workspaces. */
 size_t kda_segment_scan_workspace(const kda_config *cfg, int32_t nseg, int32_t algo);
 
 /*

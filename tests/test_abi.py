@@ -145,7 +145,9 @@ def test_workspace_queries():
     # too short to split, or enough heads to fill the device: the schedule only
     assert K.LIB.kda_prefill_workspace(ctypes.byref(c), 600, 1) == 256
     assert K.LIB.kda_prefill_workspace(ctypes.byref(cfg(H=512)), 1 << 16, 1) == 256
-    assert K.LIB.kda_segment_scan_workspace(ctypes.byref(c), 16, K.KDA_SCAN_SEQUENTIAL) == 0
+    # sequential: one int flag per (package, head), rounded to 256 bytes
+    assert K.LIB.kda_segment_scan_workspace(ctypes.byref(c), 16, K.KDA_SCAN_SEQUENTIAL) == \
+        (16 * c.num_heads * 4 + 255) // 256 * 256
     b16 = K.LIB.kda_segment_scan_workspace(ctypes.byref(c), 16, K.KDA_SCAN_BLELLOCH)
     b17 = K.LIB.kda_segment_scan_workspace(ctypes.byref(c), 17, K.KDA_SCAN_BLELLOCH)
     # padded packages: M and D of every padded slot, at least

@@ -468,6 +468,29 @@ def test_scan_sequential_heads_and_shapes(K, H, dk, dv, nseg, zero):
         assert np.array_equal(to_numpy_f64(S_fin), D[-1].astype(np.float64))
 
 
+@pytest.mark.parametrize("H,dk,dv,nseg,zero", [(10, 128, 64, 9, (0, 3, 4, 8)),
+                                               (8, 128, 128, 8, tuple(range(8)))])
+def test_scan_sequential_without_workspace(K, H, dk, dv, nseg, zero):
+    """The sequential scan's workspace is optional: without it every
+    workgroup tests M itself, with it one launch tests each M once.  Both give
+    the same bits."""
+    import ctypes
+    import torch
+    from workloads import make_packages
+    say(f"sequential scan with and without its workspace H={H} nseg={nseg}")
+    M, D, S0 = make_packages(nseg, H, dk, dv, 7300 + H + nseg, zero=zero)
+    tM, tD, tS0 = (torch.from_numpy(x).cuda() for x in (M, D, S0))
+    S_in, S_fin = K.kda_segment_scan(tM, tD, tS0, algo=0)
+    cfg = K.kda_config(H, dk, dv, K.CHUNK, K.KDA_DTYPE_BF16, 1.0, 1)
+    assert K.LIB.kda_segment_scan_workspace(ctypes.byref(cfg), nseg, 0) > 0
+    S_in2, S_fin2 = torch.empty_like(S_in), torch.empty_like(S_fin)
+    st = K.LIB.kda_segment_scan(ctypes.byref(cfg), nseg, K._p(tM), K._p(tD), K._p(tS0),
+                                K._p(S_in2), K._p(S_fin2), 0, None, 0, K._stream(None))
+    sync()
+    assert st == 0
+    assert torch.equal(S_in, S_in2) and torch.equal(S_fin, S_fin2)
+
+
 def test_segment_path_config_gates_bf16(K):
     """The configs' gates: M underflows to exactly zero after a few chunks."""
     say("segment path bf16 d=128 config gates, 4 segments of 512")
