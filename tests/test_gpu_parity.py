@@ -1183,6 +1183,43 @@ def test_fixop_segment_path(K, gates, iv, seg, dtype, dk, dv):
         assert not route[2].any()
 
 
+@pytest.mark.parametrize("nseg", [4, 8, 16])
+def test_fixop_workgroups_per_unit(K, nseg):
+    """The operator's launch takes one to several workgroups per (segment,
+    head) unit, by the unit count: with 32 heads, 4, 8 and 16 segments give
+    128, 256 and 512 units, so each unit's chunks and rung quarters are
+    spread over 4, 2 and 1 workgroups.  Rungs every 128 tokens put one among
+    each segment's corrected rows (formed from Pi).  Outputs and rungs against
+    the recurrence's fix-up on every head, and against the oracle on two."""
+    import torch
+    T, iv = 1024 * nseg, 128
+    seg = list(range(0, T + 1, 1024))
+    w = make_workload("fixop-spread", [T], 32, 128, 128, "bf16", 5600 + nseg, s0_std=0.5,
+                      seg_start=seg)
+    say(f"fix-up operator over {nseg} x 32 units, rungs every {iv}")
+    t = to_torch(w)
+    fx = K.FixOp(nseg, 32, 128, t["q"].dtype, "cuda", interval=iv)
+    ol, M, D, _, sD = K.kda_segment_package_fx(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                               t["seg_start"], fx, ckpt_interval=iv,
+                                               want_sub_M=False)
+    S_in, _ = K.kda_segment_scan(M, D, t["S0"][0].contiguous(), algo=0)
+    o, o2 = ol.clone(), ol.clone()
+    ck2 = K.kda_output_fixup_ckpt(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o2,
+                                  sD.clone(), interval=iv)
+    ck = K.kda_output_fixup_fx(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o, fx,
+                               sub_D=sD, interval=iv, out=sD)
+    sync()
+    lens, route = fx.len.cpu().numpy(), fx.route.cpu().numpy()
+    assert (route == 0).all() and (lens >= 2).all(), "the operator should cover every unit"
+    assert_close("o: operator vs recurrence", to_numpy_f64(o), to_numpy_f64(o2), OUT_TOL["bf16"])
+    assert_close("rungs: operator vs recurrence", to_numpy_f64(ck), to_numpy_f64(ck2),
+                 STATE_TOL["bf16"])
+    for h in (0, 31):
+        ro, _, rck = oracle_unit(w, 0, h, interval=iv)
+        assert_close(f"o head {h}", to_numpy_f64(o[:, h]), ro[:, 0], OUT_TOL["bf16"])
+        assert_close(f"rungs head {h}", to_numpy_f64(ck[:, h]), rck[:, 0], STATE_TOL["bf16"])
+
+
 @pytest.mark.parametrize("gates", ["config", "long"])
 def test_fixop_split_segments(K, gates):
     """The operator when kda_segment_package splits segments into
