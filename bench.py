@@ -272,11 +272,19 @@ def long_memory_measure(K, w, t, launches: int) -> dict:
     gates: log alpha = -softplus(N(0,1) - 9) (about -1.2e-4 per token) and
     beta = sigmoid(N(0,1) - 6), drawn on the device from a seeded generator.
     Every M stays far from zero, so the M blocks run their whole segment,
-    the scan forms every product, the fix-up runs every segment to its end
-    and every rung carries the propagated incoming state.  Algorithmic
-    bytes: the package pass (1540 B per token-head at d = 128 bf16) plus the
-    M blocks' reads of k, g, beta, plus the fix-up's reads of q, k, g, beta
-    and its read and write of o; states, packages and rungs as in the step."""
+    the scan forms every product and every rung carries the propagated
+    incoming state.  When the package does not split its segments (enough
+    (segment, head) units), the step keeps a fix-up operator over whole
+    segments: the M blocks write X for every row, the fix-up is one product,
+    o += S_in^T X, and the rungs come from kda_checkpoint_write with sub_M.
+    Otherwise (split segments) it runs the headline's step, whose fix-up then
+    walks the recurrence.  Algorithmic bytes: the package pass (1540 B per
+    token-head at d = 128 bf16) plus the M blocks' reads of q, k, g, beta and
+    writes of X and the fix-up's read of X and of o and write of o (operator),
+    or the M blocks' reads of k, g, beta and the fix-up's reads of q, k, g,
+    beta and of o and write of o (recurrence); states, packages and rungs as
+    the step moves them."""
+    import ctypes
     import torch
     import torch.nn.functional as F
     gen = torch.Generator(device="cuda").manual_seed(46007)
@@ -285,6 +293,11 @@ def long_memory_measure(K, w, t, launches: int) -> dict:
     beta = torch.sigmoid(torch.randn((T, H), generator=gen, device="cuda") - 6.0)
     S0 = None if t["S0"] is None else t["S0"][0].contiguous()
     interval = w.ckpt_interval
+    nseg = len(w.seg_start) - 1
+    seg_len = np.diff(np.asarray(w.seg_start, dtype=np.int64))
+    cfg = K.make_config(H, dk, dv, t["q"].dtype)
+    whole = K.LIB.kda_segment_package_workspace(ctypes.byref(cfg), T, nseg) == 0
+    rows = T // interval if interval else 0
     ev = {}
     stream = torch.cuda.current_stream()
 
@@ -293,23 +306,31 @@ def long_memory_measure(K, w, t, launches: int) -> dict:
         e.record(stream)
         ev.setdefault(name, []).append(e)
 
-    # the step as the headline runs it, with the fix-up operator (no identity
-    # vanishes here: every segment walks the recurrence in the fix-up)
-    fx = K.FixOp(len(w.seg_start) - 1, H, dk, t["q"].dtype, "cuda", interval=interval)
+    if whole:
+        fx = K.FixOp(nseg, H, dk, t["q"].dtype, "cuda", chunks=int(-(-seg_len.max() // 64)))
+        ck_out = torch.empty((rows, H, dk, dv), dtype=torch.float32, device="cuda") if rows else None
+    else:
+        fx = K.FixOp(nseg, H, dk, t["q"].dtype, "cuda", interval=interval)
 
     def step(timed):
         if timed:
             mark("a")
-        o, M, D, _, sD = K.kda_segment_package_fx(t["q"], t["k"], t["v"], g, beta,
-                                                  t["seg_start"], fx, ckpt_interval=interval,
-                                                  want_sub_M=False)
+        o, M, D, sM, sD = K.kda_segment_package_fx(t["q"], t["k"], t["v"], g, beta,
+                                                   t["seg_start"], fx, ckpt_interval=interval,
+                                                   want_sub_M=whole)
         if timed:
             mark("b")
         S_in, _ = K.kda_segment_scan(M, D, S0, algo=w.scan_algo)
         if timed:
             mark("c")
-        K.kda_output_fixup_fx(t["q"], t["k"], g, beta, t["seg_start"], S_in, o, fx, sub_D=sD,
-                              interval=interval, out=sD)
+        if whole:
+            K.kda_output_fixup_fx(t["q"], t["k"], g, beta, t["seg_start"], S_in, o, fx)
+            if rows:
+                K.kda_checkpoint_write(t["seg_start"], S_in, sM, sD, T=T, interval=interval,
+                                       out=ck_out)
+        else:
+            K.kda_output_fixup_fx(t["q"], t["k"], g, beta, t["seg_start"], S_in, o, fx, sub_D=sD,
+                                  interval=interval, out=sD)
         if timed:
             mark("d")
         return M
@@ -317,6 +338,7 @@ def long_memory_measure(K, w, t, launches: int) -> dict:
     M = step(False)
     torch.cuda.synchronize()
     m_norm_min = float(torch.linalg.matrix_norm(M).min())
+    route = fx.route.cpu().numpy()
     for _ in range(3):
         step(False)
     torch.cuda.synchronize()
@@ -327,14 +349,21 @@ def long_memory_measure(K, w, t, launches: int) -> dict:
     def avg(a, b):
         return float(np.mean([x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]))
     ms = avg("a", "d")
-    nseg = len(w.seg_start) - 1
-    rows = T // interval if interval else 0
     io = 2 if w.dtype == "bf16" else 4
-    per_tok = (bytes_per_token_head(dk, dv, io) + (io * dk + 4 * dk + 4)
-               + (2 * io * dk + 4 * dk + 4 + 2 * io * dv))
-    alg = T * H * per_tok + 4 * H * (dk * dv + dk * dk) * nseg + 2 * 4 * H * dk * dv * rows
+    if whole:   # M blocks: q, k, g, beta read, X written; fix-up: X and o read, o written
+        per_tok = (bytes_per_token_head(dk, dv, io) + (2 * io * dk + 4 * dk + 4 + io * dk)
+                   + (io * dk + 2 * io * dv))
+        rung_bytes = 4 * H * (3 * dk * dv + 2 * dk * dk) * rows   # sub_D, sub_M, rung
+    else:       # M blocks: k, g, beta read; fix-up: q, k, g, beta and o read, o written
+        per_tok = (bytes_per_token_head(dk, dv, io) + (io * dk + 4 * dk + 4)
+                   + (2 * io * dk + 4 * dk + 4 + 2 * io * dv))
+        rung_bytes = 2 * 4 * H * dk * dv * rows
+    alg = T * H * per_tok + 4 * H * (dk * dv + dk * dk) * nseg + rung_bytes
     gbs = alg / (ms * 1e-3) / 1e9
     return {"workload": f"{w.name} with long-memory gates (log alpha ~ -1.2e-4 per token)",
+            "fixup": ("operator over whole segments, rungs by kda_checkpoint_write" if whole
+                      else "recurrence (split segments: the operator covers no segment)"),
+            "units_on_recurrence": int(route.sum()),
             "min_frobenius_norm_M": round(m_norm_min, 4),
             "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
             "steps_timed": launches,

@@ -341,10 +341,13 @@ int kda_output_fixup_ckpt(const kda_config *cfg, const void *q, const void *k, c
  * is the query as the outputs use it (normalised and scaled).  They also write
  *     len[j][h][b] = the chunks after which columns 64b..64b+63 of the
  *                    propagated identity are exactly zero,
- * or -1 if that does not happen within `chunks` chunks.  Since every later
- * row's correction is then exactly zero, the fix-up corrects a segment whose
+ * or the segment's chunk count when the segment ends within `chunks` chunks
+ * first (all its rows are kept), or -1 otherwise.  Since every row past len
+ * chunks has a correction of exactly zero, the fix-up corrects a segment whose
  * len are all >= 0 as o_t += (S_in^j)^T X_t over those rows, with no
- * recurrence.  A segment walks the recurrence as kda_output_fixup_ckpt does
+ * recurrence.  An operator whose `chunks` covers the longest segment therefore
+ * makes the fix-up a product whatever the gates (with long memory, rungs then
+ * come from kda_checkpoint_write and sub_M: Pi covers one rung).  A segment walks the recurrence as kda_output_fixup_ckpt does
  * when one of its len is -1, when its incoming state holds an infinity or a
  * NaN, or when a checkpoint rung falls among the corrected rows and Pi does
  * not cover it.  Pi covers the first rung after the segment start when the

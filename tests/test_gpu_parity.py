@@ -1183,6 +1183,43 @@ def test_fixop_segment_path(K, gates, iv, seg, dtype, dk, dv):
         assert not route[2].any()
 
 
+def test_fixop_whole_segments_long_memory(K):
+    """Long-memory gates: no propagated identity vanishes.  An operator that
+    keeps every row of each segment (chunks = the longest segment) still
+    covers them all (len = each segment's chunk count, route 0), so the
+    fix-up is one product; the rungs come from kda_checkpoint_write with
+    sub_M.  Outputs and rungs against the oracle, outputs against the
+    recurrence's fix-up."""
+    import torch
+    seg = [0, 1024, 2560, 4096]
+    w = make_workload("fixop-whole", [4096], 2, 128, 128, "bf16", 5620, s0_std=0.5,
+                      seg_start=seg, gate_shift=-9.0, beta_shift=-6.0)
+    say("fix-up operator over whole segments, long-memory gates")
+    t = to_torch(w)
+    iv = 512
+    chunks = max(b - a for a, b in zip(seg[:-1], seg[1:])) // 64
+    fx = K.FixOp(3, 2, 128, t["q"].dtype, "cuda", chunks=chunks)
+    # unsplit: a split segment's operator comes from its first sub-segment only
+    ol, M, D, sM, sD = K.kda_segment_package_fx(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                                t["seg_start"], fx, ckpt_interval=iv,
+                                                want_sub_M=True, split=False)
+    S_in, _ = K.kda_segment_scan(M, D, t["S0"][0].contiguous(), algo=1)
+    o, o2 = ol.clone(), ol.clone()
+    K.kda_output_fixup_fx(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o, fx)
+    ck = K.kda_checkpoint_write(t["seg_start"], S_in, sM, sD, T=4096, interval=iv)
+    K.kda_output_fixup(t["q"], t["k"], t["g"], t["beta"], t["seg_start"], S_in, o2)
+    sync()
+    lens, route = fx.len.cpu().numpy(), fx.route.cpu().numpy()
+    want = np.array([(b - a) // 64 for a, b in zip(seg[:-1], seg[1:])])
+    say(f"  len {lens.reshape(3, -1).tolist()} route {route.tolist()}")
+    assert (lens == want[:, None, None]).all() and (route == 0).all()
+    assert float(M.abs().max()) > 1e-3, "long-memory gates should leave M nonzero"
+    ro, _, rck = oracle_full(w, interval=iv)
+    assert_close("o (operator)", to_numpy_f64(o), ro, OUT_TOL["bf16"])
+    assert_close("o: operator vs recurrence", to_numpy_f64(o), to_numpy_f64(o2), OUT_TOL["bf16"])
+    assert_close("rungs", to_numpy_f64(ck), rck, STATE_TOL["bf16"])
+
+
 @pytest.mark.parametrize("nseg", [4, 8, 16])
 def test_fixop_workgroups_per_unit(K, nseg):
     """The operator's launch takes one to several workgroups per (segment,
