@@ -80,21 +80,17 @@ __device__ __forceinline__ float silu(float z) {
     return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs)
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, x);
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
+// 8 bf16 values, converted by the hardware's paired conversion (round to
+// nearest even, one instruction per two values; a NaN stays a NaN)
+typedef __bf16 conv_bf16x8 __attribute__((ext_vector_type(8)));
 
 template <bool BF>
 __device__ __forceinline__ void store8(void *p, int64_t i, const float *v) {
     if (BF) {
-        uint4 w;
-        w.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-        w.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
-        w.z = bf16_rne(v[4]) | (bf16_rne(v[5]) << 16);
-        w.w = bf16_rne(v[6]) | (bf16_rne(v[7]) << 16);
-        *(uint4 *)((uint16_t *)p + i) = w;
+        conv_bf16x8 w;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = (__bf16)v[j];
+        *(conv_bf16x8 *)((uint16_t *)p + i) = w;
     } else {
         *(float4 *)((float *)p + i) = make_float4(v[0], v[1], v[2], v[3]);
         *(float4 *)((float *)p + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
@@ -141,7 +137,9 @@ __device__ __forceinline__ void input_row(const ConvArgs &a, int s, int64_t row,
     }
 }
 
-template <bool BF, int W>
+// SILU: the activation (a.act == 1), chosen at launch so that neither form
+// pays for the other
+template <bool BF, int W, bool SILU>
 __global__ __launch_bounds__(kConvThreads) void conv_kernel(const ConvArgs a) {
     // thread (rg, cg): rows r0 .. r0+7, channels c .. c+7
     const int cg = threadIdx.x & (kConvGroups - 1), rg = threadIdx.x / kConvGroups;
@@ -164,7 +162,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(const ConvArgs a) {
             float acc = b[j];
 #pragma unroll
             for (int k = 0; k < W; ++k) acc = fmaf(w[k][j], win[k][j], acc);
-            y[j] = a.act == 1 ? silu(acc) : acc;
+            y[j] = SILU ? silu(acc) : acc;
         }
         store8<BF>(a.y, r * a.C + c, y);
     };
@@ -183,7 +181,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(const ConvArgs a) {
                 float acc = b[j];
 #pragma unroll
                 for (int k = 0; k < W; ++k) acc = fmaf(w[k][j], raw_at<BF>(cat[i + k], j), acc);
-                y[j] = a.act == 1 ? silu(acc) : acc;
+                y[j] = SILU ? silu(acc) : acc;
             }
             store8<BF>(a.y, (r0 + i) * a.C + c, y);
         }
@@ -251,8 +249,14 @@ hipError_t launch_w(int what, const ConvArgs &a, hipStream_t s) {
     if (what == 0) {
         const int64_t tiles = (a.T + kConvRows - 1) / kConvRows;
         const unsigned cgy = (unsigned)((a.C / kConvVec + kConvGroups - 1) / kConvGroups);
-        if (tiles > 0)
-            hipLaunchKernelGGL((conv_kernel<BF, W>), dim3((unsigned)tiles, cgy), dim3(kConvThreads), 0, s, a);
+        if (tiles > 0) {
+            if (a.act == 1)
+                hipLaunchKernelGGL((conv_kernel<BF, W, true>), dim3((unsigned)tiles, cgy),
+                                   dim3(kConvThreads), 0, s, a);
+            else
+                hipLaunchKernelGGL((conv_kernel<BF, W, false>), dim3((unsigned)tiles, cgy),
+                                   dim3(kConvThreads), 0, s, a);
+        }
         if (a.write_idx && a.N > 0)
             hipLaunchKernelGGL((window_kernel<BF, W>), dim3((unsigned)a.N, cy), dim3(kConvThreads), 0, s, a);
     } else {
