@@ -478,6 +478,24 @@ const char *kda_status_string(int status) {
 
 const char *kda_last_error(void) { return g_last_error.c_str(); }
 
+int kda_validate_inputs(const kda_config *cfg, int64_t T, const int64_t *bounds, int32_t n,
+                        int32_t chunk_aligned, const float *g, const float *beta,
+                        int32_t *report, void *stream) {
+    KDA_TRY(check_config(cfg));
+    if (T < 0) return fail(KDA_ERR_ARG, "T must be >= 0 (got %lld)", (long long)T);
+    if (bounds && n < 1) return fail(KDA_ERR_ARG, "n must be >= 1 with bounds (got %d)", n);
+    if (chunk_aligned != 0 && chunk_aligned != 1)
+        return fail(KDA_ERR_ARG, "chunk_aligned must be 0 or 1 (got %d)", chunk_aligned);
+    KDA_TRY(check_tensor(report, "report", true, 4));
+    KDA_TRY(check_tensor(bounds, "bounds", false, 8));
+    KDA_TRY(check_tensor(g, "g", false));
+    KDA_TRY(check_tensor(beta, "beta", false, 4));
+    return launched(kda::launch_validate(T, cfg->num_heads, cfg->dk, bounds, bounds ? n : 0,
+                                         chunk_aligned, g, beta, report, KDA_CHECK_FIELDS,
+                                         (hipStream_t)stream),
+                    "input validation");
+}
+
 const char *kda_version(void) { return "0.1.0"; }
 
 size_t kda_prefill_workspace(const kda_config *cfg, int64_t T, int32_t N) {

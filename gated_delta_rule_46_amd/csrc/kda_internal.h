@@ -153,6 +153,11 @@ hipError_t launch_split_rung_m(int dk, int H, int nseg, int f, int k, const int6
                                int interval, int64_t rows, const float *Ms, float *sub_M,
                                hipStream_t s);
 
+// Debug check of device-side inputs into report[0..fields) (kda_validate.hip).
+hipError_t launch_validate(int64_t T, int H, int dk, const int64_t *bounds, int n, int aligned,
+                           const float *g, const float *beta, int *report, int fields,
+                           hipStream_t s);
+
 // Segment-path checkpoints: states[row] = sub_M[row] S_in[j] + sub_D[row].
 hipError_t launch_ckpt_write(int dk, int dv, int H, int64_t T, const int64_t *seg_start,
                              int nseg, int interval, const float *S_in, const float *sub_M,

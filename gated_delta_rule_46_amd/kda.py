@@ -24,7 +24,10 @@ EXPORTS = ("kda_prefill_workspace", "kda_prefill", "kda_prefill_noalloc", "kda_p
            "kda_segment_scan_workspace", "kda_segment_scan", "kda_output_fixup",
            "kda_output_fixup_ckpt", "kda_segment_package_fx", "kda_output_fixup_fx",
            "kda_checkpoint_write", "kda_decode", "kda_short_conv", "kda_conv_halo",
-           "kda_status_string", "kda_last_error", "kda_version")
+           "kda_validate_inputs", "kda_status_string", "kda_last_error", "kda_version")
+# fields of kda_validate_inputs' report
+KDA_CHECK_FIELDS = 8
+CHECK_NAMES = ("bounds", "g_positive", "g_nonfinite", "g_block_floor", "beta_nonfinite")
 KDA_ACT_NONE, KDA_ACT_SILU = 0, 1
 
 
@@ -92,6 +95,7 @@ def _load():
         "kda_decode": (ctypes.c_int, [cfgp, I32, P, P, P, P, P, I32, poolp, P, P]),
         "kda_short_conv": (ctypes.c_int, [I32, I32, I32, I32, P, I64, P, I32, P, P, convp, P, P]),
         "kda_conv_halo": (ctypes.c_int, [I32, I32, I32, P, I64, P, I32, convp, P]),
+        "kda_validate_inputs": (ctypes.c_int, [cfgp, I64, P, I32, I32, P, P, P, P]),
         "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "kda_last_error": (ctypes.c_char_p, []),
         "kda_version": (ctypes.c_char_p, []),
@@ -514,6 +518,30 @@ def kda_output_fixup_fx(q, k, g, beta, seg_start, S_in, o, fx, *, sub_D=None, in
                                  ctypes.byref(fxc) if fxc is not None else None, _stream(stream))
     _check(st, "kda_output_fixup_fx")
     return states
+
+
+def kda_validate_inputs(*, T, H, dk, g=None, beta=None, bounds=None, chunk_aligned=False,
+                        stream=None):
+    """Debug check of device-side inputs (kda_validate_inputs): bounds are
+    cu_seqlens, or segment starts with chunk_aligned=True.  Waits for the
+    stream and returns the report as a dict of counts (all zero: inside what
+    the kernels assume)."""
+    dev = next(x.device for x in (g, beta, bounds) if x is not None)
+    if g is not None:
+        _need(g, "g", (T, H, dk), torch.float32, dev)
+    if beta is not None:
+        _need(beta, "beta", (T, H), torch.float32, dev)
+    n = 0
+    if bounds is not None:
+        n = bounds.numel() - 1
+        _need(bounds, "bounds", (n + 1,), torch.int64, dev)
+    report = torch.empty(KDA_CHECK_FIELDS, dtype=torch.int32, device=dev)
+    cfg = make_config(H, dk, dk, torch.bfloat16)
+    st = LIB.kda_validate_inputs(ctypes.byref(cfg), int(T), _p(bounds), n, int(bool(chunk_aligned)),
+                                 _p(g), _p(beta), _p(report), _stream(stream))
+    _check(st, "kda_validate_inputs")
+    r = report.cpu().tolist()
+    return dict(zip(CHECK_NAMES, r))
 
 
 def kda_checkpoint_write(seg_start, S_in, sub_M, sub_D, *, T, interval, dtype=torch.bfloat16,

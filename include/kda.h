@@ -75,7 +75,8 @@
  *    null stream) without synchronising.  Argument errors are detected on
  *    the host and returned before anything is launched.  A failed launch
  *    returns KDA_ERR_DEVICE.  Device-side data (cu_seqlens monotone, segment
- *    starts chunk-aligned, g <= 0) is not validated: that would need a sync.
+ *    starts chunk-aligned, g <= 0) is not validated by the calls: that would
+ *    need a sync.  kda_validate_inputs checks it on the device for debug runs.
  *  - Numerical domain: the per-channel log-decay summed over any aligned
  *    16-token block must stay above about -80 (a mean alpha above ~0.007
  *    per token); beyond it intermediate exponentials leave fp32 range.
@@ -481,6 +482,37 @@ int kda_conv_halo(int32_t io_dtype, int32_t channels, int32_t width, const void 
 /* Diagnostics                                                               */
 /* ------------------------------------------------------------------------ */
 const char *kda_status_string(int status);
+
+/*
+ * Debug check of device-side inputs the calls take on trust.  Counts, into
+ * report[0 .. KDA_CHECK_FIELDS) (device int32, 4-byte aligned, zeroed by the
+ * call; read it after the stream's work), for a tensor of T tokens with
+ * cfg->num_heads heads and cfg->dk key channels:
+ *   [KDA_CHECK_BOUNDS]         entries of bounds[0..n] at fault: bounds[0] != 0,
+ *                              bounds[n] != T, a decrease, or (chunk_aligned = 1,
+ *                              for segment starts) an interior entry off the
+ *                              chunk grid.  bounds = cu_seqlens (n sequences) or
+ *                              seg_start (n segments); NULL: one unit [0, T).
+ *   [KDA_CHECK_G_POSITIVE]     elements of g above 0 (a decay alpha = e^g above 1);
+ *   [KDA_CHECK_G_NONFINITE]    elements of g that are infinite or NaN;
+ *   [KDA_CHECK_G_BLOCK_FLOOR]  (16-token block, head, channel) triples whose
+ *                              summed g is below -80, the blocks counted from
+ *                              each unit's first token: the numerical domain
+ *                              stated above;
+ *   [KDA_CHECK_BETA_NONFINITE] elements of beta that are infinite or NaN.
+ * g [T, H, dk] and beta [T, H] may each be NULL (not checked).  All zeros:
+ * the inputs are inside what the kernels assume.  Enqueued on `stream`; it
+ * reads g once (about T * H * dk * 4 bytes) and is meant for debug runs.
+ */
+#define KDA_CHECK_BOUNDS         0
+#define KDA_CHECK_G_POSITIVE     1
+#define KDA_CHECK_G_NONFINITE    2
+#define KDA_CHECK_G_BLOCK_FLOOR  3
+#define KDA_CHECK_BETA_NONFINITE 4
+#define KDA_CHECK_FIELDS         8
+int kda_validate_inputs(const kda_config *cfg, int64_t T, const int64_t *bounds, int32_t n,
+                        int32_t chunk_aligned, const float *g, const float *beta,
+                        int32_t *report, void *stream);
 /* Detail of the last error returned on the calling thread ("" if none). */
 const char *kda_last_error(void);
 /* Library version, "major.minor.patch". */

@@ -199,6 +199,21 @@ def test_segment_entry_points_validate():
     assert cw(ctypes.byref(ck), subD=MISALIGNED) == K.KDA_ERR_ALIGN
 
 
+def test_validate_inputs_validates():
+    """Argument errors of the debug input check, all before any launch."""
+    c = cfg()
+    v = lambda **kw: K.LIB.kda_validate_inputs(
+        ctypes.byref(c) if kw.get("c", True) else None, kw.get("T", 128), kw.get("bounds", FAKE),
+        kw.get("n", 2), kw.get("aligned", 0), kw.get("g", FAKE), kw.get("beta", FAKE),
+        kw.get("report", FAKE), None)
+    assert v(c=False) == K.KDA_ERR_ARG
+    assert v(T=-1) == K.KDA_ERR_ARG
+    assert v(n=0) == K.KDA_ERR_ARG and "n must be" in last_error()
+    assert v(aligned=2) == K.KDA_ERR_ARG
+    assert v(report=None) == K.KDA_ERR_ARG and "report" in last_error()
+    assert v(g=MISALIGNED) == K.KDA_ERR_ALIGN
+
+
 def decode(c, N=4, gate_logits=1, pool=None, q=FAKE, o=FAKE, beta=FAKE):
     if pool is None:
         pool = K.kda_state_pool(FAKE, 8, FAKE, FAKE)

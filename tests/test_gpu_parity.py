@@ -553,6 +553,42 @@ def test_package_split_without_M(K, gates):
         assert torch.equal(full[i], part[i]), name
 
 
+def test_validate_inputs_counts_planted_faults(K):
+    """The debug input check is silent on the workloads' inputs and counts
+    exactly the faults planted on a copy of them (integer counts)."""
+    import torch
+    w = make_workload("validate", [300, 0, 517, 64], 2, 128, 128, "bf16", 5700, s0_std=None)
+    t = to_torch(w)
+    T, H, dk = w.T, 2, 128
+    say("input validation on clean and faulty inputs")
+    clean = K.kda_validate_inputs(T=T, H=H, dk=dk, g=t["g"], beta=t["beta"], bounds=t["cu_seqlens"])
+    assert clean == dict.fromkeys(K.CHECK_NAMES, 0), clean
+    seg = torch.tensor([0, 128, 448, T], dtype=torch.int64, device="cuda")
+    assert K.kda_validate_inputs(T=T, H=H, dk=dk, g=t["g"], bounds=seg, chunk_aligned=True) \
+        == dict.fromkeys(K.CHECK_NAMES, 0)
+    # planted: three g > 0, one NaN, one block of 16 summing below -80 in one
+    # channel, two non-finite betas, bounds out of order / off the chunk grid
+    g, beta = t["g"].clone(), t["beta"].clone()
+    g[5, 0, 3] = 0.5
+    g[400, 1, 100] = 1e-3
+    g[880, 1, 0] = 2.0
+    g[77, 0, 64] = float("nan")
+    start = 300 + 32                                  # a block start of sequence 2 (starts at 300)
+    g[start:start + 16, 1, 17] = -6.0                 # 16 x -6 = -96 < -80
+    beta[10, 1] = float("inf")
+    beta[600, 0] = float("nan")
+    r = K.kda_validate_inputs(T=T, H=H, dk=dk, g=g, beta=beta, bounds=t["cu_seqlens"])
+    assert r == {"bounds": 0, "g_positive": 3, "g_nonfinite": 1, "g_block_floor": 1,
+                 "beta_nonfinite": 2}, r
+    bad_cu = t["cu_seqlens"].clone()
+    bad_cu[2] = bad_cu[1] - 1                          # a decrease
+    assert K.kda_validate_inputs(T=T, H=H, dk=dk, bounds=bad_cu, g=t["g"])["bounds"] == 1
+    bad_seg = torch.tensor([0, 100, 448, T + 1], dtype=torch.int64, device="cuda")
+    # 100 off the chunk grid, the last entry not T (the block sums stop at T)
+    assert K.kda_validate_inputs(T=T, H=H, dk=dk, g=t["g"], bounds=bad_seg,
+                                 chunk_aligned=True)["bounds"] == 2
+
+
 # ---------------------------------------------------------------------------
 # Prefill resumed from a state pool
 # ---------------------------------------------------------------------------
