@@ -335,3 +335,23 @@ def test_long_memory_bf16_d128(K, segmentation):
     norms = np.linalg.norm(M.reshape(M.shape[0], M.shape[1], -1), axis=-1)
     say(f"  |M|_F per segment: min {norms.min():.3f} max {norms.max():.3f}")
     assert norms.min() > 0.1
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_workload_inputs_in_domain(K, idx):
+    """The four workloads' inputs, and config 3's with long-memory gates, are
+    inside what the kernels assume (kda_validate_inputs reports nothing):
+    ordered bounds (segment starts on the chunk grid), g <= 0 and finite,
+    every 16-token block's summed g above the floor, beta finite."""
+    import torch
+    ws = [standard_workload(idx)] + ([standard_workload(3, **LONG)] if idx == 3 else [])
+    for w in ws:
+        t = to_torch(w)
+        seg = w.seg_start is not None
+        bounds = t["seg_start"] if seg else t["cu_seqlens"]
+        r = K.kda_validate_inputs(T=w.T, H=w.H, dk=w.dk, g=t["g"], beta=t["beta"], bounds=bounds,
+                                  chunk_aligned=seg)
+        say(f"{w.name}: {r}")
+        assert r == dict.fromkeys(K.CHECK_NAMES, 0), r
+        del t
+        torch.cuda.empty_cache()
