@@ -110,6 +110,8 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--roofline-launches", type=int, default=5,
                     help="extra launches of the dominant kernel timed alone for the roofline")
+    ap.add_argument("--no-reference", action="store_true",
+                    help="skip the device reference points (1 GiB copy, bf16 GEMM)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes three times (a known-size "
                          "reference for the HBM traffic counters) and exit")
@@ -125,6 +127,42 @@ def copy_probe(nbytes: int):
         y.copy_(x)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": n * 4, "launches": 3}), flush=True)
+
+
+def reference_rates(reps: int = 10) -> dict:
+    """Reference points measured on this device, for context beside the
+    spec peaks (neither is part of the library): a 1 GiB device-to-device
+    copy (torch copy_, bytes read + written per second) and a bf16 matrix
+    product of 8192 x 8192 x 8192 (torch matmul, a library GEMM, contiguous
+    operands).  Median over reps, HIP events around each."""
+    import torch
+    stream = torch.cuda.current_stream()
+
+    def median_ms(fn):
+        fn()
+        pairs = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in pairs]))
+    n = (1 << 30) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    copy_ms = median_ms(lambda: y.copy_(x))
+    del x, y
+    m = 8192
+    a = torch.randn((m, m), device="cuda").to(torch.bfloat16)
+    b = torch.randn((m, m), device="cuda").to(torch.bfloat16)
+    gemm_ms = median_ms(lambda: torch.matmul(a, b))
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_1gib_gbs": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
+            "bf16_gemm_8192_tflops": round(2 * m ** 3 / (gemm_ms * 1e-3) / 1e12, 1)}
 
 
 def cpu_baseline(w, target_s: float) -> dict:
@@ -585,6 +623,13 @@ def main():
     torch.cuda.synchronize()
     kernel_ms = avg_ms("dom0", "dom1")
     breakdown = {"package" if segmented else "prefill": round(avg_ms("pkg0", "pkg1"), 4)}
+    # spread of the timed steps (each step's first and last event; the value
+    # above is total time over steps, host gaps included)
+    last = "fix1" if segmented else "pkg1"
+    per_step = np.array([x.elapsed_time(y) for x, y in zip(ev["pkg0"], ev[last])])
+    step_spread = {"p10": round(float(np.percentile(per_step, 10)), 4),
+                   "p50": round(float(np.percentile(per_step, 50)), 4),
+                   "p90": round(float(np.percentile(per_step, 90)), 4)}
     if segmented:
         breakdown.update(scan=round(avg_ms("pkg1", "scan1"), 4),
                          fixup_and_rungs=round(avg_ms("scan1", "fix1"), 4))
@@ -618,6 +663,7 @@ def main():
                      "alg_bytes_per_launch": int(alg_bytes),
                      "launch_ms": round(kernel_ms, 4), "launches_timed": args.roofline_launches},
         "breakdown_ms": breakdown,
+        "step_ms_spread": step_spread,
     }
     if value_blocks is not None:
         vb_ms = avg_ms("vb0", "vb1")
@@ -643,6 +689,12 @@ def main():
         result["single_sequence_8192"] = single_sequence_measure(K, args.roofline_launches)
     if not args.no_decode:
         result["decode"] = decode_measure(K, args.decode_launches)
+    if not args.no_reference:
+        ref = reference_rates()
+        result["reference"] = ref
+        result["roofline"]["frac_of_measured_copy"] = round(achieved / ref["copy_1gib_gbs"], 4)
+        result["mfma_frac_of_measured_gemm"] = round(
+            flops / (ms_per_step * 1e-3) / 1e12 / ref["bf16_gemm_8192_tflops"], 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
